@@ -1,0 +1,206 @@
+/*
+ * vla.h -- C ABI of the dual-phase policy step on AMD Instinct MI355X (gfx950).
+ *
+ * A bidirectional prefix pass encodes an observation once and writes an explicit
+ * cross-attention K/V cache; a flow-matching action expert then refines a noise
+ * chunk over T Euler steps, reading that cache at every step.
+ *
+ * Sources ("the paper" is vla.cpp: A Unified Inference Runtime for
+ * Vision-Language-Action Models, arXiv 2606.08094; "the reading notes" are the
+ * paper.gecl.asia notes on it):
+ *   - prefix computed once per observation, its projections reused by every
+ *     solver step, refreshed on each new observation; graphs and buffers kept
+ *     for unchanged shapes ............................... the paper, §III-B
+ *   - cross-attention K_C = Z W_K, V_C = Z W_V, softmax(Q K_C^T/sqrt(d_k) + M) V_C
+ *                                                          the paper, §III-B, Eq. 2
+ *   - Euler solver X^{k+1} = X^k + (tau_{k+1} - tau_k) v(X^k, tau_k)
+ *                                                          the paper, §III-A, Eq. 1
+ *   - bidirectional prefix mask; hidden states taken before the LM output
+ *     projection ........................................ the reading notes, Method 1-2
+ *   - ternary W2A8 linear ............................... the paper, §III-D, Eq. 4
+ *   - a request returns the chunk and its dimensions, "or an error"
+ *                                                          the paper, §III-C
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are HIP device addresses on the current device; "host"
+ *     pointers are ordinary CPU memory.  `stream` is a hipStream_t (NULL = the
+ *     null stream).  Work is enqueued asynchronously on `stream`; the returned
+ *     status covers argument/shape validation and launch errors, and a device
+ *     fault surfaces at the caller's next synchronising call.
+ *   - On any status other than VLA_OK no output buffer has been written.
+ *   - The library never aborts or exits; vla_last_error() gives a per-thread
+ *     message for the last failing call.
+ *   - A model handle is not re-entrant: calls that use the same model (encode,
+ *     denoise) must not run concurrently, on any streams, because they share
+ *     the model's workspace.  Different models are independent.
+ */
+#ifndef VLA_H_
+#define VLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VLA_ABI_VERSION 1
+
+typedef enum {
+  VLA_OK = 0,
+  VLA_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, bad value   */
+  VLA_ERR_SHAPE_MISMATCH = 2,   /* sizes disagree with the model or the cache   */
+  VLA_ERR_INVALID_HANDLE = 3,   /* released, foreign or corrupted handle        */
+  VLA_ERR_UNSUPPORTED = 4,      /* a shape or mode this build does not support  */
+  VLA_ERR_OUT_OF_MEMORY = 5,    /* a device allocation failed                   */
+  VLA_ERR_DEVICE = 6            /* no usable gfx950 device, or a HIP call failed */
+} vla_status;
+
+typedef enum {
+  VLA_F32 = 0,       /* every weight and activation float32                       */
+  VLA_BF16 = 1,      /* bf16 weights and GEMM operands, fp32 residual and softmax  */
+  VLA_W2A8_BF16 = 2  /* prefix linears ternary W2A8 (Eq. 4), the rest as VLA_BF16  */
+} vla_precision;
+
+typedef enum { VLA_OUT_F32 = 0, VLA_OUT_BF16 = 1 } vla_out_dtype;
+
+/* Model shape.  Prefix: d_p wide, L_p layers, Hq query heads sharing Hkv
+ * key/value heads of width hd, GeGLU width F_p.  Expert: the same fields with
+ * suffix _e.  H x d_a is the action chunk (d_a <= 256).  Requirements:
+ * Hq % Hkv == 0 and Hq_e % Hkv_e == 0; for VLA_F32, hd and hd_e in {32, 64}
+ * and d_p, d_e, F_p, F_e multiples of 16; otherwise hd and hd_e in
+ * {64, 128, 256}, d_p, d_e, F_p, F_e multiples of 64 and d_e <= 4096, and for
+ * VLA_W2A8_BF16 also d_p, F_p and Hq*hd multiples of 128. */
+typedef struct {
+  int32_t abi_version; /* must be VLA_ABI_VERSION */
+  int32_t precision;   /* vla_precision */
+  int32_t d_p, L_p, Hq, Hkv, hd, F_p;
+  int32_t d_e, L_e, Hq_e, Hkv_e, hd_e, F_e;
+  int32_t H, d_a;
+  float rms_eps;       /* RMSNorm epsilon, e.g. 1e-6 */
+} vla_model_config;
+
+/* Weights, all linear layers [out, in] row-major (y = x W^T), in this order:
+ *   per prefix layer l = 0..L_p-1:  w1[d_p] wq[Hq*hd, d_p] wk[Hkv*hd, d_p]
+ *       wv[Hkv*hd, d_p] wo[d_p, Hq*hd] w2[d_p] wg[F_p, d_p] wu[F_p, d_p] wd[d_p, F_p]
+ *   prefix final norm gain [d_p]
+ *   per expert layer e: cache wk[Hkv_e*hd_e, d_p], cache wv[Hkv_e*hd_e, d_p]
+ *   w_in[d_e, d_a]
+ *   per expert layer e:  a1[d_e] wqs[Hq_e*hd_e, d_e] wks[Hkv_e*hd_e, d_e]
+ *       wvs[Hkv_e*hd_e, d_e] wos[d_e, Hq_e*hd_e] a2[d_e] wqc[Hq_e*hd_e, d_e]
+ *       woc[d_e, Hq_e*hd_e] a3[d_e] wg[F_e, d_e] wu[F_e, d_e] wd[d_e, F_e]
+ *   expert final norm gain [d_e], w_out[d_a, d_e]
+ * RMSNorm gains ("w1", "a1", final norms ...) are float32 and applied as (1 + w).
+ * Linear weights are float32 for VLA_F32 and bfloat16 otherwise, except that
+ * with VLA_W2A8_BF16 the seven prefix linears of every layer (wq wk wv
+ * wo wg wu wd) are packed ternary: uint8 [out, in/4], four 2-bit codes per byte,
+ * code = q + 1, element 4j+i of a row in bits 2i..2i+1 of byte j (code 3 is
+ * invalid); their fp32 scales beta are listed, in the same order, in
+ * `ternary_beta` (host memory, 7 * L_p entries).
+ * The library copies every weight into its own layout during vla_model_create;
+ * the caller's buffers may be freed once it returns. */
+typedef struct {
+  const void* const* tensors; /* host array of n_tensors device pointers */
+  int32_t n_tensors;          /* must equal vla_n_tensors(cfg)            */
+  const float* ternary_beta;  /* host; NULL unless precision is W2A8      */
+} vla_weights;
+
+/* Integration schedule of Eq. 1.  If `schedule` is non-NULL it is a host array
+ * of steps + 1 times tau_0..tau_T; otherwise tau_k = tau_start + k (tau_end -
+ * tau_start) / steps.  Passing NULL for the whole struct means 0 -> 1. */
+typedef struct {
+  float tau_start, tau_end;
+  const float* schedule;
+} vla_solver;
+
+/* Optional per-call timings (filled only when a pointer is passed; that makes
+ * the call synchronise its stream). */
+typedef struct {
+  float prefix_ms;        /* vla_prefix_encode: whole call on the device      */
+  float denoise_ms;       /* vla_denoise_chunk: all steps on the device       */
+  float step_ms;          /* denoise_ms / steps                               */
+  int32_t graph_replayed; /* 1 if the solver loop replayed a cached HIP graph */
+} vla_timing;
+
+typedef struct vla_model vla_model;
+typedef struct vla_kv_cache vla_kv_cache;
+
+/* Human-readable name of a status, and the calling thread's last error message. */
+const char* vla_status_string(vla_status s);
+const char* vla_last_error(void);
+
+/* Number of weight tensors the model config expects (-1 if cfg is invalid). */
+int32_t vla_n_tensors(const vla_model_config* cfg);
+
+/* Shape and kind of tensor `index` in the order above: rows x cols (cols = 1 for
+ * gains); kind 0 = fp32 gain, 1 = linear (fp32 or bf16 by precision), 2 = packed
+ * ternary (cols is the packed byte count in/4). */
+vla_status vla_tensor_info(const vla_model_config* cfg, int32_t index, int64_t* rows,
+                           int64_t* cols, int32_t* kind);
+
+/* Build a model on the current device: validates cfg, copies and repacks the
+ * weights (ternary codes are checked; an invalid code 3 gives
+ * VLA_ERR_INVALID_ARGUMENT), and owns the result until vla_model_destroy.
+ * Synchronises `stream`.  Returns VLA_ERR_DEVICE if no gfx950 device is present. */
+vla_status vla_model_create(const vla_model_config* cfg, const vla_weights* weights,
+                            void* stream, vla_model** out);
+vla_status vla_model_destroy(vla_model* model);
+
+/* Bytes of K/V cache storage for `batch` observations of `n_prefix` tokens:
+ * layout [batch][L_e][2 (K, V)][Hkv_e][n_prefix][hd_e], bfloat16 (float32 for
+ * VLA_F32).  Returns 0 for invalid arguments. */
+size_t vla_kv_cache_bytes(const vla_model* model, int32_t batch, int32_t n_prefix);
+
+/* Prefix pass (the paper, §III-B; the reading notes, Method 1-3): encodes
+ * `batch` observations of `n_prefix` tokens, prefix_hidden = device float32
+ * [batch][n_prefix][d_p], through L_p bidirectional layers and the final
+ * RMSNorm, and projects the result into every expert layer's K and V, written
+ * to `kv_storage` (device, caller-owned, >= vla_kv_cache_bytes bytes, layout as
+ * above).  *out receives a handle that refers to kv_storage; it stays valid
+ * until vla_kv_cache_release and may serve any number of denoise calls. */
+vla_status vla_prefix_encode(vla_model* model, const float* prefix_hidden, int32_t batch,
+                             int32_t n_prefix, void* kv_storage, size_t kv_bytes,
+                             void* stream, vla_kv_cache** out);
+
+/* Flow-matching solver (the paper, §III-A, Eq. 1): X^0 = noise (device float32
+ * [batch][H][d_a], batch and n_prefix taken from the cache), `steps` Euler
+ * steps of the action expert over the cached K/V, X^T written to actions_out
+ * (device [batch][H][d_a], float32 or bfloat16 by out_dtype).  At batch 1 the
+ * step loop runs as a HIP graph captured once per (cache, batch, n_prefix,
+ * steps) and replayed afterwards.  noise and actions_out may alias. */
+vla_status vla_denoise_chunk(vla_model* model, const vla_kv_cache* kv, const float* noise,
+                             int32_t steps, const vla_solver* solver, void* actions_out,
+                             int32_t out_dtype, void* stream, vla_timing* timing);
+
+/* Release a cache handle (the storage stays the caller's). */
+vla_status vla_kv_cache_release(vla_kv_cache* kv);
+
+/* Batch and prefix length a cache was encoded with. */
+vla_status vla_kv_cache_info(const vla_kv_cache* kv, int32_t* batch, int32_t* n_prefix);
+
+/* Per-row int8 quantization of Eq. 4 (the paper, §III-D): for each row m of
+ * x (device float32 [M][K]) alpha[m] = max(max_j |x_mj|, 1e-5) / 127 and
+ * a[m][j] = clip(rint(x_mj / alpha[m]), -128, 127), IEEE float32 division,
+ * ties to even.  Outputs: a (device int8 [M][K]), alpha (device float32 [M]). */
+vla_status vla_quantize_rows_i8(const float* x, int32_t M, int32_t K, int8_t* a,
+                                float* alpha, void* stream);
+
+/* Ternary W2A8 GEMM of Eq. 4: acc[m][n] = sum_j a[m][j] q[n][j] in int32, with
+ * q unpacked from q_packed (device uint8 [N][K/4], format as above; K % 128 == 0),
+ * and y[m][n] = bf16(float(acc) * (alpha[m] * beta)) rounded to nearest even.
+ * a: device int8 [M][K]; alpha: device float32 [M]; acc_out (device int32
+ * [M][N]) may be NULL; y_bf16 (device uint16 bit patterns [M][N]) may be NULL. */
+vla_status vla_w2a8_gemm(const int8_t* a, const float* alpha, const uint8_t* q_packed,
+                         float beta, int32_t M, int32_t N, int32_t K, int32_t* acc_out,
+                         uint16_t* y_bf16, void* stream);
+
+/* Host helpers for the packed ternary format: pack codes q in {-1, 0, 1}
+ * (host int8 [N][K], K % 4 == 0) into host uint8 [N][K/4]; unpack the reverse
+ * (VLA_ERR_INVALID_ARGUMENT on a code 3). */
+vla_status vla_ternary_pack(const int8_t* q, int32_t N, int32_t K, uint8_t* packed);
+vla_status vla_ternary_unpack(const uint8_t* packed, int32_t N, int32_t K, int8_t* q);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VLA_H_ */

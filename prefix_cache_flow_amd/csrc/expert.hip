@@ -1,0 +1,137 @@
+// Small row kernels of the action expert: the chunk-token embedding with the
+// solver time, and the velocity head fused with the Euler update of the
+// paper's §III-A, Eq. 1: X^{k+1} = X^k + (tau_{k+1} - tau_k) v(X^k, tau_k).
+//
+// The time embedding is not defined on the pages; the plainest reading of a
+// sinusoidal embedding of tau is used: phi_{2i} = sin(tau / 10000^(2i/d)),
+// phi_{2i+1} = cos(tau / 10000^(2i/d)), added to every chunk token after the
+// input projection.  tau_k and tau_{k+1} are read from a device copy of the
+// schedule, so one captured graph serves any schedule of the same length.
+#include "common.h"
+#include "kernels.h"
+
+namespace vla {
+
+template <bool WF32>
+__device__ __forceinline__ float ld_w(const void* w, long i) {
+  if (WF32) return ((const float*)w)[i];
+  return bf2f(((const bf16_t*)w)[i]);
+}
+
+// One 256-thread workgroup per chunk row m; d_e <= 4096, d_a <= 256.
+template <bool WF32>
+__global__ __launch_bounds__(256) void k_embed(const float* X, int d_a, const void* w_in, int d_e, const float* sched,
+                                               int k, float* E, const float* gain, float eps, void* u, int u_f32) {
+  __shared__ float xs[256];
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  if (threadIdx.x < d_a) xs[threadIdx.x] = X[(long)m * d_a + threadIdx.x];
+  __syncthreads();
+  const float tau = sched[k];
+  const float l2 = 13.287712379549449f;  // log2(10000)
+  float vals[16];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int n = threadIdx.x + i * 256;
+    float v = 0.f;
+    if (n < d_e) {
+      for (int a = 0; a < d_a; ++a) v = fmaf(xs[a], ld_w<WF32>(w_in, (long)n * d_a + a), v);
+      const int pair = n >> 1;
+      const float freq = exp2f(-l2 * (2.0f * (float)pair / (float)d_e));
+      const float arg = tau * freq;
+      v += (n & 1) ? cosf(arg) : sinf(arg);
+      E[(long)m * d_e + n] = v;
+    }
+    vals[i] = v;
+    ss = fmaf(v, v, ss);
+  }
+  ss = block_sum<256>(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)d_e + eps);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int n = threadIdx.x + i * 256;
+    if (n < d_e) {
+      const float un = vals[i] * r * (1.0f + gain[n]);
+      if (u_f32) ((float*)u)[(long)m * d_e + n] = un; else ((bf16_t*)u)[(long)m * d_e + n] = f2bf(un);
+    }
+  }
+}
+
+hipError_t expert_embed(const float* X, int M, int d_a, const void* w_in, int w_f32, int d_e, const float* sched,
+                        int k, float* E, const float* gain, float eps, void* u, int u_f32, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (d_a > 256 || d_e > 4096) return hipErrorInvalidValue;
+  if (w_f32)
+    hipLaunchKernelGGL(k_embed<true>, dim3(M), dim3(256), 0, s, X, d_a, w_in, d_e, sched, k, E, gain, eps, u, u_f32);
+  else
+    hipLaunchKernelGGL(k_embed<false>, dim3(M), dim3(256), 0, s, X, d_a, w_in, d_e, sched, k, E, gain, eps, u, u_f32);
+  return hipGetLastError();
+}
+
+// One 256-thread workgroup per chunk row: final RMSNorm, W_out, Euler update.
+template <bool WF32>
+__global__ __launch_bounds__(256) void k_head(const float* E, int d_e, const float* gain, float eps, const void* w_out,
+                                              int d_a, const float* sched, int k, float* X) {
+  __shared__ float us[4096];
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  float ss = 0.f;
+  for (int n = threadIdx.x; n < d_e; n += 256) {
+    const float v = E[(long)m * d_e + n];
+    us[n] = v;
+    ss = fmaf(v, v, ss);
+  }
+  ss = block_sum<256>(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)d_e + eps);
+  for (int n = threadIdx.x; n < d_e; n += 256) us[n] = us[n] * r * (1.0f + gain[n]);
+  __syncthreads();
+  const float dt = sched[k + 1] - sched[k];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  for (int a = wid; a < d_a; a += 4) {
+    float v = 0.f;
+    for (int n = lane; n < d_e; n += 64) v = fmaf(us[n], ld_w<WF32>(w_out, (long)a * d_e + n), v);
+    v = wave_sum(v);
+    if (lane == 0) X[(long)m * d_a + a] += dt * v;
+  }
+}
+
+hipError_t expert_head(const float* E, int M, int d_e, const float* gain, float eps, const void* w_out, int w_f32,
+                       int d_a, const float* sched, int k, float* X, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (d_e > 4096) return hipErrorInvalidValue;
+  if (w_f32)
+    hipLaunchKernelGGL(k_head<true>, dim3(M), dim3(256), 0, s, E, d_e, gain, eps, w_out, d_a, sched, k, X);
+  else
+    hipLaunchKernelGGL(k_head<false>, dim3(M), dim3(256), 0, s, E, d_e, gain, eps, w_out, d_a, sched, k, X);
+  return hipGetLastError();
+}
+
+__global__ void k_copy_out(const float* src, void* dst, long n, int out_bf16) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+    if (out_bf16) ((bf16_t*)dst)[i] = f2bf(src[i]); else ((float*)dst)[i] = src[i];
+  }
+}
+
+hipError_t copy_out(const float* src, void* dst, long n, int out_bf16, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (int)std::min<long>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(k_copy_out, dim3(blocks), dim3(256), 0, s, src, dst, n, out_bf16);
+  return hipGetLastError();
+}
+
+hipError_t copy_f32(const float* src, float* dst, long n, hipStream_t s) { return copy_out(src, dst, n, 0, s); }
+
+__global__ void k_f32_to_bf16(const float* src, uint16_t* dst, long n) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+    dst[i] = f2bf(src[i]);
+}
+
+hipError_t f32_to_bf16(const float* src, uint16_t* dst, long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (int)std::min<long>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_f32_to_bf16, dim3(blocks), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace vla

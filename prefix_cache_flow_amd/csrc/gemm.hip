@@ -1,0 +1,296 @@
+// Dense projections of the policy step: C = A W^T with A [M, K] activations and
+// W [N, K] weights (the [out, in] layout of every linear layer).
+//
+// gemm_bf16: bf16 operands, fp32 accumulation on the 32x32x16 bf16 MFMA of gfx950.
+//   Workgroup tile BM x BN, 64-wide K slices staged through LDS with one
+//   register-prefetched slice ahead (double-buffered LDS, one barrier per slice).
+//   Each wave owns a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.  Rows of
+//   LDS are padded by 16 bytes so the 16-byte reads of a 32-lane column group hit
+//   distinct banks.  Output tiles are mapped XCD-major: consecutive workgroup ids
+//   land on different XCDs, so tiles that share a weight panel (same n, every m)
+//   are numbered to run on one XCD and share its L2.
+//   Split-K writes fp32 partials [split][M][N] that a fixed-order reduction (or
+//   the row kernel of norm.hip) sums, so results never depend on timing.
+// gemm_f32: fp32 SIMT tiles for the fp32 workload (small shapes).
+#include "common.h"
+#include "kernels.h"
+
+namespace vla {
+
+struct GemmP {
+  const uint16_t* A;
+  int lda;
+  const uint16_t* W;
+  int ldw;
+  int M, N, K, kchunk, nM, nN;
+  Epilogue epi;
+  float* ws;
+};
+
+__device__ __forceinline__ void cache_index(const Epilogue& e, int m, int n, long& idx) {
+  const int per_kv = e.hkv * e.hd, per_l = 2 * per_kv;
+  const int l = n / per_l;
+  int r = n - l * per_l;
+  const int kv = r / per_kv;
+  r -= kv * per_kv;
+  const int h = r / e.hd, d = r - h * e.hd;
+  const int b = m / e.npre, t = m - b * e.npre;
+  idx = ((((long)(b * e.L + l) * 2 + kv) * e.hkv + h) * e.npre + t) * e.hd + d;
+}
+
+// Store one finished element (every kind but GEGLU, which needs a pair).
+__device__ __forceinline__ void epi_store(const Epilogue& e, int m, int n, float v) {
+  if (e.kind == EPI_STORE) {
+    const long i = (long)m * e.ldo + n;
+    if (e.out_f32) ((float*)e.out)[i] = v; else ((bf16_t*)e.out)[i] = f2bf(v);
+  } else if (e.kind == EPI_RESID) {
+    e.resid[(long)m * e.ldr + n] += v;
+  } else if (e.kind == EPI_CACHE) {
+    long i;
+    cache_index(e, m, n, i);
+    if (e.out_f32) ((float*)e.out)[i] = v; else ((bf16_t*)e.out)[i] = f2bf(v);
+  }
+}
+
+__device__ __forceinline__ void epi_geglu(const Epilogue& e, int m, int f, float g, float u) {
+  const float v = gelu_erf(g) * u;
+  const long i = (long)m * e.ldo + f;
+  if (e.out_f32) ((float*)e.out)[i] = v; else ((bf16_t*)e.out)[i] = f2bf(v);
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GemmP p) {
+  constexpr int NT = 64 * WM * WN, BK = 64, LDK = BK + 8;
+  constexpr int TM = BM / (32 * WM), TN = BN / (32 * WN);
+  static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "tile shape");
+  constexpr int AV = BM * BK / 8, WV = BN * BK / 8;  // 16-byte vectors per slice
+  constexpr int AVT = (AV + NT - 1) / NT, WVT = (WV + NT - 1) / NT;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2][BN * LDK];
+
+  const int nt = p.nM * p.nN, L = blockIdx.x;
+  const int tile = (nt % 8 == 0) ? (L % 8) * (nt / 8) + L / 8 : L;
+  const int tm = tile % p.nM, tn = tile / p.nM;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kb = blockIdx.y * p.kchunk;
+  const int ke = min(p.K, kb + p.kchunk);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WN, wn = wid % WN;
+
+  u32x4_t ra[AVT], rw[WVT];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < AVT; ++i) {
+      const int v = tid + i * NT;
+      if (AV % NT == 0 || v < AV) {
+        const int r = v >> 3, c = (v & 7) * 8, gm = m0 + r;
+        ra[i] = gm < p.M ? *(const u32x4_t*)(p.A + (long)gm * p.lda + k0 + c) : u32x4_t{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < WVT; ++i) {
+      const int v = tid + i * NT;
+      if (WV % NT == 0 || v < WV) {
+        const int r = v >> 3, c = (v & 7) * 8, gn = n0 + r;
+        rw[i] = gn < p.N ? *(const u32x4_t*)(p.W + (long)gn * p.ldw + k0 + c) : u32x4_t{0, 0, 0, 0};
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < AVT; ++i) {
+      const int v = tid + i * NT;
+      if (AV % NT == 0 || v < AV) *(u32x4_t*)&sA[buf][(v >> 3) * LDK + (v & 7) * 8] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < WVT; ++i) {
+      const int v = tid + i * NT;
+      if (WV % NT == 0 || v < WV) *(u32x4_t*)&sW[buf][(v >> 3) * LDK + (v & 7) * 8] = rw[i];
+    }
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  if (kb < ke) {
+    gload(kb);
+    sstore(0);
+  }
+  __syncthreads();
+  int it = 0;
+  for (int k0 = kb; k0 < ke; k0 += BK, ++it) {
+    const int buf = it & 1;
+    const bool more = k0 + BK < ke;
+    if (more) gload(k0 + BK);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8_t af[TM], wf[TN];
+      const int koff = kk * 16 + (lane >> 5) * 8;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = as_bf16x8(*(const u32x4_t*)&sA[buf][((wm * TM + i) * 32 + (lane & 31)) * LDK + koff]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        wf[j] = as_bf16x8(*(const u32x4_t*)&sW[buf][((wn * TN + j) * 32 + (lane & 31)) * LDK + koff]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(af[i], wf[j], acc[i][j]);
+    }
+    if (more) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  const bool partial = gridDim.y > 1 || p.epi.kind == EPI_PARTIAL;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + (wn * TN + j) * 32 + (lane & 31);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + (wm * TM + i) * 32 + mfma32_row(e, lane);
+        const float v = acc[i][j][e];
+        if (partial) {
+          if (m < p.M && n < p.N) p.ws[((long)blockIdx.y * p.M + m) * p.N + n] = v;
+        } else if (p.epi.kind == EPI_GEGLU) {
+          const float other = __shfl_xor(v, 16, 64);
+          if (!(lane & 16) && m < p.M && n < p.N) epi_geglu(p.epi, m, (n >> 5) * 16 + (lane & 15), v, other);
+        } else if (m < p.M && n < p.N) {
+          epi_store(p.epi, m, n, v);
+        }
+      }
+    }
+  }
+}
+
+// Fixed-order sum of split-K partials followed by the epilogue.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* ws, int splits, int M, int N, Epilogue e) {
+  const long total = (e.kind == EPI_GEGLU) ? (long)M * (N / 2) : (long)M * N;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total; i += (long)gridDim.x * blockDim.x) {
+    if (e.kind == EPI_GEGLU) {
+      const int F = N / 2;
+      const int m = (int)(i / F), f = (int)(i % F);
+      const int ng = (f >> 4) * 32 + (f & 15), nu = ng + 16;
+      float g = 0.f, u = 0.f;
+      for (int s = 0; s < splits; ++s) {
+        g += ws[((long)s * M + m) * N + ng];
+        u += ws[((long)s * M + m) * N + nu];
+      }
+      epi_geglu(e, m, f, g, u);
+    } else {
+      const int m = (int)(i / N), n = (int)(i % N);
+      float v = 0.f;
+      for (int s = 0; s < splits; ++s) v += ws[((long)s * M + m) * N + n];
+      epi_store(e, m, n, v);
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+static hipError_t launch_bf16(const GemmP& p, int splits, hipStream_t s) {
+  GemmP q = p;
+  q.nM = (p.M + BM - 1) / BM;
+  q.nN = (p.N + BN - 1) / BN;
+  const int slices = p.K / 64;
+  const int per = (slices + splits - 1) / splits;
+  q.kchunk = per * 64;
+  const int used = (slices + per - 1) / per;
+  dim3 grid(q.nM * q.nN, used);
+  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN>), grid, dim3(64 * WM * WN), 0, s, q);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (used > 1 && p.epi.kind != EPI_PARTIAL) {
+    const long total = (long)p.M * p.N;
+    const int blocks = (int)std::min<long>((total + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, (const float*)p.ws, used, p.M, p.N, p.epi);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+int gemm_bf16_splits(int K, int splits) {
+  const int slices = K / 64;
+  if (slices <= 0) return 1;
+  splits = std::max(1, std::min(splits, slices));
+  const int per = (slices + splits - 1) / splits;
+  return (slices + per - 1) / per;
+}
+
+hipError_t gemm_bf16(const uint16_t* A, int lda, const uint16_t* W, int ldw, int M, int N, int K,
+                     const Epilogue& epi, int splits, float* ws, hipStream_t s) {
+  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  if (K % 64 || N % 32) return hipErrorInvalidValue;
+  if (splits < 1) splits = 1;
+  if (splits > K / 64) splits = K / 64;
+  GemmP p{A, lda, W, ldw, M, N, K, 0, 0, 0, epi, ws};
+  if ((splits > 1 || epi.kind == EPI_PARTIAL) && !ws) return hipErrorInvalidValue;
+  // Tile choice: skinny row counts (the action chunk) take 64-row tiles, the
+  // prefix (hundreds of rows) 96 x 128 tiles, four waves of 96 x 32.
+  if (M <= 64) return launch_bf16<64, 64, 2, 2>(p, splits, s);
+  return launch_bf16<96, 128, 1, 4>(p, splits, s);
+}
+
+// ------------------------------------------------------------------ fp32 SIMT
+__global__ __launch_bounds__(256) void k_gemm_f32(const float* A, int lda, const float* W, int ldw, int M, int N,
+                                                  int K, Epilogue e) {
+  __shared__ float sA[16][64 + 4], sW[16][64 + 4];
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int el = threadIdx.x + i * 256, r = el >> 4, c = el & 15;
+      sA[c][r] = (m0 + r < M) ? A[(long)(m0 + r) * lda + k0 + c] : 0.f;
+      sW[c][r] = (n0 + r < N) ? W[(long)(n0 + r) * ldw + k0 + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = sA[kk][ty * 4 + i];
+        w[i] = sW[kk][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], w[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (e.kind == EPI_GEGLU) {
+        // columns 16 apart pair up: thread tx holds 4 columns, its partner is tx ^ 4
+        const float other = __shfl_xor(acc[i][j], 4, 64);
+        if (!(tx & 4) && m < M && n < N) epi_geglu(e, m, (n >> 5) * 16 + (n & 15), acc[i][j], other);
+      } else if (m < M && n < N) {
+        epi_store(e, m, n, acc[i][j]);
+      }
+    }
+  }
+}
+
+hipError_t gemm_f32(const float* A, int lda, const float* W, int ldw, int M, int N, int K, const Epilogue& epi,
+                    hipStream_t s) {
+  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  if (K % 16 || (epi.kind == EPI_GEGLU && N % 32)) return hipErrorInvalidValue;
+  dim3 grid((N + 63) / 64, (M + 63) / 64);
+  hipLaunchKernelGGL(k_gemm_f32, grid, dim3(256), 0, s, A, lda, W, ldw, M, N, K, epi);
+  return hipGetLastError();
+}
+
+}  // namespace vla

@@ -1,0 +1,106 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vla {
+
+// ------------------------------------------------------------------ epilogues
+// What a GEMM does with its fp32 result v at (m, n).
+enum EpiKind {
+  EPI_STORE = 0,  // out[m * ldo + n] = v                       (bf16 or fp32)
+  EPI_RESID = 1,  // resid[m * ldr + n] += v                     (fp32 residual)
+  EPI_GEGLU = 2,  // gate/up rows interleaved in blocks of 16: column n = 32 b + i is
+                  // gate feature 16 b + i for i < 16, up feature 16 b + i - 16 otherwise;
+                  // out[m * ldo + f] = GELU(gate_f) * up_f     (bf16 or fp32)
+  EPI_CACHE = 3,  // K/V cache scatter: row m = (b, t) with b = m / npre, t = m % npre;
+                  // column n = ((l * 2 + kv) * hkv + h) * hd + d;
+                  // out[((((b * L + l) * 2 + kv) * hkv + h) * npre + t) * hd + d] = v
+  EPI_PARTIAL = 4 // raw fp32 partial sums to ws[split][m][n], left for a row kernel
+};
+
+struct Epilogue {
+  int kind = EPI_STORE;
+  void* out = nullptr;
+  int ldo = 0;
+  int out_f32 = 0;       // 1: fp32 output, 0: bf16
+  float* resid = nullptr;
+  int ldr = 0;
+  int npre = 0, L = 0, hkv = 0, hd = 0;  // EPI_CACHE
+  // W2A8 output scaling: y = bf16(float(acc) * (alpha[m] * beta[n])) before the epilogue
+  const float* alpha = nullptr;
+  const float* beta = nullptr;
+  int32_t* acc_out = nullptr;  // optional raw int32 accumulators [M][N]
+};
+
+// C = A[M,K] W[N,K]^T, bf16 operands, fp32 accumulation on MFMA; `splits` > 1
+// splits K and reduces the partial sums in a fixed order in `ws`
+// (splits * M * N floats).  K % 64 == 0, N % 32 == 0.
+hipError_t gemm_bf16(const uint16_t* A, int lda, const uint16_t* W, int ldw, int M, int N, int K,
+                     const Epilogue& epi, int splits, float* ws, hipStream_t s);
+
+// Number of K splits gemm_bf16 actually uses for a request of `splits`.
+int gemm_bf16_splits(int K, int splits);
+
+// Same contraction in fp32 on the vector ALU (fp32 workloads); K % 16 == 0.
+hipError_t gemm_f32(const float* A, int lda, const float* W, int ldw, int M, int N, int K,
+                    const Epilogue& epi, hipStream_t s);
+
+// Ternary W2A8: acc = a[M,K] q[N,K]^T in int32 on int8 MFMA, q in the library's
+// packed layout (see w2a8.hip); y = bf16(float(acc) * alpha[m] * beta[n]) into the
+// epilogue (epi.alpha / epi.beta must be set).  K % 128 == 0, N % 32 == 0.
+hipError_t gemm_w2a8(const int8_t* a, int lda, const uint32_t* qp, int M, int N, int K,
+                     const Epilogue& epi, hipStream_t s);
+
+// Same with one scale beta for every output channel (epi.beta ignored).
+hipError_t gemm_w2a8_scalar(const int8_t* a, int lda, const uint32_t* qp, int M, int N, int K,
+                            const Epilogue& epi, float beta_scalar, hipStream_t s);
+
+// Canonical packed ternary [N][K/4] bytes -> library layout; flags[0] |= 1 on a code 3.
+hipError_t ternary_repack(const uint8_t* canon, int N, int K, uint32_t* out, int* flags, hipStream_t s);
+
+// ------------------------------------------------------------------ row kernels
+// Row-wise residual update and RMSNorm: for each row m,
+//   h[m] += sum_s part[s][m]           (if nsplit > 0; part is [nsplit][M][N] fp32)
+//   u = h[m] / sqrt(mean(h[m]^2) + eps) * (1 + gain)
+// and u is written as bf16 / fp32 (u_out), or quantized per Eq. 4 to int8 codes
+// (q_out) with its scale (alpha_out).  Any of the outputs may be null.
+hipError_t resid_norm(float* h, int ldh, const float* part, int nsplit, int M, int N,
+                      const float* gain, float eps, void* u_out, int u_f32, int ldu,
+                      int8_t* q_out, float* alpha_out, hipStream_t s);
+
+// Eq. 4 per-row quantization of fp32 rows (x: [M][ldx], K valid columns).
+hipError_t quantize_rows(const float* x, int ldx, int M, int K, int8_t* a, float* alpha, hipStream_t s);
+
+// ------------------------------------------------------------------ attention
+struct AttnArgs {
+  const void* q; long q_bs, q_hs, q_rs;   // element strides: batch, head, row
+  const void* k; long k_bs, k_hs, k_rs;
+  const void* v; long v_bs, v_hs, v_rs;
+  void* o; long o_bs, o_rs;               // output head j at column j * hd
+  int B, Nq, Nk, Hq, Hkv, hd;
+  int o_f32;                              // 1: fp32 output, 0: bf16
+};
+// softmax(Q K^T / sqrt(hd)) V per head, no mask; bf16 inputs on MFMA (hd in 64..256)
+hipError_t attention_bf16(const AttnArgs& a, hipStream_t s);
+// fp32 inputs on the vector ALU (small shapes)
+hipError_t attention_f32(const AttnArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------------ expert pieces
+// E[m] = X[m] W_in^T + phi(tau_k) for the chunk rows, then u = RMS(E[m]; gain).
+hipError_t expert_embed(const float* X, int M, int d_a, const void* w_in, int w_f32, int d_e,
+                        const float* sched, int k, float* E, const float* gain, float eps,
+                        void* u, int u_f32, hipStream_t s);
+// v = RMS(E[m]; gain) W_out^T; X[m] += (tau_{k+1} - tau_k) v
+hipError_t expert_head(const float* E, int M, int d_e, const float* gain, float eps,
+                       const void* w_out, int w_f32, int d_a, const float* sched, int k, float* X,
+                       hipStream_t s);
+// dst = src (fp32), or bf16(src) when out_bf16
+hipError_t copy_out(const float* src, void* dst, long n, int out_bf16, hipStream_t s);
+hipError_t copy_f32(const float* src, float* dst, long n, hipStream_t s);
+// fp32 -> bf16 conversion of a weight tensor
+hipError_t f32_to_bf16(const float* src, uint16_t* dst, long n, hipStream_t s);
+
+}  // namespace vla

@@ -1,0 +1,138 @@
+// Row kernels: residual update + RMSNorm, and the per-row int8 quantizer of the
+// paper's §III-D, Eq. 4.
+//
+// RMSNorm (the pages do not define the norm; the plainest reading is a pre-norm
+// RMSNorm before every sublayer): u = x / sqrt(mean(x^2) + eps) * (1 + w).
+// The residual kernel also folds in the split-K partial sums of the projection
+// that feeds the residual stream, in a fixed order, so the stream update is
+// deterministic.  One 256-thread workgroup per row; a row stays in registers.
+//
+// Eq. 4: alpha = max(||x||_inf, 1e-5) / 127 in fp32, a = clip(rint(x / alpha),
+// -128, 127).  Both divisions are IEEE-rounded fp32 divisions (this library is
+// never built with fast-math) and rint rounds ties to even.
+#include "common.h"
+#include "kernels.h"
+
+namespace vla {
+
+__device__ __forceinline__ void quantize_store(const float* x, int per, int N, int8_t* q, float* alpha_out,
+                                               float* red) {
+  float am = 0.f;
+  for (int i = 0; i < per; ++i) {
+    const int n = threadIdx.x + i * 256;
+    if (n < N) am = fmaxf(am, fabsf(x[i]));
+  }
+  am = block_max<256>(am, red);
+  const float alpha = fmaxf(am, 1e-5f) / 127.0f;
+  for (int i = 0; i < per; ++i) {
+    const int n = threadIdx.x + i * 256;
+    if (n < N) {
+      const float c = rintf(x[i] / alpha);
+      q[n] = (int8_t)fminf(fmaxf(c, -128.f), 127.f);
+    }
+  }
+  if (threadIdx.x == 0) *alpha_out = alpha;
+}
+
+template <int PER>
+__global__ __launch_bounds__(256) void k_resid_norm(float* h, int ldh, const float* part, int nsplit, int M, int N,
+                                                    const float* gain, float eps, void* u, int u_f32, int ldu,
+                                                    int8_t* q, float* alpha) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  float x[PER];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int n = threadIdx.x + i * 256;
+    float v = 0.f;
+    if (n < N) {
+      v = h[(long)m * ldh + n];
+      for (int s = 0; s < nsplit; ++s) v += part[((long)s * M + m) * N + n];
+      if (nsplit > 0) h[(long)m * ldh + n] = v;
+    }
+    x[i] = v;
+    ss = fmaf(v, v, ss);
+  }
+  ss = block_sum<256>(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)N + eps);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int n = threadIdx.x + i * 256;
+    if (n < N) x[i] = x[i] * r * (1.0f + gain[n]);
+  }
+  if (u) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int n = threadIdx.x + i * 256;
+      if (n < N) {
+        if (u_f32) ((float*)u)[(long)m * ldu + n] = x[i];
+        else ((bf16_t*)u)[(long)m * ldu + n] = f2bf(x[i]);
+      }
+    }
+  }
+  if (q) quantize_store(x, PER, N, q + (long)m * N, alpha + m, red);
+}
+
+hipError_t resid_norm(float* h, int ldh, const float* part, int nsplit, int M, int N, const float* gain, float eps,
+                      void* u_out, int u_f32, int ldu, int8_t* q_out, float* alpha_out, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  const int per = (N + 255) / 256;
+#define VLA_RN(P)                                                                                          \
+  hipLaunchKernelGGL(k_resid_norm<P>, dim3(M), dim3(256), 0, s, h, ldh, part, nsplit, M, N, gain, eps, u_out, \
+                     u_f32, ldu, q_out, alpha_out)
+  if (per <= 1) VLA_RN(1);
+  else if (per <= 2) VLA_RN(2);
+  else if (per <= 4) VLA_RN(4);
+  else if (per <= 8) VLA_RN(8);
+  else if (per <= 12) VLA_RN(12);
+  else if (per <= 16) VLA_RN(16);
+  else return hipErrorInvalidValue;
+#undef VLA_RN
+  return hipGetLastError();
+}
+
+template <int PER>
+__global__ __launch_bounds__(256) void k_quantize(const float* x, int ldx, int K, int8_t* a, float* alpha) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  float v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int n = threadIdx.x + i * 256;
+    v[i] = n < K ? x[(long)m * ldx + n] : 0.f;
+  }
+  quantize_store(v, PER, K, a + (long)m * K, alpha + m, red);
+}
+
+// Rows longer than 16 * 256 elements go through a two-pass loop over global memory.
+__global__ __launch_bounds__(256) void k_quantize_long(const float* x, int ldx, int K, int8_t* a, float* alpha) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  const float* row = x + (long)m * ldx;
+  float am = 0.f;
+  for (int n = threadIdx.x; n < K; n += 256) am = fmaxf(am, fabsf(row[n]));
+  am = block_max<256>(am, red);
+  const float al = fmaxf(am, 1e-5f) / 127.0f;
+  for (int n = threadIdx.x; n < K; n += 256) {
+    const float c = rintf(row[n] / al);
+    a[(long)m * K + n] = (int8_t)fminf(fmaxf(c, -128.f), 127.f);
+  }
+  if (threadIdx.x == 0) alpha[m] = al;
+}
+
+hipError_t quantize_rows(const float* x, int ldx, int M, int K, int8_t* a, float* alpha, hipStream_t s) {
+  if (M <= 0 || K <= 0) return hipSuccess;
+  const int per = (K + 255) / 256;
+#define VLA_Q(P) hipLaunchKernelGGL(k_quantize<P>, dim3(M), dim3(256), 0, s, x, ldx, K, a, alpha)
+  if (per <= 1) VLA_Q(1);
+  else if (per <= 4) VLA_Q(4);
+  else if (per <= 8) VLA_Q(8);
+  else if (per <= 16) VLA_Q(16);
+  else if (per <= 28) VLA_Q(28);
+  else hipLaunchKernelGGL(k_quantize_long, dim3(M), dim3(256), 0, s, x, ldx, K, a, alpha);
+#undef VLA_Q
+  return hipGetLastError();
+}
+
+}  // namespace vla

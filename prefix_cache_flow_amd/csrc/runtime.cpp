@@ -1,0 +1,1022 @@
+// C ABI of the policy step (include/vla.h): handles, validation, weight layout,
+// workspace planning, the prefix and solver sequences, and the per-shape HIP
+// graph cache of the solver loop.
+//
+// The paper (vla.cpp, arXiv 2606.08094, §III-B) keeps the observation's cached
+// conditioning for the solver steps of one request, refreshes it on each new
+// observation, and keeps graphs and buffers for unchanged shapes across
+// requests; here a K/V cache handle is the conditioning of one encode call, the
+// model owns a workspace that grows to the largest shape seen, and the solver
+// loop is captured once per (cache storage, batch, prefix length, steps) and
+// replayed.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <set>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/vla.h"
+#include "kernels.h"
+
+using namespace vla;
+
+// ============================================================== errors
+static thread_local std::string g_last_error;
+
+static vla_status fail(vla_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+#define HIP_TRY(expr)                                                                                   \
+  do {                                                                                                  \
+    hipError_t e_ = (expr);                                                                             \
+    if (e_ != hipSuccess)                                                                               \
+      return fail(e_ == hipErrorOutOfMemory ? VLA_ERR_OUT_OF_MEMORY : VLA_ERR_DEVICE,                    \
+                  std::string(#expr) + ": " + hipGetErrorString(e_));                                   \
+  } while (0)
+
+extern "C" const char* vla_status_string(vla_status s) {
+  switch (s) {
+    case VLA_OK: return "VLA_OK";
+    case VLA_ERR_INVALID_ARGUMENT: return "VLA_ERR_INVALID_ARGUMENT";
+    case VLA_ERR_SHAPE_MISMATCH: return "VLA_ERR_SHAPE_MISMATCH";
+    case VLA_ERR_INVALID_HANDLE: return "VLA_ERR_INVALID_HANDLE";
+    case VLA_ERR_UNSUPPORTED: return "VLA_ERR_UNSUPPORTED";
+    case VLA_ERR_OUT_OF_MEMORY: return "VLA_ERR_OUT_OF_MEMORY";
+    case VLA_ERR_DEVICE: return "VLA_ERR_DEVICE";
+  }
+  return "VLA_ERR_UNKNOWN";
+}
+
+extern "C" const char* vla_last_error(void) { return g_last_error.c_str(); }
+
+// ============================================================== config
+static bool pos(int v) { return v > 0; }
+
+static vla_status check_config(const vla_model_config* c) {
+  if (!c) return fail(VLA_ERR_INVALID_ARGUMENT, "config is NULL");
+  if (c->abi_version != VLA_ABI_VERSION) return fail(VLA_ERR_UNSUPPORTED, "abi_version mismatch");
+  if (c->precision < VLA_F32 || c->precision > VLA_W2A8_BF16) return fail(VLA_ERR_INVALID_ARGUMENT, "bad precision");
+  const int v[] = {c->d_p, c->L_p, c->Hq, c->Hkv, c->hd, c->F_p, c->d_e, c->L_e, c->Hq_e, c->Hkv_e, c->hd_e, c->F_e, c->H, c->d_a};
+  for (int x : v)
+    if (!pos(x)) return fail(VLA_ERR_INVALID_ARGUMENT, "every model dimension must be positive");
+  if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps)) return fail(VLA_ERR_INVALID_ARGUMENT, "rms_eps must be >= 0");
+  if (c->Hq % c->Hkv || c->Hq_e % c->Hkv_e) return fail(VLA_ERR_UNSUPPORTED, "query heads must be a multiple of kv heads");
+  if (c->d_a > 256) return fail(VLA_ERR_UNSUPPORTED, "d_a > 256");
+  if (c->precision == VLA_F32) {
+    if ((c->hd != 32 && c->hd != 64) || (c->hd_e != 32 && c->hd_e != 64))
+      return fail(VLA_ERR_UNSUPPORTED, "fp32 models need head widths 32 or 64");
+    if (c->d_p % 16 || c->d_e % 16 || c->F_p % 16 || c->F_e % 16 || (c->Hq * c->hd) % 16 || (c->Hq_e * c->hd_e) % 16)
+      return fail(VLA_ERR_UNSUPPORTED, "fp32 model widths must be multiples of 16");
+  } else {
+    auto hd_ok = [](int h) { return h == 64 || h == 128 || h == 256; };
+    if (!hd_ok(c->hd) || !hd_ok(c->hd_e)) return fail(VLA_ERR_UNSUPPORTED, "head widths must be 64, 128 or 256");
+    if (c->d_p % 64 || c->d_e % 64 || c->F_p % 64 || c->F_e % 64)
+      return fail(VLA_ERR_UNSUPPORTED, "model widths must be multiples of 64");
+    if (c->d_e > 4096) return fail(VLA_ERR_UNSUPPORTED, "d_e > 4096");
+    if (c->precision == VLA_W2A8_BF16 && (c->d_p % 128 || c->F_p % 128 || (c->Hq * c->hd) % 128))
+      return fail(VLA_ERR_UNSUPPORTED, "ternary prefix widths must be multiples of 128");
+  }
+  if (c->d_p > 16 * 256 * 4 || c->F_p > (1 << 20)) return fail(VLA_ERR_UNSUPPORTED, "model too wide");
+  return VLA_OK;
+}
+
+// Tensor order of the boundary: (rows, cols, kind) with kind 0 gain, 1 linear, 2 ternary.
+struct Spec {
+  int64_t rows, cols;
+  int kind;
+};
+
+static std::vector<Spec> specs(const vla_model_config* c) {
+  std::vector<Spec> s;
+  const int lp = c->precision == VLA_W2A8_BF16 ? 2 : 1;
+  auto lin_p = [&](int64_t r, int64_t k) { s.push_back({r, lp == 2 ? k / 4 : k, lp}); };
+  const int64_t qw = (int64_t)c->Hq * c->hd, kvw = (int64_t)c->Hkv * c->hd;
+  const int64_t qe = (int64_t)c->Hq_e * c->hd_e, kve = (int64_t)c->Hkv_e * c->hd_e;
+  for (int l = 0; l < c->L_p; ++l) {
+    s.push_back({c->d_p, 1, 0});
+    lin_p(qw, c->d_p);
+    lin_p(kvw, c->d_p);
+    lin_p(kvw, c->d_p);
+    lin_p(c->d_p, qw);
+    s.push_back({c->d_p, 1, 0});
+    lin_p(c->F_p, c->d_p);
+    lin_p(c->F_p, c->d_p);
+    lin_p(c->d_p, c->F_p);
+  }
+  s.push_back({c->d_p, 1, 0});
+  for (int e = 0; e < c->L_e; ++e) {
+    s.push_back({kve, c->d_p, 1});
+    s.push_back({kve, c->d_p, 1});
+  }
+  s.push_back({c->d_e, c->d_a, 1});
+  for (int e = 0; e < c->L_e; ++e) {
+    s.push_back({c->d_e, 1, 0});
+    s.push_back({qe, c->d_e, 1});
+    s.push_back({kve, c->d_e, 1});
+    s.push_back({kve, c->d_e, 1});
+    s.push_back({c->d_e, qe, 1});
+    s.push_back({c->d_e, 1, 0});
+    s.push_back({qe, c->d_e, 1});
+    s.push_back({c->d_e, qe, 1});
+    s.push_back({c->d_e, 1, 0});
+    s.push_back({c->F_e, c->d_e, 1});
+    s.push_back({c->F_e, c->d_e, 1});
+    s.push_back({c->d_e, c->F_e, 1});
+  }
+  s.push_back({c->d_e, 1, 0});
+  s.push_back({c->d_a, c->d_e, 1});
+  return s;
+}
+
+extern "C" int32_t vla_n_tensors(const vla_model_config* cfg) {
+  if (check_config(cfg) != VLA_OK) return -1;
+  return (int32_t)specs(cfg).size();
+}
+
+extern "C" vla_status vla_tensor_info(const vla_model_config* cfg, int32_t index, int64_t* rows, int64_t* cols,
+                                      int32_t* kind) {
+  vla_status st = check_config(cfg);
+  if (st != VLA_OK) return st;
+  auto s = specs(cfg);
+  if (index < 0 || index >= (int32_t)s.size()) return fail(VLA_ERR_INVALID_ARGUMENT, "tensor index out of range");
+  if (rows) *rows = s[index].rows;
+  if (cols) *cols = s[index].cols;
+  if (kind) *kind = s[index].kind;
+  return VLA_OK;
+}
+
+// ============================================================== model
+static const uint32_t MODEL_MAGIC = 0x564c414du;  // "VLAM"
+static const uint32_t CACHE_MAGIC = 0x564c414bu;  // "VLAK"
+
+struct PrefixLayer {
+  float* w1 = nullptr;
+  float* w2 = nullptr;
+  void* wqkv = nullptr;  // [(Hq + 2 Hkv) hd][d_p]   bf16 / fp32 / packed words
+  void* wo = nullptr;    // [d_p][Hq hd]
+  void* wgu = nullptr;   // [2 F_p][d_p], gate/up interleaved in blocks of 16 rows
+  void* wd = nullptr;    // [d_p][F_p]
+  float *bqkv = nullptr, *bo = nullptr, *bgu = nullptr, *bd = nullptr;  // ternary scales per output row
+};
+
+struct ExpertLayer {
+  float *a1 = nullptr, *a2 = nullptr, *a3 = nullptr;
+  void* wqkv = nullptr;  // [(Hq_e + 2 Hkv_e) hd_e][d_e]
+  void* wos = nullptr;   // [d_e][Hq_e hd_e]
+  void* wqc = nullptr;   // [Hq_e hd_e][d_e]
+  void* woc = nullptr;   // [d_e][Hq_e hd_e]
+  void* wgu = nullptr;   // [2 F_e][d_e] interleaved
+  void* wd = nullptr;    // [d_e][F_e]
+};
+
+struct GraphKey {
+  const void* kv;
+  int B, N, steps;
+  bool operator<(const GraphKey& o) const { return std::tie(kv, B, N, steps) < std::tie(o.kv, o.B, o.N, o.steps); }
+};
+
+struct vla_model {
+  uint32_t magic = MODEL_MAGIC;
+  vla_model_config cfg{};
+  int device = 0;
+  bool f32 = false, w2a8 = false;
+  std::vector<void*> allocs;  // every device allocation of weights
+  std::vector<PrefixLayer> pl;
+  std::vector<ExpertLayer> el;
+  float* w_pf = nullptr;
+  void* wcache = nullptr;  // [L_e 2 Hkv_e hd_e][d_p]
+  void* w_in = nullptr;
+  float* w_ef = nullptr;
+  void* w_out = nullptr;
+  // workspace
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  float* sched_dev = nullptr;  // [max_steps + 1]
+  float* sched_host = nullptr; // pinned staging
+  int sched_cap = 0;
+  hipStream_t cap_stream = nullptr;
+  std::map<GraphKey, hipGraphExec_t> graphs;
+  std::set<vla_kv_cache*> caches;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  int64_t plan_rows = 0, plan_erows = 0;  // largest prefix / chunk row counts seen
+};
+
+struct vla_kv_cache {
+  uint32_t magic = CACHE_MAGIC;
+  vla_model* model = nullptr;
+  int B = 0, N = 0;
+  void* storage = nullptr;
+};
+
+static std::mutex g_mu;
+static std::set<vla_model*> g_models;
+
+static bool live_model(const vla_model* m) {
+  std::lock_guard<std::mutex> g(g_mu);
+  return m && g_models.count(const_cast<vla_model*>(m)) && m->magic == MODEL_MAGIC;
+}
+
+static bool live_cache(const vla_kv_cache* k) {
+  if (!k) return false;
+  std::lock_guard<std::mutex> g(g_mu);
+  for (vla_model* m : g_models)
+    if (m->caches.count(const_cast<vla_kv_cache*>(k))) return k->magic == CACHE_MAGIC;
+  return false;
+}
+
+static vla_status check_device() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return fail(VLA_ERR_DEVICE, "no HIP device");
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(VLA_ERR_DEVICE, "hipGetDevice failed");
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, dev) != hipSuccess) return fail(VLA_ERR_DEVICE, "hipGetDeviceProperties failed");
+  if (strncmp(p.gcnArchName, "gfx950", 6) != 0)
+    return fail(VLA_ERR_DEVICE, std::string("this library is built for gfx950, device is ") + p.gcnArchName);
+  return VLA_OK;
+}
+
+static size_t elt(const vla_model* m) { return m->f32 ? 4 : 2; }
+
+static vla_status dev_alloc(vla_model* m, void** p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) bytes = 16;
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(VLA_ERR_OUT_OF_MEMORY, "hipMalloc of " + std::to_string(bytes) + " bytes failed");
+  }
+  m->allocs.push_back(*p);
+  return VLA_OK;
+}
+
+static void free_model(vla_model* m) {
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  m->graphs.clear();
+  for (void* p : m->allocs) (void)hipFree(p);
+  m->allocs.clear();
+  if (m->ws) (void)hipFree(m->ws);
+  if (m->sched_dev) (void)hipFree(m->sched_dev);
+  if (m->sched_host) (void)hipHostFree(m->sched_host);
+  if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
+  if (m->ev0) (void)hipEventDestroy(m->ev0);
+  if (m->ev1) (void)hipEventDestroy(m->ev1);
+  m->magic = 0;
+  delete m;
+}
+
+// ---- weight copy helpers (all on `s`)
+struct Src {
+  const void* const* t;
+  int i = 0;
+  const float* beta;
+  int bi = 0;
+};
+
+// copy rows of a linear weight, converting fp32 -> bf16 is never needed (the
+// caller gives the precision's own type), into dst at row offset `row0`
+static vla_status put_rows(vla_model* m, void* dst, int64_t row0, const void* src, int64_t rows, int64_t cols,
+                           hipStream_t s) {
+  const size_t es = elt(m);
+  HIP_TRY(hipMemcpyAsync((char*)dst + row0 * cols * es, src, rows * cols * es, hipMemcpyDeviceToDevice, s));
+  return VLA_OK;
+}
+
+// interleave gate and up [F][cols] into [2F][cols] in blocks of 16 rows
+static vla_status put_interleaved(void* dst, const void* g, const void* u, int64_t F, size_t row_bytes, hipStream_t s) {
+  const size_t blk = 16 * row_bytes;
+  HIP_TRY(hipMemcpy2DAsync(dst, 2 * blk, g, blk, blk, F / 16, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(hipMemcpy2DAsync((char*)dst + blk, 2 * blk, u, blk, blk, F / 16, hipMemcpyDeviceToDevice, s));
+  return VLA_OK;
+}
+
+static vla_status put_gain(vla_model* m, float** dst, const void* src, int64_t n, hipStream_t s) {
+  vla_status st = dev_alloc(m, (void**)dst, n * 4);
+  if (st != VLA_OK) return st;
+  HIP_TRY(hipMemcpyAsync(*dst, src, n * 4, hipMemcpyDeviceToDevice, s));
+  return VLA_OK;
+}
+
+// ternary: canonical bytes -> library words at row offset (rows of K/16 words)
+static vla_status put_ternary(uint32_t* dst, int64_t row0, const void* src, int64_t rows, int64_t K, int* flags,
+                              hipStream_t s) {
+  HIP_TRY(ternary_repack((const uint8_t*)src, (int)rows, (int)K, dst + row0 * (K / 16), flags, s));
+  return VLA_OK;
+}
+
+static vla_status build_weights(vla_model* m, const vla_weights* w, hipStream_t s) {
+  const vla_model_config& c = m->cfg;
+  Src src{w->tensors, 0, w->ternary_beta, 0};
+  const size_t es = elt(m);
+  const int64_t qw = (int64_t)c.Hq * c.hd, kvw = (int64_t)c.Hkv * c.hd, qkvw = qw + 2 * kvw;
+  const int64_t qe = (int64_t)c.Hq_e * c.hd_e, kve = (int64_t)c.Hkv_e * c.hd_e, qkve = qe + 2 * kve;
+  vla_status st;
+  int* flags = nullptr;
+  std::vector<void*> temps;
+  auto cleanup = [&]() {
+    for (void* p : temps) (void)hipFree(p);
+  };
+  if (m->w2a8) {
+    if (hipMalloc(&flags, 64) != hipSuccess) return fail(VLA_ERR_OUT_OF_MEMORY, "flags");
+    temps.push_back(flags);
+    if (hipMemsetAsync(flags, 0, 64, s) != hipSuccess) { cleanup(); return fail(VLA_ERR_DEVICE, "memset"); }
+  }
+#define TRY(x)           \
+  do {                   \
+    st = (x);            \
+    if (st != VLA_OK) {  \
+      cleanup();         \
+      return st;         \
+    }                    \
+  } while (0)
+  m->pl.resize(c.L_p);
+  for (int l = 0; l < c.L_p; ++l) {
+    PrefixLayer& P = m->pl[l];
+    TRY(put_gain(m, &P.w1, src.t[src.i++], c.d_p, s));
+    const void* wq = src.t[src.i++];
+    const void* wk = src.t[src.i++];
+    const void* wv = src.t[src.i++];
+    const void* wo = src.t[src.i++];
+    TRY(put_gain(m, &P.w2, src.t[src.i++], c.d_p, s));
+    const void* wg = src.t[src.i++];
+    const void* wu = src.t[src.i++];
+    const void* wd = src.t[src.i++];
+    if (!m->w2a8) {
+      TRY(dev_alloc(m, &P.wqkv, qkvw * c.d_p * es));
+      TRY(put_rows(m, P.wqkv, 0, wq, qw, c.d_p, s));
+      TRY(put_rows(m, P.wqkv, qw, wk, kvw, c.d_p, s));
+      TRY(put_rows(m, P.wqkv, qw + kvw, wv, kvw, c.d_p, s));
+      TRY(dev_alloc(m, &P.wo, (int64_t)c.d_p * qw * es));
+      TRY(put_rows(m, P.wo, 0, wo, c.d_p, qw, s));
+      TRY(dev_alloc(m, &P.wgu, 2 * (int64_t)c.F_p * c.d_p * es));
+      TRY(put_interleaved(P.wgu, wg, wu, c.F_p, c.d_p * es, s));
+      TRY(dev_alloc(m, &P.wd, (int64_t)c.d_p * c.F_p * es));
+      TRY(put_rows(m, P.wd, 0, wd, c.d_p, c.F_p, s));
+    } else {
+      const float bq = src.beta[src.bi++], bk = src.beta[src.bi++], bv = src.beta[src.bi++], bo = src.beta[src.bi++];
+      const float bg = src.beta[src.bi++], bu = src.beta[src.bi++], bdn = src.beta[src.bi++];
+      TRY(dev_alloc(m, &P.wqkv, qkvw * c.d_p / 4));
+      TRY(put_ternary((uint32_t*)P.wqkv, 0, wq, qw, c.d_p, flags, s));
+      TRY(put_ternary((uint32_t*)P.wqkv, qw, wk, kvw, c.d_p, flags, s));
+      TRY(put_ternary((uint32_t*)P.wqkv, qw + kvw, wv, kvw, c.d_p, flags, s));
+      TRY(dev_alloc(m, &P.wo, (int64_t)c.d_p * qw / 4));
+      TRY(put_ternary((uint32_t*)P.wo, 0, wo, c.d_p, qw, flags, s));
+      // gate/up: repack each, then interleave the word rows
+      void *tg = nullptr, *tu = nullptr;
+      const int64_t gbytes = (int64_t)c.F_p * c.d_p / 4;
+      if (hipMalloc(&tg, gbytes) != hipSuccess || hipMalloc(&tu, gbytes) != hipSuccess) {
+        if (tg) (void)hipFree(tg);
+        cleanup();
+        return fail(VLA_ERR_OUT_OF_MEMORY, "ternary staging");
+      }
+      temps.push_back(tg);
+      temps.push_back(tu);
+      TRY(put_ternary((uint32_t*)tg, 0, wg, c.F_p, c.d_p, flags, s));
+      TRY(put_ternary((uint32_t*)tu, 0, wu, c.F_p, c.d_p, flags, s));
+      TRY(dev_alloc(m, &P.wgu, 2 * gbytes));
+      TRY(put_interleaved(P.wgu, tg, tu, c.F_p, c.d_p / 4, s));
+      TRY(dev_alloc(m, &P.wd, (int64_t)c.d_p * c.F_p / 4));
+      TRY(put_ternary((uint32_t*)P.wd, 0, wd, c.d_p, c.F_p, flags, s));
+      // per-output-row scales
+      std::vector<float> h;
+      auto put_beta = [&](float** dst, const std::vector<float>& v) -> vla_status {
+        vla_status r = dev_alloc(m, (void**)dst, v.size() * 4);
+        if (r != VLA_OK) return r;
+        if (hipMemcpy(*dst, v.data(), v.size() * 4, hipMemcpyHostToDevice) != hipSuccess)
+          return fail(VLA_ERR_DEVICE, "beta upload");
+        return VLA_OK;
+      };
+      h.assign(qkvw, bq);
+      std::fill(h.begin() + qw, h.begin() + qw + kvw, bk);
+      std::fill(h.begin() + qw + kvw, h.end(), bv);
+      TRY(put_beta(&P.bqkv, h));
+      h.assign(c.d_p, bo);
+      TRY(put_beta(&P.bo, h));
+      h.assign(2 * (int64_t)c.F_p, bg);
+      for (int64_t r = 0; r < 2 * (int64_t)c.F_p; ++r) h[r] = ((r / 16) & 1) ? bu : bg;
+      TRY(put_beta(&P.bgu, h));
+      h.assign(c.d_p, bdn);
+      TRY(put_beta(&P.bd, h));
+    }
+  }
+  TRY(put_gain(m, &m->w_pf, src.t[src.i++], c.d_p, s));
+  // expert prefix-side projections, concatenated in boundary order: [l][k|v][h][d]
+  TRY(dev_alloc(m, &m->wcache, (int64_t)c.L_e * 2 * kve * c.d_p * es));
+  for (int e = 0; e < c.L_e; ++e) {
+    TRY(put_rows(m, m->wcache, (int64_t)(2 * e) * kve, src.t[src.i++], kve, c.d_p, s));
+    TRY(put_rows(m, m->wcache, (int64_t)(2 * e + 1) * kve, src.t[src.i++], kve, c.d_p, s));
+  }
+  TRY(dev_alloc(m, &m->w_in, (int64_t)c.d_e * c.d_a * es));
+  TRY(put_rows(m, m->w_in, 0, src.t[src.i++], c.d_e, c.d_a, s));
+  m->el.resize(c.L_e);
+  for (int e = 0; e < c.L_e; ++e) {
+    ExpertLayer& E = m->el[e];
+    TRY(put_gain(m, &E.a1, src.t[src.i++], c.d_e, s));
+    const void* wqs = src.t[src.i++];
+    const void* wks = src.t[src.i++];
+    const void* wvs = src.t[src.i++];
+    TRY(dev_alloc(m, &E.wqkv, qkve * c.d_e * es));
+    TRY(put_rows(m, E.wqkv, 0, wqs, qe, c.d_e, s));
+    TRY(put_rows(m, E.wqkv, qe, wks, kve, c.d_e, s));
+    TRY(put_rows(m, E.wqkv, qe + kve, wvs, kve, c.d_e, s));
+    TRY(dev_alloc(m, &E.wos, (int64_t)c.d_e * qe * es));
+    TRY(put_rows(m, E.wos, 0, src.t[src.i++], c.d_e, qe, s));
+    TRY(put_gain(m, &E.a2, src.t[src.i++], c.d_e, s));
+    TRY(dev_alloc(m, &E.wqc, qe * c.d_e * es));
+    TRY(put_rows(m, E.wqc, 0, src.t[src.i++], qe, c.d_e, s));
+    TRY(dev_alloc(m, &E.woc, (int64_t)c.d_e * qe * es));
+    TRY(put_rows(m, E.woc, 0, src.t[src.i++], c.d_e, qe, s));
+    TRY(put_gain(m, &E.a3, src.t[src.i++], c.d_e, s));
+    const void* wg = src.t[src.i++];
+    const void* wu = src.t[src.i++];
+    TRY(dev_alloc(m, &E.wgu, 2 * (int64_t)c.F_e * c.d_e * es));
+    TRY(put_interleaved(E.wgu, wg, wu, c.F_e, c.d_e * es, s));
+    TRY(dev_alloc(m, &E.wd, (int64_t)c.d_e * c.F_e * es));
+    TRY(put_rows(m, E.wd, 0, src.t[src.i++], c.d_e, c.F_e, s));
+  }
+  TRY(put_gain(m, &m->w_ef, src.t[src.i++], c.d_e, s));
+  TRY(dev_alloc(m, &m->w_out, (int64_t)c.d_a * c.d_e * es));
+  TRY(put_rows(m, m->w_out, 0, src.t[src.i++], c.d_a, c.d_e, s));
+#undef TRY
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    cleanup();
+    return fail(VLA_ERR_DEVICE, std::string("weight copy: ") + hipGetErrorString(e));
+  }
+  if (flags) {
+    int hf = 0;
+    e = hipMemcpy(&hf, flags, 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess || hf) {
+      cleanup();
+      return fail(e != hipSuccess ? VLA_ERR_DEVICE : VLA_ERR_INVALID_ARGUMENT,
+                  e != hipSuccess ? "flag readback failed" : "ternary weights contain the invalid code 3");
+    }
+  }
+  cleanup();
+  return VLA_OK;
+}
+
+extern "C" vla_status vla_model_create(const vla_model_config* cfg, const vla_weights* weights, void* stream,
+                                       vla_model** out) {
+  if (!out) return fail(VLA_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  vla_status st = check_config(cfg);
+  if (st != VLA_OK) return st;
+  if (!weights || !weights->tensors) return fail(VLA_ERR_INVALID_ARGUMENT, "weights are NULL");
+  const int n = (int)specs(cfg).size();
+  if (weights->n_tensors != n)
+    return fail(VLA_ERR_SHAPE_MISMATCH, "expected " + std::to_string(n) + " weight tensors, got " +
+                                            std::to_string(weights->n_tensors));
+  for (int i = 0; i < n; ++i)
+    if (!weights->tensors[i]) return fail(VLA_ERR_INVALID_ARGUMENT, "weight tensor " + std::to_string(i) + " is NULL");
+  if (cfg->precision == VLA_W2A8_BF16) {
+    if (!weights->ternary_beta) return fail(VLA_ERR_INVALID_ARGUMENT, "ternary_beta is NULL");
+    for (int i = 0; i < 7 * cfg->L_p; ++i)
+      if (!std::isfinite(weights->ternary_beta[i])) return fail(VLA_ERR_INVALID_ARGUMENT, "non-finite ternary beta");
+  }
+  st = check_device();
+  if (st != VLA_OK) return st;
+  vla_model* m = new vla_model();
+  m->cfg = *cfg;
+  m->f32 = cfg->precision == VLA_F32;
+  m->w2a8 = cfg->precision == VLA_W2A8_BF16;
+  (void)hipGetDevice(&m->device);
+  hipStream_t s = (hipStream_t)stream;
+  st = build_weights(m, weights, s);
+  if (st == VLA_OK && (hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking) != hipSuccess ||
+                       hipEventCreate(&m->ev0) != hipSuccess || hipEventCreate(&m->ev1) != hipSuccess))
+    st = fail(VLA_ERR_DEVICE, "stream/event creation failed");
+  if (st != VLA_OK) {
+    free_model(m);
+    return st;
+  }
+  {
+    std::lock_guard<std::mutex> g(g_mu);
+    g_models.insert(m);
+  }
+  *out = m;
+  return VLA_OK;
+}
+
+extern "C" vla_status vla_model_destroy(vla_model* m) {
+  {
+    std::lock_guard<std::mutex> g(g_mu);
+    if (!m || !g_models.count(m) || m->magic != MODEL_MAGIC) return fail(VLA_ERR_INVALID_HANDLE, "unknown model");
+    g_models.erase(m);
+  }
+  (void)hipDeviceSynchronize();
+  for (vla_kv_cache* k : m->caches) {
+    k->magic = 0;
+    delete k;
+  }
+  m->caches.clear();
+  free_model(m);
+  return VLA_OK;
+}
+
+// ============================================================== workspace
+// Byte layout of the model workspace for `rows` prefix tokens and `erows` chunk rows.
+struct WS {
+  float* h;         // prefix residual [rows][d_p]
+  void* u;          // normalized activations [rows][max(d_p, d_e)]
+  void* qkv;        // [rows][(Hq + 2 Hkv) hd]
+  void* attn;       // [rows][Hq hd]       (fp32 for the ternary prefix)
+  void* mlp;        // [rows][F_p]         (fp32 for the ternary prefix)
+  int8_t* qa;       // ternary: int8 codes [rows][max(d_p, Hq hd, F_p)]
+  float* alpha;     // ternary: [rows]
+  float* part;      // split-K partials
+  // expert
+  float* X;         // [erows][d_a]
+  float* E;         // [erows][d_e]
+  void* eu;         // [erows][d_e]
+  void* eqkv;       // [erows][(Hq_e + 2 Hkv_e) hd_e]
+  void* eq;         // [erows][Hq_e hd_e]
+  void* eattn;      // [erows][Hq_e hd_e]
+  void* emlp;       // [erows][F_e]
+  float* epart;     // split-K partials of the expert
+  size_t total;
+};
+
+static const int kPrefixSplits = 4;
+static const int kExpertSplits = 16;
+
+static WS plan(const vla_model* m, int64_t rows, int64_t erows, char* base) {
+  const vla_model_config& c = m->cfg;
+  const size_t es = elt(m);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off += (bytes + 255) / 256 * 256;
+    return p;
+  };
+  WS w{};
+  const int64_t qkvw = (int64_t)(c.Hq + 2 * c.Hkv) * c.hd, qw = (int64_t)c.Hq * c.hd;
+  const int64_t act_es = m->w2a8 ? 4 : es;  // ternary: fp32 attention / GeGLU outputs feed the quantizer
+  w.h = (float*)take(rows * c.d_p * 4);
+  w.u = take(rows * std::max<int64_t>(c.d_p, c.d_e) * es);
+  w.qkv = take(rows * qkvw * es);
+  w.attn = take(rows * qw * act_es);
+  w.mlp = take(rows * (int64_t)c.F_p * act_es);
+  if (m->w2a8) {
+    w.qa = (int8_t*)take(rows * std::max<int64_t>(std::max<int64_t>(c.d_p, qw), c.F_p));
+    w.alpha = (float*)take(rows * 4);
+  }
+  w.part = (float*)take((size_t)kPrefixSplits * rows * c.d_p * 4);
+  const int64_t qe = (int64_t)c.Hq_e * c.hd_e, qkve = (int64_t)(c.Hq_e + 2 * c.Hkv_e) * c.hd_e;
+  w.X = (float*)take(erows * c.d_a * 4);
+  w.E = (float*)take(erows * c.d_e * 4);
+  w.eu = take(erows * c.d_e * es);
+  w.eqkv = take(erows * qkve * es);
+  w.eq = take(erows * qe * es);
+  w.eattn = take(erows * qe * es);
+  w.emlp = take(erows * (int64_t)c.F_e * es);
+  // split partials: residual GEMMs [S][erows][d_e], other split GEMMs [S][erows][N]
+  const int64_t widest = std::max<int64_t>(std::max<int64_t>(qkve, 2 * (int64_t)c.F_e), c.d_e);
+  w.epart = (float*)take((size_t)kExpertSplits * erows * widest * 4);
+  w.total = off;
+  return w;
+}
+
+static vla_status ensure_ws(vla_model* m, int64_t rows, int64_t erows, WS* out) {
+  WS need = plan(m, rows, erows, nullptr);
+  if (need.total > m->ws_bytes) {
+    if (m->ws) {
+      hipError_t e = hipDeviceSynchronize();
+      if (e != hipSuccess) return fail(VLA_ERR_DEVICE, std::string("sync: ") + hipGetErrorString(e));
+      (void)hipFree(m->ws);
+      m->ws = nullptr;
+      m->ws_bytes = 0;
+      for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+      m->graphs.clear();
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, need.total) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(VLA_ERR_OUT_OF_MEMORY, "workspace allocation of " + std::to_string(need.total) + " bytes failed");
+    }
+    m->ws = (char*)p;
+    m->ws_bytes = need.total;
+  }
+  *out = plan(m, rows, erows, m->ws);
+  return VLA_OK;
+}
+
+// Encode plans prefix rows, denoise chunk rows; both share one arena sized for
+// the largest of each seen so far.
+static vla_status get_ws(vla_model* m, int64_t rows, int64_t erows, WS* out) {
+  m->plan_rows = std::max(m->plan_rows, rows);
+  m->plan_erows = std::max(m->plan_erows, erows);
+  return ensure_ws(m, m->plan_rows, m->plan_erows, out);
+}
+
+// ============================================================== prefix
+static vla_status hip_ok(hipError_t e, const char* what) {
+  if (e == hipSuccess) return VLA_OK;
+  return fail(e == hipErrorOutOfMemory ? VLA_ERR_OUT_OF_MEMORY : VLA_ERR_DEVICE,
+              std::string(what) + ": " + hipGetErrorString(e));
+}
+#define K_TRY(expr, what)                          \
+  do {                                             \
+    vla_status st_ = hip_ok((expr), what);         \
+    if (st_ != VLA_OK) return st_;                 \
+  } while (0)
+
+static Epilogue epi_store(void* out, int ldo, int out_f32) {
+  Epilogue e;
+  e.kind = EPI_STORE;
+  e.out = out;
+  e.ldo = ldo;
+  e.out_f32 = out_f32;
+  return e;
+}
+
+static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* kv, const WS& w, hipStream_t s) {
+  const vla_model_config& c = m->cfg;
+  const int M = B * N;
+  const int qw = c.Hq * c.hd, qkvw = (c.Hq + 2 * c.Hkv) * c.hd;
+  const float eps = c.rms_eps;
+  const int uf = m->f32 ? 1 : 0;
+  K_TRY(copy_f32(x, w.h, (long)M * c.d_p, s), "copy prefix");
+  AttnArgs aa{};
+  aa.q = w.qkv; aa.q_bs = (long)N * qkvw; aa.q_hs = c.hd; aa.q_rs = qkvw;
+  aa.k = (const char*)w.qkv + (size_t)qw * elt(m); aa.k_bs = aa.q_bs; aa.k_hs = c.hd; aa.k_rs = qkvw;
+  aa.v = (const char*)w.qkv + (size_t)(qw + c.Hkv * c.hd) * elt(m); aa.v_bs = aa.q_bs; aa.v_hs = c.hd; aa.v_rs = qkvw;
+  aa.o = w.attn; aa.o_bs = (long)N * qw; aa.o_rs = qw;
+  aa.B = B; aa.Nq = N; aa.Nk = N; aa.Hq = c.Hq; aa.Hkv = c.Hkv; aa.hd = c.hd;
+  aa.o_f32 = (m->f32 || m->w2a8) ? 1 : 0;
+
+  if (m->w2a8) {
+    K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, m->pl[0].w1, eps, nullptr, 0, 0, w.qa, w.alpha, s), "norm");
+    for (int l = 0; l < c.L_p; ++l) {
+      const PrefixLayer& P = m->pl[l];
+      Epilogue e = epi_store(w.qkv, qkvw, 0);
+      e.alpha = w.alpha; e.beta = P.bqkv;
+      K_TRY(gemm_w2a8(w.qa, c.d_p, (const uint32_t*)P.wqkv, M, qkvw, c.d_p, e, s), "qkv");
+      K_TRY(attention_bf16(aa, s), "attention");
+      K_TRY(quantize_rows((const float*)w.attn, qw, M, qw, w.qa, w.alpha, s), "quantize attn");
+      Epilogue r;
+      r.kind = EPI_RESID; r.resid = w.h; r.ldr = c.d_p; r.alpha = w.alpha; r.beta = P.bo;
+      K_TRY(gemm_w2a8(w.qa, qw, (const uint32_t*)P.wo, M, c.d_p, qw, r, s), "o proj");
+      K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, P.w2, eps, nullptr, 0, 0, w.qa, w.alpha, s), "norm");
+      Epilogue g;
+      g.kind = EPI_GEGLU; g.out = w.mlp; g.ldo = c.F_p; g.out_f32 = 1; g.alpha = w.alpha; g.beta = P.bgu;
+      K_TRY(gemm_w2a8(w.qa, c.d_p, (const uint32_t*)P.wgu, M, 2 * c.F_p, c.d_p, g, s), "gate/up");
+      K_TRY(quantize_rows((const float*)w.mlp, c.F_p, M, c.F_p, w.qa, w.alpha, s), "quantize mlp");
+      r.beta = P.bd;
+      K_TRY(gemm_w2a8(w.qa, c.F_p, (const uint32_t*)P.wd, M, c.d_p, c.F_p, r, s), "down");
+      if (l + 1 < c.L_p)
+        K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, m->pl[l + 1].w1, eps, nullptr, 0, 0, w.qa, w.alpha, s),
+              "norm");
+      else
+        K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, m->w_pf, eps, w.u, 0, c.d_p, nullptr, nullptr, s), "norm");
+    }
+  } else {
+    K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, m->pl[0].w1, eps, w.u, uf, c.d_p, nullptr, nullptr, s), "norm");
+    for (int l = 0; l < c.L_p; ++l) {
+      const PrefixLayer& P = m->pl[l];
+      const float* next_gain = l + 1 < c.L_p ? m->pl[l + 1].w1 : m->w_pf;
+      if (m->f32) {
+        K_TRY(gemm_f32((const float*)w.u, c.d_p, (const float*)P.wqkv, c.d_p, M, qkvw, c.d_p, epi_store(w.qkv, qkvw, 1), s), "qkv");
+        K_TRY(attention_f32(aa, s), "attention");
+        Epilogue r;
+        r.kind = EPI_RESID; r.resid = w.h; r.ldr = c.d_p;
+        K_TRY(gemm_f32((const float*)w.attn, qw, (const float*)P.wo, qw, M, c.d_p, qw, r, s), "o proj");
+        K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, P.w2, eps, w.u, 1, c.d_p, nullptr, nullptr, s), "norm");
+        Epilogue g = epi_store(w.mlp, c.F_p, 1);
+        g.kind = EPI_GEGLU;
+        K_TRY(gemm_f32((const float*)w.u, c.d_p, (const float*)P.wgu, c.d_p, M, 2 * c.F_p, c.d_p, g, s), "gate/up");
+        K_TRY(gemm_f32((const float*)w.mlp, c.F_p, (const float*)P.wd, c.F_p, M, c.d_p, c.F_p, r, s), "down");
+        K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, next_gain, eps, w.u, 1, c.d_p, nullptr, nullptr, s), "norm");
+      } else {
+        const uint16_t* u = (const uint16_t*)w.u;
+        K_TRY(gemm_bf16(u, c.d_p, (const uint16_t*)P.wqkv, c.d_p, M, qkvw, c.d_p, epi_store(w.qkv, qkvw, 0), 1, w.part, s), "qkv");
+        K_TRY(attention_bf16(aa, s), "attention");
+        Epilogue pe;
+        pe.kind = EPI_PARTIAL;
+        K_TRY(gemm_bf16((const uint16_t*)w.attn, qw, (const uint16_t*)P.wo, qw, M, c.d_p, qw, pe, kPrefixSplits, w.part, s), "o proj");
+        K_TRY(resid_norm(w.h, c.d_p, w.part, gemm_bf16_splits(qw, kPrefixSplits), M, c.d_p, P.w2, eps, w.u, 0, c.d_p, nullptr, nullptr, s), "norm");
+        Epilogue g = epi_store(w.mlp, c.F_p, 0);
+        g.kind = EPI_GEGLU;
+        K_TRY(gemm_bf16(u, c.d_p, (const uint16_t*)P.wgu, c.d_p, M, 2 * c.F_p, c.d_p, g, 1, w.part, s), "gate/up");
+        K_TRY(gemm_bf16((const uint16_t*)w.mlp, c.F_p, (const uint16_t*)P.wd, c.F_p, M, c.d_p, c.F_p, pe, kPrefixSplits, w.part, s), "down");
+        K_TRY(resid_norm(w.h, c.d_p, w.part, gemm_bf16_splits(c.F_p, kPrefixSplits), M, c.d_p, next_gain, eps, w.u, 0, c.d_p, nullptr, nullptr, s), "norm");
+      }
+    }
+  }
+  // Z = RMS(h; w_final) is in w.u; project into every expert layer's K and V
+  Epilogue ce;
+  ce.kind = EPI_CACHE; ce.out = kv; ce.out_f32 = m->f32 ? 1 : 0;
+  ce.npre = N; ce.L = c.L_e; ce.hkv = c.Hkv_e; ce.hd = c.hd_e;
+  const int ncache = c.L_e * 2 * c.Hkv_e * c.hd_e;
+  if (m->f32)
+    K_TRY(gemm_f32((const float*)w.u, c.d_p, (const float*)m->wcache, c.d_p, M, ncache, c.d_p, ce, s), "cache");
+  else
+    K_TRY(gemm_bf16((const uint16_t*)w.u, c.d_p, (const uint16_t*)m->wcache, c.d_p, M, ncache, c.d_p, ce, 1, w.part, s), "cache");
+  return VLA_OK;
+}
+
+extern "C" size_t vla_kv_cache_bytes(const vla_model* m, int32_t batch, int32_t n_prefix) {
+  if (!live_model(m) || batch <= 0 || n_prefix <= 0) return 0;
+  const vla_model_config& c = m->cfg;
+  return (size_t)batch * c.L_e * 2 * c.Hkv_e * (size_t)n_prefix * c.hd_e * elt(m);
+}
+
+extern "C" vla_status vla_prefix_encode(vla_model* m, const float* x, int32_t batch, int32_t n_prefix, void* kv_storage,
+                                        size_t kv_bytes, void* stream, vla_kv_cache** out) {
+  if (!out) return fail(VLA_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  if (!live_model(m)) return fail(VLA_ERR_INVALID_HANDLE, "unknown model");
+  if (!x || !kv_storage) return fail(VLA_ERR_INVALID_ARGUMENT, "prefix_hidden or kv_storage is NULL");
+  if (batch <= 0 || n_prefix <= 0) return fail(VLA_ERR_INVALID_ARGUMENT, "batch and n_prefix must be positive");
+  if ((int64_t)batch * n_prefix > (1 << 22)) return fail(VLA_ERR_UNSUPPORTED, "too many prefix tokens");
+  const size_t need = vla_kv_cache_bytes(m, batch, n_prefix);
+  if (kv_bytes < need)
+    return fail(VLA_ERR_SHAPE_MISMATCH, "kv_bytes " + std::to_string(kv_bytes) + " < required " + std::to_string(need));
+  hipStream_t s = (hipStream_t)stream;
+  WS w;
+  vla_status st = get_ws(m, (int64_t)batch * n_prefix, 0, &w);
+  if (st != VLA_OK) return st;
+  st = run_prefix(m, x, batch, n_prefix, kv_storage, w, s);
+  if (st != VLA_OK) return st;
+  vla_kv_cache* k = new vla_kv_cache();
+  k->model = m;
+  k->B = batch;
+  k->N = n_prefix;
+  k->storage = kv_storage;
+  {
+    std::lock_guard<std::mutex> g(g_mu);
+    m->caches.insert(k);
+  }
+  *out = k;
+  return VLA_OK;
+}
+
+extern "C" vla_status vla_kv_cache_release(vla_kv_cache* k) {
+  std::lock_guard<std::mutex> g(g_mu);
+  for (vla_model* m : g_models) {
+    if (m->caches.count(k)) {
+      m->caches.erase(k);
+      k->magic = 0;
+      delete k;
+      return VLA_OK;
+    }
+  }
+  return fail(VLA_ERR_INVALID_HANDLE, "unknown or released cache");
+}
+
+extern "C" vla_status vla_kv_cache_info(const vla_kv_cache* k, int32_t* batch, int32_t* n_prefix) {
+  if (!live_cache(k)) return fail(VLA_ERR_INVALID_HANDLE, "unknown or released cache");
+  if (batch) *batch = k->B;
+  if (n_prefix) *n_prefix = k->N;
+  return VLA_OK;
+}
+
+// ============================================================== solver
+static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, const WS& w, hipStream_t s) {
+  const vla_model_config& c = m->cfg;
+  const int B = kv->B, N = kv->N, H = c.H, M = B * H;
+  const int qe = c.Hq_e * c.hd_e, qkve = (c.Hq_e + 2 * c.Hkv_e) * c.hd_e;
+  const float eps = c.rms_eps;
+  const bool f32 = m->f32;
+  const size_t es = elt(m);
+  // self-attention over the H chunk tokens of each observation
+  AttnArgs sa{};
+  sa.q = w.eqkv; sa.q_bs = (long)H * qkve; sa.q_hs = c.hd_e; sa.q_rs = qkve;
+  sa.k = (const char*)w.eqkv + (size_t)qe * es; sa.k_bs = sa.q_bs; sa.k_hs = c.hd_e; sa.k_rs = qkve;
+  sa.v = (const char*)w.eqkv + (size_t)(qe + c.Hkv_e * c.hd_e) * es; sa.v_bs = sa.q_bs; sa.v_hs = c.hd_e; sa.v_rs = qkve;
+  sa.o = w.eattn; sa.o_bs = (long)H * qe; sa.o_rs = qe;
+  sa.B = B; sa.Nq = H; sa.Nk = H; sa.Hq = c.Hq_e; sa.Hkv = c.Hkv_e; sa.hd = c.hd_e; sa.o_f32 = f32 ? 1 : 0;
+  // cross-attention into the cache [B][L_e][2][Hkv_e][N][hd_e]
+  AttnArgs ca = sa;
+  const long layer_stride = 2L * c.Hkv_e * N * c.hd_e;
+  ca.q = w.eq; ca.q_bs = (long)H * qe; ca.q_hs = c.hd_e; ca.q_rs = qe;
+  ca.k_bs = c.L_e * layer_stride; ca.k_hs = (long)N * c.hd_e; ca.k_rs = c.hd_e;
+  ca.v_bs = ca.k_bs; ca.v_hs = ca.k_hs; ca.v_rs = c.hd_e;
+  ca.Nk = N;
+  Epilogue pe;
+  pe.kind = EPI_PARTIAL;
+  const int S_o = gemm_bf16_splits(qe, kExpertSplits), S_d = gemm_bf16_splits(c.F_e, kExpertSplits);
+  for (int k = 0; k < steps; ++k) {
+    K_TRY(expert_embed(w.X, M, c.d_a, m->w_in, f32, c.d_e, m->sched_dev, k, w.E, m->el[0].a1, eps, w.eu, f32, s), "embed");
+    for (int e = 0; e < c.L_e; ++e) {
+      const ExpertLayer& L = m->el[e];
+      ca.k = (const char*)kv->storage + (size_t)e * layer_stride * es;
+      ca.v = (const char*)ca.k + (size_t)c.Hkv_e * N * c.hd_e * es;
+      if (f32) {
+        K_TRY(gemm_f32((const float*)w.eu, c.d_e, (const float*)L.wqkv, c.d_e, M, qkve, c.d_e, epi_store(w.eqkv, qkve, 1), s), "qkv_s");
+        K_TRY(attention_f32(sa, s), "self attn");
+        Epilogue r;
+        r.kind = EPI_RESID; r.resid = w.E; r.ldr = c.d_e;
+        K_TRY(gemm_f32((const float*)w.eattn, qe, (const float*)L.wos, qe, M, c.d_e, qe, r, s), "o_s");
+        K_TRY(resid_norm(w.E, c.d_e, nullptr, 0, M, c.d_e, L.a2, eps, w.eu, 1, c.d_e, nullptr, nullptr, s), "norm");
+        K_TRY(gemm_f32((const float*)w.eu, c.d_e, (const float*)L.wqc, c.d_e, M, qe, c.d_e, epi_store(w.eq, qe, 1), s), "q_c");
+        K_TRY(attention_f32(ca, s), "cross attn");
+        K_TRY(gemm_f32((const float*)w.eattn, qe, (const float*)L.woc, qe, M, c.d_e, qe, r, s), "o_c");
+        K_TRY(resid_norm(w.E, c.d_e, nullptr, 0, M, c.d_e, L.a3, eps, w.eu, 1, c.d_e, nullptr, nullptr, s), "norm");
+        Epilogue g = epi_store(w.emlp, c.F_e, 1);
+        g.kind = EPI_GEGLU;
+        K_TRY(gemm_f32((const float*)w.eu, c.d_e, (const float*)L.wgu, c.d_e, M, 2 * c.F_e, c.d_e, g, s), "gate/up");
+        K_TRY(gemm_f32((const float*)w.emlp, c.F_e, (const float*)L.wd, c.F_e, M, c.d_e, c.F_e, r, s), "down");
+        if (e + 1 < c.L_e)
+          K_TRY(resid_norm(w.E, c.d_e, nullptr, 0, M, c.d_e, m->el[e + 1].a1, eps, w.eu, 1, c.d_e, nullptr, nullptr, s), "norm");
+      } else {
+        const uint16_t* u = (const uint16_t*)w.eu;
+        K_TRY(gemm_bf16(u, c.d_e, (const uint16_t*)L.wqkv, c.d_e, M, qkve, c.d_e, epi_store(w.eqkv, qkve, 0), 4, w.epart, s), "qkv_s");
+        K_TRY(attention_bf16(sa, s), "self attn");
+        K_TRY(gemm_bf16((const uint16_t*)w.eattn, qe, (const uint16_t*)L.wos, qe, M, c.d_e, qe, pe, S_o, w.epart, s), "o_s");
+        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s), "norm");
+        K_TRY(gemm_bf16(u, c.d_e, (const uint16_t*)L.wqc, c.d_e, M, qe, c.d_e, epi_store(w.eq, qe, 0), 4, w.epart, s), "q_c");
+        K_TRY(attention_bf16(ca, s), "cross attn");
+        K_TRY(gemm_bf16((const uint16_t*)w.eattn, qe, (const uint16_t*)L.woc, qe, M, c.d_e, qe, pe, S_o, w.epart, s), "o_c");
+        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s), "norm");
+        Epilogue g = epi_store(w.emlp, c.F_e, 0);
+        g.kind = EPI_GEGLU;
+        K_TRY(gemm_bf16(u, c.d_e, (const uint16_t*)L.wgu, c.d_e, M, 2 * c.F_e, c.d_e, g, 2, w.epart, s), "gate/up");
+        K_TRY(gemm_bf16((const uint16_t*)w.emlp, c.F_e, (const uint16_t*)L.wd, c.F_e, M, c.d_e, c.F_e, pe, S_d, w.epart, s), "down");
+        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_d, M, c.d_e, e + 1 < c.L_e ? m->el[e + 1].a1 : m->w_ef, eps,
+                         e + 1 < c.L_e ? w.eu : nullptr, 0, c.d_e, nullptr, nullptr, s), "norm");
+      }
+    }
+    K_TRY(expert_head(w.E, M, c.d_e, m->w_ef, eps, m->w_out, f32, c.d_a, m->sched_dev, k, w.X, s), "head");
+  }
+  return VLA_OK;
+}
+
+static bool use_graphs() {
+  const char* v = getenv("VLA_NO_GRAPH");
+  return !(v && v[0] == '1');
+}
+
+extern "C" vla_status vla_denoise_chunk(vla_model* m, const vla_kv_cache* kv, const float* noise, int32_t steps,
+                                        const vla_solver* solver, void* actions_out, int32_t out_dtype, void* stream,
+                                        vla_timing* timing) {
+  if (!live_model(m)) return fail(VLA_ERR_INVALID_HANDLE, "unknown model");
+  if (!live_cache(kv)) return fail(VLA_ERR_INVALID_HANDLE, "unknown or released cache");
+  if (kv->model != m) return fail(VLA_ERR_INVALID_HANDLE, "cache belongs to another model");
+  if (!noise || !actions_out) return fail(VLA_ERR_INVALID_ARGUMENT, "noise or actions_out is NULL");
+  if (steps <= 0 || steps > 4096) return fail(VLA_ERR_INVALID_ARGUMENT, "steps must be in 1..4096");
+  if (out_dtype != VLA_OUT_F32 && out_dtype != VLA_OUT_BF16) return fail(VLA_ERR_INVALID_ARGUMENT, "bad out_dtype");
+  std::vector<float> sched(steps + 1);
+  if (solver && solver->schedule) {
+    for (int k = 0; k <= steps; ++k) {
+      sched[k] = solver->schedule[k];
+      if (!std::isfinite(sched[k])) return fail(VLA_ERR_INVALID_ARGUMENT, "non-finite schedule");
+    }
+  } else {
+    const double t0 = solver ? solver->tau_start : 0.0, t1 = solver ? solver->tau_end : 1.0;
+    if (!std::isfinite(t0) || !std::isfinite(t1)) return fail(VLA_ERR_INVALID_ARGUMENT, "non-finite tau");
+    for (int k = 0; k <= steps; ++k) sched[k] = (float)(t0 + k * (t1 - t0) / steps);
+  }
+  const vla_model_config& c = m->cfg;
+  hipStream_t s = (hipStream_t)stream;
+  WS w;
+  vla_status st = get_ws(m, 0, (int64_t)kv->B * c.H, &w);
+  if (st != VLA_OK) return st;
+  if (steps + 1 > m->sched_cap) {
+    if (m->sched_dev) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(m->sched_dev);
+      (void)hipHostFree(m->sched_host);
+      m->sched_dev = nullptr;
+      m->sched_host = nullptr;
+      for (auto& g : m->graphs) (void)hipGraphExecDestroy(g.second);
+      m->graphs.clear();
+    }
+    const int cap = std::max(64, steps + 1);
+    if (hipMalloc(&m->sched_dev, cap * 4) != hipSuccess || hipHostMalloc(&m->sched_host, cap * 4) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(VLA_ERR_OUT_OF_MEMORY, "schedule buffers");
+    }
+    m->sched_cap = cap;
+  }
+  // the pinned staging buffer may still feed an earlier copy on this stream
+  K_TRY(hipStreamSynchronize(s), "sync");
+  memcpy(m->sched_host, sched.data(), (steps + 1) * 4);
+  if (timing) K_TRY(hipEventRecord(m->ev0, s), "event");
+  K_TRY(hipMemcpyAsync(m->sched_dev, m->sched_host, (steps + 1) * 4, hipMemcpyHostToDevice, s), "schedule upload");
+  const long nx = (long)kv->B * c.H * c.d_a;
+  K_TRY(copy_f32(noise, w.X, nx, s), "noise in");
+  int replayed = 0;
+  if (use_graphs()) {
+    GraphKey key{kv->storage, kv->B, kv->N, steps};
+    auto it = m->graphs.find(key);
+    hipGraphExec_t exec = nullptr;
+    if (it == m->graphs.end()) {
+      K_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal), "begin capture");
+      vla_status rs = run_steps(m, kv, steps, w, m->cap_stream);
+      hipGraph_t graph = nullptr;
+      hipError_t ce = hipStreamEndCapture(m->cap_stream, &graph);
+      if (rs != VLA_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return rs;
+      }
+      K_TRY(ce, "end capture");
+      hipError_t ie = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(graph);
+      K_TRY(ie, "graph instantiate");
+      m->graphs[key] = exec;
+    } else {
+      exec = it->second;
+      replayed = 1;
+    }
+    K_TRY(hipGraphLaunch(exec, s), "graph launch");
+  } else {
+    st = run_steps(m, kv, steps, w, s);
+    if (st != VLA_OK) return st;
+  }
+  K_TRY(copy_out(w.X, actions_out, nx, out_dtype == VLA_OUT_BF16, s), "actions out");
+  if (timing) {
+    K_TRY(hipEventRecord(m->ev1, s), "event");
+    K_TRY(hipEventSynchronize(m->ev1), "event sync");
+    float ms = 0.f;
+    K_TRY(hipEventElapsedTime(&ms, m->ev0, m->ev1), "elapsed");
+    timing->prefix_ms = 0.f;
+    timing->denoise_ms = ms;
+    timing->step_ms = ms / steps;
+    timing->graph_replayed = replayed;
+  }
+  return VLA_OK;
+}
+
+// ============================================================== ternary unit entry points
+extern "C" vla_status vla_quantize_rows_i8(const float* x, int32_t M, int32_t K, int8_t* a, float* alpha, void* stream) {
+  if (!x || !a || !alpha) return fail(VLA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (M <= 0 || K <= 0) return fail(VLA_ERR_INVALID_ARGUMENT, "M and K must be positive");
+  vla_status st = check_device();
+  if (st != VLA_OK) return st;
+  K_TRY(quantize_rows(x, K, M, K, a, alpha, (hipStream_t)stream), "quantize");
+  return VLA_OK;
+}
+
+extern "C" vla_status vla_w2a8_gemm(const int8_t* a, const float* alpha, const uint8_t* q_packed, float beta, int32_t M,
+                                    int32_t N, int32_t K, int32_t* acc_out, uint16_t* y_bf16, void* stream) {
+  if (!a || !alpha || !q_packed) return fail(VLA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (M <= 0 || N <= 0 || K <= 0) return fail(VLA_ERR_INVALID_ARGUMENT, "M, N and K must be positive");
+  if (K % 128 || N % 32) return fail(VLA_ERR_UNSUPPORTED, "need K % 128 == 0 and N % 32 == 0");
+  if (!std::isfinite(beta)) return fail(VLA_ERR_INVALID_ARGUMENT, "non-finite beta");
+  vla_status st = check_device();
+  if (st != VLA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* words = nullptr;
+  int* flags = nullptr;
+  if (hipMalloc(&words, (size_t)N * K / 4) != hipSuccess || hipMalloc(&flags, 64) != hipSuccess) {
+    (void)hipGetLastError();
+    if (words) (void)hipFree(words);
+    return fail(VLA_ERR_OUT_OF_MEMORY, "staging");
+  }
+  auto done = [&](vla_status r) {
+    (void)hipFree(words);
+    (void)hipFree(flags);
+    return r;
+  };
+  if (hipMemsetAsync(flags, 0, 64, s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "memset"));
+  if (ternary_repack(q_packed, N, K, words, flags, s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "repack"));
+  int hf = 0;
+  if (hipMemcpyAsync(&hf, flags, 4, hipMemcpyDeviceToHost, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+    return done(fail(VLA_ERR_DEVICE, "flag readback"));
+  if (hf) return done(fail(VLA_ERR_INVALID_ARGUMENT, "packed weights contain the invalid code 3"));
+  Epilogue e = epi_store(y_bf16, N, 0);
+  e.alpha = alpha;
+  e.acc_out = acc_out;
+  if (gemm_w2a8_scalar(a, K, words, M, N, K, e, beta, s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "w2a8 launch"));
+  if (hipStreamSynchronize(s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "w2a8 sync"));
+  return done(VLA_OK);
+}
+
+extern "C" vla_status vla_ternary_pack(const int8_t* q, int32_t N, int32_t K, uint8_t* packed) {
+  if (!q || !packed) return fail(VLA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (N <= 0 || K <= 0 || K % 4) return fail(VLA_ERR_INVALID_ARGUMENT, "need N, K > 0 and K % 4 == 0");
+  for (int64_t i = 0; i < (int64_t)N * K; ++i)
+    if (q[i] < -1 || q[i] > 1) return fail(VLA_ERR_INVALID_ARGUMENT, "ternary values must be -1, 0 or +1");
+  for (int64_t r = 0; r < N; ++r)
+    for (int64_t j = 0; j < K / 4; ++j) {
+      uint8_t b = 0;
+      for (int i = 0; i < 4; ++i) b |= (uint8_t)((q[r * K + 4 * j + i] + 1) << (2 * i));
+      packed[r * (K / 4) + j] = b;
+    }
+  return VLA_OK;
+}
+
+extern "C" vla_status vla_ternary_unpack(const uint8_t* packed, int32_t N, int32_t K, int8_t* q) {
+  if (!q || !packed) return fail(VLA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (N <= 0 || K <= 0 || K % 4) return fail(VLA_ERR_INVALID_ARGUMENT, "need N, K > 0 and K % 4 == 0");
+  for (int64_t i = 0; i < (int64_t)N * K / 4; ++i)
+    for (int t = 0; t < 4; ++t)
+      if (((packed[i] >> (2 * t)) & 3) == 3) return fail(VLA_ERR_INVALID_ARGUMENT, "invalid ternary code 3");
+  for (int64_t i = 0; i < (int64_t)N * K / 4; ++i)
+    for (int t = 0; t < 4; ++t) q[4 * i + t] = (int8_t)(((packed[i] >> (2 * t)) & 3) - 1);
+  return VLA_OK;
+}

@@ -1,0 +1,179 @@
+// Ternary W2A8 GEMM of the paper's §III-D, Eq. 4:
+//   acc[m][n] = sum_j a[m][j] q[n][j]   (int8 activations x ternary weights, int32)
+//   y[m][n]   = bf16(float(acc) * (alpha[m] * beta[n]))   (nearest, ties to even)
+//
+// Weight layout inside the library: one 32-bit word per 16 consecutive inputs of
+// an output row, input e = 4i + b of the group at bits 8b + 2i (code = q + 1).
+// With that order, (word >> 2i) & 0x03030303 holds inputs 4i..4i+3 in its four
+// bytes, and one byte permute against the table {-1, 0, +1} turns the 2-bit
+// codes into int8 lanes: a 16-input MFMA fragment comes out of one word with
+// four shifts, four masks and four permutes.  The canonical format of the C ABI
+// (input 4j + i in bits 2i of byte j) is converted to this order once, when the
+// model is created.
+//
+// Tiles: 64 activation rows x 128 output channels x 128 inputs per slice,
+// four waves of 32 x 64 on the 32x32x32 int8 MFMA.  The activation slice is
+// staged in LDS as int8; the weight slice is staged *packed* (2 bits per weight,
+// a quarter of the int8 bytes) and unpacked in registers right before the MFMA.
+#include "common.h"
+#include "kernels.h"
+
+namespace vla {
+
+struct W2A8P {
+  const int8_t* a;
+  int lda;
+  const uint32_t* q;  // [N][K/16] words
+  int M, N, K, nM, nN;
+  Epilogue epi;
+  float beta_scalar;
+};
+
+__device__ __forceinline__ i32x4_t unpack16(uint32_t w) {
+  i32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (int)__builtin_amdgcn_perm(0u, 0x000100FFu, (w >> (2 * i)) & 0x03030303u);
+  return r;
+}
+
+__device__ __forceinline__ float w2a8_scale(const W2A8P& p, int m, int n, int acc) {
+  const float b = p.epi.beta ? p.epi.beta[n] : p.beta_scalar;
+  const float s = p.epi.alpha[m] * b;
+  return bf2f(f2bf((float)acc * s));
+}
+
+__global__ __launch_bounds__(256) void k_gemm_w2a8(W2A8P p) {
+  constexpr int BM = 64, BN = 128, BK = 128, LDA = BK + 16, LDW = BK / 16 + 1;
+  __shared__ __attribute__((aligned(16))) int8_t sA[2][BM * LDA];
+  __shared__ uint32_t sW[2][BN * LDW];
+  const int nt = p.nM * p.nN, L = blockIdx.x;
+  const int tile = (nt % 8 == 0) ? (L % 8) * (nt / 8) + L / 8 : L;
+  const int tm = tile % p.nM, tn = tile / p.nM;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int KW = p.K / 16;  // words per weight row
+
+  u32x4_t ra[2], rw;
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int v = tid + i * 256, r = v >> 3, c = (v & 7) * 16;
+      ra[i] = (m0 + r < p.M) ? *(const u32x4_t*)(p.a + (long)(m0 + r) * p.lda + k0 + c) : u32x4_t{0, 0, 0, 0};
+    }
+    const int r = tid >> 1, c = (tid & 1) * 4;  // 128 rows x 8 words
+    rw = (n0 + r < p.N) ? *(const u32x4_t*)(p.q + (long)(n0 + r) * KW + k0 / 16 + c)
+                        : u32x4_t{0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u};  // code 1 = 0
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int v = tid + i * 256;
+      *(u32x4_t*)&sA[buf][(v >> 3) * LDA + (v & 7) * 16] = ra[i];
+    }
+    const int r = tid >> 1, c = (tid & 1) * 4;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sW[buf][r * LDW + c + t] = rw[t];
+  };
+
+  i32x16_t acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0;
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  int it = 0;
+  for (int k0 = 0; k0 < p.K; k0 += BK, ++it) {
+    const int buf = it & 1;
+    const bool more = k0 + BK < p.K;
+    if (more) gload(k0 + BK);
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      const i32x4_t af = __builtin_bit_cast(
+          i32x4_t, *(const u32x4_t*)&sA[buf][(wm * 32 + (lane & 31)) * LDA + kk * 32 + (lane >> 5) * 16]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t w = sW[buf][(wn * 64 + j * 32 + (lane & 31)) * LDW + kk * 2 + (lane >> 5)];
+        acc[j] = mfma32x32x32_i8(af, unpack16(w), acc[j]);
+      }
+    }
+    if (more) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  const Epilogue& e = p.epi;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * 32 + mfma32_row(r, lane);
+      const bool ok = m < p.M && n < p.N;
+      const int accv = acc[j][r];
+      if (e.acc_out && ok) e.acc_out[(long)m * p.N + n] = accv;
+      const float y = ok ? w2a8_scale(p, m, n, accv) : 0.f;
+      if (e.kind == EPI_GEGLU) {
+        const float other = __shfl_xor(y, 16, 64);
+        if (!(lane & 16) && ok) {
+          const float v = gelu_erf(y) * other;
+          const long i = (long)m * e.ldo + (n >> 5) * 16 + (lane & 15);
+          if (e.out_f32) ((float*)e.out)[i] = v; else ((bf16_t*)e.out)[i] = f2bf(v);
+        }
+      } else if (ok) {
+        if (e.kind == EPI_STORE && e.out) {
+          const long i = (long)m * e.ldo + n;
+          if (e.out_f32) ((float*)e.out)[i] = y; else ((bf16_t*)e.out)[i] = f2bf(y);
+        } else if (e.kind == EPI_RESID) {
+          e.resid[(long)m * e.ldr + n] += y;
+        }
+      }
+    }
+  }
+}
+
+hipError_t gemm_w2a8_scalar(const int8_t* a, int lda, const uint32_t* qp, int M, int N, int K, const Epilogue& epi,
+                            float beta_scalar, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (K % 128 || N % 32 || !epi.alpha) return hipErrorInvalidValue;
+  W2A8P p{a, lda, qp, M, N, K, (M + 63) / 64, (N + 127) / 128, epi, beta_scalar};
+  hipLaunchKernelGGL(k_gemm_w2a8, dim3(p.nM * p.nN), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t gemm_w2a8(const int8_t* a, int lda, const uint32_t* qp, int M, int N, int K, const Epilogue& epi,
+                     hipStream_t s) {
+  return gemm_w2a8_scalar(a, lda, qp, M, N, K, epi, 0.f, s);
+}
+
+// canonical [N][K/4] bytes -> [N][K/16] words in the library's order
+__global__ void k_ternary_repack(const uint8_t* canon, int N, int K, uint32_t* out, int* flags) {
+  const long words = (long)N * (K / 16);
+  for (long w = blockIdx.x * (long)blockDim.x + threadIdx.x; w < words; w += (long)gridDim.x * blockDim.x) {
+    const long row = w / (K / 16), col = w % (K / 16);
+    const uint8_t* src = canon + row * (K / 4) + col * 4;
+    uint32_t o = 0;
+    int bad = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t code = (src[e >> 2] >> (2 * (e & 3))) & 3u;
+      bad |= code == 3u;
+      o |= code << (8 * (e & 3) + 2 * (e >> 2));
+    }
+    out[w] = o;
+    if (bad) atomicOr(flags, 1);
+  }
+}
+
+hipError_t ternary_repack(const uint8_t* canon, int N, int K, uint32_t* out, int* flags, hipStream_t s) {
+  if (N <= 0 || K <= 0) return hipSuccess;
+  if (K % 16) return hipErrorInvalidValue;
+  const long words = (long)N * (K / 16);
+  const int blocks = (int)std::min<long>((words + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_ternary_repack, dim3(blocks), dim3(256), 0, s, canon, N, K, out, flags);
+  return hipGetLastError();
+}
+
+}  // namespace vla

@@ -1,0 +1,76 @@
+"""Shared helpers of the GPU parity tests: workloads, device inputs, oracle runs."""
+from __future__ import annotations
+
+import functools
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+# Small workloads that still span several tiles and ragged tails of every kernel.
+SMALL_BF16 = synth.config(1, name="small_bf16", n_prefix=100, d_p=256, L_p=2, Hq=4, Hkv=1, hd=64, F_p=512,
+                          d_e=128, L_e=2, Hq_e=2, Hkv_e=1, hd_e=64, F_e=256, H=20, d_a=7, steps=3)
+SMALL_BF16_B3 = synth.config(1, name="small_bf16_b3", batch=3, n_prefix=70, d_p=256, L_p=2, Hq=8, Hkv=1, hd=128,
+                             F_p=512, d_e=128, L_e=2, Hq_e=8, Hkv_e=1, hd_e=128, F_e=256, H=33, d_a=5, steps=2)
+SMALL_W2A8 = synth.config(4, name="small_w2a8", n_prefix=100, d_p=256, L_p=2, Hq=2, Hkv=2, hd=128, F_p=384,
+                          d_e=128, L_e=2, Hq_e=2, Hkv_e=1, hd_e=64, F_e=256, H=8, d_a=7, steps=3)
+
+
+def ordered(cfg, weights):
+    return [weights[name] for name, _, _ in synth.weight_specs(cfg)]
+
+
+def ordered_betas(cfg, betas):
+    return [betas[name] for name, _, kind in synth.weight_specs(cfg) if kind == "ternary"] or None
+
+
+@functools.lru_cache(maxsize=4)
+def host_inputs(cfg, seed):
+    w, b = synth.make_weights(cfg, seed)
+    return w, b, synth.make_prefix(cfg, seed), synth.make_noise(cfg, seed)
+
+
+def build_model(cfg, weights, betas):
+    from prefix_cache_flow_amd import vla
+    tensors = vla.upload_weights(cfg.to_dict(), ordered(cfg, weights))
+    model = vla.vla_model_create(cfg.to_dict(), tensors, ordered_betas(cfg, betas))
+    del tensors
+    return model
+
+
+def gpu_run(cfg, model, z0, x0, steps=None, out_dtype=None, schedule=None):
+    """Encode + denoise on the GPU; returns (X^T as float64 numpy, cache storage tensor)."""
+    import torch
+    from prefix_cache_flow_amd import vla
+    zt = torch.from_numpy(np.ascontiguousarray(z0)).cuda()
+    xt = torch.from_numpy(np.ascontiguousarray(x0)).cuda()
+    kv = vla.vla_prefix_encode(model, zt)
+    out = vla.vla_denoise_chunk(model, kv, xt, steps or cfg.steps, schedule=schedule,
+                                out_dtype=out_dtype or torch.float32)
+    torch.cuda.synchronize()
+    res = out.float().cpu().numpy().astype(np.float64)
+    storage = kv.storage
+    kv.close()
+    return res, storage
+
+
+def cache_from_storage(cfg, storage, B, N):
+    """[B][L_e][2][Hkv_e][N][hd_e] device storage -> per observation list of (K_C, V_C) [N, Hkv_e*hd_e]."""
+    import torch
+    dt = torch.float32 if cfg.precision == "f32" else torch.bfloat16
+    t = storage.view(dt).float().cpu().numpy().reshape(B, cfg.L_e, 2, cfg.Hkv_e, N, cfg.hd_e)
+    out = []
+    for b in range(B):
+        layers = []
+        for e in range(cfg.L_e):
+            k = t[b, e, 0].transpose(1, 0, 2).reshape(N, cfg.Hkv_e * cfg.hd_e)
+            v = t[b, e, 1].transpose(1, 0, 2).reshape(N, cfg.Hkv_e * cfg.hd_e)
+            layers.append((k.astype(np.float64), v.astype(np.float64)))
+        out.append(layers)
+    return out

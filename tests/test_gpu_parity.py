@@ -1,0 +1,235 @@
+"""Parity of the HIP library with the CPU oracle on seeded inputs (needs a gfx950 GPU).
+
+Floating-point results are compared with Eq. 5 of the paper (§III-E): relative
+Euclidean error of the flattened action chunk against the float64 oracle.  The
+bound is 1e-3 for the fp32 workload and 2e-2 for the bf16 and ternary
+workloads; the displacement D = X^T - X^0 (which the exact noise term does not
+dilute) and the K/V cache are checked as well.  Integer work (the int8 codes
+and int32 accumulators of Eq. 4) must match bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from policy_cases import (SMALL_BF16, SMALL_BF16_B3, SMALL_W2A8, build_model, cache_from_storage, gpu_run,
+                          host_inputs)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from prefix_cache_flow_amd import vla  # noqa: E402
+
+
+def report(name, got, ref, x0):
+    e = oracle.e_rel(got, ref)
+    ed = oracle.e_rel(got - x0, ref - x0)
+    print(f"[{name}] e_rel(X^T)={e:.3e} e_rel(X^T-X^0)={ed:.3e} e_inf={oracle.e_inf(got, ref):.3e}", flush=True)
+    return e, ed
+
+
+# ---------------------------------------------------------------- end to end
+
+@pytest.mark.parametrize("cfg,tol,dtol", [
+    (synth.config(0), 1e-3, 1e-3),
+    (SMALL_BF16, 2e-2, 2e-2),
+    (SMALL_BF16_B3, 2e-2, 2e-2),
+    (SMALL_W2A8, 2e-2, 5e-2),
+], ids=lambda v: getattr(v, "name", ""))
+def test_end_to_end_small(cfg, tol, dtol):
+    w, b, z0, x0 = host_inputs(cfg, 0)
+    print(f"case {cfg.name} seed 0", flush=True)
+    ref, caches = oracle.Oracle(cfg, w, b).run(z0, x0, keep_cache=True)
+    model = build_model(cfg, w, b)
+    got, storage = gpu_run(cfg, model, z0, x0)
+    x0d = x0.astype(np.float64)
+    e, ed = report(cfg.name, got, ref, x0d)
+    assert e <= tol and ed <= dtol
+    # the cache itself
+    gc = cache_from_storage(cfg, storage, cfg.batch, cfg.n_prefix)
+    for bb in range(cfg.batch):
+        for l in range(cfg.L_e):
+            for i in range(2):
+                ec = oracle.e_rel(gc[bb][l][i], caches[bb][l][i])
+                assert ec <= (1e-4 if cfg.precision == "f32" else 2e-2), (bb, l, i, ec)
+    # bf16 output equals the rounded fp32 output
+    got16, _ = gpu_run(cfg, model, z0, x0, out_dtype=torch.bfloat16)
+    np.testing.assert_array_equal(got16, torch.from_numpy(got.astype(np.float32)).bfloat16().float().numpy())
+    model.close()
+
+
+def test_zero_velocity_and_determinism():
+    cfg = SMALL_BF16
+    w, b, z0, x0 = host_inputs(cfg, 0)
+    model = build_model(cfg, w, b)
+    a1, _ = gpu_run(cfg, model, z0, x0)
+    a2, _ = gpu_run(cfg, model, z0, x0)
+    np.testing.assert_array_equal(a1, a2)
+    import os
+    os.environ["VLA_NO_GRAPH"] = "1"
+    try:
+        a3, _ = gpu_run(cfg, model, z0, x0)
+    finally:
+        del os.environ["VLA_NO_GRAPH"]
+    np.testing.assert_array_equal(a1, a3)
+    model.close()
+    w0 = dict(w)
+    w0["expert.w_out"] = np.zeros_like(w["expert.w_out"])
+    model = build_model(cfg, w0, b)
+    a0, _ = gpu_run(cfg, model, z0, x0)
+    np.testing.assert_array_equal(a0, x0.astype(np.float64))
+    model.close()
+
+
+def test_cached_equals_recompute_on_gpu():
+    """Re-encoding the prefix before every step gives the cached result bit for bit."""
+    cfg = SMALL_BF16
+    w, b, z0, x0 = host_inputs(cfg, 1)
+    model = build_model(cfg, w, b)
+    sched = [float(np.float32(k / cfg.steps)) for k in range(cfg.steps + 1)]
+    cached, _ = gpu_run(cfg, model, z0, x0, schedule=sched)
+    x = torch.from_numpy(x0).cuda()
+    zt = torch.from_numpy(z0).cuda()
+    for k in range(cfg.steps):
+        kv = vla.vla_prefix_encode(model, zt)
+        x = vla.vla_denoise_chunk(model, kv, x.contiguous(), 1, schedule=sched[k:k + 2])
+        torch.cuda.synchronize()
+        kv.close()
+    np.testing.assert_array_equal(cached, x.cpu().numpy().astype(np.float64))
+    model.close()
+
+
+def test_bidirectional_first_token_sees_last_on_gpu():
+    cfg = synth.config(1, n_prefix=64, d_p=128, L_p=1, Hq=2, Hkv=1, hd=64, F_p=256, d_e=128, L_e=1, Hq_e=2,
+                       Hkv_e=1, hd_e=64, F_e=128, H=4, d_a=4, steps=1)
+    w, b, z0, x0 = host_inputs(cfg, 2)
+    model = build_model(cfg, w, b)
+    _, s0 = gpu_run(cfg, model, z0, x0)
+    c0 = cache_from_storage(cfg, s0.clone(), 1, cfg.n_prefix)
+    z1 = z0.copy()
+    z1[0, -1] += 3.0
+    _, s1 = gpu_run(cfg, model, z1, x0)
+    c1 = cache_from_storage(cfg, s1, 1, cfg.n_prefix)
+    assert np.abs(c1[0][0][0][0] - c0[0][0][0][0]).max() > 0  # token 0's key moved
+    model.close()
+
+
+def test_scheduled_reverse_time():
+    """1 -> 0 integration (tau decreasing) matches the oracle with the same schedule."""
+    cfg = SMALL_BF16
+    w, b, z0, x0 = host_inputs(cfg, 0)
+    model = build_model(cfg, w, b)
+    sched = oracle.uniform_schedule(cfg.steps, 1.0, 0.0)
+    ref = oracle.Oracle(cfg, w, b).run(z0, x0, schedule=sched)
+    got, _ = gpu_run(cfg, model, z0, x0, schedule=list(sched))
+    e, _ = report("reverse", got, ref, x0.astype(np.float64))
+    assert e <= 2e-2
+    model.close()
+
+
+# ---------------------------------------------------------------- ternary units (bit-exact)
+
+def _x_rows(M, K, seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((M, K)) * rng.uniform(1e-3, 30.0, (M, 1))).astype(np.float32)
+    x[min(3, M - 1)] = 0.0  # an all-zero row
+    x[0, :8] = np.array([127, 2.5, 3.5, -2.5, 0.5, -0.5, 1.5, -1.5], dtype=np.float32)  # exact ties
+    x[0, 8:] = np.clip(x[0, 8:], -100, 100)
+    return x
+
+
+@pytest.mark.parametrize("M,K", [(320, 2560), (320, 6912), (7, 130), (1, 4096)])
+def test_quantizer_bit_exact(M, K):
+    x = _x_rows(M, K, M + K)
+    a_ref, al_ref = oracle.quantize_rows(x)
+    a, al = vla.vla_quantize_rows_i8(torch.from_numpy(x).cuda())
+    np.testing.assert_array_equal(a.cpu().numpy(), a_ref)
+    np.testing.assert_array_equal(al.cpu().numpy(), al_ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(320, 7680, 2560), (320, 2560, 2560), (320, 13824, 2560), (320, 2560, 6912),
+                                   (37, 96, 384), (1, 32, 128)])
+def test_w2a8_gemm_bit_exact(M, N, K):
+    rng = np.random.default_rng(N + K)
+    x = _x_rows(M, K, K)
+    a_ref, al_ref = oracle.quantize_rows(x)
+    q = rng.integers(-1, 2, (N, K), dtype=np.int8)
+    beta = float(np.float32(rng.uniform(0.005, 0.05)))
+    acc_ref = oracle.w2a8_accumulate(a_ref, q)
+    y_ref = oracle.w2a8_linear(x, q, beta)
+    packed = torch.from_numpy(oracle.pack_ternary(q)).cuda()
+    acc, y = vla.vla_w2a8_gemm(torch.from_numpy(a_ref).cuda(), torch.from_numpy(al_ref).cuda(), packed, beta)
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+    np.testing.assert_array_equal(y.float().cpu().numpy(), y_ref)
+
+
+def test_w2a8_special_patterns():
+    M, K = 64, 256
+    rng = np.random.default_rng(5)
+    a = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    al = np.ones(M, dtype=np.float32)
+    ones = np.ones((32, K), dtype=np.int8)
+    acc, _ = vla.vla_w2a8_gemm(torch.from_numpy(a).cuda(), torch.from_numpy(al).cuda(),
+                               torch.from_numpy(oracle.pack_ternary(ones)).cuda(), 1.0)
+    np.testing.assert_array_equal(acc.cpu().numpy(), np.repeat(a.astype(np.int64).sum(1, keepdims=True), 32, 1))
+    eye = np.eye(K, dtype=np.int8)
+    acc, _ = vla.vla_w2a8_gemm(torch.from_numpy(a).cuda(), torch.from_numpy(al).cuda(),
+                               torch.from_numpy(oracle.pack_ternary(eye)).cuda(), 1.0)
+    np.testing.assert_array_equal(acc.cpu().numpy(), a.astype(np.int32))
+
+
+def test_w2a8_rejects_code_3():
+    a = torch.zeros((32, 128), dtype=torch.int8, device="cuda")
+    al = torch.ones(32, dtype=torch.float32, device="cuda")
+    bad = np.zeros((32, 32), dtype=np.uint8)
+    bad[5, 7] = 0b11 << 4
+    with pytest.raises(vla.VlaError) as ei:
+        vla.vla_w2a8_gemm(a, al, torch.from_numpy(bad).cuda(), 1.0)
+    assert ei.value.status == 1
+
+
+# ---------------------------------------------------------------- handles and errors on a device
+
+def test_handle_errors_on_device():
+    cfg = SMALL_BF16
+    w, b, z0, x0 = host_inputs(cfg, 0)
+    m1 = build_model(cfg, w, b)
+    m2 = build_model(cfg, w, b)
+    zt = torch.from_numpy(z0).cuda()
+    xt = torch.from_numpy(x0).cuda()
+    kv = vla.vla_prefix_encode(m1, zt)
+    assert vla.vla_kv_cache_info(kv) == (1, cfg.n_prefix)
+    with pytest.raises(vla.VlaError) as ei:  # cache of another model
+        vla.vla_denoise_chunk(m2, kv, xt, 2)
+    assert ei.value.status == 3
+    with pytest.raises(vla.VlaError) as ei:  # too little storage
+        small = torch.empty(16, dtype=torch.uint8, device="cuda")
+        vla.vla_prefix_encode(m1, zt, kv_storage=small)
+    assert ei.value.status == 2
+    with pytest.raises(vla.VlaError) as ei:  # zero steps
+        vla.vla_denoise_chunk(m1, kv, xt, 0)
+    assert ei.value.status == 1
+    h = kv.handle
+    kv.close()
+    stale = vla.KVCache(h, kv.storage, 1, cfg.n_prefix)
+    with pytest.raises(vla.VlaError) as ei:  # released handle
+        vla.vla_denoise_chunk(m1, stale, xt, 2)
+    assert ei.value.status == 3
+    stale.handle = None
+    m1.close()
+    m2.close()
+
+
+def test_invalid_ternary_weights_rejected_at_create():
+    cfg = SMALL_W2A8
+    w, b, _, _ = host_inputs(cfg, 0)
+    from policy_cases import ordered, ordered_betas
+    tensors = vla.upload_weights(cfg.to_dict(), ordered(cfg, w))
+    idx = [i for i, (n, _, k) in enumerate(synth.weight_specs(cfg)) if k == "ternary"][3]
+    tensors[idx][2, 1] = 0xFF  # four code-3 entries
+    with pytest.raises(vla.VlaError) as ei:
+        vla.vla_model_create(cfg.to_dict(), tensors, ordered_betas(cfg, b))
+    assert ei.value.status == 1
