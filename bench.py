@@ -1,0 +1,214 @@
+"""Benchmark of the dual-phase policy step on one MI355X.
+
+One step = one observation through the whole hot path: the bidirectional
+prefix pass writing the K/V cache (vla_prefix_encode) and the flow-matching
+action expert refining a noise chunk over T Euler steps (vla_denoise_chunk).
+Workload: the single-camera bf16 policy (288 prefix tokens, 18 + 18 layers,
+50 x 32 action chunk, 10 steps, batch 1) with seeded synthetic weights and
+inputs, all resident in HBM before timing starts.
+
+Prints one JSON line: action chunks/s, per-phase latency, the roofline of the
+dominant kernel (timed live with HIP events around its launches inside the
+timed region) and the CPU oracle timed on a bounded sample of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_INT8_TOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=1, help="workload index (1 = single camera bf16)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-s", type=float, default=30.0)
+    return p.parse_args()
+
+
+def prefix_flops(c):
+    """Algorithmic FLOPs of one prefix pass (+ cache projection) for one observation."""
+    N = c.n_prefix
+    qkv = 2 * N * c.d_p * (c.Hq + 2 * c.Hkv) * c.hd
+    attn = 4 * N * N * c.Hq * c.hd
+    o = 2 * N * c.Hq * c.hd * c.d_p
+    mlp = 2 * N * c.d_p * 2 * c.F_p + 2 * N * c.F_p * c.d_p
+    cache = 2 * N * c.d_p * c.L_e * 2 * c.Hkv_e * c.hd_e
+    return c.L_p * (qkv + attn + o + mlp) + cache
+
+
+def expert_step_bytes(c):
+    """Algorithmic HBM bytes of one denoise step: every expert weight once (bf16) plus the cache."""
+    qe, kve = c.Hq_e * c.hd_e, c.Hkv_e * c.hd_e
+    per_layer = (qe + 2 * kve) * c.d_e + c.d_e * qe + qe * c.d_e + c.d_e * qe + 2 * c.F_e * c.d_e + c.d_e * c.F_e
+    weights = c.L_e * per_layer + c.d_e * c.d_a * 2
+    cache = c.batch * c.L_e * 2 * kve * c.n_prefix
+    return 2 * (weights + cache)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (the sharding design is "
+                                   "described in DESIGN.md)"}))
+        sys.exit(2)
+    import torch
+
+    import synth
+    from prefix_cache_flow_amd import vla
+
+    torch.cuda.set_device(0)
+    cfg = synth.config(args.config)
+    t0 = time.time()
+    w, betas = synth.make_weights(cfg, args.config)
+    z0 = synth.make_prefix(cfg, args.config)
+    x0 = synth.make_noise(cfg, args.config)
+    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    names = [n for n, _, _ in synth.weight_specs(cfg)]
+    tensors = vla.upload_weights(cfg.to_dict(), [w[n] for n in names])
+    bl = [betas[n] for n, _, k in synth.weight_specs(cfg) if k == "ternary"] or None
+    model = vla.vla_model_create(cfg.to_dict(), tensors, bl)
+    del tensors
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    print(f"# model built at {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    zt = torch.from_numpy(z0).cuda()
+    xt = torch.from_numpy(x0).cuda()
+    out = torch.empty(x0.shape, dtype=torch.bfloat16, device="cuda")
+    kv_storage = torch.empty(vla.vla_kv_cache_bytes(model, cfg.batch, cfg.n_prefix), dtype=torch.uint8,
+                             device="cuda")
+
+    def step():
+        kv = vla.vla_prefix_encode(model, zt, kv_storage=kv_storage)
+        vla.vla_denoise_chunk(model, kv, xt, cfg.steps, out=out)
+        kv.close()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"# warmup done at {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    # ---- timed region: K whole steps
+    probe = vla.Probe(model, vla.PROBE_PREFIX_GATEUP)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    probe_ms, probe_launches = probe.collect()
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = cfg.batch * args.steps / elapsed
+
+    # ---- per-phase latency (separate, synchronised calls)
+    pre_ms, den_ms, stp_ms = [], [], []
+    for _ in range(5):
+        kv, tp = vla.vla_prefix_encode(model, zt, kv_storage=kv_storage, timing=True)
+        _, td = vla.vla_denoise_chunk(model, kv, xt, cfg.steps, out=out, timing=True)
+        kv.close()
+        pre_ms.append(tp["prefix_ms"])
+        den_ms.append(td["denoise_ms"])
+        stp_ms.append(td["step_ms"])
+    phases = {"prefix_ms": float(np.median(pre_ms)), "denoise_ms": float(np.median(den_ms)),
+              "denoise_step_ms": float(np.median(stp_ms))}
+    pf = prefix_flops(cfg)
+    sb = expert_step_bytes(cfg)
+    phases["prefix_mfma_frac"] = pf / (phases["prefix_ms"] * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
+    phases["denoise_hbm_frac"] = sb / (phases["denoise_step_ms"] * 1e-3) / (PEAK_HBM_GBS * 1e9)
+
+    # ---- roofline of the dominant kernel: prefix gate/up GEMM (GeGLU epilogue)
+    N = cfg.n_prefix * cfg.batch
+    flops_per_launch = 2 * N * cfg.d_p * 2 * cfg.F_p
+    avg_ms = probe_ms / max(probe_launches, 1)
+    achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "k_gemm_bf16 (prefix gate/up + GeGLU)",
+                "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "avg_launch_us": avg_ms * 1e3, "launches": probe_launches,
+                "flops_per_launch": flops_per_launch}
+
+    # ---- CPU oracle on a bounded sample
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, w, betas, z0, x0, args.cpu_sample_s)
+
+    model.close()
+    rec = {
+        "metric": "action chunks/s at batch 1 (prefix+denoise), % of MFMA / HBM roofline",
+        "value": value, "unit": "chunks/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "prefix_tokens": cfg.n_prefix,
+                   "prefix_layers": cfg.L_p, "d_prefix": cfg.d_p, "expert_layers": cfg.L_e, "d_expert": cfg.d_e,
+                   "chunk": [cfg.H, cfg.d_a], "solver_steps": cfg.steps},
+        "phases": phases,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(cfg, w, betas, z0, x0, budget_s):
+    """The oracle, as it stands, on host cores: prefix layers then solver steps, stopped at the budget.
+
+    Time per chunk is extrapolated from the measured per-layer costs: the prefix
+    layers actually run, and whole expert velocity evaluations actually run.
+    """
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    o = oracle.Oracle(cfg, w, betas)
+    t0 = time.perf_counter()
+    h = np.asarray(z0[0], dtype=np.float64)
+    layers_done = 0
+    for l in range(cfg.L_p):
+        h = o.prefix_layer(h, l)
+        layers_done += 1
+        if time.perf_counter() - t0 > budget_s / 2:
+            break
+    t_pre = (time.perf_counter() - t0) / layers_done * cfg.L_p
+    z = oracle.rms_norm(h, o._w("prefix.norm"), cfg.rms_eps)
+    t1 = time.perf_counter()
+    cache = o.cache_project(z)
+    t_cache = time.perf_counter() - t1
+    x = np.asarray(x0[0], dtype=np.float64)
+    sched = oracle.uniform_schedule(cfg.steps)
+    t2 = time.perf_counter()
+    steps_done = 0
+    for k in range(cfg.steps):
+        x = x + (sched[k + 1] - sched[k]) * o.velocity(x, sched[k], cache)
+        steps_done += 1
+        if time.perf_counter() - t2 > budget_s / 2:
+            break
+    t_step = (time.perf_counter() - t2) / steps_done
+    t_chunk = t_pre + t_cache + cfg.steps * t_step
+    return {"value": 1.0 / t_chunk, "unit": "chunks/s", "cores": threads, "kind": "oracle",
+            "sample": f"one observation: {layers_done} of {cfg.L_p} prefix layers, the cache projection and "
+                      f"{steps_done} of {cfg.steps} solver steps run in float64 numpy, the rest extrapolated "
+                      f"from the measured per-layer and per-step times",
+            "seconds_measured": time.perf_counter() - t0,
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

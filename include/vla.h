@@ -157,10 +157,11 @@ size_t vla_kv_cache_bytes(const vla_model* model, int32_t batch, int32_t n_prefi
  * RMSNorm, and projects the result into every expert layer's K and V, written
  * to `kv_storage` (device, caller-owned, >= vla_kv_cache_bytes bytes, layout as
  * above).  *out receives a handle that refers to kv_storage; it stays valid
- * until vla_kv_cache_release and may serve any number of denoise calls. */
+ * until vla_kv_cache_release and may serve any number of denoise calls.
+ * `timing` (nullable) receives prefix_ms and makes the call synchronise. */
 vla_status vla_prefix_encode(vla_model* model, const float* prefix_hidden, int32_t batch,
                              int32_t n_prefix, void* kv_storage, size_t kv_bytes,
-                             void* stream, vla_kv_cache** out);
+                             void* stream, vla_kv_cache** out, vla_timing* timing);
 
 /* Flow-matching solver (the paper, §III-A, Eq. 1): X^0 = noise (device float32
  * [batch][H][d_a], batch and n_prefix taken from the cache), `steps` Euler
@@ -199,6 +200,25 @@ vla_status vla_w2a8_gemm(const int8_t* a, const float* alpha, const uint8_t* q_p
  * (VLA_ERR_INVALID_ARGUMENT on a code 3). */
 vla_status vla_ternary_pack(const int8_t* q, int32_t N, int32_t K, uint8_t* packed);
 vla_status vla_ternary_unpack(const uint8_t* packed, int32_t N, int32_t K, int8_t* q);
+
+/* Kernel probes, for measurement.  While a probe is armed on a model, each of
+ * the next `max_launches` launches of the chosen kernel class issued by that
+ * model outside a HIP graph is bracketed by a pair of HIP events on the stream
+ * it runs on.  vla_probe_read synchronises those events and returns the summed
+ * device time of the bracketed launches and their count; arming again resets
+ * the probe, kind 0 disarms it.  Probes add two event records per launch and
+ * nothing else to the measured work. */
+typedef enum {
+  VLA_PROBE_NONE = 0,
+  VLA_PROBE_PREFIX_GATEUP = 1, /* prefix gate/up projection with the GeGLU epilogue */
+  VLA_PROBE_PREFIX_DOWN = 2,   /* prefix down projection                            */
+  VLA_PROBE_PREFIX_QKV = 3,    /* prefix fused Q/K/V projection                     */
+  VLA_PROBE_PREFIX_ATTN = 4,   /* prefix bidirectional attention                    */
+  VLA_PROBE_PREFIX_O = 5,      /* prefix output projection                          */
+  VLA_PROBE_CACHE = 6          /* cache-writing projection                          */
+} vla_probe_kind;
+vla_status vla_probe_arm(vla_model* model, int32_t kind, int32_t max_launches);
+vla_status vla_probe_read(vla_model* model, float* total_ms, int32_t* launches);
 
 #ifdef __cplusplus
 }

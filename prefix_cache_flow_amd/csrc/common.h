@@ -34,6 +34,10 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
 // exact erf-form GELU, 0.5 x (1 + erf(x / sqrt 2)), using the device erff
 __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
+// 2^x on the hardware exponential unit (one instruction; results below the
+// normal range flush to zero, 2^-inf = 0).  Used for softmax weights in (0, 1].
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

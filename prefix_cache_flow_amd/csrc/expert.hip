@@ -18,43 +18,43 @@ __device__ __forceinline__ float ld_w(const void* w, long i) {
   return bf2f(((const bf16_t*)w)[i]);
 }
 
-// One 256-thread workgroup per chunk row m; d_e <= 4096, d_a <= 256.
+// One 256-thread workgroup per chunk row m; d_e <= 4096, d_a <= 256.  The
+// row's d_a inputs sit in LDS; each thread loads its weight rows for all of
+// its outputs before using any (clamped indices, masked products).
 template <bool WF32>
 __global__ __launch_bounds__(256) void k_embed(const float* X, int d_a, const void* w_in, int d_e, const float* sched,
                                                int k, float* E, const float* gain, float eps, void* u, int u_f32) {
   __shared__ float xs[256];
+  __shared__ float es[4096];
   __shared__ float red[4];
   const int m = blockIdx.x;
   if (threadIdx.x < d_a) xs[threadIdx.x] = X[(long)m * d_a + threadIdx.x];
   __syncthreads();
   const float tau = sched[k];
   const float l2 = 13.287712379549449f;  // log2(10000)
-  float vals[16];
   float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int n = threadIdx.x + i * 256;
+  for (int n = threadIdx.x; n < d_e; n += 256) {
     float v = 0.f;
-    if (n < d_e) {
-      for (int a = 0; a < d_a; ++a) v = fmaf(xs[a], ld_w<WF32>(w_in, (long)n * d_a + a), v);
-      const int pair = n >> 1;
-      const float freq = exp2f(-l2 * (2.0f * (float)pair / (float)d_e));
-      const float arg = tau * freq;
-      v += (n & 1) ? cosf(arg) : sinf(arg);
-      E[(long)m * d_e + n] = v;
+    for (int a0 = 0; a0 < d_a; a0 += 8) {
+      float wv[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) wv[t] = ld_w<WF32>(w_in, (long)n * d_a + min(a0 + t, d_a - 1));
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v = fmaf(a0 + t < d_a ? xs[a0 + t] : 0.f, wv[t], v);
     }
-    vals[i] = v;
+    // phi: frequency 10000^(-2i/d) on the exponential unit, angle tau * freq <= |tau|
+    const float freq = fast_exp2(-l2 * (2.0f * (float)(n >> 1) / (float)d_e));
+    const float arg = tau * freq;
+    v += (n & 1) ? __cosf(arg) : __sinf(arg);
+    E[(long)m * d_e + n] = v;
+    es[n] = v;
     ss = fmaf(v, v, ss);
   }
   ss = block_sum<256>(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)d_e + eps);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int n = threadIdx.x + i * 256;
-    if (n < d_e) {
-      const float un = vals[i] * r * (1.0f + gain[n]);
-      if (u_f32) ((float*)u)[(long)m * d_e + n] = un; else ((bf16_t*)u)[(long)m * d_e + n] = f2bf(un);
-    }
+  for (int n = threadIdx.x; n < d_e; n += 256) {
+    const float un = es[n] * r * (1.0f + gain[n]);
+    if (u_f32) ((float*)u)[(long)m * d_e + n] = un; else ((bf16_t*)u)[(long)m * d_e + n] = f2bf(un);
   }
 }
 
@@ -70,11 +70,15 @@ hipError_t expert_embed(const float* X, int M, int d_a, const void* w_in, int w_
 }
 
 // One 256-thread workgroup per chunk row: final RMSNorm, W_out, Euler update.
+// The normalized row goes to LDS; then G = 8 threads share each output: thread
+// t takes output t / 8 (and every 32nd after it) and the t % 8-th slice of the
+// row, loads that slice of the weight row before using it, and the eight
+// partial dot products are summed with lane exchanges in a fixed order.
 template <bool WF32>
 __global__ __launch_bounds__(256) void k_head(const float* E, int d_e, const float* gain, float eps, const void* w_out,
                                               int d_a, const float* sched, int k, float* X) {
-  __shared__ float us[4096];
   __shared__ float red[4];
+  __shared__ float us[4096];
   const int m = blockIdx.x;
   float ss = 0.f;
   for (int n = threadIdx.x; n < d_e; n += 256) {
@@ -87,12 +91,34 @@ __global__ __launch_bounds__(256) void k_head(const float* E, int d_e, const flo
   for (int n = threadIdx.x; n < d_e; n += 256) us[n] = us[n] * r * (1.0f + gain[n]);
   __syncthreads();
   const float dt = sched[k + 1] - sched[k];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  for (int a = wid; a < d_a; a += 4) {
-    float v = 0.f;
-    for (int n = lane; n < d_e; n += 64) v = fmaf(us[n], ld_w<WF32>(w_out, (long)a * d_e + n), v);
-    v = wave_sum(v);
-    if (lane == 0) X[(long)m * d_a + a] += dt * v;
+  constexpr int G = 8;
+  const int slice = d_e / G;  // d_e % 64 == 0 for bf16 weights (8-element vectors)
+  const int part = threadIdx.x % G;
+  for (int a = threadIdx.x / G; a < d_a; a += 256 / G) {
+    float acc = 0.f;
+    if (WF32) {
+      for (int n = part; n < d_e; n += G) acc = fmaf(us[n], ld_w<true>(w_out, (long)a * d_e + n), acc);
+    } else {
+      const bf16_t* wr = (const bf16_t*)w_out + (long)a * d_e + part * slice;
+      for (int c = 0; c < slice; c += 128) {  // 16 vectors of 8 weights in flight at once
+        u32x4_t wv[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) wv[t] = *(const u32x4_t*)(wr + min(c + t * 8, slice - 8));
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          if (c + t * 8 >= slice) break;
+          const float* ur = &us[part * slice + c + t * 8];
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            acc = fmaf(ur[2 * h], bf2f((bf16_t)(wv[t][h] & 0xffffu)), acc);
+            acc = fmaf(ur[2 * h + 1], bf2f((bf16_t)(wv[t][h] >> 16)), acc);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) acc += __shfl_xor(acc, o, 64);
+    if (part == 0) X[(long)m * d_a + a] += dt * acc;
   }
 }
 

@@ -38,18 +38,28 @@ __device__ __forceinline__ void cache_index(const Epilogue& e, int m, int n, lon
   idx = ((((long)(b * e.L + l) * 2 + kv) * e.hkv + h) * e.npre + t) * e.hd + d;
 }
 
-// Store one finished element (every kind but GEGLU, which needs a pair).
-__device__ __forceinline__ void epi_store(const Epilogue& e, int m, int n, float v) {
-  if (e.kind == EPI_STORE) {
+// Store one finished element (every kind but GEGLU, which needs a pair).  The
+// kind is a template parameter so a kernel carries only its own store path:
+// kernels here start with a cold instruction cache, and in a chain of short
+// kernels their code size is latency.
+template <int KIND>
+__device__ __forceinline__ void epi_store_t(const Epilogue& e, int m, int n, float v) {
+  if (KIND == EPI_STORE) {
     const long i = (long)m * e.ldo + n;
     if (e.out_f32) ((float*)e.out)[i] = v; else ((bf16_t*)e.out)[i] = f2bf(v);
-  } else if (e.kind == EPI_RESID) {
+  } else if (KIND == EPI_RESID) {
     e.resid[(long)m * e.ldr + n] += v;
-  } else if (e.kind == EPI_CACHE) {
+  } else if (KIND == EPI_CACHE) {
     long i;
     cache_index(e, m, n, i);
     if (e.out_f32) ((float*)e.out)[i] = v; else ((bf16_t*)e.out)[i] = f2bf(v);
   }
+}
+
+__device__ __forceinline__ void epi_store(const Epilogue& e, int m, int n, float v) {
+  if (e.kind == EPI_STORE) epi_store_t<EPI_STORE>(e, m, n, v);
+  else if (e.kind == EPI_RESID) epi_store_t<EPI_RESID>(e, m, n, v);
+  else if (e.kind == EPI_CACHE) epi_store_t<EPI_CACHE>(e, m, n, v);
 }
 
 __device__ __forceinline__ void epi_geglu(const Epilogue& e, int m, int f, float g, float u) {
@@ -58,15 +68,20 @@ __device__ __forceinline__ void epi_geglu(const Epilogue& e, int m, int f, float
   if (e.out_f32) ((float*)e.out)[i] = v; else ((bf16_t*)e.out)[i] = f2bf(v);
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int KIND>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GemmP p) {
   constexpr int NT = 64 * WM * WN, BK = 64, LDK = BK + 8;
   constexpr int TM = BM / (32 * WM), TN = BN / (32 * WN);
   static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "tile shape");
   constexpr int AV = BM * BK / 8, WV = BN * BK / 8;  // 16-byte vectors per slice
   constexpr int AVT = (AV + NT - 1) / NT, WVT = (WV + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][BN * LDK];
+  constexpr int LDC = BN + 4;                         // epilogue tile row stride (floats)
+  constexpr int STAGE = 2 * (BM + BN) * LDK * 2;      // bytes of the two staging buffers
+  static_assert(BM * LDC * 4 <= STAGE, "epilogue tile must fit in the staging area");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDK];
+  // buffer b of the activation tile at smem + b * BM * LDK, of the weight tile after both
+  auto sA = [&](int b) { return smem + b * (BM * LDK); };
+  auto sW = [&](int b) { return smem + 2 * BM * LDK + b * (BN * LDK); };
 
   const int nt = p.nM * p.nN, L = blockIdx.x;
   const int tile = (nt % 8 == 0) ? (L % 8) * (nt / 8) + L / 8 : L;
@@ -83,16 +98,16 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GemmP p) {
     for (int i = 0; i < AVT; ++i) {
       const int v = tid + i * NT;
       if (AV % NT == 0 || v < AV) {
-        const int r = v >> 3, c = (v & 7) * 8, gm = m0 + r;
-        ra[i] = gm < p.M ? *(const u32x4_t*)(p.A + (long)gm * p.lda + k0 + c) : u32x4_t{0, 0, 0, 0};
+        const int r = v >> 3, c = (v & 7) * 8, gm = min(m0 + r, p.M - 1);  // clamped rows are never stored
+        ra[i] = *(const u32x4_t*)(p.A + (long)gm * p.lda + k0 + c);
       }
     }
 #pragma unroll
     for (int i = 0; i < WVT; ++i) {
       const int v = tid + i * NT;
       if (WV % NT == 0 || v < WV) {
-        const int r = v >> 3, c = (v & 7) * 8, gn = n0 + r;
-        rw[i] = gn < p.N ? *(const u32x4_t*)(p.W + (long)gn * p.ldw + k0 + c) : u32x4_t{0, 0, 0, 0};
+        const int r = v >> 3, c = (v & 7) * 8, gn = min(n0 + r, p.N - 1);
+        rw[i] = *(const u32x4_t*)(p.W + (long)gn * p.ldw + k0 + c);
       }
     }
   };
@@ -100,12 +115,12 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GemmP p) {
 #pragma unroll
     for (int i = 0; i < AVT; ++i) {
       const int v = tid + i * NT;
-      if (AV % NT == 0 || v < AV) *(u32x4_t*)&sA[buf][(v >> 3) * LDK + (v & 7) * 8] = ra[i];
+      if (AV % NT == 0 || v < AV) *(u32x4_t*)&sA(buf)[(v >> 3) * LDK + (v & 7) * 8] = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < WVT; ++i) {
       const int v = tid + i * NT;
-      if (WV % NT == 0 || v < WV) *(u32x4_t*)&sW[buf][(v >> 3) * LDK + (v & 7) * 8] = rw[i];
+      if (WV % NT == 0 || v < WV) *(u32x4_t*)&sW(buf)[(v >> 3) * LDK + (v & 7) * 8] = rw[i];
     }
   };
 
@@ -133,10 +148,10 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GemmP p) {
       const int koff = kk * 16 + (lane >> 5) * 8;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = as_bf16x8(*(const u32x4_t*)&sA[buf][((wm * TM + i) * 32 + (lane & 31)) * LDK + koff]);
+        af[i] = as_bf16x8(*(const u32x4_t*)&sA(buf)[((wm * TM + i) * 32 + (lane & 31)) * LDK + koff]);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        wf[j] = as_bf16x8(*(const u32x4_t*)&sW[buf][((wn * TN + j) * 32 + (lane & 31)) * LDK + koff]);
+        wf[j] = as_bf16x8(*(const u32x4_t*)&sW(buf)[((wn * TN + j) * 32 + (lane & 31)) * LDK + koff]);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -146,26 +161,33 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GemmP p) {
     __syncthreads();
   }
 
-  // ---- epilogue
-  const bool partial = gridDim.y > 1 || p.epi.kind == EPI_PARTIAL;
+  // ---- epilogue: the tile goes through LDS, then a rolled loop stores it row by row
+  float* ct = (float*)smem;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = n0 + (wn * TN + j) * 32 + (lane & 31);
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + (wm * TM + i) * 32 + mfma32_row(e, lane);
-        const float v = acc[i][j][e];
-        if (partial) {
-          if (m < p.M && n < p.N) p.ws[((long)blockIdx.y * p.M + m) * p.N + n] = v;
-        } else if (p.epi.kind == EPI_GEGLU) {
-          const float other = __shfl_xor(v, 16, 64);
-          if (!(lane & 16) && m < p.M && n < p.N) epi_geglu(p.epi, m, (n >> 5) * 16 + (lane & 15), v, other);
-        } else if (m < p.M && n < p.N) {
-          epi_store(p.epi, m, n, v);
-        }
-      }
+      for (int e = 0; e < 16; ++e)
+        ct[((wm * TM + i) * 32 + mfma32_row(e, lane)) * LDC + (wn * TN + j) * 32 + (lane & 31)] = acc[i][j][e];
+  __syncthreads();
+  const int rows = min(BM, p.M - m0);
+  if (KIND == EPI_GEGLU) {
+    // column 32 b + c (c < 16) is gate feature 16 b + c, column 32 b + 16 + c its up value
+    constexpr int FW = BN / 2;
+    for (int idx = tid; idx < rows * FW; idx += NT) {
+      const int r = idx / FW, f = idx % FW;
+      const int cg = (f >> 4) * 32 + (f & 15);
+      epi_geglu(p.epi, m0 + r, (n0 >> 1) + f, ct[r * LDC + cg], ct[r * LDC + cg + 16]);
+    }
+  } else {
+    for (int idx = tid; idx < rows * BN; idx += NT) {
+      const int r = idx / BN, c = idx % BN;
+      const int m = m0 + r, n = n0 + c;
+      if (n >= p.N) continue;
+      const float v = ct[r * LDC + c];
+      if (KIND == EPI_PARTIAL) p.ws[((long)blockIdx.y * p.M + m) * p.N + n] = v;
+      else epi_store_t<KIND>(p.epi, m, n, v);
     }
   }
 }
@@ -193,6 +215,158 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* ws, int spli
   }
 }
 
+
+// ------------------------------------------------------------------ skinny M
+// Activations of at most 64 rows (the action chunk).  The contraction is a
+// weight stream.  A workgroup of four waves owns 16 * NB output columns; the
+// four waves split the workgroup's K range, each taking at most eight k-steps
+// of 32, and every wave issues all of its weight and activation loads at once
+// (straight from global memory, the activations staying in L2) before the
+// 16x16x32 MFMAs, so one memory round trip covers the whole slice.  The four
+// partial tiles are then summed through LDS in wave order.  With NB = 2 and the
+// gate/up interleave, lane l holds the gate and the up value of one feature.
+// Rows past M and k-steps past the range are clamped to valid addresses and
+// masked to zero instead of branching around the loads.
+struct SkinnyP {
+  const uint16_t* A;
+  int lda;
+  const uint16_t* W;
+  int ldw;
+  int M, N, K, kchunk;
+  Epilogue epi;
+  float* ws;
+};
+
+constexpr int kSkinnySteps = 8;  // k-steps of 32 per wave
+
+template <int NB, int KIND>
+__global__ __launch_bounds__(256) void k_skinny(SkinnyP p) {
+  constexpr int SPW = kSkinnySteps;
+  __shared__ float red[4][4 * NB * 4][64];  // [wave][row block, column block, element][lane]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int n0 = blockIdx.x * 16 * NB;
+  const int kw = p.kchunk / 4;
+  const int kb = blockIdx.y * p.kchunk + w * kw;
+  const int ke = min(p.K, kb + kw);
+  const int nsteps = max(0, ke - kb) / 32;
+
+  const uint16_t* wp[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) wp[nb] = p.W + (long)(n0 + nb * 16 + col) * p.ldw + grp * 8;
+  const uint16_t* ap[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) ap[rb] = p.A + (long)min(rb * 16 + col, p.M - 1) * p.lda + grp * 8;
+
+  u32x4_t wv[SPW][NB], av[SPW][4];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const int k = min(kb + s * 32, p.K - 32);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) wv[s][nb] = *(const u32x4_t*)(wp[nb] + k);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) av[s][rb] = *(const u32x4_t*)(ap[rb] + k);
+  }
+  f32x4_t acc[4][NB];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const bool on = s < nsteps;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const u32x4_t a4 = on ? av[s][rb] : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = mfma16x16x32(as_bf16x8(a4), as_bf16x8(wv[s][nb]), acc[rb][nb]);
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[w][(rb * NB + nb) * 4 + e][lane] = acc[rb][nb][e];
+  __syncthreads();
+
+  // wave w finishes row block w: sum the four K ranges in order, then the epilogue
+  const int rb = w;
+  float v[NB][4];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = (rb * NB + nb) * 4 + e;
+      v[nb][e] = red[0][idx][lane] + red[1][idx][lane] + red[2][idx][lane] + red[3][idx][lane];
+    }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int m = rb * 16 + grp * 4 + e;
+    if (m >= p.M) continue;
+    if (KIND == EPI_GEGLU) {
+      epi_geglu(p.epi, m, (n0 >> 5) * 16 + col, v[0][e], v[NB - 1][e]);
+      continue;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = n0 + nb * 16 + col;
+      if (KIND == EPI_PARTIAL) p.ws[((long)blockIdx.y * p.M + m) * p.N + n] = v[nb][e];
+      else epi_store_t<KIND>(p.epi, m, n, v[nb][e]);
+    }
+  }
+}
+
+// K is cut into `used` workgroup chunks of a multiple of 4 k-steps each and at
+// most 4 * kSkinnySteps k-steps; `splits` asks for more chunks than that floor.
+static void skinny_plan(int K, int splits, int* used, int* per_steps) {
+  const int steps = K / 32;
+  const int cap = 4 * kSkinnySteps;
+  int u0 = std::max((steps + cap - 1) / cap, std::min(std::max(splits, 1), (steps + 3) / 4));
+  u0 = std::max(u0, 1);
+  int per = (steps + u0 - 1) / u0;
+  per = (per + 3) / 4 * 4;
+  *per_steps = per;
+  *used = (steps + per - 1) / per;
+}
+
+int gemm_skinny_splits(int K, int splits) {
+  int used, per;
+  skinny_plan(K, splits, &used, &per);
+  return used;
+}
+
+template <int NB>
+static hipError_t launch_skinny(const SkinnyP& p0, int splits, hipStream_t s) {
+  SkinnyP p = p0;
+  int used, per;
+  skinny_plan(p.K, splits, &used, &per);
+  p.kchunk = per * 32;
+  const dim3 grid(p.N / (16 * NB), used);
+  const int kind = used > 1 ? EPI_PARTIAL : p.epi.kind;
+  if constexpr (NB == 2) {
+    if (kind != EPI_GEGLU) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_skinny<2, EPI_GEGLU>), grid, dim3(256), 0, s, p);
+  } else {
+    switch (kind) {
+      case EPI_STORE: hipLaunchKernelGGL((k_skinny<1, EPI_STORE>), grid, dim3(256), 0, s, p); break;
+      case EPI_RESID: hipLaunchKernelGGL((k_skinny<1, EPI_RESID>), grid, dim3(256), 0, s, p); break;
+      case EPI_CACHE: hipLaunchKernelGGL((k_skinny<1, EPI_CACHE>), grid, dim3(256), 0, s, p); break;
+      case EPI_PARTIAL: hipLaunchKernelGGL((k_skinny<1, EPI_PARTIAL>), grid, dim3(256), 0, s, p); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (used > 1 && p.epi.kind != EPI_PARTIAL) {
+    const long tot = (long)p.M * p.N;
+    const int blocks = (int)std::min<long>((tot + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, (const float*)p.ws, used, p.M, p.N, p.epi);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
 template <int BM, int BN, int WM, int WN>
 static hipError_t launch_bf16(const GemmP& p, int splits, hipStream_t s) {
   GemmP q = p;
@@ -201,9 +375,16 @@ static hipError_t launch_bf16(const GemmP& p, int splits, hipStream_t s) {
   const int slices = p.K / 64;
   const int per = (slices + splits - 1) / splits;
   q.kchunk = per * 64;
-  const int used = (slices + per - 1) / per;
+  const int used = (slices + per - 1) / per;  // == splits for counts from gemm_bf16_splits
   dim3 grid(q.nM * q.nN, used);
-  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN>), grid, dim3(64 * WM * WN), 0, s, q);
+  const int kind = used > 1 ? EPI_PARTIAL : p.epi.kind;
+  switch (kind) {
+    case EPI_STORE: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_STORE>), grid, dim3(64 * WM * WN), 0, s, q); break;
+    case EPI_RESID: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_RESID>), grid, dim3(64 * WM * WN), 0, s, q); break;
+    case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_GEGLU>), grid, dim3(64 * WM * WN), 0, s, q); break;
+    case EPI_CACHE: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_CACHE>), grid, dim3(64 * WM * WN), 0, s, q); break;
+    default: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_PARTIAL>), grid, dim3(64 * WM * WN), 0, s, q); break;
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (used > 1 && p.epi.kind != EPI_PARTIAL) {
@@ -215,7 +396,8 @@ static hipError_t launch_bf16(const GemmP& p, int splits, hipStream_t s) {
   return err;
 }
 
-int gemm_bf16_splits(int K, int splits) {
+int gemm_bf16_splits(int K, int splits, int M) {
+  if (M <= 64) return gemm_skinny_splits(K, splits);
   const int slices = K / 64;
   if (slices <= 0) return 1;
   splits = std::max(1, std::min(splits, slices));
@@ -227,13 +409,22 @@ hipError_t gemm_bf16(const uint16_t* A, int lda, const uint16_t* W, int ldw, int
                      const Epilogue& epi, int splits, float* ws, hipStream_t s) {
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
   if (K % 64 || N % 32) return hipErrorInvalidValue;
-  if (splits < 1) splits = 1;
-  if (splits > K / 64) splits = K / 64;
+  // the one place that fixes how many partial slices are written: callers that
+  // consume EPI_PARTIAL output read gemm_bf16_splits(K, splits, M) of them
+  splits = gemm_bf16_splits(K, splits, M);
   GemmP p{A, lda, W, ldw, M, N, K, 0, 0, 0, epi, ws};
   if ((splits > 1 || epi.kind == EPI_PARTIAL) && !ws) return hipErrorInvalidValue;
-  // Tile choice: skinny row counts (the action chunk) take 64-row tiles, the
-  // prefix (hundreds of rows) 96 x 128 tiles, four waves of 96 x 32.
-  if (M <= 64) return launch_bf16<64, 64, 2, 2>(p, splits, s);
+  // Tile choice: skinny row counts (the action chunk) stream weights one wave
+  // per 16 or 32 columns; the prefix (hundreds of rows) takes 96 x 128 tiles,
+  // four waves of 96 x 32.
+  if (M <= 64) {
+    SkinnyP q{A, lda, W, ldw, M, N, K, 0, epi, ws};
+    if (epi.kind == EPI_GEGLU) {
+      if (splits > 1) return hipErrorInvalidValue;  // GeGLU needs whole sums
+      return launch_skinny<2>(q, splits, s);
+    }
+    return launch_skinny<1>(q, splits, s);
+  }
   return launch_bf16<96, 128, 1, 4>(p, splits, s);
 }
 

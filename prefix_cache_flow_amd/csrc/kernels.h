@@ -37,12 +37,13 @@ struct Epilogue {
 
 // C = A[M,K] W[N,K]^T, bf16 operands, fp32 accumulation on MFMA; `splits` > 1
 // splits K and reduces the partial sums in a fixed order in `ws`
-// (splits * M * N floats).  K % 64 == 0, N % 32 == 0.
+// (splits * M * N floats).  K % 64 == 0, N % 32 == 0.  At most 64 rows take the
+// weight-streaming skinny kernel (GeGLU there needs splits == 1).
 hipError_t gemm_bf16(const uint16_t* A, int lda, const uint16_t* W, int ldw, int M, int N, int K,
                      const Epilogue& epi, int splits, float* ws, hipStream_t s);
 
-// Number of K splits gemm_bf16 actually uses for a request of `splits`.
-int gemm_bf16_splits(int K, int splits);
+// Number of K splits gemm_bf16 actually uses for a request of `splits` at M rows.
+int gemm_bf16_splits(int K, int splits, int M);
 
 // Same contraction in fp32 on the vector ALU (fp32 workloads); K % 16 == 0.
 hipError_t gemm_f32(const float* A, int lda, const float* W, int ldw, int M, int N, int K,

@@ -34,25 +34,40 @@ __device__ __forceinline__ void quantize_store(const float* x, int per, int N, i
   if (threadIdx.x == 0) *alpha_out = alpha;
 }
 
-template <int PER>
+// NS is a compile-time bound on the split count: every load of the row and of
+// its partials is issued before any is used (partials past nsplit re-read the
+// last one at a valid address and are masked out).
+template <int PER, int NS>
 __global__ __launch_bounds__(256) void k_resid_norm(float* h, int ldh, const float* part, int nsplit, int M, int N,
                                                     const float* gain, float eps, void* u, int u_f32, int ldu,
                                                     int8_t* q, float* alpha) {
   __shared__ float red[4];
   const int m = blockIdx.x;
   float x[PER];
+  float pv[NS > 0 ? NS : 1][PER];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int n = threadIdx.x + i * 256;
-    float v = 0.f;
-    if (n < N) {
-      v = h[(long)m * ldh + n];
-      for (int s = 0; s < nsplit; ++s) v += part[((long)s * M + m) * N + n];
-      if (nsplit > 0) h[(long)m * ldh + n] = v;
+    const int n = min(threadIdx.x + i * 256, N - 1);
+    x[i] = h[(long)m * ldh + n];
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int n = min(threadIdx.x + i * 256, N - 1);
+      pv[s][i] = part[((long)min(s, nsplit - 1) * M + m) * N + n];
     }
-    x[i] = v;
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) x[i] += s < nsplit ? pv[s][i] : 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int n = threadIdx.x + i * 256;
+    if (n >= N) x[i] = 0.f;
+    if (NS > 0 && n < N) h[(long)m * ldh + n] = x[i];
+    ss = fmaf(x[i], x[i], ss);
   }
   ss = block_sum<256>(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)N + eps);
@@ -74,21 +89,32 @@ __global__ __launch_bounds__(256) void k_resid_norm(float* h, int ldh, const flo
   if (q) quantize_store(x, PER, N, q + (long)m * N, alpha + m, red);
 }
 
+template <int PER>
+static void launch_rn(int nsplit, hipStream_t s, float* h, int ldh, const float* part, int M, int N,
+                      const float* gain, float eps, void* u_out, int u_f32, int ldu, int8_t* q_out, float* alpha_out) {
+#define VLA_RN(NS)                                                                                             \
+  hipLaunchKernelGGL((k_resid_norm<PER, NS>), dim3(M), dim3(256), 0, s, h, ldh, part, nsplit, M, N, gain, eps, \
+                     u_out, u_f32, ldu, q_out, alpha_out)
+  if (nsplit <= 0) VLA_RN(0);
+  else if (nsplit <= 1) VLA_RN(1);
+  else if (nsplit <= 4) VLA_RN(4);
+  else if (nsplit <= 8) VLA_RN(8);
+  else VLA_RN(16);
+#undef VLA_RN
+}
+
 hipError_t resid_norm(float* h, int ldh, const float* part, int nsplit, int M, int N, const float* gain, float eps,
                       void* u_out, int u_f32, int ldu, int8_t* q_out, float* alpha_out, hipStream_t s) {
   if (M <= 0) return hipSuccess;
+  if (nsplit > 16) return hipErrorInvalidValue;
   const int per = (N + 255) / 256;
-#define VLA_RN(P)                                                                                          \
-  hipLaunchKernelGGL(k_resid_norm<P>, dim3(M), dim3(256), 0, s, h, ldh, part, nsplit, M, N, gain, eps, u_out, \
-                     u_f32, ldu, q_out, alpha_out)
-  if (per <= 1) VLA_RN(1);
-  else if (per <= 2) VLA_RN(2);
-  else if (per <= 4) VLA_RN(4);
-  else if (per <= 8) VLA_RN(8);
-  else if (per <= 12) VLA_RN(12);
-  else if (per <= 16) VLA_RN(16);
+  if (per <= 1) launch_rn<1>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out);
+  else if (per <= 2) launch_rn<2>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out);
+  else if (per <= 4) launch_rn<4>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out);
+  else if (per <= 8) launch_rn<8>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out);
+  else if (per <= 12) launch_rn<12>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out);
+  else if (per <= 16) launch_rn<16>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out);
   else return hipErrorInvalidValue;
-#undef VLA_RN
   return hipGetLastError();
 }
 
@@ -100,7 +126,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* x, int ldx, int K
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int n = threadIdx.x + i * 256;
-    v[i] = n < K ? x[(long)m * ldx + n] : 0.f;
+    v[i] = x[(long)m * ldx + min(n, K - 1)];  // entries past K are never used
   }
   quantize_store(v, PER, K, a + (long)m * K, alpha + m, red);
 }

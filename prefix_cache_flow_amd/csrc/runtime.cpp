@@ -209,6 +209,10 @@ struct vla_model {
   std::set<vla_kv_cache*> caches;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   int64_t plan_rows = 0, plan_erows = 0;  // largest prefix / chunk row counts seen
+  // kernel probe
+  int probe_kind = 0, probe_max = 0, probe_used = 0;
+  std::vector<hipEvent_t> probe_ev;
+  hipStream_t probe_stream = nullptr;
 };
 
 struct vla_kv_cache {
@@ -274,6 +278,7 @@ static void free_model(vla_model* m) {
   if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
   if (m->ev0) (void)hipEventDestroy(m->ev0);
   if (m->ev1) (void)hipEventDestroy(m->ev1);
+  for (hipEvent_t e : m->probe_ev) (void)hipEventDestroy(e);
   m->magic = 0;
   delete m;
 }
@@ -551,7 +556,7 @@ struct WS {
 };
 
 static const int kPrefixSplits = 4;
-static const int kExpertSplits = 16;
+static const int kExpertSplits = 4;
 
 static WS plan(const vla_model* m, int64_t rows, int64_t erows, char* base) {
   const vla_model_config& c = m->cfg;
@@ -634,6 +639,51 @@ static vla_status hip_ok(hipError_t e, const char* what) {
     if (st_ != VLA_OK) return st_;                 \
   } while (0)
 
+// Bracket one launch of kernel class `kind` with probe events when armed for it.
+struct ProbeScope {
+  vla_model* m;
+  bool on;
+  hipStream_t s;
+  ProbeScope(vla_model* m_, int kind, hipStream_t s_) : m(m_), on(false), s(s_) {
+    if (m->probe_kind == kind && m->probe_used < m->probe_max) {
+      on = hipEventRecord(m->probe_ev[2 * m->probe_used], s) == hipSuccess;
+    }
+  }
+  ~ProbeScope() {
+    if (on && hipEventRecord(m->probe_ev[2 * m->probe_used + 1], s) == hipSuccess) ++m->probe_used;
+  }
+};
+
+extern "C" vla_status vla_probe_arm(vla_model* m, int32_t kind, int32_t max_launches) {
+  if (!live_model(m)) return fail(VLA_ERR_INVALID_HANDLE, "unknown model");
+  if (kind < VLA_PROBE_NONE || kind > VLA_PROBE_CACHE) return fail(VLA_ERR_INVALID_ARGUMENT, "bad probe kind");
+  if (max_launches < 0 || max_launches > 100000) return fail(VLA_ERR_INVALID_ARGUMENT, "bad max_launches");
+  while ((int)m->probe_ev.size() < 2 * max_launches) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return fail(VLA_ERR_DEVICE, "event creation failed");
+    m->probe_ev.push_back(e);
+  }
+  m->probe_kind = kind;
+  m->probe_max = kind ? max_launches : 0;
+  m->probe_used = 0;
+  return VLA_OK;
+}
+
+extern "C" vla_status vla_probe_read(vla_model* m, float* total_ms, int32_t* launches) {
+  if (!live_model(m)) return fail(VLA_ERR_INVALID_HANDLE, "unknown model");
+  if (!total_ms || !launches) return fail(VLA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  double sum = 0.0;
+  for (int i = 0; i < m->probe_used; ++i) {
+    K_TRY(hipEventSynchronize(m->probe_ev[2 * i + 1]), "probe sync");
+    float ms = 0.f;
+    K_TRY(hipEventElapsedTime(&ms, m->probe_ev[2 * i], m->probe_ev[2 * i + 1]), "probe elapsed");
+    sum += ms;
+  }
+  *total_ms = (float)sum;
+  *launches = m->probe_used;
+  return VLA_OK;
+}
+
 static Epilogue epi_store(void* out, int ldo, int out_f32) {
   Epilogue e;
   e.kind = EPI_STORE;
@@ -702,17 +752,32 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
         K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, next_gain, eps, w.u, 1, c.d_p, nullptr, nullptr, s), "norm");
       } else {
         const uint16_t* u = (const uint16_t*)w.u;
-        K_TRY(gemm_bf16(u, c.d_p, (const uint16_t*)P.wqkv, c.d_p, M, qkvw, c.d_p, epi_store(w.qkv, qkvw, 0), 1, w.part, s), "qkv");
-        K_TRY(attention_bf16(aa, s), "attention");
+        {
+          ProbeScope ps(m, VLA_PROBE_PREFIX_QKV, s);
+          K_TRY(gemm_bf16(u, c.d_p, (const uint16_t*)P.wqkv, c.d_p, M, qkvw, c.d_p, epi_store(w.qkv, qkvw, 0), 1, w.part, s), "qkv");
+        }
+        {
+          ProbeScope ps(m, VLA_PROBE_PREFIX_ATTN, s);
+          K_TRY(attention_bf16(aa, s), "attention");
+        }
         Epilogue pe;
         pe.kind = EPI_PARTIAL;
-        K_TRY(gemm_bf16((const uint16_t*)w.attn, qw, (const uint16_t*)P.wo, qw, M, c.d_p, qw, pe, kPrefixSplits, w.part, s), "o proj");
-        K_TRY(resid_norm(w.h, c.d_p, w.part, gemm_bf16_splits(qw, kPrefixSplits), M, c.d_p, P.w2, eps, w.u, 0, c.d_p, nullptr, nullptr, s), "norm");
+        {
+          ProbeScope ps(m, VLA_PROBE_PREFIX_O, s);
+          K_TRY(gemm_bf16((const uint16_t*)w.attn, qw, (const uint16_t*)P.wo, qw, M, c.d_p, qw, pe, kPrefixSplits, w.part, s), "o proj");
+        }
+        K_TRY(resid_norm(w.h, c.d_p, w.part, gemm_bf16_splits(qw, kPrefixSplits, M), M, c.d_p, P.w2, eps, w.u, 0, c.d_p, nullptr, nullptr, s), "norm");
         Epilogue g = epi_store(w.mlp, c.F_p, 0);
         g.kind = EPI_GEGLU;
-        K_TRY(gemm_bf16(u, c.d_p, (const uint16_t*)P.wgu, c.d_p, M, 2 * c.F_p, c.d_p, g, 1, w.part, s), "gate/up");
-        K_TRY(gemm_bf16((const uint16_t*)w.mlp, c.F_p, (const uint16_t*)P.wd, c.F_p, M, c.d_p, c.F_p, pe, kPrefixSplits, w.part, s), "down");
-        K_TRY(resid_norm(w.h, c.d_p, w.part, gemm_bf16_splits(c.F_p, kPrefixSplits), M, c.d_p, next_gain, eps, w.u, 0, c.d_p, nullptr, nullptr, s), "norm");
+        {
+          ProbeScope ps(m, VLA_PROBE_PREFIX_GATEUP, s);
+          K_TRY(gemm_bf16(u, c.d_p, (const uint16_t*)P.wgu, c.d_p, M, 2 * c.F_p, c.d_p, g, 1, w.part, s), "gate/up");
+        }
+        {
+          ProbeScope ps(m, VLA_PROBE_PREFIX_DOWN, s);
+          K_TRY(gemm_bf16((const uint16_t*)w.mlp, c.F_p, (const uint16_t*)P.wd, c.F_p, M, c.d_p, c.F_p, pe, kPrefixSplits, w.part, s), "down");
+        }
+        K_TRY(resid_norm(w.h, c.d_p, w.part, gemm_bf16_splits(c.F_p, kPrefixSplits, M), M, c.d_p, next_gain, eps, w.u, 0, c.d_p, nullptr, nullptr, s), "norm");
       }
     }
   }
@@ -721,6 +786,7 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
   ce.kind = EPI_CACHE; ce.out = kv; ce.out_f32 = m->f32 ? 1 : 0;
   ce.npre = N; ce.L = c.L_e; ce.hkv = c.Hkv_e; ce.hd = c.hd_e;
   const int ncache = c.L_e * 2 * c.Hkv_e * c.hd_e;
+  ProbeScope ps(m, VLA_PROBE_CACHE, s);
   if (m->f32)
     K_TRY(gemm_f32((const float*)w.u, c.d_p, (const float*)m->wcache, c.d_p, M, ncache, c.d_p, ce, s), "cache");
   else
@@ -735,7 +801,7 @@ extern "C" size_t vla_kv_cache_bytes(const vla_model* m, int32_t batch, int32_t 
 }
 
 extern "C" vla_status vla_prefix_encode(vla_model* m, const float* x, int32_t batch, int32_t n_prefix, void* kv_storage,
-                                        size_t kv_bytes, void* stream, vla_kv_cache** out) {
+                                        size_t kv_bytes, void* stream, vla_kv_cache** out, vla_timing* timing) {
   if (!out) return fail(VLA_ERR_INVALID_ARGUMENT, "out is NULL");
   *out = nullptr;
   if (!live_model(m)) return fail(VLA_ERR_INVALID_HANDLE, "unknown model");
@@ -749,8 +815,19 @@ extern "C" vla_status vla_prefix_encode(vla_model* m, const float* x, int32_t ba
   WS w;
   vla_status st = get_ws(m, (int64_t)batch * n_prefix, 0, &w);
   if (st != VLA_OK) return st;
+  if (timing) K_TRY(hipEventRecord(m->ev0, s), "event");
   st = run_prefix(m, x, batch, n_prefix, kv_storage, w, s);
   if (st != VLA_OK) return st;
+  if (timing) {
+    K_TRY(hipEventRecord(m->ev1, s), "event");
+    K_TRY(hipEventSynchronize(m->ev1), "event sync");
+    float ms = 0.f;
+    K_TRY(hipEventElapsedTime(&ms, m->ev0, m->ev1), "elapsed");
+    timing->prefix_ms = ms;
+    timing->denoise_ms = 0.f;
+    timing->step_ms = 0.f;
+    timing->graph_replayed = 0;
+  }
   vla_kv_cache* k = new vla_kv_cache();
   k->model = m;
   k->B = batch;
@@ -808,7 +885,7 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
   ca.Nk = N;
   Epilogue pe;
   pe.kind = EPI_PARTIAL;
-  const int S_o = gemm_bf16_splits(qe, kExpertSplits), S_d = gemm_bf16_splits(c.F_e, kExpertSplits);
+  const int S_o = gemm_bf16_splits(qe, kExpertSplits, M), S_d = gemm_bf16_splits(c.F_e, kExpertSplits, M);
   for (int k = 0; k < steps; ++k) {
     K_TRY(expert_embed(w.X, M, c.d_a, m->w_in, f32, c.d_e, m->sched_dev, k, w.E, m->el[0].a1, eps, w.eu, f32, s), "embed");
     for (int e = 0; e < c.L_e; ++e) {
@@ -834,17 +911,17 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
           K_TRY(resid_norm(w.E, c.d_e, nullptr, 0, M, c.d_e, m->el[e + 1].a1, eps, w.eu, 1, c.d_e, nullptr, nullptr, s), "norm");
       } else {
         const uint16_t* u = (const uint16_t*)w.eu;
-        K_TRY(gemm_bf16(u, c.d_e, (const uint16_t*)L.wqkv, c.d_e, M, qkve, c.d_e, epi_store(w.eqkv, qkve, 0), 4, w.epart, s), "qkv_s");
+        K_TRY(gemm_bf16(u, c.d_e, (const uint16_t*)L.wqkv, c.d_e, M, qkve, c.d_e, epi_store(w.eqkv, qkve, 0), 1, w.epart, s), "qkv_s");
         K_TRY(attention_bf16(sa, s), "self attn");
         K_TRY(gemm_bf16((const uint16_t*)w.eattn, qe, (const uint16_t*)L.wos, qe, M, c.d_e, qe, pe, S_o, w.epart, s), "o_s");
         K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s), "norm");
-        K_TRY(gemm_bf16(u, c.d_e, (const uint16_t*)L.wqc, c.d_e, M, qe, c.d_e, epi_store(w.eq, qe, 0), 4, w.epart, s), "q_c");
+        K_TRY(gemm_bf16(u, c.d_e, (const uint16_t*)L.wqc, c.d_e, M, qe, c.d_e, epi_store(w.eq, qe, 0), 1, w.epart, s), "q_c");
         K_TRY(attention_bf16(ca, s), "cross attn");
         K_TRY(gemm_bf16((const uint16_t*)w.eattn, qe, (const uint16_t*)L.woc, qe, M, c.d_e, qe, pe, S_o, w.epart, s), "o_c");
         K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s), "norm");
         Epilogue g = epi_store(w.emlp, c.F_e, 0);
         g.kind = EPI_GEGLU;
-        K_TRY(gemm_bf16(u, c.d_e, (const uint16_t*)L.wgu, c.d_e, M, 2 * c.F_e, c.d_e, g, 2, w.epart, s), "gate/up");
+        K_TRY(gemm_bf16(u, c.d_e, (const uint16_t*)L.wgu, c.d_e, M, 2 * c.F_e, c.d_e, g, 1, w.epart, s), "gate/up");
         K_TRY(gemm_bf16((const uint16_t*)w.emlp, c.F_e, (const uint16_t*)L.wd, c.F_e, M, c.d_e, c.F_e, pe, S_d, w.epart, s), "down");
         K_TRY(resid_norm(w.E, c.d_e, w.epart, S_d, M, c.d_e, e + 1 < c.L_e ? m->el[e + 1].a1 : m->w_ef, eps,
                          e + 1 < c.L_e ? w.eu : nullptr, 0, c.d_e, nullptr, nullptr, s), "norm");

@@ -59,11 +59,11 @@ __global__ __launch_bounds__(256) void k_gemm_w2a8(W2A8P p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int v = tid + i * 256, r = v >> 3, c = (v & 7) * 16;
-      ra[i] = (m0 + r < p.M) ? *(const u32x4_t*)(p.a + (long)(m0 + r) * p.lda + k0 + c) : u32x4_t{0, 0, 0, 0};
+      // rows past the end are clamped to valid ones; their results are never stored
+      ra[i] = *(const u32x4_t*)(p.a + (long)min(m0 + r, p.M - 1) * p.lda + k0 + c);
     }
     const int r = tid >> 1, c = (tid & 1) * 4;  // 128 rows x 8 words
-    rw = (n0 + r < p.N) ? *(const u32x4_t*)(p.q + (long)(n0 + r) * KW + k0 / 16 + c)
-                        : u32x4_t{0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u};  // code 1 = 0
+    rw = *(const u32x4_t*)(p.q + (long)min(n0 + r, p.N - 1) * KW + k0 / 16 + c);
   };
   auto sstore = [&](int buf) {
 #pragma unroll

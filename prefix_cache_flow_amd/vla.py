@@ -28,8 +28,9 @@ EXPORTS = (
     "vla_status_string", "vla_last_error", "vla_n_tensors", "vla_tensor_info", "vla_model_create",
     "vla_model_destroy", "vla_kv_cache_bytes", "vla_prefix_encode", "vla_denoise_chunk",
     "vla_kv_cache_release", "vla_kv_cache_info", "vla_quantize_rows_i8", "vla_w2a8_gemm",
-    "vla_ternary_pack", "vla_ternary_unpack",
+    "vla_ternary_pack", "vla_ternary_unpack", "vla_probe_arm", "vla_probe_read",
 )
+PROBE_PREFIX_GATEUP, PROBE_PREFIX_DOWN, PROBE_PREFIX_QKV, PROBE_PREFIX_ATTN, PROBE_PREFIX_O, PROBE_CACHE = range(1, 7)
 
 
 class VlaError(RuntimeError):
@@ -82,7 +83,7 @@ def lib():
         "vla_model_create": (I, [C.POINTER(vla_model_config), C.POINTER(vla_weights), P, C.POINTER(P)]),
         "vla_model_destroy": (I, [P]),
         "vla_kv_cache_bytes": (S, [P, I, I]),
-        "vla_prefix_encode": (I, [P, P, I, I, P, S, P, C.POINTER(P)]),
+        "vla_prefix_encode": (I, [P, P, I, I, P, S, P, C.POINTER(P), C.POINTER(vla_timing)]),
         "vla_denoise_chunk": (I, [P, P, P, I, C.POINTER(vla_solver), P, I, P, C.POINTER(vla_timing)]),
         "vla_kv_cache_release": (I, [P]),
         "vla_kv_cache_info": (I, [P, C.POINTER(I), C.POINTER(I)]),
@@ -90,6 +91,8 @@ def lib():
         "vla_w2a8_gemm": (I, [P, P, P, C.c_float, I, I, I, P, P, P]),
         "vla_ternary_pack": (I, [P, I, I, P]),
         "vla_ternary_unpack": (I, [P, I, I, P]),
+        "vla_probe_arm": (I, [P, I, I]),
+        "vla_probe_read": (I, [P, C.POINTER(C.c_float), C.POINTER(I)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -248,8 +251,8 @@ def vla_kv_cache_bytes(model: Model, batch: int, n_prefix: int) -> int:
     return lib().vla_kv_cache_bytes(model.handle, batch, n_prefix)
 
 
-def vla_prefix_encode(model: Model, prefix_hidden, kv_storage=None, stream=None) -> KVCache:
-    """prefix_hidden: float32 cuda tensor [B, N, d_p]; returns a KVCache."""
+def vla_prefix_encode(model: Model, prefix_hidden, kv_storage=None, stream=None, timing: bool = False):
+    """prefix_hidden: float32 cuda tensor [B, N, d_p]; returns a KVCache (and a timing dict when asked)."""
     import torch
     assert prefix_hidden.dtype == torch.float32 and prefix_hidden.is_contiguous()
     B, N, _ = prefix_hidden.shape
@@ -257,9 +260,37 @@ def vla_prefix_encode(model: Model, prefix_hidden, kv_storage=None, stream=None)
     if kv_storage is None:
         kv_storage = torch.empty(nbytes, dtype=torch.uint8, device=prefix_hidden.device)
     h = C.c_void_p()
+    tm = vla_timing() if timing else None
     _check(lib().vla_prefix_encode(model.handle, _ptr(prefix_hidden), B, N, _ptr(kv_storage),
-                                   kv_storage.numel() * kv_storage.element_size(), _stream(stream), C.byref(h)))
-    return KVCache(h, kv_storage, B, N)
+                                   kv_storage.numel() * kv_storage.element_size(), _stream(stream), C.byref(h),
+                                   C.byref(tm) if tm is not None else None))
+    kv = KVCache(h, kv_storage, B, N)
+    if timing:
+        return kv, {"prefix_ms": tm.prefix_ms}
+    return kv
+
+
+def vla_probe_arm(model: Model, kind: int, max_launches: int = 4096):
+    _check(lib().vla_probe_arm(model.handle, int(kind), int(max_launches)))
+
+
+def vla_probe_read(model: Model):
+    ms, n = C.c_float(), C.c_int32()
+    _check(lib().vla_probe_read(model.handle, C.byref(ms), C.byref(n)))
+    return ms.value, n.value
+
+
+class Probe:
+    """Arms a kernel probe on construction; collect() reads and disarms it."""
+
+    def __init__(self, model: Model, kind: int, max_launches: int = 4096):
+        self.model = model
+        vla_probe_arm(model, kind, max_launches)
+
+    def collect(self):
+        r = vla_probe_read(self.model)
+        vla_probe_arm(self.model, 0, 0)
+        return r
 
 
 def vla_denoise_chunk(model: Model, kv: KVCache, noise, steps: int, schedule=None, tau=None, out_dtype=None,

@@ -85,7 +85,8 @@ def test_null_and_foreign_handles_are_rejected():
     b, n = C.c_int32(), C.c_int32()
     assert L.vla_kv_cache_info(C.c_void_p(0x10), C.byref(b), C.byref(n)) == 3
     out = C.c_void_p()
-    assert L.vla_prefix_encode(None, None, 1, 1, None, 0, None, C.byref(out)) == 3
+    assert L.vla_prefix_encode(None, None, 1, 1, None, 0, None, C.byref(out), None) == 3
+    assert L.vla_probe_arm(None, 1, 4) == 3
     assert L.vla_denoise_chunk(None, None, None, 1, None, None, 0, None, None) == 3
     cfg = vla.make_config(synth.config(0).to_dict())
     assert L.vla_model_create(C.byref(cfg), None, None, C.byref(out)) == 1

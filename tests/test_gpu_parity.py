@@ -33,13 +33,17 @@ def report(name, got, ref, x0):
 
 # ---------------------------------------------------------------- end to end
 
-@pytest.mark.parametrize("cfg,tol,dtol", [
-    (synth.config(0), 1e-3, 1e-3),
-    (SMALL_BF16, 2e-2, 2e-2),
-    (SMALL_BF16_B3, 2e-2, 2e-2),
-    (SMALL_W2A8, 2e-2, 5e-2),
+# Bounds: tol is the stated bound on X^T (Eq. 5's e_rel); dtol and ctol bound the
+# displacement and the K/V cache.  For bf16 they sit well above what a CPU
+# emulation of this library's rounding points gives at these shapes (e_rel(D)
+# about 1.2e-4, cache about 2.4e-3), so a wrong term fails them.
+@pytest.mark.parametrize("cfg,tol,dtol,ctol", [
+    (synth.config(0), 1e-3, 1e-3, 1e-4),
+    (SMALL_BF16, 2e-2, 5e-3, 4e-3),
+    (SMALL_BF16_B3, 2e-2, 5e-3, 4e-3),
+    (SMALL_W2A8, 2e-2, 1e-2, 4e-3),
 ], ids=lambda v: getattr(v, "name", ""))
-def test_end_to_end_small(cfg, tol, dtol):
+def test_end_to_end_small(cfg, tol, dtol, ctol):
     w, b, z0, x0 = host_inputs(cfg, 0)
     print(f"case {cfg.name} seed 0", flush=True)
     ref, caches = oracle.Oracle(cfg, w, b).run(z0, x0, keep_cache=True)
@@ -54,7 +58,7 @@ def test_end_to_end_small(cfg, tol, dtol):
         for l in range(cfg.L_e):
             for i in range(2):
                 ec = oracle.e_rel(gc[bb][l][i], caches[bb][l][i])
-                assert ec <= (1e-4 if cfg.precision == "f32" else 2e-2), (bb, l, i, ec)
+                assert ec <= ctol, (bb, l, i, ec)
     # bf16 output equals the rounded fp32 output
     got16, _ = gpu_run(cfg, model, z0, x0, out_dtype=torch.bfloat16)
     np.testing.assert_array_equal(got16, torch.from_numpy(got.astype(np.float32)).bfloat16().float().numpy())
