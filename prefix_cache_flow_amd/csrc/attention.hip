@@ -184,8 +184,12 @@ __global__ __launch_bounds__(256) void k_attn16(AttnArgs a) {
       O += e * ob[(ww * 16 + q) * LDO + d];
     }
     const float val = O * __builtin_amdgcn_rcpf(L);
-    const long oi = b * a.o_bs + (long)gq * a.o_rs + (long)j * D + d;
-    if (a.o_f32) ((float*)a.o)[oi] = val; else ((bf16_t*)a.o)[oi] = f2bf(val);
+    if (a.o_frag) {
+      ((bf16_t*)a.o)[frag_idx(b * a.Nq + gq, j * D + d, a.Hq * D)] = f2bf(val);
+    } else {
+      const long oi = b * a.o_bs + (long)gq * a.o_rs + (long)j * D + d;
+      if (a.o_f32) ((float*)a.o)[oi] = val; else ((bf16_t*)a.o)[oi] = f2bf(val);
+    }
   }
 }
 
@@ -200,6 +204,7 @@ static hipError_t launch_attn16(const AttnArgs& a, hipStream_t s) {
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.Nq <= 0 || a.Nk <= 0) return hipSuccess;
   if (a.Hq % a.Hkv) return hipErrorInvalidValue;
+  if (a.o_frag && (a.o_f32 || a.B * a.Nq > 64)) return hipErrorInvalidValue;
   switch (a.hd) {
     case 64: return launch_attn16<64>(a, s);
     case 128: return launch_attn16<128>(a, s);

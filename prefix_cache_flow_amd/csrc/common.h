@@ -96,6 +96,14 @@ __device__ __forceinline__ i32x16_t mfma32x32x32_i8(i32x4_t a, i32x4_t b, i32x16
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// Fragment layout of a [rows][K] bf16 matrix for the 16x16x32 MFMA: blocks of
+// 16 rows x 32 columns, each block 1 KB in the order the 64 lanes of a wave
+// consume it (lane = row % 16 + 16 * ((col % 32) / 8), 8 consecutive columns per
+// lane), blocks row-block major.  One wave loads one block as one contiguous 1 KB.
+__host__ __device__ __forceinline__ long frag_idx(int m, int k, int K) {
+  return ((((long)(m >> 4) * (K >> 5) + (k >> 5)) * 64 + ((m & 15) + ((k >> 3) & 3) * 16)) << 3) + (k & 7);
+}
+
 // acc row index of element i for lane l in a 32x32 MFMA block
 __device__ __forceinline__ int mfma32_row(int i, int lane) { return (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3); }
 

@@ -23,7 +23,8 @@ __device__ __forceinline__ float ld_w(const void* w, long i) {
 // its outputs before using any (clamped indices, masked products).
 template <bool WF32>
 __global__ __launch_bounds__(256) void k_embed(const float* X, int d_a, const void* w_in, int d_e, const float* sched,
-                                               int k, float* E, const float* gain, float eps, void* u, int u_f32) {
+                                               int k, float* E, const float* gain, float eps, void* u, int u_f32,
+                                               int u_frag) {
   __shared__ float xs[256];
   __shared__ float es[4096];
   __shared__ float red[4];
@@ -54,18 +55,22 @@ __global__ __launch_bounds__(256) void k_embed(const float* X, int d_a, const vo
   const float r = 1.0f / sqrtf(ss / (float)d_e + eps);
   for (int n = threadIdx.x; n < d_e; n += 256) {
     const float un = es[n] * r * (1.0f + gain[n]);
-    if (u_f32) ((float*)u)[(long)m * d_e + n] = un; else ((bf16_t*)u)[(long)m * d_e + n] = f2bf(un);
+    if (u_f32) ((float*)u)[(long)m * d_e + n] = un;
+    else ((bf16_t*)u)[u_frag ? frag_idx(m, n, d_e) : (long)m * d_e + n] = f2bf(un);
   }
 }
 
 hipError_t expert_embed(const float* X, int M, int d_a, const void* w_in, int w_f32, int d_e, const float* sched,
-                        int k, float* E, const float* gain, float eps, void* u, int u_f32, hipStream_t s) {
+                        int k, float* E, const float* gain, float eps, void* u, int u_f32, hipStream_t s, int u_frag) {
   if (M <= 0) return hipSuccess;
   if (d_a > 256 || d_e > 4096) return hipErrorInvalidValue;
+  if (u_frag && (u_f32 || d_e % 32 || M > 64)) return hipErrorInvalidValue;
   if (w_f32)
-    hipLaunchKernelGGL(k_embed<true>, dim3(M), dim3(256), 0, s, X, d_a, w_in, d_e, sched, k, E, gain, eps, u, u_f32);
+    hipLaunchKernelGGL(k_embed<true>, dim3(M), dim3(256), 0, s, X, d_a, w_in, d_e, sched, k, E, gain, eps, u, u_f32,
+                       u_frag);
   else
-    hipLaunchKernelGGL(k_embed<false>, dim3(M), dim3(256), 0, s, X, d_a, w_in, d_e, sched, k, E, gain, eps, u, u_f32);
+    hipLaunchKernelGGL(k_embed<false>, dim3(M), dim3(256), 0, s, X, d_a, w_in, d_e, sched, k, E, gain, eps, u, u_f32,
+                       u_frag);
   return hipGetLastError();
 }
 

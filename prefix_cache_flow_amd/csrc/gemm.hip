@@ -64,11 +64,11 @@ __device__ __forceinline__ void epi_store(const Epilogue& e, int m, int n, float
 
 __device__ __forceinline__ void epi_geglu(const Epilogue& e, int m, int f, float g, float u) {
   const float v = gelu_erf(g) * u;
-  const long i = (long)m * e.ldo + f;
+  const long i = e.out_frag ? frag_idx(m, f, e.ldo) : (long)m * e.ldo + f;
   if (e.out_f32) ((float*)e.out)[i] = v; else ((bf16_t*)e.out)[i] = f2bf(v);
 }
 
-template <int BM, int BN, int WM, int WN, int KIND>
+template <int BM, int BN, int WM, int WN, int KIND, bool WF>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GemmP p) {
   constexpr int NT = 64 * WM * WN, BK = 64, LDK = BK + 8;
   constexpr int TM = BM / (32 * WM), TN = BN / (32 * WN);
@@ -107,7 +107,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GemmP p) {
       const int v = tid + i * NT;
       if (WV % NT == 0 || v < WV) {
         const int r = v >> 3, c = (v & 7) * 8, gn = min(n0 + r, p.N - 1);
-        rw[i] = *(const u32x4_t*)(p.W + (long)gn * p.ldw + k0 + c);
+        // WF: the weights are in the fragment layout; 8 consecutive k stay one 16-byte vector
+        rw[i] = *(const u32x4_t*)(p.W + (WF ? frag_idx(gn, k0 + c, p.ldw) : (long)gn * p.ldw + k0 + c));
       }
     }
   };
@@ -367,7 +368,7 @@ static hipError_t launch_skinny(const SkinnyP& p0, int splits, hipStream_t s) {
   return err;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool WF>
 static hipError_t launch_bf16(const GemmP& p, int splits, hipStream_t s) {
   GemmP q = p;
   q.nM = (p.M + BM - 1) / BM;
@@ -378,12 +379,22 @@ static hipError_t launch_bf16(const GemmP& p, int splits, hipStream_t s) {
   const int used = (slices + per - 1) / per;  // == splits for counts from gemm_bf16_splits
   dim3 grid(q.nM * q.nN, used);
   const int kind = used > 1 ? EPI_PARTIAL : p.epi.kind;
-  switch (kind) {
-    case EPI_STORE: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_STORE>), grid, dim3(64 * WM * WN), 0, s, q); break;
-    case EPI_RESID: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_RESID>), grid, dim3(64 * WM * WN), 0, s, q); break;
-    case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_GEGLU>), grid, dim3(64 * WM * WN), 0, s, q); break;
-    case EPI_CACHE: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_CACHE>), grid, dim3(64 * WM * WN), 0, s, q); break;
-    default: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_PARTIAL>), grid, dim3(64 * WM * WN), 0, s, q); break;
+  const dim3 blk(64 * WM * WN);
+  if constexpr (WF) {  // expert weights: only the kinds of the expert layer
+    switch (kind) {
+      case EPI_STORE: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_STORE, true>), grid, blk, 0, s, q); break;
+      case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_GEGLU, true>), grid, blk, 0, s, q); break;
+      case EPI_PARTIAL: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_PARTIAL, true>), grid, blk, 0, s, q); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (kind) {
+      case EPI_STORE: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_STORE, false>), grid, blk, 0, s, q); break;
+      case EPI_RESID: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_RESID, false>), grid, blk, 0, s, q); break;
+      case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_GEGLU, false>), grid, blk, 0, s, q); break;
+      case EPI_CACHE: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_CACHE, false>), grid, blk, 0, s, q); break;
+      default: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_PARTIAL, false>), grid, blk, 0, s, q); break;
+    }
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -406,9 +417,10 @@ int gemm_bf16_splits(int K, int splits, int M) {
 }
 
 hipError_t gemm_bf16(const uint16_t* A, int lda, const uint16_t* W, int ldw, int M, int N, int K,
-                     const Epilogue& epi, int splits, float* ws, hipStream_t s) {
+                     const Epilogue& epi, int splits, float* ws, hipStream_t s, int w_frag) {
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
   if (K % 64 || N % 32) return hipErrorInvalidValue;
+  if (w_frag && (M <= 64 || ldw != K || epi.kind == EPI_RESID || epi.kind == EPI_CACHE)) return hipErrorInvalidValue;
   // the one place that fixes how many partial slices are written: callers that
   // consume EPI_PARTIAL output read gemm_bf16_splits(K, splits, M) of them
   splits = gemm_bf16_splits(K, splits, M);
@@ -425,7 +437,155 @@ hipError_t gemm_bf16(const uint16_t* A, int lda, const uint16_t* W, int ldw, int
     }
     return launch_skinny<1>(q, splits, s);
   }
-  return launch_bf16<96, 128, 1, 4>(p, splits, s);
+  if (w_frag) return launch_bf16<96, 128, 1, 4, true>(p, splits, s);
+  return launch_bf16<96, 128, 1, 4, false>(p, splits, s);
+}
+
+// ------------------------------------------------------------------ chunk rows, fragment layout
+// Activations of at most 64 rows with both operands in the fragment layout of
+// common.h.  The work split is that of the skinny kernel above (a workgroup
+// owns 16 * NB columns, its four waves split the K range, at most kSkinnySteps
+// k-steps each, partial tiles summed through LDS in wave order), but every
+// load of a wave is one contiguous 1 KB fragment: a weight fragment per
+// 16 columns and k-step, an activation fragment per 16 rows and k-step.  MB is
+// the number of 16-row blocks that hold rows (1, 2 or 4); blocks past the rows
+// are never loaded.  Rows past M inside the last block are read but their
+// results are never stored.
+struct ChunkP {
+  const uint16_t* A;
+  const uint16_t* W;
+  int M, N, K, kchunk;
+  Epilogue epi;
+  float* ws;
+};
+
+template <int NB, int MB, int KIND>
+__global__ __launch_bounds__(256) void k_chunk(ChunkP p) {
+  constexpr int SPW = kSkinnySteps;
+  __shared__ float red[4][MB * NB * 4][64];  // [wave][row block, column block, element][lane]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int nb0 = blockIdx.x * NB;  // first 16-column block of the workgroup
+  const int KS = p.K >> 5;          // k-steps (fragments per 16-row block)
+  const int sb = (blockIdx.y * p.kchunk + w * (p.kchunk >> 2)) >> 5;
+  const int nsteps = max(0, min(KS - sb, p.kchunk >> 7));
+  const u32x4_t* Wv = (const u32x4_t*)p.W + lane;
+  const u32x4_t* Av = (const u32x4_t*)p.A + lane;
+
+  u32x4_t wv[SPW][NB], av[SPW][MB];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const int ks = min(sb + s, KS - 1);  // clamped; steps past the range are masked below
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) wv[s][nb] = Wv[((long)(nb0 + nb) * KS + ks) * 64];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) av[s][rb] = Av[((long)rb * KS + ks) * 64];
+  }
+  f32x4_t acc[MB][NB];
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const bool on = s < nsteps;
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+      const u32x4_t a4 = on ? av[s][rb] : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = mfma16x16x32(as_bf16x8(a4), as_bf16x8(wv[s][nb]), acc[rb][nb]);
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[w][(rb * NB + nb) * 4 + e][lane] = acc[rb][nb][e];
+  __syncthreads();
+
+  // wave w finishes row block w: the four K ranges summed in wave order, then the epilogue
+  const int rb = w;
+  if (rb >= MB) return;
+  float v[NB][4];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = (rb * NB + nb) * 4 + e;
+      v[nb][e] = red[0][idx][lane] + red[1][idx][lane] + red[2][idx][lane] + red[3][idx][lane];
+    }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int m = rb * 16 + grp * 4 + e;
+    if (m >= p.M) continue;
+    if (KIND == EPI_GEGLU) {
+      epi_geglu(p.epi, m, (nb0 >> 1) * 16 + col, v[0][e], v[NB - 1][e]);
+      continue;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = (nb0 + nb) * 16 + col;
+      if (KIND == EPI_PARTIAL) p.ws[((long)blockIdx.y * p.M + m) * p.N + n] = v[nb][e];
+      else epi_store_t<KIND>(p.epi, m, n, v[nb][e]);
+    }
+  }
+}
+
+template <int MB>
+static hipError_t launch_chunk_mb(const ChunkP& p, int kind, dim3 grid, hipStream_t s) {
+  switch (kind) {
+    case EPI_GEGLU: hipLaunchKernelGGL((k_chunk<2, MB, EPI_GEGLU>), grid, dim3(256), 0, s, p); break;
+    case EPI_STORE: hipLaunchKernelGGL((k_chunk<1, MB, EPI_STORE>), grid, dim3(256), 0, s, p); break;
+    case EPI_PARTIAL: hipLaunchKernelGGL((k_chunk<1, MB, EPI_PARTIAL>), grid, dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, const Epilogue& epi, int splits,
+                      float* ws, hipStream_t s) {
+  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  if (M > 64 || K % 32 || N % 32) return hipErrorInvalidValue;
+  if (epi.kind != EPI_STORE && epi.kind != EPI_PARTIAL && epi.kind != EPI_GEGLU) return hipErrorInvalidValue;
+  int used, per;
+  skinny_plan(K, splits, &used, &per);
+  if (epi.kind == EPI_GEGLU && used > 1) return hipErrorInvalidValue;  // GeGLU needs whole sums
+  if (used > 1 && !ws) return hipErrorInvalidValue;
+  ChunkP p{Af, Wf, M, N, K, per * 32, epi, ws};
+  const int nb = epi.kind == EPI_GEGLU ? 2 : 1;
+  const dim3 grid(N / (16 * nb), used);
+  const int kind = (used > 1 && epi.kind == EPI_STORE) ? EPI_PARTIAL : epi.kind;
+  const int mb = (M + 15) / 16;
+  hipError_t err = mb == 1 ? launch_chunk_mb<1>(p, kind, grid, s)
+                 : mb == 2 ? launch_chunk_mb<2>(p, kind, grid, s)
+                           : launch_chunk_mb<4>(p, kind, grid, s);
+  if (err != hipSuccess) return err;
+  if (used > 1 && epi.kind == EPI_STORE) {
+    const long tot = (long)M * N;
+    const int blocks = (int)std::min<long>((tot + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, (const float*)ws, used, M, N, epi);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+// row-major [N][K] -> fragment layout, one 16-byte vector (8 k) per thread
+__global__ void k_frag_pack(const u32x4_t* src, int N, int K, uint16_t* dst) {
+  const long vecs = (long)N * (K / 8);
+  for (long v = blockIdx.x * (long)blockDim.x + threadIdx.x; v < vecs; v += (long)gridDim.x * blockDim.x) {
+    const int n = (int)(v / (K / 8)), k = (int)(v % (K / 8)) * 8;
+    *(u32x4_t*)(dst + frag_idx(n, k, K)) = src[v];
+  }
+}
+
+hipError_t frag_pack(const uint16_t* src, int N, int K, uint16_t* dst, hipStream_t s) {
+  if (N <= 0 || K <= 0) return hipSuccess;
+  if (N % 16 || K % 32) return hipErrorInvalidValue;
+  const long vecs = (long)N * (K / 8);
+  const int blocks = (int)std::min<long>((vecs + 255) / 256, 8192);
+  hipLaunchKernelGGL(k_frag_pack, dim3(blocks), dim3(256), 0, s, (const u32x4_t*)src, N, K, dst);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ fp32 SIMT

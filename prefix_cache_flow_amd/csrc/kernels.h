@@ -33,17 +33,31 @@ struct Epilogue {
   const float* alpha = nullptr;
   const float* beta = nullptr;
   int32_t* acc_out = nullptr;  // optional raw int32 accumulators [M][N]
+  int out_frag = 0;  // bf16 output in fragment layout (frag_idx with K = ldo) instead of rows
 };
 
 // C = A[M,K] W[N,K]^T, bf16 operands, fp32 accumulation on MFMA; `splits` > 1
 // splits K and reduces the partial sums in a fixed order in `ws`
 // (splits * M * N floats).  K % 64 == 0, N % 32 == 0.  At most 64 rows take the
-// weight-streaming skinny kernel (GeGLU there needs splits == 1).
+// weight-streaming skinny kernel (GeGLU there needs splits == 1).  With w_frag
+// the weights are in the fragment layout of common.h (ldw == K, more than 64
+// rows, STORE / GEGLU / PARTIAL only).
 hipError_t gemm_bf16(const uint16_t* A, int lda, const uint16_t* W, int ldw, int M, int N, int K,
-                     const Epilogue& epi, int splits, float* ws, hipStream_t s);
+                     const Epilogue& epi, int splits, float* ws, hipStream_t s, int w_frag = 0);
 
 // Number of K splits gemm_bf16 actually uses for a request of `splits` at M rows.
 int gemm_bf16_splits(int K, int splits, int M);
+
+// The same contraction for at most 64 rows with A and W ([N][K]) both in the
+// fragment layout of common.h: every load of a wave is one contiguous 1 KB
+// block.  A holds 16 rows when M <= 16, 32 when M <= 32, else 64; rows past M
+// are read but their results never stored.  K % 32 == 0, N % 32 == 0; kinds
+// STORE, PARTIAL and GEGLU (splits == 1, out_frag honoured); splits and
+// partials as gemm_bf16.
+hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, const Epilogue& epi,
+                      int splits, float* ws, hipStream_t s);
+// row-major bf16 [N][K] -> fragment layout (N % 16 == 0, K % 32 == 0)
+hipError_t frag_pack(const uint16_t* src, int N, int K, uint16_t* dst, hipStream_t s);
 
 // Same contraction in fp32 on the vector ALU (fp32 workloads); K % 16 == 0.
 hipError_t gemm_f32(const float* A, int lda, const float* W, int ldw, int M, int N, int K,
@@ -68,9 +82,10 @@ hipError_t ternary_repack(const uint8_t* canon, int N, int K, uint32_t* out, int
 //   u = h[m] / sqrt(mean(h[m]^2) + eps) * (1 + gain)
 // and u is written as bf16 / fp32 (u_out), or quantized per Eq. 4 to int8 codes
 // (q_out) with its scale (alpha_out).  Any of the outputs may be null.
+// With u_frag the bf16 u goes out in the fragment layout (K = N) instead of rows.
 hipError_t resid_norm(float* h, int ldh, const float* part, int nsplit, int M, int N,
                       const float* gain, float eps, void* u_out, int u_f32, int ldu,
-                      int8_t* q_out, float* alpha_out, hipStream_t s);
+                      int8_t* q_out, float* alpha_out, hipStream_t s, int u_frag = 0);
 
 // Eq. 4 per-row quantization of fp32 rows (x: [M][ldx], K valid columns).
 hipError_t quantize_rows(const float* x, int ldx, int M, int K, int8_t* a, float* alpha, hipStream_t s);
@@ -83,6 +98,7 @@ struct AttnArgs {
   void* o; long o_bs, o_rs;               // output head j at column j * hd
   int B, Nq, Nk, Hq, Hkv, hd;
   int o_f32;                              // 1: fp32 output, 0: bf16
+  int o_frag;                             // bf16 output in fragment layout: row b * Nq + q, K = Hq * hd
 };
 // softmax(Q K^T / sqrt(hd)) V per head, no mask; bf16 inputs on MFMA (hd in 64..256)
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s);
@@ -93,7 +109,7 @@ hipError_t attention_f32(const AttnArgs& a, hipStream_t s);
 // E[m] = X[m] W_in^T + phi(tau_k) for the chunk rows, then u = RMS(E[m]; gain).
 hipError_t expert_embed(const float* X, int M, int d_a, const void* w_in, int w_f32, int d_e,
                         const float* sched, int k, float* E, const float* gain, float eps,
-                        void* u, int u_f32, hipStream_t s);
+                        void* u, int u_f32, hipStream_t s, int u_frag = 0);
 // v = RMS(E[m]; gain) W_out^T; X[m] += (tau_{k+1} - tau_k) v
 hipError_t expert_head(const float* E, int M, int d_e, const float* gain, float eps,
                        const void* w_out, int w_f32, int d_a, const float* sched, int k, float* X,

@@ -426,6 +426,30 @@ static vla_status build_weights(vla_model* m, const vla_weights* w, hipStream_t 
   }
   TRY(dev_alloc(m, &m->w_in, (int64_t)c.d_e * c.d_a * es));
   TRY(put_rows(m, m->w_in, 0, src.t[src.i++], c.d_e, c.d_a, s));
+  // Expert projections.  In bf16 they are assembled row-major in a staging
+  // buffer and stored in the MFMA fragment layout (kernels.h, frag_pack): the
+  // chunk has few rows, so these GEMMs are weight streams and every weight load
+  // is then one contiguous 1 KB per wave.
+  void* stage = nullptr;
+  if (!m->f32) {
+    const int64_t big = std::max<int64_t>(std::max<int64_t>(qkve, 2 * (int64_t)c.F_e) * c.d_e, (int64_t)c.d_e * std::max<int64_t>(qe, c.F_e));
+    if (hipMalloc(&stage, big * es) != hipSuccess) {
+      (void)hipGetLastError();
+      cleanup();
+      return fail(VLA_ERR_OUT_OF_MEMORY, "staging");
+    }
+    temps.push_back(stage);
+  }
+  // rows x cols assembled by `fill` (row-major) into a new buffer, fragment layout in bf16
+  auto expert_weight = [&](void** dst, int64_t rows, int64_t cols, auto fill) -> vla_status {
+    vla_status r = dev_alloc(m, dst, rows * cols * es);
+    if (r != VLA_OK) return r;
+    if (m->f32) return fill(*dst);
+    r = fill(stage);
+    if (r != VLA_OK) return r;
+    HIP_TRY(frag_pack((const uint16_t*)stage, (int)rows, (int)cols, (uint16_t*)*dst, s));
+    return VLA_OK;
+  };
   m->el.resize(c.L_e);
   for (int e = 0; e < c.L_e; ++e) {
     ExpertLayer& E = m->el[e];
@@ -433,24 +457,26 @@ static vla_status build_weights(vla_model* m, const vla_weights* w, hipStream_t 
     const void* wqs = src.t[src.i++];
     const void* wks = src.t[src.i++];
     const void* wvs = src.t[src.i++];
-    TRY(dev_alloc(m, &E.wqkv, qkve * c.d_e * es));
-    TRY(put_rows(m, E.wqkv, 0, wqs, qe, c.d_e, s));
-    TRY(put_rows(m, E.wqkv, qe, wks, kve, c.d_e, s));
-    TRY(put_rows(m, E.wqkv, qe + kve, wvs, kve, c.d_e, s));
-    TRY(dev_alloc(m, &E.wos, (int64_t)c.d_e * qe * es));
-    TRY(put_rows(m, E.wos, 0, src.t[src.i++], c.d_e, qe, s));
+    TRY(expert_weight(&E.wqkv, qkve, c.d_e, [&](void* d) {
+      vla_status r = put_rows(m, d, 0, wqs, qe, c.d_e, s);
+      if (r == VLA_OK) r = put_rows(m, d, qe, wks, kve, c.d_e, s);
+      if (r == VLA_OK) r = put_rows(m, d, qe + kve, wvs, kve, c.d_e, s);
+      return r;
+    }));
+    const void* wos = src.t[src.i++];
+    TRY(expert_weight(&E.wos, c.d_e, qe, [&](void* d) { return put_rows(m, d, 0, wos, c.d_e, qe, s); }));
     TRY(put_gain(m, &E.a2, src.t[src.i++], c.d_e, s));
-    TRY(dev_alloc(m, &E.wqc, qe * c.d_e * es));
-    TRY(put_rows(m, E.wqc, 0, src.t[src.i++], qe, c.d_e, s));
-    TRY(dev_alloc(m, &E.woc, (int64_t)c.d_e * qe * es));
-    TRY(put_rows(m, E.woc, 0, src.t[src.i++], c.d_e, qe, s));
+    const void* wqc = src.t[src.i++];
+    TRY(expert_weight(&E.wqc, qe, c.d_e, [&](void* d) { return put_rows(m, d, 0, wqc, qe, c.d_e, s); }));
+    const void* woc = src.t[src.i++];
+    TRY(expert_weight(&E.woc, c.d_e, qe, [&](void* d) { return put_rows(m, d, 0, woc, c.d_e, qe, s); }));
     TRY(put_gain(m, &E.a3, src.t[src.i++], c.d_e, s));
     const void* wg = src.t[src.i++];
     const void* wu = src.t[src.i++];
-    TRY(dev_alloc(m, &E.wgu, 2 * (int64_t)c.F_e * c.d_e * es));
-    TRY(put_interleaved(E.wgu, wg, wu, c.F_e, c.d_e * es, s));
-    TRY(dev_alloc(m, &E.wd, (int64_t)c.d_e * c.F_e * es));
-    TRY(put_rows(m, E.wd, 0, src.t[src.i++], c.d_e, c.F_e, s));
+    TRY(expert_weight(&E.wgu, 2 * (int64_t)c.F_e, c.d_e,
+                      [&](void* d) { return put_interleaved(d, wg, wu, c.F_e, c.d_e * es, s); }));
+    const void* wd = src.t[src.i++];
+    TRY(expert_weight(&E.wd, c.d_e, c.F_e, [&](void* d) { return put_rows(m, d, 0, wd, c.d_e, c.F_e, s); }));
   }
   TRY(put_gain(m, &m->w_ef, src.t[src.i++], c.d_e, s));
   TRY(dev_alloc(m, &m->w_out, (int64_t)c.d_a * c.d_e * es));
@@ -583,11 +609,14 @@ static WS plan(const vla_model* m, int64_t rows, int64_t erows, char* base) {
   const int64_t qe = (int64_t)c.Hq_e * c.hd_e, qkve = (int64_t)(c.Hq_e + 2 * c.Hkv_e) * c.hd_e;
   w.X = (float*)take(erows * c.d_a * 4);
   w.E = (float*)take(erows * c.d_e * 4);
-  w.eu = take(erows * c.d_e * es);
+  // GEMM inputs of the chunk: the fragment-layout kernel reads 1, 2 or 4 whole
+  // 16-row blocks, so up to 64 rows the buffers hold 64
+  const int64_t frows = erows <= 64 ? 64 : erows;
+  w.eu = take(frows * c.d_e * es);
   w.eqkv = take(erows * qkve * es);
   w.eq = take(erows * qe * es);
-  w.eattn = take(erows * qe * es);
-  w.emlp = take(erows * (int64_t)c.F_e * es);
+  w.eattn = take(frows * qe * es);
+  w.emlp = take(frows * (int64_t)c.F_e * es);
   // split partials: residual GEMMs [S][erows][d_e], other split GEMMs [S][erows][N]
   const int64_t widest = std::max<int64_t>(std::max<int64_t>(qkve, 2 * (int64_t)c.F_e), c.d_e);
   w.epart = (float*)take((size_t)kExpertSplits * erows * widest * 4);
@@ -611,6 +640,12 @@ static vla_status ensure_ws(vla_model* m, int64_t rows, int64_t erows, WS* out) 
     if (hipMalloc(&p, need.total) != hipSuccess) {
       (void)hipGetLastError();
       return fail(VLA_ERR_OUT_OF_MEMORY, "workspace allocation of " + std::to_string(need.total) + " bytes failed");
+    }
+    // zeroed once, so the padding rows of fragment-layout buffers hold finite values
+    if (hipMemset(p, 0, need.total) != hipSuccess) {
+      (void)hipGetLastError();
+      (void)hipFree(p);
+      return fail(VLA_ERR_DEVICE, "workspace clear failed");
     }
     m->ws = (char*)p;
     m->ws_bytes = need.total;
@@ -876,6 +911,9 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
   sa.v = (const char*)w.eqkv + (size_t)(qe + c.Hkv_e * c.hd_e) * es; sa.v_bs = sa.q_bs; sa.v_hs = c.hd_e; sa.v_rs = qkve;
   sa.o = w.eattn; sa.o_bs = (long)H * qe; sa.o_rs = qe;
   sa.B = B; sa.Nq = H; sa.Nk = H; sa.Hq = c.Hq_e; sa.Hkv = c.Hkv_e; sa.hd = c.hd_e; sa.o_f32 = f32 ? 1 : 0;
+  // up to 64 chunk rows: GEMM inputs in the fragment layout, weights always are (bf16)
+  const int fr = (!f32 && M <= 64) ? 1 : 0;
+  sa.o_frag = fr;
   // cross-attention into the cache [B][L_e][2][Hkv_e][N][hd_e]
   AttnArgs ca = sa;
   const long layer_stride = 2L * c.Hkv_e * N * c.hd_e;
@@ -887,7 +925,8 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
   pe.kind = EPI_PARTIAL;
   const int S_o = gemm_bf16_splits(qe, kExpertSplits, M), S_d = gemm_bf16_splits(c.F_e, kExpertSplits, M);
   for (int k = 0; k < steps; ++k) {
-    K_TRY(expert_embed(w.X, M, c.d_a, m->w_in, f32, c.d_e, m->sched_dev, k, w.E, m->el[0].a1, eps, w.eu, f32, s), "embed");
+    K_TRY(expert_embed(w.X, M, c.d_a, m->w_in, f32, c.d_e, m->sched_dev, k, w.E, m->el[0].a1, eps, w.eu, f32, s, fr),
+          "embed");
     for (int e = 0; e < c.L_e; ++e) {
       const ExpertLayer& L = m->el[e];
       ca.k = (const char*)kv->storage + (size_t)e * layer_stride * es;
@@ -911,20 +950,26 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
           K_TRY(resid_norm(w.E, c.d_e, nullptr, 0, M, c.d_e, m->el[e + 1].a1, eps, w.eu, 1, c.d_e, nullptr, nullptr, s), "norm");
       } else {
         const uint16_t* u = (const uint16_t*)w.eu;
-        K_TRY(gemm_bf16(u, c.d_e, (const uint16_t*)L.wqkv, c.d_e, M, qkve, c.d_e, epi_store(w.eqkv, qkve, 0), 1, w.epart, s), "qkv_s");
+        // C = A W^T on the chunk: fragment-layout operands up to 64 rows, else the tiled kernel
+        auto mm = [&](const void* A, int lda, const void* W, int N, int K, const Epilogue& ep, int splits) {
+          if (fr) return gemm_chunk((const uint16_t*)A, (const uint16_t*)W, M, N, K, ep, splits, w.epart, s);
+          return gemm_bf16((const uint16_t*)A, lda, (const uint16_t*)W, K, M, N, K, ep, splits, w.epart, s, 1);
+        };
+        K_TRY(mm(u, c.d_e, L.wqkv, qkve, c.d_e, epi_store(w.eqkv, qkve, 0), 1), "qkv_s");
         K_TRY(attention_bf16(sa, s), "self attn");
-        K_TRY(gemm_bf16((const uint16_t*)w.eattn, qe, (const uint16_t*)L.wos, qe, M, c.d_e, qe, pe, S_o, w.epart, s), "o_s");
-        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s), "norm");
-        K_TRY(gemm_bf16(u, c.d_e, (const uint16_t*)L.wqc, c.d_e, M, qe, c.d_e, epi_store(w.eq, qe, 0), 1, w.epart, s), "q_c");
+        K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
+        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
+        K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, epi_store(w.eq, qe, 0), 1), "q_c");
         K_TRY(attention_bf16(ca, s), "cross attn");
-        K_TRY(gemm_bf16((const uint16_t*)w.eattn, qe, (const uint16_t*)L.woc, qe, M, c.d_e, qe, pe, S_o, w.epart, s), "o_c");
-        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s), "norm");
+        K_TRY(mm(w.eattn, qe, L.woc, c.d_e, qe, pe, S_o), "o_c");
+        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
         Epilogue g = epi_store(w.emlp, c.F_e, 0);
         g.kind = EPI_GEGLU;
-        K_TRY(gemm_bf16(u, c.d_e, (const uint16_t*)L.wgu, c.d_e, M, 2 * c.F_e, c.d_e, g, 1, w.epart, s), "gate/up");
-        K_TRY(gemm_bf16((const uint16_t*)w.emlp, c.F_e, (const uint16_t*)L.wd, c.F_e, M, c.d_e, c.F_e, pe, S_d, w.epart, s), "down");
+        g.out_frag = fr;
+        K_TRY(mm(u, c.d_e, L.wgu, 2 * c.F_e, c.d_e, g, 1), "gate/up");
+        K_TRY(mm(w.emlp, c.F_e, L.wd, c.d_e, c.F_e, pe, S_d), "down");
         K_TRY(resid_norm(w.E, c.d_e, w.epart, S_d, M, c.d_e, e + 1 < c.L_e ? m->el[e + 1].a1 : m->w_ef, eps,
-                         e + 1 < c.L_e ? w.eu : nullptr, 0, c.d_e, nullptr, nullptr, s), "norm");
+                         e + 1 < c.L_e ? w.eu : nullptr, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
       }
     }
     K_TRY(expert_head(w.E, M, c.d_e, m->w_ef, eps, m->w_out, f32, c.d_a, m->sched_dev, k, w.X, s), "head");
