@@ -147,8 +147,14 @@ vla_status vla_model_create(const vla_model_config* cfg, const vla_weights* weig
 vla_status vla_model_destroy(vla_model* model);
 
 /* Bytes of K/V cache storage for `batch` observations of `n_prefix` tokens:
- * layout [batch][L_e][2 (K, V)][Hkv_e][n_prefix][hd_e], bfloat16 (float32 for
- * VLA_F32).  Returns 0 for invalid arguments. */
+ * blocks [batch][L_e][2 (K, V)][Hkv_e], each of Np x hd_e elements.
+ * VLA_F32: float32, Np = n_prefix, element (t, d) at t * hd_e + d.
+ * Otherwise bfloat16 in the operand orders of the 16x16x32 MFMA, Np = n_prefix
+ * rounded up to a multiple of 32 (padding rows hold zero):
+ *   K block: (t, d) at ((((t/16) * (hd_e/32) + d/32) * 64 + t%16 + 16*((d/8)%4)) * 8 + d%8
+ *   V block: with u = t%32, (t, d) at
+ *            ((((t/32) * (hd_e/16) + d/16) * 64 + d%16 + 16*((u%16)/4)) * 8 + 4*(u/16) + u%4
+ * Returns 0 for invalid arguments. */
 size_t vla_kv_cache_bytes(const vla_model* model, int32_t batch, int32_t n_prefix);
 
 /* Prefix pass (the paper, §III-B; the reading notes, Method 1-3): encodes

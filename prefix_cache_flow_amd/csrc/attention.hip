@@ -101,7 +101,9 @@ __global__ __launch_bounds__(256) void k_attn16(AttnArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (t + 1 < t1) fetch(kt + 32);  // next tile in flight during this tile's math
+    // next tile in flight during this tile's math (the last tile again at the
+    // end: an unconditional fetch keeps the wait before each use to one tile)
+    fetch(min(t + 1, t1 - 1) * 32);
 
     // S^T = K Q^T for keys 0-15 (s0) and 16-31 (s1) of the tile
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -120,21 +122,30 @@ __global__ __launch_bounds__(256) void k_attn16(AttnArgs a) {
       s1[i] = kb2 < a.Nk ? s1[i] * sl2 : -INFINITY;
       mt = fmaxf(mt, fmaxf(s0[i], s1[i]));
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mnew = fmaxf(mrun, mt);
-    const float alpha = fast_exp2(mrun - mnew);
+    mt = group4_max(mt);
+    // Lazy rescaling: the reference max moves (and O, l are rescaled) only
+    // when some query's max grew by more than 8 (log2 units), so weights stay
+    // below 2^8 and the rescale of the output registers is rare.  The result
+    // O / l does not depend on the reference, only its rounding does.
+    const bool grow = mt > mrun + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float mnew = grow ? mt : mrun;
+      const float alpha = fast_exp2(mrun - mnew);
+#pragma unroll
+      for (int t2 = 0; t2 < D / 16; ++t2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[t2][e] *= alpha;
+      lrun *= alpha;
+      mrun = mnew;
+    }
     float ls = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s0[i] = fast_exp2(s0[i] - mnew);
-      s1[i] = fast_exp2(s1[i] - mnew);
+      s0[i] = fast_exp2(s0[i] - mrun);
+      s1[i] = fast_exp2(s1[i] - mrun);
       ls += s0[i] + s1[i];
     }
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
-    lrun = lrun * alpha + ls;
-    mrun = mnew;
+    lrun += group4_sum(ls);
     // P^T as the B operand: abstract k = grp * 8 + kk is key (kk / 4) * 16 + grp * 4 + kk % 4
     const u32x4_t pw = {pack_bf2(s0[0], s0[1]), pack_bf2(s0[2], s0[3]), pack_bf2(s1[0], s1[1]), pack_bf2(s1[2], s1[3])};
     const bf16x8_t pf = as_bf16x8(pw);
@@ -144,10 +155,7 @@ __global__ __launch_bounds__(256) void k_attn16(AttnArgs a) {
       const u32x2_t lo = *(const u32x2_t*)row;
       const u32x2_t hi = *(const u32x2_t*)(row + 16);
       const u32x4_t vw = {lo[0], lo[1], hi[0], hi[1]};
-      f32x4_t acc = o[t2];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] *= alpha;
-      o[t2] = mfma16x16x32(as_bf16x8(vw), pf, acc);
+      o[t2] = mfma16x16x32(as_bf16x8(vw), pf, o[t2]);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -211,6 +219,169 @@ hipError_t attention_bf16(const AttnArgs& a, hipStream_t s) {
     case 256: return launch_attn16<256>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// ------------------------------------------------------------------ chunk queries
+// attention_chunk: the same attention for short query sets (the action chunk)
+// with K and V stored in the MFMA operand orders of common.h (K in frag_idx,
+// V in vfrag_idx order, key rows padded to whole 32-key tiles with zero
+// values), so every fragment is one contiguous 1 KB wave load straight into
+// registers: no LDS staging, no transposes.  All query heads that share a
+// key/value head are stacked into R = (Hq / Hkv) * Nq rows (row r is query
+// r % Nq of head r / Nq of the group); a workgroup owns 16 rows and its four
+// waves take interleaved 32-key tiles (w, w + 4, ...), each with the next
+// tile's fragments in flight.  Scores and outputs are formed transposed as in
+// k_attn16, with a lazily moved reference max, and the four waves' partial
+// softmax states are merged through LDS in wave order.
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
+  constexpr int KS = D / 32;  // K fragments per 16 keys
+  constexpr int VS = D / 16;  // V fragments per 32-key tile
+  constexpr int LDO = D + 4;  // merge rows (floats): 16-lane groups of 16-byte accesses hit distinct banks
+  __shared__ float mbuf[4][16], lbuf[4][16];
+  __shared__ __attribute__((aligned(16))) float obuf[4][16][LDO];
+
+  const int G = a.Hq / a.Hkv, R = G * a.Nq;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  int r = min((int)blockIdx.x * 16 + col, R - 1);  // clamped rows are computed, never stored
+  int jl = r / a.Nq, q = r - jl * a.Nq, j = g * G + jl;
+  const bf16_t* Qp = (const bf16_t*)a.q + b * a.q_bs + j * a.q_hs + (long)q * a.q_rs;
+  const u32x4_t* Kf = (const u32x4_t*)((const bf16_t*)a.k + b * a.k_bs + g * a.k_hs) + lane;
+  const u32x4_t* Vf = (const u32x4_t*)((const bf16_t*)a.v + b * a.v_bs + g * a.v_hs) + lane;
+  const int T = (a.Nk + 31) / 32;
+  const int NI = (T + 3) / 4;  // tiles per wave (the same for all waves; tiles past T are fully masked)
+
+  struct Tile { u32x4_t k[2 * KS], v[VS]; };
+  auto fetch = [&](Tile& t, int tl) {
+    const int tile = min(tl, T - 1);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) t.k[i] = Kf[((long)tile * 2 * KS + i) * 64];
+#pragma unroll
+    for (int i = 0; i < VS; ++i) t.v[i] = Vf[((long)tile * VS + i) * 64];
+  };
+
+  u32x4_t qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qf[s] = *(const u32x4_t*)(Qp + s * 32 + grp * 8);
+  Tile ta, tb;
+  fetch(ta, w);
+  fetch(tb, w + 4);
+
+  f32x4_t o[VS];
+#pragma unroll
+  for (int t = 0; t < VS; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // finite start: a tile whose keys are all masked then adds exp2(-inf) = 0
+  float mrun = -3.0e38f, lrun = 0.f;
+  const float sl2 = 1.4426950408889634f / sqrtf((float)D);
+
+  auto consume = [&](const Tile& t, int tl) {
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      s0 = mfma16x16x32(as_bf16x8(t.k[s]), as_bf16x8(qf[s]), s0);
+      s1 = mfma16x16x32(as_bf16x8(t.k[KS + s]), as_bf16x8(qf[s]), s1);
+    }
+    const int kt = tl * 32;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ka = kt + grp * 4 + i;
+      s0[i] = ka < a.Nk ? s0[i] * sl2 : -INFINITY;
+      s1[i] = ka + 16 < a.Nk ? s1[i] * sl2 : -INFINITY;
+      mt = fmaxf(mt, fmaxf(s0[i], s1[i]));
+    }
+    mt = group4_max(mt);
+    // the reference max moves (and O, l are rescaled) only when some query's
+    // max grew by more than 8 (log2 units); weights stay below 2^8
+    const bool grow = mt > mrun + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float mnew = grow ? mt : mrun;
+      const float alpha = fast_exp2(mrun - mnew);
+#pragma unroll
+      for (int t2 = 0; t2 < VS; ++t2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[t2][e] *= alpha;
+      lrun *= alpha;
+      mrun = mnew;
+    }
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s0[i] = fast_exp2(s0[i] - mrun);
+      s1[i] = fast_exp2(s1[i] - mrun);
+      ls += s0[i] + s1[i];
+    }
+    lrun += group4_sum(ls);
+    const u32x4_t pw = {pack_bf2(s0[0], s0[1]), pack_bf2(s0[2], s0[3]), pack_bf2(s1[0], s1[1]), pack_bf2(s1[2], s1[3])};
+    const bf16x8_t pf = as_bf16x8(pw);
+#pragma unroll
+    for (int t2 = 0; t2 < VS; ++t2) o[t2] = mfma16x16x32(as_bf16x8(t.v[t2]), pf, o[t2]);
+  };
+
+  // tile w + 4 i is consumed from ta (even i) or tb (odd i) while the next is in flight
+  for (int i = 0; i < NI; i += 2) {
+    consume(ta, w + 4 * i);
+    fetch(ta, w + 4 * (i + 2));
+    if (i + 1 >= NI) break;
+    consume(tb, w + 4 * (i + 1));
+    fetch(tb, w + 4 * (i + 3));
+  }
+
+  // merge the four waves' (max, sum, unnormalised O) in wave order
+  if (grp == 0) {
+    mbuf[w][col] = mrun;
+    lbuf[w][col] = lrun;
+  }
+#pragma unroll
+  for (int t2 = 0; t2 < VS; ++t2) *(f32x4_t*)&obuf[w][col][t2 * 16 + grp * 4] = o[t2];
+  __syncthreads();
+  const int qq = threadIdx.x & 15, d0 = (threadIdx.x >> 4) * (D / 16);
+  r = blockIdx.x * 16 + qq;
+  if (r >= R) return;
+  jl = r / a.Nq;
+  q = r - jl * a.Nq;
+  j = g * G + jl;
+  float M = mbuf[0][qq];
+#pragma unroll
+  for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, mbuf[ww][qq]);
+  float ew[4], L = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) {
+    ew[ww] = fast_exp2(mbuf[ww][qq] - M);
+    L += ew[ww] * lbuf[ww][qq];
+  }
+  const float inv = __builtin_amdgcn_rcpf(L);
+  const long row = (long)b * a.Nq + q;
+#pragma unroll
+  for (int d = d0; d < d0 + D / 16; d += 4) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const f32x4_t x = *(const f32x4_t*)&obuf[ww][qq][d];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += ew[ww] * x[e];
+    }
+    const u32x2_t pk = {pack_bf2(acc[0] * inv, acc[1] * inv), pack_bf2(acc[2] * inv, acc[3] * inv)};
+    const long oi = a.o_frag ? frag_idx((int)row, j * D + d, a.Hq * D) : b * a.o_bs + (long)q * a.o_rs + (long)j * D + d;
+    *(u32x2_t*)((bf16_t*)a.o + oi) = pk;
+  }
+}
+
+hipError_t attention_chunk(const AttnArgs& a, hipStream_t s) {
+  if (a.B <= 0 || a.Nq <= 0 || a.Nk <= 0) return hipSuccess;
+  if (a.Hq % a.Hkv || a.o_f32) return hipErrorInvalidValue;
+  if (a.o_frag && a.B * a.Nq > 64) return hipErrorInvalidValue;
+  const int R = a.Hq / a.Hkv * a.Nq;
+  dim3 grid((R + 15) / 16, a.Hkv, a.B);
+  switch (a.hd) {
+    case 64: hipLaunchKernelGGL(k_attn_chunk<64>, grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(k_attn_chunk<128>, grid, dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(k_attn_chunk<256>, grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ fp32

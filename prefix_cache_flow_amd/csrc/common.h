@@ -19,12 +19,12 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 // ---------------------------------------------------------------- bfloat16
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// float -> bfloat16, round to nearest, ties to even (NaN kept quiet)
+// float -> bfloat16, round to nearest, ties to even (NaN kept quiet); written
+// as a select so that stores of converted values stay free of branches
 __device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (bf16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : r);
 }
 
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
@@ -39,6 +39,22 @@ __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + e
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------- reductions
+// Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48)
+// with the gfx950 lane-swap instructions: each swap pairs lane l with l^32
+// (l^16) as its two results, a VALU round trip instead of an LDS permute.
+__device__ __forceinline__ float group4_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float group4_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -102,6 +118,17 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_
 // lane), blocks row-block major.  One wave loads one block as one contiguous 1 KB.
 __host__ __device__ __forceinline__ long frag_idx(int m, int k, int K) {
   return ((((long)(m >> 4) * (K >> 5) + (k >> 5)) * 64 + ((m & 15) + ((k >> 3) & 3) * 16)) << 3) + (k & 7);
+}
+
+// Value layout for the P V product of attention, O^T += V^T P^T on the 16x16x32
+// MFMA, for a [keys][D] matrix V: one 1 KB block per 32-key tile and 16 columns
+// d, holding V^T's A-operand fragment.  Lane (d % 16) + 16 * g supplies 8 keys
+// of the tile, {4 g .. 4 g + 3} then {16 + 4 g .. 16 + 4 g + 3}: the order in
+// which the transposed score accumulator (rows = keys) hands P^T to the B operand.
+__host__ __device__ __forceinline__ long vfrag_idx(int t, int d, int D) {
+  const int kin = t & 31;
+  const long blk = (long)(t >> 5) * (D >> 4) + (d >> 4);
+  return ((blk * 64 + (d & 15) + 16 * ((kin & 15) >> 2)) << 3) + (kin >> 4) * 4 + (kin & 3);
 }
 
 // acc row index of element i for lane l in a 32x32 MFMA block

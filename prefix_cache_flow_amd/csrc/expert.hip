@@ -165,4 +165,17 @@ hipError_t f32_to_bf16(const float* src, uint16_t* dst, long n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// zero the last `tail` 16-bit elements of each of `nblk` blocks of `blk` elements
+__global__ void k_zero_tails(uint16_t* base, long blk, int tail) {
+  uint16_t* p = base + (long)blockIdx.x * blk + (blk - tail);
+  for (int i = threadIdx.x * 8; i < tail; i += blockDim.x * 8) *(u32x4_t*)(p + i) = u32x4_t{0u, 0u, 0u, 0u};
+}
+
+hipError_t zero_tails(void* base, long nblk, long blk, int tail, hipStream_t s) {
+  if (nblk <= 0 || tail <= 0) return hipSuccess;
+  if (tail % 8 || blk % 8 || tail > blk || nblk > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_zero_tails, dim3((unsigned)nblk), dim3(256), 0, s, (uint16_t*)base, blk, tail);
+  return hipGetLastError();
+}
+
 }  // namespace vla

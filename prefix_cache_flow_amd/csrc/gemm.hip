@@ -35,7 +35,23 @@ __device__ __forceinline__ void cache_index(const Epilogue& e, int m, int n, lon
   r -= kv * per_kv;
   const int h = r / e.hd, d = r - h * e.hd;
   const int b = m / e.npre, t = m - b * e.npre;
-  idx = ((((long)(b * e.L + l) * 2 + kv) * e.hkv + h) * e.npre + t) * e.hd + d;
+  const long blk = ((((long)(b * e.L + l) * 2 + kv) * e.hkv + h) * e.npad) * e.hd;
+  idx = blk + (!e.out_frag ? (long)t * e.hd + d : kv ? vfrag_idx(t, d, e.hd) : frag_idx(t, d, e.hd));
+}
+
+// EPI_QKV: query columns to rows, keys and values of the chunk in their MFMA orders
+__device__ __forceinline__ void qkv_store(const Epilogue& e, int m, int n, float v) {
+  if (n < e.nq) {
+    ((bf16_t*)e.out)[(long)m * e.ldo + n] = f2bf(v);
+    return;
+  }
+  const int per = e.hkv * e.hd;
+  const int kv = (n - e.nq) >= per, r = n - e.nq - kv * per;
+  const int h = r / e.hd, d = r - h * e.hd;
+  const int b = m / e.npre, t = m - b * e.npre;
+  const long blk = ((long)b * e.hkv + h) * e.npad * e.hd;
+  if (kv) ((bf16_t*)e.vout)[blk + vfrag_idx(t, d, e.hd)] = f2bf(v);
+  else ((bf16_t*)e.kout)[blk + frag_idx(t, d, e.hd)] = f2bf(v);
 }
 
 // Store one finished element (every kind but GEGLU, which needs a pair).  The
@@ -53,6 +69,8 @@ __device__ __forceinline__ void epi_store_t(const Epilogue& e, int m, int n, flo
     long i;
     cache_index(e, m, n, i);
     if (e.out_f32) ((float*)e.out)[i] = v; else ((bf16_t*)e.out)[i] = f2bf(v);
+  } else if (KIND == EPI_QKV) {
+    qkv_store(e, m, n, v);
   }
 }
 
@@ -60,6 +78,7 @@ __device__ __forceinline__ void epi_store(const Epilogue& e, int m, int n, float
   if (e.kind == EPI_STORE) epi_store_t<EPI_STORE>(e, m, n, v);
   else if (e.kind == EPI_RESID) epi_store_t<EPI_RESID>(e, m, n, v);
   else if (e.kind == EPI_CACHE) epi_store_t<EPI_CACHE>(e, m, n, v);
+  else if (e.kind == EPI_QKV) epi_store_t<EPI_QKV>(e, m, n, v);
 }
 
 __device__ __forceinline__ void epi_geglu(const Epilogue& e, int m, int f, float g, float u) {
@@ -383,6 +402,7 @@ static hipError_t launch_bf16(const GemmP& p, int splits, hipStream_t s) {
   if constexpr (WF) {  // expert weights: only the kinds of the expert layer
     switch (kind) {
       case EPI_STORE: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_STORE, true>), grid, blk, 0, s, q); break;
+      case EPI_QKV: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_QKV, true>), grid, blk, 0, s, q); break;
       case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_GEGLU, true>), grid, blk, 0, s, q); break;
       case EPI_PARTIAL: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_PARTIAL, true>), grid, blk, 0, s, q); break;
       default: return hipErrorInvalidValue;
@@ -421,6 +441,7 @@ hipError_t gemm_bf16(const uint16_t* A, int lda, const uint16_t* W, int ldw, int
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
   if (K % 64 || N % 32) return hipErrorInvalidValue;
   if (w_frag && (M <= 64 || ldw != K || epi.kind == EPI_RESID || epi.kind == EPI_CACHE)) return hipErrorInvalidValue;
+  if (!w_frag && epi.kind == EPI_QKV) return hipErrorInvalidValue;
   // the one place that fixes how many partial slices are written: callers that
   // consume EPI_PARTIAL output read gemm_bf16_splits(K, splits, M) of them
   splits = gemm_bf16_splits(K, splits, M);
@@ -537,6 +558,7 @@ static hipError_t launch_chunk_mb(const ChunkP& p, int kind, dim3 grid, hipStrea
   switch (kind) {
     case EPI_GEGLU: hipLaunchKernelGGL((k_chunk<2, MB, EPI_GEGLU>), grid, dim3(256), 0, s, p); break;
     case EPI_STORE: hipLaunchKernelGGL((k_chunk<1, MB, EPI_STORE>), grid, dim3(256), 0, s, p); break;
+    case EPI_QKV: hipLaunchKernelGGL((k_chunk<1, MB, EPI_QKV>), grid, dim3(256), 0, s, p); break;
     case EPI_PARTIAL: hipLaunchKernelGGL((k_chunk<1, MB, EPI_PARTIAL>), grid, dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
@@ -547,7 +569,8 @@ hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int 
                       float* ws, hipStream_t s) {
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
   if (M > 64 || K % 32 || N % 32) return hipErrorInvalidValue;
-  if (epi.kind != EPI_STORE && epi.kind != EPI_PARTIAL && epi.kind != EPI_GEGLU) return hipErrorInvalidValue;
+  if (epi.kind != EPI_STORE && epi.kind != EPI_PARTIAL && epi.kind != EPI_GEGLU && epi.kind != EPI_QKV)
+    return hipErrorInvalidValue;
   int used, per;
   skinny_plan(K, splits, &used, &per);
   if (epi.kind == EPI_GEGLU && used > 1) return hipErrorInvalidValue;  // GeGLU needs whole sums
@@ -555,13 +578,14 @@ hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int 
   ChunkP p{Af, Wf, M, N, K, per * 32, epi, ws};
   const int nb = epi.kind == EPI_GEGLU ? 2 : 1;
   const dim3 grid(N / (16 * nb), used);
-  const int kind = (used > 1 && epi.kind == EPI_STORE) ? EPI_PARTIAL : epi.kind;
+  const bool reduce = used > 1 && (epi.kind == EPI_STORE || epi.kind == EPI_QKV);
+  const int kind = reduce ? EPI_PARTIAL : epi.kind;
   const int mb = (M + 15) / 16;
   hipError_t err = mb == 1 ? launch_chunk_mb<1>(p, kind, grid, s)
                  : mb == 2 ? launch_chunk_mb<2>(p, kind, grid, s)
                            : launch_chunk_mb<4>(p, kind, grid, s);
   if (err != hipSuccess) return err;
-  if (used > 1 && epi.kind == EPI_STORE) {
+  if (reduce) {
     const long tot = (long)M * N;
     const int blocks = (int)std::min<long>((tot + 255) / 256, 4096);
     hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, (const float*)ws, used, M, N, epi);

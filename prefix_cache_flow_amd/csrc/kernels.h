@@ -16,9 +16,15 @@ enum EpiKind {
                   // gate feature 16 b + i for i < 16, up feature 16 b + i - 16 otherwise;
                   // out[m * ldo + f] = GELU(gate_f) * up_f     (bf16 or fp32)
   EPI_CACHE = 3,  // K/V cache scatter: row m = (b, t) with b = m / npre, t = m % npre;
-                  // column n = ((l * 2 + kv) * hkv + h) * hd + d;
-                  // out[((((b * L + l) * 2 + kv) * hkv + h) * npre + t) * hd + d] = v
-  EPI_PARTIAL = 4 // raw fp32 partial sums to ws[split][m][n], left for a row kernel
+                  // column n = ((l * 2 + kv) * hkv + h) * hd + d; block
+                  // ((b * L + l) * 2 + kv) * hkv + h of npad * hd elements holds
+                  // (t, d) row-major (out_frag == 0) or, with out_frag, K in
+                  // frag_idx and V in vfrag_idx order (common.h)
+  EPI_PARTIAL = 4,// raw fp32 partial sums to ws[split][m][n], left for a row kernel
+  EPI_QKV = 5     // fused self-attention projection of the chunk, row m = (b, t) with
+                  // b = m / npre: columns n < nq go to out[m * ldo + n] (bf16 rows),
+                  // the next hkv * hd to kout and the last hkv * hd to vout, blocks
+                  // b * hkv + h of npad * hd elements in frag_idx / vfrag_idx order
 };
 
 struct Epilogue {
@@ -28,7 +34,11 @@ struct Epilogue {
   int out_f32 = 0;       // 1: fp32 output, 0: bf16
   float* resid = nullptr;
   int ldr = 0;
-  int npre = 0, L = 0, hkv = 0, hd = 0;  // EPI_CACHE
+  int npre = 0, L = 0, hkv = 0, hd = 0;  // EPI_CACHE, EPI_QKV
+  int npad = 0;                          // EPI_CACHE, EPI_QKV: key rows per block (npre rounded up)
+  int nq = 0;                            // EPI_QKV: query columns
+  void* kout = nullptr;                  // EPI_QKV
+  void* vout = nullptr;                  // EPI_QKV
   // W2A8 output scaling: y = bf16(float(acc) * (alpha[m] * beta[n])) before the epilogue
   const float* alpha = nullptr;
   const float* beta = nullptr;
@@ -102,6 +112,11 @@ struct AttnArgs {
 };
 // softmax(Q K^T / sqrt(hd)) V per head, no mask; bf16 inputs on MFMA (hd in 64..256)
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s);
+// The same for short query sets with K and V in the MFMA operand orders of
+// common.h (frag_idx / vfrag_idx per batch-and-head block of k_bs / k_hs
+// elements, key rows padded to a multiple of 32 with zero values); Q rows as
+// above (k_rs, v_rs unused); bf16 output only.
+hipError_t attention_chunk(const AttnArgs& a, hipStream_t s);
 // fp32 inputs on the vector ALU (small shapes)
 hipError_t attention_f32(const AttnArgs& a, hipStream_t s);
 
@@ -114,6 +129,9 @@ hipError_t expert_embed(const float* X, int M, int d_a, const void* w_in, int w_
 hipError_t expert_head(const float* E, int M, int d_e, const float* gain, float eps,
                        const void* w_out, int w_f32, int d_a, const float* sched, int k, float* X,
                        hipStream_t s);
+// Zero the last `tail` 16-bit elements of each of nblk blocks of `blk` elements
+// (the padding key rows of fragment-ordered K/V blocks); tail, blk % 8 == 0.
+hipError_t zero_tails(void* base, long nblk, long blk, int tail, hipStream_t s);
 // dst = src (fp32), or bf16(src) when out_bf16
 hipError_t copy_out(const float* src, void* dst, long n, int out_bf16, hipStream_t s);
 hipError_t copy_f32(const float* src, float* dst, long n, hipStream_t s);

@@ -558,6 +558,10 @@ extern "C" vla_status vla_model_destroy(vla_model* m) {
   return VLA_OK;
 }
 
+// Key rows of one K or V block: bf16 blocks hold whole 32-key tiles in the MFMA
+// operand orders (padding rows zero), fp32 blocks are plain rows.
+static int64_t key_rows(const vla_model* m, int64_t n) { return m->f32 ? n : (n + 31) / 32 * 32; }
+
 // ============================================================== workspace
 // Byte layout of the model workspace for `rows` prefix tokens and `erows` chunk rows.
 struct WS {
@@ -573,7 +577,9 @@ struct WS {
   float* X;         // [erows][d_a]
   float* E;         // [erows][d_e]
   void* eu;         // [erows][d_e]
-  void* eqkv;       // [erows][(Hq_e + 2 Hkv_e) hd_e]
+  void* eqkv;       // [erows][(Hq_e + 2 Hkv_e) hd_e] (bf16: queries only, [erows][Hq_e hd_e])
+  void* ek;         // bf16 chunk keys   [B][Hkv_e][Hp][hd_e], frag_idx order, Hp = H rounded up to 32
+  void* ev;         // bf16 chunk values [B][Hkv_e][Hp][hd_e], vfrag_idx order
   void* eq;         // [erows][Hq_e hd_e]
   void* eattn;      // [erows][Hq_e hd_e]
   void* emlp;       // [erows][F_e]
@@ -614,6 +620,9 @@ static WS plan(const vla_model* m, int64_t rows, int64_t erows, char* base) {
   const int64_t frows = erows <= 64 ? 64 : erows;
   w.eu = take(frows * c.d_e * es);
   w.eqkv = take(erows * qkve * es);
+  const int64_t kvblk = c.H > 0 ? erows / c.H * c.Hkv_e * key_rows(m, c.H) * c.hd_e : 0;
+  w.ek = take(kvblk * es);
+  w.ev = take(kvblk * es);
   w.eq = take(erows * qe * es);
   w.eattn = take(frows * qe * es);
   w.emlp = take(frows * (int64_t)c.F_e * es);
@@ -820,7 +829,12 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
   Epilogue ce;
   ce.kind = EPI_CACHE; ce.out = kv; ce.out_f32 = m->f32 ? 1 : 0;
   ce.npre = N; ce.L = c.L_e; ce.hkv = c.Hkv_e; ce.hd = c.hd_e;
+  ce.npad = (int)key_rows(m, N);
+  ce.out_frag = m->f32 ? 0 : 1;
   const int ncache = c.L_e * 2 * c.Hkv_e * c.hd_e;
+  // padding key rows of the last tile must hold finite values (zero weight times value)
+  if (ce.npad > N)
+    K_TRY(zero_tails(kv, (long)B * c.L_e * 2 * c.Hkv_e, (long)ce.npad * c.hd_e, 32 * c.hd_e, s), "cache padding");
   ProbeScope ps(m, VLA_PROBE_CACHE, s);
   if (m->f32)
     K_TRY(gemm_f32((const float*)w.u, c.d_p, (const float*)m->wcache, c.d_p, M, ncache, c.d_p, ce, s), "cache");
@@ -832,7 +846,7 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
 extern "C" size_t vla_kv_cache_bytes(const vla_model* m, int32_t batch, int32_t n_prefix) {
   if (!live_model(m) || batch <= 0 || n_prefix <= 0) return 0;
   const vla_model_config& c = m->cfg;
-  return (size_t)batch * c.L_e * 2 * c.Hkv_e * (size_t)n_prefix * c.hd_e * elt(m);
+  return (size_t)batch * c.L_e * 2 * c.Hkv_e * (size_t)key_rows(m, n_prefix) * c.hd_e * elt(m);
 }
 
 extern "C" vla_status vla_prefix_encode(vla_model* m, const float* x, int32_t batch, int32_t n_prefix, void* kv_storage,
@@ -906,19 +920,29 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
   const size_t es = elt(m);
   // self-attention over the H chunk tokens of each observation
   AttnArgs sa{};
-  sa.q = w.eqkv; sa.q_bs = (long)H * qkve; sa.q_hs = c.hd_e; sa.q_rs = qkve;
-  sa.k = (const char*)w.eqkv + (size_t)qe * es; sa.k_bs = sa.q_bs; sa.k_hs = c.hd_e; sa.k_rs = qkve;
-  sa.v = (const char*)w.eqkv + (size_t)(qe + c.Hkv_e * c.hd_e) * es; sa.v_bs = sa.q_bs; sa.v_hs = c.hd_e; sa.v_rs = qkve;
+  const int Hp = (int)key_rows(m, H), Np = (int)key_rows(m, N);
+  if (f32) {  // plain rows of the fused projection output
+    sa.q = w.eqkv; sa.q_bs = (long)H * qkve; sa.q_hs = c.hd_e; sa.q_rs = qkve;
+    sa.k = (const char*)w.eqkv + (size_t)qe * es; sa.k_bs = sa.q_bs; sa.k_hs = c.hd_e; sa.k_rs = qkve;
+    sa.v = (const char*)w.eqkv + (size_t)(qe + c.Hkv_e * c.hd_e) * es; sa.v_bs = sa.q_bs; sa.v_hs = c.hd_e; sa.v_rs = qkve;
+  } else {  // query rows, keys and values in the MFMA operand orders (EPI_QKV)
+    sa.q = w.eqkv; sa.q_bs = (long)H * qe; sa.q_hs = c.hd_e; sa.q_rs = qe;
+    sa.k = w.ek; sa.k_bs = (long)c.Hkv_e * Hp * c.hd_e; sa.k_hs = (long)Hp * c.hd_e;
+    sa.v = w.ev; sa.v_bs = sa.k_bs; sa.v_hs = sa.k_hs;
+  }
   sa.o = w.eattn; sa.o_bs = (long)H * qe; sa.o_rs = qe;
   sa.B = B; sa.Nq = H; sa.Nk = H; sa.Hq = c.Hq_e; sa.Hkv = c.Hkv_e; sa.hd = c.hd_e; sa.o_f32 = f32 ? 1 : 0;
+  Epilogue qkv_e;  // bf16 fused self-attention projection
+  qkv_e.kind = EPI_QKV; qkv_e.out = w.eqkv; qkv_e.ldo = qe; qkv_e.nq = qe;
+  qkv_e.kout = w.ek; qkv_e.vout = w.ev; qkv_e.hkv = c.Hkv_e; qkv_e.hd = c.hd_e; qkv_e.npre = H; qkv_e.npad = Hp;
   // up to 64 chunk rows: GEMM inputs in the fragment layout, weights always are (bf16)
   const int fr = (!f32 && M <= 64) ? 1 : 0;
   sa.o_frag = fr;
   // cross-attention into the cache [B][L_e][2][Hkv_e][N][hd_e]
   AttnArgs ca = sa;
-  const long layer_stride = 2L * c.Hkv_e * N * c.hd_e;
+  const long layer_stride = 2L * c.Hkv_e * Np * c.hd_e;
   ca.q = w.eq; ca.q_bs = (long)H * qe; ca.q_hs = c.hd_e; ca.q_rs = qe;
-  ca.k_bs = c.L_e * layer_stride; ca.k_hs = (long)N * c.hd_e; ca.k_rs = c.hd_e;
+  ca.k_bs = c.L_e * layer_stride; ca.k_hs = (long)Np * c.hd_e; ca.k_rs = c.hd_e;
   ca.v_bs = ca.k_bs; ca.v_hs = ca.k_hs; ca.v_rs = c.hd_e;
   ca.Nk = N;
   Epilogue pe;
@@ -930,7 +954,7 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
     for (int e = 0; e < c.L_e; ++e) {
       const ExpertLayer& L = m->el[e];
       ca.k = (const char*)kv->storage + (size_t)e * layer_stride * es;
-      ca.v = (const char*)ca.k + (size_t)c.Hkv_e * N * c.hd_e * es;
+      ca.v = (const char*)ca.k + (size_t)c.Hkv_e * Np * c.hd_e * es;
       if (f32) {
         K_TRY(gemm_f32((const float*)w.eu, c.d_e, (const float*)L.wqkv, c.d_e, M, qkve, c.d_e, epi_store(w.eqkv, qkve, 1), s), "qkv_s");
         K_TRY(attention_f32(sa, s), "self attn");
@@ -955,12 +979,12 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
           if (fr) return gemm_chunk((const uint16_t*)A, (const uint16_t*)W, M, N, K, ep, splits, w.epart, s);
           return gemm_bf16((const uint16_t*)A, lda, (const uint16_t*)W, K, M, N, K, ep, splits, w.epart, s, 1);
         };
-        K_TRY(mm(u, c.d_e, L.wqkv, qkve, c.d_e, epi_store(w.eqkv, qkve, 0), 1), "qkv_s");
-        K_TRY(attention_bf16(sa, s), "self attn");
+        K_TRY(mm(u, c.d_e, L.wqkv, qkve, c.d_e, qkv_e, 1), "qkv_s");
+        K_TRY(attention_chunk(sa, s), "self attn");
         K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
         K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
         K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, epi_store(w.eq, qe, 0), 1), "q_c");
-        K_TRY(attention_bf16(ca, s), "cross attn");
+        K_TRY(attention_chunk(ca, s), "cross attn");
         K_TRY(mm(w.eattn, qe, L.woc, c.d_e, qe, pe, S_o), "o_c");
         K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
         Epilogue g = epi_store(w.emlp, c.F_e, 0);

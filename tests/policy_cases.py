@@ -60,17 +60,37 @@ def gpu_run(cfg, model, z0, x0, steps=None, out_dtype=None, schedule=None):
     return res, storage
 
 
+def _cache_index_maps(N, hd):
+    """Positions of (t, d) inside one bf16 K block and one V block (the layout vla.h states)."""
+    t = np.arange(N)[:, None]
+    d = np.arange(hd)[None, :]
+    kpos = ((((t // 16) * (hd // 32) + d // 32) * 64 + t % 16 + 16 * ((d // 8) % 4)) * 8 + d % 8)
+    u = t % 32
+    vpos = ((((t // 32) * (hd // 16) + d // 16) * 64 + d % 16 + 16 * ((u % 16) // 4)) * 8 + 4 * (u // 16) + u % 4)
+    return kpos, vpos
+
+
 def cache_from_storage(cfg, storage, B, N):
-    """[B][L_e][2][Hkv_e][N][hd_e] device storage -> per observation list of (K_C, V_C) [N, Hkv_e*hd_e]."""
+    """Cache storage -> per observation list of (K_C, V_C), each [N, Hkv_e*hd_e] float64.
+
+    fp32 caches are plain rows; bf16 caches hold 32-row-padded blocks in the MFMA operand orders.
+    """
     import torch
-    dt = torch.float32 if cfg.precision == "f32" else torch.bfloat16
-    t = storage.view(dt).float().cpu().numpy().reshape(B, cfg.L_e, 2, cfg.Hkv_e, N, cfg.hd_e)
+    f32 = cfg.precision == "f32"
+    dt = torch.float32 if f32 else torch.bfloat16
+    Np = N if f32 else (N + 31) // 32 * 32
+    t = storage.view(dt)[: B * cfg.L_e * 2 * cfg.Hkv_e * Np * cfg.hd_e].float().cpu().numpy()
+    t = t.reshape(B, cfg.L_e, 2, cfg.Hkv_e, Np * cfg.hd_e)
+    if f32:
+        kpos = vpos = (np.arange(N)[:, None] * cfg.hd_e + np.arange(cfg.hd_e)[None, :])
+    else:
+        kpos, vpos = _cache_index_maps(N, cfg.hd_e)
     out = []
     for b in range(B):
         layers = []
         for e in range(cfg.L_e):
-            k = t[b, e, 0].transpose(1, 0, 2).reshape(N, cfg.Hkv_e * cfg.hd_e)
-            v = t[b, e, 1].transpose(1, 0, 2).reshape(N, cfg.Hkv_e * cfg.hd_e)
+            k = t[b, e, 0][:, kpos].transpose(1, 0, 2).reshape(N, cfg.Hkv_e * cfg.hd_e)
+            v = t[b, e, 1][:, vpos].transpose(1, 0, 2).reshape(N, cfg.Hkv_e * cfg.hd_e)
             layers.append((k.astype(np.float64), v.astype(np.float64)))
         out.append(layers)
     return out
