@@ -39,7 +39,21 @@ def parse():
     p.add_argument("--config", type=int, default=1, help="workload index (1 = single camera bf16)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-s", type=float, default=30.0)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB mebibytes (reference for the HBM byte counters) and exit")
     return p.parse_args()
+
+
+def copy_calibration(mib):
+    """One plain device-to-device copy of a known size: its FETCH_SIZE / WRITE_SIZE counters scale the kernels'."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n}), flush=True)
 
 
 def prefix_flops(c):
@@ -69,6 +83,10 @@ def main():
                                    "described in DESIGN.md)"}))
         sys.exit(2)
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import synth
     from prefix_cache_flow_amd import vla
