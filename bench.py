@@ -30,6 +30,12 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_INT8_TOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch of the prefix gate/up kernel from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE),
+# scaled by what the same counters read for a plain copy (profiles/hbm_bytes_prefix_gateup_single_camera_bf16.md).
+# Valid only for the kernel instance named here; None once that kernel changes until it is measured again.
+GATEUP_KERNEL = "k_gemm_bf16<96, 128, 1, 4, 2, false>"
+GATEUP_TRAFFIC_BYTES = 166815027
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -156,9 +162,9 @@ def main():
     flops_per_launch = 2 * N * cfg.d_p * 2 * cfg.F_p
     avg_ms = probe_ms / max(probe_launches, 1)
     achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "k_gemm_bf16 (prefix gate/up + GeGLU)",
+    roofline = {"bound": "mfma", "kernel": GATEUP_KERNEL + " (prefix gate/up + GeGLU)",
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": GATEUP_TRAFFIC_BYTES,
                 "avg_launch_us": avg_ms * 1e3, "launches": probe_launches,
                 "flops_per_launch": flops_per_launch}
 
