@@ -1,14 +1,14 @@
 // Dense projections of the policy step: C = A W^T with A [M, K] activations and
 // W [N, K] weights (the [out, in] layout of every linear layer).
 //
-// gemm_bf16: bf16 operands, fp32 accumulation on the 32x32x16 bf16 MFMA of gfx950.
-//   Workgroup tile BM x BN, 64-wide K slices staged through LDS with one
-//   register-prefetched slice ahead (double-buffered LDS, one barrier per slice).
-//   Each wave owns a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.  Rows of
-//   LDS are padded by 16 bytes so the 16-byte reads of a 32-lane column group hit
-//   distinct banks.  Output tiles are mapped XCD-major: consecutive workgroup ids
-//   land on different XCDs, so tiles that share a weight panel (same n, every m)
-//   are numbered to run on one XCD and share its L2.
+// gemm_bf16: bf16 operands, fp32 accumulation on the bf16 MFMA of gfx950.
+//   More than 64 rows: 288 x 128 workgroup tiles (k_gemm_wide), 64-wide K slices
+//   staged through LDS with one register-prefetched slice ahead.  Rows of LDS are
+//   padded by 16 bytes so the 16-byte fragment reads of 16 consecutive rows hit
+//   distinct banks.  Output tiles are numbered XCD-major so tiles that share a
+//   weight panel run on one XCD and share its L2.
+//   At most 64 rows: weight-streaming kernels (k_skinny for row-major operands,
+//   k_chunk for the fragment layout of common.h).
 //   Split-K writes fp32 partials [split][M][N] that a fixed-order reduction (or
 //   the row kernel of norm.hip) sums, so results never depend on timing.
 // gemm_f32: fp32 SIMT tiles for the fp32 workload (small shapes).
@@ -85,131 +85,6 @@ __device__ __forceinline__ void epi_geglu(const Epilogue& e, int m, int f, float
   const float v = gelu_erf(g) * u;
   const long i = e.out_frag ? frag_idx(m, f, e.ldo) : (long)m * e.ldo + f;
   if (e.out_f32) ((float*)e.out)[i] = v; else ((bf16_t*)e.out)[i] = f2bf(v);
-}
-
-template <int BM, int BN, int WM, int WN, int KIND, bool WF>
-__global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GemmP p) {
-  constexpr int NT = 64 * WM * WN, BK = 64, LDK = BK + 8;
-  constexpr int TM = BM / (32 * WM), TN = BN / (32 * WN);
-  static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "tile shape");
-  constexpr int AV = BM * BK / 8, WV = BN * BK / 8;  // 16-byte vectors per slice
-  constexpr int AVT = (AV + NT - 1) / NT, WVT = (WV + NT - 1) / NT;
-  constexpr int LDC = BN + 4;                         // epilogue tile row stride (floats)
-  constexpr int STAGE = 2 * (BM + BN) * LDK * 2;      // bytes of the two staging buffers
-  static_assert(BM * LDC * 4 <= STAGE, "epilogue tile must fit in the staging area");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDK];
-  // buffer b of the activation tile at smem + b * BM * LDK, of the weight tile after both
-  auto sA = [&](int b) { return smem + b * (BM * LDK); };
-  auto sW = [&](int b) { return smem + 2 * BM * LDK + b * (BN * LDK); };
-
-  const int nt = p.nM * p.nN, L = blockIdx.x;
-  const int tile = (nt % 8 == 0) ? (L % 8) * (nt / 8) + L / 8 : L;
-  const int tm = tile % p.nM, tn = tile / p.nM;
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int kb = blockIdx.y * p.kchunk;
-  const int ke = min(p.K, kb + p.kchunk);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid / WN, wn = wid % WN;
-
-  u32x4_t ra[AVT], rw[WVT];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < AVT; ++i) {
-      const int v = tid + i * NT;
-      if (AV % NT == 0 || v < AV) {
-        const int r = v >> 3, c = (v & 7) * 8, gm = min(m0 + r, p.M - 1);  // clamped rows are never stored
-        ra[i] = *(const u32x4_t*)(p.A + (long)gm * p.lda + k0 + c);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < WVT; ++i) {
-      const int v = tid + i * NT;
-      if (WV % NT == 0 || v < WV) {
-        const int r = v >> 3, c = (v & 7) * 8, gn = min(n0 + r, p.N - 1);
-        // WF: the weights are in the fragment layout; 8 consecutive k stay one 16-byte vector
-        rw[i] = *(const u32x4_t*)(p.W + (WF ? frag_idx(gn, k0 + c, p.ldw) : (long)gn * p.ldw + k0 + c));
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < AVT; ++i) {
-      const int v = tid + i * NT;
-      if (AV % NT == 0 || v < AV) *(u32x4_t*)&sA(buf)[(v >> 3) * LDK + (v & 7) * 8] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < WVT; ++i) {
-      const int v = tid + i * NT;
-      if (WV % NT == 0 || v < WV) *(u32x4_t*)&sW(buf)[(v >> 3) * LDK + (v & 7) * 8] = rw[i];
-    }
-  };
-
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  if (kb < ke) {
-    gload(kb);
-    sstore(0);
-  }
-  __syncthreads();
-  int it = 0;
-  for (int k0 = kb; k0 < ke; k0 += BK, ++it) {
-    const int buf = it & 1;
-    const bool more = k0 + BK < ke;
-    if (more) gload(k0 + BK);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t af[TM], wf[TN];
-      const int koff = kk * 16 + (lane >> 5) * 8;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = as_bf16x8(*(const u32x4_t*)&sA(buf)[((wm * TM + i) * 32 + (lane & 31)) * LDK + koff]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        wf[j] = as_bf16x8(*(const u32x4_t*)&sW(buf)[((wn * TN + j) * 32 + (lane & 31)) * LDK + koff]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(af[i], wf[j], acc[i][j]);
-    }
-    if (more) sstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: the tile goes through LDS, then a rolled loop stores it row by row
-  float* ct = (float*)smem;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        ct[((wm * TM + i) * 32 + mfma32_row(e, lane)) * LDC + (wn * TN + j) * 32 + (lane & 31)] = acc[i][j][e];
-  __syncthreads();
-  const int rows = min(BM, p.M - m0);
-  if (KIND == EPI_GEGLU) {
-    // column 32 b + c (c < 16) is gate feature 16 b + c, column 32 b + 16 + c its up value
-    constexpr int FW = BN / 2;
-    for (int idx = tid; idx < rows * FW; idx += NT) {
-      const int r = idx / FW, f = idx % FW;
-      const int cg = (f >> 4) * 32 + (f & 15);
-      epi_geglu(p.epi, m0 + r, (n0 >> 1) + f, ct[r * LDC + cg], ct[r * LDC + cg + 16]);
-    }
-  } else {
-    for (int idx = tid; idx < rows * BN; idx += NT) {
-      const int r = idx / BN, c = idx % BN;
-      const int m = m0 + r, n = n0 + c;
-      if (n >= p.N) continue;
-      const float v = ct[r * LDC + c];
-      if (KIND == EPI_PARTIAL) p.ws[((long)blockIdx.y * p.M + m) * p.N + n] = v;
-      else epi_store_t<KIND>(p.epi, m, n, v);
-    }
-  }
 }
 
 // Fixed-order sum of split-K partials followed by the epilogue.
@@ -387,10 +262,130 @@ static hipError_t launch_skinny(const SkinnyP& p0, int splits, hipStream_t s) {
   return err;
 }
 
-template <int BM, int BN, int WM, int WN, bool WF>
-static hipError_t launch_bf16(const GemmP& p, int splits, hipStream_t s) {
+// ------------------------------------------------------------------ wide tiles (prefix)
+// Many rows (the prefix: hundreds of tokens).  A workgroup owns a 288 x BN
+// output tile; four waves in a 2 x 2 arrangement each hold 144 x BN/2 of it as
+// 9 x BN/32 accumulators of the 16x16x32 MFMA.  Per 32-wide k step a wave reads
+// 9 + BN/32 fragments from LDS for 9 * BN/32 MFMAs, and per 64-wide K slice the
+// workgroup fetches (288 + BN) x 64 bf16 from global memory: both stay below the
+// LDS and L1 rates that the MFMA rate needs, which smaller tiles (fewer MFMAs per
+// byte) do not.  K slices are double-buffered in LDS with one slice prefetched
+// in registers; rows past M and columns past N are clamped on load and never
+// stored.  Epilogues are applied straight from the accumulators: with BN/2 a
+// multiple of 32, the gate and up blocks of the GeGLU interleave sit in the same
+// lane.
+template <int BN, int KIND, bool WF>
+__global__ __launch_bounds__(256) void k_gemm_wide(GemmP p) {
+  constexpr int BM = 288, BK = 64, LDK = BK + 8;
+  constexpr int TM = BM / 2 / 16, TN = BN / 2 / 16;
+  constexpr int AVT = BM * BK / 8 / 256, WVT = BN * BK / 8 / 256;  // 16-byte vectors per thread and slice
+  static_assert(AVT * 256 * 8 == BM * BK && WVT * 256 * 8 == BN * BK, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDK];
+  auto sA = [&](int b) { return smem + b * (BM * LDK); };
+  auto sW = [&](int b) { return smem + 2 * BM * LDK + b * (BN * LDK); };
+
+  const int nt = p.nM * p.nN, L = blockIdx.x;
+  const int tile = (nt % 8 == 0) ? (L % 8) * (nt / 8) + L / 8 : L;
+  const int tm = tile % p.nM, tn = tile / p.nM;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kb = blockIdx.y * p.kchunk;
+  const int ke = min(p.K, kb + p.kchunk);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+
+  u32x4_t ra[AVT], rw[WVT];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < AVT; ++i) {
+      const int v = tid + i * 256, r = v >> 3, c = (v & 7) * 8;
+      ra[i] = *(const u32x4_t*)(p.A + (long)min(m0 + r, p.M - 1) * p.lda + k0 + c);
+    }
+#pragma unroll
+    for (int i = 0; i < WVT; ++i) {
+      const int v = tid + i * 256, r = v >> 3, c = (v & 7) * 8, gn = min(n0 + r, p.N - 1);
+      rw[i] = *(const u32x4_t*)(p.W + (WF ? frag_idx(gn, k0 + c, p.ldw) : (long)gn * p.ldw + k0 + c));
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < AVT; ++i) {
+      const int v = tid + i * 256;
+      *(u32x4_t*)&sA(buf)[(v >> 3) * LDK + (v & 7) * 8] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < WVT; ++i) {
+      const int v = tid + i * 256;
+      *(u32x4_t*)&sW(buf)[(v >> 3) * LDK + (v & 7) * 8] = rw[i];
+    }
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (kb < ke) {
+    gload(kb);
+    sstore(0);
+  }
+  __syncthreads();
+  int it = 0;
+  for (int k0 = kb; k0 < ke; k0 += BK, ++it) {
+    const int buf = it & 1;
+    const bool more = k0 + BK < ke;
+    if (more) gload(k0 + BK);
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      const int koff = kk * 32 + (lane >> 4) * 8;
+      bf16x8_t wf[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        wf[j] = as_bf16x8(*(const u32x4_t*)&sW(buf)[(wn * (BN / 2) + j * 16 + (lane & 15)) * LDK + koff]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const bf16x8_t af = as_bf16x8(*(const u32x4_t*)&sA(buf)[(wm * (BM / 2) + i * 16 + (lane & 15)) * LDK + koff]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(af, wf[j], acc[i][j]);
+      }
+    }
+    if (more) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: accumulator element e of lane l is row (l / 16) * 4 + e, column l % 16 of its block
+  const int rbase = m0 + wm * (BM / 2) + (lane >> 4) * 4;
+  const int cbase = n0 + wn * (BN / 2);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = rbase + i * 16 + e;
+      if (m >= p.M) continue;
+      if (KIND == EPI_GEGLU) {
+#pragma unroll
+        for (int j = 0; j < TN; j += 2) {
+          if (cbase + j * 16 >= p.N) break;  // N % 32 == 0: a gate block in range has its up block
+          const int f = ((cbase + j * 16) >> 5) * 16 + (lane & 15);
+          epi_geglu(p.epi, m, f, acc[i][j][e], acc[i][j + 1][e]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = cbase + j * 16 + (lane & 15);
+          if (n >= p.N) continue;
+          if (KIND == EPI_PARTIAL) p.ws[((long)blockIdx.y * p.M + m) * p.N + n] = acc[i][j][e];
+          else epi_store_t<KIND>(p.epi, m, n, acc[i][j][e]);
+        }
+      }
+    }
+  }
+}
+
+template <int BN, bool WF>
+static hipError_t launch_wide(const GemmP& p, int splits, hipStream_t s) {
   GemmP q = p;
-  q.nM = (p.M + BM - 1) / BM;
+  q.nM = (p.M + 287) / 288;
   q.nN = (p.N + BN - 1) / BN;
   const int slices = p.K / 64;
   const int per = (slices + splits - 1) / splits;
@@ -398,23 +393,21 @@ static hipError_t launch_bf16(const GemmP& p, int splits, hipStream_t s) {
   const int used = (slices + per - 1) / per;  // == splits for counts from gemm_bf16_splits
   dim3 grid(q.nM * q.nN, used);
   const int kind = used > 1 ? EPI_PARTIAL : p.epi.kind;
-  const dim3 blk(64 * WM * WN);
-  if constexpr (WF) {  // expert weights: only the kinds of the expert layer
-    switch (kind) {
-      case EPI_STORE: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_STORE, true>), grid, blk, 0, s, q); break;
-      case EPI_QKV: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_QKV, true>), grid, blk, 0, s, q); break;
-      case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_GEGLU, true>), grid, blk, 0, s, q); break;
-      case EPI_PARTIAL: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_PARTIAL, true>), grid, blk, 0, s, q); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    switch (kind) {
-      case EPI_STORE: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_STORE, false>), grid, blk, 0, s, q); break;
-      case EPI_RESID: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_RESID, false>), grid, blk, 0, s, q); break;
-      case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_GEGLU, false>), grid, blk, 0, s, q); break;
-      case EPI_CACHE: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_CACHE, false>), grid, blk, 0, s, q); break;
-      default: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_PARTIAL, false>), grid, blk, 0, s, q); break;
-    }
+  const dim3 blk(256);
+  switch (kind) {
+    case EPI_STORE: hipLaunchKernelGGL((k_gemm_wide<BN, EPI_STORE, WF>), grid, blk, 0, s, q); break;
+    case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_wide<BN, EPI_GEGLU, WF>), grid, blk, 0, s, q); break;
+    case EPI_PARTIAL: hipLaunchKernelGGL((k_gemm_wide<BN, EPI_PARTIAL, WF>), grid, blk, 0, s, q); break;
+    case EPI_QKV:
+      if constexpr (WF) { hipLaunchKernelGGL((k_gemm_wide<BN, EPI_QKV, WF>), grid, blk, 0, s, q); break; }
+      return hipErrorInvalidValue;
+    case EPI_CACHE:
+      if constexpr (!WF) { hipLaunchKernelGGL((k_gemm_wide<BN, EPI_CACHE, WF>), grid, blk, 0, s, q); break; }
+      return hipErrorInvalidValue;
+    case EPI_RESID:
+      if constexpr (!WF) { hipLaunchKernelGGL((k_gemm_wide<BN, EPI_RESID, WF>), grid, blk, 0, s, q); break; }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -425,6 +418,17 @@ static hipError_t launch_bf16(const GemmP& p, int splits, hipStream_t s) {
     err = hipGetLastError();
   }
   return err;
+}
+
+// Split count that fills the chip for an M x N x K product on the tiles
+// gemm_bf16 picks: about two workgroups per CU, at least 4 K slices of 64 each.
+int gemm_bf16_auto_splits(int M, int N, int K) {
+  if (M <= 64) return 4;
+  const int tiles = (M + 287) / 288 * ((N + 127) / 128);
+  const int slices = K / 64;
+  int s = 1;
+  while (tiles * s < 256 && slices / (2 * s) >= 4 && 2 * s <= 16) s *= 2;
+  return s;
 }
 
 int gemm_bf16_splits(int K, int splits, int M) {
@@ -448,8 +452,8 @@ hipError_t gemm_bf16(const uint16_t* A, int lda, const uint16_t* W, int ldw, int
   GemmP p{A, lda, W, ldw, M, N, K, 0, 0, 0, epi, ws};
   if ((splits > 1 || epi.kind == EPI_PARTIAL) && !ws) return hipErrorInvalidValue;
   // Tile choice: skinny row counts (the action chunk) stream weights one wave
-  // per 16 or 32 columns; the prefix (hundreds of rows) takes 96 x 128 tiles,
-  // four waves of 96 x 32.
+  // per 16 or 32 columns; the prefix (hundreds of rows) takes 288 x 128 tiles,
+  // four waves of 144 x 64.
   if (M <= 64) {
     SkinnyP q{A, lda, W, ldw, M, N, K, 0, epi, ws};
     if (epi.kind == EPI_GEGLU) {
@@ -458,8 +462,8 @@ hipError_t gemm_bf16(const uint16_t* A, int lda, const uint16_t* W, int ldw, int
     }
     return launch_skinny<1>(q, splits, s);
   }
-  if (w_frag) return launch_bf16<96, 128, 1, 4, true>(p, splits, s);
-  return launch_bf16<96, 128, 1, 4, false>(p, splits, s);
+  if (w_frag) return launch_wide<128, true>(p, splits, s);
+  return launch_wide<128, false>(p, splits, s);
 }
 
 // ------------------------------------------------------------------ chunk rows, fragment layout

@@ -55,6 +55,8 @@ struct Epilogue {
 hipError_t gemm_bf16(const uint16_t* A, int lda, const uint16_t* W, int ldw, int M, int N, int K,
                      const Epilogue& epi, int splits, float* ws, hipStream_t s, int w_frag = 0);
 
+// A split count for gemm_bf16 that fills the chip at this shape (partials need splits x M x N floats).
+int gemm_bf16_auto_splits(int M, int N, int K);
 // Number of K splits gemm_bf16 actually uses for a request of `splits` at M rows.
 int gemm_bf16_splits(int K, int splits, int M);
 
@@ -129,6 +131,10 @@ hipError_t expert_embed(const float* X, int M, int d_a, const void* w_in, int w_
 hipError_t expert_head(const float* E, int M, int d_e, const float* gain, float eps,
                        const void* w_out, int w_f32, int d_a, const float* sched, int k, float* X,
                        hipStream_t s);
+// Read two byte ranges once (16-byte units, 64 workgroups) and drop the data, so a
+// later kernel finds them in the memory-side cache; sink: 64 words, written never
+// in practice.
+hipError_t prefetch(const void* p, size_t bytes, const void* p2, size_t bytes2, unsigned* sink, hipStream_t s);
 // Zero the last `tail` 16-bit elements of each of nblk blocks of `blk` elements
 // (the padding key rows of fragment-ordered K/V blocks); tail, blk % 8 == 0.
 hipError_t zero_tails(void* base, long nblk, long blk, int tail, hipStream_t s);

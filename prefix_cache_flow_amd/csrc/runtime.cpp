@@ -205,6 +205,9 @@ struct vla_model {
   float* sched_host = nullptr; // pinned staging
   int sched_cap = 0;
   hipStream_t cap_stream = nullptr;
+  // expert weights of all layers in one allocation, layer e at ew + e * ew_layer
+  char* ew = nullptr;
+  size_t ew_layer = 0;
   std::map<GraphKey, hipGraphExec_t> graphs;
   std::set<vla_kv_cache*> caches;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
@@ -440,10 +443,18 @@ static vla_status build_weights(vla_model* m, const vla_weights* w, hipStream_t 
     }
     temps.push_back(stage);
   }
-  // rows x cols assembled by `fill` (row-major) into a new buffer, fragment layout in bf16
+  // all expert projections in one allocation, layer by layer
+  auto rnd = [](int64_t b) { return (b + 255) / 256 * 256; };
+  const int64_t shapes[6][2] = {{qkve, c.d_e}, {c.d_e, qe}, {qe, c.d_e}, {c.d_e, qe}, {2 * (int64_t)c.F_e, c.d_e}, {c.d_e, c.F_e}};
+  m->ew_layer = 0;
+  for (auto& sh : shapes) m->ew_layer += rnd(sh[0] * sh[1] * (int64_t)es);
+  TRY(dev_alloc(m, (void**)&m->ew, m->ew_layer * c.L_e));
+  size_t ew_off = 0;
+  // rows x cols assembled by `fill` (row-major) into the next slot, fragment layout in bf16
   auto expert_weight = [&](void** dst, int64_t rows, int64_t cols, auto fill) -> vla_status {
-    vla_status r = dev_alloc(m, dst, rows * cols * es);
-    if (r != VLA_OK) return r;
+    *dst = m->ew + ew_off;
+    ew_off += rnd(rows * cols * (int64_t)es);
+    vla_status r = VLA_OK;
     if (m->f32) return fill(*dst);
     r = fill(stage);
     if (r != VLA_OK) return r;
@@ -584,11 +595,43 @@ struct WS {
   void* eattn;      // [erows][Hq_e hd_e]
   void* emlp;       // [erows][F_e]
   float* epart;     // split-K partials of the expert
+  unsigned* sink;   // 64 words for the prefetch kernel
   size_t total;
 };
 
-static const int kPrefixSplits = 4;
 static const int kExpertSplits = 4;
+
+// Split-K counts: the one place that fixes them for a GEMM and for the row
+// kernel (or reduction) that sums its partials.
+static int prefix_splits(int64_t M, int N, int K) {
+  return gemm_bf16_splits(K, gemm_bf16_auto_splits((int)M, N, K), (int)M);
+}
+static int expert_splits(int64_t M, int N, int K) {
+  return M <= 64 ? gemm_bf16_splits(K, kExpertSplits, (int)M) : prefix_splits(M, N, K);
+}
+// floats of split-K partials the prefix (rows tokens) and the expert (erows chunk rows) need
+static int64_t prefix_part_floats(const vla_model_config& c, int64_t rows) {
+  if (rows <= 0) return 0;
+  const int qw = c.Hq * c.hd, qkvw = (c.Hq + 2 * c.Hkv) * c.hd, ncache = c.L_e * 2 * c.Hkv_e * c.hd_e;
+  int64_t f = (int64_t)prefix_splits(rows, ncache, c.d_p) * ncache;
+  if (c.precision != VLA_W2A8_BF16) {
+    f = std::max<int64_t>(f, (int64_t)prefix_splits(rows, qkvw, c.d_p) * qkvw);
+    f = std::max<int64_t>(f, (int64_t)prefix_splits(rows, c.d_p, qw) * c.d_p);
+    f = std::max<int64_t>(f, (int64_t)prefix_splits(rows, c.d_p, c.F_p) * c.d_p);
+    f = std::max<int64_t>(f, (int64_t)prefix_splits(rows, 2 * c.F_p, c.d_p) * 2 * c.F_p);
+  }
+  return f * rows;
+}
+static int64_t expert_part_floats(const vla_model_config& c, int64_t erows) {
+  if (erows <= 0) return 0;
+  const int qe = c.Hq_e * c.hd_e, qkve = (c.Hq_e + 2 * c.Hkv_e) * c.hd_e;
+  int64_t f = (int64_t)expert_splits(erows, c.d_e, qe) * c.d_e;
+  f = std::max<int64_t>(f, (int64_t)expert_splits(erows, c.d_e, c.F_e) * c.d_e);
+  f = std::max<int64_t>(f, (int64_t)expert_splits(erows, qkve, c.d_e) * qkve);
+  f = std::max<int64_t>(f, (int64_t)expert_splits(erows, qe, c.d_e) * qe);
+  f = std::max<int64_t>(f, (int64_t)expert_splits(erows, 2 * c.F_e, c.d_e) * 2 * c.F_e);
+  return f * erows;
+}
 
 static WS plan(const vla_model* m, int64_t rows, int64_t erows, char* base) {
   const vla_model_config& c = m->cfg;
@@ -611,7 +654,7 @@ static WS plan(const vla_model* m, int64_t rows, int64_t erows, char* base) {
     w.qa = (int8_t*)take(rows * std::max<int64_t>(std::max<int64_t>(c.d_p, qw), c.F_p));
     w.alpha = (float*)take(rows * 4);
   }
-  w.part = (float*)take((size_t)kPrefixSplits * rows * c.d_p * 4);
+  w.part = (float*)take((size_t)prefix_part_floats(c, rows) * 4);
   const int64_t qe = (int64_t)c.Hq_e * c.hd_e, qkve = (int64_t)(c.Hq_e + 2 * c.Hkv_e) * c.hd_e;
   w.X = (float*)take(erows * c.d_a * 4);
   w.E = (float*)take(erows * c.d_e * 4);
@@ -626,9 +669,9 @@ static WS plan(const vla_model* m, int64_t rows, int64_t erows, char* base) {
   w.eq = take(erows * qe * es);
   w.eattn = take(frows * qe * es);
   w.emlp = take(frows * (int64_t)c.F_e * es);
-  // split partials: residual GEMMs [S][erows][d_e], other split GEMMs [S][erows][N]
-  const int64_t widest = std::max<int64_t>(std::max<int64_t>(qkve, 2 * (int64_t)c.F_e), c.d_e);
-  w.epart = (float*)take((size_t)kExpertSplits * erows * widest * 4);
+  // split partials [S][erows][N] of the expert GEMMs
+  w.epart = (float*)take((size_t)expert_part_floats(c, erows) * 4);
+  w.sink = (unsigned*)take(256);
   w.total = off;
   return w;
 }
@@ -798,7 +841,8 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
         const uint16_t* u = (const uint16_t*)w.u;
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_QKV, s);
-          K_TRY(gemm_bf16(u, c.d_p, (const uint16_t*)P.wqkv, c.d_p, M, qkvw, c.d_p, epi_store(w.qkv, qkvw, 0), 1, w.part, s), "qkv");
+          K_TRY(gemm_bf16(u, c.d_p, (const uint16_t*)P.wqkv, c.d_p, M, qkvw, c.d_p, epi_store(w.qkv, qkvw, 0),
+                          prefix_splits(M, qkvw, c.d_p), w.part, s), "qkv");
         }
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_ATTN, s);
@@ -808,20 +852,23 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
         pe.kind = EPI_PARTIAL;
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_O, s);
-          K_TRY(gemm_bf16((const uint16_t*)w.attn, qw, (const uint16_t*)P.wo, qw, M, c.d_p, qw, pe, kPrefixSplits, w.part, s), "o proj");
+          K_TRY(gemm_bf16((const uint16_t*)w.attn, qw, (const uint16_t*)P.wo, qw, M, c.d_p, qw, pe,
+                          prefix_splits(M, c.d_p, qw), w.part, s), "o proj");
         }
-        K_TRY(resid_norm(w.h, c.d_p, w.part, gemm_bf16_splits(qw, kPrefixSplits, M), M, c.d_p, P.w2, eps, w.u, 0, c.d_p, nullptr, nullptr, s), "norm");
+        K_TRY(resid_norm(w.h, c.d_p, w.part, prefix_splits(M, c.d_p, qw), M, c.d_p, P.w2, eps, w.u, 0, c.d_p, nullptr, nullptr, s), "norm");
         Epilogue g = epi_store(w.mlp, c.F_p, 0);
         g.kind = EPI_GEGLU;
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_GATEUP, s);
-          K_TRY(gemm_bf16(u, c.d_p, (const uint16_t*)P.wgu, c.d_p, M, 2 * c.F_p, c.d_p, g, 1, w.part, s), "gate/up");
+          K_TRY(gemm_bf16(u, c.d_p, (const uint16_t*)P.wgu, c.d_p, M, 2 * c.F_p, c.d_p, g, prefix_splits(M, 2 * c.F_p, c.d_p),
+                          w.part, s), "gate/up");
         }
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_DOWN, s);
-          K_TRY(gemm_bf16((const uint16_t*)w.mlp, c.F_p, (const uint16_t*)P.wd, c.F_p, M, c.d_p, c.F_p, pe, kPrefixSplits, w.part, s), "down");
+          K_TRY(gemm_bf16((const uint16_t*)w.mlp, c.F_p, (const uint16_t*)P.wd, c.F_p, M, c.d_p, c.F_p, pe,
+                          prefix_splits(M, c.d_p, c.F_p), w.part, s), "down");
         }
-        K_TRY(resid_norm(w.h, c.d_p, w.part, gemm_bf16_splits(c.F_p, kPrefixSplits, M), M, c.d_p, next_gain, eps, w.u, 0, c.d_p, nullptr, nullptr, s), "norm");
+        K_TRY(resid_norm(w.h, c.d_p, w.part, prefix_splits(M, c.d_p, c.F_p), M, c.d_p, next_gain, eps, w.u, 0, c.d_p, nullptr, nullptr, s), "norm");
       }
     }
   }
@@ -839,7 +886,8 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
   if (m->f32)
     K_TRY(gemm_f32((const float*)w.u, c.d_p, (const float*)m->wcache, c.d_p, M, ncache, c.d_p, ce, s), "cache");
   else
-    K_TRY(gemm_bf16((const uint16_t*)w.u, c.d_p, (const uint16_t*)m->wcache, c.d_p, M, ncache, c.d_p, ce, 1, w.part, s), "cache");
+    K_TRY(gemm_bf16((const uint16_t*)w.u, c.d_p, (const uint16_t*)m->wcache, c.d_p, M, ncache, c.d_p, ce,
+                    prefix_splits(M, ncache, c.d_p), w.part, s), "cache");
   return VLA_OK;
 }
 
@@ -947,7 +995,7 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
   ca.Nk = N;
   Epilogue pe;
   pe.kind = EPI_PARTIAL;
-  const int S_o = gemm_bf16_splits(qe, kExpertSplits, M), S_d = gemm_bf16_splits(c.F_e, kExpertSplits, M);
+  const int S_o = expert_splits(M, c.d_e, qe), S_d = expert_splits(M, c.d_e, c.F_e);
   for (int k = 0; k < steps; ++k) {
     K_TRY(expert_embed(w.X, M, c.d_a, m->w_in, f32, c.d_e, m->sched_dev, k, w.E, m->el[0].a1, eps, w.eu, f32, s, fr),
           "embed");
@@ -979,18 +1027,18 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
           if (fr) return gemm_chunk((const uint16_t*)A, (const uint16_t*)W, M, N, K, ep, splits, w.epart, s);
           return gemm_bf16((const uint16_t*)A, lda, (const uint16_t*)W, K, M, N, K, ep, splits, w.epart, s, 1);
         };
-        K_TRY(mm(u, c.d_e, L.wqkv, qkve, c.d_e, qkv_e, 1), "qkv_s");
+        K_TRY(mm(u, c.d_e, L.wqkv, qkve, c.d_e, qkv_e, fr ? 1 : expert_splits(M, qkve, c.d_e)), "qkv_s");
         K_TRY(attention_chunk(sa, s), "self attn");
         K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
         K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
-        K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, epi_store(w.eq, qe, 0), 1), "q_c");
+        K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, epi_store(w.eq, qe, 0), fr ? 1 : expert_splits(M, qe, c.d_e)), "q_c");
         K_TRY(attention_chunk(ca, s), "cross attn");
         K_TRY(mm(w.eattn, qe, L.woc, c.d_e, qe, pe, S_o), "o_c");
         K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
         Epilogue g = epi_store(w.emlp, c.F_e, 0);
         g.kind = EPI_GEGLU;
         g.out_frag = fr;
-        K_TRY(mm(u, c.d_e, L.wgu, 2 * c.F_e, c.d_e, g, 1), "gate/up");
+        K_TRY(mm(u, c.d_e, L.wgu, 2 * c.F_e, c.d_e, g, fr ? 1 : expert_splits(M, 2 * c.F_e, c.d_e)), "gate/up");
         K_TRY(mm(w.emlp, c.F_e, L.wd, c.d_e, c.F_e, pe, S_d), "down");
         K_TRY(resid_norm(w.E, c.d_e, w.epart, S_d, M, c.d_e, e + 1 < c.L_e ? m->el[e + 1].a1 : m->w_ef, eps,
                          e + 1 < c.L_e ? w.eu : nullptr, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
