@@ -242,6 +242,11 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float obuf[4][16][LDO];
 
   const int G = a.Hq / a.Hkv, R = G * a.Nq;
+  const int nrb = (R + 15) / 16;
+  if ((int)blockIdx.x >= nrb) {  // extra workgroups (first batch and group only): warm the next weights
+    if (blockIdx.y == 0 && blockIdx.z == 0) prefetch_share(a.pf, blockIdx.x - nrb, gridDim.x - nrb);
+    return;
+  }
   const int g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -373,8 +378,9 @@ hipError_t attention_chunk(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.Nq <= 0 || a.Nk <= 0) return hipSuccess;
   if (a.Hq % a.Hkv || a.o_f32) return hipErrorInvalidValue;
   if (a.o_frag && a.B * a.Nq > 64) return hipErrorInvalidValue;
+  if (a.pf.blocks < 0 || a.pf.blocks > 1024 || (a.pf.blocks && !a.pf.sink)) return hipErrorInvalidValue;
   const int R = a.Hq / a.Hkv * a.Nq;
-  dim3 grid((R + 15) / 16, a.Hkv, a.B);
+  dim3 grid((R + 15) / 16 + a.pf.blocks, a.Hkv, a.B);
   switch (a.hd) {
     case 64: hipLaunchKernelGGL(k_attn_chunk<64>, grid, dim3(256), 0, s, a); break;
     case 128: hipLaunchKernelGGL(k_attn_chunk<128>, grid, dim3(256), 0, s, a); break;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace vla {
 
 typedef uint16_t bf16_t;  // bfloat16 bit pattern in memory
@@ -129,6 +131,28 @@ __host__ __device__ __forceinline__ long vfrag_idx(int t, int d, int D) {
   const int kin = t & 31;
   const long blk = (long)(t >> 5) * (D >> 4) + (d >> 4);
   return ((blk * 64 + (d & 15) + 16 * ((kin & 15) >> 2)) << 3) + (kin >> 4) * 4 + (kin & 3);
+}
+
+// Workgroup `blk` of `nblk` reads its share of the ranges, 16 loads of 16 bytes
+// per thread in flight, and folds them so the loads are kept.
+__device__ __forceinline__ void prefetch_share(const Prefetch& f, int blk, int nblk) {
+  constexpr int U = 16;
+  const long n = (long)(f.bytes >> 4), n2 = (long)(f.bytes2 >> 4), tot = n + n2;
+  const u32x4_t* p = (const u32x4_t*)f.p;
+  const u32x4_t* p2 = (const u32x4_t*)f.p2;
+  const long stride = (long)nblk * blockDim.x;
+  unsigned x = 0;
+  for (long base = (long)blk * blockDim.x + threadIdx.x; base < tot; base += stride * U) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long i = min(base + u * stride, tot - 1);
+      v[u] = *(i < n ? p + i : p2 + (i - n));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u][0] ^ v[u][3];
+  }
+  if (x == 0x9E3779B9u) f.sink[blk & 63] = x;
 }
 
 // acc row index of element i for lane l in a 32x32 MFMA block

@@ -24,9 +24,13 @@ __device__ __forceinline__ float ld_w(const void* w, long i) {
 template <bool WF32>
 __global__ __launch_bounds__(256) void k_embed(const float* X, int d_a, const void* w_in, int d_e, const float* sched,
                                                int k, float* E, const float* gain, float eps, void* u, int u_f32,
-                                               int u_frag) {
+                                               int u_frag, int M, Prefetch pf) {
   __shared__ float xs[256];
   __shared__ float es[4096];
+  if ((int)blockIdx.x >= M) {  // extra workgroups: warm the next kernel's weights
+    prefetch_share(pf, blockIdx.x - M, gridDim.x - M);
+    return;
+  }
   __shared__ float red[4];
   const int m = blockIdx.x;
   if (threadIdx.x < d_a) xs[threadIdx.x] = X[(long)m * d_a + threadIdx.x];
@@ -61,16 +65,19 @@ __global__ __launch_bounds__(256) void k_embed(const float* X, int d_a, const vo
 }
 
 hipError_t expert_embed(const float* X, int M, int d_a, const void* w_in, int w_f32, int d_e, const float* sched,
-                        int k, float* E, const float* gain, float eps, void* u, int u_f32, hipStream_t s, int u_frag) {
+                        int k, float* E, const float* gain, float eps, void* u, int u_f32, hipStream_t s, int u_frag,
+                        const Prefetch* prefetch) {
   if (M <= 0) return hipSuccess;
   if (d_a > 256 || d_e > 4096) return hipErrorInvalidValue;
   if (u_frag && (u_f32 || d_e % 32 || M > 64)) return hipErrorInvalidValue;
+  const Prefetch pf = prefetch ? *prefetch : Prefetch{};
+  if (pf.blocks < 0 || pf.blocks > 1024 || (pf.blocks && !pf.sink)) return hipErrorInvalidValue;
   if (w_f32)
-    hipLaunchKernelGGL(k_embed<true>, dim3(M), dim3(256), 0, s, X, d_a, w_in, d_e, sched, k, E, gain, eps, u, u_f32,
-                       u_frag);
+    hipLaunchKernelGGL(k_embed<true>, dim3(M + pf.blocks), dim3(256), 0, s, X, d_a, w_in, d_e, sched, k, E, gain, eps,
+                       u, u_f32, u_frag, M, pf);
   else
-    hipLaunchKernelGGL(k_embed<false>, dim3(M), dim3(256), 0, s, X, d_a, w_in, d_e, sched, k, E, gain, eps, u, u_f32,
-                       u_frag);
+    hipLaunchKernelGGL(k_embed<false>, dim3(M + pf.blocks), dim3(256), 0, s, X, d_a, w_in, d_e, sched, k, E, gain,
+                       eps, u, u_f32, u_frag, M, pf);
   return hipGetLastError();
 }
 
@@ -162,34 +169,6 @@ hipError_t f32_to_bf16(const float* src, uint16_t* dst, long n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int blocks = (int)std::min<long>((n + 255) / 256, 4096);
   hipLaunchKernelGGL(k_f32_to_bf16, dim3(blocks), dim3(256), 0, s, src, dst, n);
-  return hipGetLastError();
-}
-
-// Read [p, p + n) then [p2, p2 + n2) (16-byte units) once and drop the data: it
-// warms the memory-side cache for a kernel that reads the same bytes soon.  The
-// fold into `sink` (written only for an impossible value) keeps the loads alive.
-__global__ __launch_bounds__(256) void k_prefetch(const u32x4_t* p, long n, const u32x4_t* p2, long n2, unsigned* sink) {
-  constexpr int U = 8;
-  const long stride = (long)gridDim.x * 256, tot = n + n2;
-  unsigned x = 0;
-  for (long base = blockIdx.x * 256L + threadIdx.x; base < tot; base += stride * U) {
-    u32x4_t v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const long i = min(base + u * stride, tot - 1);
-      v[u] = *(i < n ? p + i : p2 + (i - n));
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) x ^= v[u][0] ^ v[u][3];
-  }
-  if (x == 0x9E3779B9u) sink[blockIdx.x & 63] = x;
-}
-
-hipError_t prefetch(const void* p, size_t bytes, const void* p2, size_t bytes2, unsigned* sink, hipStream_t s) {
-  const long n = (long)(bytes / 16), n2 = p2 ? (long)(bytes2 / 16) : 0;
-  if (n + n2 <= 0) return hipSuccess;
-  if (!p && n) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_prefetch, dim3(64), dim3(256), 0, s, (const u32x4_t*)p, n, (const u32x4_t*)p2, n2, sink);
   return hipGetLastError();
 }
 

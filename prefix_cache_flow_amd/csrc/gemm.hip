@@ -335,19 +335,29 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmP p) {
     const int buf = it & 1;
     const bool more = k0 + BK < ke;
     if (more) gload(k0 + BK);
+    // Fragments are read two MFMA groups ahead, and scheduling barriers keep
+    // each read issued before the group it runs under: the LDS latency then
+    // overlaps MFMAs instead of stalling the single wave per SIMD.
+    const uint16_t* aBase = sA(buf) + (wm * (BM / 2) + (lane & 15)) * LDK + (lane >> 4) * 8;
+    const uint16_t* wBase = sW(buf) + (wn * (BN / 2) + (lane & 15)) * LDK + (lane >> 4) * 8;
+    constexpr int KS = BK / 32, NG = KS * TM;  // MFMA groups per slice: one activation fragment each
+    auto lda_frag = [&](int g) {
+      return as_bf16x8(*(const u32x4_t*)(aBase + (g % TM) * 16 * LDK + (g / TM) * 32));
+    };
+    bf16x8_t wf[KS][TN], af[NG];
 #pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      const int koff = kk * 32 + (lane >> 4) * 8;
-      bf16x8_t wf[TN];
+    for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        wf[j] = as_bf16x8(*(const u32x4_t*)&sW(buf)[(wn * (BN / 2) + j * 16 + (lane & 15)) * LDK + koff]);
+      for (int j = 0; j < TN; ++j) wf[kk][j] = as_bf16x8(*(const u32x4_t*)(wBase + j * 16 * LDK + kk * 32));
+    af[0] = lda_frag(0);
+    af[1] = lda_frag(1);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const bf16x8_t af = as_bf16x8(*(const u32x4_t*)&sA(buf)[(wm * (BM / 2) + i * 16 + (lane & 15)) * LDK + koff]);
+    for (int gi = 0; gi < NG; ++gi) {
+      if (gi + 2 < NG) af[gi + 2] = lda_frag(gi + 2);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(af, wf[j], acc[i][j]);
-      }
+      for (int j = 0; j < TN; ++j) acc[gi % TM][j] = mfma16x16x32(af[gi], wf[gi / TM][j], acc[gi % TM][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (more) sstore(buf ^ 1);
     __syncthreads();

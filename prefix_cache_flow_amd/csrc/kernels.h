@@ -7,6 +7,18 @@
 
 namespace vla {
 
+// Two byte ranges that extra workgroups of a short kernel read once and drop,
+// so that the next kernel (which streams them) finds them in the memory-side
+// cache instead of waiting on HBM.  `blocks` workgroups are added to the grid.
+struct Prefetch {
+  const void* p = nullptr;
+  size_t bytes = 0;
+  const void* p2 = nullptr;
+  size_t bytes2 = 0;
+  unsigned* sink = nullptr;  // 64 words, written only for an impossible value
+  int blocks = 0;
+};
+
 // ------------------------------------------------------------------ epilogues
 // What a GEMM does with its fp32 result v at (m, n).
 enum EpiKind {
@@ -95,9 +107,11 @@ hipError_t ternary_repack(const uint8_t* canon, int N, int K, uint32_t* out, int
 // and u is written as bf16 / fp32 (u_out), or quantized per Eq. 4 to int8 codes
 // (q_out) with its scale (alpha_out).  Any of the outputs may be null.
 // With u_frag the bf16 u goes out in the fragment layout (K = N) instead of rows.
+// `prefetch` (nullable) adds workgroups that read the next kernel's weights once.
 hipError_t resid_norm(float* h, int ldh, const float* part, int nsplit, int M, int N,
                       const float* gain, float eps, void* u_out, int u_f32, int ldu,
-                      int8_t* q_out, float* alpha_out, hipStream_t s, int u_frag = 0);
+                      int8_t* q_out, float* alpha_out, hipStream_t s, int u_frag = 0,
+                      const Prefetch* prefetch = nullptr);
 
 // Eq. 4 per-row quantization of fp32 rows (x: [M][ldx], K valid columns).
 hipError_t quantize_rows(const float* x, int ldx, int M, int K, int8_t* a, float* alpha, hipStream_t s);
@@ -111,6 +125,7 @@ struct AttnArgs {
   int B, Nq, Nk, Hq, Hkv, hd;
   int o_f32;                              // 1: fp32 output, 0: bf16
   int o_frag;                             // bf16 output in fragment layout: row b * Nq + q, K = Hq * hd
+  Prefetch pf;                            // attention_chunk: extra workgroups warming the next weights
 };
 // softmax(Q K^T / sqrt(hd)) V per head, no mask; bf16 inputs on MFMA (hd in 64..256)
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s);
@@ -126,15 +141,11 @@ hipError_t attention_f32(const AttnArgs& a, hipStream_t s);
 // E[m] = X[m] W_in^T + phi(tau_k) for the chunk rows, then u = RMS(E[m]; gain).
 hipError_t expert_embed(const float* X, int M, int d_a, const void* w_in, int w_f32, int d_e,
                         const float* sched, int k, float* E, const float* gain, float eps,
-                        void* u, int u_f32, hipStream_t s, int u_frag = 0);
+                        void* u, int u_f32, hipStream_t s, int u_frag = 0, const Prefetch* prefetch = nullptr);
 // v = RMS(E[m]; gain) W_out^T; X[m] += (tau_{k+1} - tau_k) v
 hipError_t expert_head(const float* E, int M, int d_e, const float* gain, float eps,
                        const void* w_out, int w_f32, int d_a, const float* sched, int k, float* X,
                        hipStream_t s);
-// Read two byte ranges once (16-byte units, 64 workgroups) and drop the data, so a
-// later kernel finds them in the memory-side cache; sink: 64 words, written never
-// in practice.
-hipError_t prefetch(const void* p, size_t bytes, const void* p2, size_t bytes2, unsigned* sink, hipStream_t s);
 // Zero the last `tail` 16-bit elements of each of nblk blocks of `blk` elements
 // (the padding key rows of fragment-ordered K/V blocks); tail, blk % 8 == 0.
 hipError_t zero_tails(void* base, long nblk, long blk, int tail, hipStream_t s);

@@ -40,9 +40,13 @@ __device__ __forceinline__ void quantize_store(const float* x, int per, int N, i
 template <int PER, int NS>
 __global__ __launch_bounds__(256) void k_resid_norm(float* h, int ldh, const float* part, int nsplit, int M, int N,
                                                     const float* gain, float eps, void* u, int u_f32, int ldu,
-                                                    int8_t* q, float* alpha, int u_frag) {
+                                                    int8_t* q, float* alpha, int u_frag, Prefetch pf) {
   __shared__ float red[4];
   const int m = blockIdx.x;
+  if (m >= M) {  // extra workgroups: warm the next kernel's weights
+    prefetch_share(pf, m - M, gridDim.x - M);
+    return;
+  }
   float x[PER];
   float pv[NS > 0 ? NS : 1][PER];
   float ss = 0.f;
@@ -92,10 +96,10 @@ __global__ __launch_bounds__(256) void k_resid_norm(float* h, int ldh, const flo
 template <int PER>
 static void launch_rn(int nsplit, hipStream_t s, float* h, int ldh, const float* part, int M, int N,
                       const float* gain, float eps, void* u_out, int u_f32, int ldu, int8_t* q_out, float* alpha_out,
-                      int u_frag) {
-#define VLA_RN(NS)                                                                                             \
-  hipLaunchKernelGGL((k_resid_norm<PER, NS>), dim3(M), dim3(256), 0, s, h, ldh, part, nsplit, M, N, gain, eps, \
-                     u_out, u_f32, ldu, q_out, alpha_out, u_frag)
+                      int u_frag, const Prefetch& pf) {
+#define VLA_RN(NS)                                                                                                  \
+  hipLaunchKernelGGL((k_resid_norm<PER, NS>), dim3(M + pf.blocks), dim3(256), 0, s, h, ldh, part, nsplit, M, N, gain, \
+                     eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf)
   if (nsplit <= 0) VLA_RN(0);
   else if (nsplit <= 1) VLA_RN(1);
   else if (nsplit <= 4) VLA_RN(4);
@@ -105,17 +109,20 @@ static void launch_rn(int nsplit, hipStream_t s, float* h, int ldh, const float*
 }
 
 hipError_t resid_norm(float* h, int ldh, const float* part, int nsplit, int M, int N, const float* gain, float eps,
-                      void* u_out, int u_f32, int ldu, int8_t* q_out, float* alpha_out, hipStream_t s, int u_frag) {
+                      void* u_out, int u_f32, int ldu, int8_t* q_out, float* alpha_out, hipStream_t s, int u_frag,
+                      const Prefetch* prefetch) {
+  const Prefetch pf = prefetch ? *prefetch : Prefetch{};
+  if (pf.blocks < 0 || pf.blocks > 1024 || (pf.blocks && !pf.sink)) return hipErrorInvalidValue;
   if (u_frag && (u_f32 || N % 32 || M > 64)) return hipErrorInvalidValue;
   if (M <= 0) return hipSuccess;
   if (nsplit > 16) return hipErrorInvalidValue;
   const int per = (N + 255) / 256;
-  if (per <= 1) launch_rn<1>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag);
-  else if (per <= 2) launch_rn<2>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag);
-  else if (per <= 4) launch_rn<4>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag);
-  else if (per <= 8) launch_rn<8>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag);
-  else if (per <= 12) launch_rn<12>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag);
-  else if (per <= 16) launch_rn<16>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag);
+  if (per <= 1) launch_rn<1>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf);
+  else if (per <= 2) launch_rn<2>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf);
+  else if (per <= 4) launch_rn<4>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf);
+  else if (per <= 8) launch_rn<8>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf);
+  else if (per <= 12) launch_rn<12>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf);
+  else if (per <= 16) launch_rn<16>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -996,8 +996,24 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
   Epilogue pe;
   pe.kind = EPI_PARTIAL;
   const int S_o = expert_splits(M, c.d_e, qe), S_d = expert_splits(M, c.d_e, c.F_e);
+  // Each short kernel of the chain (embed, norms, attention) gets extra
+  // workgroups that read the weights of the GEMM after it once, so that GEMM
+  // finds them in the memory-side cache: its weight loads then cost a cache hit
+  // instead of an HBM round trip, while the short kernel's own work hides the
+  // read.  Only for the fragment path (batch-1 sized chunks).
+  const size_t b_qkv = (size_t)qkve * c.d_e * es, b_o = (size_t)c.d_e * qe * es, b_q = (size_t)qe * c.d_e * es;
+  const size_t b_gu = (size_t)2 * c.F_e * c.d_e * es, b_d = (size_t)c.d_e * c.F_e * es;
+  const size_t layer_kv = (size_t)layer_stride * es;
+  auto pfr = [&](const void* p, size_t bytes, const void* p2, size_t bytes2, int blocks) {
+    Prefetch f;
+    if (!fr) return f;
+    f.p = p; f.bytes = bytes; f.p2 = p2; f.bytes2 = p2 ? bytes2 : 0; f.sink = w.sink; f.blocks = blocks;
+    return f;
+  };
   for (int k = 0; k < steps; ++k) {
-    K_TRY(expert_embed(w.X, M, c.d_a, m->w_in, f32, c.d_e, m->sched_dev, k, w.E, m->el[0].a1, eps, w.eu, f32, s, fr),
+    const Prefetch pf_embed = pfr(m->el[0].wqkv, b_qkv, nullptr, 0, 64);
+    K_TRY(expert_embed(w.X, M, c.d_a, m->w_in, f32, c.d_e, m->sched_dev, k, w.E, m->el[0].a1, eps, w.eu, f32, s, fr,
+                       &pf_embed),
           "embed");
     for (int e = 0; e < c.L_e; ++e) {
       const ExpertLayer& L = m->el[e];
@@ -1028,20 +1044,27 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
           return gemm_bf16((const uint16_t*)A, lda, (const uint16_t*)W, K, M, N, K, ep, splits, w.epart, s, 1);
         };
         K_TRY(mm(u, c.d_e, L.wqkv, qkve, c.d_e, qkv_e, fr ? 1 : expert_splits(M, qkve, c.d_e)), "qkv_s");
+        sa.pf = pfr(L.wos, b_o, nullptr, 0, 192);
         K_TRY(attention_chunk(sa, s), "self attn");
         K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
-        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
+        const Prefetch pf_qc = pfr(L.wqc, b_q, B == 1 ? ca.k : nullptr, layer_kv, 192);
+        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_qc),
+              "norm");
         K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, epi_store(w.eq, qe, 0), fr ? 1 : expert_splits(M, qe, c.d_e)), "q_c");
+        ca.pf = pfr(L.woc, b_o, L.wd, b_d, 192);
         K_TRY(attention_chunk(ca, s), "cross attn");
         K_TRY(mm(w.eattn, qe, L.woc, c.d_e, qe, pe, S_o), "o_c");
-        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
+        const Prefetch pf_gu = pfr(L.wgu, b_gu, nullptr, 0, 192);
+        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_gu),
+              "norm");
         Epilogue g = epi_store(w.emlp, c.F_e, 0);
         g.kind = EPI_GEGLU;
         g.out_frag = fr;
         K_TRY(mm(u, c.d_e, L.wgu, 2 * c.F_e, c.d_e, g, fr ? 1 : expert_splits(M, 2 * c.F_e, c.d_e)), "gate/up");
         K_TRY(mm(w.emlp, c.F_e, L.wd, c.d_e, c.F_e, pe, S_d), "down");
+        const Prefetch pf_next = e + 1 < c.L_e ? pfr(m->el[e + 1].wqkv, b_qkv, nullptr, 0, 192) : Prefetch{};
         K_TRY(resid_norm(w.E, c.d_e, w.epart, S_d, M, c.d_e, e + 1 < c.L_e ? m->el[e + 1].a1 : m->w_ef, eps,
-                         e + 1 < c.L_e ? w.eu : nullptr, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
+                         e + 1 < c.L_e ? w.eu : nullptr, 0, c.d_e, nullptr, nullptr, s, fr, &pf_next), "norm");
       }
     }
     K_TRY(expert_head(w.E, M, c.d_e, m->w_ef, eps, m->w_out, f32, c.d_a, m->sched_dev, k, w.X, s), "head");
