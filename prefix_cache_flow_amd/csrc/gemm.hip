@@ -2,7 +2,7 @@
 // W [N, K] weights (the [out, in] layout of every linear layer).
 //
 // gemm_bf16: bf16 operands, fp32 accumulation on the bf16 MFMA of gfx950.
-//   More than 64 rows: 288 x 128 workgroup tiles (k_gemm_wide), 64-wide K slices
+//   More than 64 rows: 288 x 128 workgroup tiles (k_gemm_ws), 64-wide K slices
 //   staged through LDS with one register-prefetched slice ahead.  Rows of LDS are
 //   padded by 16 bytes so the 16-byte fragment reads of 16 consecutive rows hit
 //   distinct banks.  Output tiles are numbered XCD-major so tiles that share a
@@ -264,22 +264,29 @@ static hipError_t launch_skinny(const SkinnyP& p0, int splits, hipStream_t s) {
 
 // ------------------------------------------------------------------ wide tiles (prefix)
 // Many rows (the prefix: hundreds of tokens).  A workgroup owns a 288 x BN
-// output tile; four waves in a 2 x 2 arrangement each hold 144 x BN/2 of it as
-// 9 x BN/32 accumulators of the 16x16x32 MFMA.  Per 32-wide k step a wave reads
-// 9 + BN/32 fragments from LDS for 9 * BN/32 MFMAs, and per 64-wide K slice the
-// workgroup fetches (288 + BN) x 64 bf16 from global memory: both stay below the
-// LDS and L1 rates that the MFMA rate needs, which smaller tiles (fewer MFMAs per
-// byte) do not.  K slices are double-buffered in LDS with one slice prefetched
-// in registers; rows past M and columns past N are clamped on load and never
-// stored.  Epilogues are applied straight from the accumulators: with BN/2 a
-// multiple of 32, the gate and up blocks of the GeGLU interleave sit in the same
-// lane.
+// output tile and has 8 waves.  Four compute waves in a 2 x 2 arrangement each
+// hold 144 x BN/2 of the tile as 9 x BN/32 accumulators of the 16x16x32 MFMA,
+// reading their fragments from LDS two MFMA groups ahead under scheduling
+// barriers.  Four loader waves fill LDS: two fetch the activation slice one
+// 64-wide K slice ahead, two fetch the weight slices four slices ahead in four
+// register sets.  Each wave has its own memory counter, so waiting for one
+// slice never waits for the weight slices queued behind it, and enough weight
+// bytes are in flight per CU to cover HBM latency.  One barrier per slice hands
+// the two LDS buffers between loaders and compute waves; the slice loop runs a
+// multiple of 4 times (the weight register sets rotate) and slices past the end
+// are fetched clamped and never computed.  LDS rows are 64 bf16 (128 bytes) with
+// the 16-byte chunk index XOR-ed by (row / 2) % 8, so fragment reads and loader
+// stores hit distinct banks.  Rows past M and columns past N are clamped on
+// load and never stored.  Epilogues run straight from the accumulators.
 template <int BN, int KIND, bool WF>
-__global__ __launch_bounds__(256) void k_gemm_wide(GemmP p) {
-  constexpr int BM = 288, BK = 64, LDK = BK + 8;
-  constexpr int TM = BM / 2 / 16, TN = BN / 2 / 16;
-  constexpr int AVT = BM * BK / 8 / 256, WVT = BN * BK / 8 / 256;  // 16-byte vectors per thread and slice
-  static_assert(AVT * 256 * 8 == BM * BK && WVT * 256 * 8 == BN * BK, "tile shape");
+__global__ __launch_bounds__(512) void k_gemm_ws(GemmP p) {
+  constexpr int BM = 288, BK = 64, LDK = BK;
+  constexpr int TM = BM / 2 / 16, TN = BN / 2 / 16;  // 16x16 blocks per compute wave (2 x 2 waves)
+  // 16-byte vectors per loader thread and slice: two activation and two weight loader waves
+  constexpr int AVL = BM * BK / 8 / 128, WVL = BN * BK / 8 / 128;
+  // element offset of 16-byte chunk c of LDS row r (swizzled)
+  auto sw = [](int r, int c) { return r * LDK + ((c ^ ((r >> 1) & 7)) << 3); };
+  static_assert(AVL * 128 * 8 == BM * BK && WVL * 128 * 8 == BN * BK, "tile shape");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDK];
   auto sA = [&](int b) { return smem + b * (BM * LDK); };
   auto sW = [&](int b) { return smem + 2 * BM * LDK + b * (BN * LDK); };
@@ -290,80 +297,127 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmP p) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int kb = blockIdx.y * p.kchunk;
   const int ke = min(p.K, kb + p.kchunk);
+  const int nsl = max(0, (ke - kb) / BK);
+  const int nsl4 = (nsl + 3) & ~3;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  auto slice_k = [&](int sl) { return kb + min(sl, max(nsl - 1, 0)) * BK; };
+
+  if (wid >= 6) {  // ---------------- weight loaders: four slices in flight
+    const int lt = tid - 384;
+    struct RW { u32x4_t v[WVL]; };
+    RW r0, r1, r2, r3;
+    auto load = [&](RW& R, int sl) {
+      const int k0 = slice_k(sl);
+#pragma unroll
+      for (int i = 0; i < WVL; ++i) {
+        const int v = lt + i * 128, r = v >> 3, c = (v & 7) * 8, gn = min(n0 + r, p.N - 1);
+        // 32-bit element offsets (the launcher checks that both operands fit): base + offset addressing
+        const uint32_t off = WF ? (uint32_t)frag_idx(gn, k0 + c, p.ldw) : (uint32_t)gn * (uint32_t)p.ldw + k0 + c;
+        R.v[i] = *(const u32x4_t*)(p.W + off);
+      }
+    };
+    auto store = [&](const RW& R, int buf) {
+#pragma unroll
+      for (int i = 0; i < WVL; ++i) {
+        const int v = lt + i * 128;
+        *(u32x4_t*)&sW(buf)[sw(v >> 3, v & 7)] = R.v[i];
+      }
+    };
+    load(r0, 0);
+    load(r1, 1);
+    load(r2, 2);
+    load(r3, 3);
+    store(r0, 0);
+    load(r0, 4);
+    __syncthreads();
+    // entering iteration s: slices s+1 .. s+4 are in the sets (s+1)%4 .. (s+4)%4
+    for (int s = 0; s < nsl4; s += 4) {
+      store(r1, 1);
+      load(r1, s + 5);
+      __syncthreads();
+      store(r2, 0);
+      load(r2, s + 6);
+      __syncthreads();
+      store(r3, 1);
+      load(r3, s + 7);
+      __syncthreads();
+      store(r0, 0);
+      load(r0, s + 8);
+      __syncthreads();
+    }
+    return;
+  }
+  if (wid >= 4) {  // ---------------- activation loaders: one slice ahead
+    const int lt = tid - 256;
+    u32x4_t ra[AVL];
+    auto load = [&](int sl) {
+      const int k0 = slice_k(sl);
+#pragma unroll
+      for (int i = 0; i < AVL; ++i) {
+        const int v = lt + i * 128, r = v >> 3, c = (v & 7) * 8;
+        ra[i] = *(const u32x4_t*)(p.A + ((uint32_t)min(m0 + r, p.M - 1) * (uint32_t)p.lda + k0 + c));
+      }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < AVL; ++i) {
+        const int v = lt + i * 128;
+        *(u32x4_t*)&sA(buf)[sw(v >> 3, v & 7)] = ra[i];
+      }
+    };
+    load(0);
+    store(0);
+    load(1);
+    __syncthreads();
+    for (int s = 0; s < nsl4; ++s) {
+      store((s + 1) & 1);
+      load(s + 2);
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ---------------- compute waves: 2 x 2 waves of 144 x BN/2 on the 16x16x32 MFMA
   const int wm = wid >> 1, wn = wid & 1;
-
-  u32x4_t ra[AVT], rw[WVT];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < AVT; ++i) {
-      const int v = tid + i * 256, r = v >> 3, c = (v & 7) * 8;
-      ra[i] = *(const u32x4_t*)(p.A + (long)min(m0 + r, p.M - 1) * p.lda + k0 + c);
-    }
-#pragma unroll
-    for (int i = 0; i < WVT; ++i) {
-      const int v = tid + i * 256, r = v >> 3, c = (v & 7) * 8, gn = min(n0 + r, p.N - 1);
-      rw[i] = *(const u32x4_t*)(p.W + (WF ? frag_idx(gn, k0 + c, p.ldw) : (long)gn * p.ldw + k0 + c));
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < AVT; ++i) {
-      const int v = tid + i * 256;
-      *(u32x4_t*)&sA(buf)[(v >> 3) * LDK + (v & 7) * 8] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < WVT; ++i) {
-      const int v = tid + i * 256;
-      *(u32x4_t*)&sW(buf)[(v >> 3) * LDK + (v & 7) * 8] = rw[i];
-    }
-  };
-
   f32x4_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  if (kb < ke) {
-    gload(kb);
-    sstore(0);
-  }
   __syncthreads();
-  int it = 0;
-  for (int k0 = kb; k0 < ke; k0 += BK, ++it) {
-    const int buf = it & 1;
-    const bool more = k0 + BK < ke;
-    if (more) gload(k0 + BK);
-    // Fragments are read two MFMA groups ahead, and scheduling barriers keep
-    // each read issued before the group it runs under: the LDS latency then
-    // overlaps MFMAs instead of stalling the single wave per SIMD.
-    const uint16_t* aBase = sA(buf) + (wm * (BM / 2) + (lane & 15)) * LDK + (lane >> 4) * 8;
-    const uint16_t* wBase = sW(buf) + (wn * (BN / 2) + (lane & 15)) * LDK + (lane >> 4) * 8;
-    constexpr int KS = BK / 32, NG = KS * TM;  // MFMA groups per slice: one activation fragment each
-    auto lda_frag = [&](int g) {
-      return as_bf16x8(*(const u32x4_t*)(aBase + (g % TM) * 16 * LDK + (g / TM) * 32));
-    };
-    bf16x8_t wf[KS][TN], af[NG];
+  for (int s = 0; s < nsl4; ++s) {
+    if (s < nsl) {
+      const int buf = s & 1;
+      // fragment rows start at multiples of 16, so the chunk swizzle of a lane's row is ((lane & 15) >> 1)
+      const int xr = (lane & 15) >> 1;
+      const uint16_t* aBase = sA(buf) + (wm * (BM / 2) + (lane & 15)) * LDK;
+      const uint16_t* wBase = sW(buf) + (wn * (BN / 2) + (lane & 15)) * LDK;
+      constexpr int KS = BK / 32, NG = KS * TM;  // MFMA groups per slice: one activation fragment each
+      auto chunk = [&](int kk) { return ((kk * 4 + (lane >> 4)) ^ xr) << 3; };
+      auto lda_frag = [&](int g) {
+        return as_bf16x8(*(const u32x4_t*)(aBase + (g % TM) * 16 * LDK + chunk(g / TM)));
+      };
+      bf16x8_t wf[KS][TN], af[NG];
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
+      for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) wf[kk][j] = as_bf16x8(*(const u32x4_t*)(wBase + j * 16 * LDK + kk * 32));
-    af[0] = lda_frag(0);
-    af[1] = lda_frag(1);
+        for (int j = 0; j < TN; ++j) wf[kk][j] = as_bf16x8(*(const u32x4_t*)(wBase + j * 16 * LDK + chunk(kk)));
+      af[0] = lda_frag(0);
+      af[1] = lda_frag(1);
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      if (gi + 2 < NG) af[gi + 2] = lda_frag(gi + 2);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int gi = 0; gi < NG; ++gi) {
+        if (gi + 2 < NG) af[gi + 2] = lda_frag(gi + 2);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[gi % TM][j] = mfma16x16x32(af[gi], wf[gi / TM][j], acc[gi % TM][j]);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < TN; ++j) acc[gi % TM][j] = mfma16x16x32(af[gi], wf[gi / TM][j], acc[gi % TM][j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    if (more) sstore(buf ^ 1);
     __syncthreads();
   }
 
-  // epilogue: accumulator element e of lane l is row (l / 16) * 4 + e, column l % 16 of its block
+  // epilogue: accumulator element e of lane l is row (l / 16) * 4 + e, column l % 16 of its block; with
+  // BN/2 a multiple of 32 the gate and up blocks of the GeGLU interleave sit in the same lane
   const int rbase = m0 + wm * (BM / 2) + (lane >> 4) * 4;
   const int cbase = n0 + wn * (BN / 2);
 #pragma unroll
@@ -393,7 +447,9 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmP p) {
 }
 
 template <int BN, bool WF>
-static hipError_t launch_wide(const GemmP& p, int splits, hipStream_t s) {
+static hipError_t launch_ws(const GemmP& p, int splits, hipStream_t s) {
+  // the loaders address both operands with 32-bit element offsets
+  if ((size_t)p.M * p.lda >= (1ull << 31) || (size_t)p.N * p.ldw >= (1ull << 31)) return hipErrorInvalidValue;
   GemmP q = p;
   q.nM = (p.M + 287) / 288;
   q.nN = (p.N + BN - 1) / BN;
@@ -403,19 +459,19 @@ static hipError_t launch_wide(const GemmP& p, int splits, hipStream_t s) {
   const int used = (slices + per - 1) / per;  // == splits for counts from gemm_bf16_splits
   dim3 grid(q.nM * q.nN, used);
   const int kind = used > 1 ? EPI_PARTIAL : p.epi.kind;
-  const dim3 blk(256);
+  const dim3 blk2(512);
   switch (kind) {
-    case EPI_STORE: hipLaunchKernelGGL((k_gemm_wide<BN, EPI_STORE, WF>), grid, blk, 0, s, q); break;
-    case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_wide<BN, EPI_GEGLU, WF>), grid, blk, 0, s, q); break;
-    case EPI_PARTIAL: hipLaunchKernelGGL((k_gemm_wide<BN, EPI_PARTIAL, WF>), grid, blk, 0, s, q); break;
+    case EPI_STORE: hipLaunchKernelGGL((k_gemm_ws<BN, EPI_STORE, WF>), grid, blk2, 0, s, q); break;
+    case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_ws<BN, EPI_GEGLU, WF>), grid, blk2, 0, s, q); break;
+    case EPI_PARTIAL: hipLaunchKernelGGL((k_gemm_ws<BN, EPI_PARTIAL, WF>), grid, blk2, 0, s, q); break;
     case EPI_QKV:
-      if constexpr (WF) { hipLaunchKernelGGL((k_gemm_wide<BN, EPI_QKV, WF>), grid, blk, 0, s, q); break; }
+      if constexpr (WF) { hipLaunchKernelGGL((k_gemm_ws<BN, EPI_QKV, WF>), grid, blk2, 0, s, q); break; }
       return hipErrorInvalidValue;
     case EPI_CACHE:
-      if constexpr (!WF) { hipLaunchKernelGGL((k_gemm_wide<BN, EPI_CACHE, WF>), grid, blk, 0, s, q); break; }
+      if constexpr (!WF) { hipLaunchKernelGGL((k_gemm_ws<BN, EPI_CACHE, WF>), grid, blk2, 0, s, q); break; }
       return hipErrorInvalidValue;
     case EPI_RESID:
-      if constexpr (!WF) { hipLaunchKernelGGL((k_gemm_wide<BN, EPI_RESID, WF>), grid, blk, 0, s, q); break; }
+      if constexpr (!WF) { hipLaunchKernelGGL((k_gemm_ws<BN, EPI_RESID, WF>), grid, blk2, 0, s, q); break; }
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -472,8 +528,8 @@ hipError_t gemm_bf16(const uint16_t* A, int lda, const uint16_t* W, int ldw, int
     }
     return launch_skinny<1>(q, splits, s);
   }
-  if (w_frag) return launch_wide<128, true>(p, splits, s);
-  return launch_wide<128, false>(p, splits, s);
+  if (w_frag) return launch_ws<128, true>(p, splits, s);
+  return launch_ws<128, false>(p, splits, s);
 }
 
 // ------------------------------------------------------------------ chunk rows, fragment layout
