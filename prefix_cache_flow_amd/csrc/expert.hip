@@ -1,6 +1,6 @@
-// Small row kernels of the action expert: the chunk-token embedding with the
-// solver time, and the velocity head fused with the Euler update of the
-// paper's §III-A, Eq. 1: X^{k+1} = X^k + (tau_{k+1} - tau_k) v(X^k, tau_k).
+// Row kernels of the action expert's solver loop: the chunk-token embedding
+// with the solver time, and the velocity head fused with the Euler update of
+// the paper's §III-A, Eq. 1: X^{k+1} = X^k + (tau_{k+1} - tau_k) v(X^k, tau_k).
 //
 // The time embedding is not defined on the pages; the plainest reading of a
 // sinusoidal embedding of tau is used: phi_{2i} = sin(tau / 10000^(2i/d)),
@@ -18,130 +18,192 @@ __device__ __forceinline__ float ld_w(const void* w, long i) {
   return bf2f(((const bf16_t*)w)[i]);
 }
 
-// One 256-thread workgroup per chunk row m; d_e <= 4096, d_a <= 256.  The
-// row's d_a inputs sit in LDS; each thread loads its weight rows for all of
-// its outputs before using any (clamped indices, masked products).
-template <bool WF32>
-__global__ __launch_bounds__(256) void k_embed(const float* X, int d_a, const void* w_in, int d_e, const float* sched,
-                                               int k, float* E, const float* gain, float eps, void* u, int u_f32,
-                                               int u_frag, int M, Prefetch pf) {
-  __shared__ float xs[256];
-  __shared__ float es[4096];
-  if ((int)blockIdx.x >= M) {  // extra workgroups: warm the next kernel's weights
-    prefetch_share(pf, blockIdx.x - M, gridDim.x - M);
-    return;
-  }
-  __shared__ float red[4];
-  const int m = blockIdx.x;
-  if (threadIdx.x < d_a) xs[threadIdx.x] = X[(long)m * d_a + threadIdx.x];
-  __syncthreads();
-  const float tau = sched[k];
-  const float l2 = 13.287712379549449f;  // log2(10000)
-  float ss = 0.f;
-  for (int n = threadIdx.x; n < d_e; n += 256) {
-    float v = 0.f;
-    for (int a0 = 0; a0 < d_a; a0 += 8) {
-      float wv[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) wv[t] = ld_w<WF32>(w_in, (long)n * d_a + min(a0 + t, d_a - 1));
-#pragma unroll
-      for (int t = 0; t < 8; ++t) v = fmaf(a0 + t < d_a ? xs[a0 + t] : 0.f, wv[t], v);
-    }
-    // phi: frequency 10000^(-2i/d) on the exponential unit, angle tau * freq <= |tau|
-    const float freq = fast_exp2(-l2 * (2.0f * (float)(n >> 1) / (float)d_e));
-    const float arg = tau * freq;
-    v += (n & 1) ? __cosf(arg) : __sinf(arg);
-    E[(long)m * d_e + n] = v;
-    es[n] = v;
-    ss = fmaf(v, v, ss);
-  }
-  ss = block_sum<256>(ss, red);
-  const float r = 1.0f / sqrtf(ss / (float)d_e + eps);
-  for (int n = threadIdx.x; n < d_e; n += 256) {
-    const float un = es[n] * r * (1.0f + gain[n]);
-    if (u_f32) ((float*)u)[(long)m * d_e + n] = un;
-    else ((bf16_t*)u)[u_frag ? frag_idx(m, n, d_e) : (long)m * d_e + n] = f2bf(un);
-  }
-}
-
-hipError_t expert_embed(const float* X, int M, int d_a, const void* w_in, int w_f32, int d_e, const float* sched,
-                        int k, float* E, const float* gain, float eps, void* u, int u_f32, hipStream_t s, int u_frag,
-                        const Prefetch* prefetch) {
-  if (M <= 0) return hipSuccess;
-  if (d_a > 256 || d_e > 4096) return hipErrorInvalidValue;
-  if (u_frag && (u_f32 || d_e % 32 || M > 64)) return hipErrorInvalidValue;
-  const Prefetch pf = prefetch ? *prefetch : Prefetch{};
-  if (pf.blocks < 0 || pf.blocks > 1024 || (pf.blocks && !pf.sink)) return hipErrorInvalidValue;
-  if (w_f32)
-    hipLaunchKernelGGL(k_embed<true>, dim3(M + pf.blocks), dim3(256), 0, s, X, d_a, w_in, d_e, sched, k, E, gain, eps,
-                       u, u_f32, u_frag, M, pf);
-  else
-    hipLaunchKernelGGL(k_embed<false>, dim3(M + pf.blocks), dim3(256), 0, s, X, d_a, w_in, d_e, sched, k, E, gain,
-                       eps, u, u_f32, u_frag, M, pf);
-  return hipGetLastError();
-}
-
-// One 256-thread workgroup per chunk row: final RMSNorm, W_out, Euler update.
-// The normalized row goes to LDS; then G = 8 threads share each output: thread
-// t takes output t / 8 (and every 32nd after it) and the t % 8-th slice of the
-// row, loads that slice of the weight row before using it, and the eight
-// partial dot products are summed with lane exchanges in a fixed order.
-template <bool WF32>
-__global__ __launch_bounds__(256) void k_head(const float* E, int d_e, const float* gain, float eps, const void* w_out,
-                                              int d_a, const float* sched, int k, float* X) {
+// Head of step k fused with the embedding of step k + 1, one 256-thread
+// workgroup per chunk row (both are row-local): final RMSNorm, W_out and the
+// Euler update, then the new row through W_in plus phi(tau_{k+1}) and the first
+// layer's RMSNorm.  Either part can be switched off (first and last step).  In
+// their fast forms (bf16 weights and d_e <= 1024, d_a <= 32; the head also
+// needs d_e % 64 == 0, the embedding d_a % 8 == 0) every weight vector is
+// requested before the row itself is read, so the kernel is one memory round
+// trip.  Each part's form depends on the shapes alone.
+template <bool WF32, bool FH, bool FE>
+__global__ __launch_bounds__(256) void k_step_rows(StepRows a) {
   __shared__ float red[4];
   __shared__ float us[4096];
+  __shared__ float xs[256];
   const int m = blockIdx.x;
-  float ss = 0.f;
-  for (int n = threadIdx.x; n < d_e; n += 256) {
-    const float v = E[(long)m * d_e + n];
-    us[n] = v;
-    ss = fmaf(v, v, ss);
+  if (m >= a.M) {  // extra workgroups: warm the next kernel's weights
+    prefetch_share(a.pf, m - a.M, gridDim.x - a.M);
+    return;
   }
-  ss = block_sum<256>(ss, red);
-  const float r = 1.0f / sqrtf(ss / (float)d_e + eps);
-  for (int n = threadIdx.x; n < d_e; n += 256) us[n] = us[n] * r * (1.0f + gain[n]);
-  __syncthreads();
-  const float dt = sched[k + 1] - sched[k];
-  constexpr int G = 8;
-  const int slice = d_e / G;  // d_e % 64 == 0 for bf16 weights (8-element vectors)
-  const int part = threadIdx.x % G;
-  for (int a = threadIdx.x / G; a < d_a; a += 256 / G) {
-    float acc = 0.f;
-    if (WF32) {
-      for (int n = part; n < d_e; n += G) acc = fmaf(us[n], ld_w<true>(w_out, (long)a * d_e + n), acc);
+  const int tid = threadIdx.x;
+  const bool head = a.k_head >= 0, emb = a.k_embed >= 0;
+  constexpr int G = 8;  // threads per head output
+  const int part = tid % G, ao = tid / G;
+  // ---- every global operand first (fast forms): weights, the row, both gains
+  constexpr int PER = 4;  // row elements per thread when d_e <= 1024
+  u32x4_t wo[16], wi[16];
+  float er[PER], gf[PER], g1[PER];
+  if (FH && head) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int n = min(tid + i * 256, a.d_e - 1);
+      er[i] = a.E[(long)m * a.d_e + n];
+      gf[i] = a.gain_f[n];
+    }
+  }
+  if (FE && emb) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) g1[i] = a.gain_1[min(tid + i * 256, a.d_e - 1)];
+  }
+  {
+    if (FH && head) {
+      const int sl = a.d_e / G;  // slice of a W_out row per thread, multiple of 8
+      const bf16_t* wr = (const bf16_t*)a.w_out + (long)min(ao, a.d_a - 1) * a.d_e + part * sl;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) wo[t] = *(const u32x4_t*)(wr + min(t * 8, sl - 8));
+    }
+    if (FE && emb) {
+      const int dv = a.d_a / 8;  // vectors per W_in row
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int i = t / 4, v = t % 4;  // output tid + 256 i, vector v of its row
+        const int n = min(tid + i * 256, a.d_e - 1);
+        wi[t] = *(const u32x4_t*)((const bf16_t*)a.w_in + (long)n * a.d_a + min(v, dv - 1) * 8);
+      }
+    }
+  }
+  // ---- head: v = RMS(E; w_ef) W_out^T, X += dt v
+  if (head) {
+    float ss = 0.f;
+    if (FH) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) ss = fmaf(er[i], tid + i * 256 < a.d_e ? er[i] : 0.f, ss);
+      ss = block_sum<256>(ss, red);
+      const float r = 1.0f / sqrtf(ss / (float)a.d_e + a.eps);
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (tid + i * 256 < a.d_e) us[tid + i * 256] = er[i] * r * (1.0f + gf[i]);
     } else {
-      const bf16_t* wr = (const bf16_t*)w_out + (long)a * d_e + part * slice;
-      for (int c = 0; c < slice; c += 128) {  // 16 vectors of 8 weights in flight at once
-        u32x4_t wv[16];
+      for (int n = tid; n < a.d_e; n += 256) {
+        const float v = a.E[(long)m * a.d_e + n];
+        us[n] = v;
+        ss = fmaf(v, v, ss);
+      }
+      ss = block_sum<256>(ss, red);
+      const float r = 1.0f / sqrtf(ss / (float)a.d_e + a.eps);
+      for (int n = tid; n < a.d_e; n += 256) us[n] = us[n] * r * (1.0f + a.gain_f[n]);
+    }
+    __syncthreads();
+    const float dt = a.sched[a.k_head + 1] - a.sched[a.k_head];
+    if (FH) {
+      const int sl = a.d_e / G;
+      float acc = 0.f;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) wv[t] = *(const u32x4_t*)(wr + min(c + t * 8, slice - 8));
+      for (int t = 0; t < 16; ++t) {
+        if (t * 8 >= sl) break;
+        const float* ur = &us[part * sl + t * 8];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          if (c + t * 8 >= slice) break;
-          const float* ur = &us[part * slice + c + t * 8];
+        for (int h = 0; h < 4; ++h) {
+          acc = fmaf(ur[2 * h], bf2f((bf16_t)(wo[t][h] & 0xffffu)), acc);
+          acc = fmaf(ur[2 * h + 1], bf2f((bf16_t)(wo[t][h] >> 16)), acc);
+        }
+      }
 #pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            acc = fmaf(ur[2 * h], bf2f((bf16_t)(wv[t][h] & 0xffffu)), acc);
-            acc = fmaf(ur[2 * h + 1], bf2f((bf16_t)(wv[t][h] >> 16)), acc);
-          }
+      for (int o = 1; o < G; o <<= 1) acc += __shfl_xor(acc, o, 64);
+      if (part == 0 && ao < a.d_a) {
+        const float x = a.X[(long)m * a.d_a + ao] + dt * acc;
+        a.X[(long)m * a.d_a + ao] = x;
+        xs[ao] = x;
+      }
+    } else {
+      for (int o = ao; o < a.d_a; o += 256 / G) {
+        float acc = 0.f;
+        for (int n = part; n < a.d_e; n += G) acc = fmaf(us[n], ld_w<WF32>(a.w_out, (long)o * a.d_e + n), acc);
+#pragma unroll
+        for (int q = 1; q < G; q <<= 1) acc += __shfl_xor(acc, q, 64);
+        if (part == 0) {
+          const float x = a.X[(long)m * a.d_a + o] + dt * acc;
+          a.X[(long)m * a.d_a + o] = x;
+          xs[o] = x;
         }
       }
     }
+  } else if (tid < a.d_a) {
+    xs[tid] = a.X[(long)m * a.d_a + tid];
+  }
+  if (!emb) return;
+  __syncthreads();
+  // ---- embedding of step k_embed: E = X W_in^T + phi(tau), u = RMS(E; a1)
+  const float tau = a.sched[a.k_embed];
+  const float l2 = 13.287712379549449f;  // log2(10000)
+  float ss = 0.f;
+  // the embedded row element n = tid + 256 i
+  auto emit = [&](int n, float v) {
+    // phi: frequency 10000^(-2i/d) on the exponential unit, angle tau * freq <= |tau|
+    const float freq = fast_exp2(-l2 * (2.0f * (float)(n >> 1) / (float)a.d_e));
+    const float arg = tau * freq;
+    v += (n & 1) ? __cosf(arg) : __sinf(arg);
+    a.Eout[(long)m * a.d_e + n] = v;
+    us[n] = v;
+    ss = fmaf(v, v, ss);
+  };
+  if (FE) {
+    const int dv = a.d_a / 8;
 #pragma unroll
-    for (int o = 1; o < G; o <<= 1) acc += __shfl_xor(acc, o, 64);
-    if (part == 0) X[(long)m * d_a + a] += dt * acc;
+    for (int i = 0; i < PER; ++i) {  // unrolled: the weight registers are indexed statically
+      const int n = tid + i * 256;
+      if (n >= a.d_e) break;
+      float v = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q >= dv) break;
+        const u32x4_t w = wi[i * 4 + q];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          v = fmaf(xs[q * 8 + 2 * h], bf2f((bf16_t)(w[h] & 0xffffu)), v);
+          v = fmaf(xs[q * 8 + 2 * h + 1], bf2f((bf16_t)(w[h] >> 16)), v);
+        }
+      }
+      emit(n, v);
+    }
+  } else {
+    for (int n = tid; n < a.d_e; n += 256) {
+      float v = 0.f;
+      for (int a0 = 0; a0 < a.d_a; ++a0) v = fmaf(xs[a0], ld_w<WF32>(a.w_in, (long)n * a.d_a + a0), v);
+      emit(n, v);
+    }
+  }
+  ss = block_sum<256>(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)a.d_e + a.eps);
+  auto put_u = [&](int n, float g) {
+    const float un = us[n] * r * (1.0f + g);
+    if (a.u_f32) ((float*)a.u)[(long)m * a.d_e + n] = un;
+    else ((bf16_t*)a.u)[a.u_frag ? frag_idx(m, n, a.d_e) : (long)m * a.d_e + n] = f2bf(un);
+  };
+  if (FE) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (tid + i * 256 < a.d_e) put_u(tid + i * 256, g1[i]);
+  } else {
+    for (int n = tid; n < a.d_e; n += 256) put_u(n, a.gain_1[n]);
   }
 }
 
-hipError_t expert_head(const float* E, int M, int d_e, const float* gain, float eps, const void* w_out, int w_f32,
-                       int d_a, const float* sched, int k, float* X, hipStream_t s) {
-  if (M <= 0) return hipSuccess;
-  if (d_e > 4096) return hipErrorInvalidValue;
-  if (w_f32)
-    hipLaunchKernelGGL(k_head<true>, dim3(M), dim3(256), 0, s, E, d_e, gain, eps, w_out, d_a, sched, k, X);
-  else
-    hipLaunchKernelGGL(k_head<false>, dim3(M), dim3(256), 0, s, E, d_e, gain, eps, w_out, d_a, sched, k, X);
+hipError_t step_rows(const StepRows& a, int w_f32, hipStream_t s) {
+  if (a.M <= 0 || (a.k_head < 0 && a.k_embed < 0)) return hipSuccess;
+  if (a.d_a > 256 || a.d_e > 4096) return hipErrorInvalidValue;
+  if (a.k_embed >= 0 && a.u_frag && (a.u_f32 || a.d_e % 32 || a.M > 64)) return hipErrorInvalidValue;
+  if (a.pf.blocks < 0 || a.pf.blocks > 1024 || (a.pf.blocks && !a.pf.sink)) return hipErrorInvalidValue;
+  // each part's form depends on the shapes only, so a step computes the same bits fused or alone
+  const bool fh = !w_f32 && a.d_e % 64 == 0 && a.d_e <= 1024 && a.d_a <= 32;
+  const bool fe = !w_f32 && a.d_a % 8 == 0 && a.d_a <= 32 && a.d_e <= 1024;
+  const dim3 grid(a.M + a.pf.blocks);
+  if (w_f32) hipLaunchKernelGGL((k_step_rows<true, false, false>), grid, dim3(256), 0, s, a);
+  else if (fh && fe) hipLaunchKernelGGL((k_step_rows<false, true, true>), grid, dim3(256), 0, s, a);
+  else if (fh) hipLaunchKernelGGL((k_step_rows<false, true, false>), grid, dim3(256), 0, s, a);
+  else if (fe) hipLaunchKernelGGL((k_step_rows<false, false, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_step_rows<false, false, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -138,17 +138,30 @@ hipError_t attention_chunk(const AttnArgs& a, hipStream_t s);
 hipError_t attention_f32(const AttnArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------------ expert pieces
-// E[m] = X[m] W_in^T + phi(tau_k) for the chunk rows, then u = RMS(E[m]; gain).
-hipError_t expert_embed(const float* X, int M, int d_a, const void* w_in, int w_f32, int d_e,
-                        const float* sched, int k, float* E, const float* gain, float eps,
-                        void* u, int u_f32, hipStream_t s, int u_frag = 0, const Prefetch* prefetch = nullptr);
-// v = RMS(E[m]; gain) W_out^T; X[m] += (tau_{k+1} - tau_k) v
-hipError_t expert_head(const float* E, int M, int d_e, const float* gain, float eps,
-                       const void* w_out, int w_f32, int d_a, const float* sched, int k, float* X,
-                       hipStream_t s);
 // Zero the last `tail` 16-bit elements of each of nblk blocks of `blk` elements
 // (the padding key rows of fragment-ordered K/V blocks); tail, blk % 8 == 0.
 hipError_t zero_tails(void* base, long nblk, long blk, int tail, hipStream_t s);
+// Row kernel of the solver loop: the velocity head and Euler update of step
+// k_head (skipped when < 0), then the embedding of step k_embed with the first
+// layer's RMSNorm (skipped when < 0).  E is read by the head, Eout written by
+// the embedding (they may alias).
+struct StepRows {
+  const float* E = nullptr;
+  float* Eout = nullptr;
+  float* X = nullptr;
+  int M = 0, d_e = 0, d_a = 0;
+  float eps = 0.f;
+  const float* gain_f = nullptr;  // final expert norm gain (head)
+  const void* w_out = nullptr;
+  const void* w_in = nullptr;
+  const float* gain_1 = nullptr;  // first expert layer's norm gain (embedding)
+  void* u = nullptr;
+  int u_f32 = 0, u_frag = 0;
+  const float* sched = nullptr;
+  int k_head = -1, k_embed = -1;
+  Prefetch pf;
+};
+hipError_t step_rows(const StepRows& a, int w_f32, hipStream_t s);
 // dst = src (fp32), or bf16(src) when out_bf16
 hipError_t copy_out(const float* src, void* dst, long n, int out_bf16, hipStream_t s);
 hipError_t copy_f32(const float* src, float* dst, long n, hipStream_t s);

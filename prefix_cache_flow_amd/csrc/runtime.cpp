@@ -1010,11 +1010,18 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
     f.p = p; f.bytes = bytes; f.p2 = p2; f.bytes2 = p2 ? bytes2 : 0; f.sink = w.sink; f.blocks = blocks;
     return f;
   };
+  // row kernel between steps: head of step k - 1 (if any) fused with the embedding of step k (if any)
+  auto rows = [&](int k_head, int k_embed) {
+    StepRows a;
+    a.E = w.E; a.Eout = w.E; a.X = w.X; a.M = M; a.d_e = c.d_e; a.d_a = c.d_a; a.eps = eps;
+    a.gain_f = m->w_ef; a.w_out = m->w_out; a.w_in = m->w_in; a.gain_1 = m->el[0].a1;
+    a.u = w.eu; a.u_f32 = f32 ? 1 : 0; a.u_frag = fr; a.sched = m->sched_dev;
+    a.k_head = k_head; a.k_embed = k_embed;
+    if (k_embed >= 0) a.pf = pfr(m->el[0].wqkv, b_qkv, nullptr, 0, 64);
+    return step_rows(a, f32 ? 1 : 0, s);
+  };
   for (int k = 0; k < steps; ++k) {
-    const Prefetch pf_embed = pfr(m->el[0].wqkv, b_qkv, nullptr, 0, 64);
-    K_TRY(expert_embed(w.X, M, c.d_a, m->w_in, f32, c.d_e, m->sched_dev, k, w.E, m->el[0].a1, eps, w.eu, f32, s, fr,
-                       &pf_embed),
-          "embed");
+    if (k == 0) K_TRY(rows(-1, 0), "embed");
     for (int e = 0; e < c.L_e; ++e) {
       const ExpertLayer& L = m->el[e];
       ca.k = (const char*)kv->storage + (size_t)e * layer_stride * es;
@@ -1067,7 +1074,7 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
                          e + 1 < c.L_e ? w.eu : nullptr, 0, c.d_e, nullptr, nullptr, s, fr, &pf_next), "norm");
       }
     }
-    K_TRY(expert_head(w.E, M, c.d_e, m->w_ef, eps, m->w_out, f32, c.d_a, m->sched_dev, k, w.X, s), "head");
+    K_TRY(rows(k, k + 1 < steps ? k + 1 : -1), "head");
   }
   return VLA_OK;
 }
