@@ -464,9 +464,7 @@ static hipError_t launch_ws(const GemmP& p, int splits, hipStream_t s) {
     case EPI_STORE: hipLaunchKernelGGL((k_gemm_ws<BN, EPI_STORE, WF>), grid, blk2, 0, s, q); break;
     case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_ws<BN, EPI_GEGLU, WF>), grid, blk2, 0, s, q); break;
     case EPI_PARTIAL: hipLaunchKernelGGL((k_gemm_ws<BN, EPI_PARTIAL, WF>), grid, blk2, 0, s, q); break;
-    case EPI_QKV:
-      if constexpr (WF) { hipLaunchKernelGGL((k_gemm_ws<BN, EPI_QKV, WF>), grid, blk2, 0, s, q); break; }
-      return hipErrorInvalidValue;
+    case EPI_QKV: hipLaunchKernelGGL((k_gemm_ws<BN, EPI_QKV, WF>), grid, blk2, 0, s, q); break;
     case EPI_CACHE:
       if constexpr (!WF) { hipLaunchKernelGGL((k_gemm_ws<BN, EPI_CACHE, WF>), grid, blk2, 0, s, q); break; }
       return hipErrorInvalidValue;
@@ -511,7 +509,7 @@ hipError_t gemm_bf16(const uint16_t* A, int lda, const uint16_t* W, int ldw, int
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
   if (K % 64 || N % 32) return hipErrorInvalidValue;
   if (w_frag && (M <= 64 || ldw != K || epi.kind == EPI_RESID || epi.kind == EPI_CACHE)) return hipErrorInvalidValue;
-  if (!w_frag && epi.kind == EPI_QKV) return hipErrorInvalidValue;
+  if (M <= 64 && epi.kind == EPI_QKV) return hipErrorInvalidValue;
   // the one place that fixes how many partial slices are written: callers that
   // consume EPI_PARTIAL output read gemm_bf16_splits(K, splits, M) of them
   splits = gemm_bf16_splits(K, splits, M);

@@ -212,6 +212,7 @@ struct vla_model {
   std::set<vla_kv_cache*> caches;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   int64_t plan_rows = 0, plan_erows = 0;  // largest prefix / chunk row counts seen
+  int64_t plan_kvrows = 0;                 // largest batch x padded prefix length seen
   // kernel probe
   int probe_kind = 0, probe_max = 0, probe_used = 0;
   std::vector<hipEvent_t> probe_ev;
@@ -578,7 +579,9 @@ static int64_t key_rows(const vla_model* m, int64_t n) { return m->f32 ? n : (n 
 struct WS {
   float* h;         // prefix residual [rows][d_p]
   void* u;          // normalized activations [rows][max(d_p, d_e)]
-  void* qkv;        // [rows][(Hq + 2 Hkv) hd]
+  void* qkv;        // [rows][(Hq + 2 Hkv) hd]; bf16 above 64 rows: queries only, [rows][Hq hd]
+  void* pk;         // bf16 prefix keys   [B][Hkv][Np][hd], frag_idx order (Np = N rounded up to 32)
+  void* pv;         // bf16 prefix values [B][Hkv][Np][hd], vfrag_idx order
   void* attn;       // [rows][Hq hd]       (fp32 for the ternary prefix)
   void* mlp;        // [rows][F_p]         (fp32 for the ternary prefix)
   int8_t* qa;       // ternary: int8 codes [rows][max(d_p, Hq hd, F_p)]
@@ -633,7 +636,7 @@ static int64_t expert_part_floats(const vla_model_config& c, int64_t erows) {
   return f * erows;
 }
 
-static WS plan(const vla_model* m, int64_t rows, int64_t erows, char* base) {
+static WS plan(const vla_model* m, int64_t rows, int64_t erows, int64_t kvrows, char* base) {
   const vla_model_config& c = m->cfg;
   const size_t es = elt(m);
   size_t off = 0;
@@ -648,6 +651,8 @@ static WS plan(const vla_model* m, int64_t rows, int64_t erows, char* base) {
   w.h = (float*)take(rows * c.d_p * 4);
   w.u = take(rows * std::max<int64_t>(c.d_p, c.d_e) * es);
   w.qkv = take(rows * qkvw * es);
+  w.pk = take(kvrows * c.Hkv * c.hd * es);
+  w.pv = take(kvrows * c.Hkv * c.hd * es);
   w.attn = take(rows * qw * act_es);
   w.mlp = take(rows * (int64_t)c.F_p * act_es);
   if (m->w2a8) {
@@ -676,8 +681,8 @@ static WS plan(const vla_model* m, int64_t rows, int64_t erows, char* base) {
   return w;
 }
 
-static vla_status ensure_ws(vla_model* m, int64_t rows, int64_t erows, WS* out) {
-  WS need = plan(m, rows, erows, nullptr);
+static vla_status ensure_ws(vla_model* m, int64_t rows, int64_t erows, int64_t kvrows, WS* out) {
+  WS need = plan(m, rows, erows, kvrows, nullptr);
   if (need.total > m->ws_bytes) {
     if (m->ws) {
       hipError_t e = hipDeviceSynchronize();
@@ -702,16 +707,17 @@ static vla_status ensure_ws(vla_model* m, int64_t rows, int64_t erows, WS* out) 
     m->ws = (char*)p;
     m->ws_bytes = need.total;
   }
-  *out = plan(m, rows, erows, m->ws);
+  *out = plan(m, rows, erows, kvrows, m->ws);
   return VLA_OK;
 }
 
-// Encode plans prefix rows, denoise chunk rows; both share one arena sized for
-// the largest of each seen so far.
-static vla_status get_ws(vla_model* m, int64_t rows, int64_t erows, WS* out) {
+// Encode plans prefix rows (and padded key rows), denoise chunk rows; all share
+// one arena sized for the largest of each seen so far.
+static vla_status get_ws(vla_model* m, int64_t rows, int64_t erows, WS* out, int64_t kvrows = 0) {
   m->plan_rows = std::max(m->plan_rows, rows);
   m->plan_erows = std::max(m->plan_erows, erows);
-  return ensure_ws(m, m->plan_rows, m->plan_erows, out);
+  m->plan_kvrows = std::max(m->plan_kvrows, kvrows);
+  return ensure_ws(m, m->plan_rows, m->plan_erows, m->plan_kvrows, out);
 }
 
 // ============================================================== prefix
@@ -794,6 +800,22 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
   aa.o = w.attn; aa.o_bs = (long)N * qw; aa.o_rs = qw;
   aa.B = B; aa.Nq = N; aa.Nk = N; aa.Hq = c.Hq; aa.Hkv = c.Hkv; aa.hd = c.hd;
   aa.o_f32 = (m->f32 || m->w2a8) ? 1 : 0;
+  // bf16 above 64 rows: the fused projection writes query rows and the keys and
+  // values in the MFMA operand orders, read by the chunk-style attention kernel
+  const bool kvfrag = !m->f32 && !m->w2a8 && M > 64;
+  const int Np = (int)key_rows(m, N);
+  Epilogue qkv_e = epi_store(w.qkv, qkvw, 0);
+  if (kvfrag) {
+    qkv_e.kind = EPI_QKV; qkv_e.ldo = qw; qkv_e.nq = qw;
+    qkv_e.kout = w.pk; qkv_e.vout = w.pv; qkv_e.hkv = c.Hkv; qkv_e.hd = c.hd; qkv_e.npre = N; qkv_e.npad = Np;
+    aa.q_bs = (long)N * qw; aa.q_rs = qw;
+    aa.k = w.pk; aa.k_bs = (long)c.Hkv * Np * c.hd; aa.k_hs = (long)Np * c.hd;
+    aa.v = w.pv; aa.v_bs = aa.k_bs; aa.v_hs = aa.k_hs;
+    if (Np > N) {  // padding key rows: finite values (zero weights times values)
+      K_TRY(zero_tails(w.pk, (long)B * c.Hkv, (long)Np * c.hd, 32 * c.hd, s), "key padding");
+      K_TRY(zero_tails(w.pv, (long)B * c.Hkv, (long)Np * c.hd, 32 * c.hd, s), "value padding");
+    }
+  }
 
   if (m->w2a8) {
     K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, m->pl[0].w1, eps, nullptr, 0, 0, w.qa, w.alpha, s), "norm");
@@ -841,12 +863,12 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
         const uint16_t* u = (const uint16_t*)w.u;
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_QKV, s);
-          K_TRY(gemm_bf16(u, c.d_p, (const uint16_t*)P.wqkv, c.d_p, M, qkvw, c.d_p, epi_store(w.qkv, qkvw, 0),
+          K_TRY(gemm_bf16(u, c.d_p, (const uint16_t*)P.wqkv, c.d_p, M, qkvw, c.d_p, qkv_e,
                           prefix_splits(M, qkvw, c.d_p), w.part, s), "qkv");
         }
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_ATTN, s);
-          K_TRY(attention_bf16(aa, s), "attention");
+          K_TRY(kvfrag ? attention_chunk(aa, s) : attention_bf16(aa, s), "attention");
         }
         Epilogue pe;
         pe.kind = EPI_PARTIAL;
@@ -910,7 +932,7 @@ extern "C" vla_status vla_prefix_encode(vla_model* m, const float* x, int32_t ba
     return fail(VLA_ERR_SHAPE_MISMATCH, "kv_bytes " + std::to_string(kv_bytes) + " < required " + std::to_string(need));
   hipStream_t s = (hipStream_t)stream;
   WS w;
-  vla_status st = get_ws(m, (int64_t)batch * n_prefix, 0, &w);
+  vla_status st = get_ws(m, (int64_t)batch * n_prefix, 0, &w, (int64_t)batch * key_rows(m, n_prefix));
   if (st != VLA_OK) return st;
   if (timing) K_TRY(hipEventRecord(m->ev0, s), "event");
   st = run_prefix(m, x, batch, n_prefix, kv_storage, w, s);
