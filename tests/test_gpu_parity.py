@@ -12,8 +12,8 @@ import pytest
 
 import oracle
 import synth
-from policy_cases import (SMALL_BF16, SMALL_BF16_B3, SMALL_W2A8, build_model, cache_from_storage, gpu_run,
-                          host_inputs)
+from policy_cases import (SMALL_BF16, SMALL_BF16_B3, SMALL_GQA, SMALL_W2A8, build_model, cache_from_storage,
+                          gpu_run, host_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,6 +41,7 @@ def report(name, got, ref, x0):
     (synth.config(0), 1e-3, 1e-3, 1e-4),
     (SMALL_BF16, 2e-2, 5e-3, 4e-3),
     (SMALL_BF16_B3, 2e-2, 5e-3, 4e-3),
+    (SMALL_GQA, 2e-2, 5e-3, 4e-3),
     (SMALL_W2A8, 2e-2, 1e-2, 4e-3),
 ], ids=lambda v: getattr(v, "name", ""))
 def test_end_to_end_small(cfg, tol, dtol, ctol):
@@ -85,6 +86,35 @@ def test_zero_velocity_and_determinism():
     model = build_model(cfg, w0, b)
     a0, _ = gpu_run(cfg, model, z0, x0)
     np.testing.assert_array_equal(a0, x0.astype(np.float64))
+    model.close()
+
+
+def test_graph_replays_match_eager():
+    """The captured solver loop, replayed several times with other GPU work in between and with
+    different schedules of the same length, gives the eager result bit for bit every time."""
+    import os
+    cfg = SMALL_GQA
+    w, b, z0, x0 = host_inputs(cfg, 3)
+    model = build_model(cfg, w, b)
+    zt, xt = torch.from_numpy(z0).cuda(), torch.from_numpy(x0).cuda()
+    kv = vla.vla_prefix_encode(model, zt)
+    scheds = [None, [0.0, 0.3, 1.0], [1.0, 0.5, 0.0]]
+    os.environ["VLA_NO_GRAPH"] = "1"
+    try:
+        eager = [vla.vla_denoise_chunk(model, kv, xt, cfg.steps, schedule=sc).cpu().numpy() for sc in scheds]
+    finally:
+        del os.environ["VLA_NO_GRAPH"]
+    replayed = 0
+    for rep in range(3):
+        for sc, ref in zip(scheds, eager):
+            junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated work between replays
+            out, t = vla.vla_denoise_chunk(model, kv, xt, cfg.steps, schedule=sc, timing=True)
+            replayed += t["graph_replayed"]
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(out.cpu().numpy(), ref)
+            del junk
+    assert replayed >= 8  # one capture, then replays
+    kv.close()
     model.close()
 
 
