@@ -377,7 +377,6 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
 hipError_t attention_chunk(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.Nq <= 0 || a.Nk <= 0) return hipSuccess;
   if (a.Hq % a.Hkv || a.o_f32) return hipErrorInvalidValue;
-  if (a.o_frag && a.B * a.Nq > 64) return hipErrorInvalidValue;
   if (a.pf.blocks < 0 || a.pf.blocks > 1024 || (a.pf.blocks && !a.pf.sink)) return hipErrorInvalidValue;
   const int R = a.Hq / a.Hkv * a.Nq;
   dim3 grid((R + 15) / 16 + a.pf.blocks, a.Hkv, a.B);

@@ -1,17 +1,18 @@
 // Dense projections of the policy step: C = A W^T with A [M, K] activations and
 // W [N, K] weights (the [out, in] layout of every linear layer).
 //
-// gemm_bf16: bf16 operands, fp32 accumulation on the bf16 MFMA of gfx950.
-//   More than 64 rows: 288 x 128 workgroup tiles (k_gemm_ws), 64-wide K slices
-//   staged through LDS with one register-prefetched slice ahead.  Rows of LDS are
-//   padded by 16 bytes so the 16-byte fragment reads of 16 consecutive rows hit
-//   distinct banks.  Output tiles are numbered XCD-major so tiles that share a
-//   weight panel run on one XCD and share its L2.
-//   At most 64 rows: weight-streaming kernels (k_skinny for row-major operands,
-//   k_chunk for the fragment layout of common.h).
+// gemm_frag (the prefix, and any bf16 product with both operands in the
+//   fragment layout of common.h): 288-row tiles, k_gemm_af.
+// gemm_chunk (at most 64 rows, fragment layout): weight-streaming k_chunk.
+// gemm_bf16 (row-major activations): k_gemm_ws above 64 rows (wave-specialised
+//   288 x 128 tiles staged through LDS), k_skinny up to 64.
 //   Split-K writes fp32 partials [split][M][N] that a fixed-order reduction (or
 //   the row kernel of norm.hip) sums, so results never depend on timing.
+//   Output tiles are numbered XCD-major so tiles that share a weight panel or
+//   an activation K range run on one XCD and share its L2.
 // gemm_f32: fp32 SIMT tiles for the fp32 workload (small shapes).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -484,6 +485,320 @@ static hipError_t launch_ws(const GemmP& p, int splits, hipStream_t s) {
   return err;
 }
 
+// ------------------------------------------------------------------ wide tiles, fragment operands
+// Many rows with both operands in the fragment layout of common.h.  A
+// workgroup owns a 288 x BN output tile (BN = 128, or 64 for small products)
+// and has four waves, one per SIMD, so at BN = 128 each may hold up to 512
+// registers (at 64, two workgroups share a CU).  Wave w owns the 16-row blocks
+// w, w + 4, ..., w + 16 across all BN columns (BN / 16 x 5 accumulators; the fifth block of
+// waves 2 and 3 lies past the tile: it is computed on clamped rows and
+// dropped).  Every row block belongs to one wave, so activation fragments go
+// straight from global memory into registers (two register sets, issued two
+// 64-wide K slices ahead) without touching LDS.  The weight slice, BN columns
+// x 64 k = BN / 8 fragments of 1 KB, is shared by the four waves: each thread
+// fetches BN / 32 of its 16-byte vectors into one of two register sets three
+// slices ahead and writes them into one of two LDS buffers in fragment order,
+// so every LDS read and write of a wave is a contiguous 1 KB.  One barrier per
+// slice.  The MFMA takes the weight fragment as its first operand: a lane's
+// accumulator then holds four consecutive columns of one row, and the
+// epilogue stores 8 (bf16) or 16 (fp32) contiguous bytes per lane.  Slices past
+// the end are fetched clamped and never computed; rows past M and columns past
+// N are never stored.  (row, split) work items are numbered so that the
+// workgroups of one XCD share a split's activation K range and whole weight
+// panels.
+struct FragP {
+  const uint16_t* A;
+  const uint16_t* W;
+  int M, N, K, kchunk, nM, nN;
+  Epilogue epi;
+  float* ws;
+};
+
+constexpr int kFragBM = 288;
+
+// The accumulator is pinned to the accumulation registers: with the builtin,
+// the register allocator sometimes splits the 160 accumulators of k_gemm_af
+// between the two register files and copies them back and forth every
+// iteration.  The first k-step starts from a zero accumulator operand, so no
+// register write precedes an MFMA; the caller inserts the wait states between
+// the last MFMA and the first read of its results.
+template <bool FIRST>
+__device__ __forceinline__ void mfma16_acc(f32x4_t& c, bf16x8_t a, bf16x8_t b) {
+  if (FIRST) asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+  else asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_wait_states() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+__device__ __forceinline__ u32x2_t pack4_bf16(float a, float b, float c, float d) {
+  return u32x2_t{pack_bf2(a, b), pack_bf2(c, d)};
+}
+
+template <int KIND, bool ODD, int BN>
+__global__ __launch_bounds__(256, BN == 64 ? 2 : 1) void k_gemm_af(FragP p) {
+  constexpr int RB = kFragBM / 16, TB = 5, NB = BN / 16, KS = 2, FR = NB * KS, WV = FR / 4;
+  __shared__ u32x4_t sw[2][FR][64];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int total = gridDim.x, L = blockIdx.x;
+  const int q = (total % 8 == 0) ? (L % 8) * (total / 8) + L / 8 : L;
+  const int ntile = p.nM * p.nN;
+  const int split = q / ntile, tile = q - split * ntile;
+  const int tm = tile % p.nM, tn = tile / p.nM;
+  const int KSt = p.K >> 5;
+  const int kb0 = split * (p.kchunk >> 5);
+  const int nsl = max(0, min(p.kchunk, p.K - split * p.kchunk) >> 6);
+  const int mbt = (p.M + 15) >> 4, nbt = p.N >> 4;
+
+  // wave-uniform fragment bases (scalar registers) plus one per-lane byte offset
+  const char* ab[TB];
+#pragma unroll
+  for (int i = 0; i < TB; ++i)
+    ab[i] = (const char*)p.A + ((long)min(tm * RB + w + 4 * i, mbt - 1) * KSt + kb0) * 1024;
+  const char* wb[WV];
+#pragma unroll
+  for (int i = 0; i < WV; ++i) {
+    const int f = w + 4 * i, nb = f / KS, kk = f % KS;
+    wb[i] = (const char*)p.W + ((long)min(tn * NB + nb, nbt - 1) * KSt + kb0 + kk) * 1024;
+  }
+  const uint32_t lo = lane * 16;
+  auto soff = [&](int s) { return (uint32_t)min(s, max(nsl - 1, 0)) * (KS * 1024); };
+  u32x4_t a0[TB][KS], a1[TB][KS], w0[WV], w1[WV];
+  auto lda = [&](u32x4_t(&a)[TB][KS], int s) {
+    const uint32_t o = soff(s) + lo;
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) a[i][kk] = *(const u32x4_t*)(ab[i] + o + kk * 1024);
+  };
+  auto ldw = [&](u32x4_t(&r)[WV], int s) {
+    const uint32_t o = soff(s) + lo;
+#pragma unroll
+    for (int i = 0; i < WV; ++i) r[i] = *(const u32x4_t*)(wb[i] + o);
+  };
+  auto stw = [&](const u32x4_t(&r)[WV], int buf) {
+#pragma unroll
+    for (int i = 0; i < WV; ++i) sw[buf][w + 4 * i][lane] = r[i];
+  };
+  f32x4_t acc[TB][NB];
+  // MFMAs run weight fragment by weight fragment; as soon as fragment j has
+  // served its five row blocks, the same k-step's successor is read into its
+  // registers, so at most one k-step of fragments is live and each read has
+  // the rest of the k-step to land.  The fences pin that order (left to
+  // itself the compiler hoists every read and runs out of registers).
+  auto compute = [&](const u32x4_t(&a)[TB][KS], int buf, auto first) {
+    bf16x8_t b[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) b[j] = as_bf16x8(sw[buf][j * KS][lane]);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+#pragma unroll
+        for (int i = 0; i < TB; ++i) {
+          if (decltype(first)::value && kk == 0) mfma16_acc<true>(acc[i][j], b[j], as_bf16x8(a[i][kk]));
+          else mfma16_acc<false>(acc[i][j], b[j], as_bf16x8(a[i][kk]));
+        }
+        if (kk + 1 < KS) b[j] = as_bf16x8(sw[buf][j * KS + kk + 1][lane]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  using First = std::integral_constant<bool, true>;
+  using Next = std::integral_constant<bool, false>;
+
+  // entering slice s (even): W(s) in LDS buffer 0, W(s+1) in w1, W(s+2) in w0, A(s) in a0, A(s+1) in a1
+  ldw(w0, 0);
+  ldw(w1, 1);
+  lda(a0, 0);
+  lda(a1, 1);
+  stw(w0, 0);
+  ldw(w0, 2);
+  __syncthreads();
+  // scheduling barriers keep each register set's reload behind its last use
+  auto two_slices = [&](int s, auto first) {
+    stw(w1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    ldw(w1, s + 3);
+    compute(a0, 0, first);
+    __builtin_amdgcn_sched_barrier(0);
+    lda(a0, s + 2);
+    __syncthreads();
+    stw(w0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    ldw(w0, s + 4);
+    if (ODD && s + 1 >= nsl) {  // odd slice count: the pair's second half adds nothing
+#pragma unroll
+      for (int i = 0; i < TB; ++i)
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) a1[i][kk] = u32x4_t{0, 0, 0, 0};
+    }
+    compute(a1, 1, Next{});
+    __builtin_amdgcn_sched_barrier(0);
+    lda(a1, s + 3);
+    __syncthreads();
+  };
+  two_slices(0, First{});
+  for (int s = 2; s < nsl; s += 2) two_slices(s, Next{});
+
+  // the results are read below by VALU and memory instructions, which the
+  // compiler does not know the MFMAs above have to finish for
+  mfma_wait_states();
+#pragma unroll
+  for (int i = 0; i < TB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) asm volatile("" : "+a"(acc[i][j]));
+  // epilogue: accumulator element e of lane l is row l % 16 and column (l / 16) * 4 + e of its block
+  const int cq = (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < TB; ++i) {
+    const int rb = w + 4 * i;
+    const int m = tm * kFragBM + rb * 16 + (lane & 15);
+    if (rb >= RB || m >= p.M || KIND == EPI_QKV || KIND == EPI_CACHE) continue;
+    if (KIND == EPI_GEGLU) {
+#pragma unroll
+      for (int j = 0; j < NB; j += 2) {
+        const int n = tn * BN + j * 16;
+        if (n >= p.N) break;  // N % 32 == 0: a gate block in range has its up block
+        const int f = (n >> 1) + cq;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = gelu_erf(acc[i][j][e]) * acc[i][j + 1][e];
+        const Epilogue& E = p.epi;
+        if (E.out_f32) {
+          *(f32x4_t*)((float*)E.out + (long)m * E.ldo + f) = f32x4_t{v[0], v[1], v[2], v[3]};
+        } else {
+          const long o = E.out_frag ? frag_idx(m, f, E.ldo) : (long)m * E.ldo + f;
+          *(u32x2_t*)((bf16_t*)E.out + o) = pack4_bf16(v[0], v[1], v[2], v[3]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int n = tn * BN + j * 16 + cq;
+        if (n >= p.N) break;
+        // copy out through VALU registers: storing the accumulator registers
+        // directly lets the register allocator move accumulators out of the
+        // accumulation registers, which costs copies in the main loop
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = acc[i][j][e];
+          asm volatile("" : "+v"(x[e]));
+        }
+        const f32x4_t v = f32x4_t{x[0], x[1], x[2], x[3]};
+        if (KIND == EPI_PARTIAL || KIND == EPI_STORE) {
+          // partials are an fp32 store into the split's [M][N] slab
+          const bool f32 = KIND == EPI_PARTIAL || p.epi.out_f32;
+          void* out = KIND == EPI_PARTIAL ? (void*)(p.ws + (long)split * p.M * p.N) : p.epi.out;
+          const long o = (long)m * (KIND == EPI_PARTIAL ? p.N : p.epi.ldo) + n;
+          if (f32) *(f32x4_t*)((float*)out + o) = v;
+          else *(u32x2_t*)((bf16_t*)out + o) = pack4_bf16(v[0], v[1], v[2], v[3]);
+        } else if (KIND == EPI_RESID) {
+          f32x4_t* r = (f32x4_t*)(p.epi.resid + (long)m * p.epi.ldr + n);
+          *r = *r + v;
+        }
+      }
+    }
+  }
+  if (KIND == EPI_QKV || KIND == EPI_CACHE) {
+    // element-wise scatters: a row block's accumulators go through this wave's
+    // quarter of the (now idle) LDS so the store loop can stay rolled
+    float* st = (float*)&sw[0][0][0] + w * (NB * 4 * 64);
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      const int rb = w + 4 * i;
+      const int m = tm * kFragBM + rb * 16 + (lane & 15);
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = acc[i][j][e];
+          asm volatile("" : "+v"(x));
+          st[(j * 4 + e) * 64 + lane] = x;
+        }
+      if (rb < RB && m < p.M) {
+#pragma unroll 1
+        for (int j = 0; j < NB; ++j) {
+          const int n = tn * BN + j * 16 + cq;
+          if (n >= p.N) break;
+#pragma unroll 1
+          for (int e = 0; e < 4; ++e) epi_store_t<KIND>(p.epi, m, n + e, st[(j * 4 + e) * 64 + lane]);
+        }
+      }
+    }
+  }
+}
+
+// K is cut into chunks of an even number of 64-wide slices (the kernel runs
+// slices in pairs; only the last chunk may hold an odd count); `splits` <= 0
+// asks for a count that fills the chip, about one workgroup per CU with at
+// least 4 slices each.
+// Tile width: 64 columns for the small square products (two workgroups then
+// share a CU, and the grid reaches the CU count with fewer K splits), 128 else.
+static int frag_bn(int N, int K) { return (N <= 2048 && K <= 2048) ? 64 : 128; }
+
+static int frag_per(int M, int N, int K, int splits, int bn) {
+  const int pairs = (K / 64 + 1) / 2;
+  if (splits <= 0) {
+    const int tiles = (M + kFragBM - 1) / kFragBM * ((N + bn - 1) / bn);
+    splits = 1;
+    while (tiles * splits < 256 && pairs / (2 * splits) >= 2 && 2 * splits <= 16) splits *= 2;
+  }
+  splits = std::max(1, std::min(splits, pairs));
+  return (pairs + splits - 1) / splits;  // pairs per chunk
+}
+
+int gemm_frag_splits(int M, int N, int K, int splits) {
+  if (K < 64) return 1;
+  const int per = frag_per(M, N, K, splits, frag_bn(N, K));
+  return ((K / 64 + 1) / 2 + per - 1) / per;
+}
+
+template <bool ODD, int BN>
+static hipError_t launch_af(const FragP& p, int kind, dim3 grid, hipStream_t s) {
+  switch (kind) {
+    case EPI_STORE: hipLaunchKernelGGL((k_gemm_af<EPI_STORE, ODD, BN>), grid, dim3(256), 0, s, p); break;
+    case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_af<EPI_GEGLU, ODD, BN>), grid, dim3(256), 0, s, p); break;
+    case EPI_PARTIAL: hipLaunchKernelGGL((k_gemm_af<EPI_PARTIAL, ODD, BN>), grid, dim3(256), 0, s, p); break;
+    case EPI_QKV: hipLaunchKernelGGL((k_gemm_af<EPI_QKV, ODD, BN>), grid, dim3(256), 0, s, p); break;
+    case EPI_CACHE: hipLaunchKernelGGL((k_gemm_af<EPI_CACHE, ODD, BN>), grid, dim3(256), 0, s, p); break;
+    case EPI_RESID: hipLaunchKernelGGL((k_gemm_af<EPI_RESID, ODD, BN>), grid, dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t gemm_frag(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, const Epilogue& epi, int splits,
+                     float* ws, hipStream_t s) {
+  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  if (K % 64 || N % 32) return hipErrorInvalidValue;
+  const int kind0 = epi.kind;
+  if ((kind0 == EPI_STORE || kind0 == EPI_GEGLU) && epi.ldo % 4) return hipErrorInvalidValue;
+  if (kind0 == EPI_RESID && epi.ldr % 4) return hipErrorInvalidValue;
+  if (epi.out_frag && kind0 != EPI_GEGLU && kind0 != EPI_CACHE) return hipErrorInvalidValue;
+  if (epi.out_frag && epi.out_f32) return hipErrorInvalidValue;
+  const int bn = frag_bn(N, K);
+  const int per = frag_per(M, N, K, splits, bn);
+  splits = ((K / 64 + 1) / 2 + per - 1) / per;
+  if ((splits > 1 || kind0 == EPI_PARTIAL) && !ws) return hipErrorInvalidValue;
+  FragP p{Af, Wf, M, N, K, 0, 0, 0, epi, ws};
+  p.nM = (M + kFragBM - 1) / kFragBM;
+  p.nN = (N + bn - 1) / bn;
+  p.kchunk = per * 128;
+  const dim3 grid(p.nM * p.nN * splits);
+  const int kind = splits > 1 ? EPI_PARTIAL : kind0;
+  const bool odd = (K / 64) % 2;
+  hipError_t err = bn == 64 ? (odd ? launch_af<true, 64>(p, kind, grid, s) : launch_af<false, 64>(p, kind, grid, s))
+                            : (odd ? launch_af<true, 128>(p, kind, grid, s) : launch_af<false, 128>(p, kind, grid, s));
+  if (err != hipSuccess) return err;
+  if (splits > 1 && kind0 != EPI_PARTIAL) {
+    const long total = (long)M * N;
+    const int blocks = (int)std::min<long>((total + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, (const float*)ws, splits, M, N, epi);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
 // Split count that fills the chip for an M x N x K product on the tiles
 // gemm_bf16 picks: about two workgroups per CU, at least 4 K slices of 64 each.
 int gemm_bf16_auto_splits(int M, int N, int K) {
@@ -627,6 +942,7 @@ static hipError_t launch_chunk_mb(const ChunkP& p, int kind, dim3 grid, hipStrea
     case EPI_GEGLU: hipLaunchKernelGGL((k_chunk<2, MB, EPI_GEGLU>), grid, dim3(256), 0, s, p); break;
     case EPI_STORE: hipLaunchKernelGGL((k_chunk<1, MB, EPI_STORE>), grid, dim3(256), 0, s, p); break;
     case EPI_QKV: hipLaunchKernelGGL((k_chunk<1, MB, EPI_QKV>), grid, dim3(256), 0, s, p); break;
+    case EPI_CACHE: hipLaunchKernelGGL((k_chunk<1, MB, EPI_CACHE>), grid, dim3(256), 0, s, p); break;
     case EPI_PARTIAL: hipLaunchKernelGGL((k_chunk<1, MB, EPI_PARTIAL>), grid, dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
@@ -637,16 +953,16 @@ hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int 
                       float* ws, hipStream_t s) {
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
   if (M > 64 || K % 32 || N % 32) return hipErrorInvalidValue;
-  if (epi.kind != EPI_STORE && epi.kind != EPI_PARTIAL && epi.kind != EPI_GEGLU && epi.kind != EPI_QKV)
+  if (epi.kind != EPI_STORE && epi.kind != EPI_PARTIAL && epi.kind != EPI_GEGLU && epi.kind != EPI_QKV &&
+      epi.kind != EPI_CACHE)
     return hipErrorInvalidValue;
   int used, per;
   skinny_plan(K, splits, &used, &per);
-  if (epi.kind == EPI_GEGLU && used > 1) return hipErrorInvalidValue;  // GeGLU needs whole sums
   if (used > 1 && !ws) return hipErrorInvalidValue;
   ChunkP p{Af, Wf, M, N, K, per * 32, epi, ws};
-  const int nb = epi.kind == EPI_GEGLU ? 2 : 1;
+  const bool reduce = used > 1 && epi.kind != EPI_PARTIAL;
+  const int nb = epi.kind == EPI_GEGLU && !reduce ? 2 : 1;
   const dim3 grid(N / (16 * nb), used);
-  const bool reduce = used > 1 && (epi.kind == EPI_STORE || epi.kind == EPI_QKV);
   const int kind = reduce ? EPI_PARTIAL : epi.kind;
   const int mb = (M + 15) / 16;
   hipError_t err = mb == 1 ? launch_chunk_mb<1>(p, kind, grid, s)

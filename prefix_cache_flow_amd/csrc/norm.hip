@@ -113,7 +113,7 @@ hipError_t resid_norm(float* h, int ldh, const float* part, int nsplit, int M, i
                       const Prefetch* prefetch) {
   const Prefetch pf = prefetch ? *prefetch : Prefetch{};
   if (pf.blocks < 0 || pf.blocks > 1024 || (pf.blocks && !pf.sink)) return hipErrorInvalidValue;
-  if (u_frag && (u_f32 || N % 32 || M > 64)) return hipErrorInvalidValue;
+  if (u_frag && (u_f32 || N % 32)) return hipErrorInvalidValue;
   if (M <= 0) return hipSuccess;
   if (nsplit > 16) return hipErrorInvalidValue;
   const int per = (N + 255) / 256;

@@ -351,6 +351,34 @@ static vla_status build_weights(vla_model* m, const vla_weights* w, hipStream_t 
       return st;         \
     }                    \
   } while (0)
+  // Every bf16 projection is assembled row-major in a staging buffer and stored
+  // in the MFMA fragment layout (kernels.h, frag_pack): every weight load of a
+  // wave is then one contiguous 1 KB.
+  const int64_t ncache = (int64_t)c.L_e * 2 * kve;
+  void* stage = nullptr;
+  if (!m->f32) {
+    int64_t big = std::max<int64_t>(std::max<int64_t>(qkve, 2 * (int64_t)c.F_e) * c.d_e, (int64_t)c.d_e * std::max<int64_t>(qe, c.F_e));
+    big = std::max<int64_t>(big, ncache * c.d_p);
+    if (!m->w2a8)
+      big = std::max<int64_t>(big, std::max<int64_t>(std::max<int64_t>(qkvw, 2 * (int64_t)c.F_p) * c.d_p,
+                                                     (int64_t)c.d_p * std::max<int64_t>(qw, c.F_p)));
+    if (hipMalloc(&stage, big * es) != hipSuccess) {
+      (void)hipGetLastError();
+      cleanup();
+      return fail(VLA_ERR_OUT_OF_MEMORY, "staging");
+    }
+    temps.push_back(stage);
+  }
+  // rows x cols assembled by `fill` (row-major) into a new allocation, fragment layout in bf16
+  auto packed_weight = [&](void** dst, int64_t rows, int64_t cols, auto fill) -> vla_status {
+    vla_status r = dev_alloc(m, dst, rows * cols * es);
+    if (r != VLA_OK) return r;
+    if (m->f32) return fill(*dst);
+    r = fill(stage);
+    if (r != VLA_OK) return r;
+    HIP_TRY(frag_pack((const uint16_t*)stage, (int)rows, (int)cols, (uint16_t*)*dst, s));
+    return VLA_OK;
+  };
   m->pl.resize(c.L_p);
   for (int l = 0; l < c.L_p; ++l) {
     PrefixLayer& P = m->pl[l];
@@ -364,16 +392,16 @@ static vla_status build_weights(vla_model* m, const vla_weights* w, hipStream_t 
     const void* wu = src.t[src.i++];
     const void* wd = src.t[src.i++];
     if (!m->w2a8) {
-      TRY(dev_alloc(m, &P.wqkv, qkvw * c.d_p * es));
-      TRY(put_rows(m, P.wqkv, 0, wq, qw, c.d_p, s));
-      TRY(put_rows(m, P.wqkv, qw, wk, kvw, c.d_p, s));
-      TRY(put_rows(m, P.wqkv, qw + kvw, wv, kvw, c.d_p, s));
-      TRY(dev_alloc(m, &P.wo, (int64_t)c.d_p * qw * es));
-      TRY(put_rows(m, P.wo, 0, wo, c.d_p, qw, s));
-      TRY(dev_alloc(m, &P.wgu, 2 * (int64_t)c.F_p * c.d_p * es));
-      TRY(put_interleaved(P.wgu, wg, wu, c.F_p, c.d_p * es, s));
-      TRY(dev_alloc(m, &P.wd, (int64_t)c.d_p * c.F_p * es));
-      TRY(put_rows(m, P.wd, 0, wd, c.d_p, c.F_p, s));
+      TRY(packed_weight(&P.wqkv, qkvw, c.d_p, [&](void* d) {
+        vla_status r = put_rows(m, d, 0, wq, qw, c.d_p, s);
+        if (r == VLA_OK) r = put_rows(m, d, qw, wk, kvw, c.d_p, s);
+        if (r == VLA_OK) r = put_rows(m, d, qw + kvw, wv, kvw, c.d_p, s);
+        return r;
+      }));
+      TRY(packed_weight(&P.wo, c.d_p, qw, [&](void* d) { return put_rows(m, d, 0, wo, c.d_p, qw, s); }));
+      TRY(packed_weight(&P.wgu, 2 * (int64_t)c.F_p, c.d_p,
+                        [&](void* d) { return put_interleaved(d, wg, wu, c.F_p, c.d_p * es, s); }));
+      TRY(packed_weight(&P.wd, c.d_p, c.F_p, [&](void* d) { return put_rows(m, d, 0, wd, c.d_p, c.F_p, s); }));
     } else {
       const float bq = src.beta[src.bi++], bk = src.beta[src.bi++], bv = src.beta[src.bi++], bo = src.beta[src.bi++];
       const float bg = src.beta[src.bi++], bu = src.beta[src.bi++], bdn = src.beta[src.bi++];
@@ -423,27 +451,18 @@ static vla_status build_weights(vla_model* m, const vla_weights* w, hipStream_t 
   }
   TRY(put_gain(m, &m->w_pf, src.t[src.i++], c.d_p, s));
   // expert prefix-side projections, concatenated in boundary order: [l][k|v][h][d]
-  TRY(dev_alloc(m, &m->wcache, (int64_t)c.L_e * 2 * kve * c.d_p * es));
-  for (int e = 0; e < c.L_e; ++e) {
-    TRY(put_rows(m, m->wcache, (int64_t)(2 * e) * kve, src.t[src.i++], kve, c.d_p, s));
-    TRY(put_rows(m, m->wcache, (int64_t)(2 * e + 1) * kve, src.t[src.i++], kve, c.d_p, s));
-  }
+  TRY(packed_weight(&m->wcache, ncache, c.d_p, [&](void* d) {
+    vla_status r = VLA_OK;
+    for (int e = 0; e < c.L_e && r == VLA_OK; ++e) {
+      r = put_rows(m, d, (int64_t)(2 * e) * kve, src.t[src.i++], kve, c.d_p, s);
+      if (r == VLA_OK) r = put_rows(m, d, (int64_t)(2 * e + 1) * kve, src.t[src.i++], kve, c.d_p, s);
+    }
+    return r;
+  }));
   TRY(dev_alloc(m, &m->w_in, (int64_t)c.d_e * c.d_a * es));
   TRY(put_rows(m, m->w_in, 0, src.t[src.i++], c.d_e, c.d_a, s));
-  // Expert projections.  In bf16 they are assembled row-major in a staging
-  // buffer and stored in the MFMA fragment layout (kernels.h, frag_pack): the
-  // chunk has few rows, so these GEMMs are weight streams and every weight load
-  // is then one contiguous 1 KB per wave.
-  void* stage = nullptr;
-  if (!m->f32) {
-    const int64_t big = std::max<int64_t>(std::max<int64_t>(qkve, 2 * (int64_t)c.F_e) * c.d_e, (int64_t)c.d_e * std::max<int64_t>(qe, c.F_e));
-    if (hipMalloc(&stage, big * es) != hipSuccess) {
-      (void)hipGetLastError();
-      cleanup();
-      return fail(VLA_ERR_OUT_OF_MEMORY, "staging");
-    }
-    temps.push_back(stage);
-  }
+  // Expert projections (fragment layout in bf16, like the prefix): the chunk
+  // has few rows, so these GEMMs are weight streams.
   // all expert projections in one allocation, layer by layer
   auto rnd = [](int64_t b) { return (b + 255) / 256 * 256; };
   const int64_t shapes[6][2] = {{qkve, c.d_e}, {c.d_e, qe}, {qe, c.d_e}, {c.d_e, qe}, {2 * (int64_t)c.F_e, c.d_e}, {c.d_e, c.F_e}};
@@ -606,11 +625,19 @@ static const int kExpertSplits = 4;
 
 // Split-K counts: the one place that fixes them for a GEMM and for the row
 // kernel (or reduction) that sums its partials.
+static const int kPrefixChunkSplits = 4;  // split request of the chunk-sized kernel
 static int prefix_splits(int64_t M, int N, int K) {
-  return gemm_bf16_splits(K, gemm_bf16_auto_splits((int)M, N, K), (int)M);
+  return M <= 64 ? gemm_bf16_splits(K, kPrefixChunkSplits, (int)M) : gemm_frag_splits((int)M, N, K, 0);
 }
 static int expert_splits(int64_t M, int N, int K) {
-  return M <= 64 ? gemm_bf16_splits(K, kExpertSplits, (int)M) : prefix_splits(M, N, K);
+  return gemm_bf16_splits(K, M <= 64 ? kExpertSplits : gemm_bf16_auto_splits((int)M, N, K), (int)M);
+}
+// bf16 product with both operands in the fragment layout: the chunk-sized
+// kernel up to 64 rows, 288-row tiles above; split counts as prefix_splits
+static hipError_t mm_frag(const void* A, const void* W, int64_t M, int N, int K, const Epilogue& e, float* ws,
+                          hipStream_t s) {
+  if (M <= 64) return gemm_chunk((const uint16_t*)A, (const uint16_t*)W, (int)M, N, K, e, kPrefixChunkSplits, ws, s);
+  return gemm_frag((const uint16_t*)A, (const uint16_t*)W, (int)M, N, K, e, 0, ws, s);
 }
 // floats of split-K partials the prefix (rows tokens) and the expert (erows chunk rows) need
 static int64_t prefix_part_floats(const vla_model_config& c, int64_t rows) {
@@ -648,13 +675,17 @@ static WS plan(const vla_model* m, int64_t rows, int64_t erows, int64_t kvrows, 
   WS w{};
   const int64_t qkvw = (int64_t)(c.Hq + 2 * c.Hkv) * c.hd, qw = (int64_t)c.Hq * c.hd;
   const int64_t act_es = m->w2a8 ? 4 : es;  // ternary: fp32 attention / GeGLU outputs feed the quantizer
+  // bf16 GEMM inputs are in the fragment layout, whole 16-row blocks (at
+  // least 64 rows for the chunk-sized kernel); the ternary prefix keeps fp32 rows
+  const int64_t prow = m->f32 ? rows : std::max<int64_t>(64, (rows + 15) / 16 * 16);
+  const int64_t arow = m->w2a8 ? rows : prow;
   w.h = (float*)take(rows * c.d_p * 4);
-  w.u = take(rows * std::max<int64_t>(c.d_p, c.d_e) * es);
+  w.u = take(prow * std::max<int64_t>(c.d_p, c.d_e) * es);
   w.qkv = take(rows * qkvw * es);
   w.pk = take(kvrows * c.Hkv * c.hd * es);
   w.pv = take(kvrows * c.Hkv * c.hd * es);
-  w.attn = take(rows * qw * act_es);
-  w.mlp = take(rows * (int64_t)c.F_p * act_es);
+  w.attn = take(arow * qw * act_es);
+  w.mlp = take(arow * (int64_t)c.F_p * act_es);
   if (m->w2a8) {
     w.qa = (int8_t*)take(rows * std::max<int64_t>(std::max<int64_t>(c.d_p, qw), c.F_p));
     w.alpha = (float*)take(rows * 4);
@@ -800,9 +831,10 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
   aa.o = w.attn; aa.o_bs = (long)N * qw; aa.o_rs = qw;
   aa.B = B; aa.Nq = N; aa.Nk = N; aa.Hq = c.Hq; aa.Hkv = c.Hkv; aa.hd = c.hd;
   aa.o_f32 = (m->f32 || m->w2a8) ? 1 : 0;
-  // bf16 above 64 rows: the fused projection writes query rows and the keys and
-  // values in the MFMA operand orders, read by the chunk-style attention kernel
-  const bool kvfrag = !m->f32 && !m->w2a8 && M > 64;
+  // bf16: the fused projection writes query rows and the keys and values in the
+  // MFMA operand orders, read by the chunk-style attention kernel, which writes
+  // its output in the fragment layout for the O projection
+  const bool kvfrag = !m->f32 && !m->w2a8;
   const int Np = (int)key_rows(m, N);
   Epilogue qkv_e = epi_store(w.qkv, qkvw, 0);
   if (kvfrag) {
@@ -811,6 +843,7 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
     aa.q_bs = (long)N * qw; aa.q_rs = qw;
     aa.k = w.pk; aa.k_bs = (long)c.Hkv * Np * c.hd; aa.k_hs = (long)Np * c.hd;
     aa.v = w.pv; aa.v_bs = aa.k_bs; aa.v_hs = aa.k_hs;
+    aa.o_frag = 1;
     if (Np > N) {  // padding key rows: finite values (zero weights times values)
       K_TRY(zero_tails(w.pk, (long)B * c.Hkv, (long)Np * c.hd, 32 * c.hd, s), "key padding");
       K_TRY(zero_tails(w.pv, (long)B * c.Hkv, (long)Np * c.hd, 32 * c.hd, s), "value padding");
@@ -840,10 +873,11 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
         K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, m->pl[l + 1].w1, eps, nullptr, 0, 0, w.qa, w.alpha, s),
               "norm");
       else
-        K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, m->w_pf, eps, w.u, 0, c.d_p, nullptr, nullptr, s), "norm");
+        K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, m->w_pf, eps, w.u, 0, c.d_p, nullptr, nullptr, s, 1), "norm");
     }
   } else {
-    K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, m->pl[0].w1, eps, w.u, uf, c.d_p, nullptr, nullptr, s), "norm");
+    K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, m->pl[0].w1, eps, w.u, uf, c.d_p, nullptr, nullptr, s, uf ? 0 : 1),
+          "norm");
     for (int l = 0; l < c.L_p; ++l) {
       const PrefixLayer& P = m->pl[l];
       const float* next_gain = l + 1 < c.L_p ? m->pl[l + 1].w1 : m->w_pf;
@@ -860,37 +894,37 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
         K_TRY(gemm_f32((const float*)w.mlp, c.F_p, (const float*)P.wd, c.F_p, M, c.d_p, c.F_p, r, s), "down");
         K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, next_gain, eps, w.u, 1, c.d_p, nullptr, nullptr, s), "norm");
       } else {
-        const uint16_t* u = (const uint16_t*)w.u;
+        // every GEMM input in the fragment layout: u from the row kernels, the
+        // attention output, the GeGLU output
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_QKV, s);
-          K_TRY(gemm_bf16(u, c.d_p, (const uint16_t*)P.wqkv, c.d_p, M, qkvw, c.d_p, qkv_e,
-                          prefix_splits(M, qkvw, c.d_p), w.part, s), "qkv");
+          K_TRY(mm_frag(w.u, P.wqkv, M, qkvw, c.d_p, qkv_e, w.part, s), "qkv");
         }
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_ATTN, s);
-          K_TRY(kvfrag ? attention_chunk(aa, s) : attention_bf16(aa, s), "attention");
+          K_TRY(attention_chunk(aa, s), "attention");
         }
         Epilogue pe;
         pe.kind = EPI_PARTIAL;
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_O, s);
-          K_TRY(gemm_bf16((const uint16_t*)w.attn, qw, (const uint16_t*)P.wo, qw, M, c.d_p, qw, pe,
-                          prefix_splits(M, c.d_p, qw), w.part, s), "o proj");
+          K_TRY(mm_frag(w.attn, P.wo, M, c.d_p, qw, pe, w.part, s), "o proj");
         }
-        K_TRY(resid_norm(w.h, c.d_p, w.part, prefix_splits(M, c.d_p, qw), M, c.d_p, P.w2, eps, w.u, 0, c.d_p, nullptr, nullptr, s), "norm");
+        K_TRY(resid_norm(w.h, c.d_p, w.part, prefix_splits(M, c.d_p, qw), M, c.d_p, P.w2, eps, w.u, 0, c.d_p, nullptr,
+                         nullptr, s, 1), "norm");
         Epilogue g = epi_store(w.mlp, c.F_p, 0);
         g.kind = EPI_GEGLU;
+        g.out_frag = 1;
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_GATEUP, s);
-          K_TRY(gemm_bf16(u, c.d_p, (const uint16_t*)P.wgu, c.d_p, M, 2 * c.F_p, c.d_p, g, prefix_splits(M, 2 * c.F_p, c.d_p),
-                          w.part, s), "gate/up");
+          K_TRY(mm_frag(w.u, P.wgu, M, 2 * c.F_p, c.d_p, g, w.part, s), "gate/up");
         }
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_DOWN, s);
-          K_TRY(gemm_bf16((const uint16_t*)w.mlp, c.F_p, (const uint16_t*)P.wd, c.F_p, M, c.d_p, c.F_p, pe,
-                          prefix_splits(M, c.d_p, c.F_p), w.part, s), "down");
+          K_TRY(mm_frag(w.mlp, P.wd, M, c.d_p, c.F_p, pe, w.part, s), "down");
         }
-        K_TRY(resid_norm(w.h, c.d_p, w.part, prefix_splits(M, c.d_p, c.F_p), M, c.d_p, next_gain, eps, w.u, 0, c.d_p, nullptr, nullptr, s), "norm");
+        K_TRY(resid_norm(w.h, c.d_p, w.part, prefix_splits(M, c.d_p, c.F_p), M, c.d_p, next_gain, eps, w.u, 0, c.d_p,
+                         nullptr, nullptr, s, 1), "norm");
       }
     }
   }
@@ -908,8 +942,7 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
   if (m->f32)
     K_TRY(gemm_f32((const float*)w.u, c.d_p, (const float*)m->wcache, c.d_p, M, ncache, c.d_p, ce, s), "cache");
   else
-    K_TRY(gemm_bf16((const uint16_t*)w.u, c.d_p, (const uint16_t*)m->wcache, c.d_p, M, ncache, c.d_p, ce,
-                    prefix_splits(M, ncache, c.d_p), w.part, s), "cache");
+    K_TRY(mm_frag(w.u, m->wcache, M, ncache, c.d_p, ce, w.part, s), "cache");
   return VLA_OK;
 }
 
