@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
   const u32x4_t* Kf = (const u32x4_t*)((const bf16_t*)a.k + b * a.k_bs + g * a.k_hs) + lane;
   const u32x4_t* Vf = (const u32x4_t*)((const bf16_t*)a.v + b * a.v_bs + g * a.v_hs) + lane;
   const int T = (a.Nk + 31) / 32;
-  const int NI = (T + 3) / 4;  // tiles per wave (the same for all waves; tiles past T are fully masked)
+  const int NI = T > w ? (T - 1 - w) / 4 + 1 : 0;  // tiles of this wave (w, w + 4, ...)
 
   struct Tile { u32x4_t k[2 * KS], v[VS]; };
   auto fetch = [&](Tile& t, int tl) {
@@ -271,8 +271,6 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
 #pragma unroll
   for (int s = 0; s < KS; ++s) qf[s] = *(const u32x4_t*)(Qp + s * 32 + grp * 8);
   Tile ta, tb;
-  fetch(ta, w);
-  fetch(tb, w + 4);
 
   f32x4_t o[VS];
 #pragma unroll
@@ -325,13 +323,41 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
     for (int t2 = 0; t2 < VS; ++t2) o[t2] = mfma16x16x32(as_bf16x8(t.v[t2]), pf, o[t2]);
   };
 
-  // tile w + 4 i is consumed from ta (even i) or tb (odd i) while the next is in flight
-  for (int i = 0; i < NI; i += 2) {
-    consume(ta, w + 4 * i);
-    fetch(ta, w + 4 * (i + 2));
-    if (i + 1 >= NI) break;
-    consume(tb, w + 4 * (i + 1));
-    fetch(tb, w + 4 * (i + 3));
+  // Tile w + 4 i is consumed from ta (even i) or tb (odd i) while the next is
+  // in flight.  A wave fetches only tiles it owns: the kernel's time is largely
+  // the bytes one CU pulls through its L1, and with up to three tiles per wave
+  // (up to 384 keys) each count has its own straight-line schedule, since
+  // branches around the fetches inside one loop cost the compiler registers.
+  switch (NI) {
+    case 0: break;
+    case 1:
+      fetch(ta, w);
+      consume(ta, w);
+      break;
+    case 2:
+      fetch(ta, w);
+      fetch(tb, w + 4);
+      consume(ta, w);
+      consume(tb, w + 4);
+      break;
+    case 3:
+      fetch(ta, w);
+      fetch(tb, w + 4);
+      consume(ta, w);
+      fetch(ta, w + 8);
+      consume(tb, w + 4);
+      consume(ta, w + 8);
+      break;
+    default:  // longer key sets: the last fetches of each buffer are clamped repeats
+      fetch(ta, w);
+      fetch(tb, w + 4);
+      for (int i = 0; i < NI; i += 2) {
+        consume(ta, w + 4 * i);
+        fetch(ta, w + 4 * (i + 2));
+        if (i + 1 >= NI) break;
+        consume(tb, w + 4 * (i + 1));
+        fetch(tb, w + 4 * (i + 3));
+      }
   }
 
   // merge the four waves' (max, sum, unnormalised O) in wave order
