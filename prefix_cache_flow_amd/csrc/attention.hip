@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
   const int G = a.Hq / a.Hkv, R = G * a.Nq;
   const int nrb = (R + 15) / 16;
   if ((int)blockIdx.x >= nrb) {  // extra workgroups (first batch and group only): warm the next weights
-    if (blockIdx.y == 0 && blockIdx.z == 0) prefetch_share(a.pf, blockIdx.x - nrb, gridDim.x - nrb);
+    if (blockIdx.y == 0 && blockIdx.z == 0) prefetch_share(a.pf, blockIdx.x, nrb, gridDim.x - nrb);
     return;
   }
   const int g = blockIdx.y, b = blockIdx.z;

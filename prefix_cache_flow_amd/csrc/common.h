@@ -153,24 +153,56 @@ __host__ __device__ __forceinline__ long vfrag_idx(int t, int d, int D) {
 
 // Workgroup `blk` of `nblk` reads its share of the ranges, 16 loads of 16 bytes
 // per thread in flight, and folds them so the loads are kept.
-__device__ __forceinline__ void prefetch_share(const Prefetch& f, int blk, int nblk) {
+// Extra workgroups [first, first + count) of a kernel (linear ids) read the
+// byte ranges of `f` once and drop them, so the kernel after finds them in
+// cache: a range without a group is shared by all of them; a grouped range is
+// read XCD by XCD (see Prefetch), each workgroup taking a share of the groups
+// of its own XCD (linear id % 8); groups that are not a power of two in size
+// are read like ungrouped ranges.  Sixteen 16-byte loads per thread are in
+// flight at a time.  Ranges are below 32 GB.
+__device__ __forceinline__ void prefetch_share(const Prefetch& f, int L, int first, int count) {
   constexpr int U = 16;
-  const long n = (long)(f.bytes >> 4), n2 = (long)(f.bytes2 >> 4), tot = n + n2;
-  const u32x4_t* p = (const u32x4_t*)f.p;
-  const u32x4_t* p2 = (const u32x4_t*)f.p2;
-  const long stride = (long)nblk * blockDim.x;
+  const int c = L & 7;
+  const int fc = first + ((c - first) & 7);                      // first prefetch workgroup on this XCD
+  const int nc = fc < first + count ? (first + count - 1 - fc) / 8 + 1 : 1;
+  const int rc = (L - fc) >> 3;
   unsigned x = 0;
-  for (long base = (long)blk * blockDim.x + threadIdx.x; base < tot; base += stride * U) {
-    u32x4_t v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const long i = min(base + u * stride, tot - 1);
-      v[u] = *(i < n ? p + i : p2 + (i - n));
+  auto range = [&](const void* p, size_t bytes, size_t group) {
+    if (!p || bytes < 16) return;
+    const u32x4_t* v = (const u32x4_t*)p;
+    // vector i of this workgroup's share maps to v[(i >> sh) * jump + (i & mk)]:
+    // groups of 2^sh vectors, of which every eighth is this XCD's (jump = 8
+    // groups, starting at group c), or the whole range (sh = 31)
+    uint32_t n, part, stride, sh = 31, mk = 0xffffffffu;
+    size_t jump = 0;
+    const u32x4_t* v0 = v;
+    if (group >= 16 && !(group & (group - 1))) {
+      sh = 31 - __builtin_clz((uint32_t)(group >> 4));
+      mk = (1u << sh) - 1;
+      const uint32_t ng = (uint32_t)(bytes / group);
+      n = ng > (uint32_t)c ? (((ng - 1 - c) >> 3) + 1) << sh : 0;  // vectors of the groups c, c + 8, ...
+      jump = (size_t)8 << sh;
+      v0 = v + ((size_t)c << sh);
+      part = rc; stride = nc;
+    } else {
+      n = (uint32_t)(bytes >> 4);
+      part = L - first; stride = count;
     }
+    const uint32_t step = stride * blockDim.x;
+    for (uint32_t base = part * blockDim.x + threadIdx.x; base < n; base += step * U) {
+      u32x4_t t[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) x ^= v[u][0] ^ v[u][3];
-  }
-  if (x == 0x9E3779B9u) f.sink[blk & 63] = x;
+      for (int u = 0; u < U; ++u) {
+        const uint32_t i = min(base + u * step, n - 1);
+        t[u] = v0[(i >> sh) * jump + (i & mk)];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) x ^= t[u][0] ^ t[u][3];
+    }
+  };
+  range(f.p, f.bytes, f.group);
+  range(f.p2, f.bytes2, f.group2);
+  if (x == 0x9E3779B9u) f.sink[L & 63] = x;
 }
 
 // acc row index of element i for lane l in a 32x32 MFMA block

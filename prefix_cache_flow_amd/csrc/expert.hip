@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void k_step_rows(StepRows a) {
   __shared__ float xs[256];
   const int m = blockIdx.x;
   if (m >= a.M) {  // extra workgroups: warm the next kernel's weights
-    prefetch_share(a.pf, m - a.M, gridDim.x - a.M);
+    prefetch_share(a.pf, m, a.M, gridDim.x - a.M);
     return;
   }
   const int tid = threadIdx.x;

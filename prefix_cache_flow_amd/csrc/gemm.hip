@@ -978,6 +978,15 @@ hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int 
   return err;
 }
 
+size_t gemm_chunk_group_bytes(int M, int N, int K, int kind, int splits) {
+  if (M > 64 || K % 32 || N % 32) return 0;
+  int used, per;
+  skinny_plan(K, splits, &used, &per);
+  const int nb = kind == EPI_GEGLU && used == 1 ? 2 : 1;
+  const int gx = N / (16 * nb);
+  return gx % 8 ? 0 : (size_t)nb * 16 * K * 2;
+}
+
 // row-major [N][K] -> fragment layout, one 16-byte vector (8 k) per thread
 __global__ void k_frag_pack(const u32x4_t* src, int N, int K, uint16_t* dst) {
   const long vecs = (long)N * (K / 8);

@@ -10,11 +10,15 @@ namespace vla {
 // Two byte ranges that extra workgroups of a short kernel read once and drop,
 // so that the next kernel (which streams them) finds them in the memory-side
 // cache instead of waiting on HBM.  `blocks` workgroups are added to the grid.
+// With group > 0 a range is read XCD by XCD: the consuming kernel's workgroup
+// for column group g of `group` bytes runs on XCD g % 8 (workgroups go to the
+// eight XCDs round robin), so the extra workgroups on XCD c read the groups
+// g = c (mod 8) into that XCD's L2, where the consumer finds them.
 struct Prefetch {
   const void* p = nullptr;
-  size_t bytes = 0;
+  size_t bytes = 0, group = 0;
   const void* p2 = nullptr;
-  size_t bytes2 = 0;
+  size_t bytes2 = 0, group2 = 0;
   unsigned* sink = nullptr;  // 64 words, written only for an impossible value
   int blocks = 0;
 };
@@ -91,6 +95,10 @@ int gemm_bf16_splits(int K, int splits, int M);
 // gemm_bf16.
 hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, const Epilogue& epi,
                       int splits, float* ws, hipStream_t s);
+// Bytes of fragment-layout weight that one column group of gemm_chunk reads
+// (the workgroup grid's x index), or 0 when the groups do not map to XCDs
+// round robin (grid width not a multiple of 8): the `group` of a Prefetch.
+size_t gemm_chunk_group_bytes(int M, int N, int K, int kind, int splits);
 // row-major bf16 [N][K] -> fragment layout (N % 16 == 0, K % 32 == 0)
 hipError_t frag_pack(const uint16_t* src, int N, int K, uint16_t* dst, hipStream_t s);
 

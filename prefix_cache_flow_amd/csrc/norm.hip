@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void k_resid_norm(float* h, int ldh, const flo
   __shared__ float red[4];
   const int m = blockIdx.x;
   if (m >= M) {  // extra workgroups: warm the next kernel's weights
-    prefetch_share(pf, m - M, gridDim.x - M);
+    prefetch_share(pf, m, M, gridDim.x - M);
     return;
   }
   float x[PER];

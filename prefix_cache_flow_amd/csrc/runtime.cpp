@@ -1053,16 +1053,25 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
   const int S_o = expert_splits(M, c.d_e, qe), S_d = expert_splits(M, c.d_e, c.F_e);
   // Each short kernel of the chain (embed, norms, attention) gets extra
   // workgroups that read the weights of the GEMM after it once, so that GEMM
-  // finds them in the memory-side cache: its weight loads then cost a cache hit
-  // instead of an HBM round trip, while the short kernel's own work hides the
-  // read.  Only for the fragment path (batch-1 sized chunks).
+  // finds them in cache: its weight loads then cost an L2 hit instead of an
+  // HBM round trip, while the short kernel's own work hides the read.  Only
+  // for the fragment path (batch-1 sized chunks).
   const size_t b_qkv = (size_t)qkve * c.d_e * es, b_o = (size_t)c.d_e * qe * es, b_q = (size_t)qe * c.d_e * es;
   const size_t b_gu = (size_t)2 * c.F_e * c.d_e * es, b_d = (size_t)c.d_e * c.F_e * es;
   const size_t layer_kv = (size_t)layer_stride * es;
-  auto pfr = [&](const void* p, size_t bytes, const void* p2, size_t bytes2, int blocks) {
+  // Weight ranges are read XCD by XCD, in the column groups of the GEMM that
+  // consumes them, so each lands in the L2 its consumer's workgroups read from.
+  const size_t g_qkv = gemm_chunk_group_bytes(M, qkve, c.d_e, EPI_QKV, 1);
+  const size_t g_o = gemm_chunk_group_bytes(M, c.d_e, qe, EPI_PARTIAL, S_o);
+  const size_t g_q = gemm_chunk_group_bytes(M, qe, c.d_e, EPI_STORE, 1);
+  const size_t g_gu = gemm_chunk_group_bytes(M, 2 * c.F_e, c.d_e, EPI_GEGLU, 1);
+  const size_t g_d = gemm_chunk_group_bytes(M, c.d_e, c.F_e, EPI_PARTIAL, S_d);
+  auto pfr = [&](const void* p, size_t bytes, size_t group, const void* p2, size_t bytes2, size_t group2, int blocks) {
     Prefetch f;
     if (!fr) return f;
-    f.p = p; f.bytes = bytes; f.p2 = p2; f.bytes2 = p2 ? bytes2 : 0; f.sink = w.sink; f.blocks = blocks;
+    f.p = p; f.bytes = bytes; f.group = group;
+    f.p2 = p2; f.bytes2 = p2 ? bytes2 : 0; f.group2 = p2 ? group2 : 0;
+    f.sink = w.sink; f.blocks = blocks;
     return f;
   };
   // row kernel between steps: head of step k - 1 (if any) fused with the embedding of step k (if any)
@@ -1072,7 +1081,7 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
     a.gain_f = m->w_ef; a.w_out = m->w_out; a.w_in = m->w_in; a.gain_1 = m->el[0].a1;
     a.u = w.eu; a.u_f32 = f32 ? 1 : 0; a.u_frag = fr; a.sched = m->sched_dev;
     a.k_head = k_head; a.k_embed = k_embed;
-    if (k_embed >= 0) a.pf = pfr(m->el[0].wqkv, b_qkv, nullptr, 0, 64);
+    if (k_embed >= 0) a.pf = pfr(m->el[0].wqkv, b_qkv, g_qkv, nullptr, 0, 0, 64);
     return step_rows(a, f32 ? 1 : 0, s);
   };
   for (int k = 0; k < steps; ++k) {
@@ -1106,17 +1115,17 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
           return gemm_bf16((const uint16_t*)A, lda, (const uint16_t*)W, K, M, N, K, ep, splits, w.epart, s, 1);
         };
         K_TRY(mm(u, c.d_e, L.wqkv, qkve, c.d_e, qkv_e, fr ? 1 : expert_splits(M, qkve, c.d_e)), "qkv_s");
-        sa.pf = pfr(L.wos, b_o, nullptr, 0, 192);
+        sa.pf = pfr(L.wos, b_o, g_o, nullptr, 0, 0, 192);
         K_TRY(attention_chunk(sa, s), "self attn");
         K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
-        const Prefetch pf_qc = pfr(L.wqc, b_q, B == 1 ? ca.k : nullptr, layer_kv, 192);
+        const Prefetch pf_qc = pfr(L.wqc, b_q, g_q, B == 1 ? ca.k : nullptr, layer_kv, 0, 192);
         K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_qc),
               "norm");
         K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, epi_store(w.eq, qe, 0), fr ? 1 : expert_splits(M, qe, c.d_e)), "q_c");
-        ca.pf = pfr(L.woc, b_o, L.wd, b_d, 192);
+        ca.pf = pfr(L.woc, b_o, g_o, L.wd, b_d, g_d, 192);
         K_TRY(attention_chunk(ca, s), "cross attn");
         K_TRY(mm(w.eattn, qe, L.woc, c.d_e, qe, pe, S_o), "o_c");
-        const Prefetch pf_gu = pfr(L.wgu, b_gu, nullptr, 0, 192);
+        const Prefetch pf_gu = pfr(L.wgu, b_gu, g_gu, nullptr, 0, 0, 192);
         K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_gu),
               "norm");
         Epilogue g = epi_store(w.emlp, c.F_e, 0);
@@ -1124,7 +1133,7 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
         g.out_frag = fr;
         K_TRY(mm(u, c.d_e, L.wgu, 2 * c.F_e, c.d_e, g, fr ? 1 : expert_splits(M, 2 * c.F_e, c.d_e)), "gate/up");
         K_TRY(mm(w.emlp, c.F_e, L.wd, c.d_e, c.F_e, pe, S_d), "down");
-        const Prefetch pf_next = e + 1 < c.L_e ? pfr(m->el[e + 1].wqkv, b_qkv, nullptr, 0, 192) : Prefetch{};
+        const Prefetch pf_next = e + 1 < c.L_e ? pfr(m->el[e + 1].wqkv, b_qkv, g_qkv, nullptr, 0, 0, 192) : Prefetch{};
         K_TRY(resid_norm(w.E, c.d_e, w.epart, S_d, M, c.d_e, e + 1 < c.L_e ? m->el[e + 1].a1 : m->w_ef, eps,
                          e + 1 < c.L_e ? w.eu : nullptr, 0, c.d_e, nullptr, nullptr, s, fr, &pf_next), "norm");
       }
