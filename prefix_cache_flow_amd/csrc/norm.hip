@@ -15,17 +15,26 @@
 
 namespace vla {
 
+// Element i of a thread's row share: column threadIdx.x + 256 i, or with VEC
+// (rows of a multiple of 1024 columns) column 4 (threadIdx.x + 256 (i / 4)) +
+// i % 4, so that each thread moves 16-byte vectors.
+template <bool VEC>
+__device__ __forceinline__ int row_col(int i) {
+  return VEC ? (((int)threadIdx.x + (i >> 2) * 256) << 2) + (i & 3) : (int)threadIdx.x + i * 256;
+}
+
+template <bool VEC = false>
 __device__ __forceinline__ void quantize_store(const float* x, int per, int N, int8_t* q, float* alpha_out,
                                                float* red) {
   float am = 0.f;
   for (int i = 0; i < per; ++i) {
-    const int n = threadIdx.x + i * 256;
+    const int n = row_col<VEC>(i);
     if (n < N) am = fmaxf(am, fabsf(x[i]));
   }
   am = block_max<256>(am, red);
   const float alpha = fmaxf(am, 1e-5f) / 127.0f;
   for (int i = 0; i < per; ++i) {
-    const int n = threadIdx.x + i * 256;
+    const int n = row_col<VEC>(i);
     if (n < N) {
       const float c = rintf(x[i] / alpha);
       q[n] = (int8_t)fminf(fmaxf(c, -128.f), 127.f);
@@ -36,70 +45,94 @@ __device__ __forceinline__ void quantize_store(const float* x, int per, int N, i
 
 // NS is a compile-time bound on the split count: every load of the row and of
 // its partials is issued before any is used (partials past nsplit re-read the
-// last one at a valid address and are masked out).
-template <int PER, int NS>
+// last one at a valid address and are masked out).  VEC: see row_col.
+template <int PER, int NS, bool VEC>
 __global__ __launch_bounds__(256) void k_resid_norm(float* h, int ldh, const float* part, int nsplit, int M, int N,
                                                     const float* gain, float eps, void* u, int u_f32, int ldu,
                                                     int8_t* q, float* alpha, int u_frag, Prefetch pf) {
+  static_assert(!VEC || PER % 4 == 0, "vector rows");
   __shared__ float red[4];
   const int m = blockIdx.x;
   if (m >= M) {  // extra workgroups: warm the next kernel's weights
     prefetch_share(pf, m, M, gridDim.x - M);
     return;
   }
+  constexpr int G = VEC ? 4 : 1;  // consecutive columns per access
   float x[PER];
   float pv[NS > 0 ? NS : 1][PER];
   float ss = 0.f;
+  auto load = [&](const float* row, float* dst) {
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int n = min(threadIdx.x + i * 256, N - 1);
-    x[i] = h[(long)m * ldh + n];
-  }
+    for (int i = 0; i < PER; i += G) {
+      if (VEC) {
+        const f32x4_t v = *(const f32x4_t*)(row + row_col<true>(i));
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int n = min(threadIdx.x + i * 256, N - 1);
-      pv[s][i] = part[((long)min(s, nsplit - 1) * M + m) * N + n];
+        for (int j = 0; j < 4; ++j) dst[i + j] = v[j];
+      } else {
+        dst[i] = row[min(row_col<false>(i), N - 1)];
+      }
     }
+  };
+  load(h + (long)m * ldh, x);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) load(part + ((long)min(s, nsplit - 1) * M + m) * N, pv[s]);
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int i = 0; i < PER; ++i) x[i] += s < nsplit ? pv[s][i] : 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int n = threadIdx.x + i * 256;
-    if (n >= N) x[i] = 0.f;
-    if (NS > 0 && n < N) h[(long)m * ldh + n] = x[i];
+    if (row_col<VEC>(i) >= N) x[i] = 0.f;
     ss = fmaf(x[i], x[i], ss);
+  }
+  if (NS > 0) {
+#pragma unroll
+    for (int i = 0; i < PER; i += G) {
+      const int n = row_col<VEC>(i);
+      if (VEC) *(f32x4_t*)(h + (long)m * ldh + n) = f32x4_t{x[i], x[i + 1], x[i + 2], x[i + 3]};
+      else if (n < N) h[(long)m * ldh + n] = x[i];
+    }
   }
   ss = block_sum<256>(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)N + eps);
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int n = threadIdx.x + i * 256;
-    if (n < N) x[i] = x[i] * r * (1.0f + gain[n]);
+  for (int i = 0; i < PER; i += G) {
+    const int n = row_col<VEC>(i);
+    if (VEC) {
+      const f32x4_t gv = *(const f32x4_t*)(gain + n);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[i + j] = x[i + j] * r * (1.0f + gv[j]);
+    } else if (n < N) {
+      x[i] = x[i] * r * (1.0f + gain[n]);
+    }
   }
   if (u) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int n = threadIdx.x + i * 256;
-      if (n < N) {
+    for (int i = 0; i < PER; i += G) {
+      const int n = row_col<VEC>(i);
+      if (VEC) {
+        if (u_f32) {
+          *(f32x4_t*)((float*)u + (long)m * ldu + n) = f32x4_t{x[i], x[i + 1], x[i + 2], x[i + 3]};
+        } else {
+          const long o = u_frag ? frag_idx(m, n, N) : (long)m * ldu + n;
+          *(u32x2_t*)((bf16_t*)u + o) = u32x2_t{pack_bf2(x[i], x[i + 1]), pack_bf2(x[i + 2], x[i + 3])};
+        }
+      } else if (n < N) {
         if (u_f32) ((float*)u)[(long)m * ldu + n] = x[i];
         else ((bf16_t*)u)[u_frag ? frag_idx(m, n, N) : (long)m * ldu + n] = f2bf(x[i]);
       }
     }
   }
-  if (q) quantize_store(x, PER, N, q + (long)m * N, alpha + m, red);
+  if (q) quantize_store<VEC>(x, PER, N, q + (long)m * N, alpha + m, red);
 }
 
-template <int PER>
+template <int PER, bool VEC>
 static void launch_rn(int nsplit, hipStream_t s, float* h, int ldh, const float* part, int M, int N,
                       const float* gain, float eps, void* u_out, int u_f32, int ldu, int8_t* q_out, float* alpha_out,
                       int u_frag, const Prefetch& pf) {
 #define VLA_RN(NS)                                                                                                  \
-  hipLaunchKernelGGL((k_resid_norm<PER, NS>), dim3(M + pf.blocks), dim3(256), 0, s, h, ldh, part, nsplit, M, N, gain, \
-                     eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf)
+  hipLaunchKernelGGL((k_resid_norm<PER, NS, VEC>), dim3(M + pf.blocks), dim3(256), 0, s, h, ldh, part, nsplit, M, N, \
+                     gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf)
   if (nsplit <= 0) VLA_RN(0);
   else if (nsplit <= 1) VLA_RN(1);
   else if (nsplit <= 4) VLA_RN(4);
@@ -117,13 +150,19 @@ hipError_t resid_norm(float* h, int ldh, const float* part, int nsplit, int M, i
   if (M <= 0) return hipSuccess;
   if (nsplit > 16) return hipErrorInvalidValue;
   const int per = (N + 255) / 256;
-  if (per <= 1) launch_rn<1>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf);
-  else if (per <= 2) launch_rn<2>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf);
-  else if (per <= 4) launch_rn<4>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf);
-  else if (per <= 8) launch_rn<8>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf);
-  else if (per <= 12) launch_rn<12>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf);
-  else if (per <= 16) launch_rn<16>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf);
+  // 16-byte row accesses for rows of a multiple of 1024 columns with aligned strides
+  const bool vec = N % 1024 == 0 && ldh % 4 == 0 && (!u_out || ldu % 4 == 0);
+#define VLA_RNP(P)                                                                                                \
+  (vec ? launch_rn<P, true>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf) \
+       : launch_rn<P, false>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf))
+  if (per <= 1) launch_rn<1, false>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf);
+  else if (per <= 2) launch_rn<2, false>(nsplit, s, h, ldh, part, M, N, gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf);
+  else if (per <= 4) VLA_RNP(4);
+  else if (per <= 8) VLA_RNP(8);
+  else if (per <= 12) VLA_RNP(12);
+  else if (per <= 16) VLA_RNP(16);
   else return hipErrorInvalidValue;
+#undef VLA_RNP
   return hipGetLastError();
 }
 
