@@ -88,11 +88,28 @@ __device__ __forceinline__ void epi_geglu(const Epilogue& e, int m, int f, float
   if (e.out_f32) ((float*)e.out)[i] = v; else ((bf16_t*)e.out)[i] = f2bf(v);
 }
 
-// Fixed-order sum of split-K partials followed by the epilogue.
+// Fixed-order sum of split-K partials followed by the epilogue.  Except for
+// GeGLU (which pairs columns 16 apart), a thread takes four consecutive
+// columns of a row with 16-byte partial loads (N % 4 == 0 for every caller).
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* ws, int splits, int M, int N, Epilogue e) {
-  const long total = (e.kind == EPI_GEGLU) ? (long)M * (N / 2) : (long)M * N;
+  if (e.kind != EPI_GEGLU) {
+    const long total4 = (long)M * N / 4, slab = (long)M * N;
+    for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total4; i += (long)gridDim.x * blockDim.x) {
+      f32x4_t v = *(const f32x4_t*)(ws + 4 * i);
+      for (int s = 1; s < splits; ++s) v += *(const f32x4_t*)(ws + s * slab + 4 * i);
+      const int m = (int)(4 * i / N), n = (int)(4 * i % N);
+      if (e.kind == EPI_STORE && !e.out_f32) {
+        *(u32x2_t*)((bf16_t*)e.out + (long)m * e.ldo + n) = u32x2_t{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) epi_store(e, m, n + j, v[j]);
+      }
+    }
+    return;
+  }
+  const long total = (long)M * (N / 2);
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total; i += (long)gridDim.x * blockDim.x) {
-    if (e.kind == EPI_GEGLU) {
+    {
       const int F = N / 2;
       const int m = (int)(i / F), f = (int)(i % F);
       const int ng = (f >> 4) * 32 + (f & 15), nu = ng + 16;
@@ -102,11 +119,6 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* ws, int spli
         u += ws[((long)s * M + m) * N + nu];
       }
       epi_geglu(e, m, f, g, u);
-    } else {
-      const int m = (int)(i / N), n = (int)(i % N);
-      float v = 0.f;
-      for (int s = 0; s < splits; ++s) v += ws[((long)s * M + m) * N + n];
-      epi_store(e, m, n, v);
     }
   }
 }
@@ -255,7 +267,7 @@ static hipError_t launch_skinny(const SkinnyP& p0, int splits, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (used > 1 && p.epi.kind != EPI_PARTIAL) {
-    const long tot = (long)p.M * p.N;
+    const long tot = (long)p.M * p.N / 4;
     const int blocks = (int)std::min<long>((tot + 255) / 256, 4096);
     hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, (const float*)p.ws, used, p.M, p.N, p.epi);
     err = hipGetLastError();
@@ -477,7 +489,7 @@ static hipError_t launch_ws(const GemmP& p, int splits, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (used > 1 && p.epi.kind != EPI_PARTIAL) {
-    const long total = (long)p.M * p.N;
+    const long total = (long)p.M * p.N / 4;
     const int blocks = (int)std::min<long>((total + 255) / 256, 4096);
     hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, (const float*)p.ws, used, p.M, p.N, p.epi);
     err = hipGetLastError();
@@ -791,7 +803,7 @@ hipError_t gemm_frag(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K
                             : (odd ? launch_af<true, 128>(p, kind, grid, s) : launch_af<false, 128>(p, kind, grid, s));
   if (err != hipSuccess) return err;
   if (splits > 1 && kind0 != EPI_PARTIAL) {
-    const long total = (long)M * N;
+    const long total = (long)M * N / 4;
     const int blocks = (int)std::min<long>((total + 255) / 256, 4096);
     hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, (const float*)ws, splits, M, N, epi);
     err = hipGetLastError();
@@ -970,7 +982,7 @@ hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int 
                            : launch_chunk_mb<4>(p, kind, grid, s);
   if (err != hipSuccess) return err;
   if (reduce) {
-    const long tot = (long)M * N;
+    const long tot = (long)M * N / 4;
     const int blocks = (int)std::min<long>((tot + 255) / 256, 4096);
     hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, (const float*)ws, used, M, N, epi);
     err = hipGetLastError();
