@@ -1051,11 +1051,15 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
   Epilogue pe;
   pe.kind = EPI_PARTIAL;
   const int S_o = expert_splits(M, c.d_e, qe), S_d = expert_splits(M, c.d_e, c.F_e);
-  // Each short kernel of the chain (embed, norms, attention) gets extra
-  // workgroups that read the weights of the GEMM after it once, so that GEMM
-  // finds them in cache: its weight loads then cost an L2 hit instead of an
-  // HBM round trip, while the short kernel's own work hides the read.  Only
-  // for the fragment path (batch-1 sized chunks).
+  // The short kernels of the chain (row kernel, attention, norms) get extra
+  // workgroups that read the weights of the GEMMs ahead once, so those GEMMs
+  // find them in cache: a weight load then costs an L2 hit instead of an HBM
+  // round trip, while the short kernel's own work hides the read.  The
+  // attention kernels run longest with the fewest workgroups of their own, so
+  // they carry most of it: self attention reads the O and cross-query weights,
+  // cross attention the cross O and gate/up weights; the norms read the
+  // layer's cache block, the down weights and the next layer's QKV weights.
+  // Only for the fragment path (batch-1 sized chunks).
   const size_t b_qkv = (size_t)qkve * c.d_e * es, b_o = (size_t)c.d_e * qe * es, b_q = (size_t)qe * c.d_e * es;
   const size_t b_gu = (size_t)2 * c.F_e * c.d_e * es, b_d = (size_t)c.d_e * c.F_e * es;
   const size_t layer_kv = (size_t)layer_stride * es;
@@ -1115,18 +1119,18 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
           return gemm_bf16((const uint16_t*)A, lda, (const uint16_t*)W, K, M, N, K, ep, splits, w.epart, s, 1);
         };
         K_TRY(mm(u, c.d_e, L.wqkv, qkve, c.d_e, qkv_e, fr ? 1 : expert_splits(M, qkve, c.d_e)), "qkv_s");
-        sa.pf = pfr(L.wos, b_o, g_o, nullptr, 0, 0, 192);
+        sa.pf = pfr(L.wos, b_o, g_o, L.wqc, b_q, g_q, 192);
         K_TRY(attention_chunk(sa, s), "self attn");
         K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
-        const Prefetch pf_qc = pfr(L.wqc, b_q, g_q, B == 1 ? ca.k : nullptr, layer_kv, 0, 192);
-        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_qc),
+        const Prefetch pf_kv = pfr(B == 1 ? ca.k : nullptr, B == 1 ? layer_kv : 0, 0, nullptr, 0, 0, 64);
+        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_kv),
               "norm");
         K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, epi_store(w.eq, qe, 0), fr ? 1 : expert_splits(M, qe, c.d_e)), "q_c");
-        ca.pf = pfr(L.woc, b_o, g_o, L.wd, b_d, g_d, 192);
+        ca.pf = pfr(L.woc, b_o, g_o, L.wgu, b_gu, g_gu, 192);
         K_TRY(attention_chunk(ca, s), "cross attn");
         K_TRY(mm(w.eattn, qe, L.woc, c.d_e, qe, pe, S_o), "o_c");
-        const Prefetch pf_gu = pfr(L.wgu, b_gu, g_gu, nullptr, 0, 0, 192);
-        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_gu),
+        const Prefetch pf_d = pfr(L.wd, b_d, g_d, nullptr, 0, 0, 192);
+        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_d),
               "norm");
         Epilogue g = epi_store(w.emlp, c.F_e, 0);
         g.kind = EPI_GEGLU;
