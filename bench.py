@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--config", type=int, default=1, help="workload index (1 = single camera bf16)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-s", type=float, default=30.0)
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the solver-step sweep and the two-stream pipelined run")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB mebibytes (reference for the HBM byte counters) and exit")
     return p.parse_args()
@@ -80,6 +82,83 @@ def expert_step_bytes(c):
     weights = c.L_e * per_layer + c.d_e * c.d_a * 2
     cache = c.batch * c.L_e * 2 * kve * c.n_prefix
     return 2 * (weights + cache)
+
+
+SWEEP_STEPS = (1, 2, 4, 8, 16)
+
+
+def solver_sweep(vla, model, zt, xt, kv_storage, reps=5):
+    """Eq. 3 measured: latency with the cache (one prefix pass, then T solver steps) against re-encoding the
+    prefix before every step, for T in SWEEP_STEPS, each the median of `reps` runs timed with the library's
+    HIP events.  L(T) = P + T E is fitted to the cached latencies; `ideal_speedup` is T (P + E) / (P + T E)."""
+    import torch
+    xa = torch.empty_like(xt)
+    xb = torch.empty_like(xt)
+    cached, recompute = [], []
+    for T in SWEEP_STEPS:
+        c, r = [], []
+        for _ in range(reps):
+            kv, tp = vla.vla_prefix_encode(model, zt, kv_storage=kv_storage, timing=True)
+            _, td = vla.vla_denoise_chunk(model, kv, xt, T, out=xa, timing=True)
+            kv.close()
+            c.append(tp["prefix_ms"] + td["denoise_ms"])
+            tot, x, y = 0.0, xt, xa
+            for k in range(T):
+                kv, tp = vla.vla_prefix_encode(model, zt, kv_storage=kv_storage, timing=True)
+                _, td = vla.vla_denoise_chunk(model, kv, x, 1, schedule=[k / T, (k + 1) / T], out=y, timing=True)
+                kv.close()
+                tot += tp["prefix_ms"] + td["denoise_ms"]
+                x, y = y, (xb if y is xa else xa)
+            r.append(tot)
+        cached.append(float(np.median(c)))
+        recompute.append(float(np.median(r)))
+    Ts = np.array(SWEEP_STEPS, dtype=np.float64)
+    E, P = np.polyfit(Ts, np.array(cached), 1)
+    return {"T": list(SWEEP_STEPS), "cached_ms": cached, "recompute_ms": recompute,
+            "speedup": [r / c for r, c in zip(recompute, cached)],
+            "fit": {"P_ms": float(P), "E_ms": float(E)},
+            "ideal_speedup": [float(T * (P + E) / (P + T * E)) for T in Ts]}
+
+
+def pipelined(vla, model, cfg, zt, xt, n, warmup=2):
+    """Observations back to back with the prefix pass of observation k + 1 on a second stream while the solver
+    of observation k runs (two cache buffers).  Returns chunks/s over n observations; every output is the same
+    as the serial run's (the test suite checks that bit for bit)."""
+    import torch
+    nbytes = vla.vla_kv_cache_bytes(model, cfg.batch, cfg.n_prefix)
+    store = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    outs = [torch.empty(xt.shape, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    sp, sd = torch.cuda.Stream(), torch.cuda.Stream()
+    enc = [torch.cuda.Event() for _ in range(2)]
+    dec = [torch.cuda.Event() for _ in range(2)]
+
+    def run(count):
+        kvs = [None, None]
+        kvs[0] = vla.vla_prefix_encode(model, zt, kv_storage=store[0], stream=sp)
+        enc[0].record(sp)
+        for k in range(count):
+            b = k % 2
+            if k + 1 < count:
+                nb = 1 - b
+                if k >= 1:
+                    sp.wait_event(dec[nb])  # the solver of observation k - 1 has read that cache
+                    kvs[nb].close()
+                kvs[nb] = vla.vla_prefix_encode(model, zt, kv_storage=store[nb], stream=sp)
+                enc[nb].record(sp)
+            sd.wait_event(enc[b])
+            vla.vla_denoise_chunk(model, kvs[b], xt, cfg.steps, out=outs[b], stream=sd)
+            dec[b].record(sd)
+        torch.cuda.synchronize()
+        for kv in kvs:
+            if kv is not None:
+                kv.close()
+
+    run(warmup)
+    t0 = time.perf_counter()
+    run(n)
+    el = time.perf_counter() - t0
+    return {"value": cfg.batch * n / el, "unit": "chunks/s", "observations": n,
+            "note": "prefix of observation k+1 overlapped with the solver of observation k on two streams"}
 
 
 def main():
@@ -168,6 +247,12 @@ def main():
                 "avg_launch_us": avg_ms * 1e3, "launches": probe_launches,
                 "flops_per_launch": flops_per_launch}
 
+    # ---- solver-step sweep (Eq. 3) and the two-stream pipelined rate: context, not the metric
+    extras = {}
+    if not args.no_extras:
+        extras["solver_sweep"] = solver_sweep(vla, model, zt, xt, kv_storage)
+        extras["pipelined_two_stream"] = pipelined(vla, model, cfg, zt, xt, max(args.steps, 10))
+
     # ---- CPU oracle on a bounded sample
     cpu = None
     if not args.no_cpu_baseline:
@@ -185,6 +270,7 @@ def main():
         "phases": phases,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        **extras,
     }
     print(json.dumps(rec), flush=True)
 

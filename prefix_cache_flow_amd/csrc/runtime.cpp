@@ -204,6 +204,8 @@ struct vla_model {
   float* sched_dev = nullptr;  // [max_steps + 1]
   float* sched_host = nullptr; // pinned staging
   int sched_cap = 0;
+  std::vector<float> sched_last;     // what sched_dev holds (empty: unknown)
+  hipStream_t sched_stream = nullptr;  // the stream that wrote it
   hipStream_t cap_stream = nullptr;
   // expert weights of all layers in one allocation, layer e at ew + e * ew_layer
   char* ew = nullptr;
@@ -1184,6 +1186,7 @@ extern "C" vla_status vla_denoise_chunk(vla_model* m, const vla_kv_cache* kv, co
       (void)hipHostFree(m->sched_host);
       m->sched_dev = nullptr;
       m->sched_host = nullptr;
+      m->sched_last.clear();
       for (auto& g : m->graphs) (void)hipGraphExecDestroy(g.second);
       m->graphs.clear();
     }
@@ -1194,11 +1197,20 @@ extern "C" vla_status vla_denoise_chunk(vla_model* m, const vla_kv_cache* kv, co
     }
     m->sched_cap = cap;
   }
-  // the pinned staging buffer may still feed an earlier copy on this stream
-  K_TRY(hipStreamSynchronize(s), "sync");
-  memcpy(m->sched_host, sched.data(), (steps + 1) * 4);
+  // The device schedule is uploaded only when it changes (or comes from
+  // another stream), so a repeated call neither waits on the host nor copies.
+  const bool upload = m->sched_stream != s || m->sched_last != sched;
+  if (upload) {
+    // the pinned staging buffer may still feed an earlier copy on this stream
+    K_TRY(hipStreamSynchronize(s), "sync");
+    memcpy(m->sched_host, sched.data(), (steps + 1) * 4);
+  }
   if (timing) K_TRY(hipEventRecord(m->ev0, s), "event");
-  K_TRY(hipMemcpyAsync(m->sched_dev, m->sched_host, (steps + 1) * 4, hipMemcpyHostToDevice, s), "schedule upload");
+  if (upload) {
+    K_TRY(hipMemcpyAsync(m->sched_dev, m->sched_host, (steps + 1) * 4, hipMemcpyHostToDevice, s), "schedule upload");
+    m->sched_last = sched;
+    m->sched_stream = s;
+  }
   const long nx = (long)kv->B * c.H * c.d_a;
   K_TRY(copy_f32(noise, w.X, nx, s), "noise in");
   int replayed = 0;

@@ -136,6 +136,50 @@ def test_cached_equals_recompute_on_gpu():
     model.close()
 
 
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_GQA], ids=lambda c: c.name)
+def test_two_stream_pipeline_matches_serial(cfg):
+    """Prefix passes on one stream overlapping solver runs on another (one model, two cache
+    buffers, the prefix of observation k + 1 beside the solver of observation k) give every
+    observation its serial result bit for bit."""
+    w, b, _, _ = host_inputs(cfg, 2)
+    model = build_model(cfg, w, b)
+    obs = [(torch.from_numpy(synth.make_prefix(cfg, 20 + i)).cuda(),
+            torch.from_numpy(synth.make_noise(cfg, 20 + i)).cuda()) for i in range(5)]
+    serial = []
+    for zt, xt in obs:
+        kv = vla.vla_prefix_encode(model, zt)
+        serial.append(vla.vla_denoise_chunk(model, kv, xt, cfg.steps).cpu().numpy())
+        kv.close()
+    nbytes = vla.vla_kv_cache_bytes(model, cfg.batch, cfg.n_prefix)
+    store = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    outs = [torch.empty(xt.shape, dtype=torch.float32, device="cuda") for _, xt in obs]
+    sp, sd = torch.cuda.Stream(), torch.cuda.Stream()
+    enc = [torch.cuda.Event() for _ in range(2)]
+    dec = [torch.cuda.Event() for _ in range(2)]
+    for rep in range(2):
+        kvs = [vla.vla_prefix_encode(model, obs[0][0], kv_storage=store[0], stream=sp), None]
+        enc[0].record(sp)
+        for k in range(len(obs)):
+            bb = k % 2
+            if k + 1 < len(obs):
+                nb = 1 - bb
+                if k >= 1:
+                    sp.wait_event(dec[nb])
+                    kvs[nb].close()
+                kvs[nb] = vla.vla_prefix_encode(model, obs[k + 1][0], kv_storage=store[nb], stream=sp)
+                enc[nb].record(sp)
+            sd.wait_event(enc[bb])
+            vla.vla_denoise_chunk(model, kvs[bb], obs[k][1], cfg.steps, out=outs[k], stream=sd)
+            dec[bb].record(sd)
+        torch.cuda.synchronize()
+        for kv in kvs:
+            kv.close()
+        for k in range(len(obs)):
+            np.testing.assert_array_equal(outs[k].cpu().numpy(), serial[k], err_msg=f"rep {rep} observation {k}")
+            outs[k].zero_()
+    model.close()
+
+
 def test_bidirectional_first_token_sees_last_on_gpu():
     cfg = synth.config(1, n_prefix=64, d_p=128, L_p=1, Hq=2, Hkv=1, hd=64, F_p=256, d_e=128, L_e=1, Hq_e=2,
                        Hkv_e=1, hd_e=64, F_e=128, H=4, d_a=4, steps=1)
