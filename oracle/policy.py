@@ -23,6 +23,18 @@ One observation at a time:
            E = E + GeGLU(RMS(E; a3))
        v = RMS(E; w_final) W_out^T
 
+Joint attention (the paper, §III-B: pi0 caches every layer's prefix keys and
+values, and joint-attention layers append the suffix's keys and values) is the
+other cache form.  The cache is the keys and values each prefix layer computes
+for itself, [(K_l, V_l)], with no final norm and no projection; expert layer l
+has one attention sublayer, whose keys are prefix layer l's followed by the
+chunk's own, in one softmax, then the MLP:
+           u = RMS(E; a1);  Q, K, V = u Wqs^T, u Wks^T, u Wvs^T
+           E = E + Attn(Q, [K_l; K], [V_l; V]; M = 0) Wos^T
+           E = E + GeGLU(RMS(E; a3))
+Prefix tokens never see the chunk (their keys and values come from the prefix
+pass alone): the block mask of the joint sequence.
+
 Readings where the pages are silent (the pages name none of these pieces):
   * RMS(x; w) = x / sqrt(mean(x^2) + eps) * (1 + w), pre-norm before every
     sublayer, eps = 1e-6;
@@ -156,8 +168,12 @@ class Oracle:
             return y.astype(self.dtype)
         return x @ self._w(name).T
 
+    def is_joint(self) -> bool:
+        return getattr(self.cfg, "attn", "cross") == "joint"
+
     # ---- phase 1: prefix
-    def prefix_layer(self, h, l: int):
+    def prefix_layer_kv(self, h, l: int):
+        """One prefix layer: (its output, its keys K, its values V)."""
         c, p = self.cfg, f"prefix.{l}."
         u = rms_norm(h, self._w(p + "w1"), c.rms_eps)
         q = self._plin(u, p + "wq")
@@ -166,7 +182,19 @@ class Oracle:
         h = h + self._plin(attention(q, k, v, c.Hq, c.Hkv, c.hd), p + "wo")
         u = rms_norm(h, self._w(p + "w2"), c.rms_eps)
         m = gelu(self._plin(u, p + "wg")) * self._plin(u, p + "wu")
-        return h + self._plin(m, p + "wd")
+        return h + self._plin(m, p + "wd"), k, v
+
+    def prefix_layer(self, h, l: int):
+        return self.prefix_layer_kv(h, l)[0]
+
+    def prefix_kv(self, z0) -> List[Tuple[np.ndarray, np.ndarray]]:
+        """Joint-attention cache: [(K_l, V_l)] of every prefix layer, each [N, Hkv * hd]."""
+        h = np.asarray(z0, dtype=self.dtype)
+        kv = []
+        for l in range(self.cfg.L_p):
+            h, k, v = self.prefix_layer_kv(h, l)
+            kv.append((k, v))
+        return kv
 
     def encode_prefix(self, z0):
         """Z = RMS(h_L; w_final) for one observation's prefix z0 [N, d_p]."""
@@ -181,6 +209,12 @@ class Oracle:
         return [(z @ self._w(f"cache.{e}.wk").T, z @ self._w(f"cache.{e}.wv").T)
                 for e in range(self.cfg.L_e)]
 
+    def conditioning(self, z0):
+        """The cached collection for one observation: projected final states, or per-layer prefix K/V."""
+        if self.is_joint():
+            return self.prefix_kv(z0)
+        return self.cache_project(self.encode_prefix(z0))
+
     # ---- phase 3: expert and solver
     def velocity(self, x, tau: float, cache):
         c = self.cfg
@@ -190,11 +224,15 @@ class Oracle:
             p = f"expert.{e}."
             u = rms_norm(e_, W(p + "a1"), c.rms_eps)
             q, k, v = u @ W(p + "wqs").T, u @ W(p + "wks").T, u @ W(p + "wvs").T
+            if self.is_joint():
+                kp, vp = cache[e]  # prefix layer e's keys and values, then the chunk's
+                k, v = np.concatenate([kp, k]), np.concatenate([vp, v])
             e_ = e_ + attention(q, k, v, c.Hq_e, c.Hkv_e, c.hd_e) @ W(p + "wos").T
-            u = rms_norm(e_, W(p + "a2"), c.rms_eps)
-            kc, vc = cache[e]
-            e_ = e_ + attention(u @ W(p + "wqc").T, kc, vc, c.Hq_e, c.Hkv_e,
-                                c.hd_e) @ W(p + "woc").T
+            if not self.is_joint():
+                u = rms_norm(e_, W(p + "a2"), c.rms_eps)
+                kc, vc = cache[e]
+                e_ = e_ + attention(u @ W(p + "wqc").T, kc, vc, c.Hq_e, c.Hkv_e,
+                                    c.hd_e) @ W(p + "woc").T
             u = rms_norm(e_, W(p + "a3"), c.rms_eps)
             e_ = e_ + (gelu(u @ W(p + "wg").T) * (u @ W(p + "wu").T)) @ W(p + "wd").T
         return rms_norm(e_, W("expert.norm"), c.rms_eps) @ W("expert.w_out").T
@@ -207,7 +245,7 @@ class Oracle:
     def denoise_recompute(self, z0, x0, schedule):
         """Same result, re-encoding the prefix and re-projecting the cache every step."""
         def v(x, tau):
-            return self.velocity(x, tau, self.cache_project(self.encode_prefix(z0)))
+            return self.velocity(x, tau, self.conditioning(z0))
         return euler_integrate(np.asarray(x0, dtype=self.dtype), schedule, v)
 
     def run(self, z0, x0, schedule=None, keep_cache: bool = False):
@@ -216,7 +254,7 @@ class Oracle:
             schedule = uniform_schedule(self.cfg.steps)
         outs, caches = [], []
         for b in range(np.shape(z0)[0]):
-            cache = self.cache_project(self.encode_prefix(z0[b]))
+            cache = self.conditioning(z0[b])
             outs.append(self.denoise(cache, x0[b], schedule))
             if keep_cache:
                 caches.append(cache)

@@ -63,6 +63,7 @@ class PolicyConfig:
     d_a: int
     steps: int
     rms_eps: float = 1e-6
+    attn: str = "cross"     # "cross" (projected final states, Eq. 2) or "joint" (per-layer prefix K/V)
 
     def to_dict(self) -> dict:
         return asdict(self)
@@ -122,12 +123,14 @@ def weight_specs(cfg: PolicyConfig) -> List[Tuple[str, Tuple[int, ...], str]]:
             (p + "wu", (cfg.F_p, cfg.d_p), lin_p),
             (p + "wd", (cfg.d_p, cfg.F_p), lin_p),
         ]
-    specs.append(("prefix.norm", (cfg.d_p,), "gain"))
-    for e in range(cfg.L_e):
-        specs += [
-            (f"cache.{e}.wk", (kve, cfg.d_p), "linear"),
-            (f"cache.{e}.wv", (kve, cfg.d_p), "linear"),
-        ]
+    joint = cfg.attn == "joint"
+    if not joint:
+        specs.append(("prefix.norm", (cfg.d_p,), "gain"))
+        for e in range(cfg.L_e):
+            specs += [
+                (f"cache.{e}.wk", (kve, cfg.d_p), "linear"),
+                (f"cache.{e}.wv", (kve, cfg.d_p), "linear"),
+            ]
     specs.append(("expert.w_in", (cfg.d_e, cfg.d_a), "linear"))
     for e in range(cfg.L_e):
         p = f"expert.{e}."
@@ -137,9 +140,14 @@ def weight_specs(cfg: PolicyConfig) -> List[Tuple[str, Tuple[int, ...], str]]:
             (p + "wks", (kve, cfg.d_e), "linear"),
             (p + "wvs", (kve, cfg.d_e), "linear"),
             (p + "wos", (cfg.d_e, qe), "linear"),
-            (p + "a2", (cfg.d_e,), "gain"),
-            (p + "wqc", (qe, cfg.d_e), "linear"),
-            (p + "woc", (cfg.d_e, qe), "linear"),
+        ]
+        if not joint:
+            specs += [
+                (p + "a2", (cfg.d_e,), "gain"),
+                (p + "wqc", (qe, cfg.d_e), "linear"),
+                (p + "woc", (cfg.d_e, qe), "linear"),
+            ]
+        specs += [
             (p + "a3", (cfg.d_e,), "gain"),
             (p + "wg", (cfg.F_e, cfg.d_e), "linear"),
             (p + "wu", (cfg.F_e, cfg.d_e), "linear"),

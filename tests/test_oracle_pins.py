@@ -381,6 +381,103 @@ def test_cached_equals_recompute_bitwise():
     np.testing.assert_array_equal(cached, o.denoise_recompute(z0, x0, sched))
 
 
+# ---------------------------------------------------------------- joint attention (pi0 form, §III-B)
+
+JOINT = synth.config(0, name="tiny_joint_fp32", attn="joint", n_prefix=20, H=6)
+
+
+def _masked_sequence_velocity(c, W, z0, x, tau):
+    """v(x, tau) from ONE transformer pass over the joint sequence [prefix; chunk]: prefix
+    rows use the backbone's weights, chunk rows the expert's, every layer attends over all
+    N + H keys with the block mask (prefix queries see no chunk key), then the head.  Written
+    out from the page's description of joint attention, independently of the oracle's cached
+    form (which keeps per-layer prefix K/V and appends the chunk's)."""
+    N, H = z0.shape[0], x.shape[0]
+    mask = np.zeros((N + H, N + H))
+    mask[:N, N:] = -np.inf
+    f = lambda n: W[n].astype(np.float64)
+    hp = z0.astype(np.float64)
+    he = x @ f("expert.w_in").T + oracle.time_embedding(tau, c.d_e)
+    for l in range(c.L_p):
+        p, e = f"prefix.{l}.", f"expert.{l}."
+        up, ue = oracle.rms_norm(hp, f(p + "w1"), c.rms_eps), oracle.rms_norm(he, f(e + "a1"), c.rms_eps)
+        q = np.concatenate([up @ f(p + "wq").T, ue @ f(e + "wqs").T])
+        k = np.concatenate([up @ f(p + "wk").T, ue @ f(e + "wks").T])
+        v = np.concatenate([up @ f(p + "wv").T, ue @ f(e + "wvs").T])
+        o = oracle.attention(q, k, v, c.Hq, c.Hkv, c.hd, mask=mask)
+        hp = hp + o[:N] @ f(p + "wo").T
+        he = he + o[N:] @ f(e + "wos").T
+        up, ue = oracle.rms_norm(hp, f(p + "w2"), c.rms_eps), oracle.rms_norm(he, f(e + "a3"), c.rms_eps)
+        hp = hp + (oracle.gelu(up @ f(p + "wg").T) * (up @ f(p + "wu").T)) @ f(p + "wd").T
+        he = he + (oracle.gelu(ue @ f(e + "wg").T) * (ue @ f(e + "wu").T)) @ f(e + "wd").T
+    return oracle.rms_norm(he, f("expert.norm"), c.rms_eps) @ f("expert.w_out").T
+
+
+def test_joint_cache_equals_block_masked_sequence():
+    """The cached joint form (per-layer prefix K/V, chunk keys appended) equals one masked pass
+    over the whole sequence, for every solver time: pins the cache contents (each layer's own
+    pre-attention keys and values), the concatenation and the joint layer's structure."""
+    c = JOINT
+    W, _ = synth.make_weights(c, 11)
+    z0, x = synth.make_prefix(c, 11)[0], synth.make_noise(c, 11)[0].astype(np.float64)
+    o = oracle.Oracle(c, W)
+    cache = o.conditioning(z0)
+    assert len(cache) == c.L_p and cache[0][0].shape == (c.n_prefix, c.Hkv * c.hd)
+    for tau in (0.0, 0.37, 1.0):
+        np.testing.assert_allclose(o.velocity(x, tau, cache), _masked_sequence_velocity(c, W, z0, x, tau),
+                                   rtol=1e-11, atol=1e-13)
+
+
+def test_joint_cache_is_each_layers_own_keys_and_values():
+    c = JOINT
+    W, _ = synth.make_weights(c, 12)
+    o = oracle.Oracle(c, W)
+    z0 = synth.make_prefix(c, 12)[0].astype(np.float64)
+    cache = o.prefix_kv(z0)
+    h = z0
+    for l in range(c.L_p):
+        u = oracle.rms_norm(h, W[f"prefix.{l}.w1"], c.rms_eps)
+        np.testing.assert_array_equal(cache[l][0], u @ W[f"prefix.{l}.wk"].astype(np.float64).T)
+        np.testing.assert_array_equal(cache[l][1], u @ W[f"prefix.{l}.wv"].astype(np.float64).T)
+        h = o.prefix_layer(h, l)
+
+
+def test_joint_attention_merges_prefix_and_chunk_softmaxes():
+    """Attention over [prefix keys; chunk keys] is the log-sum-exp merge of the two separate
+    attentions (one softmax over both sets, not two)."""
+    rng = np.random.default_rng(13)
+    hd, n, h = 32, 9, 5
+    q = rng.standard_normal((4, 2 * hd))
+    kp, vp = rng.standard_normal((n, hd)), rng.standard_normal((n, hd))
+    ks, vs = rng.standard_normal((h, hd)), rng.standard_normal((h, hd))
+    joint = oracle.attention(q, np.concatenate([kp, ks]), np.concatenate([vp, vs]), 2, 1, hd)
+    for j in range(2):
+        qj = q[:, j * hd:(j + 1) * hd] / math.sqrt(hd)
+        sp, ss = qj @ kp.T, qj @ ks.T
+        m = np.maximum(sp.max(1), ss.max(1))[:, None]
+        ap, as_ = np.exp(sp - m), np.exp(ss - m)
+        want = (ap @ vp + as_ @ vs) / (ap.sum(1) + as_.sum(1))[:, None]
+        np.testing.assert_allclose(joint[:, j * hd:(j + 1) * hd], want, rtol=1e-12, atol=1e-14)
+
+
+def test_joint_cached_equals_recompute_and_zero_velocity():
+    c = JOINT
+    W, _ = synth.make_weights(c, 14)
+    o = oracle.Oracle(c, W)
+    z0, x0 = synth.make_prefix(c, 14)[0], synth.make_noise(c, 14)[0]
+    sched = oracle.uniform_schedule(c.steps)
+    np.testing.assert_array_equal(o.denoise(o.conditioning(z0), x0, sched), o.denoise_recompute(z0, x0, sched))
+    W["expert.w_out"] = np.zeros_like(W["expert.w_out"])
+    np.testing.assert_array_equal(oracle.Oracle(c, W).run(z0[None], x0[None])[0], x0.astype(np.float64))
+
+
+def test_joint_weight_order_has_no_cross_attention_or_projection():
+    names = [n for n, _, _ in synth.weight_specs(JOINT)]
+    assert not any(n.startswith("cache.") or n == "prefix.norm" for n in names)
+    assert not any(n.endswith((".a2", ".wqc", ".woc")) for n in names)
+    assert len(names) == len(synth.weight_specs(synth.config(0))) - 1 - 2 * JOINT.L_e - 3 * JOINT.L_e
+
+
 def test_float32_vs_float64_self_consistency():
     c = synth.config(0)
     W, _ = synth.make_weights(c, 7)
