@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=1, help="workload index (1 = single camera bf16)")
+    p.add_argument("--attn", choices=("cross", "joint"), default="cross",
+                   help="cache form: projected final states (cross) or per-layer prefix K/V (joint, the pi0 form)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-s", type=float, default=30.0)
     p.add_argument("--no-extras", action="store_true",
@@ -65,12 +67,15 @@ def copy_calibration(mib):
 
 
 def prefix_flops(c):
-    """Algorithmic FLOPs of one prefix pass (+ cache projection) for one observation."""
+    """Algorithmic FLOPs of one prefix pass (+ cache projection) for one observation.  With joint
+    attention the cache is the layers' own K/V: no projection, and the last layer stops at its K/V."""
     N = c.n_prefix
     qkv = 2 * N * c.d_p * (c.Hq + 2 * c.Hkv) * c.hd
     attn = 4 * N * N * c.Hq * c.hd
     o = 2 * N * c.Hq * c.hd * c.d_p
     mlp = 2 * N * c.d_p * 2 * c.F_p + 2 * N * c.F_p * c.d_p
+    if c.attn == "joint":
+        return c.L_p * qkv + (c.L_p - 1) * (attn + o + mlp)
     cache = 2 * N * c.d_p * c.L_e * 2 * c.Hkv_e * c.hd_e
     return c.L_p * (qkv + attn + o + mlp) + cache
 
@@ -78,7 +83,8 @@ def prefix_flops(c):
 def expert_step_bytes(c):
     """Algorithmic HBM bytes of one denoise step: every expert weight once (bf16) plus the cache."""
     qe, kve = c.Hq_e * c.hd_e, c.Hkv_e * c.hd_e
-    per_layer = (qe + 2 * kve) * c.d_e + c.d_e * qe + qe * c.d_e + c.d_e * qe + 2 * c.F_e * c.d_e + c.d_e * c.F_e
+    cross = 0 if c.attn == "joint" else qe * c.d_e + c.d_e * qe  # cross-attention query and output
+    per_layer = (qe + 2 * kve) * c.d_e + c.d_e * qe + cross + 2 * c.F_e * c.d_e + c.d_e * c.F_e
     weights = c.L_e * per_layer + c.d_e * c.d_a * 2
     cache = c.batch * c.L_e * 2 * kve * c.n_prefix
     return 2 * (weights + cache)
@@ -178,6 +184,8 @@ def main():
 
     torch.cuda.set_device(0)
     cfg = synth.config(args.config)
+    if args.attn == "joint":
+        cfg = synth.config(args.config, attn="joint", name=cfg.name.replace("_bf16", "") + "_joint_bf16")
     t0 = time.time()
     w, betas = synth.make_weights(cfg, args.config)
     z0 = synth.make_prefix(cfg, args.config)
@@ -264,7 +272,7 @@ def main():
         "value": value, "unit": "chunks/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": cfg.name, "batch": cfg.batch, "prefix_tokens": cfg.n_prefix,
+        "config": {"workload": cfg.name, "attention": cfg.attn, "batch": cfg.batch, "prefix_tokens": cfg.n_prefix,
                    "prefix_layers": cfg.L_p, "d_prefix": cfg.d_p, "expert_layers": cfg.L_e, "d_expert": cfg.d_e,
                    "chunk": [cfg.H, cfg.d_a], "solver_steps": cfg.steps},
         "phases": phases,
@@ -291,15 +299,19 @@ def cpu_baseline(cfg, w, betas, z0, x0, budget_s):
     t0 = time.perf_counter()
     h = np.asarray(z0[0], dtype=np.float64)
     layers_done = 0
+    kv = []
     for l in range(cfg.L_p):
-        h = o.prefix_layer(h, l)
+        h, k, v = o.prefix_layer_kv(h, l)
+        kv.append((k, v))
         layers_done += 1
         if time.perf_counter() - t0 > budget_s / 2:
             break
     t_pre = (time.perf_counter() - t0) / layers_done * cfg.L_p
-    z = oracle.rms_norm(h, o._w("prefix.norm"), cfg.rms_eps)
     t1 = time.perf_counter()
-    cache = o.cache_project(z)
+    if cfg.attn == "joint":  # the layers' own K/V (layers not run reuse the last ones: timing only)
+        cache = [kv[min(l, len(kv) - 1)] for l in range(cfg.L_e)]
+    else:
+        cache = o.cache_project(oracle.rms_norm(h, o._w("prefix.norm"), cfg.rms_eps))
     t_cache = time.perf_counter() - t1
     x = np.asarray(x0[0], dtype=np.float64)
     sched = oracle.uniform_schedule(cfg.steps)
@@ -313,7 +325,8 @@ def cpu_baseline(cfg, w, betas, z0, x0, budget_s):
     t_step = (time.perf_counter() - t2) / steps_done
     t_chunk = t_pre + t_cache + cfg.steps * t_step
     return {"value": 1.0 / t_chunk, "unit": "chunks/s", "cores": threads, "kind": "oracle",
-            "sample": f"one observation: {layers_done} of {cfg.L_p} prefix layers, the cache projection and "
+            "sample": f"one observation: {layers_done} of {cfg.L_p} prefix layers, "
+                      f"{'the per-layer K/V' if cfg.attn == 'joint' else 'the cache projection'} and "
                       f"{steps_done} of {cfg.steps} solver steps run in float64 numpy, the rest extrapolated "
                       f"from the measured per-layer and per-step times",
             "seconds_measured": time.perf_counter() - t0,

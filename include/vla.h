@@ -13,6 +13,9 @@
  *     for unchanged shapes ............................... the paper, §III-B
  *   - cross-attention K_C = Z W_K, V_C = Z W_V, softmax(Q K_C^T/sqrt(d_k) + M) V_C
  *                                                          the paper, §III-B, Eq. 2
+ *   - joint attention: each prefix layer's own keys and values are the cache,
+ *     and the action tokens' keys and values are appended to them in one
+ *     softmax (the pi0 form) ............................. the paper, §III-B
  *   - Euler solver X^{k+1} = X^k + (tau_{k+1} - tau_k) v(X^k, tau_k)
  *                                                          the paper, §III-A, Eq. 1
  *   - bidirectional prefix mask; hidden states taken before the LM output
@@ -30,9 +33,13 @@
  *   - On any status other than VLA_OK no output buffer has been written.
  *   - The library never aborts or exits; vla_last_error() gives a per-thread
  *     message for the last failing call.
- *   - A model handle is not re-entrant: calls that use the same model (encode,
- *     denoise) must not run concurrently, on any streams, because they share
- *     the model's workspace.  Different models are independent.
+ *   - Calls on one model come from one host thread at a time.  On the device,
+ *     a prefix encode and a denoise of the same model may run concurrently on
+ *     different streams (they use separate parts of the model's workspace) if
+ *     they use different cache storage and neither asks for timings; two
+ *     encodes, or two denoises, of one model must not overlap.  A call that
+ *     has to grow the workspace (a larger batch or prefix than before)
+ *     synchronises the device first.  Different models are independent.
  */
 #ifndef VLA_H_
 #define VLA_H_
@@ -44,7 +51,7 @@
 extern "C" {
 #endif
 
-#define VLA_ABI_VERSION 1
+#define VLA_ABI_VERSION 2
 
 typedef enum {
   VLA_OK = 0,
@@ -64,6 +71,17 @@ typedef enum {
 
 typedef enum { VLA_OUT_F32 = 0, VLA_OUT_BF16 = 1 } vla_out_dtype;
 
+/* How the action expert reads the observation (the paper, §III-B).
+ * CROSS: the final prefix states Z are projected into per-expert-layer K_C, V_C
+ *   (Eq. 2), and every expert layer has self-attention over the chunk, then
+ *   cross-attention into its K_C, V_C, then the MLP.
+ * JOINT: the cache holds every prefix layer's own keys and values; expert layer
+ *   l attends, in one softmax, over prefix layer l's keys followed by the
+ *   chunk's own keys (prefix tokens never see the chunk: their keys and values
+ *   come from the prefix pass alone), then runs the MLP.  Needs L_e == L_p,
+ *   Hkv_e == Hkv, hd_e == hd and precision VLA_F32 or VLA_BF16. */
+typedef enum { VLA_ATTN_CROSS = 0, VLA_ATTN_JOINT = 1 } vla_attn_mode;
+
 /* Model shape.  Prefix: d_p wide, L_p layers, Hq query heads sharing Hkv
  * key/value heads of width hd, GeGLU width F_p.  Expert: the same fields with
  * suffix _e.  H x d_a is the action chunk (d_a <= 256).  Requirements:
@@ -78,6 +96,7 @@ typedef struct {
   int32_t d_e, L_e, Hq_e, Hkv_e, hd_e, F_e;
   int32_t H, d_a;
   float rms_eps;       /* RMSNorm epsilon, e.g. 1e-6 */
+  int32_t attn_mode;   /* vla_attn_mode */
 } vla_model_config;
 
 /* Weights, all linear layers [out, in] row-major (y = x W^T), in this order:
@@ -90,6 +109,9 @@ typedef struct {
  *       wvs[Hkv_e*hd_e, d_e] wos[d_e, Hq_e*hd_e] a2[d_e] wqc[Hq_e*hd_e, d_e]
  *       woc[d_e, Hq_e*hd_e] a3[d_e] wg[F_e, d_e] wu[F_e, d_e] wd[d_e, F_e]
  *   expert final norm gain [d_e], w_out[d_a, d_e]
+ * With VLA_ATTN_JOINT there is no prefix final norm, no cache projection and
+ * no cross-attention: the prefix layers as above, then w_in, then per expert
+ * layer a1 wqs wks wvs wos a3 wg wu wd, then the expert final norm and w_out.
  * RMSNorm gains ("w1", "a1", final norms ...) are float32 and applied as (1 + w).
  * Linear weights are float32 for VLA_F32 and bfloat16 otherwise, except that
  * with VLA_W2A8_BF16 the seven prefix linears of every layer (wq wk wv
@@ -147,7 +169,8 @@ vla_status vla_model_create(const vla_model_config* cfg, const vla_weights* weig
 vla_status vla_model_destroy(vla_model* model);
 
 /* Bytes of K/V cache storage for `batch` observations of `n_prefix` tokens:
- * blocks [batch][L_e][2 (K, V)][Hkv_e], each of Np x hd_e elements.
+ * blocks [batch][L_e][2 (K, V)][Hkv_e], each of Np x hd_e elements (with
+ * VLA_ATTN_JOINT, block l holds prefix layer l's keys and values).
  * VLA_F32: float32, Np = n_prefix, element (t, d) at t * hd_e + d.
  * Otherwise bfloat16 in the operand orders of the 16x16x32 MFMA, Np = n_prefix
  * rounded up to a multiple of 32 (padding rows hold zero):
@@ -162,7 +185,9 @@ size_t vla_kv_cache_bytes(const vla_model* model, int32_t batch, int32_t n_prefi
  * [batch][n_prefix][d_p], through L_p bidirectional layers and the final
  * RMSNorm, and projects the result into every expert layer's K and V, written
  * to `kv_storage` (device, caller-owned, >= vla_kv_cache_bytes bytes, layout as
- * above).  *out receives a handle that refers to kv_storage; it stays valid
+ * above).  With VLA_ATTN_JOINT each layer's keys and values go to the cache
+ * instead (the last layer stops after its keys and values: nothing reads the
+ * rest).  *out receives a handle that refers to kv_storage; it stays valid
  * until vla_kv_cache_release and may serve any number of denoise calls.
  * `timing` (nullable) receives prefix_ms and makes the call synchronise. */
 vla_status vla_prefix_encode(vla_model* model, const float* prefix_hidden, int32_t batch,

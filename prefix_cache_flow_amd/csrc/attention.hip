@@ -211,7 +211,7 @@ static hipError_t launch_attn16(const AttnArgs& a, hipStream_t s) {
 
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.Nq <= 0 || a.Nk <= 0) return hipSuccess;
-  if (a.Hq % a.Hkv) return hipErrorInvalidValue;
+  if (a.Hq % a.Hkv || a.Nk2) return hipErrorInvalidValue;  // one key source only
   if (a.o_frag && (a.o_f32 || a.B * a.Nq > 64)) return hipErrorInvalidValue;
   switch (a.hd) {
     case 64: return launch_attn16<64>(a, s);
@@ -255,16 +255,24 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
   const bf16_t* Qp = (const bf16_t*)a.q + b * a.q_bs + j * a.q_hs + (long)q * a.q_rs;
   const u32x4_t* Kf = (const u32x4_t*)((const bf16_t*)a.k + b * a.k_bs + g * a.k_hs) + lane;
   const u32x4_t* Vf = (const u32x4_t*)((const bf16_t*)a.v + b * a.v_bs + g * a.v_hs) + lane;
-  const int T = (a.Nk + 31) / 32;
+  // joint attention: the second source's tiles follow the first's
+  const u32x4_t* Kf2 = a.Nk2 ? (const u32x4_t*)((const bf16_t*)a.k2 + b * a.k2_bs + g * a.k2_hs) + lane : Kf;
+  const u32x4_t* Vf2 = a.Nk2 ? (const u32x4_t*)((const bf16_t*)a.v2 + b * a.v2_bs + g * a.v2_hs) + lane : Vf;
+  const int TA = (a.Nk + 31) / 32;
+  const int T = TA + (a.Nk2 + 31) / 32;
   const int NI = T > w ? (T - 1 - w) / 4 + 1 : 0;  // tiles of this wave (w, w + 4, ...)
 
   struct Tile { u32x4_t k[2 * KS], v[VS]; };
   auto fetch = [&](Tile& t, int tl) {
-    const int tile = min(tl, T - 1);
+    int tile = min(tl, T - 1);
+    const bool second = tile >= TA;
+    const u32x4_t* kp = second ? Kf2 : Kf;
+    const u32x4_t* vp = second ? Vf2 : Vf;
+    tile -= second ? TA : 0;
 #pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) t.k[i] = Kf[((long)tile * 2 * KS + i) * 64];
+    for (int i = 0; i < 2 * KS; ++i) t.k[i] = kp[((long)tile * 2 * KS + i) * 64];
 #pragma unroll
-    for (int i = 0; i < VS; ++i) t.v[i] = Vf[((long)tile * VS + i) * 64];
+    for (int i = 0; i < VS; ++i) t.v[i] = vp[((long)tile * VS + i) * 64];
   };
 
   u32x4_t qf[KS];
@@ -286,13 +294,14 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
       s0 = mfma16x16x32(as_bf16x8(t.k[s]), as_bf16x8(qf[s]), s0);
       s1 = mfma16x16x32(as_bf16x8(t.k[KS + s]), as_bf16x8(qf[s]), s1);
     }
-    const int kt = tl * 32;
+    const bool second = tl >= TA;
+    const int kt = (second ? tl - TA : tl) * 32, nk = second ? a.Nk2 : a.Nk;
     float mt = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ka = kt + grp * 4 + i;
-      s0[i] = ka < a.Nk ? s0[i] * sl2 : -INFINITY;
-      s1[i] = ka + 16 < a.Nk ? s1[i] * sl2 : -INFINITY;
+      s0[i] = ka < nk ? s0[i] * sl2 : -INFINITY;
+      s1[i] = ka + 16 < nk ? s1[i] * sl2 : -INFINITY;
       mt = fmaxf(mt, fmaxf(s0[i], s1[i]));
     }
     mt = group4_max(mt);
@@ -403,6 +412,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
 hipError_t attention_chunk(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.Nq <= 0 || a.Nk <= 0) return hipSuccess;
   if (a.Hq % a.Hkv || a.o_f32) return hipErrorInvalidValue;
+  if (a.Nk2 < 0 || (a.Nk2 && (!a.k2 || !a.v2))) return hipErrorInvalidValue;
   if (a.pf.blocks < 0 || a.pf.blocks > 1024 || (a.pf.blocks && !a.pf.sink)) return hipErrorInvalidValue;
   const int R = a.Hq / a.Hkv * a.Nq;
   dim3 grid((R + 15) / 16 + a.pf.blocks, a.Hkv, a.B);
@@ -432,16 +442,21 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
     qv[d] = q[d] * sc;
     o[d] = 0.f;
   }
+  // joint attention: the second source's keys follow the first's
+  const float* K2 = a.Nk2 ? (const float*)a.k2 + b * a.k2_bs + g * a.k2_hs : K;
+  const float* V2 = a.Nk2 ? (const float*)a.v2 + b * a.v2_bs + g * a.v2_hs : V;
   float m = -INFINITY, l = 0.f;
-  for (int t = 0; t < a.Nk; ++t) {
-    const float* kr = K + (long)t * a.k_rs;
+  for (int t = 0; t < a.Nk + a.Nk2; ++t) {
+    const bool second = t >= a.Nk;
+    const int tt = second ? t - a.Nk : t;
+    const float* kr = second ? K2 + (long)tt * a.k2_rs : K + (long)tt * a.k_rs;
     float s = 0.f;
 #pragma unroll
     for (int d = 0; d < D; ++d) s = fmaf(qv[d], kr[d], s);
     const float mn = fmaxf(m, s);
     const float al = expf(m - mn), p = expf(s - mn);
     l = l * al + p;
-    const float* vr = V + (long)t * a.v_rs;
+    const float* vr = second ? V2 + (long)tt * a.v2_rs : V + (long)tt * a.v_rs;
 #pragma unroll
     for (int d = 0; d < D; ++d) o[d] = fmaf(p, vr[d], o[d] * al);
     m = mn;
@@ -455,6 +470,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
 hipError_t attention_f32(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.Nq <= 0 || a.Nk <= 0) return hipSuccess;
   if (a.Hq % a.Hkv || !a.o_f32) return hipErrorInvalidValue;
+  if (a.Nk2 < 0 || (a.Nk2 && (!a.k2 || !a.v2))) return hipErrorInvalidValue;
   dim3 grid((a.Nq + 63) / 64, a.Hq, a.B);
   switch (a.hd) {
     case 32: hipLaunchKernelGGL(k_attn_f32<32>, grid, dim3(64), 0, s, a); break;

@@ -40,18 +40,21 @@ __device__ __forceinline__ void cache_index(const Epilogue& e, int m, int n, lon
   idx = blk + (!e.out_frag ? (long)t * e.hd + d : kv ? vfrag_idx(t, d, e.hd) : frag_idx(t, d, e.hd));
 }
 
-// EPI_QKV: query columns to rows, keys and values of the chunk in their MFMA orders
+// EPI_QKV: query columns to rows, keys and values in their blocks (bf16: MFMA orders)
 __device__ __forceinline__ void qkv_store(const Epilogue& e, int m, int n, float v) {
   if (n < e.nq) {
-    ((bf16_t*)e.out)[(long)m * e.ldo + n] = f2bf(v);
+    const long i = (long)m * e.ldo + n;
+    if (e.out_f32) ((float*)e.out)[i] = v; else ((bf16_t*)e.out)[i] = f2bf(v);
     return;
   }
   const int per = e.hkv * e.hd;
   const int kv = (n - e.nq) >= per, r = n - e.nq - kv * per;
   const int h = r / e.hd, d = r - h * e.hd;
   const int b = m / e.npre, t = m - b * e.npre;
-  const long blk = ((long)b * e.hkv + h) * e.npad * e.hd;
-  if (kv) ((bf16_t*)e.vout)[blk + vfrag_idx(t, d, e.hd)] = f2bf(v);
+  const long bs = e.kv_bs ? e.kv_bs : (long)per * e.npad;
+  const long blk = b * bs + (long)h * e.npad * e.hd;
+  if (e.out_f32) ((float*)(kv ? e.vout : e.kout))[blk + (long)t * e.hd + d] = v;
+  else if (kv) ((bf16_t*)e.vout)[blk + vfrag_idx(t, d, e.hd)] = f2bf(v);
   else ((bf16_t*)e.kout)[blk + frag_idx(t, d, e.hd)] = f2bf(v);
 }
 

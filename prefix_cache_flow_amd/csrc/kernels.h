@@ -37,10 +37,12 @@ enum EpiKind {
                   // (t, d) row-major (out_frag == 0) or, with out_frag, K in
                   // frag_idx and V in vfrag_idx order (common.h)
   EPI_PARTIAL = 4,// raw fp32 partial sums to ws[split][m][n], left for a row kernel
-  EPI_QKV = 5     // fused self-attention projection of the chunk, row m = (b, t) with
-                  // b = m / npre: columns n < nq go to out[m * ldo + n] (bf16 rows),
-                  // the next hkv * hd to kout and the last hkv * hd to vout, blocks
-                  // b * hkv + h of npad * hd elements in frag_idx / vfrag_idx order
+  EPI_QKV = 5     // fused self-attention projection, row m = (b, t) with b = m / npre:
+                  // columns n < nq go to out[m * ldo + n] (rows), the next hkv * hd
+                  // to kout and the last hkv * hd to vout, in blocks of npad * hd
+                  // elements, block h of batch b at (b * kv_bs / (npad * hd) + h)
+                  // (kv_bs = 0: hkv * npad * hd); bf16 K / V in frag_idx /
+                  // vfrag_idx order, fp32 (out_f32) as rows t * hd + d
 };
 
 struct Epilogue {
@@ -55,6 +57,7 @@ struct Epilogue {
   int nq = 0;                            // EPI_QKV: query columns
   void* kout = nullptr;                  // EPI_QKV
   void* vout = nullptr;                  // EPI_QKV
+  long kv_bs = 0;                        // EPI_QKV: elements between batches of K (and V) blocks
   // W2A8 output scaling: y = bf16(float(acc) * (alpha[m] * beta[n])) before the epilogue
   const float* alpha = nullptr;
   const float* beta = nullptr;
@@ -142,6 +145,11 @@ struct AttnArgs {
   const void* v; long v_bs, v_hs, v_rs;
   void* o; long o_bs, o_rs;               // output head j at column j * hd
   int B, Nq, Nk, Hq, Hkv, hd;
+  // optional second key/value source, appended after the first Nk keys in one
+  // softmax (joint attention): Nk2 keys laid out like the first source
+  const void* k2; long k2_bs, k2_hs, k2_rs;
+  const void* v2; long v2_bs, v2_hs, v2_rs;
+  int Nk2;
   int o_f32;                              // 1: fp32 output, 0: bf16
   int o_frag;                             // bf16 output in fragment layout: row b * Nq + q, K = Hq * hd
   Prefetch pf;                            // attention_chunk: extra workgroups warming the next weights

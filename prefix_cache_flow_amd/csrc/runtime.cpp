@@ -87,6 +87,13 @@ static vla_status check_config(const vla_model_config* c) {
       return fail(VLA_ERR_UNSUPPORTED, "ternary prefix widths must be multiples of 128");
   }
   if (c->d_p > 16 * 256 * 4 || c->F_p > (1 << 20)) return fail(VLA_ERR_UNSUPPORTED, "model too wide");
+  if (c->attn_mode != VLA_ATTN_CROSS && c->attn_mode != VLA_ATTN_JOINT)
+    return fail(VLA_ERR_INVALID_ARGUMENT, "bad attn_mode");
+  if (c->attn_mode == VLA_ATTN_JOINT) {
+    if (c->L_e != c->L_p || c->Hkv_e != c->Hkv || c->hd_e != c->hd)
+      return fail(VLA_ERR_SHAPE_MISMATCH, "joint attention needs L_e == L_p, Hkv_e == Hkv and hd_e == hd");
+    if (c->precision == VLA_W2A8_BF16) return fail(VLA_ERR_UNSUPPORTED, "joint attention with a ternary prefix");
+  }
   return VLA_OK;
 }
 
@@ -113,10 +120,13 @@ static std::vector<Spec> specs(const vla_model_config* c) {
     lin_p(c->F_p, c->d_p);
     lin_p(c->d_p, c->F_p);
   }
-  s.push_back({c->d_p, 1, 0});
-  for (int e = 0; e < c->L_e; ++e) {
-    s.push_back({kve, c->d_p, 1});
-    s.push_back({kve, c->d_p, 1});
+  const bool joint = c->attn_mode == VLA_ATTN_JOINT;
+  if (!joint) {
+    s.push_back({c->d_p, 1, 0});
+    for (int e = 0; e < c->L_e; ++e) {
+      s.push_back({kve, c->d_p, 1});
+      s.push_back({kve, c->d_p, 1});
+    }
   }
   s.push_back({c->d_e, c->d_a, 1});
   for (int e = 0; e < c->L_e; ++e) {
@@ -125,9 +135,11 @@ static std::vector<Spec> specs(const vla_model_config* c) {
     s.push_back({kve, c->d_e, 1});
     s.push_back({kve, c->d_e, 1});
     s.push_back({c->d_e, qe, 1});
-    s.push_back({c->d_e, 1, 0});
-    s.push_back({qe, c->d_e, 1});
-    s.push_back({c->d_e, qe, 1});
+    if (!joint) {
+      s.push_back({c->d_e, 1, 0});
+      s.push_back({qe, c->d_e, 1});
+      s.push_back({c->d_e, qe, 1});
+    }
     s.push_back({c->d_e, 1, 0});
     s.push_back({c->F_e, c->d_e, 1});
     s.push_back({c->F_e, c->d_e, 1});
@@ -189,7 +201,7 @@ struct vla_model {
   uint32_t magic = MODEL_MAGIC;
   vla_model_config cfg{};
   int device = 0;
-  bool f32 = false, w2a8 = false;
+  bool f32 = false, w2a8 = false, joint = false;
   std::vector<void*> allocs;  // every device allocation of weights
   std::vector<PrefixLayer> pl;
   std::vector<ExpertLayer> el;
@@ -356,7 +368,7 @@ static vla_status build_weights(vla_model* m, const vla_weights* w, hipStream_t 
   // Every bf16 projection is assembled row-major in a staging buffer and stored
   // in the MFMA fragment layout (kernels.h, frag_pack): every weight load of a
   // wave is then one contiguous 1 KB.
-  const int64_t ncache = (int64_t)c.L_e * 2 * kve;
+  const int64_t ncache = m->joint ? 0 : (int64_t)c.L_e * 2 * kve;
   void* stage = nullptr;
   if (!m->f32) {
     int64_t big = std::max<int64_t>(std::max<int64_t>(qkve, 2 * (int64_t)c.F_e) * c.d_e, (int64_t)c.d_e * std::max<int64_t>(qe, c.F_e));
@@ -451,23 +463,28 @@ static vla_status build_weights(vla_model* m, const vla_weights* w, hipStream_t 
       TRY(put_beta(&P.bd, h));
     }
   }
-  TRY(put_gain(m, &m->w_pf, src.t[src.i++], c.d_p, s));
-  // expert prefix-side projections, concatenated in boundary order: [l][k|v][h][d]
-  TRY(packed_weight(&m->wcache, ncache, c.d_p, [&](void* d) {
-    vla_status r = VLA_OK;
-    for (int e = 0; e < c.L_e && r == VLA_OK; ++e) {
-      r = put_rows(m, d, (int64_t)(2 * e) * kve, src.t[src.i++], kve, c.d_p, s);
-      if (r == VLA_OK) r = put_rows(m, d, (int64_t)(2 * e + 1) * kve, src.t[src.i++], kve, c.d_p, s);
-    }
-    return r;
-  }));
+  if (!m->joint) {
+    TRY(put_gain(m, &m->w_pf, src.t[src.i++], c.d_p, s));
+    // expert prefix-side projections, concatenated in boundary order: [l][k|v][h][d]
+    TRY(packed_weight(&m->wcache, ncache, c.d_p, [&](void* d) {
+      vla_status r = VLA_OK;
+      for (int e = 0; e < c.L_e && r == VLA_OK; ++e) {
+        r = put_rows(m, d, (int64_t)(2 * e) * kve, src.t[src.i++], kve, c.d_p, s);
+        if (r == VLA_OK) r = put_rows(m, d, (int64_t)(2 * e + 1) * kve, src.t[src.i++], kve, c.d_p, s);
+      }
+      return r;
+    }));
+  }
   TRY(dev_alloc(m, &m->w_in, (int64_t)c.d_e * c.d_a * es));
   TRY(put_rows(m, m->w_in, 0, src.t[src.i++], c.d_e, c.d_a, s));
   // Expert projections (fragment layout in bf16, like the prefix): the chunk
   // has few rows, so these GEMMs are weight streams.
   // all expert projections in one allocation, layer by layer
   auto rnd = [](int64_t b) { return (b + 255) / 256 * 256; };
-  const int64_t shapes[6][2] = {{qkve, c.d_e}, {c.d_e, qe}, {qe, c.d_e}, {c.d_e, qe}, {2 * (int64_t)c.F_e, c.d_e}, {c.d_e, c.F_e}};
+  // (joint attention has no cross-attention projections: slots 2 and 3 are empty)
+  const int64_t njoint = m->joint ? 0 : 1;
+  const int64_t shapes[6][2] = {{qkve, c.d_e}, {c.d_e, qe}, {qe * njoint, c.d_e}, {c.d_e * njoint, qe},
+                                {2 * (int64_t)c.F_e, c.d_e}, {c.d_e, c.F_e}};
   m->ew_layer = 0;
   for (auto& sh : shapes) m->ew_layer += rnd(sh[0] * sh[1] * (int64_t)es);
   TRY(dev_alloc(m, (void**)&m->ew, m->ew_layer * c.L_e));
@@ -498,11 +515,13 @@ static vla_status build_weights(vla_model* m, const vla_weights* w, hipStream_t 
     }));
     const void* wos = src.t[src.i++];
     TRY(expert_weight(&E.wos, c.d_e, qe, [&](void* d) { return put_rows(m, d, 0, wos, c.d_e, qe, s); }));
-    TRY(put_gain(m, &E.a2, src.t[src.i++], c.d_e, s));
-    const void* wqc = src.t[src.i++];
-    TRY(expert_weight(&E.wqc, qe, c.d_e, [&](void* d) { return put_rows(m, d, 0, wqc, qe, c.d_e, s); }));
-    const void* woc = src.t[src.i++];
-    TRY(expert_weight(&E.woc, c.d_e, qe, [&](void* d) { return put_rows(m, d, 0, woc, c.d_e, qe, s); }));
+    if (!m->joint) {
+      TRY(put_gain(m, &E.a2, src.t[src.i++], c.d_e, s));
+      const void* wqc = src.t[src.i++];
+      TRY(expert_weight(&E.wqc, qe, c.d_e, [&](void* d) { return put_rows(m, d, 0, wqc, qe, c.d_e, s); }));
+      const void* woc = src.t[src.i++];
+      TRY(expert_weight(&E.woc, c.d_e, qe, [&](void* d) { return put_rows(m, d, 0, woc, c.d_e, qe, s); }));
+    }
     TRY(put_gain(m, &E.a3, src.t[src.i++], c.d_e, s));
     const void* wg = src.t[src.i++];
     const void* wu = src.t[src.i++];
@@ -557,6 +576,7 @@ extern "C" vla_status vla_model_create(const vla_model_config* cfg, const vla_we
   m->cfg = *cfg;
   m->f32 = cfg->precision == VLA_F32;
   m->w2a8 = cfg->precision == VLA_W2A8_BF16;
+  m->joint = cfg->attn_mode == VLA_ATTN_JOINT;
   (void)hipGetDevice(&m->device);
   hipStream_t s = (hipStream_t)stream;
   st = build_weights(m, weights, s);
@@ -846,11 +866,35 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
     aa.k = w.pk; aa.k_bs = (long)c.Hkv * Np * c.hd; aa.k_hs = (long)Np * c.hd;
     aa.v = w.pv; aa.v_bs = aa.k_bs; aa.v_hs = aa.k_hs;
     aa.o_frag = 1;
-    if (Np > N) {  // padding key rows: finite values (zero weights times values)
+    if (Np > N && !m->joint) {  // padding key rows: finite values (zero weights times values)
       K_TRY(zero_tails(w.pk, (long)B * c.Hkv, (long)Np * c.hd, 32 * c.hd, s), "key padding");
       K_TRY(zero_tails(w.pv, (long)B * c.Hkv, (long)Np * c.hd, 32 * c.hd, s), "value padding");
     }
   }
+  // Joint attention (the pi0 form): layer l's keys and values are the cache,
+  // so the fused projection writes them straight into cache block l (K and V
+  // of every KV head, per observation jbs elements apart) and the layer's
+  // attention reads them there.  fp32 keeps plain rows.
+  const long jbs = (long)c.L_p * 2 * c.Hkv * Np * c.hd;
+  if (m->joint) {
+    if (m->f32) {
+      qkv_e.kind = EPI_QKV; qkv_e.ldo = qw; qkv_e.nq = qw; qkv_e.out_f32 = 1;
+      qkv_e.hkv = c.Hkv; qkv_e.hd = c.hd; qkv_e.npre = N; qkv_e.npad = Np;
+      aa.q_bs = (long)N * qw; aa.q_rs = qw;
+    } else if (Np > N) {
+      K_TRY(zero_tails(kv, (long)B * c.L_p * 2 * c.Hkv, (long)Np * c.hd, 32 * c.hd, s), "cache padding");
+    }
+    qkv_e.kv_bs = jbs;
+    aa.k_bs = aa.v_bs = jbs;
+    aa.k_hs = aa.v_hs = (long)Np * c.hd;
+    aa.k_rs = aa.v_rs = c.hd;
+  }
+  auto joint_layer = [&](int l) {
+    char* kb = (char*)kv + (size_t)l * 2 * c.Hkv * Np * c.hd * elt(m);
+    char* vb = kb + (size_t)c.Hkv * Np * c.hd * elt(m);
+    qkv_e.kout = kb; qkv_e.vout = vb;
+    aa.k = kb; aa.v = vb;
+  };
 
   if (m->w2a8) {
     K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, m->pl[0].w1, eps, nullptr, 0, 0, w.qa, w.alpha, s), "norm");
@@ -883,8 +927,13 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
     for (int l = 0; l < c.L_p; ++l) {
       const PrefixLayer& P = m->pl[l];
       const float* next_gain = l + 1 < c.L_p ? m->pl[l + 1].w1 : m->w_pf;
+      if (m->joint) joint_layer(l);
+      // joint: the last layer's output is never read, only its keys and values
+      const bool kv_only = m->joint && l + 1 == c.L_p;
       if (m->f32) {
-        K_TRY(gemm_f32((const float*)w.u, c.d_p, (const float*)P.wqkv, c.d_p, M, qkvw, c.d_p, epi_store(w.qkv, qkvw, 1), s), "qkv");
+        K_TRY(gemm_f32((const float*)w.u, c.d_p, (const float*)P.wqkv, c.d_p, M, qkvw, c.d_p,
+                       m->joint ? qkv_e : epi_store(w.qkv, qkvw, 1), s), "qkv");
+        if (kv_only) break;
         K_TRY(attention_f32(aa, s), "attention");
         Epilogue r;
         r.kind = EPI_RESID; r.resid = w.h; r.ldr = c.d_p;
@@ -902,6 +951,7 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
           ProbeScope ps(m, VLA_PROBE_PREFIX_QKV, s);
           K_TRY(mm_frag(w.u, P.wqkv, M, qkvw, c.d_p, qkv_e, w.part, s), "qkv");
         }
+        if (kv_only) break;
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_ATTN, s);
           K_TRY(attention_chunk(aa, s), "attention");
@@ -930,6 +980,7 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
       }
     }
   }
+  if (m->joint) return VLA_OK;
   // Z = RMS(h; w_final) is in w.u; project into every expert layer's K and V
   Epilogue ce;
   ce.kind = EPI_CACHE; ce.out = kv; ce.out_f32 = m->f32 ? 1 : 0;
@@ -1087,7 +1138,8 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
     a.gain_f = m->w_ef; a.w_out = m->w_out; a.w_in = m->w_in; a.gain_1 = m->el[0].a1;
     a.u = w.eu; a.u_f32 = f32 ? 1 : 0; a.u_frag = fr; a.sched = m->sched_dev;
     a.k_head = k_head; a.k_embed = k_embed;
-    if (k_embed >= 0) a.pf = pfr(m->el[0].wqkv, b_qkv, g_qkv, nullptr, 0, 0, 64);
+    if (k_embed >= 0)
+      a.pf = pfr(m->el[0].wqkv, b_qkv, g_qkv, m->joint && B == 1 ? kv->storage : nullptr, layer_kv, 0, 64);
     return step_rows(a, f32 ? 1 : 0, s);
   };
   for (int k = 0; k < steps; ++k) {
@@ -1096,7 +1148,26 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
       const ExpertLayer& L = m->el[e];
       ca.k = (const char*)kv->storage + (size_t)e * layer_stride * es;
       ca.v = (const char*)ca.k + (size_t)c.Hkv_e * Np * c.hd_e * es;
-      if (f32) {
+      if (m->joint) {
+        // joint attention: the chunk's own keys, then prefix layer e's (cache block e)
+        sa.k2 = ca.k; sa.k2_bs = ca.k_bs; sa.k2_hs = ca.k_hs; sa.k2_rs = ca.k_rs;
+        sa.v2 = ca.v; sa.v2_bs = ca.v_bs; sa.v2_hs = ca.v_hs; sa.v2_rs = ca.v_rs;
+        sa.Nk2 = N;
+      }
+      if (f32 && m->joint) {
+        K_TRY(gemm_f32((const float*)w.eu, c.d_e, (const float*)L.wqkv, c.d_e, M, qkve, c.d_e, epi_store(w.eqkv, qkve, 1), s), "qkv_s");
+        K_TRY(attention_f32(sa, s), "joint attn");
+        Epilogue r;
+        r.kind = EPI_RESID; r.resid = w.E; r.ldr = c.d_e;
+        K_TRY(gemm_f32((const float*)w.eattn, qe, (const float*)L.wos, qe, M, c.d_e, qe, r, s), "o_s");
+        K_TRY(resid_norm(w.E, c.d_e, nullptr, 0, M, c.d_e, L.a3, eps, w.eu, 1, c.d_e, nullptr, nullptr, s), "norm");
+        Epilogue g = epi_store(w.emlp, c.F_e, 1);
+        g.kind = EPI_GEGLU;
+        K_TRY(gemm_f32((const float*)w.eu, c.d_e, (const float*)L.wgu, c.d_e, M, 2 * c.F_e, c.d_e, g, s), "gate/up");
+        K_TRY(gemm_f32((const float*)w.emlp, c.F_e, (const float*)L.wd, c.F_e, M, c.d_e, c.F_e, r, s), "down");
+        if (e + 1 < c.L_e)
+          K_TRY(resid_norm(w.E, c.d_e, nullptr, 0, M, c.d_e, m->el[e + 1].a1, eps, w.eu, 1, c.d_e, nullptr, nullptr, s), "norm");
+      } else if (f32) {
         K_TRY(gemm_f32((const float*)w.eu, c.d_e, (const float*)L.wqkv, c.d_e, M, qkve, c.d_e, epi_store(w.eqkv, qkve, 1), s), "qkv_s");
         K_TRY(attention_f32(sa, s), "self attn");
         Epilogue r;
@@ -1121,25 +1192,38 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
           return gemm_bf16((const uint16_t*)A, lda, (const uint16_t*)W, K, M, N, K, ep, splits, w.epart, s, 1);
         };
         K_TRY(mm(u, c.d_e, L.wqkv, qkve, c.d_e, qkv_e, fr ? 1 : expert_splits(M, qkve, c.d_e)), "qkv_s");
-        sa.pf = pfr(L.wos, b_o, g_o, L.wqc, b_q, g_q, 192);
-        K_TRY(attention_chunk(sa, s), "self attn");
-        K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
-        const Prefetch pf_kv = pfr(B == 1 ? ca.k : nullptr, B == 1 ? layer_kv : 0, 0, nullptr, 0, 0, 64);
-        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_kv),
-              "norm");
-        K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, epi_store(w.eq, qe, 0), fr ? 1 : expert_splits(M, qe, c.d_e)), "q_c");
-        ca.pf = pfr(L.woc, b_o, g_o, L.wgu, b_gu, g_gu, 192);
-        K_TRY(attention_chunk(ca, s), "cross attn");
-        K_TRY(mm(w.eattn, qe, L.woc, c.d_e, qe, pe, S_o), "o_c");
-        const Prefetch pf_d = pfr(L.wd, b_d, g_d, nullptr, 0, 0, 192);
-        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_d),
-              "norm");
+        if (m->joint) {
+          // one attention over the chunk and prefix layer e, then the MLP
+          sa.pf = pfr(L.wos, b_o, g_o, L.wgu, b_gu, g_gu, 192);
+          K_TRY(attention_chunk(sa, s), "joint attn");
+          K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
+          const Prefetch pf_d = pfr(L.wd, b_d, g_d, nullptr, 0, 0, 192);
+          K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_d),
+                "norm");
+        } else {
+          sa.pf = pfr(L.wos, b_o, g_o, L.wqc, b_q, g_q, 192);
+          K_TRY(attention_chunk(sa, s), "self attn");
+          K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
+          const Prefetch pf_kv = pfr(B == 1 ? ca.k : nullptr, B == 1 ? layer_kv : 0, 0, nullptr, 0, 0, 64);
+          K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_kv),
+                "norm");
+          K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, epi_store(w.eq, qe, 0), fr ? 1 : expert_splits(M, qe, c.d_e)), "q_c");
+          ca.pf = pfr(L.woc, b_o, g_o, L.wgu, b_gu, g_gu, 192);
+          K_TRY(attention_chunk(ca, s), "cross attn");
+          K_TRY(mm(w.eattn, qe, L.woc, c.d_e, qe, pe, S_o), "o_c");
+          const Prefetch pf_d = pfr(L.wd, b_d, g_d, nullptr, 0, 0, 192);
+          K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_d),
+                "norm");
+        }
         Epilogue g = epi_store(w.emlp, c.F_e, 0);
         g.kind = EPI_GEGLU;
         g.out_frag = fr;
         K_TRY(mm(u, c.d_e, L.wgu, 2 * c.F_e, c.d_e, g, fr ? 1 : expert_splits(M, 2 * c.F_e, c.d_e)), "gate/up");
         K_TRY(mm(w.emlp, c.F_e, L.wd, c.d_e, c.F_e, pe, S_d), "down");
-        const Prefetch pf_next = e + 1 < c.L_e ? pfr(m->el[e + 1].wqkv, b_qkv, g_qkv, nullptr, 0, 0, 192) : Prefetch{};
+        // next layer's QKV weights (and, joint, its cache block)
+        const void* next_kv = m->joint && B == 1 ? (const char*)ca.k + (size_t)layer_stride * es : nullptr;
+        const Prefetch pf_next =
+            e + 1 < c.L_e ? pfr(m->el[e + 1].wqkv, b_qkv, g_qkv, next_kv, layer_kv, 0, 192) : Prefetch{};
         K_TRY(resid_norm(w.E, c.d_e, w.epart, S_d, M, c.d_e, e + 1 < c.L_e ? m->el[e + 1].a1 : m->w_ef, eps,
                          e + 1 < c.L_e ? w.eu : nullptr, 0, c.d_e, nullptr, nullptr, s, fr, &pf_next), "norm");
       }

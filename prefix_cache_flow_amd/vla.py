@@ -21,7 +21,8 @@ STATUS = {0: "VLA_OK", 1: "VLA_ERR_INVALID_ARGUMENT", 2: "VLA_ERR_SHAPE_MISMATCH
           4: "VLA_ERR_UNSUPPORTED", 5: "VLA_ERR_OUT_OF_MEMORY", 6: "VLA_ERR_DEVICE"}
 PRECISION = {"f32": 0, "bf16": 1, "w2a8": 2}
 VLA_OUT_F32, VLA_OUT_BF16 = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
+ATTN_MODE = {"cross": 0, "joint": 1}
 
 # every symbol include/vla.h declares
 EXPORTS = (
@@ -45,7 +46,7 @@ class vla_model_config(C.Structure):
                 ("hd", C.c_int32), ("F_p", C.c_int32),
                 ("d_e", C.c_int32), ("L_e", C.c_int32), ("Hq_e", C.c_int32), ("Hkv_e", C.c_int32),
                 ("hd_e", C.c_int32), ("F_e", C.c_int32),
-                ("H", C.c_int32), ("d_a", C.c_int32), ("rms_eps", C.c_float)]
+                ("H", C.c_int32), ("d_a", C.c_int32), ("rms_eps", C.c_float), ("attn_mode", C.c_int32)]
 
 
 class vla_weights(C.Structure):
@@ -129,6 +130,11 @@ def make_config(cfg) -> vla_model_config:
     for k in ("d_p", "L_p", "Hq", "Hkv", "hd", "F_p", "d_e", "L_e", "Hq_e", "Hkv_e", "hd_e", "F_e", "H", "d_a"):
         setattr(c, k, int(get(k)))
     c.rms_eps = float(get("rms_eps"))
+    try:
+        attn = get("attn")
+    except (KeyError, AttributeError):
+        attn = "cross"
+    c.attn_mode = ATTN_MODE[attn] if isinstance(attn, str) else int(attn)
     return c
 
 

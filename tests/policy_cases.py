@@ -22,6 +22,15 @@ SMALL_BF16_B3 = synth.config(1, name="small_bf16_b3", batch=3, n_prefix=70, d_p=
 # whole number of 32-key tiles, and a chunk of three 16-row blocks.
 SMALL_GQA = synth.config(1, name="small_gqa", n_prefix=90, d_p=256, L_p=2, Hq=4, Hkv=2, hd=64, F_p=512,
                          d_e=192, L_e=2, Hq_e=4, Hkv_e=2, hd_e=64, F_e=256, H=40, d_a=16, steps=2)
+# Joint attention (per-layer prefix K/V, the pi0 form) at the same small shapes.
+JOINT_F32 = synth.config(0, name="tiny_joint_fp32", attn="joint", n_prefix=40, H=6)
+SMALL_JOINT = synth.config(1, name="small_joint_bf16", attn="joint", n_prefix=100, d_p=256, L_p=2, Hq=4, Hkv=1,
+                           hd=64, F_p=512, d_e=128, L_e=2, Hq_e=2, Hkv_e=1, hd_e=64, F_e=256, H=20, d_a=7, steps=3)
+SMALL_JOINT_GQA = synth.config(1, name="small_joint_gqa", attn="joint", n_prefix=90, d_p=256, L_p=2, Hq=4, Hkv=2,
+                               hd=64, F_p=512, d_e=192, L_e=2, Hq_e=4, Hkv_e=2, hd_e=64, F_e=256, H=40, d_a=16, steps=2)
+SMALL_JOINT_B3 = synth.config(1, name="small_joint_b3", attn="joint", batch=3, n_prefix=70, d_p=256, L_p=2, Hq=8,
+                              Hkv=1, hd=128, F_p=512, d_e=128, L_e=2, Hq_e=8, Hkv_e=1, hd_e=128, F_e=256, H=33, d_a=5,
+                              steps=2)
 SMALL_W2A8 = synth.config(4, name="small_w2a8", n_prefix=100, d_p=256, L_p=2, Hq=2, Hkv=2, hd=128, F_p=384,
                           d_e=128, L_e=2, Hq_e=2, Hkv_e=1, hd_e=64, F_e=256, H=8, d_a=7, steps=3)
 

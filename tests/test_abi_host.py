@@ -30,9 +30,9 @@ def test_library_exports_every_declared_symbol():
     assert sorted(vla.EXPORTS) == names
 
 
-@pytest.mark.parametrize("i", range(5))
+@pytest.mark.parametrize("i", list(range(5)) + ["joint0", "joint1"])
 def test_tensor_order_and_shapes_match_workloads(i):
-    cfg = synth.config(i)
+    cfg = synth.config(int(i[-1]), attn="joint") if isinstance(i, str) else synth.config(i)
     specs = synth.weight_specs(cfg)
     assert vla.vla_n_tensors(cfg.to_dict()) == len(specs)
     for idx, (name, shape, kind) in enumerate(specs):
@@ -74,6 +74,12 @@ def test_status_strings_and_config_validation():
     with pytest.raises(vla.VlaError) as ei:
         vla.vla_tensor_info(cfg, 10_000)
     assert ei.value.status == 1
+    # joint attention needs matching layer counts and K/V heads, and a dense prefix
+    assert vla.vla_n_tensors(dict(cfg, attn="joint", L_e=4)) == -1
+    assert "joint" in vla.vla_last_error()
+    assert vla.vla_n_tensors(dict(cfg, attn="joint", hd_e=128)) == -1
+    assert vla.vla_n_tensors(synth.config(4, attn="joint", L_e=30, Hkv_e=20, hd_e=128).to_dict()) == -1
+    assert vla.vla_n_tensors(dict(cfg, attn=7)) == -1
 
 
 def test_null_and_foreign_handles_are_rejected():

@@ -34,12 +34,21 @@ from prefix_cache_flow_amd import vla  # noqa: E402
 # over 30 layers.  The oracle evaluated in float32 departs from its own float64
 # evaluation by e_rel(X^T) 8.4e-3, e_rel(D) 1.8e-2 and a cache e_rel of 5.1e-2;
 # its bounds are about twice that (X^T keeps the stated 2e-2).
+# "joint" is the single-camera workload with joint attention (per-layer prefix
+# K/V as the cache, the pi0 form); its cache is the 18 layers' own keys and values.
 CASES = [
     (1, 1e-2, 2e-2, None),
     (2, 1e-2, 2e-2, None),
     (3, 1e-2, 2e-2, (0, 15)),
     (4, 4e-2, 1e-1, None),
+    ("joint", 1e-2, 2e-2, None),
 ]
+
+
+def workload(idx):
+    if idx == "joint":
+        return synth.config(1, name="single_camera_joint_bf16", attn="joint"), 5
+    return synth.config(idx), idx
 
 
 def log(msg):
@@ -48,11 +57,11 @@ def log(msg):
 
 @pytest.mark.parametrize("idx,dtol,ctol,sample", CASES, ids=lambda v: str(v))
 def test_full_size_against_oracle(idx, dtol, ctol, sample):
-    cfg = synth.config(idx)
+    cfg, seed = workload(idx)
     t0 = time.time()
     log(f"case {cfg.name}: generating seeded inputs")
-    w, b = synth.make_weights(cfg, idx)
-    z0, x0 = synth.make_prefix(cfg, idx), synth.make_noise(cfg, idx)
+    w, b = synth.make_weights(cfg, seed)
+    z0, x0 = synth.make_prefix(cfg, seed), synth.make_noise(cfg, seed)
     model = build_model(cfg, w, b)
     zt, xt = torch.from_numpy(z0).cuda(), torch.from_numpy(x0).cuda()
     kv = vla.vla_prefix_encode(model, zt)
@@ -86,10 +95,11 @@ def test_full_size_against_oracle(idx, dtol, ctol, sample):
     assert ec <= ctol
 
 
-def test_degenerate_sizes():
+@pytest.mark.parametrize("attn", ["cross", "joint"])
+def test_degenerate_sizes(attn):
     """One prefix token, one chunk row, one step."""
     cfg = synth.config(1, name="degenerate", n_prefix=1, d_p=128, L_p=1, Hq=2, Hkv=1, hd=64, F_p=128, d_e=128, L_e=1,
-                       Hq_e=2, Hkv_e=1, hd_e=64, F_e=128, H=1, d_a=1, steps=1)
+                       Hq_e=2, Hkv_e=1, hd_e=64, F_e=128, H=1, d_a=1, steps=1, attn=attn)
     w, b = synth.make_weights(cfg, 9)
     z0, x0 = synth.make_prefix(cfg, 9), synth.make_noise(cfg, 9)
     model = build_model(cfg, w, b)

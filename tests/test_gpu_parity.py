@@ -12,8 +12,8 @@ import pytest
 
 import oracle
 import synth
-from policy_cases import (SMALL_BF16, SMALL_BF16_B3, SMALL_GQA, SMALL_W2A8, build_model, cache_from_storage,
-                          gpu_run, host_inputs)
+from policy_cases import (JOINT_F32, SMALL_BF16, SMALL_BF16_B3, SMALL_GQA, SMALL_JOINT, SMALL_JOINT_B3,
+                          SMALL_JOINT_GQA, SMALL_W2A8, build_model, cache_from_storage, gpu_run, host_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +43,10 @@ def report(name, got, ref, x0):
     (SMALL_BF16_B3, 2e-2, 5e-3, 4e-3),
     (SMALL_GQA, 2e-2, 5e-3, 4e-3),
     (SMALL_W2A8, 2e-2, 1e-2, 4e-3),
+    (JOINT_F32, 1e-3, 1e-3, 1e-4),
+    (SMALL_JOINT, 2e-2, 5e-3, 4e-3),
+    (SMALL_JOINT_GQA, 2e-2, 5e-3, 4e-3),
+    (SMALL_JOINT_B3, 2e-2, 5e-3, 4e-3),
 ], ids=lambda v: getattr(v, "name", ""))
 def test_end_to_end_small(cfg, tol, dtol, ctol):
     w, b, z0, x0 = host_inputs(cfg, 0)
@@ -118,9 +122,9 @@ def test_graph_replays_match_eager():
     model.close()
 
 
-def test_cached_equals_recompute_on_gpu():
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_JOINT], ids=lambda c: c.name)
+def test_cached_equals_recompute_on_gpu(cfg):
     """Re-encoding the prefix before every step gives the cached result bit for bit."""
-    cfg = SMALL_BF16
     w, b, z0, x0 = host_inputs(cfg, 1)
     model = build_model(cfg, w, b)
     sched = [float(np.float32(k / cfg.steps)) for k in range(cfg.steps + 1)]
@@ -136,7 +140,7 @@ def test_cached_equals_recompute_on_gpu():
     model.close()
 
 
-@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_GQA], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_GQA, SMALL_JOINT], ids=lambda c: c.name)
 def test_two_stream_pipeline_matches_serial(cfg):
     """Prefix passes on one stream overlapping solver runs on another (one model, two cache
     buffers, the prefix of observation k + 1 beside the solver of observation k) give every
