@@ -126,6 +126,33 @@ def solver_sweep(vla, model, zt, xt, kv_storage, reps=5):
             "ideal_speedup": [float(T * (P + E) / (P + T * E)) for T in Ts]}
 
 
+W2A8_SHAPES = ((320, 7680, 2560), (320, 2560, 2560), (320, 13824, 2560), (320, 2560, 6912))
+
+
+def w2a8_ablation(vla, reps=5):
+    """The page's ternary-kernel comparison restated on CDNA4: the int8 matrix-core kernel the ternary
+    prefix uses against a vector-ALU kernel on v_dot4_i32_i8 (the dp4a counterpart), at the ternary
+    workload's four projection shapes (320 rows), each the median kernel time of `reps` calls."""
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(7)
+    out = []
+    for M, N, K in W2A8_SHAPES:
+        a = torch.randint(-127, 128, (M, K), generator=g, dtype=torch.int8).cuda()
+        alpha = torch.rand(M, generator=g).cuda() * 0.01
+        packed = torch.randint(0, 255, (N, K // 4), generator=g, dtype=torch.uint8)
+        packed = (packed & 0x55).cuda()  # codes 0 and 1 only: valid ternary bytes
+        row = {"M": M, "N": N, "K": K}
+        for name, path in (("mfma", vla.W2A8_MFMA), ("dot4", vla.W2A8_DOT4)):
+            ts = [vla.vla_w2a8_gemm_ex(a, alpha, packed, [0.02], N, path, want_acc=False, timing=True)[2]
+                  for _ in range(reps)]
+            ms = float(np.median(ts))
+            row[name + "_us"] = ms * 1e3
+            row[name + "_tops"] = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        row["speedup"] = row["dot4_us"] / row["mfma_us"]
+        out.append(row)
+    return out
+
+
 def pipelined(vla, model, cfg, zt, xt, n, warmup=2):
     """Observations back to back with the prefix pass of observation k + 1 on a second stream while the solver
     of observation k runs (two cache buffers).  Returns chunks/s over n observations; every output is the same
@@ -260,6 +287,7 @@ def main():
     if not args.no_extras:
         extras["solver_sweep"] = solver_sweep(vla, model, zt, xt, kv_storage)
         extras["pipelined_two_stream"] = pipelined(vla, model, cfg, zt, xt, max(args.steps, 10))
+        extras["w2a8_ablation"] = w2a8_ablation(vla)
 
     # ---- CPU oracle on a bounded sample
     cpu = None

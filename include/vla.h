@@ -226,6 +226,21 @@ vla_status vla_w2a8_gemm(const int8_t* a, const float* alpha, const uint8_t* q_p
                          float beta, int32_t M, int32_t N, int32_t K, int32_t* acc_out,
                          uint16_t* y_bf16, void* stream);
 
+/* The same GEMM with group-wise weight scales (the paper, §III-D, Eq. 4's
+ * beta_g(n)): output channel n is scaled by beta[n / group] (host float32,
+ * N / group entries; group must divide N; group == N is the per-tensor form of
+ * vla_w2a8_gemm), and `path` picks the kernel: VLA_W2A8_MFMA, the int8
+ * matrix-core kernel the model uses (K % 128 == 0, N % 32 == 0), or
+ * VLA_W2A8_DOT4, a vector-ALU kernel on v_dot4_i32_i8 (K % 64 == 0), the
+ * counterpart of the page's dp4a path kept for comparison.  Both give the same
+ * int32 accumulators bit for bit.  kernel_ms (host, nullable) receives the
+ * GEMM kernel's device time.  Synchronises `stream`. */
+typedef enum { VLA_W2A8_MFMA = 0, VLA_W2A8_DOT4 = 1 } vla_w2a8_path;
+vla_status vla_w2a8_gemm_ex(const int8_t* a, const float* alpha, const uint8_t* q_packed,
+                            const float* beta, int32_t group, int32_t path, int32_t M, int32_t N,
+                            int32_t K, int32_t* acc_out, uint16_t* y_bf16, void* stream,
+                            float* kernel_ms);
+
 /* Host helpers for the packed ternary format: pack codes q in {-1, 0, 1}
  * (host int8 [N][K], K % 4 == 0) into host uint8 [N][K/4]; unpack the reverse
  * (VLA_ERR_INVALID_ARGUMENT on a code 3). */

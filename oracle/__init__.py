@@ -38,7 +38,7 @@ from .policy import (  # noqa: F401
     denoise, denoise_recompute, run_policy, Oracle,
 )
 from .ternary import (  # noqa: F401
-    bf16_round, quantize_rows, w2a8_accumulate, w2a8_linear, pack_ternary,
+    bf16_round, quantize_rows, w2a8_accumulate, w2a8_linear, w2a8_linear_grouped, pack_ternary,
     unpack_ternary,
 )
 from .metrics import e_inf, e_rel  # noqa: F401

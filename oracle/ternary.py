@@ -13,7 +13,9 @@ Readings where the page leaves a step open:
     float32 division;
   * the scale is applied as bf16(float(acc) * (alpha_m * beta)), each product
     rounded to float32; float(acc) is exact because |acc| < 2^24 here;
-  * beta is one scale per weight tensor (one output group), the per-tensor form;
+  * beta is one scale per weight tensor (one output group), the per-tensor form,
+    in the model; w2a8_linear_grouped takes the page's group-wise beta_g(n),
+    output channel n in group n // group_size;
   * packing: code = q + 1 in {0, 1, 2} (3 is invalid), four codes per byte,
     element 4j + i of a row in bits 2i..2i+1 of byte j (least significant
     first); rows are [out, in], in a multiple of 4.
@@ -82,6 +84,17 @@ def w2a8_linear(x, q, beta) -> np.ndarray:
     scale = (alpha * _F32(beta)).astype(_F32)
     y = (acc.astype(_F32) * scale[:, None]).astype(_F32)
     return bf16_round(y)
+
+
+def w2a8_linear_grouped(x, q, betas, group_size: int) -> np.ndarray:
+    """Eq. 4 with group-wise weight scales: y_mn = bf16(float(acc_mn) * (alpha_m * beta_g(n)))
+    with g(n) = n // group_size, betas [N / group_size]; float32 products, as w2a8_linear."""
+    a, alpha = quantize_rows(x)
+    acc = w2a8_accumulate(a, q)
+    n = np.arange(np.shape(q)[0])
+    beta_n = np.asarray(betas, dtype=_F32)[n // group_size]
+    scale = (alpha[:, None] * beta_n[None, :]).astype(_F32)
+    return bf16_round((acc.astype(_F32) * scale).astype(_F32))
 
 
 def pack_ternary(q) -> np.ndarray:

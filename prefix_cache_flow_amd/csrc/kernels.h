@@ -119,6 +119,11 @@ hipError_t gemm_w2a8(const int8_t* a, int lda, const uint32_t* qp, int M, int N,
 hipError_t gemm_w2a8_scalar(const int8_t* a, int lda, const uint32_t* qp, int M, int N, int K,
                             const Epilogue& epi, float beta_scalar, hipStream_t s);
 
+// The same on the vector ALU (v_dot4_i32_i8), bf16 STORE epilogue and/or raw
+// accumulators only; beta[n] from epi.beta when set, else beta_scalar.  K % 64 == 0.
+hipError_t gemm_w2a8_dot4(const int8_t* a, int lda, const uint32_t* qp, int M, int N, int K,
+                          const Epilogue& epi, float beta_scalar, hipStream_t s);
+
 // Canonical packed ternary [N][K/4] bytes -> library layout; flags[0] |= 1 on a code 3.
 hipError_t ternary_repack(const uint8_t* canon, int N, int K, uint32_t* out, int* flags, hipStream_t s);
 

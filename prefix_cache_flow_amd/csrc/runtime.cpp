@@ -1384,6 +1384,65 @@ extern "C" vla_status vla_w2a8_gemm(const int8_t* a, const float* alpha, const u
   return done(VLA_OK);
 }
 
+extern "C" vla_status vla_w2a8_gemm_ex(const int8_t* a, const float* alpha, const uint8_t* q_packed, const float* beta,
+                                       int32_t group, int32_t path, int32_t M, int32_t N, int32_t K, int32_t* acc_out,
+                                       uint16_t* y_bf16, void* stream, float* kernel_ms) {
+  if (!a || !alpha || !q_packed || !beta) return fail(VLA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (M <= 0 || N <= 0 || K <= 0) return fail(VLA_ERR_INVALID_ARGUMENT, "M, N and K must be positive");
+  if (group <= 0 || N % group) return fail(VLA_ERR_INVALID_ARGUMENT, "group must be positive and divide N");
+  if (path != VLA_W2A8_MFMA && path != VLA_W2A8_DOT4) return fail(VLA_ERR_INVALID_ARGUMENT, "bad path");
+  if (path == VLA_W2A8_MFMA && (K % 128 || N % 32)) return fail(VLA_ERR_UNSUPPORTED, "need K % 128 == 0 and N % 32 == 0");
+  if (path == VLA_W2A8_DOT4 && K % 64) return fail(VLA_ERR_UNSUPPORTED, "need K % 64 == 0");
+  std::vector<float> bn(N);
+  for (int n = 0; n < N; ++n) {
+    bn[n] = beta[n / group];
+    if (!std::isfinite(bn[n])) return fail(VLA_ERR_INVALID_ARGUMENT, "non-finite beta");
+  }
+  vla_status st = check_device();
+  if (st != VLA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* words = nullptr;
+  int* flags = nullptr;
+  float* bdev = nullptr;
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  auto done = [&](vla_status r) {
+    if (words) (void)hipFree(words);
+    if (flags) (void)hipFree(flags);
+    if (bdev) (void)hipFree(bdev);
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
+    return r;
+  };
+  if (hipMalloc(&words, (size_t)N * K / 4) != hipSuccess || hipMalloc(&flags, 64) != hipSuccess ||
+      hipMalloc(&bdev, (size_t)N * 4) != hipSuccess) {
+    (void)hipGetLastError();
+    return done(fail(VLA_ERR_OUT_OF_MEMORY, "staging"));
+  }
+  if (kernel_ms && (hipEventCreate(&ev[0]) != hipSuccess || hipEventCreate(&ev[1]) != hipSuccess))
+    return done(fail(VLA_ERR_DEVICE, "events"));
+  if (hipMemsetAsync(flags, 0, 64, s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "memset"));
+  if (ternary_repack(q_packed, N, K, words, flags, s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "repack"));
+  int hf = 0;
+  if (hipMemcpyAsync(&hf, flags, 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipMemcpyAsync(bdev, bn.data(), (size_t)N * 4, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return done(fail(VLA_ERR_DEVICE, "flag readback"));
+  if (hf) return done(fail(VLA_ERR_INVALID_ARGUMENT, "packed weights contain the invalid code 3"));
+  Epilogue e = epi_store(y_bf16, N, 0);
+  e.alpha = alpha;
+  e.beta = bdev;
+  e.acc_out = acc_out;
+  if (kernel_ms && hipEventRecord(ev[0], s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "event"));
+  const hipError_t le = path == VLA_W2A8_MFMA ? gemm_w2a8(a, K, words, M, N, K, e, s)
+                                               : gemm_w2a8_dot4(a, K, words, M, N, K, e, 0.f, s);
+  if (le != hipSuccess) return done(fail(VLA_ERR_DEVICE, "w2a8 launch"));
+  if (kernel_ms && hipEventRecord(ev[1], s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "event"));
+  if (hipStreamSynchronize(s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "w2a8 sync"));
+  if (kernel_ms && hipEventElapsedTime(kernel_ms, ev[0], ev[1]) != hipSuccess)
+    return done(fail(VLA_ERR_DEVICE, "elapsed"));
+  return done(VLA_OK);
+}
+
 extern "C" vla_status vla_ternary_pack(const int8_t* q, int32_t N, int32_t K, uint8_t* packed) {
   if (!q || !packed) return fail(VLA_ERR_INVALID_ARGUMENT, "NULL pointer");
   if (N <= 0 || K <= 0 || K % 4) return fail(VLA_ERR_INVALID_ARGUMENT, "need N, K > 0 and K % 4 == 0");

@@ -148,6 +148,82 @@ hipError_t gemm_w2a8(const int8_t* a, int lda, const uint32_t* qp, int M, int N,
   return gemm_w2a8_scalar(a, lda, qp, M, N, K, epi, 0.f, s);
 }
 
+// The same contraction on the vector ALU with v_dot4_i32_i8 (four int8
+// products summed into an int32 per lane and instruction): the counterpart of
+// the page's dp4a path, kept to compare against the matrix cores.  Tiles of
+// 64 rows x 64 output channels x 64 inputs: the activation slice (int8) and the
+// packed weight slice go through LDS, and each thread accumulates 4 rows x 4
+// channels, unpacking each weight word once for its four rows.  Integer sums
+// are exact, so the accumulators equal the MFMA kernel's bit for bit.
+__global__ __launch_bounds__(256) void k_gemm_w2a8_dot4(W2A8P p) {
+  constexpr int BM = 64, BN = 64, BK = 64, LDA = BK / 4 + 1, LDW = BK / 16 + 1;  // LDA, LDW in words
+  __shared__ uint32_t sA[BM * LDA];
+  __shared__ uint32_t sW[BN * LDW];
+  const int tm = blockIdx.x % p.nM, tn = blockIdx.x / p.nM;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, rg = tid >> 4, cg = tid & 15;
+  const int KW = p.K / 16;
+  int acc[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[r][j] = 0;
+  for (int k0 = 0; k0 < p.K; k0 += BK) {
+    // 64 rows x 16 words of activations, 64 channels x 4 words of weights
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = tid + i * 256, r = v >> 4, c = v & 15;
+      sA[r * LDA + c] = *(const uint32_t*)(p.a + (long)min(m0 + r, p.M - 1) * p.lda + k0 + c * 4);
+    }
+    {
+      const int r = tid >> 2, c = tid & 3;
+      sW[r * LDW + c] = p.q[(long)min(n0 + r, p.N - 1) * KW + k0 / 16 + c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int wi = 0; wi < BK / 16; ++wi) {
+      uint32_t wv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wv[j] = sW[(cg * 4 + j) * LDW + wi];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int q[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q[j] = (int)__builtin_amdgcn_perm(0u, 0x000100FFu, (wv[j] >> (2 * i)) & 0x03030303u);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int av = (int)sA[(rg * 4 + r) * LDA + wi * 4 + i];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[r][j] = __builtin_amdgcn_sdot4(av, q[j], acc[r][j], false);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  const Epilogue& e = p.epi;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = m0 + rg * 4 + r;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + cg * 4 + j;
+      if (n >= p.N) continue;
+      if (e.acc_out) e.acc_out[(long)m * p.N + n] = acc[r][j];
+      if (e.out) ((bf16_t*)e.out)[(long)m * e.ldo + n] = f2bf(w2a8_scale(p, m, n, acc[r][j]));
+    }
+  }
+}
+
+hipError_t gemm_w2a8_dot4(const int8_t* a, int lda, const uint32_t* qp, int M, int N, int K, const Epilogue& epi,
+                          float beta_scalar, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (K % 64 || !epi.alpha || epi.kind != EPI_STORE || epi.out_f32 || (lda % 4)) return hipErrorInvalidValue;
+  W2A8P p{a, lda, qp, M, N, K, (M + 63) / 64, (N + 63) / 64, epi, beta_scalar};
+  hipLaunchKernelGGL(k_gemm_w2a8_dot4, dim3(p.nM * p.nN), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 // canonical [N][K/4] bytes -> [N][K/16] words in the library's order
 __global__ void k_ternary_repack(const uint8_t* canon, int N, int K, uint32_t* out, int* flags) {
   const long words = (long)N * (K / 16);

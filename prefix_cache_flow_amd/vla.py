@@ -29,8 +29,9 @@ EXPORTS = (
     "vla_status_string", "vla_last_error", "vla_n_tensors", "vla_tensor_info", "vla_model_create",
     "vla_model_destroy", "vla_kv_cache_bytes", "vla_prefix_encode", "vla_denoise_chunk",
     "vla_kv_cache_release", "vla_kv_cache_info", "vla_quantize_rows_i8", "vla_w2a8_gemm",
-    "vla_ternary_pack", "vla_ternary_unpack", "vla_probe_arm", "vla_probe_read",
+    "vla_ternary_pack", "vla_ternary_unpack", "vla_probe_arm", "vla_probe_read", "vla_w2a8_gemm_ex",
 )
+W2A8_MFMA, W2A8_DOT4 = 0, 1
 PROBE_PREFIX_GATEUP, PROBE_PREFIX_DOWN, PROBE_PREFIX_QKV, PROBE_PREFIX_ATTN, PROBE_PREFIX_O, PROBE_CACHE = range(1, 7)
 
 
@@ -90,6 +91,7 @@ def lib():
         "vla_kv_cache_info": (I, [P, C.POINTER(I), C.POINTER(I)]),
         "vla_quantize_rows_i8": (I, [P, I, I, P, P, P]),
         "vla_w2a8_gemm": (I, [P, P, P, C.c_float, I, I, I, P, P, P]),
+        "vla_w2a8_gemm_ex": (I, [P, P, P, C.POINTER(C.c_float), I, I, I, I, I, P, P, P, C.POINTER(C.c_float)]),
         "vla_ternary_pack": (I, [P, I, I, P]),
         "vla_ternary_unpack": (I, [P, I, I, P]),
         "vla_probe_arm": (I, [P, I, I]),
@@ -351,6 +353,23 @@ def vla_quantize_rows_i8(x, stream=None):
     alpha = torch.empty((M,), dtype=torch.float32, device=x.device)
     _check(lib().vla_quantize_rows_i8(_ptr(x), M, K, _ptr(a), _ptr(alpha), _stream(stream)))
     return a, alpha
+
+
+def vla_w2a8_gemm_ex(a, alpha, q_packed, beta, group: int, path: int = W2A8_MFMA, want_acc: bool = True,
+                     want_y: bool = True, stream=None, timing: bool = False):
+    """As vla_w2a8_gemm with group-wise scales beta [N / group] (host floats) and a kernel choice;
+    returns (acc, y) or, with timing, (acc, y, kernel_ms)."""
+    import torch
+    M, K = a.shape
+    N = q_packed.shape[0]
+    b = (C.c_float * len(beta))(*[float(x) for x in beta])
+    acc = torch.empty((M, N), dtype=torch.int32, device=a.device) if want_acc else None
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if want_y else None
+    ms = C.c_float()
+    _check(lib().vla_w2a8_gemm_ex(_ptr(a), _ptr(alpha), _ptr(q_packed), b, int(group), int(path), M, N, K,
+                                  _ptr(acc) if acc is not None else None, _ptr(y) if y is not None else None,
+                                  _stream(stream), C.byref(ms) if timing else None))
+    return (acc, y, ms.value) if timing else (acc, y)
 
 
 def vla_w2a8_gemm(a, alpha, q_packed, beta: float, want_acc: bool = True, want_y: bool = True, stream=None):

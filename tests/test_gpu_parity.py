@@ -248,6 +248,30 @@ def test_w2a8_gemm_bit_exact(M, N, K):
     np.testing.assert_array_equal(y.float().cpu().numpy(), y_ref)
 
 
+@pytest.mark.parametrize("M,N,K", [(320, 7680, 2560), (320, 2560, 2560), (320, 13824, 2560), (320, 2560, 6912),
+                                   (37, 96, 384), (1, 64, 64)])
+def test_w2a8_dot4_path_and_grouped_scales(M, N, K):
+    """The vector-ALU dot4 kernel gives the oracle's int32 accumulators bit for bit (and so the
+    matrix-core kernel's), and both give the oracle's bf16 outputs with group-wise scales."""
+    rng = np.random.default_rng(3 * N + K)
+    x = _x_rows(M, K, K + 1)
+    a_ref, al_ref = oracle.quantize_rows(x)
+    q = rng.integers(-1, 2, (N, K), dtype=np.int8)
+    group = 32 if N % 32 == 0 else N
+    betas = rng.uniform(0.005, 0.05, N // group).astype(np.float32)
+    acc_ref = oracle.w2a8_accumulate(a_ref, q)
+    y_ref = oracle.w2a8_linear_grouped(x, q, betas, group)
+    packed = torch.from_numpy(oracle.pack_ternary(q)).cuda()
+    at, alt = torch.from_numpy(a_ref).cuda(), torch.from_numpy(al_ref).cuda()
+    paths = [vla.W2A8_DOT4] + ([vla.W2A8_MFMA] if K % 128 == 0 and N % 32 == 0 else [])
+    for path in paths:
+        acc, y = vla.vla_w2a8_gemm_ex(at, alt, packed, betas, group, path)
+        np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref, err_msg=f"path {path}")
+        np.testing.assert_array_equal(y.float().cpu().numpy(), y_ref, err_msg=f"path {path}")
+    with pytest.raises(vla.VlaError):
+        vla.vla_w2a8_gemm_ex(at, alt, packed, betas, N + 1, vla.W2A8_DOT4)  # group must divide N
+
+
 def test_w2a8_special_patterns():
     M, K = 64, 256
     rng = np.random.default_rng(5)

@@ -560,6 +560,24 @@ def test_w2a8_linear_composition():
             assert y[m, n] == np.float32(ref)
 
 
+def test_w2a8_grouped_scales():
+    """Group-wise beta_g(n): element by element in plain Python, torch's bf16 cast as the rounding
+    reference; one group over all channels is the per-tensor form."""
+    rng = np.random.default_rng(16)
+    x = rng.standard_normal((5, 32)).astype(np.float32)
+    q = rng.integers(-1, 2, (8, 32), dtype=np.int8)
+    betas = np.array([0.011, 0.023, 0.0071, 0.05], dtype=np.float32)
+    y = oracle.w2a8_linear_grouped(x, q, betas, 2)
+    a, alpha = oracle.quantize_rows(x)
+    for m in range(5):
+        for n in range(8):
+            acc = int(sum(int(u) * int(v) for u, v in zip(a[m], q[n])))
+            s = np.float32(alpha[m] * betas[n // 2])
+            ref = torch.tensor(float(np.float32(np.float32(acc) * s))).to(torch.bfloat16).item()
+            assert y[m, n] == np.float32(ref)
+    np.testing.assert_array_equal(oracle.w2a8_linear_grouped(x, q, betas[:1], 8), oracle.w2a8_linear(x, q, betas[0]))
+
+
 def test_pack_golden_roundtrip_and_invalid_code():
     g = golden("ternary_pack.json")
     q = np.array(g["q"], dtype=np.int8)
