@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void k_step_rows(StepRows a) {
 hipError_t step_rows(const StepRows& a, int w_f32, hipStream_t s) {
   if (a.M <= 0 || (a.k_head < 0 && a.k_embed < 0)) return hipSuccess;
   if (a.d_a > 256 || a.d_e > 4096) return hipErrorInvalidValue;
-  if (a.k_embed >= 0 && a.u_frag && (a.u_f32 || a.d_e % 32 || a.M > 64)) return hipErrorInvalidValue;
+  if (a.k_embed >= 0 && a.u_frag && (a.u_f32 || a.d_e % 32)) return hipErrorInvalidValue;
   if (a.pf.blocks < 0 || a.pf.blocks > 1024 || (a.pf.blocks && !a.pf.sink)) return hipErrorInvalidValue;
   // each part's form depends on the shapes only, so a step computes the same bits fused or alone
   const bool fh = !w_f32 && a.d_e % 64 == 0 && a.d_e <= 1024 && a.d_a <= 32;

@@ -652,7 +652,8 @@ static int prefix_splits(int64_t M, int N, int K) {
   return M <= 64 ? gemm_bf16_splits(K, kPrefixChunkSplits, (int)M) : gemm_frag_splits((int)M, N, K, 0);
 }
 static int expert_splits(int64_t M, int N, int K) {
-  return gemm_bf16_splits(K, M <= 64 ? kExpertSplits : gemm_bf16_auto_splits((int)M, N, K), (int)M);
+  // chunk-sized kernel up to 64 rows, the 288-row-tile kernel (its own split choice) above
+  return M <= 64 ? gemm_bf16_splits(K, kExpertSplits, (int)M) : gemm_frag_splits((int)M, N, K, 0);
 }
 // bf16 product with both operands in the fragment layout: the chunk-sized
 // kernel up to 64 rows, 288-row tiles above; split counts as prefix_splits
@@ -716,9 +717,9 @@ static WS plan(const vla_model* m, int64_t rows, int64_t erows, int64_t kvrows, 
   const int64_t qe = (int64_t)c.Hq_e * c.hd_e, qkve = (int64_t)(c.Hq_e + 2 * c.Hkv_e) * c.hd_e;
   w.X = (float*)take(erows * c.d_a * 4);
   w.E = (float*)take(erows * c.d_e * 4);
-  // GEMM inputs of the chunk: the fragment-layout kernel reads 1, 2 or 4 whole
-  // 16-row blocks, so up to 64 rows the buffers hold 64
-  const int64_t frows = erows <= 64 ? 64 : erows;
+  // GEMM inputs of the chunk (bf16: fragment layout, whole 16-row blocks, and
+  // the chunk-sized kernel reads 1, 2 or 4 of them: at least 64 rows)
+  const int64_t frows = m->f32 ? std::max<int64_t>(64, erows) : std::max<int64_t>(64, (erows + 15) / 16 * 16);
   w.eu = take(frows * c.d_e * es);
   w.eqkv = take(erows * qkve * es);
   const int64_t kvblk = c.H > 0 ? erows / c.H * c.Hkv_e * key_rows(m, c.H) * c.hd_e : 0;
@@ -1091,8 +1092,11 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
   Epilogue qkv_e;  // bf16 fused self-attention projection
   qkv_e.kind = EPI_QKV; qkv_e.out = w.eqkv; qkv_e.ldo = qe; qkv_e.nq = qe;
   qkv_e.kout = w.ek; qkv_e.vout = w.ev; qkv_e.hkv = c.Hkv_e; qkv_e.hd = c.hd_e; qkv_e.npre = H; qkv_e.npad = Hp;
-  // up to 64 chunk rows: GEMM inputs in the fragment layout, weights always are (bf16)
-  const int fr = (!f32 && M <= 64) ? 1 : 0;
+  // bf16: every GEMM input in the fragment layout (weights always are); up to
+  // 64 chunk rows the chunk-sized kernel with weight prefetch, above that the
+  // 288-row-tile kernel of the prefix
+  const int fr = f32 ? 0 : 1;
+  const bool small = fr && M <= 64;
   sa.o_frag = fr;
   // cross-attention into the cache [B][L_e][2][Hkv_e][N][hd_e]
   AttnArgs ca = sa;
@@ -1125,7 +1129,7 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
   const size_t g_d = gemm_chunk_group_bytes(M, c.d_e, c.F_e, EPI_PARTIAL, S_d);
   auto pfr = [&](const void* p, size_t bytes, size_t group, const void* p2, size_t bytes2, size_t group2, int blocks) {
     Prefetch f;
-    if (!fr) return f;
+    if (!small) return f;
     f.p = p; f.bytes = bytes; f.group = group;
     f.p2 = p2; f.bytes2 = p2 ? bytes2 : 0; f.group2 = p2 ? group2 : 0;
     f.sink = w.sink; f.blocks = blocks;
@@ -1187,11 +1191,13 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
       } else {
         const uint16_t* u = (const uint16_t*)w.eu;
         // C = A W^T on the chunk: fragment-layout operands up to 64 rows, else the tiled kernel
+        // (splits: the chunk kernel's request; the wide kernel picks its own, as expert_splits says)
         auto mm = [&](const void* A, int lda, const void* W, int N, int K, const Epilogue& ep, int splits) {
-          if (fr) return gemm_chunk((const uint16_t*)A, (const uint16_t*)W, M, N, K, ep, splits, w.epart, s);
-          return gemm_bf16((const uint16_t*)A, lda, (const uint16_t*)W, K, M, N, K, ep, splits, w.epart, s, 1);
+          (void)lda;
+          if (small) return gemm_chunk((const uint16_t*)A, (const uint16_t*)W, M, N, K, ep, splits, w.epart, s);
+          return gemm_frag((const uint16_t*)A, (const uint16_t*)W, M, N, K, ep, 0, w.epart, s);
         };
-        K_TRY(mm(u, c.d_e, L.wqkv, qkve, c.d_e, qkv_e, fr ? 1 : expert_splits(M, qkve, c.d_e)), "qkv_s");
+        K_TRY(mm(u, c.d_e, L.wqkv, qkve, c.d_e, qkv_e, 1), "qkv_s");
         if (m->joint) {
           // one attention over the chunk and prefix layer e, then the MLP
           sa.pf = pfr(L.wos, b_o, g_o, L.wgu, b_gu, g_gu, 192);
@@ -1207,7 +1213,7 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
           const Prefetch pf_kv = pfr(B == 1 ? ca.k : nullptr, B == 1 ? layer_kv : 0, 0, nullptr, 0, 0, 64);
           K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_kv),
                 "norm");
-          K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, epi_store(w.eq, qe, 0), fr ? 1 : expert_splits(M, qe, c.d_e)), "q_c");
+          K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, epi_store(w.eq, qe, 0), 1), "q_c");
           ca.pf = pfr(L.woc, b_o, g_o, L.wgu, b_gu, g_gu, 192);
           K_TRY(attention_chunk(ca, s), "cross attn");
           K_TRY(mm(w.eattn, qe, L.woc, c.d_e, qe, pe, S_o), "o_c");
@@ -1218,7 +1224,7 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
         Epilogue g = epi_store(w.emlp, c.F_e, 0);
         g.kind = EPI_GEGLU;
         g.out_frag = fr;
-        K_TRY(mm(u, c.d_e, L.wgu, 2 * c.F_e, c.d_e, g, fr ? 1 : expert_splits(M, 2 * c.F_e, c.d_e)), "gate/up");
+        K_TRY(mm(u, c.d_e, L.wgu, 2 * c.F_e, c.d_e, g, 1), "gate/up");
         K_TRY(mm(w.emlp, c.F_e, L.wd, c.d_e, c.F_e, pe, S_d), "down");
         // next layer's QKV weights (and, joint, its cache block)
         const void* next_kv = m->joint && B == 1 ? (const char*)ca.k + (size_t)layer_stride * es : nullptr;
