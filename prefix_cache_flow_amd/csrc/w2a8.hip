@@ -12,7 +12,8 @@
 // model is created.
 //
 // Tiles: 64 activation rows x 128 output channels x 128 inputs per slice,
-// four waves of 32 x 64 on the 32x32x32 int8 MFMA.  The activation slice is
+// four waves of 64 x 32 on the 32x32x32 int8 MFMA (a wave's unpacked weight
+// fragment serves both 32-row halves).  The activation slice is
 // staged in LDS as int8; the weight slice is staged *packed* (2 bits per weight,
 // a quarter of the int8 bytes) and unpacked in registers right before the MFMA.
 #include "common.h"
@@ -42,8 +43,11 @@ __device__ __forceinline__ float w2a8_scale(const W2A8P& p, int m, int n, int ac
   return bf2f(f2bf((float)acc * s));
 }
 
+template <int BK>
 __global__ __launch_bounds__(256) void k_gemm_w2a8(W2A8P p) {
-  constexpr int BM = 64, BN = 128, BK = 128, LDA = BK + 16, LDW = BK / 16 + 1;
+  constexpr int BM = 64, BN = 128, LDA = BK + 16, LDW = BK / 16 + 1;
+  constexpr int AV = BM * BK / 16 / 256;  // 16-byte activation vectors per thread and slice
+  constexpr int WV = BN * BK / 64 / 256;  // 4-word weight vectors per thread and slice
   __shared__ __attribute__((aligned(16))) int8_t sA[2][BM * LDA];
   __shared__ uint32_t sW[2][BN * LDW];
   const int nt = p.nM * p.nN, L = blockIdx.x;
@@ -51,29 +55,39 @@ __global__ __launch_bounds__(256) void k_gemm_w2a8(W2A8P p) {
   const int tm = tile % p.nM, tn = tile / p.nM;
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
   const int KW = p.K / 16;  // words per weight row
 
-  u32x4_t ra[2], rw;
-  auto gload = [&](int k0) {
+  // Two register sets, each filled two slices before its trip to LDS, so a
+  // slice's global loads have two slices of work to land behind.
+  const int ns = p.K / BK;
+  struct Regs { u32x4_t a[AV], w[WV]; };
+  constexpr int AR = BK / 16, WR = BK / 64;  // vectors per activation row, per weight row
+  auto gload = [&](Regs& g, int sl) {
+    const int k0 = min(sl, ns - 1) * BK;  // past the end: the last slice again (never used)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int v = tid + i * 256, r = v >> 3, c = (v & 7) * 16;
+    for (int i = 0; i < AV; ++i) {
+      const int v = tid + i * 256, r = v / AR, c = (v % AR) * 16;
       // rows past the end are clamped to valid ones; their results are never stored
-      ra[i] = *(const u32x4_t*)(p.a + (long)min(m0 + r, p.M - 1) * p.lda + k0 + c);
+      g.a[i] = *(const u32x4_t*)(p.a + (long)min(m0 + r, p.M - 1) * p.lda + k0 + c);
     }
-    const int r = tid >> 1, c = (tid & 1) * 4;  // 128 rows x 8 words
-    rw = *(const u32x4_t*)(p.q + (long)min(n0 + r, p.N - 1) * KW + k0 / 16 + c);
+#pragma unroll
+    for (int i = 0; i < WV; ++i) {
+      const int v = tid + i * 256, r = v / WR, c = (v % WR) * 4;
+      g.w[i] = *(const u32x4_t*)(p.q + (long)min(n0 + r, p.N - 1) * KW + k0 / 16 + c);
+    }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](const Regs& g, int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < AV; ++i) {
       const int v = tid + i * 256;
-      *(u32x4_t*)&sA[buf][(v >> 3) * LDA + (v & 7) * 16] = ra[i];
+      *(u32x4_t*)&sA[buf][(v / AR) * LDA + (v % AR) * 16] = g.a[i];
     }
-    const int r = tid >> 1, c = (tid & 1) * 4;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) sW[buf][r * LDW + c + t] = rw[t];
+    for (int i = 0; i < WV; ++i) {
+      const int v = tid + i * 256, r = v / WR, c = (v % WR) * 4;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sW[buf][r * LDW + c + t] = g.w[i][t];
+    }
   };
 
   i32x16_t acc[2];
@@ -81,38 +95,51 @@ __global__ __launch_bounds__(256) void k_gemm_w2a8(W2A8P p) {
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[j][e] = 0;
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  int it = 0;
-  for (int k0 = 0; k0 < p.K; k0 += BK, ++it) {
-    const int buf = it & 1;
-    const bool more = k0 + BK < p.K;
-    if (more) gload(k0 + BK);
+  // wave w owns output channels 32 w .. 32 w + 31 for all 64 rows: each
+  // weight word it unpacks feeds two MFMAs (the two 32-row halves)
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
-      const i32x4_t af = __builtin_bit_cast(
-          i32x4_t, *(const u32x4_t*)&sA[buf][(wm * 32 + (lane & 31)) * LDA + kk * 32 + (lane >> 5) * 16]);
+      const uint32_t w = sW[buf][(wid * 32 + (lane & 31)) * LDW + kk * 2 + (lane >> 5)];
+      const i32x4_t wf = unpack16(w);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint32_t w = sW[buf][(wn * 64 + j * 32 + (lane & 31)) * LDW + kk * 2 + (lane >> 5)];
-        acc[j] = mfma32x32x32_i8(af, unpack16(w), acc[j]);
+      for (int i = 0; i < 2; ++i) {
+        const i32x4_t af = __builtin_bit_cast(
+            i32x4_t, *(const u32x4_t*)&sA[buf][(i * 32 + (lane & 31)) * LDA + kk * 32 + (lane >> 5) * 16]);
+        acc[i] = mfma32x32x32_i8(af, wf, acc[i]);
       }
     }
-    if (more) sstore(buf ^ 1);
+  };
+
+  Regs r0, r1;
+  gload(r0, 0);
+  gload(r1, 1);
+  sstore(r0, 0);
+  __syncthreads();
+  gload(r0, 2);
+  // entering a pair at slice sl: slice sl in LDS buffer 0, sl + 1 in r1, sl + 2 in r0
+  int sl = 0;
+  for (; sl + 2 <= ns; sl += 2) {
+    compute(0);
+    sstore(r1, 1);
     __syncthreads();
+    gload(r1, sl + 3);
+    compute(1);
+    sstore(r0, 0);
+    __syncthreads();
+    gload(r0, sl + 4);
   }
+  if (sl < ns) compute(0);  // an odd slice count ends with one more, already in buffer 0
 
   const Epilogue& e = p.epi;
+  const int n = n0 + wid * 32 + (lane & 31);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+  for (int i = 0; i < 2; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * 32 + mfma32_row(r, lane);
+      const int m = m0 + i * 32 + mfma32_row(r, lane);
       const bool ok = m < p.M && n < p.N;
-      const int accv = acc[j][r];
+      const int accv = acc[i][r];
       if (e.acc_out && ok) e.acc_out[(long)m * p.N + n] = accv;
       const float y = ok ? w2a8_scale(p, m, n, accv) : 0.f;
       if (e.kind == EPI_GEGLU) {
@@ -139,7 +166,10 @@ hipError_t gemm_w2a8_scalar(const int8_t* a, int lda, const uint32_t* qp, int M,
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K % 128 || N % 32 || !epi.alpha) return hipErrorInvalidValue;
   W2A8P p{a, lda, qp, M, N, K, (M + 63) / 64, (N + 127) / 128, epi, beta_scalar};
-  hipLaunchKernelGGL(k_gemm_w2a8, dim3(p.nM * p.nN), dim3(256), 0, s, p);
+  // 256-wide K slices when they divide K: a weight row's slice is then 64
+  // contiguous bytes and the per-slice overhead is spread over twice the MFMAs
+  if (K % 256 == 0) hipLaunchKernelGGL(k_gemm_w2a8<256>, dim3(p.nM * p.nN), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(k_gemm_w2a8<128>, dim3(p.nM * p.nN), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
