@@ -33,8 +33,8 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per launch of the prefix gate/up kernel from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE),
 # scaled by what the same counters read for a plain copy (profiles/hbm_bytes_prefix_gateup_single_camera_bf16.md).
 # Valid only for the kernel instance named here; None once that kernel changes until it is measured again.
-GATEUP_KERNEL = "k_gemm_af<2, false, 128>"
-GATEUP_TRAFFIC_BYTES = 153454624
+GATEUP_KERNEL = "k_gemm_af8<2, false>"
+GATEUP_TRAFFIC_BYTES = None
 
 
 def parse():

@@ -743,6 +743,166 @@ __global__ __launch_bounds__(256, BN == 64 ? 2 : 1) void k_gemm_af(FragP p) {
   }
 }
 
+// The same 288 x 128 tile with eight waves, two per SIMD: wave w owns row
+// blocks w, w + 8 (and w + 16 for waves 0 and 1), so SIMD s carries waves s and
+// s + 4 with five or four row blocks between them, as the four-wave kernel.
+// While one wave of a SIMD waits (on its loads, the LDS or the barrier) the
+// other issues MFMAs.  Each wave holds at most 3 x 8 accumulators, so both fit
+// the SIMD's registers; the weight slice's 16 fragments are staged by all 512
+// threads, two vectors each.  GeGLU, partial-sum and plain store epilogues.
+template <int TBW, int KIND, bool ODD>
+__device__ __forceinline__ void af8_body(const FragP& p, u32x4_t (*sw)[16][64], int w, int lane, int tm, int tn,
+                                         int split, int nsl, int kb0) {
+  constexpr int RB = kFragBM / 16, NB = 8, KS = 2, BN = 128;
+  const int KSt = p.K >> 5;
+  const int mbt = (p.M + 15) >> 4, nbt = p.N >> 4;
+  const char* ab[TBW];
+#pragma unroll
+  for (int i = 0; i < TBW; ++i)
+    ab[i] = (const char*)p.A + ((long)min(tm * RB + w + 8 * i, mbt - 1) * KSt + kb0) * 1024;
+  const char* wb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int f = w + 8 * i, nb = f / KS, kk = f % KS;
+    wb[i] = (const char*)p.W + ((long)min(tn * NB + nb, nbt - 1) * KSt + kb0 + kk) * 1024;
+  }
+  const uint32_t lo = lane * 16;
+  auto soff = [&](int s) { return (uint32_t)min(s, max(nsl - 1, 0)) * (KS * 1024); };
+  u32x4_t a0[TBW][KS], a1[TBW][KS], w0[2], w1[2];
+  auto lda = [&](u32x4_t(&a)[TBW][KS], int s) {
+    const uint32_t o = soff(s) + lo;
+#pragma unroll
+    for (int i = 0; i < TBW; ++i)
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) a[i][kk] = *(const u32x4_t*)(ab[i] + o + kk * 1024);
+  };
+  auto ldw = [&](u32x4_t(&r)[2], int s) {
+    const uint32_t o = soff(s) + lo;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) r[i] = *(const u32x4_t*)(wb[i] + o);
+  };
+  auto stw = [&](const u32x4_t(&r)[2], int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) sw[buf][w + 8 * i][lane] = r[i];
+  };
+  f32x4_t acc[TBW][NB];
+  auto compute = [&](const u32x4_t(&a)[TBW][KS], int buf, auto first) {
+    bf16x8_t b[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) b[j] = as_bf16x8(sw[buf][j * KS][lane]);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+#pragma unroll
+        for (int i = 0; i < TBW; ++i) {
+          if (decltype(first)::value && kk == 0) mfma16_acc<true>(acc[i][j], b[j], as_bf16x8(a[i][kk]));
+          else mfma16_acc<false>(acc[i][j], b[j], as_bf16x8(a[i][kk]));
+        }
+        if (kk + 1 < KS) b[j] = as_bf16x8(sw[buf][j * KS + kk + 1][lane]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  using First = std::integral_constant<bool, true>;
+  using Next = std::integral_constant<bool, false>;
+  ldw(w0, 0);
+  ldw(w1, 1);
+  lda(a0, 0);
+  lda(a1, 1);
+  stw(w0, 0);
+  ldw(w0, 2);
+  __syncthreads();
+  auto two_slices = [&](int s, auto first) {
+    stw(w1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    ldw(w1, s + 3);
+    compute(a0, 0, first);
+    __builtin_amdgcn_sched_barrier(0);
+    lda(a0, s + 2);
+    __syncthreads();
+    stw(w0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    ldw(w0, s + 4);
+    if (ODD && s + 1 >= nsl) {
+#pragma unroll
+      for (int i = 0; i < TBW; ++i)
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) a1[i][kk] = u32x4_t{0, 0, 0, 0};
+    }
+    compute(a1, 1, Next{});
+    __builtin_amdgcn_sched_barrier(0);
+    lda(a1, s + 3);
+    __syncthreads();
+  };
+  two_slices(0, First{});
+  for (int s = 2; s < nsl; s += 2) two_slices(s, Next{});
+  mfma_wait_states();
+#pragma unroll
+  for (int i = 0; i < TBW; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) asm volatile("" : "+a"(acc[i][j]));
+  const int cq = (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < TBW; ++i) {
+    const int rb = w + 8 * i;
+    const int m = tm * kFragBM + rb * 16 + (lane & 15);
+    if (rb >= RB || m >= p.M) continue;
+    if (KIND == EPI_GEGLU) {
+#pragma unroll
+      for (int j = 0; j < NB; j += 2) {
+        const int n = tn * BN + j * 16;
+        if (n >= p.N) break;
+        const int f = (n >> 1) + cq;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = gelu_erf(acc[i][j][e]) * acc[i][j + 1][e];
+        const Epilogue& E = p.epi;
+        if (E.out_f32) {
+          *(f32x4_t*)((float*)E.out + (long)m * E.ldo + f) = f32x4_t{v[0], v[1], v[2], v[3]};
+        } else {
+          const long o = E.out_frag ? frag_idx(m, f, E.ldo) : (long)m * E.ldo + f;
+          *(u32x2_t*)((bf16_t*)E.out + o) = pack4_bf16(v[0], v[1], v[2], v[3]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int n = tn * BN + j * 16 + cq;
+        if (n >= p.N) break;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = acc[i][j][e];
+          asm volatile("" : "+v"(x[e]));
+        }
+        const f32x4_t v = f32x4_t{x[0], x[1], x[2], x[3]};
+        const bool f32 = KIND == EPI_PARTIAL || p.epi.out_f32;
+        void* out = KIND == EPI_PARTIAL ? (void*)(p.ws + (long)split * p.M * p.N) : p.epi.out;
+        const long o = (long)m * (KIND == EPI_PARTIAL ? p.N : p.epi.ldo) + n;
+        if (f32) *(f32x4_t*)((float*)out + o) = v;
+        else *(u32x2_t*)((bf16_t*)out + o) = pack4_bf16(v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+}
+
+template <int KIND, bool ODD>
+__global__ __launch_bounds__(512, 1) void k_gemm_af8(FragP p) {
+  static_assert(KIND == EPI_GEGLU || KIND == EPI_PARTIAL || KIND == EPI_STORE, "epilogue kinds of the 8-wave kernel");
+  __shared__ u32x4_t sw[2][16][64];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int total = gridDim.x, L = blockIdx.x;
+  const int q = (total % 8 == 0) ? (L % 8) * (total / 8) + L / 8 : L;
+  const int ntile = p.nM * p.nN;
+  const int split = q / ntile, tile = q - split * ntile;
+  const int tm = tile % p.nM, tn = tile / p.nM;
+  const int kb0 = split * (p.kchunk >> 5);
+  const int nsl = max(0, min(p.kchunk, p.K - split * p.kchunk) >> 6);
+  if (w < 2) af8_body<3, KIND, ODD>(p, sw, w, lane, tm, tn, split, nsl, kb0);
+  else af8_body<2, KIND, ODD>(p, sw, w, lane, tm, tn, split, nsl, kb0);
+}
+
 // K is cut into chunks of an even number of 64-wide slices (the kernel runs
 // slices in pairs; only the last chunk may hold an odd count); `splits` <= 0
 // asks for a count that fills the chip, about one workgroup per CU with at
@@ -782,6 +942,17 @@ static hipError_t launch_af(const FragP& p, int kind, dim3 grid, hipStream_t s) 
   return hipGetLastError();
 }
 
+template <bool ODD>
+static hipError_t launch_af8(const FragP& p, int kind, dim3 grid, hipStream_t s) {
+  switch (kind) {
+    case EPI_STORE: hipLaunchKernelGGL((k_gemm_af8<EPI_STORE, ODD>), grid, dim3(512), 0, s, p); break;
+    case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_af8<EPI_GEGLU, ODD>), grid, dim3(512), 0, s, p); break;
+    case EPI_PARTIAL: hipLaunchKernelGGL((k_gemm_af8<EPI_PARTIAL, ODD>), grid, dim3(512), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t gemm_frag(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, const Epilogue& epi, int splits,
                      float* ws, hipStream_t s) {
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
@@ -802,8 +973,13 @@ hipError_t gemm_frag(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K
   const dim3 grid(p.nM * p.nN * splits);
   const int kind = splits > 1 ? EPI_PARTIAL : kind0;
   const bool odd = (K / 64) % 2;
-  hipError_t err = bn == 64 ? (odd ? launch_af<true, 64>(p, kind, grid, s) : launch_af<false, 64>(p, kind, grid, s))
-                            : (odd ? launch_af<true, 128>(p, kind, grid, s) : launch_af<false, 128>(p, kind, grid, s));
+  hipError_t err;
+  if (bn == 128 && (kind == EPI_GEGLU || kind == EPI_PARTIAL || kind == EPI_STORE)) {
+    err = odd ? launch_af8<true>(p, kind, grid, s) : launch_af8<false>(p, kind, grid, s);  // eight waves
+  } else {
+    err = bn == 64 ? (odd ? launch_af<true, 64>(p, kind, grid, s) : launch_af<false, 64>(p, kind, grid, s))
+                   : (odd ? launch_af<true, 128>(p, kind, grid, s) : launch_af<false, 128>(p, kind, grid, s));
+  }
   if (err != hipSuccess) return err;
   if (splits > 1 && kind0 != EPI_PARTIAL) {
     const long total = (long)M * N / 4;
