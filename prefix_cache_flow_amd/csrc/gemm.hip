@@ -963,7 +963,11 @@ hipError_t gemm_frag(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K
   if (epi.out_frag && kind0 != EPI_GEGLU && kind0 != EPI_CACHE) return hipErrorInvalidValue;
   if (epi.out_frag && epi.out_f32) return hipErrorInvalidValue;
   const int bn = frag_bn(N, K);
-  const int per = frag_per(M, N, K, splits, bn);
+  int per = frag_per(M, N, K, splits, bn);
+  // A product that finishes here (not partials for a row kernel) pays for every
+  // split twice, writing its partial slab and reading it back in the
+  // reduction: the automatic choice stops at 4 for those.
+  if (splits <= 0 && kind0 != EPI_PARTIAL && ((K / 64 + 1) / 2 + per - 1) / per > 4) per = frag_per(M, N, K, 4, bn);
   splits = ((K / 64 + 1) / 2 + per - 1) / per;
   if ((splits > 1 || kind0 == EPI_PARTIAL) && !ws) return hipErrorInvalidValue;
   FragP p{Af, Wf, M, N, K, 0, 0, 0, epi, ws};
