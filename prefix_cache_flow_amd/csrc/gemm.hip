@@ -1058,9 +1058,8 @@ struct ChunkP {
   float* ws;
 };
 
-template <int NB, int MB, int KIND>
+template <int NB, int MB, int KIND, int SPW>
 __global__ __launch_bounds__(256) void k_chunk(ChunkP p) {
-  constexpr int SPW = kSkinnySteps;
   __shared__ float red[4][MB * NB * 4][64];  // [wave][row block, column block, element][lane]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -1131,17 +1130,29 @@ __global__ __launch_bounds__(256) void k_chunk(ChunkP p) {
   }
 }
 
-template <int MB>
-static hipError_t launch_chunk_mb(const ChunkP& p, int kind, dim3 grid, hipStream_t s) {
+template <int MB, int SPW>
+static hipError_t launch_chunk_spw(const ChunkP& p, int kind, dim3 grid, hipStream_t s) {
   switch (kind) {
-    case EPI_GEGLU: hipLaunchKernelGGL((k_chunk<2, MB, EPI_GEGLU>), grid, dim3(256), 0, s, p); break;
-    case EPI_STORE: hipLaunchKernelGGL((k_chunk<1, MB, EPI_STORE>), grid, dim3(256), 0, s, p); break;
-    case EPI_QKV: hipLaunchKernelGGL((k_chunk<1, MB, EPI_QKV>), grid, dim3(256), 0, s, p); break;
-    case EPI_CACHE: hipLaunchKernelGGL((k_chunk<1, MB, EPI_CACHE>), grid, dim3(256), 0, s, p); break;
-    case EPI_PARTIAL: hipLaunchKernelGGL((k_chunk<1, MB, EPI_PARTIAL>), grid, dim3(256), 0, s, p); break;
+    case EPI_GEGLU: hipLaunchKernelGGL((k_chunk<2, MB, EPI_GEGLU, SPW>), grid, dim3(256), 0, s, p); break;
+    case EPI_STORE: hipLaunchKernelGGL((k_chunk<1, MB, EPI_STORE, SPW>), grid, dim3(256), 0, s, p); break;
+    case EPI_QKV: hipLaunchKernelGGL((k_chunk<1, MB, EPI_QKV, SPW>), grid, dim3(256), 0, s, p); break;
+    case EPI_CACHE: hipLaunchKernelGGL((k_chunk<1, MB, EPI_CACHE, SPW>), grid, dim3(256), 0, s, p); break;
+    case EPI_PARTIAL: hipLaunchKernelGGL((k_chunk<1, MB, EPI_PARTIAL, SPW>), grid, dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// A wave loads SPW k-steps at once: the smallest of 2, 4 and 8 that covers its
+// quarter of the workgroup's K chunk, so no wave fetches fragments it would
+// mask off (a fixed 8 made the O projections, four k-steps per wave, fetch
+// twice their bytes).
+template <int MB>
+static hipError_t launch_chunk_mb(const ChunkP& p, int kind, dim3 grid, hipStream_t s) {
+  const int steps = p.kchunk >> 7;
+  if (steps <= 2) return launch_chunk_spw<MB, 2>(p, kind, grid, s);
+  if (steps <= 4) return launch_chunk_spw<MB, 4>(p, kind, grid, s);
+  return launch_chunk_spw<MB, kSkinnySteps>(p, kind, grid, s);
 }
 
 hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, const Epilogue& epi, int splits,
