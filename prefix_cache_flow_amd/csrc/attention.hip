@@ -241,13 +241,9 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
   __shared__ float mbuf[4][16], lbuf[4][16];
   __shared__ __attribute__((aligned(16))) float obuf[4][16][LDO];
 
+  if (prefetch_layer(a.pf)) return;  // extra workgroups: warm the next weights
   const int G = a.Hq / a.Hkv, R = G * a.Nq;
-  const int nrb = (R + 15) / 16;
-  if ((int)blockIdx.x >= nrb) {  // extra workgroups (first batch and group only): warm the next weights
-    if (blockIdx.y == 0 && blockIdx.z == 0) prefetch_share(a.pf, blockIdx.x, nrb, gridDim.x - nrb);
-    return;
-  }
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.y % a.Hkv, b = blockIdx.y / a.Hkv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   int r = min((int)blockIdx.x * 16 + col, R - 1);  // clamped rows are computed, never stored
@@ -415,7 +411,8 @@ hipError_t attention_chunk(const AttnArgs& a, hipStream_t s) {
   if (a.Nk2 < 0 || (a.Nk2 && (!a.k2 || !a.v2))) return hipErrorInvalidValue;
   if (a.pf.blocks < 0 || a.pf.blocks > 1024 || (a.pf.blocks && !a.pf.sink)) return hipErrorInvalidValue;
   const int R = a.Hq / a.Hkv * a.Nq;
-  dim3 grid((R + 15) / 16 + a.pf.blocks, a.Hkv, a.B);
+  const int per = (R + 15) / 16 * a.Hkv * a.B;
+  dim3 grid((R + 15) / 16, a.Hkv * a.B, prefetch_depth(per, a.pf.blocks));
   switch (a.hd) {
     case 64: hipLaunchKernelGGL(k_attn_chunk<64>, grid, dim3(256), 0, s, a); break;
     case 128: hipLaunchKernelGGL(k_attn_chunk<128>, grid, dim3(256), 0, s, a); break;

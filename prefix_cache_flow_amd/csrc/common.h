@@ -205,6 +205,18 @@ __device__ __forceinline__ void prefetch_share(const Prefetch& f, int L, int fir
   if (x == 0x9E3779B9u) f.sink[L & 63] = x;
 }
 
+// A kernel's own workgroups form grid layer z = 0; its prefetch workgroups
+// follow in layers z >= 1 (workgroups are numbered x fastest, then y, then z,
+// which is the order they reach the XCDs).  The test reads the dispatch index
+// register: a test on a kernel argument made the kernel's own work wait for a
+// first scalar load before its remaining arguments were even requested.
+__device__ __forceinline__ bool prefetch_layer(const Prefetch& f) {
+  if (!blockIdx.z) return false;
+  const int per = gridDim.x * gridDim.y;
+  prefetch_share(f, per * blockIdx.z + gridDim.x * blockIdx.y + blockIdx.x, per, per * (gridDim.z - 1));
+  return true;
+}
+
 // acc row index of element i for lane l in a 32x32 MFMA block
 __device__ __forceinline__ int mfma32_row(int i, int lane) { return (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3); }
 

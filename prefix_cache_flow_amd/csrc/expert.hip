@@ -31,11 +31,8 @@ __global__ __launch_bounds__(256) void k_step_rows(StepRows a) {
   __shared__ float red[4];
   __shared__ float us[4096];
   __shared__ float xs[256];
+  if (prefetch_layer(a.pf)) return;  // extra workgroups: warm the next kernel's weights
   const int m = blockIdx.x;
-  if (m >= a.M) {  // extra workgroups: warm the next kernel's weights
-    prefetch_share(a.pf, m, a.M, gridDim.x - a.M);
-    return;
-  }
   const int tid = threadIdx.x;
   const bool head = a.k_head >= 0, emb = a.k_embed >= 0;
   constexpr int G = 8;  // threads per head output
@@ -198,7 +195,7 @@ hipError_t step_rows(const StepRows& a, int w_f32, hipStream_t s) {
   // each part's form depends on the shapes only, so a step computes the same bits fused or alone
   const bool fh = !w_f32 && a.d_e % 64 == 0 && a.d_e <= 1024 && a.d_a <= 32;
   const bool fe = !w_f32 && a.d_a % 8 == 0 && a.d_a <= 32 && a.d_e <= 1024;
-  const dim3 grid(a.M + a.pf.blocks);
+  const dim3 grid(a.M, 1, prefetch_depth(a.M, a.pf.blocks));
   if (w_f32) hipLaunchKernelGGL((k_step_rows<true, false, false>), grid, dim3(256), 0, s, a);
   else if (fh && fe) hipLaunchKernelGGL((k_step_rows<false, true, true>), grid, dim3(256), 0, s, a);
   else if (fh) hipLaunchKernelGGL((k_step_rows<false, true, false>), grid, dim3(256), 0, s, a);

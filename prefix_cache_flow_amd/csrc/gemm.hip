@@ -1056,16 +1056,19 @@ struct ChunkP {
   int M, N, K, kchunk;
   Epilogue epi;
   float* ws;
+  Prefetch pf;  // read by grid layers z >= 1, if any
 };
 
 template <int NB, int MB, int KIND, int SPW>
 __global__ __launch_bounds__(256) void k_chunk(ChunkP p) {
   __shared__ float red[4][MB * NB * 4][64];  // [wave][row block, column block, element][lane]
+  if (prefetch_layer(p.pf)) return;
+  const int bx = blockIdx.x, by = blockIdx.y;  // column group, K chunk
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int nb0 = blockIdx.x * NB;  // first 16-column block of the workgroup
-  const int KS = p.K >> 5;          // k-steps (fragments per 16-row block)
-  const int sb = (blockIdx.y * p.kchunk + w * (p.kchunk >> 2)) >> 5;
+  const int nb0 = bx * NB;  // first 16-column block of the workgroup
+  const int KS = p.K >> 5;  // k-steps (fragments per 16-row block)
+  const int sb = (by * p.kchunk + w * (p.kchunk >> 2)) >> 5;
   const int nsteps = max(0, min(KS - sb, p.kchunk >> 7));
   const u32x4_t* Wv = (const u32x4_t*)p.W + lane;
   const u32x4_t* Av = (const u32x4_t*)p.A + lane;
@@ -1124,7 +1127,7 @@ __global__ __launch_bounds__(256) void k_chunk(ChunkP p) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int n = (nb0 + nb) * 16 + col;
-      if (KIND == EPI_PARTIAL) p.ws[((long)blockIdx.y * p.M + m) * p.N + n] = v[nb][e];
+      if (KIND == EPI_PARTIAL) p.ws[((long)by * p.M + m) * p.N + n] = v[nb][e];
       else epi_store_t<KIND>(p.epi, m, n, v[nb][e]);
     }
   }
@@ -1156,7 +1159,7 @@ static hipError_t launch_chunk_mb(const ChunkP& p, int kind, dim3 grid, hipStrea
 }
 
 hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, const Epilogue& epi, int splits,
-                      float* ws, hipStream_t s) {
+                      float* ws, hipStream_t s, const Prefetch* prefetch) {
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
   if (M > 64 || K % 32 || N % 32) return hipErrorInvalidValue;
   if (epi.kind != EPI_STORE && epi.kind != EPI_PARTIAL && epi.kind != EPI_GEGLU && epi.kind != EPI_QKV &&
@@ -1165,10 +1168,12 @@ hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int 
   int used, per;
   skinny_plan(K, splits, &used, &per);
   if (used > 1 && !ws) return hipErrorInvalidValue;
-  ChunkP p{Af, Wf, M, N, K, per * 32, epi, ws};
+  const Prefetch pf = prefetch ? *prefetch : Prefetch{};
+  if (pf.blocks < 0 || pf.blocks > 1024 || (pf.blocks && !pf.sink)) return hipErrorInvalidValue;
   const bool reduce = used > 1 && epi.kind != EPI_PARTIAL;
   const int nb = epi.kind == EPI_GEGLU && !reduce ? 2 : 1;
-  const dim3 grid(N / (16 * nb), used);
+  ChunkP p{Af, Wf, M, N, K, per * 32, epi, ws, pf};
+  const dim3 grid(N / (16 * nb), used, prefetch_depth(N / (16 * nb) * used, pf.blocks));
   const int kind = reduce ? EPI_PARTIAL : epi.kind;
   const int mb = (M + 15) / 16;
   hipError_t err = mb == 1 ? launch_chunk_mb<1>(p, kind, grid, s)

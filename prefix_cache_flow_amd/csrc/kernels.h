@@ -7,9 +7,9 @@
 
 namespace vla {
 
-// Two byte ranges that extra workgroups of a short kernel read once and drop,
-// so that the next kernel (which streams them) finds them in the memory-side
-// cache instead of waiting on HBM.  `blocks` workgroups are added to the grid.
+// Two byte ranges that extra workgroups of a kernel read once and drop, so that
+// a later kernel (which streams them) finds them in cache instead of waiting
+// on HBM.  `blocks` workgroups are added to the grid.
 // With group > 0 a range is read XCD by XCD: the consuming kernel's workgroup
 // for column group g of `group` bytes runs on XCD g % 8 (workgroups go to the
 // eight XCDs round robin), so the extra workgroups on XCD c read the groups
@@ -22,6 +22,9 @@ struct Prefetch {
   unsigned* sink = nullptr;  // 64 words, written only for an impossible value
   int blocks = 0;
 };
+// Grid depth for a kernel whose own grid layer holds `per` workgroups: whole
+// layers of prefetch workgroups after it, at least `blocks` of them.
+inline int prefetch_depth(int per, int blocks) { return blocks > 0 ? 1 + (blocks + per - 1) / per : 1; }
 
 // ------------------------------------------------------------------ epilogues
 // What a GEMM does with its fp32 result v at (m, n).
@@ -95,9 +98,10 @@ int gemm_bf16_splits(int K, int splits, int M);
 // are read but their results never stored.  K % 32 == 0, N % 32 == 0; kinds
 // STORE, PARTIAL, GEGLU, QKV and CACHE (out_frag honoured); split sums of the
 // finishing kinds go through a fixed-order reduction; splits and partials as
-// gemm_bf16.
+// gemm_bf16.  `prefetch` (optional) appends extra workgroups that read weights
+// of later kernels, as for the row kernels.
 hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, const Epilogue& epi,
-                      int splits, float* ws, hipStream_t s);
+                      int splits, float* ws, hipStream_t s, const Prefetch* prefetch = nullptr);
 // Bytes of fragment-layout weight that one column group of gemm_chunk reads
 // (the workgroup grid's x index), or 0 when the groups do not map to XCDs
 // round robin (grid width not a multiple of 8): the `group` of a Prefetch.

@@ -52,11 +52,8 @@ __global__ __launch_bounds__(256) void k_resid_norm(float* h, int ldh, const flo
                                                     int8_t* q, float* alpha, int u_frag, Prefetch pf) {
   static_assert(!VEC || PER % 4 == 0, "vector rows");
   __shared__ float red[4];
+  if (prefetch_layer(pf)) return;  // extra workgroups: warm later kernels' weights
   const int m = blockIdx.x;
-  if (m >= M) {  // extra workgroups: warm the next kernel's weights
-    prefetch_share(pf, m, M, gridDim.x - M);
-    return;
-  }
   constexpr int G = VEC ? 4 : 1;  // consecutive columns per access
   float x[PER];
   float pv[NS > 0 ? NS : 1][PER];
@@ -131,7 +128,7 @@ static void launch_rn(int nsplit, hipStream_t s, float* h, int ldh, const float*
                       const float* gain, float eps, void* u_out, int u_f32, int ldu, int8_t* q_out, float* alpha_out,
                       int u_frag, const Prefetch& pf) {
 #define VLA_RN(NS)                                                                                                  \
-  hipLaunchKernelGGL((k_resid_norm<PER, NS, VEC>), dim3(M + pf.blocks), dim3(256), 0, s, h, ldh, part, nsplit, M, N, \
+  hipLaunchKernelGGL((k_resid_norm<PER, NS, VEC>), dim3(M, 1, prefetch_depth(M, pf.blocks)), dim3(256), 0, s, h, ldh, part, nsplit, M, N, \
                      gain, eps, u_out, u_f32, ldu, q_out, alpha_out, u_frag, pf)
   if (nsplit <= 0) VLA_RN(0);
   else if (nsplit <= 1) VLA_RN(1);

@@ -1108,15 +1108,15 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
   Epilogue pe;
   pe.kind = EPI_PARTIAL;
   const int S_o = expert_splits(M, c.d_e, qe), S_d = expert_splits(M, c.d_e, c.F_e);
-  // The short kernels of the chain (row kernel, attention, norms) get extra
-  // workgroups that read the weights of the GEMMs ahead once, so those GEMMs
-  // find them in cache: a weight load then costs an L2 hit instead of an HBM
-  // round trip, while the short kernel's own work hides the read.  The
-  // attention kernels run longest with the fewest workgroups of their own, so
-  // they carry most of it: self attention reads the O and cross-query weights,
-  // cross attention the cross O and gate/up weights; the norms read the
-  // layer's cache block, the down weights and the next layer's QKV weights.
-  // Only for the fragment path (batch-1 sized chunks).
+  // Kernels of the chain get extra workgroups that read the weights of the
+  // GEMMs ahead once, so those GEMMs find them in cache: a weight load then
+  // costs an L2 hit instead of an HBM round trip, while the carrier's own work
+  // hides the read.  The attention kernels run longest with the fewest
+  // workgroups of their own, so they carry most of it: self attention reads
+  // the O and cross-query weights, cross attention the cross O and gate/up
+  // weights.  The gate/up GEMM reads the down weights, and the norms the
+  // layer's cache block and the next layer's QKV weights.  Only for the
+  // fragment path (batch-1 sized chunks).
   const size_t b_qkv = (size_t)qkve * c.d_e * es, b_o = (size_t)c.d_e * qe * es, b_q = (size_t)qe * c.d_e * es;
   const size_t b_gu = (size_t)2 * c.F_e * c.d_e * es, b_d = (size_t)c.d_e * c.F_e * es;
   const size_t layer_kv = (size_t)layer_stride * es;
@@ -1192,9 +1192,10 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
         const uint16_t* u = (const uint16_t*)w.eu;
         // C = A W^T on the chunk: fragment-layout operands up to 64 rows, else the tiled kernel
         // (splits: the chunk kernel's request; the wide kernel picks its own, as expert_splits says)
-        auto mm = [&](const void* A, int lda, const void* W, int N, int K, const Epilogue& ep, int splits) {
+        auto mm = [&](const void* A, int lda, const void* W, int N, int K, const Epilogue& ep, int splits,
+                      const Prefetch* pf = nullptr) {
           (void)lda;
-          if (small) return gemm_chunk((const uint16_t*)A, (const uint16_t*)W, M, N, K, ep, splits, w.epart, s);
+          if (small) return gemm_chunk((const uint16_t*)A, (const uint16_t*)W, M, N, K, ep, splits, w.epart, s, pf);
           return gemm_frag((const uint16_t*)A, (const uint16_t*)W, M, N, K, ep, 0, w.epart, s);
         };
         K_TRY(mm(u, c.d_e, L.wqkv, qkve, c.d_e, qkv_e, 1), "qkv_s");
@@ -1203,9 +1204,7 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
           sa.pf = pfr(L.wos, b_o, g_o, L.wgu, b_gu, g_gu, 192);
           K_TRY(attention_chunk(sa, s), "joint attn");
           K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
-          const Prefetch pf_d = pfr(L.wd, b_d, g_d, nullptr, 0, 0, 192);
-          K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_d),
-                "norm");
+          K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
         } else {
           sa.pf = pfr(L.wos, b_o, g_o, L.wqc, b_q, g_q, 192);
           K_TRY(attention_chunk(sa, s), "self attn");
@@ -1217,14 +1216,13 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
           ca.pf = pfr(L.woc, b_o, g_o, L.wgu, b_gu, g_gu, 192);
           K_TRY(attention_chunk(ca, s), "cross attn");
           K_TRY(mm(w.eattn, qe, L.woc, c.d_e, qe, pe, S_o), "o_c");
-          const Prefetch pf_d = pfr(L.wd, b_d, g_d, nullptr, 0, 0, 192);
-          K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_d),
-                "norm");
+          K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
         }
         Epilogue g = epi_store(w.emlp, c.F_e, 0);
         g.kind = EPI_GEGLU;
         g.out_frag = fr;
-        K_TRY(mm(u, c.d_e, L.wgu, 2 * c.F_e, c.d_e, g, 1), "gate/up");
+        const Prefetch pf_d = pfr(L.wd, b_d, g_d, nullptr, 0, 0, 192);
+        K_TRY(mm(u, c.d_e, L.wgu, 2 * c.F_e, c.d_e, g, 1, &pf_d), "gate/up");
         K_TRY(mm(w.emlp, c.F_e, L.wd, c.d_e, c.F_e, pe, S_d), "down");
         // next layer's QKV weights (and, joint, its cache block)
         const void* next_kv = m->joint && B == 1 ? (const char*)ca.k + (size_t)layer_stride * es : nullptr;
