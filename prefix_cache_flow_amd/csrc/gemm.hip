@@ -1,15 +1,13 @@
 // Dense projections of the policy step: C = A W^T with A [M, K] activations and
 // W [N, K] weights (the [out, in] layout of every linear layer).
 //
-// gemm_frag (the prefix, and any bf16 product with both operands in the
-//   fragment layout of common.h): 288-row tiles, k_gemm_af.
+// gemm_frag (the prefix, and any bf16 product of more than 64 rows with both
+//   operands in the fragment layout of common.h): 288-row tiles, k_gemm_af8 /
+//   k_gemm_af.  Output tiles are numbered XCD-major so tiles that share a
+//   weight panel or an activation K range run on one XCD and share its L2.
 // gemm_chunk (at most 64 rows, fragment layout): weight-streaming k_chunk.
-// gemm_bf16 (row-major activations): k_gemm_ws above 64 rows (wave-specialised
-//   288 x 128 tiles staged through LDS), k_skinny up to 64.
 //   Split-K writes fp32 partials [split][M][N] that a fixed-order reduction (or
 //   the row kernel of norm.hip) sums, so results never depend on timing.
-//   Output tiles are numbered XCD-major so tiles that share a weight panel or
-//   an activation K range run on one XCD and share its L2.
 // gemm_f32: fp32 SIMT tiles for the fp32 workload (small shapes).
 #include <type_traits>
 
@@ -17,16 +15,6 @@
 #include "kernels.h"
 
 namespace vla {
-
-struct GemmP {
-  const uint16_t* A;
-  int lda;
-  const uint16_t* W;
-  int ldw;
-  int M, N, K, kchunk, nM, nN;
-  Epilogue epi;
-  float* ws;
-};
 
 __device__ __forceinline__ void cache_index(const Epilogue& e, int m, int n, long& idx) {
   const int per_kv = e.hkv * e.hd, per_l = 2 * per_kv;
@@ -127,112 +115,14 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* ws, int spli
 }
 
 
-// ------------------------------------------------------------------ skinny M
-// Activations of at most 64 rows (the action chunk).  The contraction is a
-// weight stream.  A workgroup of four waves owns 16 * NB output columns; the
-// four waves split the workgroup's K range, each taking at most eight k-steps
-// of 32, and every wave issues all of its weight and activation loads at once
-// (straight from global memory, the activations staying in L2) before the
-// 16x16x32 MFMAs, so one memory round trip covers the whole slice.  The four
-// partial tiles are then summed through LDS in wave order.  With NB = 2 and the
-// gate/up interleave, lane l holds the gate and the up value of one feature.
-// Rows past M and k-steps past the range are clamped to valid addresses and
-// masked to zero instead of branching around the loads.
-struct SkinnyP {
-  const uint16_t* A;
-  int lda;
-  const uint16_t* W;
-  int ldw;
-  int M, N, K, kchunk;
-  Epilogue epi;
-  float* ws;
-};
-
-constexpr int kSkinnySteps = 8;  // k-steps of 32 per wave
-
-template <int NB, int KIND>
-__global__ __launch_bounds__(256) void k_skinny(SkinnyP p) {
-  constexpr int SPW = kSkinnySteps;
-  __shared__ float red[4][4 * NB * 4][64];  // [wave][row block, column block, element][lane]
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * 16 * NB;
-  const int kw = p.kchunk / 4;
-  const int kb = blockIdx.y * p.kchunk + w * kw;
-  const int ke = min(p.K, kb + kw);
-  const int nsteps = max(0, ke - kb) / 32;
-
-  const uint16_t* wp[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) wp[nb] = p.W + (long)(n0 + nb * 16 + col) * p.ldw + grp * 8;
-  const uint16_t* ap[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) ap[rb] = p.A + (long)min(rb * 16 + col, p.M - 1) * p.lda + grp * 8;
-
-  u32x4_t wv[SPW][NB], av[SPW][4];
-#pragma unroll
-  for (int s = 0; s < SPW; ++s) {
-    const int k = min(kb + s * 32, p.K - 32);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) wv[s][nb] = *(const u32x4_t*)(wp[nb] + k);
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) av[s][rb] = *(const u32x4_t*)(ap[rb] + k);
-  }
-  f32x4_t acc[4][NB];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < SPW; ++s) {
-    const bool on = s < nsteps;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const u32x4_t a4 = on ? av[s][rb] : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = mfma16x16x32(as_bf16x8(a4), as_bf16x8(wv[s][nb]), acc[rb][nb]);
-    }
-  }
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) red[w][(rb * NB + nb) * 4 + e][lane] = acc[rb][nb][e];
-  __syncthreads();
-
-  // wave w finishes row block w: sum the four K ranges in order, then the epilogue
-  const int rb = w;
-  float v[NB][4];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int idx = (rb * NB + nb) * 4 + e;
-      v[nb][e] = red[0][idx][lane] + red[1][idx][lane] + red[2][idx][lane] + red[3][idx][lane];
-    }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int m = rb * 16 + grp * 4 + e;
-    if (m >= p.M) continue;
-    if (KIND == EPI_GEGLU) {
-      epi_geglu(p.epi, m, (n0 >> 5) * 16 + col, v[0][e], v[NB - 1][e]);
-      continue;
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int n = n0 + nb * 16 + col;
-      if (KIND == EPI_PARTIAL) p.ws[((long)blockIdx.y * p.M + m) * p.N + n] = v[nb][e];
-      else epi_store_t<KIND>(p.epi, m, n, v[nb][e]);
-    }
-  }
-}
+// ------------------------------------------------------------------ chunk split planning
+constexpr int kChunkSteps = 8;  // at most this many k-steps of 32 per wave
 
 // K is cut into `used` workgroup chunks of a multiple of 4 k-steps each and at
-// most 4 * kSkinnySteps k-steps; `splits` asks for more chunks than that floor.
-static void skinny_plan(int K, int splits, int* used, int* per_steps) {
+// most 4 * kChunkSteps k-steps; `splits` asks for more chunks than that floor.
+static void chunk_plan(int K, int splits, int* used, int* per_steps) {
   const int steps = K / 32;
-  const int cap = 4 * kSkinnySteps;
+  const int cap = 4 * kChunkSteps;
   int u0 = std::max((steps + cap - 1) / cap, std::min(std::max(splits, 1), (steps + 3) / 4));
   u0 = std::max(u0, 1);
   int per = (steps + u0 - 1) / u0;
@@ -241,263 +131,10 @@ static void skinny_plan(int K, int splits, int* used, int* per_steps) {
   *used = (steps + per - 1) / per;
 }
 
-int gemm_skinny_splits(int K, int splits) {
+int gemm_chunk_splits(int K, int splits) {
   int used, per;
-  skinny_plan(K, splits, &used, &per);
+  chunk_plan(K, splits, &used, &per);
   return used;
-}
-
-template <int NB>
-static hipError_t launch_skinny(const SkinnyP& p0, int splits, hipStream_t s) {
-  SkinnyP p = p0;
-  int used, per;
-  skinny_plan(p.K, splits, &used, &per);
-  p.kchunk = per * 32;
-  const dim3 grid(p.N / (16 * NB), used);
-  const int kind = used > 1 ? EPI_PARTIAL : p.epi.kind;
-  if constexpr (NB == 2) {
-    if (kind != EPI_GEGLU) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_skinny<2, EPI_GEGLU>), grid, dim3(256), 0, s, p);
-  } else {
-    switch (kind) {
-      case EPI_STORE: hipLaunchKernelGGL((k_skinny<1, EPI_STORE>), grid, dim3(256), 0, s, p); break;
-      case EPI_RESID: hipLaunchKernelGGL((k_skinny<1, EPI_RESID>), grid, dim3(256), 0, s, p); break;
-      case EPI_CACHE: hipLaunchKernelGGL((k_skinny<1, EPI_CACHE>), grid, dim3(256), 0, s, p); break;
-      case EPI_PARTIAL: hipLaunchKernelGGL((k_skinny<1, EPI_PARTIAL>), grid, dim3(256), 0, s, p); break;
-      default: return hipErrorInvalidValue;
-    }
-  }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  if (used > 1 && p.epi.kind != EPI_PARTIAL) {
-    const long tot = (long)p.M * p.N / 4;
-    const int blocks = (int)std::min<long>((tot + 255) / 256, 4096);
-    hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, (const float*)p.ws, used, p.M, p.N, p.epi);
-    err = hipGetLastError();
-  }
-  return err;
-}
-
-// ------------------------------------------------------------------ wide tiles (prefix)
-// Many rows (the prefix: hundreds of tokens).  A workgroup owns a 288 x BN
-// output tile and has 8 waves.  Four compute waves in a 2 x 2 arrangement each
-// hold 144 x BN/2 of the tile as 9 x BN/32 accumulators of the 16x16x32 MFMA,
-// reading their fragments from LDS two MFMA groups ahead under scheduling
-// barriers.  Four loader waves fill LDS: two fetch the activation slice one
-// 64-wide K slice ahead, two fetch the weight slices four slices ahead in four
-// register sets.  Each wave has its own memory counter, so waiting for one
-// slice never waits for the weight slices queued behind it, and enough weight
-// bytes are in flight per CU to cover HBM latency.  One barrier per slice hands
-// the two LDS buffers between loaders and compute waves; the slice loop runs a
-// multiple of 4 times (the weight register sets rotate) and slices past the end
-// are fetched clamped and never computed.  LDS rows are 64 bf16 (128 bytes) with
-// the 16-byte chunk index XOR-ed by (row / 2) % 8, so fragment reads and loader
-// stores hit distinct banks.  Rows past M and columns past N are clamped on
-// load and never stored.  Epilogues run straight from the accumulators.
-template <int BN, int KIND, bool WF>
-__global__ __launch_bounds__(512) void k_gemm_ws(GemmP p) {
-  constexpr int BM = 288, BK = 64, LDK = BK;
-  constexpr int TM = BM / 2 / 16, TN = BN / 2 / 16;  // 16x16 blocks per compute wave (2 x 2 waves)
-  // 16-byte vectors per loader thread and slice: two activation and two weight loader waves
-  constexpr int AVL = BM * BK / 8 / 128, WVL = BN * BK / 8 / 128;
-  // element offset of 16-byte chunk c of LDS row r (swizzled)
-  auto sw = [](int r, int c) { return r * LDK + ((c ^ ((r >> 1) & 7)) << 3); };
-  static_assert(AVL * 128 * 8 == BM * BK && WVL * 128 * 8 == BN * BK, "tile shape");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDK];
-  auto sA = [&](int b) { return smem + b * (BM * LDK); };
-  auto sW = [&](int b) { return smem + 2 * BM * LDK + b * (BN * LDK); };
-
-  const int nt = p.nM * p.nN, L = blockIdx.x;
-  const int tile = (nt % 8 == 0) ? (L % 8) * (nt / 8) + L / 8 : L;
-  const int tm = tile % p.nM, tn = tile / p.nM;
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int kb = blockIdx.y * p.kchunk;
-  const int ke = min(p.K, kb + p.kchunk);
-  const int nsl = max(0, (ke - kb) / BK);
-  const int nsl4 = (nsl + 3) & ~3;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  auto slice_k = [&](int sl) { return kb + min(sl, max(nsl - 1, 0)) * BK; };
-
-  if (wid >= 6) {  // ---------------- weight loaders: four slices in flight
-    const int lt = tid - 384;
-    struct RW { u32x4_t v[WVL]; };
-    RW r0, r1, r2, r3;
-    auto load = [&](RW& R, int sl) {
-      const int k0 = slice_k(sl);
-#pragma unroll
-      for (int i = 0; i < WVL; ++i) {
-        const int v = lt + i * 128, r = v >> 3, c = (v & 7) * 8, gn = min(n0 + r, p.N - 1);
-        // 32-bit element offsets (the launcher checks that both operands fit): base + offset addressing
-        const uint32_t off = WF ? (uint32_t)frag_idx(gn, k0 + c, p.ldw) : (uint32_t)gn * (uint32_t)p.ldw + k0 + c;
-        R.v[i] = *(const u32x4_t*)(p.W + off);
-      }
-    };
-    auto store = [&](const RW& R, int buf) {
-#pragma unroll
-      for (int i = 0; i < WVL; ++i) {
-        const int v = lt + i * 128;
-        *(u32x4_t*)&sW(buf)[sw(v >> 3, v & 7)] = R.v[i];
-      }
-    };
-    load(r0, 0);
-    load(r1, 1);
-    load(r2, 2);
-    load(r3, 3);
-    store(r0, 0);
-    load(r0, 4);
-    __syncthreads();
-    // entering iteration s: slices s+1 .. s+4 are in the sets (s+1)%4 .. (s+4)%4
-    for (int s = 0; s < nsl4; s += 4) {
-      store(r1, 1);
-      load(r1, s + 5);
-      __syncthreads();
-      store(r2, 0);
-      load(r2, s + 6);
-      __syncthreads();
-      store(r3, 1);
-      load(r3, s + 7);
-      __syncthreads();
-      store(r0, 0);
-      load(r0, s + 8);
-      __syncthreads();
-    }
-    return;
-  }
-  if (wid >= 4) {  // ---------------- activation loaders: one slice ahead
-    const int lt = tid - 256;
-    u32x4_t ra[AVL];
-    auto load = [&](int sl) {
-      const int k0 = slice_k(sl);
-#pragma unroll
-      for (int i = 0; i < AVL; ++i) {
-        const int v = lt + i * 128, r = v >> 3, c = (v & 7) * 8;
-        ra[i] = *(const u32x4_t*)(p.A + ((uint32_t)min(m0 + r, p.M - 1) * (uint32_t)p.lda + k0 + c));
-      }
-    };
-    auto store = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < AVL; ++i) {
-        const int v = lt + i * 128;
-        *(u32x4_t*)&sA(buf)[sw(v >> 3, v & 7)] = ra[i];
-      }
-    };
-    load(0);
-    store(0);
-    load(1);
-    __syncthreads();
-    for (int s = 0; s < nsl4; ++s) {
-      store((s + 1) & 1);
-      load(s + 2);
-      __syncthreads();
-    }
-    return;
-  }
-
-  // ---------------- compute waves: 2 x 2 waves of 144 x BN/2 on the 16x16x32 MFMA
-  const int wm = wid >> 1, wn = wid & 1;
-  f32x4_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();
-  for (int s = 0; s < nsl4; ++s) {
-    if (s < nsl) {
-      const int buf = s & 1;
-      // fragment rows start at multiples of 16, so the chunk swizzle of a lane's row is ((lane & 15) >> 1)
-      const int xr = (lane & 15) >> 1;
-      const uint16_t* aBase = sA(buf) + (wm * (BM / 2) + (lane & 15)) * LDK;
-      const uint16_t* wBase = sW(buf) + (wn * (BN / 2) + (lane & 15)) * LDK;
-      constexpr int KS = BK / 32, NG = KS * TM;  // MFMA groups per slice: one activation fragment each
-      auto chunk = [&](int kk) { return ((kk * 4 + (lane >> 4)) ^ xr) << 3; };
-      auto lda_frag = [&](int g) {
-        return as_bf16x8(*(const u32x4_t*)(aBase + (g % TM) * 16 * LDK + chunk(g / TM)));
-      };
-      bf16x8_t wf[KS][TN], af[NG];
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) wf[kk][j] = as_bf16x8(*(const u32x4_t*)(wBase + j * 16 * LDK + chunk(kk)));
-      af[0] = lda_frag(0);
-      af[1] = lda_frag(1);
-#pragma unroll
-      for (int gi = 0; gi < NG; ++gi) {
-        if (gi + 2 < NG) af[gi + 2] = lda_frag(gi + 2);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[gi % TM][j] = mfma16x16x32(af[gi], wf[gi / TM][j], acc[gi % TM][j]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    __syncthreads();
-  }
-
-  // epilogue: accumulator element e of lane l is row (l / 16) * 4 + e, column l % 16 of its block; with
-  // BN/2 a multiple of 32 the gate and up blocks of the GeGLU interleave sit in the same lane
-  const int rbase = m0 + wm * (BM / 2) + (lane >> 4) * 4;
-  const int cbase = n0 + wn * (BN / 2);
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int m = rbase + i * 16 + e;
-      if (m >= p.M) continue;
-      if (KIND == EPI_GEGLU) {
-#pragma unroll
-        for (int j = 0; j < TN; j += 2) {
-          if (cbase + j * 16 >= p.N) break;  // N % 32 == 0: a gate block in range has its up block
-          const int f = ((cbase + j * 16) >> 5) * 16 + (lane & 15);
-          epi_geglu(p.epi, m, f, acc[i][j][e], acc[i][j + 1][e]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int n = cbase + j * 16 + (lane & 15);
-          if (n >= p.N) continue;
-          if (KIND == EPI_PARTIAL) p.ws[((long)blockIdx.y * p.M + m) * p.N + n] = acc[i][j][e];
-          else epi_store_t<KIND>(p.epi, m, n, acc[i][j][e]);
-        }
-      }
-    }
-  }
-}
-
-template <int BN, bool WF>
-static hipError_t launch_ws(const GemmP& p, int splits, hipStream_t s) {
-  // the loaders address both operands with 32-bit element offsets
-  if ((size_t)p.M * p.lda >= (1ull << 31) || (size_t)p.N * p.ldw >= (1ull << 31)) return hipErrorInvalidValue;
-  GemmP q = p;
-  q.nM = (p.M + 287) / 288;
-  q.nN = (p.N + BN - 1) / BN;
-  const int slices = p.K / 64;
-  const int per = (slices + splits - 1) / splits;
-  q.kchunk = per * 64;
-  const int used = (slices + per - 1) / per;  // == splits for counts from gemm_bf16_splits
-  dim3 grid(q.nM * q.nN, used);
-  const int kind = used > 1 ? EPI_PARTIAL : p.epi.kind;
-  const dim3 blk2(512);
-  switch (kind) {
-    case EPI_STORE: hipLaunchKernelGGL((k_gemm_ws<BN, EPI_STORE, WF>), grid, blk2, 0, s, q); break;
-    case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_ws<BN, EPI_GEGLU, WF>), grid, blk2, 0, s, q); break;
-    case EPI_PARTIAL: hipLaunchKernelGGL((k_gemm_ws<BN, EPI_PARTIAL, WF>), grid, blk2, 0, s, q); break;
-    case EPI_QKV: hipLaunchKernelGGL((k_gemm_ws<BN, EPI_QKV, WF>), grid, blk2, 0, s, q); break;
-    case EPI_CACHE:
-      if constexpr (!WF) { hipLaunchKernelGGL((k_gemm_ws<BN, EPI_CACHE, WF>), grid, blk2, 0, s, q); break; }
-      return hipErrorInvalidValue;
-    case EPI_RESID:
-      if constexpr (!WF) { hipLaunchKernelGGL((k_gemm_ws<BN, EPI_RESID, WF>), grid, blk2, 0, s, q); break; }
-      return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
-  }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  if (used > 1 && p.epi.kind != EPI_PARTIAL) {
-    const long total = (long)p.M * p.N / 4;
-    const int blocks = (int)std::min<long>((total + 255) / 256, 4096);
-    hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, (const float*)p.ws, used, p.M, p.N, p.epi);
-    err = hipGetLastError();
-  }
-  return err;
 }
 
 // ------------------------------------------------------------------ wide tiles, fragment operands
@@ -994,58 +631,12 @@ hipError_t gemm_frag(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K
   return err;
 }
 
-// Split count that fills the chip for an M x N x K product on the tiles
-// gemm_bf16 picks: about two workgroups per CU, at least 4 K slices of 64 each.
-int gemm_bf16_auto_splits(int M, int N, int K) {
-  if (M <= 64) return 4;
-  const int tiles = (M + 287) / 288 * ((N + 127) / 128);
-  const int slices = K / 64;
-  int s = 1;
-  while (tiles * s < 256 && slices / (2 * s) >= 4 && 2 * s <= 16) s *= 2;
-  return s;
-}
-
-int gemm_bf16_splits(int K, int splits, int M) {
-  if (M <= 64) return gemm_skinny_splits(K, splits);
-  const int slices = K / 64;
-  if (slices <= 0) return 1;
-  splits = std::max(1, std::min(splits, slices));
-  const int per = (slices + splits - 1) / splits;
-  return (slices + per - 1) / per;
-}
-
-hipError_t gemm_bf16(const uint16_t* A, int lda, const uint16_t* W, int ldw, int M, int N, int K,
-                     const Epilogue& epi, int splits, float* ws, hipStream_t s, int w_frag) {
-  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
-  if (K % 64 || N % 32) return hipErrorInvalidValue;
-  if (w_frag && (M <= 64 || ldw != K || epi.kind == EPI_RESID || epi.kind == EPI_CACHE)) return hipErrorInvalidValue;
-  if (M <= 64 && epi.kind == EPI_QKV) return hipErrorInvalidValue;
-  // the one place that fixes how many partial slices are written: callers that
-  // consume EPI_PARTIAL output read gemm_bf16_splits(K, splits, M) of them
-  splits = gemm_bf16_splits(K, splits, M);
-  GemmP p{A, lda, W, ldw, M, N, K, 0, 0, 0, epi, ws};
-  if ((splits > 1 || epi.kind == EPI_PARTIAL) && !ws) return hipErrorInvalidValue;
-  // Tile choice: skinny row counts (the action chunk) stream weights one wave
-  // per 16 or 32 columns; the prefix (hundreds of rows) takes 288 x 128 tiles,
-  // four waves of 144 x 64.
-  if (M <= 64) {
-    SkinnyP q{A, lda, W, ldw, M, N, K, 0, epi, ws};
-    if (epi.kind == EPI_GEGLU) {
-      if (splits > 1) return hipErrorInvalidValue;  // GeGLU needs whole sums
-      return launch_skinny<2>(q, splits, s);
-    }
-    return launch_skinny<1>(q, splits, s);
-  }
-  if (w_frag) return launch_ws<128, true>(p, splits, s);
-  return launch_ws<128, false>(p, splits, s);
-}
-
 // ------------------------------------------------------------------ chunk rows, fragment layout
 // Activations of at most 64 rows with both operands in the fragment layout of
-// common.h.  The work split is that of the skinny kernel above (a workgroup
-// owns 16 * NB columns, its four waves split the K range, at most kSkinnySteps
-// k-steps each, partial tiles summed through LDS in wave order), but every
-// load of a wave is one contiguous 1 KB fragment: a weight fragment per
+// common.h.  A workgroup owns 16 * NB columns, its four waves split the K
+// range (at most kChunkSteps k-steps each, issued at once: one memory round
+// trip covers the slice) and their partial tiles are summed through LDS in
+// wave order.  Every load of a wave is one contiguous 1 KB fragment: a weight fragment per
 // 16 columns and k-step, an activation fragment per 16 rows and k-step.  MB is
 // the number of 16-row blocks that hold rows (1, 2 or 4); blocks past the rows
 // are never loaded.  Rows past M inside the last block are read but their
@@ -1155,7 +746,7 @@ static hipError_t launch_chunk_mb(const ChunkP& p, int kind, dim3 grid, hipStrea
   const int steps = p.kchunk >> 7;
   if (steps <= 2) return launch_chunk_spw<MB, 2>(p, kind, grid, s);
   if (steps <= 4) return launch_chunk_spw<MB, 4>(p, kind, grid, s);
-  return launch_chunk_spw<MB, kSkinnySteps>(p, kind, grid, s);
+  return launch_chunk_spw<MB, kChunkSteps>(p, kind, grid, s);
 }
 
 hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, const Epilogue& epi, int splits,
@@ -1166,7 +757,7 @@ hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int 
       epi.kind != EPI_CACHE)
     return hipErrorInvalidValue;
   int used, per;
-  skinny_plan(K, splits, &used, &per);
+  chunk_plan(K, splits, &used, &per);
   if (used > 1 && !ws) return hipErrorInvalidValue;
   const Prefetch pf = prefetch ? *prefetch : Prefetch{};
   if (pf.blocks < 0 || pf.blocks > 1024 || (pf.blocks && !pf.sink)) return hipErrorInvalidValue;
@@ -1192,7 +783,7 @@ hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int 
 size_t gemm_chunk_group_bytes(int M, int N, int K, int kind, int splits) {
   if (M > 64 || K % 32 || N % 32) return 0;
   int used, per;
-  skinny_plan(K, splits, &used, &per);
+  chunk_plan(K, splits, &used, &per);
   const int nb = kind == EPI_GEGLU && used == 1 ? 2 : 1;
   const int gx = N / (16 * nb);
   return gx % 8 ? 0 : (size_t)nb * 16 * K * 2;

@@ -68,37 +68,28 @@ struct Epilogue {
   int out_frag = 0;  // bf16 output in fragment layout (frag_idx with K = ldo) instead of rows
 };
 
-// C = A[M,K] W[N,K]^T, bf16 operands, fp32 accumulation on MFMA; `splits` > 1
-// splits K and reduces the partial sums in a fixed order in `ws`
-// (splits * M * N floats).  K % 64 == 0, N % 32 == 0.  At most 64 rows take the
-// weight-streaming skinny kernel (GeGLU there needs splits == 1).  With w_frag
-// the weights are in the fragment layout of common.h (ldw == K, more than 64
-// rows, STORE / GEGLU / PARTIAL only).
-hipError_t gemm_bf16(const uint16_t* A, int lda, const uint16_t* W, int ldw, int M, int N, int K,
-                     const Epilogue& epi, int splits, float* ws, hipStream_t s, int w_frag = 0);
-
-// The same contraction for any row count with A ([M][K], rows padded to a
-// multiple of 16) and W ([N][K]) both in the fragment layout of common.h, on
-// 288-row tiles.  K % 64 == 0, N % 32 == 0; all kinds; STORE and GEGLU need
-// ldo % 4 == 0, RESID ldr % 4 == 0; out_frag with bf16 GEGLU or CACHE only.
-// `splits` <= 0 picks a count that fills the chip; partials as gemm_bf16
-// (gemm_frag_splits of them).
+// C = A[M,K] W[N,K]^T, bf16 operands, fp32 accumulation on MFMA, for any row
+// count with A ([M][K], rows padded to a multiple of 16) and W ([N][K]) both in
+// the fragment layout of common.h, on 288-row tiles.  K % 64 == 0, N % 32 == 0;
+// all kinds; STORE and GEGLU need ldo % 4 == 0, RESID ldr % 4 == 0; out_frag
+// with bf16 GEGLU or CACHE only.  `splits` > 1 splits K: fp32 partials
+// [split][M][N] in `ws`, summed in a fixed order by a reduction (finishing
+// kinds) or left for the caller (PARTIAL).  `splits` <= 0 picks a count that
+// fills the chip (gemm_frag_splits of them).
 hipError_t gemm_frag(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, const Epilogue& epi,
                      int splits, float* ws, hipStream_t s);
 int gemm_frag_splits(int M, int N, int K, int splits);
 
-// A split count for gemm_bf16 that fills the chip at this shape (partials need splits x M x N floats).
-int gemm_bf16_auto_splits(int M, int N, int K);
-// Number of K splits gemm_bf16 actually uses for a request of `splits` at M rows.
-int gemm_bf16_splits(int K, int splits, int M);
+// Number of K splits gemm_chunk actually uses for a request of `splits`.
+int gemm_chunk_splits(int K, int splits);
 
 // The same contraction for at most 64 rows with A and W ([N][K]) both in the
 // fragment layout of common.h: every load of a wave is one contiguous 1 KB
 // block.  A holds 16 rows when M <= 16, 32 when M <= 32, else 64; rows past M
 // are read but their results never stored.  K % 32 == 0, N % 32 == 0; kinds
 // STORE, PARTIAL, GEGLU, QKV and CACHE (out_frag honoured); split sums of the
-// finishing kinds go through a fixed-order reduction; splits and partials as
-// gemm_bf16.  `prefetch` (optional) appends extra workgroups that read weights
+// finishing kinds go through a fixed-order reduction; partials as gemm_frag
+// (gemm_chunk_splits of them).  `prefetch` (optional) appends extra workgroups that read weights
 // of later kernels, as for the row kernels.
 hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, const Epilogue& epi,
                       int splits, float* ws, hipStream_t s, const Prefetch* prefetch = nullptr);

@@ -649,11 +649,11 @@ static const int kExpertSplits = 4;
 // kernel (or reduction) that sums its partials.
 static const int kPrefixChunkSplits = 4;  // split request of the chunk-sized kernel
 static int prefix_splits(int64_t M, int N, int K) {
-  return M <= 64 ? gemm_bf16_splits(K, kPrefixChunkSplits, (int)M) : gemm_frag_splits((int)M, N, K, 0);
+  return M <= 64 ? gemm_chunk_splits(K, kPrefixChunkSplits) : gemm_frag_splits((int)M, N, K, 0);
 }
 static int expert_splits(int64_t M, int N, int K) {
   // chunk-sized kernel up to 64 rows, the 288-row-tile kernel (its own split choice) above
-  return M <= 64 ? gemm_bf16_splits(K, kExpertSplits, (int)M) : gemm_frag_splits((int)M, N, K, 0);
+  return M <= 64 ? gemm_chunk_splits(K, kExpertSplits) : gemm_frag_splits((int)M, N, K, 0);
 }
 // bf16 product with both operands in the fragment layout: the chunk-sized
 // kernel up to 64 rows, 288-row tiles above; split counts as prefix_splits
