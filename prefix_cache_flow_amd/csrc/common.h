@@ -75,15 +75,28 @@ __device__ __forceinline__ float group4_sum(float v) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
+// Whole-wave reductions: inside each 16-lane row with DPP lane moves (pairs
+// i ^ 1, then i ^ 2, then the mirrored quad of each half row, then the
+// mirrored half row), then across the four rows with the lane swaps above.
+// Every step adds two equal-rank partial sums, so every lane ends with the same
+// bits, and no step goes through the LDS permute unit.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x140>(v);  // row_mirror
+  return group4_sum(v);
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  v = fmaxf(v, dpp_mov<0x140>(v));
+  return group4_max(v);
 }
 
 // Sum over a block of `NT` threads (NT a multiple of 64); every thread gets the result.

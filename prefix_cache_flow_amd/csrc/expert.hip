@@ -37,10 +37,16 @@ __global__ __launch_bounds__(256) void k_step_rows(StepRows a) {
   const bool head = a.k_head >= 0, emb = a.k_embed >= 0;
   constexpr int G = 8;  // threads per head output
   const int part = tid % G, ao = tid / G;
-  // ---- every global operand first (fast forms): weights, the row, both gains
+  // ---- every global operand first (fast forms): weights, the row, both gains,
+  // the schedule entries and the action values this thread updates (read after
+  // a barrier, each would be one more memory round trip)
   constexpr int PER = 4;  // row elements per thread when d_e <= 1024
   u32x4_t wo[16], wi[16];
   float er[PER], gf[PER], g1[PER];
+  const float dt = head ? a.sched[a.k_head + 1] - a.sched[a.k_head] : 0.f;
+  const float tau = emb ? a.sched[a.k_embed] : 0.f;
+  const bool xown = FH && head && part == 0 && ao < a.d_a;
+  const float x0 = xown ? a.X[(long)m * a.d_a + ao] : 0.f;
   if (FH && head) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -92,7 +98,6 @@ __global__ __launch_bounds__(256) void k_step_rows(StepRows a) {
       for (int n = tid; n < a.d_e; n += 256) us[n] = us[n] * r * (1.0f + a.gain_f[n]);
     }
     __syncthreads();
-    const float dt = a.sched[a.k_head + 1] - a.sched[a.k_head];
     if (FH) {
       const int sl = a.d_e / G;
       float acc = 0.f;
@@ -108,8 +113,8 @@ __global__ __launch_bounds__(256) void k_step_rows(StepRows a) {
       }
 #pragma unroll
       for (int o = 1; o < G; o <<= 1) acc += __shfl_xor(acc, o, 64);
-      if (part == 0 && ao < a.d_a) {
-        const float x = a.X[(long)m * a.d_a + ao] + dt * acc;
+      if (xown) {
+        const float x = x0 + dt * acc;
         a.X[(long)m * a.d_a + ao] = x;
         xs[ao] = x;
       }
@@ -132,7 +137,6 @@ __global__ __launch_bounds__(256) void k_step_rows(StepRows a) {
   if (!emb) return;
   __syncthreads();
   // ---- embedding of step k_embed: E = X W_in^T + phi(tau), u = RMS(E; a1)
-  const float tau = a.sched[a.k_embed];
   const float l2 = 13.287712379549449f;  // log2(10000)
   float ss = 0.f;
   // the embedded row element n = tid + 256 i

@@ -70,6 +70,19 @@ __global__ __launch_bounds__(256) void k_resid_norm(float* h, int ldh, const flo
       }
     }
   };
+  // the gain is requested with the row and its partials: after the block
+  // reduction's barrier its loads would be a second memory round trip
+  float gk[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i += G) {
+    if (VEC) {
+      const f32x4_t gv = *(const f32x4_t*)(gain + row_col<true>(i));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gk[i + j] = 1.0f + gv[j];
+    } else {
+      gk[i] = 1.0f + gain[min(row_col<false>(i), N - 1)];
+    }
+  }
   load(h + (long)m * ldh, x);
 #pragma unroll
   for (int s = 0; s < NS; ++s) load(part + ((long)min(s, nsplit - 1) * M + m) * N, pv[s]);
@@ -93,16 +106,7 @@ __global__ __launch_bounds__(256) void k_resid_norm(float* h, int ldh, const flo
   ss = block_sum<256>(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)N + eps);
 #pragma unroll
-  for (int i = 0; i < PER; i += G) {
-    const int n = row_col<VEC>(i);
-    if (VEC) {
-      const f32x4_t gv = *(const f32x4_t*)(gain + n);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[i + j] = x[i + j] * r * (1.0f + gv[j]);
-    } else if (n < N) {
-      x[i] = x[i] * r * (1.0f + gain[n]);
-    }
-  }
+  for (int i = 0; i < PER; ++i) x[i] = x[i] * r * gk[i];
   if (u) {
 #pragma unroll
     for (int i = 0; i < PER; i += G) {
