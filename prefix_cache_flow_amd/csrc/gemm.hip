@@ -546,7 +546,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_af8(FragP p) {
 // least 4 slices each.
 // Tile width: 64 columns for the small square products (two workgroups then
 // share a CU, and the grid reaches the CU count with fewer K splits), 128 else.
-static int frag_bn(int N, int K) { return (N <= 2048 && K <= 2048) ? 64 : 128; }
+// 64-column tiles (two workgroups per CU) for products of at most 2048-deep K
+// and at most 2048 columns, and for wider ones that 128-column tiles would
+// spread over fewer than 32 CUs (the 288-token prefix QKV: 20 tiles; with 64
+// columns the whole prefix went from 2.38 to 2.31 ms); 128 columns otherwise.  (At 60-72 tiles, the dual-arm and batched QKV and cache
+// projections, the two widths measured within noise of each other.)
+static int frag_bn(int M, int N, int K) {
+  if (K > 2048) return 128;
+  if (N <= 2048) return 64;
+  const int tiles128 = (M + kFragBM - 1) / kFragBM * ((N + 127) / 128);
+  return tiles128 < 32 ? 64 : 128;
+}
 
 static int frag_per(int M, int N, int K, int splits, int bn) {
   const int pairs = (K / 64 + 1) / 2;
@@ -561,7 +571,7 @@ static int frag_per(int M, int N, int K, int splits, int bn) {
 
 int gemm_frag_splits(int M, int N, int K, int splits) {
   if (K < 64) return 1;
-  const int per = frag_per(M, N, K, splits, frag_bn(N, K));
+  const int per = frag_per(M, N, K, splits, frag_bn(M, N, K));
   return ((K / 64 + 1) / 2 + per - 1) / per;
 }
 
@@ -599,7 +609,7 @@ hipError_t gemm_frag(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K
   if (kind0 == EPI_RESID && epi.ldr % 4) return hipErrorInvalidValue;
   if (epi.out_frag && kind0 != EPI_GEGLU && kind0 != EPI_CACHE) return hipErrorInvalidValue;
   if (epi.out_frag && epi.out_f32) return hipErrorInvalidValue;
-  const int bn = frag_bn(N, K);
+  const int bn = frag_bn(M, N, K);
   int per = frag_per(M, N, K, splits, bn);
   // A product that finishes here (not partials for a row kernel) pays for every
   // split twice, writing its partial slab and reading it back in the
