@@ -646,11 +646,10 @@ hipError_t gemm_frag(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K
 // common.h.  A workgroup owns 16 * NB columns, its four waves split the K
 // range (at most kChunkSteps k-steps each, issued at once: one memory round
 // trip covers the slice) and their partial tiles are summed through LDS in
-// wave order.  Every load of a wave is one contiguous 1 KB fragment: a weight fragment per
-// 16 columns and k-step, an activation fragment per 16 rows and k-step.  MB is
-// the number of 16-row blocks that hold rows (1, 2 or 4); blocks past the rows
-// are never loaded.  Rows past M inside the last block are read but their
-// results are never stored.
+// wave order.  Every load of a wave is one contiguous 1 KB fragment: a weight
+// fragment per 16 columns and k-step, an activation fragment per 16 rows and
+// k-step.  MB is 1, 2 or 4 row blocks, the fewest that cover M; the activation
+// buffer holds MB whole blocks, and rows past M are computed but never stored.
 struct ChunkP {
   const uint16_t* A;
   const uint16_t* W;
