@@ -208,8 +208,7 @@ def pipelined(vla, model, cfg, zt, xt, n, warmup=2):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (the sharding design is "
-                                   "described in DESIGN.md)"}))
+        print(json.dumps({"error": "the library runs the policy step on one GPU: --gpus must be 1"}))
         sys.exit(2)
     import torch
 

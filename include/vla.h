@@ -58,7 +58,7 @@ typedef enum {
   VLA_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, bad value   */
   VLA_ERR_SHAPE_MISMATCH = 2,   /* sizes disagree with the model or the cache   */
   VLA_ERR_INVALID_HANDLE = 3,   /* released, foreign or corrupted handle        */
-  VLA_ERR_UNSUPPORTED = 4,      /* a shape or mode this build does not support  */
+  VLA_ERR_UNSUPPORTED = 4,      /* a shape or mode the library does not support */
   VLA_ERR_OUT_OF_MEMORY = 5,    /* a device allocation failed                   */
   VLA_ERR_DEVICE = 6            /* no usable gfx950 device, or a HIP call failed */
 } vla_status;

@@ -2,8 +2,10 @@
 with the workload shapes, and its host-side validation and format helpers work.
 No kernel is launched here."""
 import ctypes as C
+import json
 import os
 import re
+import sys
 
 import numpy as np
 import pytest
@@ -120,3 +122,13 @@ def test_create_without_gpu_reports_device_error():
     assert not out.value
     x = C.c_void_p(16)
     assert L.vla_quantize_rows_i8(x, 1, 1, x, x, None) == 6
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the benchmark measures one GPU; asking for several ends with a message and status 2, before any GPU work
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "--gpus must be 1" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
