@@ -282,18 +282,29 @@ def main():
     phases["denoise_hbm_frac"] = sb / (phases["denoise_step_ms"] * 1e-3) / (PEAK_HBM_GBS * 1e9)
     phases["denoise_mfma_frac"] = expert_step_flops(cfg) / (phases["denoise_step_ms"] * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
 
-    # ---- roofline of the dominant kernel: prefix gate/up GEMM (GeGLU epilogue)
+    # ---- roofline of the dominant kernel: prefix gate/up GEMM (GeGLU epilogue).
+    # Its ceiling is whichever of the MFMA peak and the HBM peak allows less:
+    # at 288 rows it moves 144.8 MB (bf16 weights, activations, GeGLU output)
+    # for 38.65 GFLOP, 267 FLOP/B, below the 312 FLOP/B ridge of 2.5 PF over
+    # 8 TB/s, so HBM bounds it; at thousands of rows the MFMA peak does.
     N = cfg.n_prefix * cfg.batch
     flops_per_launch = 2 * N * cfg.d_p * 2 * cfg.F_p
+    bytes_per_launch = 2 * (cfg.d_p * 2 * cfg.F_p + N * cfg.d_p + N * cfg.F_p)
     if probe_launches:
         avg_ms = probe_ms / probe_launches
-        achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "kernel": GATEUP_KERNEL + " (prefix gate/up + GeGLU)",
-                    "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": achieved / PEAK_BF16_TFLOPS,
-                    "traffic": GATEUP_TRAFFIC_BYTES if args.config == 1 else None,
-                    "avg_launch_us": avg_ms * 1e3, "launches": probe_launches,
-                    "flops_per_launch": flops_per_launch}
+        tflops = flops_per_launch / (avg_ms * 1e-3) / 1e12
+        gbs = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+        hbm_bound = bytes_per_launch / (PEAK_HBM_GBS * 1e9) >= flops_per_launch / (PEAK_BF16_TFLOPS * 1e12)
+        if hbm_bound:
+            head = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}
+        else:
+            head = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": tflops / PEAK_BF16_TFLOPS}
+        roofline = dict(head, kernel=GATEUP_KERNEL + " (prefix gate/up + GeGLU)",
+                        traffic=GATEUP_TRAFFIC_BYTES if args.config == 1 else None,
+                        avg_launch_us=avg_ms * 1e3, launches=probe_launches,
+                        bytes_per_launch=bytes_per_launch, flops_per_launch=flops_per_launch,
+                        tflops=tflops, mfma_frac=tflops / PEAK_BF16_TFLOPS, hbm_frac=gbs / PEAK_HBM_GBS)
     else:  # the ternary prefix runs its gate/up on the W2A8 kernel, which has no probe
         roofline = None
 
