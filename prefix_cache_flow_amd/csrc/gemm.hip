@@ -405,7 +405,7 @@ __device__ __forceinline__ void af8_body(const FragP& p, u32x4_t (*sw)[16][64], 
   }
   const uint32_t lo = lane * 16;
   auto soff = [&](int s) { return (uint32_t)min(s, max(nsl - 1, 0)) * (KS * 1024); };
-  u32x4_t a0[TBW][KS], a1[TBW][KS], w0[2], w1[2];
+  u32x4_t a0[TBW][KS], a1[TBW][KS], a2[TBW][KS], w0[2], w1[2];
   auto lda = [&](u32x4_t(&a)[TBW][KS], int s) {
     const uint32_t o = soff(s) + lo;
 #pragma unroll
@@ -443,37 +443,35 @@ __device__ __forceinline__ void af8_body(const FragP& p, u32x4_t (*sw)[16][64], 
   };
   using First = std::integral_constant<bool, true>;
   using Next = std::integral_constant<bool, false>;
+  // Activation fragments rotate through three register sets (slice t in set
+  // t % 3, fetched three slices ahead from L2); weight slices through two
+  // register sets and two LDS buffers.
   ldw(w0, 0);
   ldw(w1, 1);
   lda(a0, 0);
   lda(a1, 1);
+  lda(a2, 2);
   stw(w0, 0);
   ldw(w0, 2);
   __syncthreads();
-  auto two_slices = [&](int s, auto first) {
-    stw(w1, 1);
+  auto slice = [&](int t, u32x4_t(&wn)[2], u32x4_t(&a)[TBW][KS], auto first) {
+    stw(wn, (t + 1) & 1);  // slice t + 1 into the buffer slice t - 1 used
     __builtin_amdgcn_sched_barrier(0);
-    ldw(w1, s + 3);
-    compute(a0, 0, first);
+    ldw(wn, t + 3);
+    compute(a, t & 1, first);
     __builtin_amdgcn_sched_barrier(0);
-    lda(a0, s + 2);
-    __syncthreads();
-    stw(w0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    ldw(w0, s + 4);
-    if (ODD && s + 1 >= nsl) {
-#pragma unroll
-      for (int i = 0; i < TBW; ++i)
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) a1[i][kk] = u32x4_t{0, 0, 0, 0};
-    }
-    compute(a1, 1, Next{});
-    __builtin_amdgcn_sched_barrier(0);
-    lda(a1, s + 3);
+    lda(a, t + 3);
     __syncthreads();
   };
-  two_slices(0, First{});
-  for (int s = 2; s < nsl; s += 2) two_slices(s, Next{});
+  for (int s = 0; s < nsl; s += 6) {
+    if (s == 0) slice(0, w1, a0, First{});
+    else slice(s, w1, a0, Next{});
+    if (s + 1 < nsl) slice(s + 1, w0, a1, Next{});
+    if (s + 2 < nsl) slice(s + 2, w1, a2, Next{});
+    if (s + 3 < nsl) slice(s + 3, w0, a0, Next{});
+    if (s + 4 < nsl) slice(s + 4, w1, a1, Next{});
+    if (s + 5 < nsl) slice(s + 5, w0, a2, Next{});
+  }
   mfma_wait_states();
 #pragma unroll
   for (int i = 0; i < TBW; ++i)
