@@ -241,6 +241,20 @@ vla_status vla_w2a8_gemm_ex(const int8_t* a, const float* alpha, const uint8_t* 
                             int32_t K, int32_t* acc_out, uint16_t* y_bf16, void* stream,
                             float* kernel_ms);
 
+/* vla_w2a8_gemm for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * same arguments, same results bit for bit, but the repacked weights and the
+ * invalid-code flag live in a fixed 16 MiB scratch array that the library
+ * holds on each device it runs on until the process ends, so this call makes
+ * no hipMalloc, hipFree or other allocating call.  N * K / 4 must not exceed
+ * 16 MiB - 256 bytes (VLA_ERR_UNSUPPORTED otherwise).  Every call on a device
+ * reuses that device's scratch: calls that overlap on one device (another
+ * thread, or another stream before this one has returned) race and give
+ * undefined results.  Synchronises `stream`. */
+vla_status vla_w2a8_gemm_noalloc(const int8_t* a, const float* alpha, const uint8_t* q_packed,
+                                 float beta, int32_t M, int32_t N, int32_t K, int32_t* acc_out,
+                                 uint16_t* y_bf16, void* stream);
+
 /* Host helpers for the packed ternary format: pack codes q in {-1, 0, 1}
  * (host int8 [N][K], K % 4 == 0) into host uint8 [N][K/4]; unpack the reverse
  * (VLA_ERR_INVALID_ARGUMENT on a code 3). */

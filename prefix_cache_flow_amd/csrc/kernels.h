@@ -122,6 +122,15 @@ hipError_t gemm_w2a8_dot4(const int8_t* a, int lda, const uint32_t* qp, int M, i
 // Canonical packed ternary [N][K/4] bytes -> library layout; flags[0] |= 1 on a code 3.
 hipError_t ternary_repack(const uint8_t* canon, int N, int K, uint32_t* out, int* flags, hipStream_t s);
 
+// Fixed device scratch of the allocation-free ternary GEMM entry point
+// (w2a8.hip): kW2A8ScratchBytes bytes per device, the repacked words first and
+// a 256-byte flag area at the end.  w2a8_scratch returns its device address on
+// the current device (looked up once per device).
+constexpr size_t kW2A8ScratchBytes = (size_t)16 << 20;
+constexpr size_t kW2A8FlagBytes = 256;
+constexpr int kMaxDevices = 64;
+hipError_t w2a8_scratch(void** ptr);
+
 // ------------------------------------------------------------------ row kernels
 // Row-wise residual update and RMSNorm: for each row m,
 //   h[m] += sum_s part[s][m]           (if nsplit > 0; part is [nsplit][M][N] fp32)

@@ -1388,6 +1388,45 @@ extern "C" vla_status vla_w2a8_gemm(const int8_t* a, const float* alpha, const u
   return done(VLA_OK);
 }
 
+// The same GEMM for callers that cannot allocate: the repacked weight words and
+// the invalid-code flag go to the library's fixed per-device scratch array
+// (kernels.h, w2a8_scratch) instead of fresh device allocations.  No
+// hipMalloc, hipFree or other allocating call is made; calls on one device
+// share the array, so calls that overlap on one device race.
+extern "C" vla_status vla_w2a8_gemm_noalloc(const int8_t* a, const float* alpha, const uint8_t* q_packed, float beta,
+                                            int32_t M, int32_t N, int32_t K, int32_t* acc_out, uint16_t* y_bf16,
+                                            void* stream) {
+  if (!a || !alpha || !q_packed) return fail(VLA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (M <= 0 || N <= 0 || K <= 0) return fail(VLA_ERR_INVALID_ARGUMENT, "M, N and K must be positive");
+  if (K % 128 || N % 32) return fail(VLA_ERR_UNSUPPORTED, "need K % 128 == 0 and N % 32 == 0");
+  if (!std::isfinite(beta)) return fail(VLA_ERR_INVALID_ARGUMENT, "non-finite beta");
+  const size_t words_bytes = (size_t)N * (size_t)K / 4;
+  if (words_bytes > kW2A8ScratchBytes - kW2A8FlagBytes)
+    return fail(VLA_ERR_UNSUPPORTED, "N * K / 4 = " + std::to_string(words_bytes) + " bytes exceeds the fixed scratch of " +
+                                         std::to_string(kW2A8ScratchBytes - kW2A8FlagBytes) + " bytes");
+  vla_status st = check_device();
+  if (st != VLA_OK) return st;
+  void* base = nullptr;
+  hipError_t e = w2a8_scratch(&base);
+  if (e != hipSuccess) return fail(VLA_ERR_DEVICE, std::string("scratch lookup: ") + hipGetErrorString(e));
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* words = (uint32_t*)base;
+  int* flags = (int*)((char*)base + kW2A8ScratchBytes - kW2A8FlagBytes);
+  // the flag keeps the previous call's value: clear it first
+  if (hipMemsetAsync(flags, 0, kW2A8FlagBytes, s) != hipSuccess) return fail(VLA_ERR_DEVICE, "flag clear");
+  if (ternary_repack(q_packed, N, K, words, flags, s) != hipSuccess) return fail(VLA_ERR_DEVICE, "repack");
+  int hf = 0;
+  if (hipMemcpyAsync(&hf, flags, 4, hipMemcpyDeviceToHost, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+    return fail(VLA_ERR_DEVICE, "flag readback");
+  if (hf) return fail(VLA_ERR_INVALID_ARGUMENT, "packed weights contain the invalid code 3");
+  Epilogue ep = epi_store(y_bf16, N, 0);
+  ep.alpha = alpha;
+  ep.acc_out = acc_out;
+  if (gemm_w2a8_scalar(a, K, words, M, N, K, ep, beta, s) != hipSuccess) return fail(VLA_ERR_DEVICE, "w2a8 launch");
+  if (hipStreamSynchronize(s) != hipSuccess) return fail(VLA_ERR_DEVICE, "w2a8 sync");
+  return VLA_OK;
+}
+
 extern "C" vla_status vla_w2a8_gemm_ex(const int8_t* a, const float* alpha, const uint8_t* q_packed, const float* beta,
                                        int32_t group, int32_t path, int32_t M, int32_t N, int32_t K, int32_t* acc_out,
                                        uint16_t* y_bf16, void* stream, float* kernel_ms) {

@@ -16,6 +16,8 @@
 // fragment serves both 32-row halves).  The activation slice is
 // staged in LDS as int8; the weight slice is staged *packed* (2 bits per weight,
 // a quarter of the int8 bytes) and unpacked in registers right before the MFMA.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -280,6 +282,35 @@ hipError_t ternary_repack(const uint8_t* canon, int N, int K, uint32_t* out, int
   const int blocks = (int)std::min<long>((words + 255) / 256, 4096);
   hipLaunchKernelGGL(k_ternary_repack, dim3(blocks), dim3(256), 0, s, canon, N, K, out, flags);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ fixed scratch
+// Device memory of the allocation-free ternary GEMM entry point: the repacked
+// weight words followed by the invalid-code flag word.  The array is part of
+// the code object, so every device the library runs on holds its own copy from
+// the moment the module is loaded on it until the process ends; calls on one
+// device share (and overwrite) it.  Its name is only a host-side handle: host
+// code uses the device address that hipGetSymbolAddress returns, looked up once
+// per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kW2A8ScratchBytes];
+
+hipError_t w2a8_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace vla

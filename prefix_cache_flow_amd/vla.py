@@ -30,6 +30,7 @@ EXPORTS = (
     "vla_model_destroy", "vla_kv_cache_bytes", "vla_prefix_encode", "vla_denoise_chunk",
     "vla_kv_cache_release", "vla_kv_cache_info", "vla_quantize_rows_i8", "vla_w2a8_gemm",
     "vla_ternary_pack", "vla_ternary_unpack", "vla_probe_arm", "vla_probe_read", "vla_w2a8_gemm_ex",
+    "vla_w2a8_gemm_noalloc",
 )
 W2A8_MFMA, W2A8_DOT4 = 0, 1
 PROBE_PREFIX_GATEUP, PROBE_PREFIX_DOWN, PROBE_PREFIX_QKV, PROBE_PREFIX_ATTN, PROBE_PREFIX_O, PROBE_CACHE = range(1, 7)
@@ -91,6 +92,7 @@ def lib():
         "vla_kv_cache_info": (I, [P, C.POINTER(I), C.POINTER(I)]),
         "vla_quantize_rows_i8": (I, [P, I, I, P, P, P]),
         "vla_w2a8_gemm": (I, [P, P, P, C.c_float, I, I, I, P, P, P]),
+        "vla_w2a8_gemm_noalloc": (I, [P, P, P, C.c_float, I, I, I, P, P, P]),
         "vla_w2a8_gemm_ex": (I, [P, P, P, C.POINTER(C.c_float), I, I, I, I, I, P, P, P, C.POINTER(C.c_float)]),
         "vla_ternary_pack": (I, [P, I, I, P]),
         "vla_ternary_unpack": (I, [P, I, I, P]),
@@ -383,3 +385,14 @@ def vla_w2a8_gemm(a, alpha, q_packed, beta: float, want_acc: bool = True, want_y
                                _ptr(acc) if acc is not None else None, _ptr(y) if y is not None else None,
                                _stream(stream)))
     return acc, y
+
+
+def vla_w2a8_gemm_noalloc(a, alpha, q_packed, beta: float, acc_out=None, y_out=None, stream=None):
+    """As vla_w2a8_gemm, writing into caller-provided outputs (acc int32 [M, N] and/or y bf16 [M, N],
+    either may be None); the library allocates nothing for the call."""
+    M, K = a.shape
+    N = q_packed.shape[0]
+    _check(lib().vla_w2a8_gemm_noalloc(_ptr(a), _ptr(alpha), _ptr(q_packed), float(beta), M, N, K,
+                                       _ptr(acc_out) if acc_out is not None else None,
+                                       _ptr(y_out) if y_out is not None else None, _stream(stream)))
+    return acc_out, y_out
