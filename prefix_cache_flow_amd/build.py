@@ -17,7 +17,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvla.so")
 ARCH = "gfx950"
 
-SOURCES = ["gemm.hip", "attention.hip", "norm.hip", "expert.hip", "w2a8.hip", "runtime.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "norm.hip", "expert.hip", "w2a8.hip", "fused.hip", "runtime.cpp"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -131,6 +131,12 @@ static void chunk_plan(int K, int splits, int* used, int* per_steps) {
   *used = (steps + per - 1) / per;
 }
 
+void gemm_chunk_plan(int K, int splits, int* used, int* kchunk) {
+  int per = 0;
+  chunk_plan(K, splits, used, &per);
+  *kchunk = per * 32;
+}
+
 int gemm_chunk_splits(int K, int splits) {
   int used, per;
   chunk_plan(K, splits, &used, &per);

@@ -198,6 +198,48 @@ struct StepRows {
   Prefetch pf;
 };
 hipError_t step_rows(const StepRows& a, int w_f32, hipStream_t s);
+// ------------------------------------------------------------------ persistent solver step
+// One solver step of the bf16 cross-attention expert for at most 64 chunk rows
+// as one persistent kernel (fused.hip): the same tiles and summation orders as
+// the kernel chain of run_steps, phases separated by grid barriers.  Byte
+// sizes bound every coherent access (buffer resources); all below 2 GB.
+struct FusedStepP {
+  int M, B, H, Hp, N, Np;               // chunk rows, batch, chunk tokens (padded), prefix tokens (padded)
+  int d_e, d_a, F, L, Hq, Hkv, D;       // expert shapes, D = hd_e
+  int qe, qkve, nrb;                    // query width, fused projection width, 16-row attention blocks
+  float eps;
+  int k_head, k_embed;                  // row phase at the start (either may be < 0)
+  int trailing_head, k_tail;            // last step: head of step k_tail after the last layer
+  unsigned gen, gen_tail;               // barrier generations of this launch
+  int kc_qkv, kc_q, kc_gu, kc_o, kc_d;  // K chunk (elements) of each GEMM, as gemm_chunk plans it
+  int s_o, s_d;                         // K splits of the O and down projections
+  int spw_qkv, spw_q, spw_gu, spw_o, spw_d;  // k-steps per wave
+  const char* ew;                       // expert weight arena, layer l at ew + l * ew_layer
+  long ew_layer, off_qkv, off_os, off_qc, off_oc, off_gu, off_d;
+  const float* egains;                  // [L][3][d_e]: a1, a2, a3
+  const float* w_ef;
+  const uint16_t* w_out;
+  const uint16_t* w_in;
+  const float* sched;
+  const uint16_t* cache;                // [B][L][2][Hkv][Np][D], MFMA operand orders
+  float* E;
+  float* X;
+  uint16_t *u, *q, *kc, *vc, *attn, *eq, *g;
+  float* part;
+  uint32_t bytes_E, bytes_X, bytes_u, bytes_q, bytes_kv, bytes_attn, bytes_g, bytes_part, bytes_cache;
+  unsigned* bar;                        // fused_barrier_words(L) words, zeroed per solver run
+  unsigned* err;                        // bit 0: a barrier wait gave up
+  int nwg;                              // compute workgroups (all resident)
+};
+long fused_barrier_words(int L);
+hipError_t fused_zero(unsigned* bar, long words, hipStream_t s);
+// workgroups of k_fused_step that fit on one CU for head width D and M chunk rows
+int fused_occupancy(int D, int M);
+// launch one step: nwg compute workgroups, plus nwg shadow workgroups if `shadows`
+hipError_t fused_step(const FusedStepP& p, int shadows, hipStream_t s);
+// K split plan of gemm_chunk: number of chunks and chunk length in elements
+void gemm_chunk_plan(int K, int splits, int* used, int* kchunk);
+
 // dst = src (fp32), or bf16(src) when out_bf16
 hipError_t copy_out(const float* src, void* dst, long n, int out_bf16, hipStream_t s);
 hipError_t copy_f32(const float* src, float* dst, long n, hipStream_t s);

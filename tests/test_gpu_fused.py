@@ -1,0 +1,81 @@
+"""The persistent solver step (one kernel per Euler step) against the kernel chain and the oracle.
+
+Both paths run the same tiles with the same summation orders, so the action
+chunk must agree bit for bit; the persistent path must also meet the oracle
+bounds of the end-to-end tests (Eq. 5 of the paper, §III-E).  Models created
+with VLA_FUSED=1 in the environment take the persistent path, the others the
+kernel chain.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from policy_cases import SMALL_BF16, SMALL_GQA, SMALL_W2A8, build_model, host_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from prefix_cache_flow_amd import vla  # noqa: E402
+
+SMALL_HD256 = synth.config(1, name="small_hd256", n_prefix=75, d_p=256, L_p=2, Hq=4, Hkv=1, hd=64, F_p=512,
+                           d_e=256, L_e=3, Hq_e=4, Hkv_e=1, hd_e=256, F_e=512, H=50, d_a=32, steps=3)
+SMALL_HD128_B2 = synth.config(1, name="small_hd128_b2", batch=2, n_prefix=40, d_p=256, L_p=2, Hq=4, Hkv=1, hd=64,
+                              F_p=512, d_e=128, L_e=2, Hq_e=4, Hkv_e=2, hd_e=128, F_e=256, H=24, d_a=6, steps=4)
+
+
+def _model(cfg, w, b, fused):
+    old = os.environ.get("VLA_FUSED")
+    os.environ["VLA_FUSED"] = "1" if fused else "0"
+    try:
+        return build_model(cfg, w, b)
+    finally:
+        if old is None:
+            del os.environ["VLA_FUSED"]
+        else:
+            os.environ["VLA_FUSED"] = old
+
+
+def _run(cfg, model, z0, x0, timing=False):
+    zt = torch.from_numpy(np.ascontiguousarray(z0)).cuda()
+    xt = torch.from_numpy(np.ascontiguousarray(x0)).cuda()
+    kv = vla.vla_prefix_encode(model, zt)
+    out = vla.vla_denoise_chunk(model, kv, xt, cfg.steps, out_dtype=torch.float32, timing=timing)
+    if timing:
+        out = out[0]
+    torch.cuda.synchronize()
+    res = out.cpu().numpy()
+    kv.close()
+    return res
+
+
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_GQA, SMALL_W2A8, SMALL_HD256, SMALL_HD128_B2],
+                         ids=lambda c: c.name)
+def test_persistent_step_equals_kernel_chain(cfg):
+    print(f"case {cfg.name}", flush=True)
+    w, b, z0, x0 = host_inputs(cfg, 0)
+    fused = _run(cfg, _model(cfg, w, b, True), z0, x0, timing=True)  # timing also checks the barrier error word
+    chain = _run(cfg, _model(cfg, w, b, False), z0, x0)
+    np.testing.assert_array_equal(fused.view(np.int32), chain.view(np.int32))
+    if cfg.name in ("small_hd256", "small_hd128_b2"):
+        ref = oracle.Oracle(cfg, w, b).run(z0, x0)
+        x0d = x0.astype(np.float64)
+        e, ed = oracle.e_rel(fused, ref), oracle.e_rel(fused - x0d, ref - x0d)
+        print(f"[{cfg.name}] e_rel(X^T)={e:.3e} e_rel(D)={ed:.3e}", flush=True)
+        assert e <= 2e-2 and ed <= 1e-2
+
+
+def test_persistent_step_replays_and_repeats():
+    """Graph replays of the persistent steps give the same bits as the first run (barrier counters are
+    cleared at the start of every solver run), and a second cache on the same model too."""
+    cfg = SMALL_GQA
+    w, b, z0, x0 = host_inputs(cfg, 0)
+    model = _model(cfg, w, b, True)
+    first = _run(cfg, model, z0, x0)
+    for _ in range(3):
+        np.testing.assert_array_equal(_run(cfg, model, z0, x0, timing=True).view(np.int32), first.view(np.int32))
