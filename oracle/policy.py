@@ -35,6 +35,15 @@ chunk's own, in one softmax, then the MLP:
 Prefix tokens never see the chunk (their keys and values come from the prefix
 pass alone): the block mask of the joint sequence.
 
+Key padding (the paper, §III-B, Eq. 2: M is 0 for visible keys and -inf for
+masked ones, and adapters keep each model's masks): an observation may fill
+only its first n of the N prefix positions.  Its keys past n then get M = -inf
+in every softmax that reads prefix keys -- the prefix's own attention, the
+cross-attention into its cache and the prefix part of joint attention -- so a
+padded observation gives the same chunk as the same observation run at length
+n, whatever the (finite) padding holds.  Padded query rows are computed and
+never read.
+
 Readings where the pages are silent (the pages name none of these pieces):
   * RMS(x; w) = x / sqrt(mean(x^2) + eps) * (1 + w), pre-norm before every
     sublayer, eps = 1e-6;
@@ -107,6 +116,20 @@ def attention(q, k, v, n_heads: int, n_kv_heads: int, head_dim: int, mask=None):
     return out
 
 
+def key_mask(n_valid: Optional[int], n_keys: int, n_extra: int = 0):
+    """Additive key mask of Eq. 2 for an observation whose first n_valid of n_keys prefix keys are
+    real: a [1, n_keys + n_extra] row, 0 for visible keys and -inf past n_valid; the n_extra keys
+    appended after the prefix's (the chunk's own, in joint attention) stay visible.  None when
+    every key is visible (n_valid is None or n_keys)."""
+    if n_valid is None or n_valid >= n_keys:
+        return None
+    if n_valid < 1:
+        raise ValueError("an observation needs at least one visible prefix key")
+    m = np.zeros((1, n_keys + n_extra), dtype=np.float64)
+    m[0, n_valid:n_keys] = -np.inf
+    return m
+
+
 def time_embedding(tau: float, d: int, dtype=np.float64):
     """Sinusoidal embedding of the solver time tau, interleaved (sin, cos) pairs."""
     i = np.arange(d // 2, dtype=np.float64)
@@ -172,35 +195,36 @@ class Oracle:
         return getattr(self.cfg, "attn", "cross") == "joint"
 
     # ---- phase 1: prefix
-    def prefix_layer_kv(self, h, l: int):
-        """One prefix layer: (its output, its keys K, its values V)."""
+    def prefix_layer_kv(self, h, l: int, n_valid: Optional[int] = None):
+        """One prefix layer: (its output, its keys K, its values V); keys past n_valid are masked."""
         c, p = self.cfg, f"prefix.{l}."
         u = rms_norm(h, self._w(p + "w1"), c.rms_eps)
         q = self._plin(u, p + "wq")
         k = self._plin(u, p + "wk")
         v = self._plin(u, p + "wv")
-        h = h + self._plin(attention(q, k, v, c.Hq, c.Hkv, c.hd), p + "wo")
+        mask = key_mask(n_valid, np.shape(h)[0])
+        h = h + self._plin(attention(q, k, v, c.Hq, c.Hkv, c.hd, mask), p + "wo")
         u = rms_norm(h, self._w(p + "w2"), c.rms_eps)
         m = gelu(self._plin(u, p + "wg")) * self._plin(u, p + "wu")
         return h + self._plin(m, p + "wd"), k, v
 
-    def prefix_layer(self, h, l: int):
-        return self.prefix_layer_kv(h, l)[0]
+    def prefix_layer(self, h, l: int, n_valid: Optional[int] = None):
+        return self.prefix_layer_kv(h, l, n_valid)[0]
 
-    def prefix_kv(self, z0) -> List[Tuple[np.ndarray, np.ndarray]]:
+    def prefix_kv(self, z0, n_valid: Optional[int] = None) -> List[Tuple[np.ndarray, np.ndarray]]:
         """Joint-attention cache: [(K_l, V_l)] of every prefix layer, each [N, Hkv * hd]."""
         h = np.asarray(z0, dtype=self.dtype)
         kv = []
         for l in range(self.cfg.L_p):
-            h, k, v = self.prefix_layer_kv(h, l)
+            h, k, v = self.prefix_layer_kv(h, l, n_valid)
             kv.append((k, v))
         return kv
 
-    def encode_prefix(self, z0):
-        """Z = RMS(h_L; w_final) for one observation's prefix z0 [N, d_p]."""
+    def encode_prefix(self, z0, n_valid: Optional[int] = None):
+        """Z = RMS(h_L; w_final) for one observation's prefix z0 [N, d_p] (first n_valid rows real)."""
         h = np.asarray(z0, dtype=self.dtype)
         for l in range(self.cfg.L_p):
-            h = self.prefix_layer(h, l)
+            h = self.prefix_layer(h, l, n_valid)
         return rms_norm(h, self._w("prefix.norm"), self.cfg.rms_eps)
 
     # ---- phase 2: cache
@@ -209,14 +233,15 @@ class Oracle:
         return [(z @ self._w(f"cache.{e}.wk").T, z @ self._w(f"cache.{e}.wv").T)
                 for e in range(self.cfg.L_e)]
 
-    def conditioning(self, z0):
+    def conditioning(self, z0, n_valid: Optional[int] = None):
         """The cached collection for one observation: projected final states, or per-layer prefix K/V."""
         if self.is_joint():
-            return self.prefix_kv(z0)
-        return self.cache_project(self.encode_prefix(z0))
+            return self.prefix_kv(z0, n_valid)
+        return self.cache_project(self.encode_prefix(z0, n_valid))
 
     # ---- phase 3: expert and solver
-    def velocity(self, x, tau: float, cache):
+    def velocity(self, x, tau: float, cache, n_valid: Optional[int] = None):
+        """v(X, tau); cached prefix keys past n_valid are masked."""
         c = self.cfg
         W = self._we
         e_ = x @ W("expert.w_in").T + time_embedding(tau, c.d_e, self.dtype)[None, :]
@@ -224,38 +249,43 @@ class Oracle:
             p = f"expert.{e}."
             u = rms_norm(e_, W(p + "a1"), c.rms_eps)
             q, k, v = u @ W(p + "wqs").T, u @ W(p + "wks").T, u @ W(p + "wvs").T
+            mask = None
             if self.is_joint():
                 kp, vp = cache[e]  # prefix layer e's keys and values, then the chunk's
+                mask = key_mask(n_valid, kp.shape[0], k.shape[0])
                 k, v = np.concatenate([kp, k]), np.concatenate([vp, v])
-            e_ = e_ + attention(q, k, v, c.Hq_e, c.Hkv_e, c.hd_e) @ W(p + "wos").T
+            e_ = e_ + attention(q, k, v, c.Hq_e, c.Hkv_e, c.hd_e, mask) @ W(p + "wos").T
             if not self.is_joint():
                 u = rms_norm(e_, W(p + "a2"), c.rms_eps)
                 kc, vc = cache[e]
                 e_ = e_ + attention(u @ W(p + "wqc").T, kc, vc, c.Hq_e, c.Hkv_e,
-                                    c.hd_e) @ W(p + "woc").T
+                                    c.hd_e, key_mask(n_valid, kc.shape[0])) @ W(p + "woc").T
             u = rms_norm(e_, W(p + "a3"), c.rms_eps)
             e_ = e_ + (gelu(u @ W(p + "wg").T) * (u @ W(p + "wu").T)) @ W(p + "wd").T
         return rms_norm(e_, W("expert.norm"), c.rms_eps) @ W("expert.w_out").T
 
-    def denoise(self, cache, x0, schedule):
+    def denoise(self, cache, x0, schedule, n_valid: Optional[int] = None):
         """X^T from X^0 [H, d_a] with the cache computed once (the cached mode)."""
         return euler_integrate(np.asarray(x0, dtype=self.dtype), schedule,
-                               lambda x, tau: self.velocity(x, tau, cache))
+                               lambda x, tau: self.velocity(x, tau, cache, n_valid))
 
-    def denoise_recompute(self, z0, x0, schedule):
+    def denoise_recompute(self, z0, x0, schedule, n_valid: Optional[int] = None):
         """Same result, re-encoding the prefix and re-projecting the cache every step."""
         def v(x, tau):
-            return self.velocity(x, tau, self.conditioning(z0))
+            return self.velocity(x, tau, self.conditioning(z0, n_valid), n_valid)
         return euler_integrate(np.asarray(x0, dtype=self.dtype), schedule, v)
 
-    def run(self, z0, x0, schedule=None, keep_cache: bool = False):
-        """Whole step for a batch: z0 [B, N, d_p], x0 [B, H, d_a] -> X^T [B, H, d_a]."""
+    def run(self, z0, x0, schedule=None, keep_cache: bool = False, lengths=None):
+        """Whole step for a batch: z0 [B, N, d_p], x0 [B, H, d_a] -> X^T [B, H, d_a].
+
+        lengths (optional, [B]): observation b fills its first lengths[b] prefix positions."""
         if schedule is None:
             schedule = uniform_schedule(self.cfg.steps)
         outs, caches = [], []
         for b in range(np.shape(z0)[0]):
-            cache = self.conditioning(z0[b])
-            outs.append(self.denoise(cache, x0[b], schedule))
+            n = None if lengths is None else int(lengths[b])
+            cache = self.conditioning(z0[b], n)
+            outs.append(self.denoise(cache, x0[b], schedule, n))
             if keep_cache:
                 caches.append(cache)
         out = np.stack(outs)

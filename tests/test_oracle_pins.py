@@ -200,11 +200,17 @@ def test_uniform_schedule():
 
 # ------------------------------------------------------ prefix layer and expert
 
-def bf_prefix_layer(W, h, l, c):
+def pad_mask(nq, nk, n):
+    """Additive key-padding mask as lists: keys t >= n get -inf for every query."""
+    return [[0.0 if t < n else -math.inf for t in range(nk)] for _ in range(nq)]
+
+
+def bf_prefix_layer(W, h, l, c, n_valid=None):
     p = f"prefix.{l}."
     u = bf_rms(h, L(W[p + "w1"]), c.rms_eps)
     q, k, v = bf_linear(u, L(W[p + "wq"])), bf_linear(u, L(W[p + "wk"])), bf_linear(u, L(W[p + "wv"]))
-    h = bf_add(h, bf_linear(bf_attention(q, k, v, c.Hq, c.Hkv, c.hd), L(W[p + "wo"])))
+    mask = None if n_valid is None else pad_mask(len(h), len(h), n_valid)
+    h = bf_add(h, bf_linear(bf_attention(q, k, v, c.Hq, c.Hkv, c.hd, mask), L(W[p + "wo"])))
     u = bf_rms(h, L(W[p + "w2"]), c.rms_eps)
     g, up = bf_linear(u, L(W[p + "wg"])), bf_linear(u, L(W[p + "wu"]))
     m = [[bf_gelu(a) * b for a, b in zip(r, s)] for r, s in zip(g, up)]
@@ -264,6 +270,65 @@ def test_velocity_brute_force(Hkv_e):
     for tau in (0.0, 0.4):
         np.testing.assert_allclose(o.velocity(x, tau, cache), bf_velocity(W, L(x), tau, cache, c),
                                    rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------------ key padding (Eq. 2 masks, §III-B)
+
+@pytest.mark.parametrize("n", [1, 3, 5])
+def test_masked_attention_brute_force_and_exact_zero_weights(n):
+    """Keys past n get M = -inf: the brute-force softmax with that mask agrees, masked keys carry
+    weight exactly 0 (any finite keys and values there leave the output bit for bit the same),
+    and the visible keys alone give the same output."""
+    rng = np.random.default_rng(40 + n)
+    Nq, Nk, Hq, Hkv, hd = 4, 5, 2, 1, 4
+    q, k, v = rng.standard_normal((Nq, Hq * hd)), rng.standard_normal((Nk, Hkv * hd)), rng.standard_normal((Nk, Hkv * hd))
+    mask = opol.key_mask(n, Nk)
+    got = oracle.attention(q, k, v, Hq, Hkv, hd, mask)
+    np.testing.assert_allclose(got, bf_attention(L(q), L(k), L(v), Hq, Hkv, hd, pad_mask(Nq, Nk, n)),
+                               rtol=1e-12, atol=1e-14)
+    k2, v2 = k.copy(), v.copy()
+    k2[n:] = 1e3 * rng.standard_normal(k2[n:].shape)
+    v2[n:] = 1e300
+    np.testing.assert_array_equal(oracle.attention(q, k2, v2, Hq, Hkv, hd, mask), got)
+    np.testing.assert_allclose(oracle.attention(q, k[:n], v[:n], Hq, Hkv, hd), got, rtol=1e-13, atol=1e-15)
+    with pytest.raises(ValueError):
+        opol.key_mask(0, Nk)
+
+
+def test_masked_prefix_layer_brute_force():
+    c = tiny_cfg(n_prefix=6)
+    W, _ = big_weights(c, seed=41)
+    h = synth.make_prefix(c, 41)[0].astype(np.float64)
+    got = oracle.Oracle(c, W).prefix_layer(h, 0, n_valid=4)
+    np.testing.assert_allclose(got, bf_prefix_layer(W, L(h), 0, c, n_valid=4), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("attn", ["cross", "joint"])
+def test_padded_observation_equals_true_length_and_ignores_padding(attn):
+    """An observation filling 4 of 9 prefix positions gives the chunk (and the valid cache rows)
+    of the same observation run at length 4; two different paddings give the same bits; and a
+    length equal to N is the unmasked computation bit for bit."""
+    c = tiny_cfg(L_p=2, L_e=2, n_prefix=9, attn=attn)
+    W, _ = big_weights(c, seed=42, scale=5.0)
+    o = oracle.Oracle(c, W)
+    rng = np.random.default_rng(42)
+    n = 4
+    z = synth.make_prefix(c, 42)[0].astype(np.float64)
+    x0 = synth.make_noise(c, 42)
+    pad1, pad2 = z.copy(), z.copy()
+    pad1[n:] = 7.0 * rng.standard_normal((c.n_prefix - n, c.d_p))
+    pad2[n:] = -3.0 * rng.standard_normal((c.n_prefix - n, c.d_p))
+    out1, caches1 = o.run(pad1[None], x0, keep_cache=True, lengths=[n])
+    out2, caches2 = o.run(pad2[None], x0, keep_cache=True, lengths=[n])
+    np.testing.assert_array_equal(out1, out2)
+    short, caches_s = o.run(z[None, :n], x0, keep_cache=True)
+    np.testing.assert_allclose(out1, short, rtol=1e-11, atol=1e-12)
+    for (k1, v1), (k2, v2), (ks, vs) in zip(caches1[0], caches2[0], caches_s[0]):
+        np.testing.assert_array_equal(k1[:n], k2[:n])
+        np.testing.assert_array_equal(v1[:n], v2[:n])
+        np.testing.assert_allclose(k1[:n], ks, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(v1[:n], vs, rtol=1e-11, atol=1e-12)
+    np.testing.assert_array_equal(o.run(z[None], x0, lengths=[c.n_prefix]), o.run(z[None], x0))
 
 
 def test_encode_prefix_is_layers_then_final_norm():
