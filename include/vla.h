@@ -11,8 +11,8 @@
  *   - prefix computed once per observation, its projections reused by every
  *     solver step, refreshed on each new observation; graphs and buffers kept
  *     for unchanged shapes ............................... the paper, §III-B
- *   - cross-attention K_C = Z W_K, V_C = Z W_V, softmax(Q K_C^T/sqrt(d_k) + M) V_C
- *                                                          the paper, §III-B, Eq. 2
+ *   - cross-attention K_C = Z W_K, V_C = Z W_V, softmax(Q K_C^T/sqrt(d_k) + M) V_C,
+ *     M = -inf on padded prefix keys, 0 elsewhere ........ the paper, §III-B, Eq. 2
  *   - joint attention: each prefix layer's own keys and values are the cache,
  *     and the action tokens' keys and values are appended to them in one
  *     softmax (the pi0 form) ............................. the paper, §III-B
@@ -170,7 +170,9 @@ vla_status vla_model_destroy(vla_model* model);
 
 /* Bytes of K/V cache storage for `batch` observations of `n_prefix` tokens:
  * blocks [batch][L_e][2 (K, V)][Hkv_e], each of Np x hd_e elements (with
- * VLA_ATTN_JOINT, block l holds prefix layer l's keys and values).
+ * VLA_ATTN_JOINT, block l holds prefix layer l's keys and values), then, at
+ * the next multiple of 256 bytes, `batch` int32 prefix lengths (written by
+ * vla_prefix_encode_masked), the total rounded up to a multiple of 256.
  * VLA_F32: float32, Np = n_prefix, element (t, d) at t * hd_e + d.
  * Otherwise bfloat16 in the operand orders of the 16x16x32 MFMA, Np = n_prefix
  * rounded up to a multiple of 32 (padding rows hold zero):
@@ -194,12 +196,29 @@ vla_status vla_prefix_encode(vla_model* model, const float* prefix_hidden, int32
                              int32_t n_prefix, void* kv_storage, size_t kv_bytes,
                              void* stream, vla_kv_cache** out, vla_timing* timing);
 
+/* vla_prefix_encode for observations of different lengths (key padding, the
+ * paper §III-B, Eq. 2: M = 0 for visible keys, -inf for masked ones).
+ * lengths: host int32 [batch], 1 <= lengths[b] <= n_prefix; observation b fills
+ * the first lengths[b] rows of its [n_prefix][d_p] block and the rest is
+ * padding, whose content is ignored (the library zeroes it on the way in).
+ * Every softmax that reads prefix keys -- the prefix attention, the expert's
+ * cross-attention and the prefix part of joint attention -- gives the padded
+ * keys weight 0, so an observation's chunk is that of the same observation
+ * encoded alone at its length.  lengths == NULL is vla_prefix_encode.  The
+ * lengths are kept in the cache storage's tail for the denoise calls.
+ * VLA_ERR_INVALID_ARGUMENT for a length outside 1..n_prefix (nothing written). */
+vla_status vla_prefix_encode_masked(vla_model* model, const float* prefix_hidden, int32_t batch,
+                                    int32_t n_prefix, const int32_t* lengths, void* kv_storage,
+                                    size_t kv_bytes, void* stream, vla_kv_cache** out,
+                                    vla_timing* timing);
+
 /* Flow-matching solver (the paper, §III-A, Eq. 1): X^0 = noise (device float32
  * [batch][H][d_a], batch and n_prefix taken from the cache), `steps` Euler
  * steps of the action expert over the cached K/V, X^T written to actions_out
- * (device [batch][H][d_a], float32 or bfloat16 by out_dtype).  At batch 1 the
- * step loop runs as a HIP graph captured once per (cache, batch, n_prefix,
- * steps) and replayed afterwards.  noise and actions_out may alias. */
+ * (device [batch][H][d_a], float32 or bfloat16 by out_dtype).  The step loop
+ * runs as a HIP graph captured once per (cache storage, prefix lengths, batch,
+ * n_prefix, steps) and replayed afterwards; the model keeps the 8 most
+ * recently used graphs.  noise and actions_out may alias. */
 vla_status vla_denoise_chunk(vla_model* model, const vla_kv_cache* kv, const float* noise,
                              int32_t steps, const vla_solver* solver, void* actions_out,
                              int32_t out_dtype, void* stream, vla_timing* timing);

@@ -1,7 +1,9 @@
-// Softmax attention of the paper's §III-B, Eq. 2, with M = 0 everywhere: the
-// prefix is bidirectional (every token sees every other), the expert's
-// self-attention covers all chunk tokens, and its cross-attention all cached
-// prefix tokens.  Query head j reads key/value head floor(j * Hkv / Hq).
+// Softmax attention of the paper's §III-B, Eq. 2: the prefix is bidirectional
+// (every token sees every other), the expert's self-attention covers all chunk
+// tokens, and its cross-attention all cached prefix tokens; the only mask is
+// key padding, M = -inf for the keys past an observation's prefix length (the
+// per-batch klen arrays of AttnArgs).  Query head j reads key/value head
+// floor(j * Hkv / Hq).
 //
 // attention_bf16 (MFMA, flash-style).  A workgroup of four waves owns 16
 // queries of one head; the four waves split the keys into four ranges and
@@ -55,8 +57,10 @@ __global__ __launch_bounds__(256) void k_attn16(AttnArgs a) {
   f32x4_t o[D / 16];
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float mrun = -INFINITY, lrun = 0.f;
+  // finite start: a wave whose keys are all padding then adds exp2(-inf) = 0
+  float mrun = -3.0e38f, lrun = 0.f;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
+  const int nk = a.klen ? min(a.klen[b], a.Nk) : a.Nk;  // visible keys of this observation
 
   uint16_t* sK = lds + w * WAVE_LDS;
   uint16_t* sVt = sK + 32 * LDK;
@@ -118,8 +122,8 @@ __global__ __launch_bounds__(256) void k_attn16(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ka = kt + grp * 4 + i, kb2 = ka + 16;
-      s0[i] = ka < a.Nk ? s0[i] * sl2 : -INFINITY;
-      s1[i] = kb2 < a.Nk ? s1[i] * sl2 : -INFINITY;
+      s0[i] = ka < nk ? s0[i] * sl2 : -INFINITY;
+      s1[i] = kb2 < nk ? s1[i] * sl2 : -INFINITY;
       mt = fmaxf(mt, fmaxf(s0[i], s1[i]));
     }
     mt = group4_max(mt);
@@ -282,6 +286,9 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
   // finite start: a tile whose keys are all masked then adds exp2(-inf) = 0
   float mrun = -3.0e38f, lrun = 0.f;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
+  // visible keys of this observation in each source (key padding)
+  const int nk1 = a.klen ? min(a.klen[b], a.Nk) : a.Nk;
+  const int nk2 = a.klen2 ? min(a.klen2[b], a.Nk2) : a.Nk2;
 
   auto consume = [&](const Tile& t, int tl) {
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
       s1 = mfma16x16x32(as_bf16x8(t.k[KS + s]), as_bf16x8(qf[s]), s1);
     }
     const bool second = tl >= TA;
-    const int kt = (second ? tl - TA : tl) * 32, nk = second ? a.Nk2 : a.Nk;
+    const int kt = (second ? tl - TA : tl) * 32, nk = second ? nk2 : nk1;
     float mt = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -443,9 +450,12 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
   const float* K2 = a.Nk2 ? (const float*)a.k2 + b * a.k2_bs + g * a.k2_hs : K;
   const float* V2 = a.Nk2 ? (const float*)a.v2 + b * a.v2_bs + g * a.v2_hs : V;
   float m = -INFINITY, l = 0.f;
+  const int nk1 = a.klen ? min(a.klen[b], a.Nk) : a.Nk;
+  const int nk2 = a.klen2 ? min(a.klen2[b], a.Nk2) : a.Nk2;
   for (int t = 0; t < a.Nk + a.Nk2; ++t) {
     const bool second = t >= a.Nk;
     const int tt = second ? t - a.Nk : t;
+    if (tt >= (second ? nk2 : nk1)) continue;  // key padding: weight 0
     const float* kr = second ? K2 + (long)tt * a.k2_rs : K + (long)tt * a.k_rs;
     float s = 0.f;
 #pragma unroll

@@ -223,6 +223,40 @@ hipError_t copy_out(const float* src, void* dst, long n, int out_bf16, hipStream
 
 hipError_t copy_f32(const float* src, float* dst, long n, hipStream_t s) { return copy_out(src, dst, n, 0, s); }
 
+struct Lengths64 {
+  int v[64];
+};
+__global__ void k_set_lengths(int* dst, Lengths64 l, int n) {
+  if ((int)threadIdx.x < n) dst[threadIdx.x] = l.v[threadIdx.x];
+}
+
+hipError_t set_lengths(int* dst, const int32_t* len, int B, int N, hipStream_t s) {
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    Lengths64 l;
+    const int n = std::min(64, B - b0);
+    for (int i = 0; i < 64; ++i) l.v[i] = i < n ? (len ? len[b0 + i] : N) : 0;
+    hipLaunchKernelGGL(k_set_lengths, dim3(1), dim3(64), 0, s, dst + b0, l, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// one row of d floats per workgroup row slot: rows past the observation's length become zeros
+__global__ void k_copy_prefix_rows(const float* src, float* dst, int N, int d, const int* lens) {
+  const long row = blockIdx.x;
+  const int b = (int)(row / N), t = (int)(row % N);
+  const bool keep = t < lens[b];
+  for (int i = threadIdx.x; i < d; i += blockDim.x) dst[row * d + i] = keep ? src[row * d + i] : 0.f;
+}
+
+hipError_t copy_prefix_rows(const float* src, float* dst, int B, int N, int d, const int* lens, hipStream_t s) {
+  if ((long)B * N <= 0) return hipSuccess;
+  if ((long)B * N > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_copy_prefix_rows, dim3((unsigned)(B * N)), dim3(256), 0, s, src, dst, N, d, lens);
+  return hipGetLastError();
+}
+
 __global__ void k_f32_to_bf16(const float* src, uint16_t* dst, long n) {
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
     dst[i] = f2bf(src[i]);

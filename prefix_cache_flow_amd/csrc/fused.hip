@@ -264,6 +264,7 @@ struct AttnT {
   long k_bs, k_hs;    // element strides (same for V)
   Buf o;
   int Nq, Nk, Hq, Hkv, R, nrb;
+  const int* klen;  // key padding: visible keys per observation (null: all Nk)
 };
 
 template <int D, int AUX>
@@ -302,6 +303,7 @@ __device__ __forceinline__ void attn_tile(const AttnT& a, int rbk, int gy, float
   for (int t = 0; t < VS; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float mrun = -3.0e38f, lrun = 0.f;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
+  const int nkb = a.klen ? min(a.klen[b], a.Nk) : a.Nk;
 
   // scores of tile tl (keys 0-15 in s0, 16-31 in s1), masked and scaled
   auto scores = [&](const Tile& t, int tl, f32x4_t& s0, f32x4_t& s1) {
@@ -315,7 +317,7 @@ __device__ __forceinline__ void attn_tile(const AttnT& a, int rbk, int gy, float
   };
   // online softmax update and O^T += V^T P^T for one tile's scores
   auto update = [&](const Tile& t, int tl, f32x4_t s0, f32x4_t s1) {
-    const int kt = tl * 32, nk = a.Nk;
+    const int kt = tl * 32, nk = nkb;
     float mt = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -826,6 +828,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_step(FusedStepP p) {
   sa.o = Ab; sa.Nq = p.H; sa.Nk = p.H; sa.Hq = p.Hq; sa.Hkv = p.Hkv; sa.R = p.Hq / p.Hkv * p.H; sa.nrb = p.nrb;
   AttnT ca = sa;
   ca.q = Cq; ca.k = Cb; ca.v = Cb; ca.k_bs = (long)L * 2 * p.Hkv * p.Np * D; ca.k_hs = (long)p.Np * D; ca.Nk = p.N;
+  ca.klen = p.klen;
   const int nat = p.nrb * p.Hkv * p.B;  // attention tiles
 
   for (int l = 0; l < L; ++l) {

@@ -162,8 +162,13 @@ struct AttnArgs {
   int o_f32;                              // 1: fp32 output, 0: bf16
   int o_frag;                             // bf16 output in fragment layout: row b * Nq + q, K = Hq * hd
   Prefetch pf;                            // attention_chunk: extra workgroups warming the next weights
+  // key padding (Eq. 2, M = -inf): batch b sees only its first klen[b] keys of
+  // the first source (klen2[b] of the second); device arrays of B entries in
+  // [1, Nk] (or [1, Nk2]), or null when every key is visible
+  const int* klen;
+  const int* klen2;
 };
-// softmax(Q K^T / sqrt(hd)) V per head, no mask; bf16 inputs on MFMA (hd in 64..256)
+// softmax(Q K^T / sqrt(hd) + M) V per head, M the key padding above; bf16 inputs on MFMA (hd in 64..256)
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s);
 // The same for short query sets with K and V in the MFMA operand orders of
 // common.h (frag_idx / vfrag_idx per batch-and-head block of k_bs / k_hs
@@ -222,6 +227,7 @@ struct FusedStepP {
   const uint16_t* w_in;
   const float* sched;
   const uint16_t* cache;                // [B][L][2][Hkv][Np][D], MFMA operand orders
+  const int* klen;                      // visible prefix keys per observation
   float* E;
   float* X;
   uint16_t *u, *q, *kc, *vc, *attn, *eq, *g;
@@ -240,6 +246,13 @@ hipError_t fused_step(const FusedStepP& p, int shadows, hipStream_t s);
 // K split plan of gemm_chunk: number of chunks and chunk length in elements
 void gemm_chunk_plan(int K, int splits, int* used, int* kchunk);
 
+// Per-observation prefix lengths into a device array: dst[b] = len[b] (host
+// values, passed to the kernel by value in groups of 64), or N for every b
+// when len is null.
+hipError_t set_lengths(int* dst, const int32_t* len, int B, int N, hipStream_t s);
+// dst = src for the [B][N][d] prefix rows, with the rows of observation b past
+// its length lens[b] (device) written as zeros.
+hipError_t copy_prefix_rows(const float* src, float* dst, int B, int N, int d, const int* lens, hipStream_t s);
 // dst = src (fp32), or bf16(src) when out_bf16
 hipError_t copy_out(const float* src, void* dst, long n, int out_bf16, hipStream_t s);
 hipError_t copy_f32(const float* src, float* dst, long n, hipStream_t s);

@@ -86,7 +86,12 @@ static vla_status check_config(const vla_model_config* c) {
     if (c->precision == VLA_W2A8_BF16 && (c->d_p % 128 || c->F_p % 128 || (c->Hq * c->hd) % 128))
       return fail(VLA_ERR_UNSUPPORTED, "ternary prefix widths must be multiples of 128");
   }
-  if (c->d_p > 16 * 256 * 4 || c->F_p > (1 << 20)) return fail(VLA_ERR_UNSUPPORTED, "model too wide");
+  // the residual + RMSNorm row kernel holds rows of up to 4096 columns and sums
+  // up to 16 split-K partials; the chunk-sized GEMM splits K in 1024-wide
+  // chunks, so the inputs of its partial products stay at 16384 or below
+  if (c->d_p > 4096) return fail(VLA_ERR_UNSUPPORTED, "d_p > 4096");
+  if (c->F_p > 16384 || c->F_e > 16384 || (int64_t)c->Hq * c->hd > 16384 || (int64_t)c->Hq_e * c->hd_e > 16384)
+    return fail(VLA_ERR_UNSUPPORTED, "F_p, F_e, Hq*hd and Hq_e*hd_e must be at most 16384");
   if (c->attn_mode != VLA_ATTN_CROSS && c->attn_mode != VLA_ATTN_JOINT)
     return fail(VLA_ERR_INVALID_ARGUMENT, "bad attn_mode");
   if (c->attn_mode == VLA_ATTN_JOINT) {
@@ -191,10 +196,22 @@ struct ExpertLayer {
   void* wd = nullptr;    // [d_e][F_e]
 };
 
+// A captured solver loop bakes in the cache storage and its lengths array, so
+// those are part of its key.  The model keeps the kMaxGraphs most recently
+// used graphs and destroys older ones (a caller that encodes every observation
+// into fresh storage would otherwise grow the set without bound).
 struct GraphKey {
   const void* kv;
+  const int* lens;
   int B, N, steps;
-  bool operator<(const GraphKey& o) const { return std::tie(kv, B, N, steps) < std::tie(o.kv, o.B, o.N, o.steps); }
+  bool operator<(const GraphKey& o) const {
+    return std::tie(kv, lens, B, N, steps) < std::tie(o.kv, o.lens, o.B, o.N, o.steps);
+  }
+};
+static const size_t kMaxGraphs = 8;
+struct GraphEntry {
+  hipGraphExec_t exec;
+  uint64_t last_use;
 };
 
 struct vla_model {
@@ -222,7 +239,8 @@ struct vla_model {
   // expert weights of all layers in one allocation, layer e at ew + e * ew_layer
   char* ew = nullptr;
   size_t ew_layer = 0;
-  std::map<GraphKey, hipGraphExec_t> graphs;
+  std::map<GraphKey, GraphEntry> graphs;
+  uint64_t graph_clock = 0;
   std::set<vla_kv_cache*> caches;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   int64_t plan_rows = 0, plan_erows = 0;  // largest prefix / chunk row counts seen
@@ -245,6 +263,7 @@ struct vla_kv_cache {
   vla_model* model = nullptr;
   int B = 0, N = 0;
   void* storage = nullptr;
+  int* lens = nullptr;  // per-observation prefix lengths, in the storage's tail
 };
 
 static std::mutex g_mu;
@@ -293,7 +312,7 @@ static vla_status dev_alloc(vla_model* m, void** p, size_t bytes) {
 }
 
 static void free_model(vla_model* m) {
-  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second.exec);
   m->graphs.clear();
   for (void* p : m->allocs) (void)hipFree(p);
   m->allocs.clear();
@@ -799,7 +818,7 @@ static vla_status ensure_ws(vla_model* m, int64_t rows, int64_t erows, int64_t k
       (void)hipFree(m->ws);
       m->ws = nullptr;
       m->ws_bytes = 0;
-      for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+      for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second.exec);
       m->graphs.clear();
     }
     void* p = nullptr;
@@ -895,14 +914,20 @@ static Epilogue epi_store(void* out, int ldo, int out_f32) {
   return e;
 }
 
-static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* kv, const WS& w, hipStream_t s) {
+// lens: per-observation prefix lengths on the device (null: every observation
+// fills all N positions).  Rows past an observation's length are zeroed on the
+// way in, and their keys are masked in the prefix attention.
+static vla_status run_prefix(vla_model* m, const float* x, int B, int N, const int* lens, void* kv, const WS& w,
+                             hipStream_t s) {
   const vla_model_config& c = m->cfg;
   const int M = B * N;
   const int qw = c.Hq * c.hd, qkvw = (c.Hq + 2 * c.Hkv) * c.hd;
   const float eps = c.rms_eps;
   const int uf = m->f32 ? 1 : 0;
-  K_TRY(copy_f32(x, w.h, (long)M * c.d_p, s), "copy prefix");
+  if (lens) K_TRY(copy_prefix_rows(x, w.h, B, N, c.d_p, lens, s), "copy prefix");
+  else K_TRY(copy_f32(x, w.h, (long)M * c.d_p, s), "copy prefix");
   AttnArgs aa{};
+  aa.klen = lens;
   aa.q = w.qkv; aa.q_bs = (long)N * qkvw; aa.q_hs = c.hd; aa.q_rs = qkvw;
   aa.k = (const char*)w.qkv + (size_t)qw * elt(m); aa.k_bs = aa.q_bs; aa.k_hs = c.hd; aa.k_rs = qkvw;
   aa.v = (const char*)w.qkv + (size_t)(qw + c.Hkv * c.hd) * elt(m); aa.v_bs = aa.q_bs; aa.v_hs = c.hd; aa.v_rs = qkvw;
@@ -1055,20 +1080,31 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, void* k
   return VLA_OK;
 }
 
-extern "C" size_t vla_kv_cache_bytes(const vla_model* m, int32_t batch, int32_t n_prefix) {
-  if (!live_model(m) || batch <= 0 || n_prefix <= 0) return 0;
+// K/V blocks of a cache; the per-observation prefix lengths follow them
+static size_t kv_core_bytes(const vla_model* m, int32_t batch, int32_t n_prefix) {
   const vla_model_config& c = m->cfg;
   return (size_t)batch * c.L_e * 2 * c.Hkv_e * (size_t)key_rows(m, n_prefix) * c.hd_e * elt(m);
 }
 
-extern "C" vla_status vla_prefix_encode(vla_model* m, const float* x, int32_t batch, int32_t n_prefix, void* kv_storage,
-                                        size_t kv_bytes, void* stream, vla_kv_cache** out, vla_timing* timing) {
+extern "C" size_t vla_kv_cache_bytes(const vla_model* m, int32_t batch, int32_t n_prefix) {
+  if (!live_model(m) || batch <= 0 || n_prefix <= 0) return 0;
+  return (kv_core_bytes(m, batch, n_prefix) + 255) / 256 * 256 + ((size_t)batch * 4 + 255) / 256 * 256;
+}
+
+extern "C" vla_status vla_prefix_encode_masked(vla_model* m, const float* x, int32_t batch, int32_t n_prefix,
+                                               const int32_t* lengths, void* kv_storage, size_t kv_bytes, void* stream,
+                                               vla_kv_cache** out, vla_timing* timing) {
   if (!out) return fail(VLA_ERR_INVALID_ARGUMENT, "out is NULL");
   *out = nullptr;
   if (!live_model(m)) return fail(VLA_ERR_INVALID_HANDLE, "unknown model");
   if (!x || !kv_storage) return fail(VLA_ERR_INVALID_ARGUMENT, "prefix_hidden or kv_storage is NULL");
   if (batch <= 0 || n_prefix <= 0) return fail(VLA_ERR_INVALID_ARGUMENT, "batch and n_prefix must be positive");
   if ((int64_t)batch * n_prefix > (1 << 22)) return fail(VLA_ERR_UNSUPPORTED, "too many prefix tokens");
+  if (lengths)
+    for (int b = 0; b < batch; ++b)
+      if (lengths[b] < 1 || lengths[b] > n_prefix)
+        return fail(VLA_ERR_INVALID_ARGUMENT, "lengths[" + std::to_string(b) + "] = " + std::to_string(lengths[b]) +
+                                                  " is outside 1.." + std::to_string(n_prefix));
   const size_t need = vla_kv_cache_bytes(m, batch, n_prefix);
   if (kv_bytes < need)
     return fail(VLA_ERR_SHAPE_MISMATCH, "kv_bytes " + std::to_string(kv_bytes) + " < required " + std::to_string(need));
@@ -1076,8 +1112,10 @@ extern "C" vla_status vla_prefix_encode(vla_model* m, const float* x, int32_t ba
   WS w;
   vla_status st = get_ws(m, (int64_t)batch * n_prefix, 0, &w, (int64_t)batch * key_rows(m, n_prefix));
   if (st != VLA_OK) return st;
+  int* lens = (int*)((char*)kv_storage + (kv_core_bytes(m, batch, n_prefix) + 255) / 256 * 256);
   if (timing) K_TRY(hipEventRecord(m->ev0, s), "event");
-  st = run_prefix(m, x, batch, n_prefix, kv_storage, w, s);
+  if (lengths) K_TRY(set_lengths(lens, lengths, batch, n_prefix, s), "prefix lengths");
+  st = run_prefix(m, x, batch, n_prefix, lengths ? lens : nullptr, kv_storage, w, s);
   if (st != VLA_OK) return st;
   if (timing) {
     K_TRY(hipEventRecord(m->ev1, s), "event");
@@ -1094,12 +1132,18 @@ extern "C" vla_status vla_prefix_encode(vla_model* m, const float* x, int32_t ba
   k->B = batch;
   k->N = n_prefix;
   k->storage = kv_storage;
+  k->lens = lengths ? lens : nullptr;
   {
     std::lock_guard<std::mutex> g(g_mu);
     m->caches.insert(k);
   }
   *out = k;
   return VLA_OK;
+}
+
+extern "C" vla_status vla_prefix_encode(vla_model* m, const float* x, int32_t batch, int32_t n_prefix, void* kv_storage,
+                                        size_t kv_bytes, void* stream, vla_kv_cache** out, vla_timing* timing) {
+  return vla_prefix_encode_masked(m, x, batch, n_prefix, nullptr, kv_storage, kv_bytes, stream, out, timing);
 }
 
 extern "C" vla_status vla_kv_cache_release(vla_kv_cache* k) {
@@ -1167,6 +1211,7 @@ static vla_status run_steps_fused(vla_model* m, const vla_kv_cache* kv, int step
   p.egains = m->egains; p.w_ef = m->w_ef;
   p.w_out = (const uint16_t*)m->w_out; p.w_in = (const uint16_t*)m->w_in; p.sched = m->sched_dev;
   p.cache = (const uint16_t*)kv->storage;
+  p.klen = kv->lens;
   p.bytes_cache = (uint32_t)vla_kv_cache_bytes(m, kv->B, kv->N);
   p.E = w.E; p.X = w.X; p.u = (uint16_t*)w.eu; p.q = (uint16_t*)w.eqkv; p.kc = (uint16_t*)w.ek; p.vc = (uint16_t*)w.ev;
   p.attn = (uint16_t*)w.eattn; p.eq = (uint16_t*)w.eq; p.g = (uint16_t*)w.emlp; p.part = w.epart;
@@ -1229,6 +1274,8 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
   ca.k_bs = c.L_e * layer_stride; ca.k_hs = (long)Np * c.hd_e; ca.k_rs = c.hd_e;
   ca.v_bs = ca.k_bs; ca.v_hs = ca.k_hs; ca.v_rs = c.hd_e;
   ca.Nk = N;
+  ca.klen = kv->lens;   // key padding of the cached prefix
+  sa.klen2 = kv->lens;  // joint attention: the prefix keys are the second source
   Epilogue pe;
   pe.kind = EPI_PARTIAL;
   const int S_o = expert_splits(M, c.d_e, qe), S_d = expert_splits(M, c.d_e, c.F_e);
@@ -1399,7 +1446,7 @@ extern "C" vla_status vla_denoise_chunk(vla_model* m, const vla_kv_cache* kv, co
       m->sched_dev = nullptr;
       m->sched_host = nullptr;
       m->sched_last.clear();
-      for (auto& g : m->graphs) (void)hipGraphExecDestroy(g.second);
+      for (auto& g : m->graphs) (void)hipGraphExecDestroy(g.second.exec);
       m->graphs.clear();
     }
     const int cap = std::max(64, steps + 1);
@@ -1427,10 +1474,19 @@ extern "C" vla_status vla_denoise_chunk(vla_model* m, const vla_kv_cache* kv, co
   K_TRY(copy_f32(noise, w.X, nx, s), "noise in");
   int replayed = 0;
   if (use_graphs()) {
-    GraphKey key{kv->storage, kv->B, kv->N, steps};
+    GraphKey key{kv->storage, kv->lens, kv->B, kv->N, steps};
     auto it = m->graphs.find(key);
     hipGraphExec_t exec = nullptr;
     if (it == m->graphs.end()) {
+      if (m->graphs.size() >= kMaxGraphs) {
+        // evict the least recently used graph, once nothing can still be running it
+        auto lru = m->graphs.begin();
+        for (auto g = m->graphs.begin(); g != m->graphs.end(); ++g)
+          if (g->second.last_use < lru->second.last_use) lru = g;
+        K_TRY(hipDeviceSynchronize(), "sync before graph eviction");
+        (void)hipGraphExecDestroy(lru->second.exec);
+        m->graphs.erase(lru);
+      }
       K_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal), "begin capture");
       vla_status rs = run_steps(m, kv, steps, w, m->cap_stream);
       hipGraph_t graph = nullptr;
@@ -1443,9 +1499,10 @@ extern "C" vla_status vla_denoise_chunk(vla_model* m, const vla_kv_cache* kv, co
       hipError_t ie = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
       (void)hipGraphDestroy(graph);
       K_TRY(ie, "graph instantiate");
-      m->graphs[key] = exec;
+      m->graphs[key] = GraphEntry{exec, ++m->graph_clock};
     } else {
-      exec = it->second;
+      exec = it->second.exec;
+      it->second.last_use = ++m->graph_clock;
       replayed = 1;
     }
     K_TRY(hipGraphLaunch(exec, s), "graph launch");

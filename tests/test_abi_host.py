@@ -82,6 +82,14 @@ def test_status_strings_and_config_validation():
     assert vla.vla_n_tensors(dict(cfg, attn="joint", hd_e=128)) == -1
     assert vla.vla_n_tensors(synth.config(4, attn="joint", L_e=30, Hkv_e=20, hd_e=128).to_dict()) == -1
     assert vla.vla_n_tensors(dict(cfg, attn=7)) == -1
+    # shapes the row kernels or the split-K planning cannot take are refused at creation,
+    # not partway through an encode or a denoise
+    assert vla.vla_n_tensors(dict(cfg, d_p=8192)) == -1
+    assert "d_p" in vla.vla_last_error()
+    assert vla.vla_n_tensors(dict(cfg, F_e=32768)) == -1
+    assert vla.vla_n_tensors(dict(cfg, F_p=32768)) == -1
+    assert vla.vla_n_tensors(dict(cfg, Hq_e=128)) == -1
+    assert vla.vla_n_tensors(dict(cfg, d_p=4096, F_p=16384, F_e=16384)) > 0
 
 
 def test_null_and_foreign_handles_are_rejected():
