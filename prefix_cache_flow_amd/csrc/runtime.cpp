@@ -59,6 +59,42 @@ extern "C" const char* vla_status_string(vla_status s) {
 
 extern "C" const char* vla_last_error(void) { return g_last_error.c_str(); }
 
+// ============================================================== allocation fault injection
+// Every device and pinned-host allocation of the library goes through
+// lib_malloc / lib_host_malloc.  With VLA_FAIL_ALLOC=n in the environment the
+// n-th allocation after the variable was (re)set fails as if memory were
+// exhausted (n <= 0 or unset: none fails), so tests can walk every
+// out-of-memory path.  The variable is read at every allocation; a changed
+// value restarts the count.
+static std::mutex g_inject_mu;
+static std::string g_inject_env;
+static long g_inject_count = 0;
+
+static bool inject_failure() {
+  const char* v = getenv("VLA_FAIL_ALLOC");
+  std::lock_guard<std::mutex> g(g_inject_mu);
+  const std::string cur = v ? v : "";
+  if (cur != g_inject_env) {
+    g_inject_env = cur;
+    g_inject_count = 0;
+  }
+  if (cur.empty()) return false;
+  const long n = strtol(cur.c_str(), nullptr, 10);
+  return n > 0 && ++g_inject_count == n;
+}
+
+static hipError_t lib_malloc(void** p, size_t bytes) {
+  *p = nullptr;
+  if (inject_failure()) return hipErrorOutOfMemory;
+  return hipMalloc(p, bytes);
+}
+
+static hipError_t lib_host_malloc(void** p, size_t bytes) {
+  *p = nullptr;
+  if (inject_failure()) return hipErrorOutOfMemory;
+  return hipHostMalloc(p, bytes);
+}
+
 // ============================================================== config
 static bool pos(int v) { return v > 0; }
 
@@ -302,7 +338,7 @@ static size_t elt(const vla_model* m) { return m->f32 ? 4 : 2; }
 static vla_status dev_alloc(vla_model* m, void** p, size_t bytes) {
   *p = nullptr;
   if (bytes == 0) bytes = 16;
-  hipError_t e = hipMalloc(p, bytes);
+  hipError_t e = lib_malloc(p, bytes);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return fail(VLA_ERR_OUT_OF_MEMORY, "hipMalloc of " + std::to_string(bytes) + " bytes failed");
@@ -382,7 +418,7 @@ static vla_status build_weights(vla_model* m, const vla_weights* w, hipStream_t 
     for (void* p : temps) (void)hipFree(p);
   };
   if (m->w2a8) {
-    if (hipMalloc(&flags, 64) != hipSuccess) return fail(VLA_ERR_OUT_OF_MEMORY, "flags");
+    if (lib_malloc((void**)&flags, 64) != hipSuccess) return fail(VLA_ERR_OUT_OF_MEMORY, "flags");
     temps.push_back(flags);
     if (hipMemsetAsync(flags, 0, 64, s) != hipSuccess) { cleanup(); return fail(VLA_ERR_DEVICE, "memset"); }
   }
@@ -405,7 +441,7 @@ static vla_status build_weights(vla_model* m, const vla_weights* w, hipStream_t 
     if (!m->w2a8)
       big = std::max<int64_t>(big, std::max<int64_t>(std::max<int64_t>(qkvw, 2 * (int64_t)c.F_p) * c.d_p,
                                                      (int64_t)c.d_p * std::max<int64_t>(qw, c.F_p)));
-    if (hipMalloc(&stage, big * es) != hipSuccess) {
+    if (lib_malloc(&stage, big * es) != hipSuccess) {
       (void)hipGetLastError();
       cleanup();
       return fail(VLA_ERR_OUT_OF_MEMORY, "staging");
@@ -457,7 +493,7 @@ static vla_status build_weights(vla_model* m, const vla_weights* w, hipStream_t 
       // gate/up: repack each, then interleave the word rows
       void *tg = nullptr, *tu = nullptr;
       const int64_t gbytes = (int64_t)c.F_p * c.d_p / 4;
-      if (hipMalloc(&tg, gbytes) != hipSuccess || hipMalloc(&tu, gbytes) != hipSuccess) {
+      if (lib_malloc(&tg, gbytes) != hipSuccess || lib_malloc(&tu, gbytes) != hipSuccess) {
         if (tg) (void)hipFree(tg);
         cleanup();
         return fail(VLA_ERR_OUT_OF_MEMORY, "ternary staging");
@@ -598,8 +634,9 @@ static vla_status setup_fused(vla_model* m, hipStream_t s) {
   if (hipGetDeviceProperties(&prop, m->device) != hipSuccess) return fail(VLA_ERR_DEVICE, "hipGetDeviceProperties");
   m->ncu = prop.multiProcessorCount;
   const size_t gb = (size_t)c.L_e * 3 * c.d_e * 4;
-  if (hipMalloc(&m->egains, gb) != hipSuccess || hipMalloc(&m->fbar, fused_barrier_words(c.L_e) * 4) != hipSuccess ||
-      hipMalloc(&m->ferr, 256) != hipSuccess) {
+  if (lib_malloc((void**)&m->egains, gb) != hipSuccess ||
+      lib_malloc((void**)&m->fbar, fused_barrier_words(c.L_e) * 4) != hipSuccess ||
+      lib_malloc((void**)&m->ferr, 256) != hipSuccess) {
     (void)hipGetLastError();
     return fail(VLA_ERR_OUT_OF_MEMORY, "persistent step buffers");
   }
@@ -822,7 +859,7 @@ static vla_status ensure_ws(vla_model* m, int64_t rows, int64_t erows, int64_t k
       m->graphs.clear();
     }
     void* p = nullptr;
-    if (hipMalloc(&p, need.total) != hipSuccess) {
+    if (lib_malloc(&p, need.total) != hipSuccess) {
       (void)hipGetLastError();
       return fail(VLA_ERR_OUT_OF_MEMORY, "workspace allocation of " + std::to_string(need.total) + " bytes failed");
     }
@@ -1450,7 +1487,7 @@ extern "C" vla_status vla_denoise_chunk(vla_model* m, const vla_kv_cache* kv, co
       m->graphs.clear();
     }
     const int cap = std::max(64, steps + 1);
-    if (hipMalloc(&m->sched_dev, cap * 4) != hipSuccess || hipHostMalloc(&m->sched_host, cap * 4) != hipSuccess) {
+    if (lib_malloc((void**)&m->sched_dev, cap * 4) != hipSuccess || lib_host_malloc((void**)&m->sched_host, cap * 4) != hipSuccess) {
       (void)hipGetLastError();
       return fail(VLA_ERR_OUT_OF_MEMORY, "schedule buffers");
     }
@@ -1553,7 +1590,7 @@ extern "C" vla_status vla_w2a8_gemm(const int8_t* a, const float* alpha, const u
   hipStream_t s = (hipStream_t)stream;
   uint32_t* words = nullptr;
   int* flags = nullptr;
-  if (hipMalloc(&words, (size_t)N * K / 4) != hipSuccess || hipMalloc(&flags, 64) != hipSuccess) {
+  if (lib_malloc((void**)&words, (size_t)N * K / 4) != hipSuccess || lib_malloc((void**)&flags, 64) != hipSuccess) {
     (void)hipGetLastError();
     if (words) (void)hipFree(words);
     return fail(VLA_ERR_OUT_OF_MEMORY, "staging");
@@ -1645,8 +1682,8 @@ extern "C" vla_status vla_w2a8_gemm_ex(const int8_t* a, const float* alpha, cons
       if (e) (void)hipEventDestroy(e);
     return r;
   };
-  if (hipMalloc(&words, (size_t)N * K / 4) != hipSuccess || hipMalloc(&flags, 64) != hipSuccess ||
-      hipMalloc(&bdev, (size_t)N * 4) != hipSuccess) {
+  if (lib_malloc((void**)&words, (size_t)N * K / 4) != hipSuccess || lib_malloc((void**)&flags, 64) != hipSuccess ||
+      lib_malloc((void**)&bdev, (size_t)N * 4) != hipSuccess) {
     (void)hipGetLastError();
     return done(fail(VLA_ERR_OUT_OF_MEMORY, "staging"));
   }

@@ -14,7 +14,8 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libvla.so")
+# VLA_LIBRARY selects another build of the same library (the sanitized host build of the tests)
+LIB_PATH = os.environ.get("VLA_LIBRARY") or os.path.join(HERE, "libvla.so")
 
 VLA_OK = 0
 STATUS = {0: "VLA_OK", 1: "VLA_ERR_INVALID_ARGUMENT", 2: "VLA_ERR_SHAPE_MISMATCH", 3: "VLA_ERR_INVALID_HANDLE",
