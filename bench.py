@@ -48,7 +48,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-s", type=float, default=30.0)
     p.add_argument("--no-extras", action="store_true",
-                   help="skip the solver-step sweep and the two-stream pipelined run")
+                   help="skip the solver-step sweep, the two-stream pipelined run and the ternary ablation")
+    p.add_argument("--no-batched", action="store_true", help="skip the batched-workload entry")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB mebibytes (reference for the HBM byte counters) and exit")
     return p.parse_args()
@@ -205,6 +206,50 @@ def pipelined(vla, model, cfg, zt, xt, n, warmup=2):
             "note": "prefix of observation k+1 overlapped with the solver of observation k on two streams"}
 
 
+DTYPE = {"f32": "f32", "bf16": "bf16", "w2a8": "int8 x ternary (int32 accumulation) prefix, bf16 expert"}
+
+
+def batched_entry(vla, model, cfg1, steps=3, warmup=1):
+    """The batched workload (16 observations of 512 prefix tokens, 800 chunk rows, 10 solver steps): the
+    same model shapes as the single-camera workload, so the line's own model times it on its own seeded
+    16 x 512 prefixes and noise.  At 800 rows the expert's products are bound by the MFMA peak."""
+    import torch
+    import synth
+    cfg = synth.config(3)
+    assert (cfg.d_p, cfg.L_p, cfg.d_e, cfg.L_e, cfg.F_p, cfg.F_e) == (cfg1.d_p, cfg1.L_p, cfg1.d_e, cfg1.L_e,
+                                                                       cfg1.F_p, cfg1.F_e)
+    zt = torch.from_numpy(synth.make_prefix(cfg, 3)).cuda()
+    xt = torch.from_numpy(synth.make_noise(cfg, 3)).cuda()
+    out = torch.empty(xt.shape, dtype=torch.bfloat16, device="cuda")
+    store = torch.empty(vla.vla_kv_cache_bytes(model, cfg.batch, cfg.n_prefix), dtype=torch.uint8, device="cuda")
+
+    def step():
+        kv = vla.vla_prefix_encode(model, zt, kv_storage=store)
+        vla.vla_denoise_chunk(model, kv, xt, cfg.steps, out=out)
+        kv.close()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    kv, tp = vla.vla_prefix_encode(model, zt, kv_storage=store, timing=True)
+    _, td = vla.vla_denoise_chunk(model, kv, xt, cfg.steps, out=out, timing=True)
+    kv.close()
+    pf, ef = prefix_flops(cfg) * cfg.batch, expert_step_flops(cfg)
+    return {"value": cfg.batch * steps / el, "unit": "chunks/s", "steps": steps,
+            "workload": f"{cfg.name}: {cfg.batch} observations x {cfg.n_prefix} prefix tokens, "
+                        f"{cfg.batch * cfg.H} chunk rows, {cfg.steps} solver steps (this line's model weights)",
+            "prefix_ms": tp["prefix_ms"], "denoise_ms": td["denoise_ms"], "denoise_step_ms": td["step_ms"],
+            "prefix_mfma_frac": pf / (tp["prefix_ms"] * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+            "denoise_mfma_frac": ef / (td["step_ms"] * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+            "denoise_hbm_frac": expert_step_bytes(cfg) / (td["step_ms"] * 1e-3) / (PEAK_HBM_GBS * 1e9),
+            "denoise_bound": "mfma"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -310,6 +355,8 @@ def main():
 
     # ---- solver-step sweep (Eq. 3) and the two-stream pipelined rate: context, not the metric
     extras = {}
+    if args.config == 1 and args.attn == "cross" and not args.no_batched:
+        extras["batched16"] = batched_entry(vla, model, cfg)
     if not args.no_extras:
         extras["solver_sweep"] = solver_sweep(vla, model, zt, xt, kv_storage)
         extras["pipelined_two_stream"] = pipelined(vla, model, cfg, zt, xt, max(args.steps, 10))
@@ -325,7 +372,7 @@ def main():
         "metric": "action chunks/s at batch 1 (prefix+denoise), % of MFMA / HBM roofline",
         "value": value, "unit": "chunks/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": DTYPE[cfg.precision], "data": "synthetic",
         "config": {"workload": cfg.name, "attention": cfg.attn, "batch": cfg.batch, "prefix_tokens": cfg.n_prefix,
                    "prefix_layers": cfg.L_p, "d_prefix": cfg.d_p, "expert_layers": cfg.L_e, "d_expert": cfg.d_e,
                    "chunk": [cfg.H, cfg.d_a], "solver_steps": cfg.steps},
@@ -384,7 +431,18 @@ def cpu_baseline(cfg, w, betas, z0, x0, budget_s):
                       f"{steps_done} of {cfg.steps} solver steps run in float64 numpy, the rest extrapolated "
                       f"from the measured per-layer and per-step times",
             "seconds_measured": time.perf_counter() - t0,
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":
