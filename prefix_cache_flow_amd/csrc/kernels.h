@@ -107,12 +107,25 @@ hipError_t gemm_f32(const float* A, int lda, const float* W, int ldw, int M, int
 // Ternary W2A8: acc = a[M,K] q[N,K]^T in int32 on int8 MFMA, q in the library's
 // packed layout (see w2a8.hip); y = bf16(float(acc) * alpha[m] * beta[n]) into the
 // epilogue (epi.alpha / epi.beta must be set).  K % 128 == 0, N % 32 == 0.
+// epi.kind is EPI_STORE, EPI_RESID or EPI_GEGLU.  With `work` the K range may be
+// split over several workgroups per output tile (when the tiles alone leave CUs
+// idle): ws holds their int32 partial sums (w2a8_part_bytes), cnt one counter
+// per tile (w2a8_counters), zero before the first launch and left zero by
+// every launch.  Launches sharing one `work` must not overlap.
+struct W2A8Work {
+  int* ws = nullptr;
+  size_t ws_bytes = 0;
+  unsigned* cnt = nullptr;
+  int ncnt = 0;
+};
+size_t w2a8_part_bytes(int M, int N);
+int w2a8_counters(int M, int N);
 hipError_t gemm_w2a8(const int8_t* a, int lda, const uint32_t* qp, int M, int N, int K,
-                     const Epilogue& epi, hipStream_t s);
+                     const Epilogue& epi, hipStream_t s, const W2A8Work* work = nullptr);
 
 // Same with one scale beta for every output channel (epi.beta ignored).
 hipError_t gemm_w2a8_scalar(const int8_t* a, int lda, const uint32_t* qp, int M, int N, int K,
-                            const Epilogue& epi, float beta_scalar, hipStream_t s);
+                            const Epilogue& epi, float beta_scalar, hipStream_t s, const W2A8Work* work = nullptr);
 
 // The same on the vector ALU (v_dot4_i32_i8), bf16 STORE epilogue and/or raw
 // accumulators only; beta[n] from epi.beta when set, else beta_scalar.  K % 64 == 0.

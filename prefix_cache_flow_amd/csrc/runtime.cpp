@@ -727,6 +727,7 @@ struct WS {
   void* mlp;        // [rows][F_p]         (fp32 for the ternary prefix)
   int8_t* qa;       // ternary: int8 codes [rows][max(d_p, Hq hd, F_p)]
   float* alpha;     // ternary: [rows]
+  W2A8Work w2;      // ternary: K-split partial sums and per-tile counters (zeroed once, left zero)
   float* part;      // split-K partials
   // expert
   float* X;         // [erows][d_a]
@@ -814,6 +815,13 @@ static WS plan(const vla_model* m, int64_t rows, int64_t erows, int64_t kvrows, 
   if (m->w2a8) {
     w.qa = (int8_t*)take(rows * std::max<int64_t>(std::max<int64_t>(c.d_p, qw), c.F_p));
     w.alpha = (float*)take(rows * 4);
+    const int M = (int)rows, Ns[3] = {(int)qkvw, c.d_p, 2 * c.F_p};
+    for (int N : Ns) {
+      w.w2.ws_bytes = std::max(w.w2.ws_bytes, w2a8_part_bytes(M, N));
+      w.w2.ncnt = std::max(w.w2.ncnt, w2a8_counters(M, N));
+    }
+    w.w2.ws = (int*)take(w.w2.ws_bytes);
+    w.w2.cnt = (unsigned*)take((size_t)w.w2.ncnt * 4);
   }
   w.part = (float*)take((size_t)prefix_part_floats(c, rows) * 4);
   const int64_t qe = (int64_t)c.Hq_e * c.hd_e, qkve = (int64_t)(c.Hq_e + 2 * c.Hkv_e) * c.hd_e;
@@ -1020,19 +1028,19 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, const i
       const PrefixLayer& P = m->pl[l];
       Epilogue e = epi_store(w.qkv, qkvw, 0);
       e.alpha = w.alpha; e.beta = P.bqkv;
-      K_TRY(gemm_w2a8(w.qa, c.d_p, (const uint32_t*)P.wqkv, M, qkvw, c.d_p, e, s), "qkv");
+      K_TRY(gemm_w2a8(w.qa, c.d_p, (const uint32_t*)P.wqkv, M, qkvw, c.d_p, e, s, &w.w2), "qkv");
       K_TRY(attention_bf16(aa, s), "attention");
       K_TRY(quantize_rows((const float*)w.attn, qw, M, qw, w.qa, w.alpha, s), "quantize attn");
       Epilogue r;
       r.kind = EPI_RESID; r.resid = w.h; r.ldr = c.d_p; r.alpha = w.alpha; r.beta = P.bo;
-      K_TRY(gemm_w2a8(w.qa, qw, (const uint32_t*)P.wo, M, c.d_p, qw, r, s), "o proj");
+      K_TRY(gemm_w2a8(w.qa, qw, (const uint32_t*)P.wo, M, c.d_p, qw, r, s, &w.w2), "o proj");
       K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, P.w2, eps, nullptr, 0, 0, w.qa, w.alpha, s), "norm");
       Epilogue g;
       g.kind = EPI_GEGLU; g.out = w.mlp; g.ldo = c.F_p; g.out_f32 = 1; g.alpha = w.alpha; g.beta = P.bgu;
-      K_TRY(gemm_w2a8(w.qa, c.d_p, (const uint32_t*)P.wgu, M, 2 * c.F_p, c.d_p, g, s), "gate/up");
+      K_TRY(gemm_w2a8(w.qa, c.d_p, (const uint32_t*)P.wgu, M, 2 * c.F_p, c.d_p, g, s, &w.w2), "gate/up");
       K_TRY(quantize_rows((const float*)w.mlp, c.F_p, M, c.F_p, w.qa, w.alpha, s), "quantize mlp");
       r.beta = P.bd;
-      K_TRY(gemm_w2a8(w.qa, c.F_p, (const uint32_t*)P.wd, M, c.d_p, c.F_p, r, s), "down");
+      K_TRY(gemm_w2a8(w.qa, c.F_p, (const uint32_t*)P.wd, M, c.d_p, c.F_p, r, s, &w.w2), "down");
       if (l + 1 < c.L_p)
         K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, m->pl[l + 1].w1, eps, nullptr, 0, 0, w.qa, w.alpha, s),
               "norm");
@@ -1579,6 +1587,23 @@ extern "C" vla_status vla_quantize_rows_i8(const float* x, int32_t M, int32_t K,
   return VLA_OK;
 }
 
+// Partial sums and counters of one ternary GEMM's K splits, allocated for the
+// call (the counters cleared on the stream); freed with free_w2work.
+static bool alloc_w2work(int M, int N, W2A8Work& w, hipStream_t s) {
+  w.ws_bytes = w2a8_part_bytes(M, N);
+  w.ncnt = w2a8_counters(M, N);
+  if (lib_malloc((void**)&w.ws, w.ws_bytes) != hipSuccess || lib_malloc((void**)&w.cnt, (size_t)w.ncnt * 4) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return hipMemsetAsync(w.cnt, 0, (size_t)w.ncnt * 4, s) == hipSuccess;
+}
+static void free_w2work(W2A8Work& w) {
+  if (w.ws) (void)hipFree(w.ws);
+  if (w.cnt) (void)hipFree(w.cnt);
+  w = W2A8Work{};
+}
+
 extern "C" vla_status vla_w2a8_gemm(const int8_t* a, const float* alpha, const uint8_t* q_packed, float beta, int32_t M,
                                     int32_t N, int32_t K, int32_t* acc_out, uint16_t* y_bf16, void* stream) {
   if (!a || !alpha || !q_packed) return fail(VLA_ERR_INVALID_ARGUMENT, "NULL pointer");
@@ -1590,16 +1615,18 @@ extern "C" vla_status vla_w2a8_gemm(const int8_t* a, const float* alpha, const u
   hipStream_t s = (hipStream_t)stream;
   uint32_t* words = nullptr;
   int* flags = nullptr;
-  if (lib_malloc((void**)&words, (size_t)N * K / 4) != hipSuccess || lib_malloc((void**)&flags, 64) != hipSuccess) {
-    (void)hipGetLastError();
-    if (words) (void)hipFree(words);
-    return fail(VLA_ERR_OUT_OF_MEMORY, "staging");
-  }
+  W2A8Work work;
   auto done = [&](vla_status r) {
-    (void)hipFree(words);
-    (void)hipFree(flags);
+    if (words) (void)hipFree(words);
+    if (flags) (void)hipFree(flags);
+    free_w2work(work);
     return r;
   };
+  if (lib_malloc((void**)&words, (size_t)N * K / 4) != hipSuccess || lib_malloc((void**)&flags, 64) != hipSuccess) {
+    (void)hipGetLastError();
+    return done(fail(VLA_ERR_OUT_OF_MEMORY, "staging"));
+  }
+  if (!alloc_w2work(M, N, work, s)) return done(fail(VLA_ERR_OUT_OF_MEMORY, "partial sums"));
   if (hipMemsetAsync(flags, 0, 64, s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "memset"));
   if (ternary_repack(q_packed, N, K, words, flags, s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "repack"));
   int hf = 0;
@@ -1609,7 +1636,8 @@ extern "C" vla_status vla_w2a8_gemm(const int8_t* a, const float* alpha, const u
   Epilogue e = epi_store(y_bf16, N, 0);
   e.alpha = alpha;
   e.acc_out = acc_out;
-  if (gemm_w2a8_scalar(a, K, words, M, N, K, e, beta, s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "w2a8 launch"));
+  if (gemm_w2a8_scalar(a, K, words, M, N, K, e, beta, s, &work) != hipSuccess)
+    return done(fail(VLA_ERR_DEVICE, "w2a8 launch"));
   if (hipStreamSynchronize(s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "w2a8 sync"));
   return done(VLA_OK);
 }
@@ -1673,11 +1701,13 @@ extern "C" vla_status vla_w2a8_gemm_ex(const int8_t* a, const float* alpha, cons
   uint32_t* words = nullptr;
   int* flags = nullptr;
   float* bdev = nullptr;
+  W2A8Work work;
   hipEvent_t ev[2] = {nullptr, nullptr};
   auto done = [&](vla_status r) {
     if (words) (void)hipFree(words);
     if (flags) (void)hipFree(flags);
     if (bdev) (void)hipFree(bdev);
+    free_w2work(work);
     for (hipEvent_t e : ev)
       if (e) (void)hipEventDestroy(e);
     return r;
@@ -1687,6 +1717,7 @@ extern "C" vla_status vla_w2a8_gemm_ex(const int8_t* a, const float* alpha, cons
     (void)hipGetLastError();
     return done(fail(VLA_ERR_OUT_OF_MEMORY, "staging"));
   }
+  if (path == VLA_W2A8_MFMA && !alloc_w2work(M, N, work, s)) return done(fail(VLA_ERR_OUT_OF_MEMORY, "partial sums"));
   if (kernel_ms && (hipEventCreate(&ev[0]) != hipSuccess || hipEventCreate(&ev[1]) != hipSuccess))
     return done(fail(VLA_ERR_DEVICE, "events"));
   if (hipMemsetAsync(flags, 0, 64, s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "memset"));
@@ -1702,7 +1733,7 @@ extern "C" vla_status vla_w2a8_gemm_ex(const int8_t* a, const float* alpha, cons
   e.beta = bdev;
   e.acc_out = acc_out;
   if (kernel_ms && hipEventRecord(ev[0], s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "event"));
-  const hipError_t le = path == VLA_W2A8_MFMA ? gemm_w2a8(a, K, words, M, N, K, e, s)
+  const hipError_t le = path == VLA_W2A8_MFMA ? gemm_w2a8(a, K, words, M, N, K, e, s, &work)
                                                : gemm_w2a8_dot4(a, K, words, M, N, K, e, 0.f, s);
   if (le != hipSuccess) return done(fail(VLA_ERR_DEVICE, "w2a8 launch"));
   if (kernel_ms && hipEventRecord(ev[1], s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "event"));

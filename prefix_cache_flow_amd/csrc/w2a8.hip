@@ -11,11 +11,14 @@
 // (input 4j + i in bits 2i of byte j) is converted to this order once, when the
 // model is created.
 //
-// Tiles: 64 activation rows x 128 output channels x 128 inputs per slice,
-// four waves of 64 x 32 on the 32x32x32 int8 MFMA (a wave's unpacked weight
-// fragment serves both 32-row halves).  The activation slice is
-// staged in LDS as int8; the weight slice is staged *packed* (2 bits per weight,
-// a quarter of the int8 bytes) and unpacked in registers right before the MFMA.
+// Tiles: 64 activation rows x 128 output channels per workgroup of eight
+// waves (two per SIMD, four with the two workgroups a CU holds), 256-input K
+// slices (128 when 256 does not divide K), 32x32x32 int8 MFMA.  The activation
+// slice is staged in LDS as int8; the weight slice is staged *packed* (2 bits
+// per weight, a quarter of the int8 bytes) and unpacked in registers right
+// before the MFMA.  When the output tiles alone would leave CUs idle, the K
+// range of a tile is split over up to three workgroups whose int32 partial
+// sums meet in a workspace (exact in any order).
 #include <mutex>
 
 #include "common.h"
@@ -30,6 +33,9 @@ struct W2A8P {
   int M, N, K, nM, nN;
   Epilogue epi;
   float beta_scalar;
+  int S = 1;               // K splits per output tile (1: no partial sums)
+  int* ws = nullptr;       // S > 1: partial sums, kW2A8PartInts per (tile, split)
+  unsigned* cnt = nullptr; // S > 1: per-tile arrival counters, zero between launches
 };
 
 __device__ __forceinline__ i32x4_t unpack16(uint32_t w) {
@@ -39,145 +45,363 @@ __device__ __forceinline__ i32x4_t unpack16(uint32_t w) {
   return r;
 }
 
-__device__ __forceinline__ float w2a8_scale(const W2A8P& p, int m, int n, int acc) {
-  const float b = p.epi.beta ? p.epi.beta[n] : p.beta_scalar;
-  const float s = p.epi.alpha[m] * b;
-  return bf2f(f2bf((float)acc * s));
-}
+namespace {
+constexpr int kBM = 64, kBN = 128;       // output tile
+constexpr int kPartInts = kBM * kBN;     // one tile's partial sums
+constexpr int kSC1 = 16;                 // cache policy bits of device-scope coherent loads and stores
+}  // namespace
 
-template <int BK>
-__global__ __launch_bounds__(256) void k_gemm_w2a8(W2A8P p) {
-  constexpr int BM = 64, BN = 128, LDA = BK + 16, LDW = BK / 16 + 1;
-  constexpr int AV = BM * BK / 16 / 256;  // 16-byte activation vectors per thread and slice
-  constexpr int WV = BN * BK / 64 / 256;  // 4-word weight vectors per thread and slice
-  __shared__ __attribute__((aligned(16))) int8_t sA[2][BM * LDA];
-  __shared__ uint32_t sW[2][BN * LDW];
-  const int nt = p.nM * p.nN, L = blockIdx.x;
-  const int tile = (nt % 8 == 0) ? (L % 8) * (nt / 8) + L / 8 : L;
-  const int tm = tile % p.nM, tn = tile / p.nM;
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int KW = p.K / 16;  // words per weight row
-
-  // Two register sets, each filled two slices before its trip to LDS, so a
-  // slice's global loads have two slices of work to land behind.
-  const int ns = p.K / BK;
-  struct Regs { u32x4_t a[AV], w[WV]; };
-  constexpr int AR = BK / 16, WR = BK / 64;  // vectors per activation row, per weight row
-  auto gload = [&](Regs& g, int sl) {
-    const int k0 = min(sl, ns - 1) * BK;  // past the end: the last slice again (never used)
-#pragma unroll
-    for (int i = 0; i < AV; ++i) {
-      const int v = tid + i * 256, r = v / AR, c = (v % AR) * 16;
-      // rows past the end are clamped to valid ones; their results are never stored
-      g.a[i] = *(const u32x4_t*)(p.a + (long)min(m0 + r, p.M - 1) * p.lda + k0 + c);
-    }
-#pragma unroll
-    for (int i = 0; i < WV; ++i) {
-      const int v = tid + i * 256, r = v / WR, c = (v % WR) * 4;
-      g.w[i] = *(const u32x4_t*)(p.q + (long)min(n0 + r, p.N - 1) * KW + k0 / 16 + c);
-    }
-  };
-  auto sstore = [&](const Regs& g, int buf) {
-#pragma unroll
-    for (int i = 0; i < AV; ++i) {
-      const int v = tid + i * 256;
-      *(u32x4_t*)&sA[buf][(v / AR) * LDA + (v % AR) * 16] = g.a[i];
-    }
-#pragma unroll
-    for (int i = 0; i < WV; ++i) {
-      const int v = tid + i * 256, r = v / WR, c = (v % WR) * 4;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) sW[buf][r * LDW + c + t] = g.w[i][t];
-    }
-  };
-
-  i32x16_t acc[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[j][e] = 0;
-  // wave w owns output channels 32 w .. 32 w + 31 for all 64 rows: each
-  // weight word it unpacks feeds two MFMAs (the two 32-row halves)
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      const uint32_t w = sW[buf][(wid * 32 + (lane & 31)) * LDW + kk * 2 + (lane >> 5)];
-      const i32x4_t wf = unpack16(w);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const i32x4_t af = __builtin_bit_cast(
-            i32x4_t, *(const u32x4_t*)&sA[buf][(i * 32 + (lane & 31)) * LDA + kk * 32 + (lane >> 5) * 16]);
-        acc[i] = mfma32x32x32_i8(af, wf, acc[i]);
-      }
-    }
-  };
-
-  Regs r0, r1;
-  gload(r0, 0);
-  gload(r1, 1);
-  sstore(r0, 0);
-  __syncthreads();
-  gload(r0, 2);
-  // entering a pair at slice sl: slice sl in LDS buffer 0, sl + 1 in r1, sl + 2 in r0
-  int sl = 0;
-  for (; sl + 2 <= ns; sl += 2) {
-    compute(0);
-    sstore(r1, 1);
-    __syncthreads();
-    gload(r1, sl + 3);
-    compute(1);
-    sstore(r0, 0);
-    __syncthreads();
-    gload(r0, sl + 4);
-  }
-  if (sl < ns) compute(0);  // an odd slice count ends with one more, already in buffer 0
-
+// Epilogue of one wave: row half `own` (rows m0 + 32 own + mfma32_row(q, lane))
+// of channel half c, both 32-channel groups g (channels n0 + 64 c + 32 g +
+// lane % 32).  The kind, the int32 copy and the output type are template
+// parameters, so each kernel carries one short straight-line store path (these
+// kernels start with a cold instruction cache), and every load (residual
+// values) is issued before the first store: loads and stores retire through one
+// counter here, so a load placed after a store would wait for that store's
+// round trip too.
+template <int KIND, bool ACC, bool F32>
+__device__ __forceinline__ void w2a8_epilogue(const W2A8P& p, const i32x16_t (&fin)[2], int own, int c, int lane,
+                                              int m0, int n0, const float* s_al, const float* s_be) {
   const Epilogue& e = p.epi;
-  const int n = n0 + wid * 32 + (lane & 31);
+  const int mb = m0 + own * 32, nb = n0 + c * 64 + (lane & 31);
+  float al[16], be[2], rv[2][16];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int q = 0; q < 16; ++q) al[q] = s_al[own * 32 + mfma32_row(q, lane)];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + i * 32 + mfma32_row(r, lane);
+  for (int g = 0; g < 2; ++g) be[g] = s_be[c * 64 + g * 32 + (lane & 31)];
+  if (KIND == EPI_RESID) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = mb + mfma32_row(q, lane), n = nb + g * 32;
+        rv[g][q] = (m < p.M && n < p.N) ? e.resid[(long)m * e.ldr + n] : 0.f;
+      }
+  }
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int n = nb + g * 32;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int m = mb + mfma32_row(q, lane);
       const bool ok = m < p.M && n < p.N;
-      const int accv = acc[i][r];
-      if (e.acc_out && ok) e.acc_out[(long)m * p.N + n] = accv;
-      const float y = ok ? w2a8_scale(p, m, n, accv) : 0.f;
-      if (e.kind == EPI_GEGLU) {
+      if (ACC && ok) e.acc_out[(long)m * p.N + n] = fin[g][q];
+      const float y = ok ? bf2f(f2bf((float)fin[g][q] * (al[q] * be[g]))) : 0.f;
+      if (KIND == EPI_GEGLU) {
         const float other = __shfl_xor(y, 16, 64);
         if (!(lane & 16) && ok) {
           const float v = gelu_erf(y) * other;
-          const long i = (long)m * e.ldo + (n >> 5) * 16 + (lane & 15);
-          if (e.out_f32) ((float*)e.out)[i] = v; else ((bf16_t*)e.out)[i] = f2bf(v);
+          const long o = (long)m * e.ldo + (n >> 5) * 16 + (lane & 15);
+          if (F32) ((float*)e.out)[o] = v; else ((bf16_t*)e.out)[o] = f2bf(v);
         }
-      } else if (ok) {
-        if (e.kind == EPI_STORE && e.out) {
-          const long i = (long)m * e.ldo + n;
-          if (e.out_f32) ((float*)e.out)[i] = y; else ((bf16_t*)e.out)[i] = f2bf(y);
-        } else if (e.kind == EPI_RESID) {
-          e.resid[(long)m * e.ldr + n] += y;
-        }
+      } else if (KIND == EPI_RESID) {
+        if (ok) e.resid[(long)m * e.ldr + n] = rv[g][q] + y;
+      } else if (ok && e.out) {
+        const long o = (long)m * e.ldo + n;
+        if (F32) ((float*)e.out)[o] = y; else ((bf16_t*)e.out)[o] = f2bf(y);
       }
     }
   }
 }
 
+// One 64 x 128 output tile (or one K split of it) per workgroup of eight
+// waves, two per SIMD.  Wave (c, kq) = (wid & 1, wid >> 1) accumulates the 64
+// rows x 64 channels of channel half c over the k quarter kq of every slice:
+// both 32-row halves against both 32-channel groups, so each activation
+// fragment and each unpacked weight word feeds two MFMAs and the wave runs
+// four independent MFMA chains.  The four k quarters are summed through LDS at
+// the end (int32: exact in any order).
+template <int BK, int KIND, bool ACC>
+__global__ __launch_bounds__(512, 4) void k_gemm_w2a8(W2A8P p) {
+  constexpr int BM = kBM, BN = kBN, LDA = BK + 16, LDW = BK / 16 + 1;
+  constexpr int KPW = BK / 32 / 4;                // MFMA k-steps per wave and slice (a quarter)
+  constexpr int AV = BM * BK / 16 / 512;          // 16-byte activation vectors per thread and slice
+  constexpr int WW = BN * BK / 16 / 512;          // weight words per thread and slice (4 or 2)
+  constexpr int STAGE = 2 * BM * LDA + 2 * BN * LDW * 4;
+  constexpr int RED = 4 * 64 * 64 * 4;            // four wave-sized slots of 64 ints per lane
+  constexpr int LDS = STAGE > RED ? STAGE : RED;
+  static_assert(AV >= 1 && (WW == 4 || WW == 2) && KPW >= 1, "slice shape");
+  typedef __attribute__((__vector_size__(WW * sizeof(uint32_t)))) uint32_t wvec_t;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS];
+  __shared__ float s_al[BM], s_be[BN];
+  __shared__ unsigned s_last;
+  int8_t(*sA)[BM * LDA] = (int8_t(*)[BM * LDA])lds;
+  uint32_t(*sW)[BN * LDW] = (uint32_t(*)[BN * LDW])(lds + 2 * BM * LDA);
+  int* red = (int*)lds;
+
+  // work item -> (tile, split); consecutive items share an XCD (linear id mod 8),
+  // so the splits of a tile and the row tiles of one weight column meet in one L2
+  const int W = p.nM * p.nN * p.S, L = blockIdx.x;
+  const int wk = (W % 8 == 0) ? (L % 8) * (W / 8) + L / 8 : L;
+  const int sp = wk % p.S, tile = wk / p.S;
+  const int tm = tile % p.nM, tn = tile / p.nM;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int c = wid & 1, kq = wid >> 1;  // channel half, k quarter of every slice
+  const int KW = p.K / 16;               // words per weight row
+  const int ns = p.K / BK, s_lo = sp * ns / p.S, nsl = (sp + 1) * ns / p.S - s_lo;
+  const Epilogue& e = p.epi;
+  if (tid < BM) s_al[tid] = e.alpha[min(m0 + tid, p.M - 1)];
+  else if (tid < BM + BN) s_be[tid - BM] = e.beta ? e.beta[min(n0 + tid - BM, p.N - 1)] : p.beta_scalar;
+
+  struct Regs { u32x4_t a[AV]; wvec_t w; };
+  constexpr int AR = BK / 16, WR = BK / 16 / WW;  // vectors per activation row, per weight row
+  auto gload = [&](Regs& g, int i) {
+    const int k0 = (s_lo + min(i, nsl - 1)) * BK;  // past the end: the last slice again (never used)
+#pragma unroll
+    for (int v0 = 0; v0 < AV; ++v0) {
+      const int v = tid + v0 * 512, r = v / AR, cc = (v % AR) * 16;
+      // rows past the end are clamped to valid ones; their results are never stored
+      g.a[v0] = *(const u32x4_t*)(p.a + (long)min(m0 + r, p.M - 1) * p.lda + k0 + cc);
+    }
+    const int r = tid / WR, cc = (tid % WR) * WW;
+    g.w = *(const wvec_t*)(p.q + (long)min(n0 + r, p.N - 1) * KW + k0 / 16 + cc);
+  };
+  auto sstore = [&](const Regs& g, int buf) {
+#pragma unroll
+    for (int v0 = 0; v0 < AV; ++v0) {
+      const int v = tid + v0 * 512;
+      *(u32x4_t*)&sA[buf][(v / AR) * LDA + (v % AR) * 16] = g.a[v0];
+    }
+    const int r = tid / WR, cc = (tid % WR) * WW;
+#pragma unroll
+    for (int t = 0; t < WW; ++t) sW[buf][r * LDW + cc + t] = g.w[t];
+  };
+
+  i32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][g][q] = 0;
+  auto compute = [&](int buf) {
+    i32x4_t af[KPW][2];
+    uint32_t wq[KPW][2];
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) {
+      const int kk = kq * KPW + j;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[j][i] = __builtin_bit_cast(
+            i32x4_t, *(const u32x4_t*)&sA[buf][(i * 32 + (lane & 31)) * LDA + kk * 32 + (lane >> 5) * 16]);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) wq[j][g] = sW[buf][(c * 64 + g * 32 + (lane & 31)) * LDW + kk * 2 + (lane >> 5)];
+    }
+#pragma unroll
+    for (int j = 0; j < KPW; ++j)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const i32x4_t wf = unpack16(wq[j][g]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[i][g] = mfma32x32x32_i8(af[j][i], wf, acc[i][g]);
+      }
+  };
+
+  // Slice t lives in register set t % NR until it is stored to LDS buffer
+  // t % 2 (NR = 3 register sets for 128-input slices, 2 for 256-input ones,
+  // which keeps four waves per SIMD within the register file).  Entering step
+  // t: slice t in LDS, slices t + 1 .. t + NR in flight.  The scheduling
+  // barriers keep the compiler from moving a load or a store across a step
+  // boundary: in program order the slice stored at step t is the oldest in
+  // flight, so its wait leaves the others outstanding.  Groups of NR steps keep
+  // the register-set index static; the LDS buffer index alternates at run
+  // time, and steps past the last slice compute nothing.
+  constexpr int NR = BK == 256 ? 2 : 3;
+  Regs rs[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) gload(rs[i], i);
+  sstore(rs[0], 0);
+  __syncthreads();
+  gload(rs[0], NR);
+#define W2A8_STEP(J)                                  \
+  if ((J) < NR) {                                     \
+    const int t = t0 + (J);                           \
+    if (t < nsl) compute(t & 1);                      \
+    __builtin_amdgcn_sched_barrier(0);                \
+    sstore(rs[((J) + 1) % NR], (t + 1) & 1);          \
+    __syncthreads();                                  \
+    gload(rs[((J) + 1) % NR], t + NR + 1);            \
+    __builtin_amdgcn_sched_barrier(0);                \
+  }
+  for (int t0 = 0; t0 < nsl; t0 += NR) {
+    W2A8_STEP(0) W2A8_STEP(1) W2A8_STEP(2)
+  }
+#undef W2A8_STEP
+
+  // Sum of the four k quarters.  A slot holds a wave's 64 ints per lane as 16
+  // chunks of four, chunk h = (i * 2 + g) * 4 + q / 4 of lane l at ints
+  // (h * 64 + l) * 4 .. + 3 (16-byte accesses).  Level 1: quarters 2, 3 hand
+  // everything to quarters 0, 1.  Level 2: quarter 0 keeps row half 0 and
+  // quarter 1 row half 1, each handing over the other.
+  auto chunk = [&](int* slot, int i, int g, int h4) -> i32x4_t* {
+    return (i32x4_t*)(slot + (((i * 2 + g) * 4 + h4) * 64 + lane) * 4);
+  };
+  auto part = [](const i32x16_t& v, int h4) { return i32x4_t{v[4 * h4], v[4 * h4 + 1], v[4 * h4 + 2], v[4 * h4 + 3]}; };
+  __syncthreads();  // the staging buffers are free from here on
+  if (kq >= 2) {
+    int* o = red + (c * 2 + kq - 2) * 64 * 64;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int h4 = 0; h4 < 4; ++h4) *chunk(o, i, g, h4) = part(acc[i][g], h4);
+  }
+  __syncthreads();
+  if (kq < 2) {
+    int* o = red + (c * 2 + kq) * 64 * 64;
+    i32x4_t in[2][2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int h4 = 0; h4 < 4; ++h4) in[i][g][h4] = *chunk(o, i, g, h4);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][g][q] += in[i][g][q / 4][q % 4];
+  }
+  __syncthreads();
+  // (the row half a wave keeps is wave-uniform; both branches index statically)
+  const int own = kq & 1;
+  i32x16_t fin[2], give[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    if (own == 0) { fin[g] = acc[0][g]; give[g] = acc[1][g]; }
+    else { fin[g] = acc[1][g]; give[g] = acc[0][g]; }
+  }
+  if (kq < 2) {
+    int* o = red + (c * 2 + kq) * 64 * 64;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int h4 = 0; h4 < 4; ++h4) *chunk(o, 1 - own, g, h4) = part(give[g], h4);
+  }
+  __syncthreads();
+  if (kq < 2) {
+    int* o = red + (c * 2 + (1 - kq)) * 64 * 64;
+    i32x4_t in[2][4];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int h4 = 0; h4 < 4; ++h4) in[g][h4] = *chunk(o, own, g, h4);
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) fin[g][q] += in[g][q / 4][q % 4];
+  }
+
+  if (p.S > 1) {
+    // K split: every split stores its sums with device-scope coherent stores
+    // (the XCDs' L2s are not coherent with one another), waits for their
+    // acknowledgement, then counts itself in; the last to arrive adds the other
+    // splits' sums (loaded the same way), resets the counter for the next
+    // launch and runs the epilogue.  No workgroup ever waits on another.
+    const uint32_t bytes = (uint32_t)((size_t)W * kPartInts * 4);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(p.ws, (short)0, (int)bytes, 0x00020000);
+    auto off = [&](int split, int g, int h4) {
+      return (uint32_t)(((size_t)(tile * p.S + split) * kPartInts + (((kq * 2 + c) * 2 + g) * 4 + h4) * 256 + lane * 4) * 4);
+    };
+    if (kq < 2) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int h4 = 0; h4 < 4; ++h4)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, part(fin[g], h4)), r, off(sp, g, h4), 0, kSC1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned old = __hip_atomic_fetch_add(p.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = old + 1 == (unsigned)p.S;
+      if (s_last) __hip_atomic_store(p.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last || kq >= 2) return;
+    for (int o = 0; o < p.S; ++o) {
+      if (o == sp) continue;
+      u32x4_t in[2][4];
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int h4 = 0; h4 < 4; ++h4) in[g][h4] = __builtin_amdgcn_raw_buffer_load_b128(r, off(o, g, h4), 0, kSC1);
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) fin[g][q] += (int)in[g][q / 4][q % 4];
+    }
+  }
+  if (kq >= 2) return;
+  if (e.out_f32) w2a8_epilogue<KIND, ACC, true>(p, fin, own, c, lane, m0, n0, s_al, s_be);
+  else w2a8_epilogue<KIND, ACC, false>(p, fin, own, c, lane, m0, n0, s_al, s_be);
+}
+
+size_t w2a8_part_bytes(int M, int N) {
+  const size_t tiles = (size_t)((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  return tiles * 3 * kPartInts * 4;
+}
+
+int w2a8_counters(int M, int N) { return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN); }
+
+namespace {
+int cu_count() {
+  static int cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+}  // namespace
+
 hipError_t gemm_w2a8_scalar(const int8_t* a, int lda, const uint32_t* qp, int M, int N, int K, const Epilogue& epi,
-                            float beta_scalar, hipStream_t s) {
+                            float beta_scalar, hipStream_t s, const W2A8Work* work) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K % 128 || N % 32 || !epi.alpha) return hipErrorInvalidValue;
-  W2A8P p{a, lda, qp, M, N, K, (M + 63) / 64, (N + 127) / 128, epi, beta_scalar};
+  if (epi.kind != EPI_STORE && epi.kind != EPI_RESID && epi.kind != EPI_GEGLU) return hipErrorInvalidValue;
+  W2A8P p{a, lda, qp, M, N, K, (M + kBM - 1) / kBM, (N + kBN - 1) / kBN, epi, beta_scalar};
   // 256-wide K slices when they divide K: a weight row's slice is then 64
-  // contiguous bytes and the per-slice overhead is spread over twice the MFMAs
-  if (K % 256 == 0) hipLaunchKernelGGL(k_gemm_w2a8<256>, dim3(p.nM * p.nN), dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(k_gemm_w2a8<128>, dim3(p.nM * p.nN), dim3(256), 0, s, p);
+  // contiguous bytes and each wave gets two k-steps per slice
+  const bool wide = K % 256 == 0;
+  // K splits while the tiles alone leave CUs idle: at most three, at least four
+  // slices each, and only with room for the partial sums and counters
+  const int tiles = p.nM * p.nN, ns = K / (wide ? 256 : 128);
+  int S = 1;
+  if (work && work->ws && work->cnt && work->ncnt >= tiles) {
+    S = std::min(3, std::max(1, cu_count() / tiles));
+    while (S > 1 && (ns / S < 4 || (size_t)tiles * S * kPartInts * 4 > work->ws_bytes)) --S;
+    if (S > 1) { p.S = S; p.ws = work->ws; p.cnt = work->cnt; }
+  }
+  const dim3 grid(tiles * S), block(512);
+  const bool acc = epi.acc_out != nullptr;
+#define W2A8_LAUNCH(BK, KIND)                                                                   \
+  do {                                                                                          \
+    if (acc) hipLaunchKernelGGL((k_gemm_w2a8<BK, KIND, true>), grid, block, 0, s, p);           \
+    else hipLaunchKernelGGL((k_gemm_w2a8<BK, KIND, false>), grid, block, 0, s, p);              \
+  } while (0)
+#define W2A8_KINDS(BK)                                                                          \
+  do {                                                                                          \
+    if (epi.kind == EPI_RESID) W2A8_LAUNCH(BK, EPI_RESID);                                      \
+    else if (epi.kind == EPI_GEGLU) W2A8_LAUNCH(BK, EPI_GEGLU);                                 \
+    else W2A8_LAUNCH(BK, EPI_STORE);                                                            \
+  } while (0)
+  if (wide) W2A8_KINDS(256);
+  else W2A8_KINDS(128);
+#undef W2A8_KINDS
+#undef W2A8_LAUNCH
   return hipGetLastError();
 }
 
 hipError_t gemm_w2a8(const int8_t* a, int lda, const uint32_t* qp, int M, int N, int K, const Epilogue& epi,
-                     hipStream_t s) {
-  return gemm_w2a8_scalar(a, lda, qp, M, N, K, epi, 0.f, s);
+                     hipStream_t s, const W2A8Work* work) {
+  return gemm_w2a8_scalar(a, lda, qp, M, N, K, epi, 0.f, s, work);
 }
 
 // The same contraction on the vector ALU with v_dot4_i32_i8 (four int8
@@ -232,7 +456,13 @@ __global__ __launch_bounds__(256) void k_gemm_w2a8_dot4(W2A8P p) {
     }
     __syncthreads();
   }
+  // scales first, then stores (a load after a store would wait for the store)
   const Epilogue& e = p.epi;
+  float al[4], bt[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) al[r] = e.alpha[min(m0 + rg * 4 + r, p.M - 1)];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bt[j] = e.beta ? e.beta[min(n0 + cg * 4 + j, p.N - 1)] : p.beta_scalar;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = m0 + rg * 4 + r;
@@ -242,7 +472,7 @@ __global__ __launch_bounds__(256) void k_gemm_w2a8_dot4(W2A8P p) {
       const int n = n0 + cg * 4 + j;
       if (n >= p.N) continue;
       if (e.acc_out) e.acc_out[(long)m * p.N + n] = acc[r][j];
-      if (e.out) ((bf16_t*)e.out)[(long)m * e.ldo + n] = f2bf(w2a8_scale(p, m, n, acc[r][j]));
+      if (e.out) ((bf16_t*)e.out)[(long)m * e.ldo + n] = f2bf((float)acc[r][j] * (al[r] * bt[j]));
     }
   }
 }

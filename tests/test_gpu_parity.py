@@ -233,7 +233,7 @@ def test_quantizer_bit_exact(M, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(320, 7680, 2560), (320, 2560, 2560), (320, 13824, 2560), (320, 2560, 6912),
-                                   (37, 96, 384), (1, 32, 128)])
+                                   (320, 7680, 1152), (37, 96, 384), (1, 32, 128)])
 def test_w2a8_gemm_bit_exact(M, N, K):
     rng = np.random.default_rng(N + K)
     x = _x_rows(M, K, K)
