@@ -8,9 +8,10 @@ Workload: the single-camera bf16 policy (288 prefix tokens, 18 + 18 layers,
 inputs, all resident in HBM before timing starts.
 
 Prints one JSON line: action chunks/s, per-phase latency, the roofline of the
-dominant kernel (timed live with HIP events around its launches inside the
-timed region) and the CPU oracle timed on a bounded sample of the same
-workload on the host cores.
+kernel with the largest share of GPU time (its launches timed with HIP events
+in a separate probe pass after the timed region, so the timing does not
+perturb the measured steps), a roofline entry per phase, and the CPU oracle
+timed on a bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -30,11 +31,12 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_INT8_TOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes per launch of the prefix gate/up kernel from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE),
-# scaled by what the same counters read for a plain copy (profiles/hbm_bytes_prefix_gateup_single_camera_bf16.md).
-# Valid only for the kernel instance named here; None once that kernel changes until it is measured again.
-GATEUP_KERNEL = "k_gemm_af8<2, false>"
-GATEUP_TRAFFIC_BYTES = 153553225
+# HBM bytes from rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter
+# reads for a plain copy of known size; the summaries are under profiles/.  Valid for the single-camera bf16
+# workload and the kernels as they were measured; None where no measurement stands.
+ATTN_KERNEL = "k_attn_chunk<256>"
+ATTN_TRAFFIC_BYTES_PER_LAUNCH = None   # mean over the launch mix of one policy step
+DENOISE_TRAFFIC_BYTES_PER_STEP = None  # every kernel of one solver step (the denoise graph's nodes)
 
 
 def parse():
@@ -50,6 +52,12 @@ def parse():
     p.add_argument("--no-extras", action="store_true",
                    help="skip the solver-step sweep, the two-stream pipelined run and the ternary ablation")
     p.add_argument("--no-batched", action="store_true", help="skip the batched-workload entry")
+    p.add_argument("--no-roofline", action="store_true",
+                   help="skip the probe pass of the dominant kernel (for counter passes that must see only the "
+                        "policy steps themselves)")
+    p.add_argument("--pipelined", action="store_true",
+                   help="also time the two-stream schedule (prefix of observation k+1 beside the solver of k); "
+                        "it is slower than the serial one on this GPU and is left out of the default line")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB mebibytes (reference for the HBM byte counters) and exit")
     return p.parse_args()
@@ -209,6 +217,106 @@ def pipelined(vla, model, cfg, zt, xt, n, warmup=2):
 DTYPE = {"f32": "f32", "bf16": "bf16", "w2a8": "int8 x ternary (int32 accumulation) prefix, bf16 expert"}
 
 
+def attn_launch_bytes(c):
+    """Algorithmic bytes of one launch of the chunk attention kernel, per class: queries and keys / values
+    read once, the output written once (bf16).  Prefix: the encode's bidirectional attention (cross form);
+    self: the expert's attention over the chunk (joint: plus prefix layer e's keys and values); cross: the
+    expert's attention into the cached block of one layer."""
+    N, M = c.batch * c.n_prefix, c.batch * c.H
+    qp, kvp = c.Hq * c.hd, c.Hkv * c.hd
+    qe, kve = c.Hq_e * c.hd_e, c.Hkv_e * c.hd_e
+    joint_kv = 2 * N * kve if c.attn == "joint" else 0
+    return {"prefix": 2 * (2 * N * qp + 2 * N * kvp),
+            "self": 2 * (2 * M * qe + 2 * M * kve + joint_kv),
+            "cross": 2 * (2 * M * qe + 2 * N * kve)}
+
+
+PROBE_REPEAT = 20
+
+
+def probe_mean_ms(vla, model, kind, run):
+    """Mean device time of one launch of a kernel class during run(): each launch of the class is issued
+    PROBE_REPEAT times back to back between two HIP events, so the events' own cost is spread thin (graphs
+    off for the run: a probe sees only launches outside a captured graph; the run's results are discarded)."""
+    import torch
+    prev = os.environ.get("VLA_NO_GRAPH")
+    os.environ["VLA_NO_GRAPH"] = "1"
+    try:
+        probe = vla.Probe(model, kind, repeat=PROBE_REPEAT)
+        run()
+        torch.cuda.synchronize()
+        ms, n = probe.collect()
+    finally:
+        if prev is None:
+            os.environ.pop("VLA_NO_GRAPH", None)
+        else:
+            os.environ["VLA_NO_GRAPH"] = prev
+    return (ms / n if n else None), n
+
+
+def dominant_kernel_roofline(vla, model, cfg, zt, xt, out, kv_storage):
+    """Roofline of the kernel with the largest share of GPU time in the committed traces: the chunk
+    attention kernel for the bf16 workloads (prefix attention in the encode, self and cross attention in
+    every solver step), the int8 ternary GEMM for the ternary one.  Achieved = algorithmic bytes (or
+    operations) of one policy step's launches of that kernel over their summed mean durations, the
+    durations probed per class after the timed region."""
+    L_p, T, L_e = cfg.L_p, cfg.steps, cfg.L_e
+
+    def encode():
+        kv = vla.vla_prefix_encode(model, zt, kv_storage=kv_storage)
+        kv.close()
+
+    def denoise():
+        kv = vla.vla_prefix_encode(model, zt, kv_storage=kv_storage)
+        vla.vla_denoise_chunk(model, kv, xt, cfg.steps, out=out)
+        kv.close()
+
+    if cfg.precision == "w2a8":
+        N = cfg.batch * cfg.n_prefix
+        qw, qkvw = cfg.Hq * cfg.hd, (cfg.Hq + 2 * cfg.Hkv) * cfg.hd
+        shapes = {vla.PROBE_PREFIX_QKV: (qkvw, cfg.d_p), vla.PROBE_PREFIX_O: (cfg.d_p, qw),
+                  vla.PROBE_PREFIX_GATEUP: (2 * cfg.F_p, cfg.d_p), vla.PROBE_PREFIX_DOWN: (cfg.d_p, cfg.F_p)}
+        ops = t = 0.0
+        per = {}
+        for kind, (n_out, k_in) in shapes.items():
+            ms, n = probe_mean_ms(vla, model, kind, encode)
+            if ms is None:
+                return None
+            o = 2.0 * N * n_out * k_in
+            per[f"{n_out}x{k_in}"] = {"us": ms * 1e3, "tops": o / (ms * 1e-3) / 1e12}
+            ops += L_p * o
+            t += L_p * ms
+        tops = ops / (t * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": tops, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                "frac": tops / PEAK_INT8_TOPS, "traffic": None, "kernel": "k_gemm_w2a8 (int8 x ternary prefix GEMMs)",
+                "avg_launch_us": t * 1e3 / (4 * L_p), "launches_per_step": 4 * L_p, "ops_per_step": ops,
+                "per_shape": per, "timing": f"HIP events around {PROBE_REPEAT} back-to-back repeats of each launch, separate probe pass after the timed region, graphs off"}
+    if cfg.precision != "bf16":
+        return None
+    b = attn_launch_bytes(cfg)
+    classes = [("prefix", vla.PROBE_PREFIX_ATTN, encode, L_p), ("self", vla.PROBE_EXPERT_SELF_ATTN, denoise, T * L_e)]
+    if cfg.attn == "cross":
+        classes.append(("cross", vla.PROBE_EXPERT_CROSS_ATTN, denoise, T * L_e))
+    tot_b = tot_t = 0.0
+    launches = 0
+    per = {}
+    for name, kind, run, count in classes:
+        ms, n = probe_mean_ms(vla, model, kind, run)
+        if ms is None:
+            return None
+        per[name] = {"us": ms * 1e3, "bytes": b[name], "gbs": b[name] / (ms * 1e-3) / 1e9, "launches_per_step": count}
+        tot_b += count * b[name]
+        tot_t += count * ms
+        launches += count
+    gbs = tot_b / (tot_t * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+            "traffic": ATTN_TRAFFIC_BYTES_PER_LAUNCH if (cfg.name == "single_camera_bf16") else None,
+            "kernel": ATTN_KERNEL + " (chunk attention: prefix, expert self and cross)",
+            "avg_launch_us": tot_t * 1e3 / launches, "bytes_per_launch": tot_b / launches,
+            "launches_per_step": launches, "per_class": per,
+            "timing": f"HIP events around {PROBE_REPEAT} back-to-back repeats of each launch, separate probe pass after the timed region, graphs off"}
+
+
 def batched_entry(vla, model, cfg1, steps=3, warmup=1):
     """The batched workload (16 observations of 512 prefix tokens, 800 chunk rows, 10 solver steps): the
     same model shapes as the single-camera workload, so the line's own model times it on its own seeded
@@ -299,14 +407,12 @@ def main():
     print(f"# warmup done at {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     # ---- timed region: K whole steps
-    probe = vla.Probe(model, vla.PROBE_PREFIX_GATEUP)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    probe_ms, probe_launches = probe.collect()
     ms_per_step = elapsed * 1e3 / args.steps
     value = cfg.batch * args.steps / elapsed
 
@@ -323,35 +429,23 @@ def main():
               "denoise_step_ms": float(np.median(stp_ms))}
     pf = prefix_flops(cfg) * cfg.batch
     sb = expert_step_bytes(cfg)
-    phases["prefix_mfma_frac"] = pf / (phases["prefix_ms"] * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
+    prefix_peak = PEAK_INT8_TOPS if cfg.precision == "w2a8" else PEAK_BF16_TFLOPS
+    phases["prefix_mfma_frac"] = pf / (phases["prefix_ms"] * 1e-3) / (prefix_peak * 1e12)
     phases["denoise_hbm_frac"] = sb / (phases["denoise_step_ms"] * 1e-3) / (PEAK_HBM_GBS * 1e9)
     phases["denoise_mfma_frac"] = expert_step_flops(cfg) / (phases["denoise_step_ms"] * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
 
-    # ---- roofline of the dominant kernel: prefix gate/up GEMM (GeGLU epilogue).
-    # Its ceiling is whichever of the MFMA peak and the HBM peak allows less:
-    # at 288 rows it moves 144.8 MB (bf16 weights, activations, GeGLU output)
-    # for 38.65 GFLOP, 267 FLOP/B, below the 312 FLOP/B ridge of 2.5 PF over
-    # 8 TB/s, so HBM bounds it; at thousands of rows the MFMA peak does.
-    N = cfg.n_prefix * cfg.batch
-    flops_per_launch = 2 * N * cfg.d_p * 2 * cfg.F_p
-    bytes_per_launch = 2 * (cfg.d_p * 2 * cfg.F_p + N * cfg.d_p + N * cfg.F_p)
-    if probe_launches:
-        avg_ms = probe_ms / probe_launches
-        tflops = flops_per_launch / (avg_ms * 1e-3) / 1e12
-        gbs = bytes_per_launch / (avg_ms * 1e-3) / 1e9
-        hbm_bound = bytes_per_launch / (PEAK_HBM_GBS * 1e9) >= flops_per_launch / (PEAK_BF16_TFLOPS * 1e12)
-        if hbm_bound:
-            head = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}
-        else:
-            head = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": tflops / PEAK_BF16_TFLOPS}
-        roofline = dict(head, kernel=GATEUP_KERNEL + " (prefix gate/up + GeGLU)",
-                        traffic=GATEUP_TRAFFIC_BYTES if args.config == 1 else None,
-                        avg_launch_us=avg_ms * 1e3, launches=probe_launches,
-                        bytes_per_launch=bytes_per_launch, flops_per_launch=flops_per_launch,
-                        tflops=tflops, mfma_frac=tflops / PEAK_BF16_TFLOPS, hbm_frac=gbs / PEAK_HBM_GBS)
-    else:  # the ternary prefix runs its gate/up on the W2A8 kernel, which has no probe
-        roofline = None
+    # ---- roofline of the kernel with the largest share of GPU time, and one entry per phase
+    roofline = None if args.no_roofline else dominant_kernel_roofline(vla, model, cfg, zt, xt, out, kv_storage)
+    d_gbs = sb / (phases["denoise_step_ms"] * 1e-3) / 1e9
+    p_rate = pf / (phases["prefix_ms"] * 1e-3) / 1e12
+    roofline_phases = {
+        "prefix": {"bound": "mfma", "achieved": p_rate, "peak": prefix_peak,
+                   "unit": "TOP/s" if cfg.precision == "w2a8" else "TFLOP/s", "frac": p_rate / prefix_peak,
+                   "work_per_pass": pf, "ms": phases["prefix_ms"]},
+        "denoise": {"bound": "hbm", "achieved": d_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": d_gbs / PEAK_HBM_GBS,
+                    "bytes_per_step": sb, "step_ms": phases["denoise_step_ms"],
+                    "traffic": DENOISE_TRAFFIC_BYTES_PER_STEP if (args.config == 1 and args.attn == "cross") else None},
+    }
 
     # ---- solver-step sweep (Eq. 3) and the two-stream pipelined rate: context, not the metric
     extras = {}
@@ -359,8 +453,9 @@ def main():
         extras["batched16"] = batched_entry(vla, model, cfg)
     if not args.no_extras:
         extras["solver_sweep"] = solver_sweep(vla, model, zt, xt, kv_storage)
-        extras["pipelined_two_stream"] = pipelined(vla, model, cfg, zt, xt, max(args.steps, 10))
         extras["w2a8_ablation"] = w2a8_ablation(vla)
+    if args.pipelined:
+        extras["pipelined_two_stream"] = pipelined(vla, model, cfg, zt, xt, max(args.steps, 10))
 
     # ---- CPU oracle on a bounded sample
     cpu = None
@@ -378,6 +473,7 @@ def main():
                    "chunk": [cfg.H, cfg.d_a], "solver_steps": cfg.steps},
         "phases": phases,
         "roofline": roofline,
+        "roofline_phases": roofline_phases,
         "cpu_baseline": cpu,
         **extras,
     }

@@ -294,9 +294,17 @@ typedef enum {
   VLA_PROBE_PREFIX_QKV = 3,    /* prefix fused Q/K/V projection                     */
   VLA_PROBE_PREFIX_ATTN = 4,   /* prefix bidirectional attention                    */
   VLA_PROBE_PREFIX_O = 5,      /* prefix output projection                          */
-  VLA_PROBE_CACHE = 6          /* cache-writing projection                          */
+  VLA_PROBE_CACHE = 6,         /* cache-writing projection                          */
+  VLA_PROBE_EXPERT_SELF_ATTN = 7,  /* action-expert self (or joint) attention          */
+  VLA_PROBE_EXPERT_CROSS_ATTN = 8  /* action-expert cross-attention into the cache     */
 } vla_probe_kind;
 vla_status vla_probe_arm(vla_model* model, int32_t kind, int32_t max_launches);
+/* The same with each bracketed launch issued `repeat` (1..1000) times back to
+ * back between its two events, so the events' own cost is spread over many
+ * launches; vla_probe_read then counts every repeat as a launch.  A kernel
+ * that adds into its output (a residual update) adds `repeat` times: the
+ * results of calls made while such a probe is armed are for timing only. */
+vla_status vla_probe_arm_ex(vla_model* model, int32_t kind, int32_t max_launches, int32_t repeat);
 vla_status vla_probe_read(vla_model* model, float* total_ms, int32_t* launches);
 
 #ifdef __cplusplus

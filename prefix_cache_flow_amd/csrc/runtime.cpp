@@ -289,7 +289,7 @@ struct vla_model {
   int ncu = 0;
   std::map<int, int> fused_occ;  // occupancy per (hd_e, row blocks)
   // kernel probe
-  int probe_kind = 0, probe_max = 0, probe_used = 0;
+  int probe_kind = 0, probe_max = 0, probe_used = 0, probe_repeat = 1;
   std::vector<hipEvent_t> probe_ev;
   hipStream_t probe_stream = nullptr;
 };
@@ -918,12 +918,20 @@ struct ProbeScope {
   ~ProbeScope() {
     if (on && hipEventRecord(m->probe_ev[2 * m->probe_used + 1], s) == hipSuccess) ++m->probe_used;
   }
+  // times the bracketed launch is issued: the probe's repeat count when armed for it, else once
+  int reps() const { return on ? m->probe_repeat : 1; }
 };
 
 extern "C" vla_status vla_probe_arm(vla_model* m, int32_t kind, int32_t max_launches) {
+  return vla_probe_arm_ex(m, kind, max_launches, 1);
+}
+
+extern "C" vla_status vla_probe_arm_ex(vla_model* m, int32_t kind, int32_t max_launches, int32_t repeat) {
   if (!live_model(m)) return fail(VLA_ERR_INVALID_HANDLE, "unknown model");
-  if (kind < VLA_PROBE_NONE || kind > VLA_PROBE_CACHE) return fail(VLA_ERR_INVALID_ARGUMENT, "bad probe kind");
+  if (kind < VLA_PROBE_NONE || kind > VLA_PROBE_EXPERT_CROSS_ATTN) return fail(VLA_ERR_INVALID_ARGUMENT, "bad probe kind");
   if (max_launches < 0 || max_launches > 100000) return fail(VLA_ERR_INVALID_ARGUMENT, "bad max_launches");
+  if (repeat < 1 || repeat > 1000) return fail(VLA_ERR_INVALID_ARGUMENT, "repeat must be in 1..1000");
+  m->probe_repeat = repeat;
   while ((int)m->probe_ev.size() < 2 * max_launches) {
     hipEvent_t e;
     if (hipEventCreate(&e) != hipSuccess) return fail(VLA_ERR_DEVICE, "event creation failed");
@@ -946,7 +954,7 @@ extern "C" vla_status vla_probe_read(vla_model* m, float* total_ms, int32_t* lau
     sum += ms;
   }
   *total_ms = (float)sum;
-  *launches = m->probe_used;
+  *launches = m->probe_used * m->probe_repeat;
   return VLA_OK;
 }
 
@@ -1028,19 +1036,35 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, const i
       const PrefixLayer& P = m->pl[l];
       Epilogue e = epi_store(w.qkv, qkvw, 0);
       e.alpha = w.alpha; e.beta = P.bqkv;
-      K_TRY(gemm_w2a8(w.qa, c.d_p, (const uint32_t*)P.wqkv, M, qkvw, c.d_p, e, s, &w.w2), "qkv");
+      {
+        ProbeScope ps(m, VLA_PROBE_PREFIX_QKV, s);
+        for (int rep = 0; rep < ps.reps(); ++rep)
+          K_TRY(gemm_w2a8(w.qa, c.d_p, (const uint32_t*)P.wqkv, M, qkvw, c.d_p, e, s, &w.w2), "qkv");
+      }
       K_TRY(attention_bf16(aa, s), "attention");
       K_TRY(quantize_rows((const float*)w.attn, qw, M, qw, w.qa, w.alpha, s), "quantize attn");
       Epilogue r;
       r.kind = EPI_RESID; r.resid = w.h; r.ldr = c.d_p; r.alpha = w.alpha; r.beta = P.bo;
-      K_TRY(gemm_w2a8(w.qa, qw, (const uint32_t*)P.wo, M, c.d_p, qw, r, s, &w.w2), "o proj");
+      {
+        ProbeScope ps(m, VLA_PROBE_PREFIX_O, s);
+        for (int rep = 0; rep < ps.reps(); ++rep)
+          K_TRY(gemm_w2a8(w.qa, qw, (const uint32_t*)P.wo, M, c.d_p, qw, r, s, &w.w2), "o proj");
+      }
       K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, P.w2, eps, nullptr, 0, 0, w.qa, w.alpha, s), "norm");
       Epilogue g;
       g.kind = EPI_GEGLU; g.out = w.mlp; g.ldo = c.F_p; g.out_f32 = 1; g.alpha = w.alpha; g.beta = P.bgu;
-      K_TRY(gemm_w2a8(w.qa, c.d_p, (const uint32_t*)P.wgu, M, 2 * c.F_p, c.d_p, g, s, &w.w2), "gate/up");
+      {
+        ProbeScope ps(m, VLA_PROBE_PREFIX_GATEUP, s);
+        for (int rep = 0; rep < ps.reps(); ++rep)
+          K_TRY(gemm_w2a8(w.qa, c.d_p, (const uint32_t*)P.wgu, M, 2 * c.F_p, c.d_p, g, s, &w.w2), "gate/up");
+      }
       K_TRY(quantize_rows((const float*)w.mlp, c.F_p, M, c.F_p, w.qa, w.alpha, s), "quantize mlp");
       r.beta = P.bd;
-      K_TRY(gemm_w2a8(w.qa, c.F_p, (const uint32_t*)P.wd, M, c.d_p, c.F_p, r, s, &w.w2), "down");
+      {
+        ProbeScope ps(m, VLA_PROBE_PREFIX_DOWN, s);
+        for (int rep = 0; rep < ps.reps(); ++rep)
+          K_TRY(gemm_w2a8(w.qa, c.F_p, (const uint32_t*)P.wd, M, c.d_p, c.F_p, r, s, &w.w2), "down");
+      }
       if (l + 1 < c.L_p)
         K_TRY(resid_norm(w.h, c.d_p, nullptr, 0, M, c.d_p, m->pl[l + 1].w1, eps, nullptr, 0, 0, w.qa, w.alpha, s),
               "norm");
@@ -1075,18 +1099,21 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, const i
         // attention output, the GeGLU output
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_QKV, s);
-          K_TRY(mm_frag(w.u, P.wqkv, M, qkvw, c.d_p, qkv_e, w.part, s), "qkv");
+          for (int rep = 0; rep < ps.reps(); ++rep)
+            K_TRY(mm_frag(w.u, P.wqkv, M, qkvw, c.d_p, qkv_e, w.part, s), "qkv");
         }
         if (kv_only) break;
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_ATTN, s);
-          K_TRY(attention_chunk(aa, s), "attention");
+          for (int rep = 0; rep < ps.reps(); ++rep)
+            K_TRY(attention_chunk(aa, s), "attention");
         }
         Epilogue pe;
         pe.kind = EPI_PARTIAL;
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_O, s);
-          K_TRY(mm_frag(w.attn, P.wo, M, c.d_p, qw, pe, w.part, s), "o proj");
+          for (int rep = 0; rep < ps.reps(); ++rep)
+            K_TRY(mm_frag(w.attn, P.wo, M, c.d_p, qw, pe, w.part, s), "o proj");
         }
         K_TRY(resid_norm(w.h, c.d_p, w.part, prefix_splits(M, c.d_p, qw), M, c.d_p, P.w2, eps, w.u, 0, c.d_p, nullptr,
                          nullptr, s, 1), "norm");
@@ -1095,11 +1122,13 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, const i
         g.out_frag = 1;
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_GATEUP, s);
-          K_TRY(mm_frag(w.u, P.wgu, M, 2 * c.F_p, c.d_p, g, w.part, s), "gate/up");
+          for (int rep = 0; rep < ps.reps(); ++rep)
+            K_TRY(mm_frag(w.u, P.wgu, M, 2 * c.F_p, c.d_p, g, w.part, s), "gate/up");
         }
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_DOWN, s);
-          K_TRY(mm_frag(w.mlp, P.wd, M, c.d_p, c.F_p, pe, w.part, s), "down");
+          for (int rep = 0; rep < ps.reps(); ++rep)
+            K_TRY(mm_frag(w.mlp, P.wd, M, c.d_p, c.F_p, pe, w.part, s), "down");
         }
         K_TRY(resid_norm(w.h, c.d_p, w.part, prefix_splits(M, c.d_p, c.F_p), M, c.d_p, next_gain, eps, w.u, 0, c.d_p,
                          nullptr, nullptr, s, 1), "norm");
@@ -1118,10 +1147,12 @@ static vla_status run_prefix(vla_model* m, const float* x, int B, int N, const i
   if (ce.npad > N)
     K_TRY(zero_tails(kv, (long)B * c.L_e * 2 * c.Hkv_e, (long)ce.npad * c.hd_e, 32 * c.hd_e, s), "cache padding");
   ProbeScope ps(m, VLA_PROBE_CACHE, s);
-  if (m->f32)
-    K_TRY(gemm_f32((const float*)w.u, c.d_p, (const float*)m->wcache, c.d_p, M, ncache, c.d_p, ce, s), "cache");
-  else
-    K_TRY(mm_frag(w.u, m->wcache, M, ncache, c.d_p, ce, w.part, s), "cache");
+  for (int rep = 0; rep < ps.reps(); ++rep) {
+    if (m->f32)
+      K_TRY(gemm_f32((const float*)w.u, c.d_p, (const float*)m->wcache, c.d_p, M, ncache, c.d_p, ce, s), "cache");
+    else
+      K_TRY(mm_frag(w.u, m->wcache, M, ncache, c.d_p, ce, w.part, s), "cache");
+  }
   return VLA_OK;
 }
 
@@ -1418,19 +1449,31 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
         if (m->joint) {
           // one attention over the chunk and prefix layer e, then the MLP
           sa.pf = pfr(L.wos, b_o, g_o, L.wgu, b_gu, g_gu, 192);
-          K_TRY(attention_chunk(sa, s), "joint attn");
+          {
+            ProbeScope ps(m, VLA_PROBE_EXPERT_SELF_ATTN, s);
+            for (int rep = 0; rep < ps.reps(); ++rep)
+              K_TRY(attention_chunk(sa, s), "joint attn");
+          }
           K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
           K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
         } else {
           sa.pf = pfr(L.wos, b_o, g_o, L.wqc, b_q, g_q, 192);
-          K_TRY(attention_chunk(sa, s), "self attn");
+          {
+            ProbeScope ps(m, VLA_PROBE_EXPERT_SELF_ATTN, s);
+            for (int rep = 0; rep < ps.reps(); ++rep)
+              K_TRY(attention_chunk(sa, s), "self attn");
+          }
           K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
           const Prefetch pf_kv = pfr(B == 1 ? ca.k : nullptr, B == 1 ? layer_kv : 0, 0, nullptr, 0, 0, 64);
           K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_kv),
                 "norm");
           K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, epi_store(w.eq, qe, 0), 1), "q_c");
           ca.pf = pfr(L.woc, b_o, g_o, L.wgu, b_gu, g_gu, 192);
-          K_TRY(attention_chunk(ca, s), "cross attn");
+          {
+            ProbeScope ps(m, VLA_PROBE_EXPERT_CROSS_ATTN, s);
+            for (int rep = 0; rep < ps.reps(); ++rep)
+              K_TRY(attention_chunk(ca, s), "cross attn");
+          }
           K_TRY(mm(w.eattn, qe, L.woc, c.d_e, qe, pe, S_o), "o_c");
           K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
         }

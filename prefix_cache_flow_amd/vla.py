@@ -30,11 +30,12 @@ EXPORTS = (
     "vla_status_string", "vla_last_error", "vla_n_tensors", "vla_tensor_info", "vla_model_create",
     "vla_model_destroy", "vla_kv_cache_bytes", "vla_prefix_encode", "vla_denoise_chunk",
     "vla_kv_cache_release", "vla_kv_cache_info", "vla_quantize_rows_i8", "vla_w2a8_gemm",
-    "vla_ternary_pack", "vla_ternary_unpack", "vla_probe_arm", "vla_probe_read", "vla_w2a8_gemm_ex",
+    "vla_ternary_pack", "vla_ternary_unpack", "vla_probe_arm", "vla_probe_arm_ex", "vla_probe_read", "vla_w2a8_gemm_ex",
     "vla_w2a8_gemm_noalloc", "vla_prefix_encode_masked",
 )
 W2A8_MFMA, W2A8_DOT4 = 0, 1
 PROBE_PREFIX_GATEUP, PROBE_PREFIX_DOWN, PROBE_PREFIX_QKV, PROBE_PREFIX_ATTN, PROBE_PREFIX_O, PROBE_CACHE = range(1, 7)
+PROBE_EXPERT_SELF_ATTN, PROBE_EXPERT_CROSS_ATTN = 7, 8
 
 
 class VlaError(RuntimeError):
@@ -100,6 +101,7 @@ def lib():
         "vla_ternary_pack": (I, [P, I, I, P]),
         "vla_ternary_unpack": (I, [P, I, I, P]),
         "vla_probe_arm": (I, [P, I, I]),
+        "vla_probe_arm_ex": (I, [P, I, I, I]),
         "vla_probe_read": (I, [P, C.POINTER(C.c_float), C.POINTER(I)]),
     }
     for name, (res, args) in sig.items():
@@ -291,8 +293,8 @@ def vla_prefix_encode(model: Model, prefix_hidden, kv_storage=None, stream=None,
     return kv
 
 
-def vla_probe_arm(model: Model, kind: int, max_launches: int = 4096):
-    _check(lib().vla_probe_arm(model.handle, int(kind), int(max_launches)))
+def vla_probe_arm(model: Model, kind: int, max_launches: int = 4096, repeat: int = 1):
+    _check(lib().vla_probe_arm_ex(model.handle, int(kind), int(max_launches), int(repeat)))
 
 
 def vla_probe_read(model: Model):
@@ -304,9 +306,9 @@ def vla_probe_read(model: Model):
 class Probe:
     """Arms a kernel probe on construction; collect() reads and disarms it."""
 
-    def __init__(self, model: Model, kind: int, max_launches: int = 4096):
+    def __init__(self, model: Model, kind: int, max_launches: int = 4096, repeat: int = 1):
         self.model = model
-        vla_probe_arm(model, kind, max_launches)
+        vla_probe_arm(model, kind, max_launches, repeat)
 
     def collect(self):
         r = vla_probe_read(self.model)
