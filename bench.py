@@ -31,12 +31,12 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_INT8_TOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes from rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter
-# reads for a plain copy of known size; the summaries are under profiles/.  Valid for the single-camera bf16
-# workload and the kernels as they were measured; None where no measurement stands.
+# HBM-side bytes from rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter
+# reads for a plain copy of known size (profiles/hbm_bytes_denoise_single_camera_bf16.md).  Valid for the
+# single-camera bf16 workload and the kernels as they were measured; None where no measurement stands.
 ATTN_KERNEL = "k_attn_chunk<256>"
-ATTN_TRAFFIC_BYTES_PER_LAUNCH = None   # mean over the launch mix of one policy step
-DENOISE_TRAFFIC_BYTES_PER_STEP = None  # every kernel of one solver step (the denoise graph's nodes)
+ATTN_TRAFFIC_BYTES_PER_LAUNCH = 16233650   # mean over all launches of a bench run (prefix, self, cross)
+DENOISE_TRAFFIC_BYTES_PER_STEP = 1992441622  # every kernel of one solver step (the denoise graph's nodes)
 
 
 def parse():
