@@ -1620,6 +1620,45 @@ extern "C" vla_status vla_denoise_chunk(vla_model* m, const vla_kv_cache* kv, co
   return VLA_OK;
 }
 
+// ============================================================== bf16 product unit entry point
+extern "C" vla_status vla_gemm_bf16(const uint16_t* a, const uint16_t* w, int32_t M, int32_t N, int32_t K,
+                                    int32_t geglu, float* out, void* stream) {
+  if (!a || !w || !out) return fail(VLA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (M <= 0 || N <= 0 || K <= 0) return fail(VLA_ERR_INVALID_ARGUMENT, "M, N and K must be positive");
+  if (K % 64 || N % 32) return fail(VLA_ERR_UNSUPPORTED, "need K % 64 == 0 and N % 32 == 0");
+  if ((int64_t)M * K > ((int64_t)1 << 31) || (int64_t)N * K > ((int64_t)1 << 31) || (int64_t)M * N > ((int64_t)1 << 29))
+    return fail(VLA_ERR_UNSUPPORTED, "operands too large for the unit entry point");
+  vla_status st = check_device();
+  if (st != VLA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // fragment-layout operands: A rows padded to whole 16-row blocks, at least 64 (zero rows)
+  const int64_t rows = std::max<int64_t>(64, ((int64_t)M + 15) / 16 * 16);
+  uint16_t *ap = nullptr, *af = nullptr, *wf = nullptr;
+  float* ws = nullptr;
+  auto done = [&](vla_status r) {
+    for (void* p : {(void*)ap, (void*)af, (void*)wf, (void*)ws})
+      if (p) (void)hipFree(p);
+    return r;
+  };
+  const size_t ws_bytes = (size_t)4 * M * N * 4;  // at most four K splits for a finishing epilogue
+  if (lib_malloc((void**)&ap, (size_t)rows * K * 2) != hipSuccess || lib_malloc((void**)&af, (size_t)rows * K * 2) != hipSuccess ||
+      lib_malloc((void**)&wf, (size_t)N * K * 2) != hipSuccess || lib_malloc((void**)&ws, ws_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return done(fail(VLA_ERR_OUT_OF_MEMORY, "staging"));
+  }
+  if (hipMemsetAsync(ap, 0, (size_t)rows * K * 2, s) != hipSuccess ||
+      hipMemcpyAsync(ap, a, (size_t)M * K * 2, hipMemcpyDeviceToDevice, s) != hipSuccess ||
+      frag_pack(ap, (int)rows, K, af, s) != hipSuccess || frag_pack(w, N, K, wf, s) != hipSuccess)
+    return done(fail(VLA_ERR_DEVICE, "operand repack"));
+  Epilogue e = epi_store(out, geglu ? N / 2 : N, 1);
+  if (geglu) e.kind = EPI_GEGLU;
+  const hipError_t le = M <= 64 ? gemm_chunk(af, wf, M, N, K, e, kPrefixChunkSplits, ws, s)
+                                : gemm_frag(af, wf, M, N, K, e, 0, ws, s);
+  if (le != hipSuccess) return done(fail(VLA_ERR_DEVICE, std::string("gemm launch: ") + hipGetErrorString(le)));
+  if (hipStreamSynchronize(s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "gemm sync"));
+  return done(VLA_OK);
+}
+
 // ============================================================== ternary unit entry points
 extern "C" vla_status vla_quantize_rows_i8(const float* x, int32_t M, int32_t K, int8_t* a, float* alpha, void* stream) {
   if (!x || !a || !alpha) return fail(VLA_ERR_INVALID_ARGUMENT, "NULL pointer");

@@ -30,7 +30,7 @@ EXPORTS = (
     "vla_status_string", "vla_last_error", "vla_n_tensors", "vla_tensor_info", "vla_model_create",
     "vla_model_destroy", "vla_kv_cache_bytes", "vla_prefix_encode", "vla_denoise_chunk",
     "vla_kv_cache_release", "vla_kv_cache_info", "vla_quantize_rows_i8", "vla_w2a8_gemm",
-    "vla_ternary_pack", "vla_ternary_unpack", "vla_probe_arm", "vla_probe_arm_ex", "vla_probe_read", "vla_w2a8_gemm_ex",
+    "vla_ternary_pack", "vla_ternary_unpack", "vla_probe_arm", "vla_probe_arm_ex", "vla_probe_read", "vla_gemm_bf16", "vla_w2a8_gemm_ex",
     "vla_w2a8_gemm_noalloc", "vla_prefix_encode_masked",
 )
 W2A8_MFMA, W2A8_DOT4 = 0, 1
@@ -102,6 +102,7 @@ def lib():
         "vla_ternary_unpack": (I, [P, I, I, P]),
         "vla_probe_arm": (I, [P, I, I]),
         "vla_probe_arm_ex": (I, [P, I, I, I]),
+        "vla_gemm_bf16": (I, [P, P, I, I, I, I, P, P]),
         "vla_probe_read": (I, [P, C.POINTER(C.c_float), C.POINTER(I)]),
     }
     for name, (res, args) in sig.items():
@@ -291,6 +292,19 @@ def vla_prefix_encode(model: Model, prefix_hidden, kv_storage=None, stream=None,
     if timing:
         return kv, {"prefix_ms": tm.prefix_ms}
     return kv
+
+
+def vla_gemm_bf16(a, w, geglu: bool = False, stream=None):
+    """a: cuda bfloat16 [M, K], w: cuda bfloat16 [N, K] -> float32 [M, N] (or [M, N / 2] with the GeGLU of
+    gate/up rows interleaved in blocks of 16), on the prefix's product kernels."""
+    import torch
+    assert a.dtype == torch.bfloat16 and w.dtype == torch.bfloat16 and a.is_contiguous() and w.is_contiguous()
+    M, K = a.shape
+    N = w.shape[0]
+    out = torch.empty((M, N // 2 if geglu else N), dtype=torch.float32, device=a.device)
+    _check(lib().vla_gemm_bf16(C.c_void_p(a.data_ptr()), C.c_void_p(w.data_ptr()), M, N, K, int(bool(geglu)),
+                               C.c_void_p(out.data_ptr()), _stream(stream)))
+    return out
 
 
 def vla_probe_arm(model: Model, kind: int, max_launches: int = 4096, repeat: int = 1):

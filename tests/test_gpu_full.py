@@ -5,7 +5,10 @@ encode and the denoise on the GPU, and compares with the float64 oracle on the
 same inputs: Eq. 5's relative error (the paper, §III-E) on the bf16 action chunk
 within 2e-2, plus bounds on the displacement X^T - X^0 and on the K/V cache.
 The batched workload runs all 16 observations on the GPU and checks a sample of
-them against the oracle (observations are independent).
+them against the oracle (observations are independent); every batched case is
+also run with its observations in reverse order, which must give the same
+chunks and caches bit for bit, reversed (no observation's result depends on
+its position or its neighbours).
 """
 import gc
 import time
@@ -39,7 +42,7 @@ from prefix_cache_flow_amd import vla  # noqa: E402
 CASES = [
     (1, 1e-2, 2e-2, None),
     (2, 1e-2, 2e-2, None),
-    (3, 1e-2, 2e-2, (0, 15)),
+    (3, 1e-2, 2e-2, (0, 5, 10, 15)),
     (4, 4e-2, 1e-1, None),
     ("joint", 1e-2, 2e-2, None),
 ]
@@ -72,6 +75,21 @@ def test_full_size_against_oracle(idx, dtol, ctol, sample):
     got32 = out32.cpu().numpy().astype(np.float64)
     gcache = cache_from_storage(cfg, kv.storage, cfg.batch, cfg.n_prefix)
     kv.close()
+    if cfg.batch > 1:
+        rev = list(range(cfg.batch))[::-1]
+        zr, xr = torch.from_numpy(z0[rev].copy()).cuda(), torch.from_numpy(x0[rev].copy()).cuda()
+        kvr = vla.vla_prefix_encode(model, zr)
+        outr = vla.vla_denoise_chunk(model, kvr, xr, cfg.steps)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(outr.cpu().numpy()[rev], got32.astype(np.float32))
+        rcache = cache_from_storage(cfg, kvr.storage, cfg.batch, cfg.n_prefix)
+        for bo in range(cfg.batch):
+            for l in range(cfg.L_e):
+                for i in range(2):
+                    np.testing.assert_array_equal(rcache[rev[bo]][l][i], gcache[bo][l][i])
+        kvr.close()
+        del zr, xr, outr
+        log(f"case {cfg.name}: reversed batch identical at {time.time() - t0:.1f}s")
     model.close()
     del zt, xt, out16, out32
     torch.cuda.empty_cache()

@@ -188,15 +188,31 @@ def test_bidirectional_first_token_sees_last_on_gpu():
     cfg = synth.config(1, n_prefix=64, d_p=128, L_p=1, Hq=2, Hkv=1, hd=64, F_p=256, d_e=128, L_e=1, Hq_e=2,
                        Hkv_e=1, hd_e=64, F_e=128, H=4, d_a=4, steps=1)
     w, b, z0, x0 = host_inputs(cfg, 2)
+    # token 0's own state scaled down, so its cache row is mostly what its attention gathers from the
+    # others; the second prefix negates the last token
+    z0 = z0.copy()
+    z0[0, 0] *= 0.01
     model = build_model(cfg, w, b)
     _, s0 = gpu_run(cfg, model, z0, x0)
     c0 = cache_from_storage(cfg, s0.clone(), 1, cfg.n_prefix)
     z1 = z0.copy()
-    z1[0, -1] += 3.0
+    z1[0, -1] = -z1[0, -1]
     _, s1 = gpu_run(cfg, model, z1, x0)
     c1 = cache_from_storage(cfg, s1, 1, cfg.n_prefix)
-    assert np.abs(c1[0][0][0][0] - c0[0][0][0][0]).max() > 0  # token 0's key moved
     model.close()
+    # the oracle's caches of both prefixes: token 0's key moves by far more than the bf16 error, and the
+    # GPU's moved cache matches the oracle's moved cache (an unmoved one would miss it by that margin)
+    o = oracle.Oracle(cfg, w, b)
+    r0 = o.run(z0, x0, keep_cache=True)[1][0]
+    r1 = o.run(z1, x0, keep_cache=True)[1][0]
+    moved = np.linalg.norm(r1[0][0][0] - r0[0][0][0]) / np.linalg.norm(r0[0][0][0])
+    assert moved > 0.1, f"oracle: token 0's key moved by only {moved:.3e}"
+    for l in range(cfg.L_e):
+        for i in range(2):
+            assert oracle.e_rel(c0[0][l][i], r0[l][i]) <= 2e-2
+            assert oracle.e_rel(c1[0][l][i], r1[l][i]) <= 2e-2
+    assert oracle.e_rel(c1[0][0][0][0], r1[0][0][0]) <= 2e-2
+    assert oracle.e_rel(c0[0][0][0][0], r1[0][0][0]) > 2e-2
 
 
 def test_scheduled_reverse_time():
@@ -339,3 +355,28 @@ def test_invalid_ternary_weights_rejected_at_create():
     with pytest.raises(vla.VlaError) as ei:
         vla.vla_model_create(cfg.to_dict(), tensors, ordered_betas(cfg, b))
     assert ei.value.status == 1
+
+
+# ---------------------------------------------------------------- the prefix's bf16 products as units
+# The four prefix products of the single-camera workload (288 tokens: QKV, O, gate/up with its GeGLU,
+# down), its cache projection (18 layers x K and V of one 256-wide head), and chunk-sized and ragged
+# shapes, through vla_gemm_bf16 (the same kernels and split choices the prefix uses), against float64
+# products of the same bf16 values.  Bound: float32 accumulation over K <= 16384 terms of bf16 products
+# gives a normwise error of a few 1e-7 (measured); 1e-5 leaves a wide margin while a dropped K split or a
+# misplaced tile (errors of order 1) fails it.
+@pytest.mark.parametrize("M,N,K,geglu", [(288, 2560, 2048, False), (288, 2048, 2048, False),
+                                         (288, 32768, 2048, True), (288, 2048, 16384, False),
+                                         (288, 9216, 2048, False), (50, 1024, 1024, False), (50, 8192, 1024, True),
+                                         (37, 96, 128, True), (1, 64, 64, False), (301, 160, 192, False)])
+def test_prefix_bf16_products(M, N, K, geglu):
+    rng = np.random.default_rng(M * 7 + N + K)
+    a = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((0.02 * rng.standard_normal((N, K))).astype(np.float32)).to(torch.bfloat16)
+    got = vla.vla_gemm_bf16(a.cuda(), w.cuda(), geglu=geglu).cpu().numpy().astype(np.float64)
+    ref = a.double().numpy() @ w.double().numpy().T
+    if geglu:
+        blk = ref.reshape(M, N // 32, 2, 16)
+        ref = (oracle.gelu(blk[:, :, 0, :]) * blk[:, :, 1, :]).reshape(M, N // 2)
+    err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert err < 1e-5, f"normwise error {err:.3e}"
+    assert np.isfinite(got).all()
