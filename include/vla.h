@@ -71,6 +71,9 @@ typedef enum {
 
 typedef enum { VLA_OUT_F32 = 0, VLA_OUT_BF16 = 1 } vla_out_dtype;
 
+/* Element type of the prefix hidden states handed to vla_prefix_encode_ex. */
+typedef enum { VLA_IN_F32 = 0, VLA_IN_BF16 = 1 } vla_in_dtype;
+
 /* How the action expert reads the observation (the paper, §III-B).
  * CROSS: the final prefix states Z are projected into per-expert-layer K_C, V_C
  *   (Eq. 2), and every expert layer has self-attention over the chunk, then
@@ -211,6 +214,19 @@ vla_status vla_prefix_encode_masked(vla_model* model, const float* prefix_hidden
                                     int32_t n_prefix, const int32_t* lengths, void* kv_storage,
                                     size_t kv_bytes, void* stream, vla_kv_cache** out,
                                     vla_timing* timing);
+
+/* vla_prefix_encode_masked with the element type of prefix_hidden given:
+ * in_dtype VLA_IN_F32 (device float32, as above) or VLA_IN_BF16 (device
+ * bfloat16 [batch][n_prefix][d_p], for callers whose vision and text encoders
+ * produce bf16 states; each value is widened exactly to the float32 residual
+ * stream, so the result equals vla_prefix_encode_masked on the widened
+ * tensor, bit for bit).  Any precision of the model accepts either type.
+ * VLA_ERR_INVALID_ARGUMENT for another in_dtype; the rest as
+ * vla_prefix_encode_masked (lengths == NULL: no key padding). */
+vla_status vla_prefix_encode_ex(vla_model* model, const void* prefix_hidden, int32_t in_dtype,
+                                int32_t batch, int32_t n_prefix, const int32_t* lengths,
+                                void* kv_storage, size_t kv_bytes, void* stream,
+                                vla_kv_cache** out, vla_timing* timing);
 
 /* Flow-matching solver (the paper, §III-A, Eq. 1): X^0 = noise (device float32
  * [batch][H][d_a], batch and n_prefix taken from the cache), `steps` Euler

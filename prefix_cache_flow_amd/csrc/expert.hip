@@ -242,18 +242,26 @@ hipError_t set_lengths(int* dst, const int32_t* len, int B, int N, hipStream_t s
   return hipSuccess;
 }
 
-// one row of d floats per workgroup row slot: rows past the observation's length become zeros
-__global__ void k_copy_prefix_rows(const float* src, float* dst, int N, int d, const int* lens) {
+// One prefix row of d values per workgroup into the fp32 residual stream: fp32
+// copied, bf16 widened (exact); rows past the observation's length (lens, if
+// given) become zeros.
+template <bool BF16>
+__global__ void k_copy_prefix_rows(const void* src, float* dst, int N, int d, const int* lens) {
   const long row = blockIdx.x;
   const int b = (int)(row / N), t = (int)(row % N);
-  const bool keep = t < lens[b];
-  for (int i = threadIdx.x; i < d; i += blockDim.x) dst[row * d + i] = keep ? src[row * d + i] : 0.f;
+  const bool keep = !lens || t < lens[b];
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    const float v = BF16 ? bf2f(((const bf16_t*)src)[row * d + i]) : ((const float*)src)[row * d + i];
+    dst[row * d + i] = keep ? v : 0.f;
+  }
 }
 
-hipError_t copy_prefix_rows(const float* src, float* dst, int B, int N, int d, const int* lens, hipStream_t s) {
+hipError_t copy_prefix_rows(const void* src, int src_bf16, float* dst, int B, int N, int d, const int* lens,
+                            hipStream_t s) {
   if ((long)B * N <= 0) return hipSuccess;
   if ((long)B * N > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_copy_prefix_rows, dim3((unsigned)(B * N)), dim3(256), 0, s, src, dst, N, d, lens);
+  if (src_bf16) hipLaunchKernelGGL(k_copy_prefix_rows<true>, dim3((unsigned)(B * N)), dim3(256), 0, s, src, dst, N, d, lens);
+  else hipLaunchKernelGGL(k_copy_prefix_rows<false>, dim3((unsigned)(B * N)), dim3(256), 0, s, src, dst, N, d, lens);
   return hipGetLastError();
 }
 

@@ -263,9 +263,11 @@ void gemm_chunk_plan(int K, int splits, int* used, int* kchunk);
 // values, passed to the kernel by value in groups of 64), or N for every b
 // when len is null.
 hipError_t set_lengths(int* dst, const int32_t* len, int B, int N, hipStream_t s);
-// dst = src for the [B][N][d] prefix rows, with the rows of observation b past
-// its length lens[b] (device) written as zeros.
-hipError_t copy_prefix_rows(const float* src, float* dst, int B, int N, int d, const int* lens, hipStream_t s);
+// dst = src for the [B][N][d] prefix rows (src fp32, or bf16 widened to fp32
+// when src_bf16), with the rows of observation b past its length lens[b]
+// (device; null: every row kept) written as zeros.
+hipError_t copy_prefix_rows(const void* src, int src_bf16, float* dst, int B, int N, int d, const int* lens,
+                            hipStream_t s);
 // dst = src (fp32), or bf16(src) when out_bf16
 hipError_t copy_out(const float* src, void* dst, long n, int out_bf16, hipStream_t s);
 hipError_t copy_f32(const float* src, float* dst, long n, hipStream_t s);

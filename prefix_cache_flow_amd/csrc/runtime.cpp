@@ -970,15 +970,15 @@ static Epilogue epi_store(void* out, int ldo, int out_f32) {
 // lens: per-observation prefix lengths on the device (null: every observation
 // fills all N positions).  Rows past an observation's length are zeroed on the
 // way in, and their keys are masked in the prefix attention.
-static vla_status run_prefix(vla_model* m, const float* x, int B, int N, const int* lens, void* kv, const WS& w,
-                             hipStream_t s) {
+static vla_status run_prefix(vla_model* m, const void* x, int x_bf16, int B, int N, const int* lens, void* kv,
+                             const WS& w, hipStream_t s) {
   const vla_model_config& c = m->cfg;
   const int M = B * N;
   const int qw = c.Hq * c.hd, qkvw = (c.Hq + 2 * c.Hkv) * c.hd;
   const float eps = c.rms_eps;
   const int uf = m->f32 ? 1 : 0;
-  if (lens) K_TRY(copy_prefix_rows(x, w.h, B, N, c.d_p, lens, s), "copy prefix");
-  else K_TRY(copy_f32(x, w.h, (long)M * c.d_p, s), "copy prefix");
+  if (lens || x_bf16) K_TRY(copy_prefix_rows(x, x_bf16, w.h, B, N, c.d_p, lens, s), "copy prefix");
+  else K_TRY(copy_f32((const float*)x, w.h, (long)M * c.d_p, s), "copy prefix");
   AttnArgs aa{};
   aa.klen = lens;
   aa.q = w.qkv; aa.q_bs = (long)N * qkvw; aa.q_hs = c.hd; aa.q_rs = qkvw;
@@ -1167,13 +1167,14 @@ extern "C" size_t vla_kv_cache_bytes(const vla_model* m, int32_t batch, int32_t 
   return (kv_core_bytes(m, batch, n_prefix) + 255) / 256 * 256 + ((size_t)batch * 4 + 255) / 256 * 256;
 }
 
-extern "C" vla_status vla_prefix_encode_masked(vla_model* m, const float* x, int32_t batch, int32_t n_prefix,
-                                               const int32_t* lengths, void* kv_storage, size_t kv_bytes, void* stream,
-                                               vla_kv_cache** out, vla_timing* timing) {
+extern "C" vla_status vla_prefix_encode_ex(vla_model* m, const void* x, int32_t x_dtype, int32_t batch,
+                                           int32_t n_prefix, const int32_t* lengths, void* kv_storage, size_t kv_bytes,
+                                           void* stream, vla_kv_cache** out, vla_timing* timing) {
   if (!out) return fail(VLA_ERR_INVALID_ARGUMENT, "out is NULL");
   *out = nullptr;
   if (!live_model(m)) return fail(VLA_ERR_INVALID_HANDLE, "unknown model");
   if (!x || !kv_storage) return fail(VLA_ERR_INVALID_ARGUMENT, "prefix_hidden or kv_storage is NULL");
+  if (x_dtype != VLA_IN_F32 && x_dtype != VLA_IN_BF16) return fail(VLA_ERR_INVALID_ARGUMENT, "bad prefix_hidden dtype");
   if (batch <= 0 || n_prefix <= 0) return fail(VLA_ERR_INVALID_ARGUMENT, "batch and n_prefix must be positive");
   if ((int64_t)batch * n_prefix > (1 << 22)) return fail(VLA_ERR_UNSUPPORTED, "too many prefix tokens");
   if (lengths)
@@ -1191,7 +1192,7 @@ extern "C" vla_status vla_prefix_encode_masked(vla_model* m, const float* x, int
   int* lens = (int*)((char*)kv_storage + (kv_core_bytes(m, batch, n_prefix) + 255) / 256 * 256);
   if (timing) K_TRY(hipEventRecord(m->ev0, s), "event");
   if (lengths) K_TRY(set_lengths(lens, lengths, batch, n_prefix, s), "prefix lengths");
-  st = run_prefix(m, x, batch, n_prefix, lengths ? lens : nullptr, kv_storage, w, s);
+  st = run_prefix(m, x, x_dtype == VLA_IN_BF16, batch, n_prefix, lengths ? lens : nullptr, kv_storage, w, s);
   if (st != VLA_OK) return st;
   if (timing) {
     K_TRY(hipEventRecord(m->ev1, s), "event");
@@ -1217,9 +1218,15 @@ extern "C" vla_status vla_prefix_encode_masked(vla_model* m, const float* x, int
   return VLA_OK;
 }
 
+extern "C" vla_status vla_prefix_encode_masked(vla_model* m, const float* x, int32_t batch, int32_t n_prefix,
+                                               const int32_t* lengths, void* kv_storage, size_t kv_bytes, void* stream,
+                                               vla_kv_cache** out, vla_timing* timing) {
+  return vla_prefix_encode_ex(m, x, VLA_IN_F32, batch, n_prefix, lengths, kv_storage, kv_bytes, stream, out, timing);
+}
+
 extern "C" vla_status vla_prefix_encode(vla_model* m, const float* x, int32_t batch, int32_t n_prefix, void* kv_storage,
                                         size_t kv_bytes, void* stream, vla_kv_cache** out, vla_timing* timing) {
-  return vla_prefix_encode_masked(m, x, batch, n_prefix, nullptr, kv_storage, kv_bytes, stream, out, timing);
+  return vla_prefix_encode_ex(m, x, VLA_IN_F32, batch, n_prefix, nullptr, kv_storage, kv_bytes, stream, out, timing);
 }
 
 extern "C" vla_status vla_kv_cache_release(vla_kv_cache* k) {

@@ -31,7 +31,7 @@ EXPORTS = (
     "vla_model_destroy", "vla_kv_cache_bytes", "vla_prefix_encode", "vla_denoise_chunk",
     "vla_kv_cache_release", "vla_kv_cache_info", "vla_quantize_rows_i8", "vla_w2a8_gemm",
     "vla_ternary_pack", "vla_ternary_unpack", "vla_probe_arm", "vla_probe_arm_ex", "vla_probe_read", "vla_gemm_bf16", "vla_w2a8_gemm_ex",
-    "vla_w2a8_gemm_noalloc", "vla_prefix_encode_masked",
+    "vla_w2a8_gemm_noalloc", "vla_prefix_encode_masked", "vla_prefix_encode_ex",
 )
 W2A8_MFMA, W2A8_DOT4 = 0, 1
 PROBE_PREFIX_GATEUP, PROBE_PREFIX_DOWN, PROBE_PREFIX_QKV, PROBE_PREFIX_ATTN, PROBE_PREFIX_O, PROBE_CACHE = range(1, 7)
@@ -91,6 +91,8 @@ def lib():
         "vla_prefix_encode": (I, [P, P, I, I, P, S, P, C.POINTER(P), C.POINTER(vla_timing)]),
         "vla_prefix_encode_masked": (I, [P, P, I, I, C.POINTER(C.c_int32), P, S, P, C.POINTER(P),
                                          C.POINTER(vla_timing)]),
+        "vla_prefix_encode_ex": (I, [P, P, I, I, I, C.POINTER(C.c_int32), P, S, P, C.POINTER(P),
+                                     C.POINTER(vla_timing)]),
         "vla_denoise_chunk": (I, [P, P, P, I, C.POINTER(vla_solver), P, I, P, C.POINTER(vla_timing)]),
         "vla_kv_cache_release": (I, [P]),
         "vla_kv_cache_info": (I, [P, C.POINTER(I), C.POINTER(I)]),
@@ -267,12 +269,15 @@ def vla_kv_cache_bytes(model: Model, batch: int, n_prefix: int) -> int:
     return lib().vla_kv_cache_bytes(model.handle, batch, n_prefix)
 
 
+IN_F32, IN_BF16 = 0, 1
+
+
 def vla_prefix_encode(model: Model, prefix_hidden, kv_storage=None, stream=None, timing: bool = False, lengths=None):
-    """prefix_hidden: float32 cuda tensor [B, N, d_p]; returns a KVCache (and a timing dict when asked).
-    lengths (optional, B ints in 1..N) calls vla_prefix_encode_masked: observation b fills its first
-    lengths[b] rows."""
+    """prefix_hidden: float32 (or bfloat16: vla_prefix_encode_ex) cuda tensor [B, N, d_p]; returns a
+    KVCache (and a timing dict when asked).  lengths (optional, B ints in 1..N) calls
+    vla_prefix_encode_masked: observation b fills its first lengths[b] rows."""
     import torch
-    assert prefix_hidden.dtype == torch.float32 and prefix_hidden.is_contiguous()
+    assert prefix_hidden.dtype in (torch.float32, torch.bfloat16) and prefix_hidden.is_contiguous()
     B, N, _ = prefix_hidden.shape
     nbytes = vla_kv_cache_bytes(model, B, N)
     if kv_storage is None:
@@ -281,7 +286,11 @@ def vla_prefix_encode(model: Model, prefix_hidden, kv_storage=None, stream=None,
     tm = vla_timing() if timing else None
     nb = kv_storage.numel() * kv_storage.element_size()
     tmp = C.byref(tm) if tm is not None else None
-    if lengths is None:
+    if prefix_hidden.dtype == torch.bfloat16:
+        lens = (C.c_int32 * B)(*[int(x) for x in lengths]) if lengths is not None else None
+        _check(lib().vla_prefix_encode_ex(model.handle, _ptr(prefix_hidden), IN_BF16, B, N, lens, _ptr(kv_storage),
+                                          nb, _stream(stream), C.byref(h), tmp))
+    elif lengths is None:
         _check(lib().vla_prefix_encode(model.handle, _ptr(prefix_hidden), B, N, _ptr(kv_storage), nb,
                                        _stream(stream), C.byref(h), tmp))
     else:

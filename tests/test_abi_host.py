@@ -102,6 +102,8 @@ def test_null_and_foreign_handles_are_rejected():
     assert L.vla_kv_cache_info(C.c_void_p(0x10), C.byref(b), C.byref(n)) == 3
     out = C.c_void_p()
     assert L.vla_prefix_encode(None, None, 1, 1, None, 0, None, C.byref(out), None) == 3
+    assert L.vla_prefix_encode_ex(None, None, 1, 1, 1, None, None, 0, None, C.byref(out), None) == 3
+    assert L.vla_prefix_encode_ex(None, None, 0, 1, 1, None, None, 0, None, None, None) == 1
     assert L.vla_probe_arm(None, 1, 4) == 3
     assert L.vla_denoise_chunk(None, None, None, 1, None, None, 0, None, None) == 3
     cfg = vla.make_config(synth.config(0).to_dict())

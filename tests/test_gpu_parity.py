@@ -140,6 +140,40 @@ def test_cached_equals_recompute_on_gpu(cfg):
     model.close()
 
 
+@pytest.mark.parametrize("cfg", [synth.config(0), SMALL_BF16_B3, SMALL_JOINT_B3, SMALL_W2A8], ids=lambda c: c.name)
+def test_bf16_prefix_input_equals_widened_f32(cfg):
+    """vla_prefix_encode_ex with bfloat16 prefix states writes the same cache bytes, and gives the same chunk,
+    as vla_prefix_encode on those states widened to float32 (widening is exact), with and without key
+    padding; an unknown input type is rejected."""
+    w, b, z0, x0 = host_inputs(cfg, 3)
+    print(f"case {cfg.name} seed 3", flush=True)
+    model = build_model(cfg, w, b)
+    z16 = torch.from_numpy(z0).cuda().bfloat16().contiguous()
+    z32 = z16.float().contiguous()
+    xt = torch.from_numpy(x0).cuda()
+    nbytes = vla.vla_kv_cache_bytes(model, cfg.batch, cfg.n_prefix)
+    lens = [max(1, cfg.n_prefix - 3 * i) for i in range(cfg.batch)]
+    for lengths in (None, lens):
+        outs = []
+        stores = []
+        for z in (z32, z16):
+            st = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+            kv = vla.vla_prefix_encode(model, z, kv_storage=st, lengths=lengths)
+            outs.append(vla.vla_denoise_chunk(model, kv, xt, cfg.steps).cpu().numpy())
+            torch.cuda.synchronize()
+            kv.close()
+            stores.append(st.cpu().numpy())
+        np.testing.assert_array_equal(stores[0], stores[1])
+        np.testing.assert_array_equal(outs[0], outs[1])
+    import ctypes
+    h = ctypes.c_void_p()
+    st = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    rc = vla.lib().vla_prefix_encode_ex(model.handle, ctypes.c_void_p(z16.data_ptr()), 7, cfg.batch, cfg.n_prefix,
+                                        None, ctypes.c_void_p(st.data_ptr()), nbytes, None, ctypes.byref(h), None)
+    assert rc == 1 and not h.value  # VLA_ERR_INVALID_ARGUMENT, no handle
+    model.close()
+
+
 @pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_GQA, SMALL_JOINT], ids=lambda c: c.name)
 def test_two_stream_pipeline_matches_serial(cfg):
     """Prefix passes on one stream overlapping solver runs on another (one model, two cache
