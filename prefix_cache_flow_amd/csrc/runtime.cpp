@@ -24,6 +24,7 @@
 #include <vector>
 
 #include "../../include/vla.h"
+#include "../../include/vla_probe.h"
 #include "kernels.h"
 
 using namespace vla;

@@ -3,6 +3,7 @@ with the workload shapes, and its host-side validation and format helpers work.
 No kernel is launched here."""
 import ctypes as C
 import json
+import glob
 import os
 import re
 import sys
@@ -18,9 +19,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "vla.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(vla_[a-z0-9_]+)\s*\(", text)))
+    """Every function the headers under include/ declare (vla.h: the policy interface; vla_probe.h: the
+    measurement probes)."""
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(vla_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
