@@ -282,8 +282,10 @@ def test_quantizer_bit_exact(M, K):
     np.testing.assert_array_equal(al.cpu().numpy(), al_ref)
 
 
+# The 2560-wide products split K over two or three workgroups; the rest run their 64 x 128 tiles whole (300 and
+# 290 rows: a ragged last row tile).
 @pytest.mark.parametrize("M,N,K", [(320, 7680, 2560), (320, 2560, 2560), (320, 13824, 2560), (320, 2560, 6912),
-                                   (320, 7680, 1152), (37, 96, 384), (1, 32, 128)])
+                                   (320, 7680, 1152), (300, 7680, 2560), (290, 8192, 512), (37, 96, 384), (1, 32, 128)])
 def test_w2a8_gemm_bit_exact(M, N, K):
     rng = np.random.default_rng(N + K)
     x = _x_rows(M, K, K)
