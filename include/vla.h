@@ -125,7 +125,7 @@ typedef struct {
  * The library copies every weight into its own layout during vla_model_create;
  * the caller's buffers may be freed once it returns. */
 typedef struct {
-  const void* const* tensors; /* host array of n_tensors device pointers */
+  const void* const* tensors; /* host array of n_tensors pointers: device or host memory */
   int32_t n_tensors;          /* must equal vla_n_tensors(cfg)            */
   const float* ternary_beta;  /* host; NULL unless precision is W2A8      */
 } vla_weights;
@@ -165,8 +165,13 @@ vla_status vla_tensor_info(const vla_model_config* cfg, int32_t index, int64_t* 
 
 /* Build a model on the current device: validates cfg, copies and repacks the
  * weights (ternary codes are checked; an invalid code 3 gives
- * VLA_ERR_INVALID_ARGUMENT), and owns the result until vla_model_destroy.
- * Synchronises `stream`.  Returns VLA_ERR_DEVICE if no gfx950 device is present. */
+ * VLA_ERR_INVALID_ARGUMENT), and owns the result until vla_model_destroy; the
+ * caller's tensors are only read during the call.  A tensor may be in device
+ * memory or in host memory (pageable or pinned, each read once through the
+ * library's staging buffer): with every tensor on the host the device holds
+ * the packed model plus one staging buffer, never a second copy of the
+ * weights.  Synchronises `stream`.  Returns VLA_ERR_DEVICE if no gfx950
+ * device is present. */
 vla_status vla_model_create(const vla_model_config* cfg, const vla_weights* weights,
                             void* stream, vla_model** out);
 vla_status vla_model_destroy(vla_model* model);

@@ -375,34 +375,62 @@ struct Src {
   int bi = 0;
 };
 
+// Source tensors may live in device memory or in host memory (pageable or
+// pinned): every copy below names no direction (hipMemcpyDefault), and the one
+// kernel that reads a source directly (the ternary repack) gets a device copy
+// of a host tensor first.
+static bool on_device(const void* p) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();  // unknown to HIP: plain host memory
+    return false;
+  }
+  return a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged;
+}
+
 // copy rows of a linear weight, converting fp32 -> bf16 is never needed (the
 // caller gives the precision's own type), into dst at row offset `row0`
 static vla_status put_rows(vla_model* m, void* dst, int64_t row0, const void* src, int64_t rows, int64_t cols,
                            hipStream_t s) {
   const size_t es = elt(m);
-  HIP_TRY(hipMemcpyAsync((char*)dst + row0 * cols * es, src, rows * cols * es, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(hipMemcpyAsync((char*)dst + row0 * cols * es, src, rows * cols * es, hipMemcpyDefault, s));
   return VLA_OK;
 }
 
 // interleave gate and up [F][cols] into [2F][cols] in blocks of 16 rows
 static vla_status put_interleaved(void* dst, const void* g, const void* u, int64_t F, size_t row_bytes, hipStream_t s) {
   const size_t blk = 16 * row_bytes;
-  HIP_TRY(hipMemcpy2DAsync(dst, 2 * blk, g, blk, blk, F / 16, hipMemcpyDeviceToDevice, s));
-  HIP_TRY(hipMemcpy2DAsync((char*)dst + blk, 2 * blk, u, blk, blk, F / 16, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(hipMemcpy2DAsync(dst, 2 * blk, g, blk, blk, F / 16, hipMemcpyDefault, s));
+  HIP_TRY(hipMemcpy2DAsync((char*)dst + blk, 2 * blk, u, blk, blk, F / 16, hipMemcpyDefault, s));
   return VLA_OK;
 }
 
 static vla_status put_gain(vla_model* m, float** dst, const void* src, int64_t n, hipStream_t s) {
   vla_status st = dev_alloc(m, (void**)dst, n * 4);
   if (st != VLA_OK) return st;
-  HIP_TRY(hipMemcpyAsync(*dst, src, n * 4, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(hipMemcpyAsync(*dst, src, n * 4, hipMemcpyDefault, s));
   return VLA_OK;
 }
 
 // ternary: canonical bytes -> library words at row offset (rows of K/16 words)
 static vla_status put_ternary(uint32_t* dst, int64_t row0, const void* src, int64_t rows, int64_t K, int* flags,
                               hipStream_t s) {
-  HIP_TRY(ternary_repack((const uint8_t*)src, (int)rows, (int)K, dst + row0 * (K / 16), flags, s));
+  if (on_device(src)) {
+    HIP_TRY(ternary_repack((const uint8_t*)src, (int)rows, (int)K, dst + row0 * (K / 16), flags, s));
+    return VLA_OK;
+  }
+  // host tensor: through a device copy, freed once the repack has run
+  void* d = nullptr;
+  const size_t bytes = (size_t)rows * K / 4;
+  if (lib_malloc(&d, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(VLA_ERR_OUT_OF_MEMORY, "ternary source staging");
+  }
+  hipError_t e = hipMemcpyAsync(d, src, bytes, hipMemcpyDefault, s);
+  if (e == hipSuccess) e = ternary_repack((const uint8_t*)d, (int)rows, (int)K, dst + row0 * (K / 16), flags, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(d);
+  if (e != hipSuccess) return fail(VLA_ERR_DEVICE, std::string("ternary upload: ") + hipGetErrorString(e));
   return VLA_OK;
 }
 

@@ -221,7 +221,8 @@ class KVCache:
 
 
 def upload_weights(cfg, arrays: Sequence[np.ndarray], device="cuda"):
-    """Device tensors in boundary order from host arrays in the same order.
+    """Tensors in boundary order from host arrays in the same order, on `device` ("cpu" keeps them in host
+    memory: vla_model_create reads host tensors directly).
 
     Gains and fp32 linears become float32 tensors, bf16 linears bfloat16
     tensors, ternary codes ({-1, 0, 1} int8) packed uint8 tensors (packed by

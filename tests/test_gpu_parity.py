@@ -140,6 +140,33 @@ def test_cached_equals_recompute_on_gpu(cfg):
     model.close()
 
 
+@pytest.mark.parametrize("cfg", [synth.config(0), SMALL_BF16, SMALL_JOINT, SMALL_W2A8], ids=lambda c: c.name)
+def test_model_from_host_weights_equals_device_weights(cfg):
+    """vla_model_create reading every tensor from host memory (pageable, then pinned) builds the same model as
+    from device memory: the same cache and the same chunk, bit for bit."""
+    w, b, z0, x0 = host_inputs(cfg, 4)
+    print(f"case {cfg.name} seed 4", flush=True)
+    names = [n for n, _, _ in synth.weight_specs(cfg)]
+    betas = [b[n] for n, _, k in synth.weight_specs(cfg) if k == "ternary"] or None
+    ref_model = build_model(cfg, w, b)
+    ref, ref_store = gpu_run(cfg, ref_model, z0, x0)
+    ref_model.close()
+    host = vla.upload_weights(cfg.to_dict(), [w[n] for n in names], device="cpu")
+    for tensors in (host, [t.pin_memory() for t in host]):
+        assert all(not t.is_cuda for t in tensors)
+        model = vla.vla_model_create(cfg.to_dict(), tensors, betas)
+        got, store = gpu_run(cfg, model, z0, x0)
+        model.close()
+        np.testing.assert_array_equal(got, ref)
+        # the cache blocks themselves (the storage's unwritten padding bytes are whatever torch.empty held)
+        gc = cache_from_storage(cfg, store, cfg.batch, cfg.n_prefix)
+        rc = cache_from_storage(cfg, ref_store, cfg.batch, cfg.n_prefix)
+        for bb in range(cfg.batch):
+            for l in range(len(rc[bb])):
+                for i in range(2):
+                    np.testing.assert_array_equal(gc[bb][l][i], rc[bb][l][i])
+
+
 @pytest.mark.parametrize("cfg", [synth.config(0), SMALL_BF16_B3, SMALL_JOINT_B3, SMALL_W2A8], ids=lambda c: c.name)
 def test_bf16_prefix_input_equals_widened_f32(cfg):
     """vla_prefix_encode_ex with bfloat16 prefix states writes the same cache bytes, and gives the same chunk,
