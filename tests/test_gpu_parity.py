@@ -289,6 +289,23 @@ def test_scheduled_reverse_time():
     model.close()
 
 
+@pytest.mark.parametrize("scale", [1e-2, 30.0])
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_W2A8], ids=lambda c: c.name)
+def test_prefix_state_scale(cfg, scale):
+    """Prefix states far from unit size (the norms rescale them, the residual stream keeps them): the chunk still
+    matches the oracle within the bf16 bound, and nothing overflows."""
+    w, b, z0, x0 = host_inputs(cfg, 5)
+    z = (z0 * scale).astype(np.float32)
+    print(f"case {cfg.name} seed 5 scale {scale}", flush=True)
+    model = build_model(cfg, w, b)
+    ref = oracle.Oracle(cfg, w, b).run(z, x0)
+    got, _ = gpu_run(cfg, model, z, x0)
+    model.close()
+    assert np.isfinite(got).all()
+    e, ed = report(f"{cfg.name} x{scale}", got, ref, x0.astype(np.float64))
+    assert e <= 2e-2 and ed <= 2e-2
+
+
 # ---------------------------------------------------------------- ternary units (bit-exact)
 
 def _x_rows(M, K, seed):
