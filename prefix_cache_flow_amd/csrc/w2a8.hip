@@ -13,12 +13,14 @@
 //
 // Tiles: 64 activation rows x 128 output channels per workgroup of eight
 // waves (two per SIMD, four with the two workgroups a CU holds), 256-input K
-// slices (128 when 256 does not divide K), 32x32x32 int8 MFMA.  The activation
-// slice is staged in LDS as int8; the weight slice is staged *packed* (2 bits
-// per weight, a quarter of the int8 bytes) and unpacked in registers right
-// before the MFMA.  When the output tiles alone would leave CUs idle, the K
-// range of a tile is split over up to three workgroups whose int32 partial
-// sums meet in a workspace (exact in any order).
+// slices (128 when 256 does not divide K), 32x32x32 int8 MFMA.  Each wave owns
+// one 32 x 32 block of the tile over the whole K range, so no partial sums
+// cross waves and all eight share the epilogue.  The activation slice is
+// staged in LDS as int8; the weight slice is staged *packed* (2 bits per
+// weight, a quarter of the int8 bytes) and unpacked in registers right before
+// the MFMA.  When the output tiles alone would leave CUs idle, the K range of
+// a tile is split over up to three workgroups whose int32 partial sums meet in
+// a workspace (exact in any order).
 #include <mutex>
 
 #include "common.h"
@@ -59,19 +61,19 @@ constexpr int kSC1 = 16;                 // cache policy bits of device-scope co
 // values) is issued before the first store: loads and stores retire through one
 // counter here, so a load placed after a store would wait for that store's
 // round trip too.
-template <int KIND, bool ACC, bool F32>
-__device__ __forceinline__ void w2a8_epilogue(const W2A8P& p, const i32x16_t (&fin)[2], int own, int c, int lane,
+template <int KIND, bool ACC, bool F32, int GB>
+__device__ __forceinline__ void w2a8_epilogue(const W2A8P& p, const i32x16_t (&fin)[GB], int own, int col0, int lane,
                                               int m0, int n0, const float* s_al, const float* s_be) {
   const Epilogue& e = p.epi;
-  const int mb = m0 + own * 32, nb = n0 + c * 64 + (lane & 31);
-  float al[16], be[2], rv[2][16];
+  const int mb = m0 + own * 32, nb = n0 + col0 + (lane & 31);
+  float al[16], be[GB], rv[GB][16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) al[q] = s_al[own * 32 + mfma32_row(q, lane)];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) be[g] = s_be[c * 64 + g * 32 + (lane & 31)];
+  for (int g = 0; g < GB; ++g) be[g] = s_be[col0 + g * 32 + (lane & 31)];
   if (KIND == EPI_RESID) {
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < GB; ++g)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int m = mb + mfma32_row(q, lane), n = nb + g * 32;
@@ -79,7 +81,7 @@ __device__ __forceinline__ void w2a8_epilogue(const W2A8P& p, const i32x16_t (&f
       }
   }
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
+  for (int g = 0; g < GB; ++g) {
     const int n = nb + g * 32;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -105,53 +107,50 @@ __device__ __forceinline__ void w2a8_epilogue(const W2A8P& p, const i32x16_t (&f
 }
 
 // One 64 x 128 output tile (or one K split of it) per workgroup of eight
-// waves, two per SIMD.  Wave (c, kq) = (wid & 1, wid >> 1) accumulates the 64
-// rows x 64 channels of channel half c over the k quarter kq of every slice:
-// both 32-row halves against both 32-channel groups, so each activation
-// fragment and each unpacked weight word feeds two MFMAs and the wave runs
-// four independent MFMA chains.  The four k quarters are summed through LDS at
-// the end (int32: exact in any order).
+// waves; wave w owns the 32 x 32 block of row half w & 1 and channel group
+// w >> 1 over the whole K range, in two accumulators (even and odd k-steps, so
+// consecutive MFMAs do not wait on each other; added at the end: int32,
+// exact).  A wave reads each of its activation fragments and weight words
+// once per slice; the four waves of a row half read the same activation
+// fragments and the two of a channel group unpack the same weight words.  An
+// earlier split of the tile into k quarters per wave (each activation fragment
+// feeding two MFMAs) needed a four-way sum through LDS at the end and an
+// epilogue on half the waves, which cost more than the extra LDS reads.
 template <int BK, int KIND, bool ACC>
 __global__ __launch_bounds__(512, 4) void k_gemm_w2a8(W2A8P p) {
   constexpr int BM = kBM, BN = kBN, LDA = BK + 16, LDW = BK / 16 + 1;
-  constexpr int KPW = BK / 32 / 4;                // MFMA k-steps per wave and slice (a quarter)
+  constexpr int KST = BK / 32;                    // MFMA k-steps per slice
   constexpr int AV = BM * BK / 16 / 512;          // 16-byte activation vectors per thread and slice
   constexpr int WW = BN * BK / 16 / 512;          // weight words per thread and slice (4 or 2)
-  constexpr int STAGE = 2 * BM * LDA + 2 * BN * LDW * 4;
-  constexpr int RED = 4 * 64 * 64 * 4;            // four wave-sized slots of 64 ints per lane
-  constexpr int LDS = STAGE > RED ? STAGE : RED;
-  static_assert(AV >= 1 && (WW == 4 || WW == 2) && KPW >= 1, "slice shape");
+  constexpr int LDS = 2 * BM * LDA + 2 * BN * LDW * 4;
+  static_assert(AV >= 1 && (WW == 4 || WW == 2) && KST % 2 == 0, "slice shape");
   typedef __attribute__((__vector_size__(WW * sizeof(uint32_t)))) uint32_t wvec_t;
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDS];
   __shared__ float s_al[BM], s_be[BN];
   __shared__ unsigned s_last;
   int8_t(*sA)[BM * LDA] = (int8_t(*)[BM * LDA])lds;
   uint32_t(*sW)[BN * LDW] = (uint32_t(*)[BN * LDW])(lds + 2 * BM * LDA);
-  int* red = (int*)lds;
 
-  // work item -> (tile, split); consecutive items share an XCD (linear id mod 8),
-  // so the splits of a tile and the row tiles of one weight column meet in one L2
   const int W = p.nM * p.nN * p.S, L = blockIdx.x;
   const int wk = (W % 8 == 0) ? (L % 8) * (W / 8) + L / 8 : L;
   const int sp = wk % p.S, tile = wk / p.S;
   const int tm = tile % p.nM, tn = tile / p.nM;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int c = wid & 1, kq = wid >> 1;  // channel half, k quarter of every slice
-  const int KW = p.K / 16;               // words per weight row
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rh = wid & 1, cg = wid >> 1;  // row half, channel group of 32
+  const int KW = p.K / 16;
   const int ns = p.K / BK, s_lo = sp * ns / p.S, nsl = (sp + 1) * ns / p.S - s_lo;
   const Epilogue& e = p.epi;
   if (tid < BM) s_al[tid] = e.alpha[min(m0 + tid, p.M - 1)];
   else if (tid < BM + BN) s_be[tid - BM] = e.beta ? e.beta[min(n0 + tid - BM, p.N - 1)] : p.beta_scalar;
 
   struct Regs { u32x4_t a[AV]; wvec_t w; };
-  constexpr int AR = BK / 16, WR = BK / 16 / WW;  // vectors per activation row, per weight row
+  constexpr int AR = BK / 16, WR = BK / 16 / WW;
   auto gload = [&](Regs& g, int i) {
-    const int k0 = (s_lo + min(i, nsl - 1)) * BK;  // past the end: the last slice again (never used)
+    const int k0 = (s_lo + min(i, nsl - 1)) * BK;
 #pragma unroll
     for (int v0 = 0; v0 < AV; ++v0) {
       const int v = tid + v0 * 512, r = v / AR, cc = (v % AR) * 16;
-      // rows past the end are clamped to valid ones; their results are never stored
       g.a[v0] = *(const u32x4_t*)(p.a + (long)min(m0 + r, p.M - 1) * p.lda + k0 + cc);
     }
     const int r = tid / WR, cc = (tid % WR) * WW;
@@ -168,36 +167,22 @@ __global__ __launch_bounds__(512, 4) void k_gemm_w2a8(W2A8P p) {
     for (int t = 0; t < WW; ++t) sW[buf][r * LDW + cc + t] = g.w[t];
   };
 
-  i32x16_t acc[2][2];
+  i32x16_t acc[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][g][q] = 0;
+    for (int q = 0; q < 16; ++q) acc[i][q] = 0;
   auto compute = [&](int buf) {
-    i32x4_t af[KPW][2];
-    uint32_t wq[KPW][2];
+    i32x4_t af[KST];
+    uint32_t wq[KST];
 #pragma unroll
-    for (int j = 0; j < KPW; ++j) {
-      const int kk = kq * KPW + j;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[j][i] = __builtin_bit_cast(
-            i32x4_t, *(const u32x4_t*)&sA[buf][(i * 32 + (lane & 31)) * LDA + kk * 32 + (lane >> 5) * 16]);
-#pragma unroll
-      for (int g = 0; g < 2; ++g) wq[j][g] = sW[buf][(c * 64 + g * 32 + (lane & 31)) * LDW + kk * 2 + (lane >> 5)];
+    for (int kk = 0; kk < KST; ++kk) {
+      af[kk] = __builtin_bit_cast(i32x4_t, *(const u32x4_t*)&sA[buf][(rh * 32 + (lane & 31)) * LDA + kk * 32 + (lane >> 5) * 16]);
+      wq[kk] = sW[buf][(cg * 32 + (lane & 31)) * LDW + kk * 2 + (lane >> 5)];
     }
 #pragma unroll
-    for (int j = 0; j < KPW; ++j)
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const i32x4_t wf = unpack16(wq[j][g]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) acc[i][g] = mfma32x32x32_i8(af[j][i], wf, acc[i][g]);
-      }
+    for (int kk = 0; kk < KST; ++kk) acc[kk & 1] = mfma32x32x32_i8(af[kk], unpack16(wq[kk]), acc[kk & 1]);
   };
-
   // Slice t lives in register set t % NR until it is stored to LDS buffer
   // t % 2 (NR = 3 register sets for 128-input slices, 2 for 256-input ones,
   // which keeps four waves per SIMD within the register file).  Entering step
@@ -228,72 +213,9 @@ __global__ __launch_bounds__(512, 4) void k_gemm_w2a8(W2A8P p) {
     W2A8_STEP(0) W2A8_STEP(1) W2A8_STEP(2)
   }
 #undef W2A8_STEP
-
-  // Sum of the four k quarters.  A slot holds a wave's 64 ints per lane as 16
-  // chunks of four, chunk h = (i * 2 + g) * 4 + q / 4 of lane l at ints
-  // (h * 64 + l) * 4 .. + 3 (16-byte accesses).  Level 1: quarters 2, 3 hand
-  // everything to quarters 0, 1.  Level 2: quarter 0 keeps row half 0 and
-  // quarter 1 row half 1, each handing over the other.
-  auto chunk = [&](int* slot, int i, int g, int h4) -> i32x4_t* {
-    return (i32x4_t*)(slot + (((i * 2 + g) * 4 + h4) * 64 + lane) * 4);
-  };
-  auto part = [](const i32x16_t& v, int h4) { return i32x4_t{v[4 * h4], v[4 * h4 + 1], v[4 * h4 + 2], v[4 * h4 + 3]}; };
-  __syncthreads();  // the staging buffers are free from here on
-  if (kq >= 2) {
-    int* o = red + (c * 2 + kq - 2) * 64 * 64;
+  i32x16_t fin[1];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int h4 = 0; h4 < 4; ++h4) *chunk(o, i, g, h4) = part(acc[i][g], h4);
-  }
-  __syncthreads();
-  if (kq < 2) {
-    int* o = red + (c * 2 + kq) * 64 * 64;
-    i32x4_t in[2][2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int h4 = 0; h4 < 4; ++h4) in[i][g][h4] = *chunk(o, i, g, h4);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[i][g][q] += in[i][g][q / 4][q % 4];
-  }
-  __syncthreads();
-  // (the row half a wave keeps is wave-uniform; both branches index statically)
-  const int own = kq & 1;
-  i32x16_t fin[2], give[2];
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    if (own == 0) { fin[g] = acc[0][g]; give[g] = acc[1][g]; }
-    else { fin[g] = acc[1][g]; give[g] = acc[0][g]; }
-  }
-  if (kq < 2) {
-    int* o = red + (c * 2 + kq) * 64 * 64;
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int h4 = 0; h4 < 4; ++h4) *chunk(o, 1 - own, g, h4) = part(give[g], h4);
-  }
-  __syncthreads();
-  if (kq < 2) {
-    int* o = red + (c * 2 + (1 - kq)) * 64 * 64;
-    i32x4_t in[2][4];
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int h4 = 0; h4 < 4; ++h4) in[g][h4] = *chunk(o, own, g, h4);
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) fin[g][q] += in[g][q / 4][q % 4];
-  }
+  for (int q = 0; q < 16; ++q) fin[0][q] = acc[0][q] + acc[1][q];
 
   if (p.S > 1) {
     // K split: every split stores its sums with device-scope coherent stores
@@ -303,17 +225,15 @@ __global__ __launch_bounds__(512, 4) void k_gemm_w2a8(W2A8P p) {
     // launch and runs the epilogue.  No workgroup ever waits on another.
     const uint32_t bytes = (uint32_t)((size_t)W * kPartInts * 4);
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(p.ws, (short)0, (int)bytes, 0x00020000);
-    auto off = [&](int split, int g, int h4) {
-      return (uint32_t)(((size_t)(tile * p.S + split) * kPartInts + (((kq * 2 + c) * 2 + g) * 4 + h4) * 256 + lane * 4) * 4);
+    auto off = [&](int split, int h4) {
+      return (uint32_t)(((size_t)(tile * p.S + split) * kPartInts + (wid * 4 + h4) * 256 + lane * 4) * 4);
     };
-    if (kq < 2) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int h4 = 0; h4 < 4; ++h4)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, part(fin[g], h4)), r, off(sp, g, h4), 0, kSC1);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    for (int h4 = 0; h4 < 4; ++h4)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4_t, i32x4_t{fin[0][4 * h4], fin[0][4 * h4 + 1], fin[0][4 * h4 + 2], fin[0][4 * h4 + 3]}), r,
+          off(sp, h4), 0, kSC1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
       const unsigned old = __hip_atomic_fetch_add(p.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -321,23 +241,18 @@ __global__ __launch_bounds__(512, 4) void k_gemm_w2a8(W2A8P p) {
       if (s_last) __hip_atomic_store(p.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    if (!s_last || kq >= 2) return;
+    if (!s_last) return;
     for (int o = 0; o < p.S; ++o) {
       if (o == sp) continue;
-      u32x4_t in[2][4];
+      u32x4_t in[4];
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
+      for (int h4 = 0; h4 < 4; ++h4) in[h4] = __builtin_amdgcn_raw_buffer_load_b128(r, off(o, h4), 0, kSC1);
 #pragma unroll
-        for (int h4 = 0; h4 < 4; ++h4) in[g][h4] = __builtin_amdgcn_raw_buffer_load_b128(r, off(o, g, h4), 0, kSC1);
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) fin[g][q] += (int)in[g][q / 4][q % 4];
+      for (int q = 0; q < 16; ++q) fin[0][q] += (int)in[q / 4][q % 4];
     }
   }
-  if (kq >= 2) return;
-  if (e.out_f32) w2a8_epilogue<KIND, ACC, true>(p, fin, own, c, lane, m0, n0, s_al, s_be);
-  else w2a8_epilogue<KIND, ACC, false>(p, fin, own, c, lane, m0, n0, s_al, s_be);
+  if (e.out_f32) w2a8_epilogue<KIND, ACC, true, 1>(p, fin, rh, cg * 32, lane, m0, n0, s_al, s_be);
+  else w2a8_epilogue<KIND, ACC, false, 1>(p, fin, rh, cg * 32, lane, m0, n0, s_al, s_be);
 }
 
 size_t w2a8_part_bytes(int M, int N) {
