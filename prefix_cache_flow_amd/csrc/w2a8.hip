@@ -13,9 +13,10 @@
 //
 // Tiles: 64 activation rows x 128 output channels per workgroup of eight
 // waves (two per SIMD, four with the two workgroups a CU holds), 256-input K
-// slices (128 when 256 does not divide K), 32x32x32 int8 MFMA.  Each wave owns
-// one 32 x 32 block of the tile over the whole K range, so no partial sums
-// cross waves and all eight share the epilogue.  The activation slice is
+// slices (128 when 256 does not divide K), 32x32x32 int8 MFMA.  Each wave
+// accumulates 64 rows x 32 channels over half of every slice; the halves meet
+// once through LDS, after which each wave holds one 32 x 32 block and all
+// eight share the epilogue.  The activation slice is
 // staged in LDS as int8; the weight slice is staged *packed* (2 bits per
 // weight, a quarter of the int8 bytes) and unpacked in registers right before
 // the MFMA.  When the output tiles alone would leave CUs idle, the K range of
@@ -107,50 +108,54 @@ __device__ __forceinline__ void w2a8_epilogue(const W2A8P& p, const i32x16_t (&f
 }
 
 // One 64 x 128 output tile (or one K split of it) per workgroup of eight
-// waves; wave w owns the 32 x 32 block of row half w & 1 and channel group
-// w >> 1 over the whole K range, in two accumulators (even and odd k-steps, so
-// consecutive MFMAs do not wait on each other; added at the end: int32,
-// exact).  A wave reads each of its activation fragments and weight words
-// once per slice; the four waves of a row half read the same activation
-// fragments and the two of a channel group unpack the same weight words.  An
-// earlier split of the tile into k quarters per wave (each activation fragment
-// feeding two MFMAs) needed a four-way sum through LDS at the end and an
-// epilogue on half the waves, which cost more than the extra LDS reads.
+// waves.  Wave (cg, kh) = (w & 3, w >> 2) accumulates all 64 rows of channel
+// group cg (32 channels) over the k half kh of every slice: each weight word
+// is unpacked by exactly one wave and feeds two MFMAs (the two 32-row blocks,
+// whose accumulators alternate, so consecutive MFMAs do not wait on each
+// other).  At the end the two k halves meet once through LDS: wave kh keeps
+// row block kh and hands the other to its partner (int32: exact in any order),
+// so all eight waves finish one 32 x 32 block each and share the epilogue.
 template <int BK, int KIND, bool ACC>
 __global__ __launch_bounds__(512, 4) void k_gemm_w2a8(W2A8P p) {
   constexpr int BM = kBM, BN = kBN, LDA = BK + 16, LDW = BK / 16 + 1;
-  constexpr int KST = BK / 32;                    // MFMA k-steps per slice
+  constexpr int KPW = BK / 32 / 2;                // MFMA k-steps per wave and slice (a half)
   constexpr int AV = BM * BK / 16 / 512;          // 16-byte activation vectors per thread and slice
   constexpr int WW = BN * BK / 16 / 512;          // weight words per thread and slice (4 or 2)
-  constexpr int LDS = 2 * BM * LDA + 2 * BN * LDW * 4;
-  static_assert(AV >= 1 && (WW == 4 || WW == 2) && KST % 2 == 0, "slice shape");
+  constexpr int STAGE = 2 * BM * LDA + 2 * BN * LDW * 4;
+  constexpr int XCH = 8 * 16 * 64 * 4;            // eight waves' handed-over blocks (16 ints a lane)
+  constexpr int LDS = STAGE > XCH ? STAGE : XCH;
+  static_assert(AV >= 1 && (WW == 4 || WW == 2) && KPW >= 1, "slice shape");
   typedef __attribute__((__vector_size__(WW * sizeof(uint32_t)))) uint32_t wvec_t;
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDS];
   __shared__ float s_al[BM], s_be[BN];
   __shared__ unsigned s_last;
   int8_t(*sA)[BM * LDA] = (int8_t(*)[BM * LDA])lds;
   uint32_t(*sW)[BN * LDW] = (uint32_t(*)[BN * LDW])(lds + 2 * BM * LDA);
+  int* xch = (int*)lds;
 
+  // work item -> (tile, split); consecutive items share an XCD (linear id mod 8),
+  // so the splits of a tile and the row tiles of one weight column meet in one L2
   const int W = p.nM * p.nN * p.S, L = blockIdx.x;
   const int wk = (W % 8 == 0) ? (L % 8) * (W / 8) + L / 8 : L;
   const int sp = wk % p.S, tile = wk / p.S;
   const int tm = tile % p.nM, tn = tile / p.nM;
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rh = wid & 1, cg = wid >> 1;  // row half, channel group of 32
-  const int KW = p.K / 16;
+  const int cg = wid & 3, kh = wid >> 2;  // channel group of 32, k half of every slice
+  const int KW = p.K / 16;                // words per weight row
   const int ns = p.K / BK, s_lo = sp * ns / p.S, nsl = (sp + 1) * ns / p.S - s_lo;
   const Epilogue& e = p.epi;
   if (tid < BM) s_al[tid] = e.alpha[min(m0 + tid, p.M - 1)];
   else if (tid < BM + BN) s_be[tid - BM] = e.beta ? e.beta[min(n0 + tid - BM, p.N - 1)] : p.beta_scalar;
 
   struct Regs { u32x4_t a[AV]; wvec_t w; };
-  constexpr int AR = BK / 16, WR = BK / 16 / WW;
+  constexpr int AR = BK / 16, WR = BK / 16 / WW;  // vectors per activation row, per weight row
   auto gload = [&](Regs& g, int i) {
-    const int k0 = (s_lo + min(i, nsl - 1)) * BK;
+    const int k0 = (s_lo + min(i, nsl - 1)) * BK;  // past the end: the last slice again (never used)
 #pragma unroll
     for (int v0 = 0; v0 < AV; ++v0) {
       const int v = tid + v0 * 512, r = v / AR, cc = (v % AR) * 16;
+      // rows past the end are clamped to valid ones; their results are never stored
       g.a[v0] = *(const u32x4_t*)(p.a + (long)min(m0 + r, p.M - 1) * p.lda + k0 + cc);
     }
     const int r = tid / WR, cc = (tid % WR) * WW;
@@ -167,21 +172,29 @@ __global__ __launch_bounds__(512, 4) void k_gemm_w2a8(W2A8P p) {
     for (int t = 0; t < WW; ++t) sW[buf][r * LDW + cc + t] = g.w[t];
   };
 
-  i32x16_t acc[2];
+  i32x16_t acc[2];  // row blocks 0 and 1
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[i][q] = 0;
   auto compute = [&](int buf) {
-    i32x4_t af[KST];
-    uint32_t wq[KST];
+    i32x4_t af[KPW][2];
+    uint32_t wq[KPW];
 #pragma unroll
-    for (int kk = 0; kk < KST; ++kk) {
-      af[kk] = __builtin_bit_cast(i32x4_t, *(const u32x4_t*)&sA[buf][(rh * 32 + (lane & 31)) * LDA + kk * 32 + (lane >> 5) * 16]);
-      wq[kk] = sW[buf][(cg * 32 + (lane & 31)) * LDW + kk * 2 + (lane >> 5)];
+    for (int j = 0; j < KPW; ++j) {
+      const int kk = kh * KPW + j;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[j][i] = __builtin_bit_cast(
+            i32x4_t, *(const u32x4_t*)&sA[buf][(i * 32 + (lane & 31)) * LDA + kk * 32 + (lane >> 5) * 16]);
+      wq[j] = sW[buf][(cg * 32 + (lane & 31)) * LDW + kk * 2 + (lane >> 5)];
     }
 #pragma unroll
-    for (int kk = 0; kk < KST; ++kk) acc[kk & 1] = mfma32x32x32_i8(af[kk], unpack16(wq[kk]), acc[kk & 1]);
+    for (int j = 0; j < KPW; ++j) {
+      const i32x4_t wf = unpack16(wq[j]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[i] = mfma32x32x32_i8(af[j][i], wf, acc[i]);
+    }
   };
   // Slice t lives in register set t % NR until it is stored to LDS buffer
   // t % 2 (NR = 3 register sets for 128-input slices, 2 for 256-input ones,
@@ -213,9 +226,30 @@ __global__ __launch_bounds__(512, 4) void k_gemm_w2a8(W2A8P p) {
     W2A8_STEP(0) W2A8_STEP(1) W2A8_STEP(2)
   }
 #undef W2A8_STEP
-  i32x16_t fin[1];
+
+  // The two k halves: wave kh keeps row block kh; the other block goes to the
+  // partner wave through LDS (16-byte chunks, lane-major).  fin is copied out
+  // of the accumulators by static indices in each branch.
+  i32x16_t fin[1], give;
+  if (kh == 0) { fin[0] = acc[0]; give = acc[1]; }
+  else { fin[0] = acc[1]; give = acc[0]; }
+  __syncthreads();  // the staging buffers are free from here on
 #pragma unroll
-  for (int q = 0; q < 16; ++q) fin[0][q] = acc[0][q] + acc[1][q];
+  for (int h4 = 0; h4 < 4; ++h4)
+    *(i32x4_t*)(xch + ((wid * 4 + h4) * 64 + lane) * 4) =
+        i32x4_t{give[4 * h4], give[4 * h4 + 1], give[4 * h4 + 2], give[4 * h4 + 3]};
+  __syncthreads();
+  {
+    const int partner = wid ^ 4;
+#pragma unroll
+    for (int h4 = 0; h4 < 4; ++h4) {
+      const i32x4_t v = *(const i32x4_t*)(xch + ((partner * 4 + h4) * 64 + lane) * 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) fin[0][4 * h4 + q] += v[q];
+    }
+  }
+  // this wave now holds row block kh of channel group cg: slot wid of a
+  // tile's partial sums below
 
   if (p.S > 1) {
     // K split: every split stores its sums with device-scope coherent stores
@@ -251,8 +285,8 @@ __global__ __launch_bounds__(512, 4) void k_gemm_w2a8(W2A8P p) {
       for (int q = 0; q < 16; ++q) fin[0][q] += (int)in[q / 4][q % 4];
     }
   }
-  if (e.out_f32) w2a8_epilogue<KIND, ACC, true, 1>(p, fin, rh, cg * 32, lane, m0, n0, s_al, s_be);
-  else w2a8_epilogue<KIND, ACC, false, 1>(p, fin, rh, cg * 32, lane, m0, n0, s_al, s_be);
+  if (e.out_f32) w2a8_epilogue<KIND, ACC, true, 1>(p, fin, kh, cg * 32, lane, m0, n0, s_al, s_be);
+  else w2a8_epilogue<KIND, ACC, false, 1>(p, fin, kh, cg * 32, lane, m0, n0, s_al, s_be);
 }
 
 size_t w2a8_part_bytes(int M, int N) {
