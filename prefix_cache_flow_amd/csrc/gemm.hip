@@ -663,10 +663,31 @@ struct ChunkP {
   Prefetch pf;  // read by grid layers z >= 1, if any
 };
 
-template <int NB, int MB, int KIND, int SPW>
+template <int NB, int MB, int KIND, int SPW, bool RS>
 __global__ __launch_bounds__(256) void k_chunk(ChunkP p) {
   __shared__ float red[4][MB * NB * 4][64];  // [wave][row block, column block, element][lane]
+  __shared__ float rsp[4][64];               // RS: each wave's partial sum of squares of each row
   if (prefetch_layer(p.pf)) return;
+  // RS: the partial sums of squares are laid out [x][row][S] (x the producer's
+  // XCD, S = nss / 8 column groups each); lane l of wave w takes row l's of
+  // XCDs 2w and 2w + 1 (S consecutive floats each, so a wave's loads cover
+  // whole lines).  They go out with the kernel's first loads and are summed
+  // after its MFMAs.
+  f32x4_t ssv[2][2];
+  if (RS) {
+    const int S = p.epi.nss >> 3;
+#pragma unroll
+    for (int xi = 0; xi < 2; ++xi) {
+      const float* b = p.epi.rss + ((long)(2 * ((int)threadIdx.x >> 6) + xi) * 64 + (threadIdx.x & 63)) * S;
+      if (S >= 4) {
+        ssv[xi][0] = *(const f32x4_t*)b;
+        ssv[xi][1] = S == 8 ? *(const f32x4_t*)(b + 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      } else {
+        ssv[xi][0] = f32x4_t{b[0], S == 2 ? b[1] : 0.f, 0.f, 0.f};
+        ssv[xi][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
   const int bx = blockIdx.x, by = blockIdx.y;  // column group, K chunk
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -707,6 +728,14 @@ __global__ __launch_bounds__(256) void k_chunk(ChunkP p) {
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) red[w][(rb * NB + nb) * 4 + e][lane] = acc[rb][nb][e];
+  if (RS) {
+    float t = 0.f;
+#pragma unroll
+    for (int xi = 0; xi < 2; ++xi)
+#pragma unroll
+      for (int v = 0; v < 2; ++v) t += (ssv[xi][v][0] + ssv[xi][v][1]) + (ssv[xi][v][2] + ssv[xi][v][3]);
+    rsp[w][lane] = t;
+  }
   __syncthreads();
 
   // wave w finishes row block w: the four K ranges summed in wave order, then the epilogue
@@ -724,6 +753,11 @@ __global__ __launch_bounds__(256) void k_chunk(ChunkP p) {
   for (int e = 0; e < 4; ++e) {
     const int m = rb * 16 + grp * 4 + e;
     if (m >= p.M) continue;
+    if (RS) {
+      const float r = 1.0f / sqrtf(((rsp[0][m] + rsp[1][m]) + (rsp[2][m] + rsp[3][m])) / (float)p.epi.rdim + p.epi.reps);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) v[nb][e] *= r;
+    }
     if (KIND == EPI_GEGLU) {
       epi_geglu(p.epi, m, (nb0 >> 1) * 16 + col, v[0][e], v[NB - 1][e]);
       continue;
@@ -739,12 +773,22 @@ __global__ __launch_bounds__(256) void k_chunk(ChunkP p) {
 
 template <int MB, int SPW>
 static hipError_t launch_chunk_spw(const ChunkP& p, int kind, dim3 grid, hipStream_t s) {
+  const bool rs = p.epi.rss != nullptr;  // row scales: the finishing kinds only
   switch (kind) {
-    case EPI_GEGLU: hipLaunchKernelGGL((k_chunk<2, MB, EPI_GEGLU, SPW>), grid, dim3(256), 0, s, p); break;
-    case EPI_STORE: hipLaunchKernelGGL((k_chunk<1, MB, EPI_STORE, SPW>), grid, dim3(256), 0, s, p); break;
-    case EPI_QKV: hipLaunchKernelGGL((k_chunk<1, MB, EPI_QKV, SPW>), grid, dim3(256), 0, s, p); break;
-    case EPI_CACHE: hipLaunchKernelGGL((k_chunk<1, MB, EPI_CACHE, SPW>), grid, dim3(256), 0, s, p); break;
-    case EPI_PARTIAL: hipLaunchKernelGGL((k_chunk<1, MB, EPI_PARTIAL, SPW>), grid, dim3(256), 0, s, p); break;
+    case EPI_GEGLU:
+      if (rs) hipLaunchKernelGGL((k_chunk<2, MB, EPI_GEGLU, SPW, true>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((k_chunk<2, MB, EPI_GEGLU, SPW, false>), grid, dim3(256), 0, s, p);
+      break;
+    case EPI_STORE:
+      if (rs) hipLaunchKernelGGL((k_chunk<1, MB, EPI_STORE, SPW, true>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((k_chunk<1, MB, EPI_STORE, SPW, false>), grid, dim3(256), 0, s, p);
+      break;
+    case EPI_QKV:
+      if (rs) hipLaunchKernelGGL((k_chunk<1, MB, EPI_QKV, SPW, true>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((k_chunk<1, MB, EPI_QKV, SPW, false>), grid, dim3(256), 0, s, p);
+      break;
+    case EPI_CACHE: hipLaunchKernelGGL((k_chunk<1, MB, EPI_CACHE, SPW, false>), grid, dim3(256), 0, s, p); break;
+    case EPI_PARTIAL: hipLaunchKernelGGL((k_chunk<1, MB, EPI_PARTIAL, SPW, false>), grid, dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -772,6 +816,11 @@ hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int 
   int used, per;
   chunk_plan(K, splits, &used, &per);
   if (used > 1 && !ws) return hipErrorInvalidValue;
+  // row scales apply to one K chunk's finished sums (no partials), at most 64 partials a row
+  if (epi.rss && (used > 1 || epi.kind == EPI_PARTIAL || epi.kind == EPI_CACHE ||
+                  (epi.nss != 8 && epi.nss != 16 && epi.nss != 32 && epi.nss != 64) || epi.rdim <= 0 ||
+                  ((uintptr_t)epi.rss & 15)))
+    return hipErrorInvalidValue;
   const Prefetch pf = prefetch ? *prefetch : Prefetch{};
   if (pf.blocks < 0 || pf.blocks > 1024 || (pf.blocks && !pf.sink)) return hipErrorInvalidValue;
   const bool reduce = used > 1 && epi.kind != EPI_PARTIAL;
@@ -791,6 +840,117 @@ hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int 
     err = hipGetLastError();
   }
   return err;
+}
+
+// ------------------------------------------------------------------ residual-updating rows
+// gemm_chunk_resnorm: a workgroup owns one 16-row block x 16 columns over the
+// whole K range; its eight waves take K / 8 each (all of a wave's fragments
+// requested at once, two accumulators so consecutive MFMAs do not wait on each
+// other), summed through LDS in wave order.  Wave 0 then adds the residual,
+// writes it back, and writes the next product's unnormalised input and the
+// row's partial sum of squares over its 16 columns.
+struct ResP {
+  const uint16_t* A;
+  const uint16_t* W;
+  int M, N, K;
+  float* h;
+  int ldh;
+  const float* gain;
+  uint16_t* xb;
+  float* ss;
+  Prefetch pf;
+};
+
+constexpr bool kResXcdMajor = true;
+
+template <int SPW>
+__global__ __launch_bounds__(512) void k_chunk_res(ResP p) {
+  __shared__ float red[8][4][64];
+  if (prefetch_layer(p.pf)) return;
+  // column block: with kResXcdMajor the blocks of one XCD (linear id % 8) are
+  // adjacent, so the residual's and the input's lines are written by one L2
+  const int bx = kResXcdMajor && !(gridDim.x & 7) ? (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  const int rb = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int KS = p.K >> 5, sb = w * SPW;
+  const int nsteps = max(0, min(SPW, KS - sb));  // the last waves may hold fewer k-steps, or none
+  const int n = bx * 16 + col;
+  const u32x4_t* Wv = (const u32x4_t*)p.W + lane;
+  const u32x4_t* Av = (const u32x4_t*)p.A + lane;
+  u32x4_t wv[SPW], av[SPW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const int ks = min(sb + s, KS - 1);  // clamped; steps past the range are masked below
+    wv[s] = Wv[((long)bx * KS + ks) * 64];
+    av[s] = Av[((long)rb * KS + ks) * 64];
+  }
+  // the residual values this block updates, requested with the fragments
+  float hold[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) hold[e] = p.h[(long)min(rb * 16 + grp * 4 + e, p.M - 1) * p.ldh + n];
+  // keep every load ahead of the first MFMA (the scheduler would otherwise
+  // interleave them, a few in flight at a time)
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const u32x4_t a4 = s < nsteps ? av[s] : u32x4_t{0, 0, 0, 0};
+    acc[s & 1] = mfma16x16x32(as_bf16x8(a4), as_bf16x8(wv[s]), acc[s & 1]);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) red[w][e][lane] = acc[0][e] + acc[1][e];
+  __syncthreads();
+  if (w) return;
+  const float g1 = p.gain ? 1.0f + p.gain[n] : 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float v = red[0][e][lane];
+#pragma unroll
+    for (int ww = 1; ww < 8; ++ww) v += red[ww][e][lane];
+    const int m = rb * 16 + grp * 4 + e;
+    const float x = hold[e] + v;
+    if (m < p.M) p.h[(long)m * p.ldh + n] = x;
+    if (p.gain) {
+      // sum of x^2 over the 16 columns (the 16 lanes of this lane's row of the
+      // wave; every lane ends with the same bits)
+      float q = x * x;
+      q += dpp_mov<0xB1>(q);
+      q += dpp_mov<0x4E>(q);
+      q += dpp_mov<0x141>(q);
+      q += dpp_mov<0x140>(q);
+      if (m < p.M) {
+        p.xb[frag_idx(m, n, p.N)] = f2bf(x * g1);
+        if (col == 0) p.ss[(((int)blockIdx.x & 7) * 64 + m) * (int)(gridDim.x >> 3) + (blockIdx.x >> 3)] = q;
+      }
+    }
+  }
+}
+
+size_t gemm_chunk_resnorm_group_bytes(int N, int K) {
+  const int gx = N / 16;
+  if (N % 16 || gx % 8) return 0;
+  const size_t g = (size_t)16 * K * 2 * (kResXcdMajor ? gx / 8 : 1);
+  return g & (g - 1) ? 0 : g;
+}
+
+hipError_t gemm_chunk_resnorm(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, float* h, int ldh,
+                              const float* gain, uint16_t* xb, float* ss, hipStream_t s, const Prefetch* prefetch) {
+  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  if (M > 64 || N % 128 || N > 1024 || K % 32 || K > 4096 || !h || (gain && (!xb || !ss))) return hipErrorInvalidValue;
+  const Prefetch pf = prefetch ? *prefetch : Prefetch{};
+  if (pf.blocks < 0 || pf.blocks > 1024 || (pf.blocks && !pf.sink)) return hipErrorInvalidValue;
+  ResP p{Af, Wf, M, N, K, h, ldh, gain, xb, ss, pf};
+  const int rbs = (M + 15) / 16, wgs = N / 16 * rbs;
+  const dim3 grid(N / 16, rbs, prefetch_depth(wgs, pf.blocks));
+  // k-steps per wave: the fewest of 1, 2, 4, 8, 16 that cover an eighth of K
+  const int spw = (K / 32 + 7) / 8;
+  if (spw <= 1) hipLaunchKernelGGL(k_chunk_res<1>, grid, dim3(512), 0, s, p);
+  else if (spw <= 2) hipLaunchKernelGGL(k_chunk_res<2>, grid, dim3(512), 0, s, p);
+  else if (spw <= 4) hipLaunchKernelGGL(k_chunk_res<4>, grid, dim3(512), 0, s, p);
+  else if (spw <= 8) hipLaunchKernelGGL(k_chunk_res<8>, grid, dim3(512), 0, s, p);
+  else hipLaunchKernelGGL(k_chunk_res<16>, grid, dim3(512), 0, s, p);
+  return hipGetLastError();
 }
 
 size_t gemm_chunk_group_bytes(int M, int N, int K, int kind, int splits) {

@@ -66,6 +66,14 @@ struct Epilogue {
   const float* beta = nullptr;
   int32_t* acc_out = nullptr;  // optional raw int32 accumulators [M][N]
   int out_frag = 0;  // bf16 output in fragment layout (frag_idx with K = ldo) instead of rows
+  // RMSNorm folded into a product (gemm_chunk, one K chunk): when rss is set,
+  // output row m is first scaled by 1 / sqrt(S_m / rdim + reps), S_m the sum
+  // of row m's nss partial sums of squares in rss as gemm_chunk_resnorm lays
+  // them out (nss = 8, 16, 32 or 64): the norm factor of the row the
+  // unnormalised A operand came from
+  const float* rss = nullptr;
+  int nss = 0, rdim = 0;
+  float reps = 0.f;
 };
 
 // C = A[M,K] W[N,K]^T, bf16 operands, fp32 accumulation on MFMA, for any row
@@ -93,6 +101,21 @@ int gemm_chunk_splits(int K, int splits);
 // of later kernels, as for the row kernels.
 hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, const Epilogue& epi,
                       int splits, float* ws, hipStream_t s, const Prefetch* prefetch = nullptr);
+// Residual-updating product of at most 64 rows with RMSNorm's inputs for the
+// next product: h[m][n] += (A W^T)[m][n] for m < M (fp32 rows, ldh apart), and,
+// when gain is set, xb = bf16(h_new * (1 + gain[n])) in the fragment layout
+// (K = N) and, per row, N / 16 partial sums of h_new^2 over 16 columns each
+// in ss (N / 16 * 64 floats, laid out [x][64][N / 128] by the XCD x whose
+// workgroups wrote them, so every line of ss, h and xb is written from one
+// L2); the next product scales its rows by the norm factor (Epilogue::rss).
+// A workgroup owns 16 rows x 16 columns over the whole K range (eight waves
+// split K, summed in wave order), so each output has one owner and the
+// results never depend on timing.  A and W in the fragment layout; M <= 64,
+// N % 128 == 0, N <= 1024, K % 32 == 0, K <= 4096.
+hipError_t gemm_chunk_resnorm(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, float* h, int ldh,
+                              const float* gain, uint16_t* xb, float* ss, hipStream_t s, const Prefetch* prefetch);
+// The Prefetch `group` for the weights of gemm_chunk_resnorm (0: ungrouped).
+size_t gemm_chunk_resnorm_group_bytes(int N, int K);
 // Bytes of fragment-layout weight that one column group of gemm_chunk reads
 // (the workgroup grid's x index), or 0 when the groups do not map to XCDs
 // round robin (grid width not a multiple of 8): the `group` of a Prefetch.

@@ -284,6 +284,10 @@ struct vla_model {
   int64_t plan_kvrows = 0;                 // largest batch x padded prefix length seen
   // persistent solver step (fused.hip): per-layer gains in one array, barrier words, error word
   bool fused = false;
+  // The chunk-sized chain folds the expert's norms into its products unless the
+  // model was created with VLA_FOLD=0 in the environment (then it runs them as
+  // row kernels, in the persistent step's summation order)
+  bool fold = true;
   float* egains = nullptr;
   unsigned* fbar = nullptr;
   unsigned* ferr = nullptr;
@@ -703,6 +707,10 @@ extern "C" vla_status vla_model_create(const vla_model_config* cfg, const vla_we
   vla_model* m = new vla_model();
   m->cfg = *cfg;
   m->f32 = cfg->precision == VLA_F32;
+  {
+    const char* fe = getenv("VLA_FOLD");
+    m->fold = !(fe && fe[0] == '0');
+  }
   m->w2a8 = cfg->precision == VLA_W2A8_BF16;
   m->joint = cfg->attn_mode == VLA_ATTN_JOINT;
   (void)hipGetDevice(&m->device);
@@ -769,6 +777,7 @@ struct WS {
   void* eattn;      // [erows][Hq_e hd_e]
   void* emlp;       // [erows][F_e]
   float* epart;     // split-K partials of the expert
+  float* ess;       // folded norms: partial sums of squares of the residual [d_e / 16][64]
   unsigned* sink;   // 64 words for the prefetch kernel
   size_t total;
   // byte sizes of the chunk buffers (bounds of the persistent step's accesses)
@@ -878,6 +887,7 @@ static WS plan(const vla_model* m, int64_t rows, int64_t erows, int64_t kvrows, 
   // split partials [S][erows][N] of the expert GEMMs
   w.n_epart = (size_t)expert_part_floats(c, erows) * 4;
   w.epart = (float*)take(w.n_epart);
+  w.ess = (float*)take((size_t)std::max(1, c.d_e / 16) * 64 * 4);
   w.sink = (unsigned*)take(256);
   w.total = off;
   return w;
@@ -1406,10 +1416,27 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
   // Weight ranges are read XCD by XCD, in the column groups of the GEMM that
   // consumes them, so each lands in the L2 its consumer's workgroups read from.
   const size_t g_qkv = gemm_chunk_group_bytes(M, qkve, c.d_e, EPI_QKV, 1);
-  const size_t g_o = gemm_chunk_group_bytes(M, c.d_e, qe, EPI_PARTIAL, S_o);
+  const size_t g_o0 = gemm_chunk_group_bytes(M, c.d_e, qe, EPI_PARTIAL, S_o);
   const size_t g_q = gemm_chunk_group_bytes(M, qe, c.d_e, EPI_STORE, 1);
   const size_t g_gu = gemm_chunk_group_bytes(M, 2 * c.F_e, c.d_e, EPI_GEGLU, 1);
-  const size_t g_d = gemm_chunk_group_bytes(M, c.d_e, c.F_e, EPI_PARTIAL, S_d);
+  const size_t g_d0 = gemm_chunk_group_bytes(M, c.d_e, c.F_e, EPI_PARTIAL, S_d);
+  // Folded norms (chunk path): the O, cross O and down products add their sums
+  // to the residual themselves and write the next product's input unnormalised,
+  // bf16(h (1 + g)), with each row's sums of squares over 16-column blocks; the
+  // next product scales its output rows by the norm factor those sums give.
+  // Three row kernels and their launch gaps less per layer.
+  int d_used = 0, d_chunk = 0;
+  gemm_chunk_plan(c.d_e, 1, &d_used, &d_chunk);
+  auto res_k = [](int K) { return K % 32 == 0 && K <= 4096; };
+  const int d8 = c.d_e / 128;  // column groups of 16 per XCD in the residual products
+  const bool fold = m->fold && small && d_used == 1 && c.d_e % 128 == 0 && (d8 == 1 || d8 == 2 || d8 == 4 || d8 == 8) &&
+                    res_k(qe) && res_k(c.F_e);
+  const size_t g_o = fold ? gemm_chunk_resnorm_group_bytes(c.d_e, qe) : g_o0;
+  const size_t g_d = fold ? gemm_chunk_resnorm_group_bytes(c.d_e, c.F_e) : g_d0;
+  auto scaled = [&](Epilogue ep) {
+    ep.rss = w.ess; ep.nss = c.d_e / 16; ep.rdim = c.d_e; ep.reps = eps;
+    return ep;
+  };
   auto pfr = [&](const void* p, size_t bytes, size_t group, const void* p2, size_t bytes2, size_t group2, int blocks) {
     Prefetch f;
     if (!small) return f;
@@ -1481,7 +1508,8 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
           if (small) return gemm_chunk((const uint16_t*)A, (const uint16_t*)W, M, N, K, ep, splits, w.epart, s, pf);
           return gemm_frag((const uint16_t*)A, (const uint16_t*)W, M, N, K, ep, 0, w.epart, s);
         };
-        K_TRY(mm(u, c.d_e, L.wqkv, qkve, c.d_e, qkv_e, 1), "qkv_s");
+        // layer 0 reads the normalised rows of the step kernel, later layers the folded input
+        K_TRY(mm(u, c.d_e, L.wqkv, qkve, c.d_e, fold && e > 0 ? scaled(qkv_e) : qkv_e, 1), "qkv_s");
         if (m->joint) {
           // one attention over the chunk and prefix layer e, then the MLP
           sa.pf = pfr(L.wos, b_o, g_o, L.wgu, b_gu, g_gu, 192);
@@ -1490,8 +1518,13 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
             for (int rep = 0; rep < ps.reps(); ++rep)
               K_TRY(attention_chunk(sa, s), "joint attn");
           }
-          K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
-          K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
+          if (fold) {
+            K_TRY(gemm_chunk_resnorm((const uint16_t*)w.eattn, (const uint16_t*)L.wos, M, c.d_e, qe, w.E, c.d_e, L.a3,
+                                     (uint16_t*)w.eu, w.ess, s, nullptr), "o_s");
+          } else {
+            K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
+            K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
+          }
         } else {
           sa.pf = pfr(L.wos, b_o, g_o, L.wqc, b_q, g_q, 192);
           {
@@ -1499,32 +1532,50 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
             for (int rep = 0; rep < ps.reps(); ++rep)
               K_TRY(attention_chunk(sa, s), "self attn");
           }
-          K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
           const Prefetch pf_kv = pfr(B == 1 ? ca.k : nullptr, B == 1 ? layer_kv : 0, 0, nullptr, 0, 0, 64);
-          K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr, &pf_kv),
-                "norm");
-          K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, epi_store(w.eq, qe, 0), 1), "q_c");
+          if (fold) {
+            K_TRY(gemm_chunk_resnorm((const uint16_t*)w.eattn, (const uint16_t*)L.wos, M, c.d_e, qe, w.E, c.d_e, L.a2,
+                                     (uint16_t*)w.eu, w.ess, s, &pf_kv), "o_s");
+          } else {
+            K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
+            K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr,
+                             &pf_kv), "norm");
+          }
+          const Epilogue qc_e = epi_store(w.eq, qe, 0);
+          K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, fold ? scaled(qc_e) : qc_e, 1), "q_c");
           ca.pf = pfr(L.woc, b_o, g_o, L.wgu, b_gu, g_gu, 192);
           {
             ProbeScope ps(m, VLA_PROBE_EXPERT_CROSS_ATTN, s);
             for (int rep = 0; rep < ps.reps(); ++rep)
               K_TRY(attention_chunk(ca, s), "cross attn");
           }
-          K_TRY(mm(w.eattn, qe, L.woc, c.d_e, qe, pe, S_o), "o_c");
-          K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
+          if (fold) {
+            K_TRY(gemm_chunk_resnorm((const uint16_t*)w.eattn, (const uint16_t*)L.woc, M, c.d_e, qe, w.E, c.d_e, L.a3,
+                                     (uint16_t*)w.eu, w.ess, s, nullptr), "o_c");
+          } else {
+            K_TRY(mm(w.eattn, qe, L.woc, c.d_e, qe, pe, S_o), "o_c");
+            K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
+          }
         }
         Epilogue g = epi_store(w.emlp, c.F_e, 0);
         g.kind = EPI_GEGLU;
         g.out_frag = fr;
         const Prefetch pf_d = pfr(L.wd, b_d, g_d, nullptr, 0, 0, 192);
-        K_TRY(mm(u, c.d_e, L.wgu, 2 * c.F_e, c.d_e, g, 1, &pf_d), "gate/up");
-        K_TRY(mm(w.emlp, c.F_e, L.wd, c.d_e, c.F_e, pe, S_d), "down");
+        K_TRY(mm(u, c.d_e, L.wgu, 2 * c.F_e, c.d_e, fold ? scaled(g) : g, 1, &pf_d), "gate/up");
         // next layer's QKV weights (and, joint, its cache block)
         const void* next_kv = m->joint && B == 1 ? (const char*)ca.k + (size_t)layer_stride * es : nullptr;
         const Prefetch pf_next =
             e + 1 < c.L_e ? pfr(m->el[e + 1].wqkv, b_qkv, g_qkv, next_kv, layer_kv, 0, 192) : Prefetch{};
-        K_TRY(resid_norm(w.E, c.d_e, w.epart, S_d, M, c.d_e, e + 1 < c.L_e ? m->el[e + 1].a1 : m->w_ef, eps,
-                         e + 1 < c.L_e ? w.eu : nullptr, 0, c.d_e, nullptr, nullptr, s, fr, &pf_next), "norm");
+        if (fold) {
+          // after the last layer only the residual: the step kernel applies the final norm
+          K_TRY(gemm_chunk_resnorm((const uint16_t*)w.emlp, (const uint16_t*)L.wd, M, c.d_e, c.F_e, w.E, c.d_e,
+                                   e + 1 < c.L_e ? m->el[e + 1].a1 : nullptr, (uint16_t*)w.eu, w.ess, s, &pf_next),
+                "down");
+        } else {
+          K_TRY(mm(w.emlp, c.F_e, L.wd, c.d_e, c.F_e, pe, S_d), "down");
+          K_TRY(resid_norm(w.E, c.d_e, w.epart, S_d, M, c.d_e, e + 1 < c.L_e ? m->el[e + 1].a1 : m->w_ef, eps,
+                           e + 1 < c.L_e ? w.eu : nullptr, 0, c.d_e, nullptr, nullptr, s, fr, &pf_next), "norm");
+        }
       }
     }
     K_TRY(rows(k, k + 1 < steps ? k + 1 : -1), "head");

@@ -49,11 +49,22 @@ def host_inputs(cfg, seed):
     return w, b, synth.make_prefix(cfg, seed), synth.make_noise(cfg, seed)
 
 
-def build_model(cfg, weights, betas):
+def build_model(cfg, weights, betas, env=None):
+    """A model on the GPU; `env` ({name: value}) is set in the environment while it is created (the
+    library reads VLA_FUSED and VLA_FOLD there)."""
     from prefix_cache_flow_amd import vla
-    tensors = vla.upload_weights(cfg.to_dict(), ordered(cfg, weights))
-    model = vla.vla_model_create(cfg.to_dict(), tensors, ordered_betas(cfg, betas))
-    del tensors
+    old = {k: os.environ.get(k) for k in (env or {})}
+    os.environ.update(env or {})
+    try:
+        tensors = vla.upload_weights(cfg.to_dict(), ordered(cfg, weights))
+        model = vla.vla_model_create(cfg.to_dict(), tensors, ordered_betas(cfg, betas))
+        del tensors
+    finally:
+        for k, v in old.items():
+            if v is None:
+                del os.environ[k]
+            else:
+                os.environ[k] = v
     return model
 
 

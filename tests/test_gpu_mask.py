@@ -7,7 +7,6 @@ padding's content must not change a single bit of the outputs (the library
 zeroes padded rows and gives padded keys weight 0), and each observation must
 match the same observation encoded alone at its own length.
 """
-import os
 
 import numpy as np
 import pytest
@@ -118,19 +117,12 @@ def test_padded_observation_matches_its_own_length_and_full_length_is_unmasked()
 
 
 def test_ragged_batch_on_the_persistent_step():
-    """The opt-in persistent solver step masks the cached keys like the kernel chain: same bits."""
+    """The opt-in persistent solver step masks the cached keys like the kernel chain (with the expert's
+    norms as row kernels, the persistent step's summation order): same bits."""
     cfg, lengths = RAGGED[1][0], RAGGED[1][1]
     w, b, z, x0 = _inputs(cfg, 5, lengths, 2.0)
-    old = os.environ.get("VLA_FUSED")
-    os.environ["VLA_FUSED"] = "1"
-    try:
-        fused_model = build_model(cfg, w, b)
-    finally:
-        if old is None:
-            del os.environ["VLA_FUSED"]
-        else:
-            os.environ["VLA_FUSED"] = old
-    chain_model = build_model(cfg, w, b)
+    fused_model = build_model(cfg, w, b, env={"VLA_FUSED": "1"})
+    chain_model = build_model(cfg, w, b, env={"VLA_FOLD": "0"})
     f, _ = _run(cfg, fused_model, z, x0, lengths)
     c, _ = _run(cfg, chain_model, z, x0, lengths)
     np.testing.assert_array_equal(f.view(np.int32), c.view(np.int32))
