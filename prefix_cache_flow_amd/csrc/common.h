@@ -215,6 +215,7 @@ __device__ __forceinline__ void prefetch_share(const Prefetch& f, int L, int fir
   };
   range(f.p, f.bytes, f.group);
   range(f.p2, f.bytes2, f.group2);
+  range(f.p3, f.bytes3, f.group3);
   if (x == 0x9E3779B9u) f.sink[L & 63] = x;
 }
 

@@ -19,6 +19,8 @@ struct Prefetch {
   size_t bytes = 0, group = 0;
   const void* p2 = nullptr;
   size_t bytes2 = 0, group2 = 0;
+  const void* p3 = nullptr;
+  size_t bytes3 = 0, group3 = 0;
   unsigned* sink = nullptr;  // 64 words, written only for an impossible value
   int blocks = 0;
 };

@@ -1408,7 +1408,9 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
   // workgroups of their own, so they carry most of it: self attention reads
   // the O and cross-query weights, cross attention the cross O and gate/up
   // weights.  The gate/up GEMM reads the down weights, and the norms the
-  // layer's cache block and the next layer's QKV weights.  Only for the
+  // layer's cache block and the next layer's QKV weights; with the norms folded
+  // into the products, the cross query reads the cache block and the gate/up
+  // GEMM the next layer's QKV weights too.  Only for the
   // fragment path (batch-1 sized chunks).
   const size_t b_qkv = (size_t)qkve * c.d_e * es, b_o = (size_t)c.d_e * qe * es, b_q = (size_t)qe * c.d_e * es;
   const size_t b_gu = (size_t)2 * c.F_e * c.d_e * es, b_d = (size_t)c.d_e * c.F_e * es;
@@ -1534,15 +1536,17 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
           }
           const Prefetch pf_kv = pfr(B == 1 ? ca.k : nullptr, B == 1 ? layer_kv : 0, 0, nullptr, 0, 0, 64);
           if (fold) {
+            // the cache block goes with the cross query below: workgroups of this product hold too many
+            // registers for a prefetch workgroup to share their CU, so one would run after them
             K_TRY(gemm_chunk_resnorm((const uint16_t*)w.eattn, (const uint16_t*)L.wos, M, c.d_e, qe, w.E, c.d_e, L.a2,
-                                     (uint16_t*)w.eu, w.ess, s, &pf_kv), "o_s");
+                                     (uint16_t*)w.eu, w.ess, s, nullptr), "o_s");
           } else {
             K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
             K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr,
                              &pf_kv), "norm");
           }
           const Epilogue qc_e = epi_store(w.eq, qe, 0);
-          K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, fold ? scaled(qc_e) : qc_e, 1), "q_c");
+          K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, fold ? scaled(qc_e) : qc_e, 1, fold ? &pf_kv : nullptr), "q_c");
           ca.pf = pfr(L.woc, b_o, g_o, L.wgu, b_gu, g_gu, 192);
           {
             ProbeScope ps(m, VLA_PROBE_EXPERT_CROSS_ATTN, s);
@@ -1560,16 +1564,21 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
         Epilogue g = epi_store(w.emlp, c.F_e, 0);
         g.kind = EPI_GEGLU;
         g.out_frag = fr;
-        const Prefetch pf_d = pfr(L.wd, b_d, g_d, nullptr, 0, 0, 192);
-        K_TRY(mm(u, c.d_e, L.wgu, 2 * c.F_e, c.d_e, fold ? scaled(g) : g, 1, &pf_d), "gate/up");
         // next layer's QKV weights (and, joint, its cache block)
         const void* next_kv = m->joint && B == 1 ? (const char*)ca.k + (size_t)layer_stride * es : nullptr;
         const Prefetch pf_next =
             e + 1 < c.L_e ? pfr(m->el[e + 1].wqkv, b_qkv, g_qkv, next_kv, layer_kv, 0, 192) : Prefetch{};
+        Prefetch pf_d = pfr(L.wd, b_d, g_d, nullptr, 0, 0, 192);
+        if (fold && e + 1 < c.L_e) {
+          // folded: the gate/up product also reads what the down product would (see the cross query above)
+          pf_d.p2 = pf_next.p; pf_d.bytes2 = pf_next.bytes; pf_d.group2 = pf_next.group;
+          pf_d.p3 = pf_next.p2; pf_d.bytes3 = pf_next.bytes2; pf_d.group3 = pf_next.group2;
+        }
+        K_TRY(mm(u, c.d_e, L.wgu, 2 * c.F_e, c.d_e, fold ? scaled(g) : g, 1, &pf_d), "gate/up");
         if (fold) {
           // after the last layer only the residual: the step kernel applies the final norm
           K_TRY(gemm_chunk_resnorm((const uint16_t*)w.emlp, (const uint16_t*)L.wd, M, c.d_e, c.F_e, w.E, c.d_e,
-                                   e + 1 < c.L_e ? m->el[e + 1].a1 : nullptr, (uint16_t*)w.eu, w.ess, s, &pf_next),
+                                   e + 1 < c.L_e ? m->el[e + 1].a1 : nullptr, (uint16_t*)w.eu, w.ess, s, nullptr),
                 "down");
         } else {
           K_TRY(mm(w.emlp, c.F_e, L.wd, c.d_e, c.F_e, pe, S_d), "down");
