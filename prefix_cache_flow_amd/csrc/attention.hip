@@ -26,6 +26,13 @@
 
 namespace vla {
 
+// A workgroup-uniform int from device memory that no kernel writes while this
+// one runs, through the scalar cache: a vector load here would make the
+// compiler wait for every load issued before it (loads retire in order).
+__device__ __forceinline__ int uniform_ld(const int* p, int i) {
+  return *((const __attribute__((address_space(4))) int*)(uintptr_t)p + i);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void k_attn16(AttnArgs a) {
   constexpr int LDK = D + 8;   // K tile row stride (bf16)
@@ -60,7 +67,7 @@ __global__ __launch_bounds__(256) void k_attn16(AttnArgs a) {
   // finite start: a wave whose keys are all padding then adds exp2(-inf) = 0
   float mrun = -3.0e38f, lrun = 0.f;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
-  const int nk = a.klen ? min(a.klen[b], a.Nk) : a.Nk;  // visible keys of this observation
+  const int nk = a.klen ? min(uniform_ld(a.klen, b), a.Nk) : a.Nk;  // visible keys of this observation
 
   uint16_t* sK = lds + w * WAVE_LDS;
   uint16_t* sVt = sK + 32 * LDK;
@@ -225,6 +232,107 @@ hipError_t attention_bf16(const AttnArgs& a, hipStream_t s) {
   }
 }
 
+// One 32-key tile of the chunk-style attention for one wave: the transposed
+// scores S^T = K Q^T of its 16 queries (keys kt .. kt + 31, those at or past nk
+// masked to -inf), the online-softmax update with a lazily moved reference max
+// (mrun, lrun), and O^T += V^T P^T with P^T taken from the score registers.
+// k holds the tile's 2 * D / 32 key fragments; vf(i) returns value fragment i of
+// D / 16 (from registers or from LDS).
+template <int D, class VF>
+__device__ __forceinline__ void attn_tile(const u32x4_t (&k)[D / 16], VF vf, const u32x4_t (&qf)[D / 32], int kt,
+                                          int nk, int grp, float sl2, float& mrun, float& lrun, f32x4_t (&o)[D / 16]) {
+  constexpr int KS = D / 32, VS = D / 16;
+  f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    s0 = mfma16x16x32(as_bf16x8(k[s]), as_bf16x8(qf[s]), s0);
+    s1 = mfma16x16x32(as_bf16x8(k[KS + s]), as_bf16x8(qf[s]), s1);
+  }
+  float mt = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ka = kt + grp * 4 + i;
+    s0[i] = ka < nk ? s0[i] * sl2 : -INFINITY;
+    s1[i] = ka + 16 < nk ? s1[i] * sl2 : -INFINITY;
+    mt = fmaxf(mt, fmaxf(s0[i], s1[i]));
+  }
+  mt = group4_max(mt);
+  // the reference max moves (and O, l are rescaled) only when some query's
+  // max grew by more than 8 (log2 units); weights stay below 2^8
+  const bool grow = mt > mrun + 8.f;
+  if (__builtin_amdgcn_ballot_w64(grow)) {
+    const float mnew = grow ? mt : mrun;
+    const float alpha = fast_exp2(mrun - mnew);
+#pragma unroll
+    for (int t2 = 0; t2 < VS; ++t2)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[t2][e] *= alpha;
+    lrun *= alpha;
+    mrun = mnew;
+  }
+  float ls = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s0[i] = fast_exp2(s0[i] - mrun);
+    s1[i] = fast_exp2(s1[i] - mrun);
+    ls += s0[i] + s1[i];
+  }
+  lrun += group4_sum(ls);
+  const u32x4_t pw = {pack_bf2(s0[0], s0[1]), pack_bf2(s0[2], s0[3]), pack_bf2(s1[0], s1[1]), pack_bf2(s1[2], s1[3])};
+  const bf16x8_t pf = as_bf16x8(pw);
+#pragma unroll
+  for (int t2 = 0; t2 < VS; ++t2) o[t2] = mfma16x16x32(as_bf16x8(vf(t2)), pf, o[t2]);
+}
+
+// Merge of the four waves' softmax states (max, sum, unnormalised O^T) of one
+// workgroup's 16 rows through LDS in wave order, normalisation and the bf16
+// store (row layout or the fragment layout of the next product).  obuf holds
+// 4 x 16 rows of D + 4 floats; ends with every wave done with it.
+template <int D>
+__device__ __forceinline__ void attn_merge_store(const AttnArgs& a, float (*mbuf)[16], float (*lbuf)[16], float* obuf,
+                                                 float mrun, float lrun, const f32x4_t (&o)[D / 16]) {
+  constexpr int VS = D / 16, LDO = D + 4;
+  const int G = a.Hq / a.Hkv, R = G * a.Nq;
+  const int g = blockIdx.y % a.Hkv, b = blockIdx.y / a.Hkv;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  if (grp == 0) {
+    mbuf[w][col] = mrun;
+    lbuf[w][col] = lrun;
+  }
+#pragma unroll
+  for (int t2 = 0; t2 < VS; ++t2) *(f32x4_t*)&obuf[(w * 16 + col) * LDO + t2 * 16 + grp * 4] = o[t2];
+  __syncthreads();
+  const int qq = threadIdx.x & 15, d0 = (threadIdx.x >> 4) * (D / 16);
+  const int r = blockIdx.x * 16 + qq;
+  if (r >= R) return;
+  const int jl = r / a.Nq, q = r - jl * a.Nq, j = g * G + jl;
+  float M = mbuf[0][qq];
+#pragma unroll
+  for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, mbuf[ww][qq]);
+  float ew[4], L = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) {
+    ew[ww] = fast_exp2(mbuf[ww][qq] - M);
+    L += ew[ww] * lbuf[ww][qq];
+  }
+  const float inv = __builtin_amdgcn_rcpf(L);
+  const long row = (long)b * a.Nq + q;
+#pragma unroll
+  for (int d = d0; d < d0 + D / 16; d += 4) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const f32x4_t x = *(const f32x4_t*)&obuf[(ww * 16 + qq) * LDO + d];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += ew[ww] * x[e];
+    }
+    const u32x2_t pk = {pack_bf2(acc[0] * inv, acc[1] * inv), pack_bf2(acc[2] * inv, acc[3] * inv)};
+    const long oi = a.o_frag ? frag_idx((int)row, j * D + d, a.Hq * D) : b * a.o_bs + (long)q * a.o_rs + (long)j * D + d;
+    *(u32x2_t*)((bf16_t*)a.o + oi) = pk;
+  }
+}
+
 // ------------------------------------------------------------------ chunk queries
 // attention_chunk: the same attention for short query sets (the action chunk)
 // with K and V stored in the MFMA operand orders of common.h (K in frag_idx,
@@ -250,8 +358,8 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
   const int g = blockIdx.y % a.Hkv, b = blockIdx.y / a.Hkv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  int r = min((int)blockIdx.x * 16 + col, R - 1);  // clamped rows are computed, never stored
-  int jl = r / a.Nq, q = r - jl * a.Nq, j = g * G + jl;
+  const int r = min((int)blockIdx.x * 16 + col, R - 1);  // clamped rows are computed, never stored
+  const int jl = r / a.Nq, q = r - jl * a.Nq, j = g * G + jl;
   const bf16_t* Qp = (const bf16_t*)a.q + b * a.q_bs + j * a.q_hs + (long)q * a.q_rs;
   const u32x4_t* Kf = (const u32x4_t*)((const bf16_t*)a.k + b * a.k_bs + g * a.k_hs) + lane;
   const u32x4_t* Vf = (const u32x4_t*)((const bf16_t*)a.v + b * a.v_bs + g * a.v_hs) + lane;
@@ -287,52 +395,13 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
   float mrun = -3.0e38f, lrun = 0.f;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
   // visible keys of this observation in each source (key padding)
-  const int nk1 = a.klen ? min(a.klen[b], a.Nk) : a.Nk;
-  const int nk2 = a.klen2 ? min(a.klen2[b], a.Nk2) : a.Nk2;
+  const int nk1 = a.klen ? min(uniform_ld(a.klen, b), a.Nk) : a.Nk;
+  const int nk2 = a.klen2 ? min(uniform_ld(a.klen2, b), a.Nk2) : a.Nk2;
 
   auto consume = [&](const Tile& t, int tl) {
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      s0 = mfma16x16x32(as_bf16x8(t.k[s]), as_bf16x8(qf[s]), s0);
-      s1 = mfma16x16x32(as_bf16x8(t.k[KS + s]), as_bf16x8(qf[s]), s1);
-    }
     const bool second = tl >= TA;
-    const int kt = (second ? tl - TA : tl) * 32, nk = second ? nk2 : nk1;
-    float mt = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ka = kt + grp * 4 + i;
-      s0[i] = ka < nk ? s0[i] * sl2 : -INFINITY;
-      s1[i] = ka + 16 < nk ? s1[i] * sl2 : -INFINITY;
-      mt = fmaxf(mt, fmaxf(s0[i], s1[i]));
-    }
-    mt = group4_max(mt);
-    // the reference max moves (and O, l are rescaled) only when some query's
-    // max grew by more than 8 (log2 units); weights stay below 2^8
-    const bool grow = mt > mrun + 8.f;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float mnew = grow ? mt : mrun;
-      const float alpha = fast_exp2(mrun - mnew);
-#pragma unroll
-      for (int t2 = 0; t2 < VS; ++t2)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[t2][e] *= alpha;
-      lrun *= alpha;
-      mrun = mnew;
-    }
-    float ls = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s0[i] = fast_exp2(s0[i] - mrun);
-      s1[i] = fast_exp2(s1[i] - mrun);
-      ls += s0[i] + s1[i];
-    }
-    lrun += group4_sum(ls);
-    const u32x4_t pw = {pack_bf2(s0[0], s0[1]), pack_bf2(s0[2], s0[3]), pack_bf2(s1[0], s1[1]), pack_bf2(s1[2], s1[3])};
-    const bf16x8_t pf = as_bf16x8(pw);
-#pragma unroll
-    for (int t2 = 0; t2 < VS; ++t2) o[t2] = mfma16x16x32(as_bf16x8(t.v[t2]), pf, o[t2]);
+    attn_tile<D>(t.k, [&](int i) { return t.v[i]; }, qf, (second ? tl - TA : tl) * 32, second ? nk2 : nk1, grp, sl2,
+                 mrun, lrun, o);
   };
 
   // Tile w + 4 i is consumed from ta (even i) or tb (odd i) while the next is
@@ -372,44 +441,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
       }
   }
 
-  // merge the four waves' (max, sum, unnormalised O) in wave order
-  if (grp == 0) {
-    mbuf[w][col] = mrun;
-    lbuf[w][col] = lrun;
-  }
-#pragma unroll
-  for (int t2 = 0; t2 < VS; ++t2) *(f32x4_t*)&obuf[w][col][t2 * 16 + grp * 4] = o[t2];
-  __syncthreads();
-  const int qq = threadIdx.x & 15, d0 = (threadIdx.x >> 4) * (D / 16);
-  r = blockIdx.x * 16 + qq;
-  if (r >= R) return;
-  jl = r / a.Nq;
-  q = r - jl * a.Nq;
-  j = g * G + jl;
-  float M = mbuf[0][qq];
-#pragma unroll
-  for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, mbuf[ww][qq]);
-  float ew[4], L = 0.f;
-#pragma unroll
-  for (int ww = 0; ww < 4; ++ww) {
-    ew[ww] = fast_exp2(mbuf[ww][qq] - M);
-    L += ew[ww] * lbuf[ww][qq];
-  }
-  const float inv = __builtin_amdgcn_rcpf(L);
-  const long row = (long)b * a.Nq + q;
-#pragma unroll
-  for (int d = d0; d < d0 + D / 16; d += 4) {
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const f32x4_t x = *(const f32x4_t*)&obuf[ww][qq][d];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += ew[ww] * x[e];
-    }
-    const u32x2_t pk = {pack_bf2(acc[0] * inv, acc[1] * inv), pack_bf2(acc[2] * inv, acc[3] * inv)};
-    const long oi = a.o_frag ? frag_idx((int)row, j * D + d, a.Hq * D) : b * a.o_bs + (long)q * a.o_rs + (long)j * D + d;
-    *(u32x2_t*)((bf16_t*)a.o + oi) = pk;
-  }
+  attn_merge_store<D>(a, mbuf, lbuf, &obuf[0][0][0], mrun, lrun, o);
 }
 
 hipError_t attention_chunk(const AttnArgs& a, hipStream_t s) {
@@ -450,8 +482,8 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
   const float* K2 = a.Nk2 ? (const float*)a.k2 + b * a.k2_bs + g * a.k2_hs : K;
   const float* V2 = a.Nk2 ? (const float*)a.v2 + b * a.v2_bs + g * a.v2_hs : V;
   float m = -INFINITY, l = 0.f;
-  const int nk1 = a.klen ? min(a.klen[b], a.Nk) : a.Nk;
-  const int nk2 = a.klen2 ? min(a.klen2[b], a.Nk2) : a.Nk2;
+  const int nk1 = a.klen ? min(uniform_ld(a.klen, b), a.Nk) : a.Nk;
+  const int nk2 = a.klen2 ? min(uniform_ld(a.klen2, b), a.Nk2) : a.Nk2;
   for (int t = 0; t < a.Nk + a.Nk2; ++t) {
     const bool second = t >= a.Nk;
     const int tt = second ? t - a.Nk : t;
