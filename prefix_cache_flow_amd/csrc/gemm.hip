@@ -647,7 +647,8 @@ hipError_t gemm_frag(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K
 
 // ------------------------------------------------------------------ chunk rows, fragment layout
 // Activations of at most 64 rows with both operands in the fragment layout of
-// common.h.  A workgroup owns 16 * NB columns, its four waves split the K
+// common.h.  A workgroup owns 16 * NB columns of every row block (or, split by
+// rows, of one row block), its four waves split the K
 // range (at most kChunkSteps k-steps each, issued at once: one memory round
 // trip covers the slice) and their partial tiles are summed through LDS in
 // wave order.  Every load of a wave is one contiguous 1 KB fragment: a weight
@@ -661,6 +662,7 @@ struct ChunkP {
   Epilogue epi;
   float* ws;
   Prefetch pf;  // read by grid layers z >= 1, if any
+  int rsplit;   // 1: one 16-row block per workgroup (grid y), K not split
 };
 
 template <int NB, int MB, int KIND, int SPW, bool RS>
@@ -688,7 +690,8 @@ __global__ __launch_bounds__(256) void k_chunk(ChunkP p) {
       }
     }
   }
-  const int bx = blockIdx.x, by = blockIdx.y;  // column group, K chunk
+  // column group, K chunk (or, split by rows, the workgroup's row block)
+  const int bx = blockIdx.x, by = p.rsplit ? 0 : blockIdx.y, rb0 = p.rsplit ? blockIdx.y : 0;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int nb0 = bx * NB;  // first 16-column block of the workgroup
@@ -696,7 +699,7 @@ __global__ __launch_bounds__(256) void k_chunk(ChunkP p) {
   const int sb = (by * p.kchunk + w * (p.kchunk >> 2)) >> 5;
   const int nsteps = max(0, min(KS - sb, p.kchunk >> 7));
   const u32x4_t* Wv = (const u32x4_t*)p.W + lane;
-  const u32x4_t* Av = (const u32x4_t*)p.A + lane;
+  const u32x4_t* Av = (const u32x4_t*)p.A + (long)rb0 * KS * 64 + lane;
 
   u32x4_t wv[SPW][NB], av[SPW][MB];
 #pragma unroll
@@ -741,6 +744,7 @@ __global__ __launch_bounds__(256) void k_chunk(ChunkP p) {
   // wave w finishes row block w: the four K ranges summed in wave order, then the epilogue
   const int rb = w;
   if (rb >= MB) return;
+  const int row0 = (rb0 + rb) * 16;
   float v[NB][4];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -751,7 +755,7 @@ __global__ __launch_bounds__(256) void k_chunk(ChunkP p) {
     }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int m = rb * 16 + grp * 4 + e;
+    const int m = row0 + grp * 4 + e;
     if (m >= p.M) continue;
     if (RS) {
       const float r = 1.0f / sqrtf(((rsp[0][m] + rsp[1][m]) + (rsp[2][m] + rsp[3][m])) / (float)p.epi.rdim + p.epi.reps);
@@ -825,13 +829,21 @@ hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int 
   if (pf.blocks < 0 || pf.blocks > 1024 || (pf.blocks && !pf.sink)) return hipErrorInvalidValue;
   const bool reduce = used > 1 && epi.kind != EPI_PARTIAL;
   const int nb = epi.kind == EPI_GEGLU && !reduce ? 2 : 1;
-  ChunkP p{Af, Wf, M, N, K, per * 32, epi, ws, pf};
-  const dim3 grid(N / (16 * nb), used, prefetch_depth(N / (16 * nb) * used, pf.blocks));
   const int kind = reduce ? EPI_PARTIAL : epi.kind;
   const int mb = (M + 15) / 16;
-  hipError_t err = mb == 1 ? launch_chunk_mb<1>(p, kind, grid, s)
-                 : mb == 2 ? launch_chunk_mb<2>(p, kind, grid, s)
-                           : launch_chunk_mb<4>(p, kind, grid, s);
+  // One 16-column block per workgroup (plain and QKV stores): with all rows
+  // each workgroup pulls four times as many activation bytes as weight bytes,
+  // so one row block per workgroup (four times the workgroups, each weight
+  // slice read once per row block, from L2) moves far fewer bytes per CU:
+  // cross query 5.7 -> about 4.8 us at 50 rows.  Two-column GeGLU workgroups
+  // already fill the chip and would read their weights four times over.
+  const int rsplit = used == 1 && mb > 1 && (kind == EPI_STORE || kind == EPI_QKV) ? 1 : 0;
+  ChunkP p{Af, Wf, M, N, K, per * 32, epi, ws, pf, rsplit};
+  const int gy = rsplit ? mb : used;
+  const dim3 grid(N / (16 * nb), gy, prefetch_depth(N / (16 * nb) * gy, pf.blocks));
+  hipError_t err = mb == 1 || rsplit ? launch_chunk_mb<1>(p, kind, grid, s)
+                 : mb == 2           ? launch_chunk_mb<2>(p, kind, grid, s)
+                                     : launch_chunk_mb<4>(p, kind, grid, s);
   if (err != hipSuccess) return err;
   if (reduce) {
     const long tot = (long)M * N / 4;
