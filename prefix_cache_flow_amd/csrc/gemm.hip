@@ -544,6 +544,95 @@ __global__ __launch_bounds__(512, 1) void k_gemm_af8(FragP p) {
   else af8_body<2, KIND, ODD>(p, sw, w, lane, tm, tn, split, nsl, kb0);
 }
 
+// Row tiles over the whole K range, for the prefix's narrow products that
+// finish in place at a few hundred rows (the fused QKV with its scatter, the
+// O projection added into the residual).  With 288-row tiles such a product
+// has 20-40 tiles, so it needs split-K partials to fill the chip, and the
+// partials then cost a reduction kernel (QKV) or a norm reading every slab
+// back (O).  Here a workgroup owns 96 x 32 outputs (six row blocks by two
+// column blocks) over the whole K range: its eight waves take K / 8 each with
+// three register sets of two k-steps (six k-steps of fragments in flight), the
+// partial tiles meet once in LDS in wave order, and waves 0-5 finish one row
+// block each: every output is stored once, by its owner.
+constexpr int kRkMB = 6, kRkNB = 2;
+constexpr int kRkSets = 3;
+constexpr int kRkMaxRows = 320;  // above this the 288-row tiles with split-K win (more rows share each weight read)
+
+template <int KIND, int PW>
+__global__ __launch_bounds__(512) void k_gemm_rk(FragP p) {
+  constexpr int MB = kRkMB, NB = kRkNB, G = 2, NG = PW / G;
+  constexpr int NS = NG < kRkSets ? NG : kRkSets;  // register sets: groups of G k-steps in flight
+  static_assert(PW % G == 0 && NG >= 1, "k-steps per wave");
+  __shared__ float red[8][MB * NB * 4][64];  // [wave][row block, column block, element][lane]
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int tn = blockIdx.x, tm = blockIdx.y;
+  const int KS = p.K >> 5, mbt = (p.M + 15) >> 4;
+  const int sb = w * PW, nst = max(0, min(PW, KS - sb));  // this wave's k-steps
+  const u32x4_t* Av = (const u32x4_t*)p.A + lane;
+  const u32x4_t* Wv = (const u32x4_t*)p.W + lane;
+  int arow[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) arow[i] = min(tm * MB + i, mbt - 1);  // clamped blocks: computed, never stored
+  u32x4_t af[NS][G][MB], wf[NS][G][NB];
+  auto load = [&](int set, int j) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int ks = min(sb + G * j + g, KS - 1);  // clamped; steps past the range are masked below
+#pragma unroll
+      for (int i = 0; i < MB; ++i) af[set][g][i] = Av[((long)arow[i] * KS + ks) * 64];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) wf[set][g][nb] = Wv[((long)(tn * NB + nb) * KS + ks) * 64];
+    }
+  };
+  f32x4_t acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[i][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto comp = [&](int set, int j) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const bool on = G * j + g < nst;
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const u32x4_t a4 = on ? af[set][g][i] : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[i][nb] = mfma16x16x32(as_bf16x8(a4), as_bf16x8(wf[set][g][nb]), acc[i][nb]);
+      }
+    }
+  };
+  // straight-line schedule (the loops unroll fully): group j in set j % NS,
+  // refilled with group j + NS once multiplied
+#pragma unroll
+  for (int j = 0; j < NS; ++j) load(j, j);
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    comp(j % NS, j);
+    if (j + NS < NG) load(j % NS, j + NS);
+  }
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[w][(i * NB + nb) * 4 + e][lane] = acc[i][nb][e];
+  __syncthreads();
+  if (w >= MB) return;
+  // wave w finishes row block w: the eight K ranges summed in wave order
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = (w * NB + nb) * 4 + e;
+      float v = red[0][idx][lane];
+#pragma unroll
+      for (int ww = 1; ww < 8; ++ww) v += red[ww][idx][lane];
+      const int m = (tm * MB + w) * 16 + grp * 4 + e, n = (tn * NB + nb) * 16 + col;
+      if (m < p.M) epi_store_t<KIND>(p.epi, m, n, v);
+    }
+}
+
 // K is cut into chunks of an even number of 64-wide slices (the kernel runs
 // slices in pairs; only the last chunk may hold an odd count); `splits` <= 0
 // asks for a count that fills the chip, about one workgroup per CU with at
@@ -604,6 +693,11 @@ static hipError_t launch_af8(const FragP& p, int kind, dim3 grid, hipStream_t s)
   return hipGetLastError();
 }
 
+bool gemm_frag_rowtile(int M, int N, int K, int kind) {
+  return (kind == EPI_QKV || kind == EPI_RESID) && M > 64 && M <= kRkMaxRows && N % (16 * kRkNB) == 0 && K % 32 == 0 &&
+         K <= 8 * 8 * 32;
+}
+
 hipError_t gemm_frag(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, const Epilogue& epi, int splits,
                      float* ws, hipStream_t s) {
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
@@ -613,6 +707,19 @@ hipError_t gemm_frag(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K
   if (kind0 == EPI_RESID && epi.ldr % 4) return hipErrorInvalidValue;
   if (epi.out_frag && kind0 != EPI_GEGLU && kind0 != EPI_CACHE) return hipErrorInvalidValue;
   if (epi.out_frag && epi.out_f32) return hipErrorInvalidValue;
+  if (splits <= 0 && gemm_frag_rowtile(M, N, K, kind0)) {
+    FragP p{Af, Wf, M, N, K, 0, 0, 0, epi, ws};
+    const dim3 grid(N / (16 * kRkNB), (M + 16 * kRkMB - 1) / (16 * kRkMB));
+    const int pw = (K / 32 + 7) / 8;  // k-steps per wave
+#define VLA_RK(KIND, PW) hipLaunchKernelGGL((k_gemm_rk<KIND, PW>), grid, dim3(512), 0, s, p)
+    if (kind0 == EPI_QKV) {
+      if (pw <= 2) VLA_RK(EPI_QKV, 2); else if (pw <= 4) VLA_RK(EPI_QKV, 4); else VLA_RK(EPI_QKV, 8);
+    } else {
+      if (pw <= 2) VLA_RK(EPI_RESID, 2); else if (pw <= 4) VLA_RK(EPI_RESID, 4); else VLA_RK(EPI_RESID, 8);
+    }
+#undef VLA_RK
+    return hipGetLastError();
+  }
   const int bn = frag_bn(M, N, K);
   int per = frag_per(M, N, K, splits, bn);
   // A product that finishes here (not partials for a row kernel) pays for every

@@ -89,6 +89,10 @@ struct Epilogue {
 hipError_t gemm_frag(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, const Epilogue& epi,
                      int splits, float* ws, hipStream_t s);
 int gemm_frag_splits(int M, int N, int K, int splits);
+// True when gemm_frag (with `splits` <= 0) runs a product of this shape and
+// kind as whole-K row tiles: no partials, every output stored once by its
+// owner (QKV and RESID kinds at a few hundred rows).
+bool gemm_frag_rowtile(int M, int N, int K, int kind);
 
 // Number of K splits gemm_chunk actually uses for a request of `splits`.
 int gemm_chunk_splits(int K, int splits);

@@ -1149,13 +1149,18 @@ static vla_status run_prefix(vla_model* m, const void* x, int x_bf16, int B, int
         }
         Epilogue pe;
         pe.kind = EPI_PARTIAL;
+        // at a few hundred rows the O projection adds into the residual itself (whole-K row tiles), and the
+        // norm reads the residual alone; otherwise it leaves split-K partials for the norm to add
+        const bool o_in_place = M > 64 && gemm_frag_rowtile(M, c.d_p, qw, EPI_RESID);
+        Epilogue oe;
+        oe.kind = EPI_RESID; oe.resid = w.h; oe.ldr = c.d_p;
         {
           ProbeScope ps(m, VLA_PROBE_PREFIX_O, s);
           for (int rep = 0; rep < ps.reps(); ++rep)
-            K_TRY(mm_frag(w.attn, P.wo, M, c.d_p, qw, pe, w.part, s), "o proj");
+            K_TRY(mm_frag(w.attn, P.wo, M, c.d_p, qw, o_in_place ? oe : pe, w.part, s), "o proj");
         }
-        K_TRY(resid_norm(w.h, c.d_p, w.part, prefix_splits(M, c.d_p, qw), M, c.d_p, P.w2, eps, w.u, 0, c.d_p, nullptr,
-                         nullptr, s, 1), "norm");
+        K_TRY(resid_norm(w.h, c.d_p, w.part, o_in_place ? 0 : prefix_splits(M, c.d_p, qw), M, c.d_p, P.w2, eps, w.u, 0,
+                         c.d_p, nullptr, nullptr, s, 1), "norm");
         Epilogue g = epi_store(w.mlp, c.F_p, 0);
         g.kind = EPI_GEGLU;
         g.out_frag = 1;
