@@ -35,8 +35,8 @@ PEAK_HBM_GBS = 8000.0
 # reads for a plain copy of known size (profiles/hbm_bytes_denoise_single_camera_bf16.md).  Valid for the
 # single-camera bf16 workload and the kernels as they were measured; None where no measurement stands.
 ATTN_KERNEL = "k_attn_chunk<256>"
-ATTN_TRAFFIC_BYTES_PER_LAUNCH = 16246932   # mean over all launches of a bench run (prefix, self, cross)
-DENOISE_TRAFFIC_BYTES_PER_STEP = 1903753045  # every kernel of one solver step (the denoise graph's nodes)
+ATTN_TRAFFIC_BYTES_PER_LAUNCH = 16246925   # mean over all launches of a bench run (prefix, self, cross)
+DENOISE_TRAFFIC_BYTES_PER_STEP = 1903578328  # every kernel of one solver step (the denoise graph's nodes)
 
 
 def parse():

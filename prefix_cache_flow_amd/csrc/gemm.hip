@@ -982,6 +982,47 @@ struct ResP {
 
 constexpr bool kResXcdMajor = true;
 
+// The end of a residual-updating product of one 16 x 16 output block: the
+// eight waves' partial sums (acc) meet in LDS in wave order, then wave 0 adds
+// the residual values (hold) and writes the new residual and, with a gain
+// (g1 = 1 + gain[n]; hold and g1 requested with the operands), the next
+// product's unnormalised input and the block's partial sums of squares.  p by
+// value: its fields stay in scalar registers across the stores.
+__device__ __forceinline__ void res_finish(const ResP p, const f32x4_t (&acc)[2], const float (&hold)[4], float g1,
+                                           float (*red)[4][64], int w, int lane, int n, int rb) {
+  const int col = lane & 15, grp = lane >> 4;
+  // where this block's sums of squares go, [x][row][column group of x] (read from the dispatch before the stores)
+  const int ss_x = ((int)blockIdx.x & 7) * 64, ss_s = (int)(gridDim.x >> 3), ss_g = (int)(blockIdx.x >> 3);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) red[w][e][lane] = acc[0][e] + acc[1][e];
+  __syncthreads();
+  if (w) return;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float v = red[0][e][lane];
+#pragma unroll
+    for (int ww = 1; ww < 8; ++ww) v += red[ww][e][lane];
+    const int m = rb * 16 + grp * 4 + e;
+    const float x = hold[e] + v;
+    if (m < p.M) p.h[(long)m * p.ldh + n] = x;
+    if (p.gain) {
+      // sum of x^2 over the 16 columns (the 16 lanes of this lane's row of the
+      // wave; every lane ends with the same bits)
+      float q = x * x;
+      q += dpp_mov<0xB1>(q);
+      q += dpp_mov<0x4E>(q);
+      q += dpp_mov<0x141>(q);
+      q += dpp_mov<0x140>(q);
+      if (m < p.M) {
+        p.xb[frag_idx(m, n, p.N)] = f2bf(x * g1);
+        if (col == 0) p.ss[(ss_x + m) * ss_s + ss_g] = q;
+      }
+    }
+  }
+}
+
+
+
 template <int SPW>
 __global__ __launch_bounds__(512) void k_chunk_res(ResP p) {
   __shared__ float red[8][4][64];
@@ -1008,6 +1049,7 @@ __global__ __launch_bounds__(512) void k_chunk_res(ResP p) {
   float hold[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) hold[e] = p.h[(long)min(rb * 16 + grp * 4 + e, p.M - 1) * p.ldh + n];
+  const float g1 = p.gain ? 1.0f + p.gain[n] : 0.f;
   // keep every load ahead of the first MFMA (the scheduler would otherwise
   // interleave them, a few in flight at a time)
   __builtin_amdgcn_sched_barrier(0);
@@ -1017,33 +1059,7 @@ __global__ __launch_bounds__(512) void k_chunk_res(ResP p) {
     const u32x4_t a4 = s < nsteps ? av[s] : u32x4_t{0, 0, 0, 0};
     acc[s & 1] = mfma16x16x32(as_bf16x8(a4), as_bf16x8(wv[s]), acc[s & 1]);
   }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) red[w][e][lane] = acc[0][e] + acc[1][e];
-  __syncthreads();
-  if (w) return;
-  const float g1 = p.gain ? 1.0f + p.gain[n] : 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float v = red[0][e][lane];
-#pragma unroll
-    for (int ww = 1; ww < 8; ++ww) v += red[ww][e][lane];
-    const int m = rb * 16 + grp * 4 + e;
-    const float x = hold[e] + v;
-    if (m < p.M) p.h[(long)m * p.ldh + n] = x;
-    if (p.gain) {
-      // sum of x^2 over the 16 columns (the 16 lanes of this lane's row of the
-      // wave; every lane ends with the same bits)
-      float q = x * x;
-      q += dpp_mov<0xB1>(q);
-      q += dpp_mov<0x4E>(q);
-      q += dpp_mov<0x141>(q);
-      q += dpp_mov<0x140>(q);
-      if (m < p.M) {
-        p.xb[frag_idx(m, n, p.N)] = f2bf(x * g1);
-        if (col == 0) p.ss[(((int)blockIdx.x & 7) * 64 + m) * (int)(gridDim.x >> 3) + (blockIdx.x >> 3)] = q;
-      }
-    }
-  }
+  res_finish(p, acc, hold, g1, red, w, lane, n, rb);
 }
 
 size_t gemm_chunk_resnorm_group_bytes(int N, int K) {
