@@ -253,16 +253,24 @@ vla_status vla_kv_cache_info(const vla_kv_cache* kv, int32_t* batch, int32_t* n_
 /* The prefix's bf16 product as a unit (the paper, §III-B: every linear of the
  * bidirectional prefix): out = A W^T in float32 accumulation on the same
  * kernels the prefix uses (both operands repacked into the MFMA fragment
- * layout first; more than 64 rows on the 288-row-tile kernels, fewer on the
- * chunk-sized kernel, K splits summed in a fixed order).  a: device bf16 bit
- * patterns [M][K], w: device bf16 [N][K], row-major.  geglu == 0: out is
- * device float32 [M][N].  geglu != 0: w's rows are gate and up interleaved in
- * blocks of 16 (rows 32 b .. 32 b + 15 are gate features 16 b .. 16 b + 15,
- * the next 16 rows their up features, as the model's gate/up weight) and out
- * is [M][N / 2] = GELU(gate) * up.  K % 64 == 0, N % 32 == 0.  Allocates
- * staging and synchronises `stream`: for tests, not a hot path. */
+ * layout first; more than 64 rows on the 288-row-tile kernels, or for the
+ * residual form at up to 320 rows the whole-K row tiles of the prefix's O
+ * projection, fewer on the chunk-sized kernel, K splits summed in a fixed
+ * order).  a: device bf16 bit patterns [M][K], w: device bf16 [N][K],
+ * row-major.  epilogue VLA_GEMM_STORE: out is device float32 [M][N].
+ * VLA_GEMM_GEGLU: w's rows are gate and up interleaved in blocks of 16 (rows
+ * 32 b .. 32 b + 15 are gate features 16 b .. 16 b + 15, the next 16 rows their
+ * up features, as the model's gate/up weight) and out is [M][N / 2] =
+ * GELU(gate) * up.  VLA_GEMM_RESIDUAL: out is device float32 [M][N], read and
+ * updated in place, out += A W^T (the residual update of the prefix's O
+ * projection).  Any other value: VLA_ERR_INVALID_ARGUMENT.  K % 64 == 0,
+ * N % 32 == 0.  Allocates staging and synchronises `stream`: for tests, not a
+ * hot path. */
+#define VLA_GEMM_STORE 0
+#define VLA_GEMM_GEGLU 1
+#define VLA_GEMM_RESIDUAL 2
 vla_status vla_gemm_bf16(const uint16_t* a, const uint16_t* w, int32_t M, int32_t N, int32_t K,
-                         int32_t geglu, float* out, void* stream);
+                         int32_t epilogue, float* out, void* stream);
 
 /* Per-row int8 quantization of Eq. 4 (the paper, §III-D): for each row m of
  * x (device float32 [M][K]) alpha[m] = max(max_j |x_mj|, 1e-5) / 127 and

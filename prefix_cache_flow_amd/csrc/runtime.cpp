@@ -1723,8 +1723,11 @@ extern "C" vla_status vla_denoise_chunk(vla_model* m, const vla_kv_cache* kv, co
 
 // ============================================================== bf16 product unit entry point
 extern "C" vla_status vla_gemm_bf16(const uint16_t* a, const uint16_t* w, int32_t M, int32_t N, int32_t K,
-                                    int32_t geglu, float* out, void* stream) {
+                                    int32_t epilogue, float* out, void* stream) {
   if (!a || !w || !out) return fail(VLA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (epilogue != VLA_GEMM_STORE && epilogue != VLA_GEMM_GEGLU && epilogue != VLA_GEMM_RESIDUAL)
+    return fail(VLA_ERR_INVALID_ARGUMENT, "epilogue must be VLA_GEMM_STORE, VLA_GEMM_GEGLU or VLA_GEMM_RESIDUAL");
+  const bool geglu = epilogue == VLA_GEMM_GEGLU;
   if (M <= 0 || N <= 0 || K <= 0) return fail(VLA_ERR_INVALID_ARGUMENT, "M, N and K must be positive");
   if (K % 64 || N % 32) return fail(VLA_ERR_UNSUPPORTED, "need K % 64 == 0 and N % 32 == 0");
   if ((int64_t)M * K > ((int64_t)1 << 31) || (int64_t)N * K > ((int64_t)1 << 31) || (int64_t)M * N > ((int64_t)1 << 29))
@@ -1753,8 +1756,15 @@ extern "C" vla_status vla_gemm_bf16(const uint16_t* a, const uint16_t* w, int32_
     return done(fail(VLA_ERR_DEVICE, "operand repack"));
   Epilogue e = epi_store(out, geglu ? N / 2 : N, 1);
   if (geglu) e.kind = EPI_GEGLU;
-  const hipError_t le = M <= 64 ? gemm_chunk(af, wf, M, N, K, e, kPrefixChunkSplits, ws, s)
-                                : gemm_frag(af, wf, M, N, K, e, 0, ws, s);
+  hipError_t le = hipSuccess;
+  if (epilogue == VLA_GEMM_RESIDUAL) {
+    // as the prefix's O projection added into the residual: whole-K row tiles where the prefix uses them,
+    // else the tile kernels whose K splits the fixed-order reduction adds into out
+    e.kind = EPI_RESID; e.resid = out; e.ldr = N;
+    le = gemm_frag(af, wf, M, N, K, e, 0, ws, s);
+  } else {
+    le = M <= 64 ? gemm_chunk(af, wf, M, N, K, e, kPrefixChunkSplits, ws, s) : gemm_frag(af, wf, M, N, K, e, 0, ws, s);
+  }
   if (le != hipSuccess) return done(fail(VLA_ERR_DEVICE, std::string("gemm launch: ") + hipGetErrorString(le)));
   if (hipStreamSynchronize(s) != hipSuccess) return done(fail(VLA_ERR_DEVICE, "gemm sync"));
   return done(VLA_OK);

@@ -22,6 +22,7 @@ STATUS = {0: "VLA_OK", 1: "VLA_ERR_INVALID_ARGUMENT", 2: "VLA_ERR_SHAPE_MISMATCH
           4: "VLA_ERR_UNSUPPORTED", 5: "VLA_ERR_OUT_OF_MEMORY", 6: "VLA_ERR_DEVICE"}
 PRECISION = {"f32": 0, "bf16": 1, "w2a8": 2}
 VLA_OUT_F32, VLA_OUT_BF16 = 0, 1
+VLA_GEMM_STORE, VLA_GEMM_GEGLU, VLA_GEMM_RESIDUAL = 0, 1, 2
 ABI_VERSION = 2
 ATTN_MODE = {"cross": 0, "joint": 1}
 
@@ -304,15 +305,22 @@ def vla_prefix_encode(model: Model, prefix_hidden, kv_storage=None, stream=None,
     return kv
 
 
-def vla_gemm_bf16(a, w, geglu: bool = False, stream=None):
+def vla_gemm_bf16(a, w, geglu: bool = False, stream=None, residual=None):
     """a: cuda bfloat16 [M, K], w: cuda bfloat16 [N, K] -> float32 [M, N] (or [M, N / 2] with the GeGLU of
-    gate/up rows interleaved in blocks of 16), on the prefix's product kernels."""
+    gate/up rows interleaved in blocks of 16), on the prefix's product kernels.  With `residual` (cuda float32
+    [M, N], updated in place and returned): residual += a w^T, the prefix's O-projection form."""
     import torch
     assert a.dtype == torch.bfloat16 and w.dtype == torch.bfloat16 and a.is_contiguous() and w.is_contiguous()
     M, K = a.shape
     N = w.shape[0]
-    out = torch.empty((M, N // 2 if geglu else N), dtype=torch.float32, device=a.device)
-    _check(lib().vla_gemm_bf16(C.c_void_p(a.data_ptr()), C.c_void_p(w.data_ptr()), M, N, K, int(bool(geglu)),
+    if residual is not None:
+        assert not geglu and residual.dtype == torch.float32 and residual.is_contiguous()
+        assert tuple(residual.shape) == (M, N)
+        out, epilogue = residual, VLA_GEMM_RESIDUAL
+    else:
+        out = torch.empty((M, N // 2 if geglu else N), dtype=torch.float32, device=a.device)
+        epilogue = VLA_GEMM_GEGLU if geglu else VLA_GEMM_STORE
+    _check(lib().vla_gemm_bf16(C.c_void_p(a.data_ptr()), C.c_void_p(w.data_ptr()), M, N, K, epilogue,
                                C.c_void_p(out.data_ptr()), _stream(stream)))
     return out
 

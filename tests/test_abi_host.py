@@ -120,6 +120,17 @@ def test_null_and_foreign_handles_are_rejected():
     assert L.vla_model_create(C.byref(cfg), C.byref(w), None, C.byref(out)) == 2
 
 
+def test_gemm_unit_entry_point_rejects_unknown_epilogues():
+    """vla_gemm_bf16 takes VLA_GEMM_STORE, _GEGLU or _RESIDUAL; anything else is refused before any device
+    call (the pointers are never dereferenced)."""
+    L = vla.lib()
+    x = C.c_void_p(16)
+    for bad in (-1, 3, 7):
+        assert L.vla_gemm_bf16(x, x, 64, 64, 64, bad, x, None) == 1
+    assert "epilogue" in vla.lib().vla_last_error().decode()
+    assert L.vla_gemm_bf16(None, x, 64, 64, 64, 0, x, None) == 1
+
+
 def test_create_without_gpu_reports_device_error():
     import torch
     if torch.cuda.is_available():

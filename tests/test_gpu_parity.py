@@ -460,3 +460,22 @@ def test_prefix_bf16_products(M, N, K, geglu):
     err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     assert err < 1e-5, f"normwise error {err:.3e}"
     assert np.isfinite(got).all()
+
+
+# The residual form (out += A W^T, the prefix's O projection) at the single-camera O and QKV shapes (whole-K
+# row tiles), a ragged row count with fewer k-steps than waves, a chunk-sized count and one above the row
+# tiles' range (288-row tiles, K splits added into out by the reduction): the update against float64, same
+# bound and reasoning as above.
+@pytest.mark.parametrize("M,N,K", [(288, 2048, 2048), (288, 2560, 2048), (100, 256, 256), (40, 128, 128),
+                                   (400, 2048, 2048), (301, 160, 192)])
+def test_prefix_bf16_residual_products(M, N, K):
+    rng = np.random.default_rng(M * 11 + N + K)
+    a = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((0.02 * rng.standard_normal((N, K))).astype(np.float32)).to(torch.bfloat16)
+    h0 = rng.standard_normal((M, N)).astype(np.float32)
+    h = torch.from_numpy(h0.copy()).cuda()
+    got = vla.vla_gemm_bf16(a.cuda(), w.cuda(), residual=h).cpu().numpy().astype(np.float64)
+    upd = a.double().numpy() @ w.double().numpy().T
+    err = np.linalg.norm(got - h0.astype(np.float64) - upd) / np.linalg.norm(upd)
+    assert err < 1e-5, f"normwise error of the update {err:.3e}"
+    assert np.isfinite(got).all()
