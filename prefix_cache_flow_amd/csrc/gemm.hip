@@ -635,8 +635,7 @@ __global__ __launch_bounds__(512) void k_gemm_rk(FragP p) {
 
 // K is cut into chunks of an even number of 64-wide slices (the kernel runs
 // slices in pairs; only the last chunk may hold an odd count); `splits` <= 0
-// asks for a count that fills the chip, about one workgroup per CU with at
-// least 4 slices each.
+// asks for the count frag_per estimates fastest.
 // Tile width: 64 columns for the small square products (two workgroups then
 // share a CU, and the grid reaches the CU count with fewer K splits), 128 else.
 // 64-column tiles (two workgroups per CU) for products of at most 2048-deep K
@@ -651,20 +650,40 @@ static int frag_bn(int M, int N, int K) {
   return tiles128 < 32 ? 64 : 128;
 }
 
-static int frag_per(int M, int N, int K, int splits, int bn) {
+// K splits of a product on the 288-row tiles (`splits` <= 0: automatic): the
+// count that minimises an estimate of the busiest CU's time, rounds of
+// workgroups times the bytes each pulls through its CU (about 52 GB/s a CU,
+// the prefix gate/up GEMM's rate) plus the partial slabs written and read back
+// (about 5 TB/s) and, for a product that finishes in the GEMM, the reduction's
+// launch (about 4 us; such products split at most four ways).  Ties go to
+// fewer splits.  Returns 128-deep K pairs per chunk.
+static int frag_per(int M, int N, int K, int splits, int bn, bool finishing) {
   const int pairs = (K / 64 + 1) / 2;
-  if (splits <= 0) {
-    const int tiles = (M + kFragBM - 1) / kFragBM * ((N + bn - 1) / bn);
-    splits = 1;
-    while (tiles * splits < 256 && pairs / (2 * splits) >= 2 && 2 * splits <= 16) splits *= 2;
+  if (splits > 0) {
+    splits = std::max(1, std::min(splits, pairs));
+    return (pairs + splits - 1) / splits;
   }
-  splits = std::max(1, std::min(splits, pairs));
-  return (pairs + splits - 1) / splits;  // pairs per chunk
+  const int tiles = (M + kFragBM - 1) / kFragBM * ((N + bn - 1) / bn);
+  double best = 0.0;
+  int best_per = pairs;
+  for (int per = pairs; per >= 1; --per) {
+    const int used = (pairs + per - 1) / per;
+    if (used > 16 || (finishing && used > 4)) break;
+    const int rounds = (tiles * used + 255) / 256;
+    double t = (double)rounds * (kFragBM + bn) * per * 128 * 2 / 52e9;
+    if (used > 1 || !finishing) t += (double)used * M * N * 8 / 5e12;
+    if (used > 1 && finishing) t += 4e-6;
+    if (per == pairs || t < best * 0.999) {
+      best = t;
+      best_per = per;
+    }
+  }
+  return best_per;
 }
 
 int gemm_frag_splits(int M, int N, int K, int splits) {
   if (K < 64) return 1;
-  const int per = frag_per(M, N, K, splits, frag_bn(M, N, K));
+  const int per = frag_per(M, N, K, splits, frag_bn(M, N, K), false);
   return ((K / 64 + 1) / 2 + per - 1) / per;
 }
 
@@ -721,11 +740,9 @@ hipError_t gemm_frag(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K
     return hipGetLastError();
   }
   const int bn = frag_bn(M, N, K);
-  int per = frag_per(M, N, K, splits, bn);
-  // A product that finishes here (not partials for a row kernel) pays for every
-  // split twice, writing its partial slab and reading it back in the
-  // reduction: the automatic choice stops at 4 for those.
-  if (splits <= 0 && kind0 != EPI_PARTIAL && ((K / 64 + 1) / 2 + per - 1) / per > 4) per = frag_per(M, N, K, 4, bn);
+  int per = frag_per(M, N, K, splits, bn, kind0 != EPI_PARTIAL);
+  // a finishing product never splits more ways than the partial count callers size workspaces for
+  if (splits <= 0 && kind0 != EPI_PARTIAL) per = std::max(per, frag_per(M, N, K, 0, bn, false));
   splits = ((K / 64 + 1) / 2 + per - 1) / per;
   if ((splits > 1 || kind0 == EPI_PARTIAL) && !ws) return hipErrorInvalidValue;
   FragP p{Af, Wf, M, N, K, 0, 0, 0, epi, ws};
