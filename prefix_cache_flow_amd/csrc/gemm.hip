@@ -652,25 +652,32 @@ static int frag_bn(int M, int N, int K) {
 
 // K splits of a product on the 288-row tiles (`splits` <= 0: automatic): the
 // count that minimises an estimate of the busiest CU's time, rounds of
-// workgroups times the bytes each pulls through its CU (about 52 GB/s a CU,
-// the prefix gate/up GEMM's rate) plus the partial slabs written and read back
-// (about 5 TB/s) and, for a product that finishes in the GEMM, the reduction's
-// launch (about 4 us; such products split at most four ways).  Ties go to
-// fewer splits.  Returns 128-deep K pairs per chunk.
-static int frag_per(int M, int N, int K, int splits, int bn, bool finishing) {
+// workgroups times the bytes each pulls through its CU, plus the partial slabs
+// written and read back (about 5 TB/s) and, for a product that finishes in the
+// GEMM (`kind` not EPI_PARTIAL), the reduction's launch (about 4 us; such
+// products split at most four ways).  A CU pulls about 52 GB/s in the eight-wave
+// kernel (128-column tiles with a GeGLU, partial-sum or plain store epilogue;
+// the prefix gate/up GEMM's rate) and in the 64-column kernel, about 16 GB/s in
+// the four-wave 128-column kernel that the scatter epilogues run on unsplit (the
+// 800-row expert QKV took 55 us there against 26 us split four ways).  Ties go
+// to fewer splits.  Returns 128-deep K pairs per chunk.
+static int frag_per(int M, int N, int K, int splits, int bn, int kind) {
   const int pairs = (K / 64 + 1) / 2;
   if (splits > 0) {
     splits = std::max(1, std::min(splits, pairs));
     return (pairs + splits - 1) / splits;
   }
+  const bool finishing = kind != EPI_PARTIAL;
   const int tiles = (M + kFragBM - 1) / kFragBM * ((N + bn - 1) / bn);
   double best = 0.0;
   int best_per = pairs;
   for (int per = pairs; per >= 1; --per) {
     const int used = (pairs + per - 1) / per;
     if (used > 16 || (finishing && used > 4)) break;
+    const int k_run = used > 1 ? EPI_PARTIAL : kind;  // the epilogue the tile kernel runs
+    const bool slow = bn == 128 && k_run != EPI_GEGLU && k_run != EPI_PARTIAL && k_run != EPI_STORE;
     const int rounds = (tiles * used + 255) / 256;
-    double t = (double)rounds * (kFragBM + bn) * per * 128 * 2 / 52e9;
+    double t = (double)rounds * (kFragBM + bn) * per * 128 * 2 / (slow ? 16e9 : 52e9);
     if (used > 1 || !finishing) t += (double)used * M * N * 8 / 5e12;
     if (used > 1 && finishing) t += 4e-6;
     if (per == pairs || t < best * 0.999) {
@@ -681,9 +688,9 @@ static int frag_per(int M, int N, int K, int splits, int bn, bool finishing) {
   return best_per;
 }
 
-int gemm_frag_splits(int M, int N, int K, int splits) {
+int gemm_frag_splits(int M, int N, int K, int splits, int kind) {
   if (K < 64) return 1;
-  const int per = frag_per(M, N, K, splits, frag_bn(M, N, K), false);
+  const int per = frag_per(M, N, K, splits, frag_bn(M, N, K), kind);
   return ((K / 64 + 1) / 2 + per - 1) / per;
 }
 
@@ -740,9 +747,7 @@ hipError_t gemm_frag(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K
     return hipGetLastError();
   }
   const int bn = frag_bn(M, N, K);
-  int per = frag_per(M, N, K, splits, bn, kind0 != EPI_PARTIAL);
-  // a finishing product never splits more ways than the partial count callers size workspaces for
-  if (splits <= 0 && kind0 != EPI_PARTIAL) per = std::max(per, frag_per(M, N, K, 0, bn, false));
+  int per = frag_per(M, N, K, splits, bn, kind0);
   splits = ((K / 64 + 1) / 2 + per - 1) / per;
   if ((splits > 1 || kind0 == EPI_PARTIAL) && !ws) return hipErrorInvalidValue;
   FragP p{Af, Wf, M, N, K, 0, 0, 0, epi, ws};

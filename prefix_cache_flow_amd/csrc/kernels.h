@@ -88,7 +88,9 @@ struct Epilogue {
 // fills the chip (gemm_frag_splits of them).
 hipError_t gemm_frag(const uint16_t* Af, const uint16_t* Wf, int M, int N, int K, const Epilogue& epi,
                      int splits, float* ws, hipStream_t s);
-int gemm_frag_splits(int M, int N, int K, int splits);
+// K splits gemm_frag uses for a product of this shape and epilogue kind (the
+// split-K partials of a PARTIAL product, the workspace any other kind needs).
+int gemm_frag_splits(int M, int N, int K, int splits, int kind = EPI_PARTIAL);
 // True when gemm_frag (with `splits` <= 0) runs a product of this shape and
 // kind as whole-K row tiles: no partials, every output stored once by its
 // owner (QKV and RESID kinds at a few hundred rows).

@@ -789,12 +789,13 @@ static const int kExpertSplits = 4;
 // Split-K counts: the one place that fixes them for a GEMM and for the row
 // kernel (or reduction) that sums its partials.
 static const int kPrefixChunkSplits = 4;  // split request of the chunk-sized kernel
-static int prefix_splits(int64_t M, int N, int K) {
-  return M <= 64 ? gemm_chunk_splits(K, kPrefixChunkSplits) : gemm_frag_splits((int)M, N, K, 0);
+// kind: the product's epilogue (its split count, and so its workspace, depends on it)
+static int prefix_splits(int64_t M, int N, int K, int kind = EPI_PARTIAL) {
+  return M <= 64 ? gemm_chunk_splits(K, kPrefixChunkSplits) : gemm_frag_splits((int)M, N, K, 0, kind);
 }
-static int expert_splits(int64_t M, int N, int K) {
+static int expert_splits(int64_t M, int N, int K, int kind = EPI_PARTIAL) {
   // chunk-sized kernel up to 64 rows, the 288-row-tile kernel (its own split choice) above
-  return M <= 64 ? gemm_chunk_splits(K, kExpertSplits) : gemm_frag_splits((int)M, N, K, 0);
+  return M <= 64 ? gemm_chunk_splits(K, kExpertSplits) : gemm_frag_splits((int)M, N, K, 0, kind);
 }
 // bf16 product with both operands in the fragment layout: the chunk-sized
 // kernel up to 64 rows, 288-row tiles above; split counts as prefix_splits
@@ -807,12 +808,12 @@ static hipError_t mm_frag(const void* A, const void* W, int64_t M, int N, int K,
 static int64_t prefix_part_floats(const vla_model_config& c, int64_t rows) {
   if (rows <= 0) return 0;
   const int qw = c.Hq * c.hd, qkvw = (c.Hq + 2 * c.Hkv) * c.hd, ncache = c.L_e * 2 * c.Hkv_e * c.hd_e;
-  int64_t f = (int64_t)prefix_splits(rows, ncache, c.d_p) * ncache;
+  int64_t f = (int64_t)prefix_splits(rows, ncache, c.d_p, EPI_CACHE) * ncache;
   if (c.precision != VLA_W2A8_BF16) {
-    f = std::max<int64_t>(f, (int64_t)prefix_splits(rows, qkvw, c.d_p) * qkvw);
+    f = std::max<int64_t>(f, (int64_t)prefix_splits(rows, qkvw, c.d_p, EPI_QKV) * qkvw);
     f = std::max<int64_t>(f, (int64_t)prefix_splits(rows, c.d_p, qw) * c.d_p);
     f = std::max<int64_t>(f, (int64_t)prefix_splits(rows, c.d_p, c.F_p) * c.d_p);
-    f = std::max<int64_t>(f, (int64_t)prefix_splits(rows, 2 * c.F_p, c.d_p) * 2 * c.F_p);
+    f = std::max<int64_t>(f, (int64_t)prefix_splits(rows, 2 * c.F_p, c.d_p, EPI_GEGLU) * 2 * c.F_p);
   }
   return f * rows;
 }
@@ -821,9 +822,9 @@ static int64_t expert_part_floats(const vla_model_config& c, int64_t erows) {
   const int qe = c.Hq_e * c.hd_e, qkve = (c.Hq_e + 2 * c.Hkv_e) * c.hd_e;
   int64_t f = (int64_t)expert_splits(erows, c.d_e, qe) * c.d_e;
   f = std::max<int64_t>(f, (int64_t)expert_splits(erows, c.d_e, c.F_e) * c.d_e);
-  f = std::max<int64_t>(f, (int64_t)expert_splits(erows, qkve, c.d_e) * qkve);
-  f = std::max<int64_t>(f, (int64_t)expert_splits(erows, qe, c.d_e) * qe);
-  f = std::max<int64_t>(f, (int64_t)expert_splits(erows, 2 * c.F_e, c.d_e) * 2 * c.F_e);
+  f = std::max<int64_t>(f, (int64_t)expert_splits(erows, qkve, c.d_e, EPI_QKV) * qkve);
+  f = std::max<int64_t>(f, (int64_t)expert_splits(erows, qe, c.d_e, EPI_STORE) * qe);
+  f = std::max<int64_t>(f, (int64_t)expert_splits(erows, 2 * c.F_e, c.d_e, EPI_GEGLU) * 2 * c.F_e);
   return f * erows;
 }
 
