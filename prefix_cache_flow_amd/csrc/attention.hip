@@ -290,10 +290,10 @@ __device__ __forceinline__ void attn_tile(const u32x4_t (&k)[D / 16], VF vf, con
 // 4 x 16 rows of D + 4 floats; ends with every wave done with it.
 template <int D>
 __device__ __forceinline__ void attn_merge_store(const AttnArgs& a, float (*mbuf)[16], float (*lbuf)[16], float* obuf,
-                                                 float mrun, float lrun, const f32x4_t (&o)[D / 16]) {
+                                                 float mrun, float lrun, const f32x4_t (&o)[D / 16], int bx, int by) {
   constexpr int VS = D / 16, LDO = D + 4;
   const int G = a.Hq / a.Hkv, R = G * a.Nq;
-  const int g = blockIdx.y % a.Hkv, b = blockIdx.y / a.Hkv;
+  const int g = by % a.Hkv, b = by / a.Hkv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   if (grp == 0) {
@@ -304,7 +304,7 @@ __device__ __forceinline__ void attn_merge_store(const AttnArgs& a, float (*mbuf
   for (int t2 = 0; t2 < VS; ++t2) *(f32x4_t*)&obuf[(w * 16 + col) * LDO + t2 * 16 + grp * 4] = o[t2];
   __syncthreads();
   const int qq = threadIdx.x & 15, d0 = (threadIdx.x >> 4) * (D / 16);
-  const int r = blockIdx.x * 16 + qq;
+  const int r = bx * 16 + qq;
   if (r >= R) return;
   const int jl = r / a.Nq, q = r - jl * a.Nq, j = g * G + jl;
   float M = mbuf[0][qq];
@@ -354,11 +354,21 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float obuf[4][16][LDO];
 
   if (prefetch_layer(a.pf)) return;  // extra workgroups: warm the next weights
+  // (row block, batch and key/value head) of this workgroup; with a multiple of
+  // eight of the latter, the workgroups of one observation and head are numbered
+  // onto one XCD (the dispatch deals workgroups to the XCDs round robin), so its
+  // keys and values are fetched into one L2 instead of all eight
+  int bx = blockIdx.x, by = blockIdx.y;
+  if ((gridDim.y & 7) == 0) {
+    const int L = blockIdx.x + gridDim.x * blockIdx.y, k = L >> 3;
+    by = (L & 7) + 8 * (k / gridDim.x);
+    bx = k % gridDim.x;
+  }
   const int G = a.Hq / a.Hkv, R = G * a.Nq;
-  const int g = blockIdx.y % a.Hkv, b = blockIdx.y / a.Hkv;
+  const int g = by % a.Hkv, b = by / a.Hkv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int r = min((int)blockIdx.x * 16 + col, R - 1);  // clamped rows are computed, never stored
+  const int r = min(bx * 16 + col, R - 1);  // clamped rows are computed, never stored
   const int jl = r / a.Nq, q = r - jl * a.Nq, j = g * G + jl;
   const bf16_t* Qp = (const bf16_t*)a.q + b * a.q_bs + j * a.q_hs + (long)q * a.q_rs;
   const u32x4_t* Kf = (const u32x4_t*)((const bf16_t*)a.k + b * a.k_bs + g * a.k_hs) + lane;
@@ -441,7 +451,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
       }
   }
 
-  attn_merge_store<D>(a, mbuf, lbuf, &obuf[0][0][0], mrun, lrun, o);
+  attn_merge_store<D>(a, mbuf, lbuf, &obuf[0][0][0], mrun, lrun, o, bx, by);
 }
 
 hipError_t attention_chunk(const AttnArgs& a, hipStream_t s) {
