@@ -454,6 +454,95 @@ __global__ __launch_bounds__(256) void k_attn_chunk(AttnArgs a) {
   attn_merge_store<D>(a, mbuf, lbuf, &obuf[0][0][0], mrun, lrun, o, bx, by);
 }
 
+// Long key sets with many query rows (batched and multi-camera prefixes): a
+// workgroup of four waves owns 64 stacked rows, wave w the 16 rows of row block
+// w, and all four walk every 32-key tile, which the workgroup stages once in LDS
+// (double-buffered, each wave copying a quarter of it): a CU then pulls the keys
+// and values once per 64 rows instead of once per 16.  Each wave keeps its rows'
+// softmax state over all keys, so there is no merge: it normalises and stores
+// its own rows.  Same tile step, hence the same arithmetic per tile, as
+// k_attn_chunk.
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_rows(AttnArgs a) {
+  constexpr int KS = D / 32, VS = D / 16, TF = 2 * KS + VS;  // fragments of one tile: keys, then values
+  constexpr int PW = TF / 4;                                 // fragments each wave stages
+  __shared__ __attribute__((aligned(16))) u32x4_t kv[2][TF][64];
+  int bx = blockIdx.x, by = blockIdx.y;
+  if ((gridDim.y & 7) == 0) {  // one observation and head per XCD, as k_attn_chunk
+    const int L = blockIdx.x + gridDim.x * blockIdx.y, k = L >> 3;
+    by = (L & 7) + 8 * (k / gridDim.x);
+    bx = k % gridDim.x;
+  }
+  const int G = a.Hq / a.Hkv, R = G * a.Nq;
+  const int g = by % a.Hkv, b = by / a.Hkv;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int rb = bx * 4 + w;  // this wave's row block
+  const int r = min(rb * 16 + col, R - 1);  // clamped rows are computed, never stored
+  const int jl = r / a.Nq, q = r - jl * a.Nq, j = g * G + jl;
+  const bf16_t* Qp = (const bf16_t*)a.q + b * a.q_bs + j * a.q_hs + (long)q * a.q_rs;
+  const u32x4_t* Kf = (const u32x4_t*)((const bf16_t*)a.k + b * a.k_bs + g * a.k_hs) + lane;
+  const u32x4_t* Vf = (const u32x4_t*)((const bf16_t*)a.v + b * a.v_bs + g * a.v_hs) + lane;
+  const u32x4_t* Kf2 = a.Nk2 ? (const u32x4_t*)((const bf16_t*)a.k2 + b * a.k2_bs + g * a.k2_hs) + lane : Kf;
+  const u32x4_t* Vf2 = a.Nk2 ? (const u32x4_t*)((const bf16_t*)a.v2 + b * a.v2_bs + g * a.v2_hs) + lane : Vf;
+  const int TA = (a.Nk + 31) / 32;
+  const int T = TA + (a.Nk2 + 31) / 32;
+  // wave w stages fragments w PW .. w PW + PW - 1 of a tile
+  auto gload = [&](u32x4_t (&regs)[PW], int tl) {
+    int tile = tl;
+    const bool second = tile >= TA;
+    const u32x4_t* kp = second ? Kf2 : Kf;
+    const u32x4_t* vp = second ? Vf2 : Vf;
+    tile -= second ? TA : 0;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int f = w * PW + i;
+      regs[i] = f < 2 * KS ? kp[((long)tile * 2 * KS + f) * 64] : vp[((long)tile * VS + f - 2 * KS) * 64];
+    }
+  };
+  auto sstore = [&](const u32x4_t (&regs)[PW], int buf) {
+#pragma unroll
+    for (int i = 0; i < PW; ++i) kv[buf][w * PW + i][lane] = regs[i];
+  };
+  u32x4_t qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qf[s] = *(const u32x4_t*)(Qp + s * 32 + grp * 8);
+  f32x4_t o[VS];
+#pragma unroll
+  for (int t = 0; t < VS; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mrun = -3.0e38f, lrun = 0.f;
+  const float sl2 = 1.4426950408889634f / sqrtf((float)D);
+  const int nk1 = a.klen ? min(uniform_ld(a.klen, b), a.Nk) : a.Nk;
+  const int nk2 = a.klen2 ? min(uniform_ld(a.klen2, b), a.Nk2) : a.Nk2;
+  u32x4_t st[PW];
+  gload(st, 0);
+  sstore(st, 0);
+  __syncthreads();
+  for (int t = 0; t < T; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < T) gload(st, t + 1);  // in flight while this tile is consumed
+    u32x4_t kt[2 * KS];
+#pragma unroll
+    for (int f = 0; f < 2 * KS; ++f) kt[f] = kv[buf][f][lane];
+    const bool second = t >= TA;
+    attn_tile<D>(kt, [&](int f) { return kv[buf][2 * KS + f][lane]; }, qf, (second ? t - TA : t) * 32,
+                 second ? nk2 : nk1, grp, sl2, mrun, lrun, o);
+    if (t + 1 < T) sstore(st, buf ^ 1);  // that buffer was last read for tile t - 1, before the barrier below
+    __syncthreads();
+  }
+  if (rb * 16 + col >= R) return;
+  // lane (col, grp) holds dims 16 t2 + 4 grp .. + 3 of its row: 8-byte stores
+  const float inv = __builtin_amdgcn_rcpf(lrun);
+  const long row = (long)b * a.Nq + q;
+#pragma unroll
+  for (int t2 = 0; t2 < VS; ++t2) {
+    const int d = t2 * 16 + grp * 4;
+    const u32x2_t pk = {pack_bf2(o[t2][0] * inv, o[t2][1] * inv), pack_bf2(o[t2][2] * inv, o[t2][3] * inv)};
+    const long oi = a.o_frag ? frag_idx((int)row, j * D + d, a.Hq * D) : b * a.o_bs + (long)q * a.o_rs + (long)j * D + d;
+    *(u32x2_t*)((bf16_t*)a.o + oi) = pk;
+  }
+}
+
 hipError_t attention_chunk(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.Nq <= 0 || a.Nk <= 0) return hipSuccess;
   if (a.Hq % a.Hkv || a.o_f32) return hipErrorInvalidValue;
@@ -462,6 +551,18 @@ hipError_t attention_chunk(const AttnArgs& a, hipStream_t s) {
   const int R = a.Hq / a.Hkv * a.Nq;
   const int per = (R + 15) / 16 * a.Hkv * a.B;
   dim3 grid((R + 15) / 16, a.Hkv * a.B, prefetch_depth(per, a.pf.blocks));
+  // at least four 16-row blocks per CU and eight key tiles: 64-row workgroups sharing key tiles through LDS
+  const int T = (a.Nk + 31) / 32 + (a.Nk2 + 31) / 32;
+  if (!a.pf.blocks && per >= 4 * 256 && T >= 8) {
+    const dim3 g4((R + 63) / 64, a.Hkv * a.B);
+    switch (a.hd) {
+      case 64: hipLaunchKernelGGL(k_attn_rows<64>, g4, dim3(256), 0, s, a); break;
+      case 128: hipLaunchKernelGGL(k_attn_rows<128>, g4, dim3(256), 0, s, a); break;
+      case 256: hipLaunchKernelGGL(k_attn_rows<256>, g4, dim3(256), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (a.hd) {
     case 64: hipLaunchKernelGGL(k_attn_chunk<64>, grid, dim3(256), 0, s, a); break;
     case 128: hipLaunchKernelGGL(k_attn_chunk<128>, grid, dim3(256), 0, s, a); break;

@@ -31,6 +31,10 @@ SMALL_JOINT_GQA = synth.config(1, name="small_joint_gqa", attn="joint", n_prefix
 SMALL_JOINT_B3 = synth.config(1, name="small_joint_b3", attn="joint", batch=3, n_prefix=70, d_p=256, L_p=2, Hq=8,
                               Hkv=1, hd=128, F_p=512, d_e=128, L_e=2, Hq_e=8, Hkv_e=1, hd_e=128, F_e=256, H=33, d_a=5,
                               steps=2)
+# Enough query rows (8 observations x 8 heads x 260 tokens: 1040 16-row blocks) and keys (9 tiles, the last
+# ragged) for the prefix attention's 64-row workgroups sharing key tiles through LDS.
+SMALL_ROWS = synth.config(1, name="small_rows_b8", batch=8, n_prefix=260, d_p=256, L_p=2, Hq=8, Hkv=1, hd=64,
+                          F_p=512, d_e=128, L_e=2, Hq_e=2, Hkv_e=1, hd_e=64, F_e=256, H=20, d_a=7, steps=2)
 SMALL_W2A8 = synth.config(4, name="small_w2a8", n_prefix=100, d_p=256, L_p=2, Hq=2, Hkv=2, hd=128, F_p=384,
                           d_e=128, L_e=2, Hq_e=2, Hkv_e=1, hd_e=64, F_e=256, H=8, d_a=7, steps=3)
 

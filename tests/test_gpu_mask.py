@@ -40,6 +40,10 @@ RAGGED = [
     (synth.config(4, name="small_w2a8_ragged", batch=3, n_prefix=100, d_p=256, L_p=2, Hq=2, Hkv=2, hd=128, F_p=384,
                   d_e=128, L_e=2, Hq_e=2, Hkv_e=1, hd_e=64, F_e=256, H=8, d_a=7, steps=3),
      [100, 61, 30], 2e-2, 1e-2),
+    # 1040 16-row blocks of prefix queries: the 64-row attention workgroups sharing key tiles through LDS
+    (synth.config(1, name="small_rows_ragged_b8", batch=8, n_prefix=260, d_p=256, L_p=2, Hq=8, Hkv=1, hd=64,
+                  F_p=512, d_e=128, L_e=2, Hq_e=2, Hkv_e=1, hd_e=64, F_e=256, H=20, d_a=7, steps=2),
+     [260, 33, 1, 200, 129, 64, 259, 96], 2e-2, 5e-3),
 ]
 
 

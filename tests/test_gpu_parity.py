@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from policy_cases import (JOINT_F32, SMALL_BF16, SMALL_BF16_B3, SMALL_GQA, SMALL_JOINT, SMALL_JOINT_B3,
+from policy_cases import (JOINT_F32, SMALL_BF16, SMALL_BF16_B3, SMALL_GQA, SMALL_JOINT, SMALL_JOINT_B3, SMALL_ROWS,
                           SMALL_JOINT_GQA, SMALL_W2A8, build_model, cache_from_storage, gpu_run, host_inputs)
 
 pytestmark = pytest.mark.gpu
@@ -42,6 +42,7 @@ def report(name, got, ref, x0):
     (SMALL_BF16, 2e-2, 5e-3, 4e-3),
     (SMALL_BF16_B3, 2e-2, 5e-3, 4e-3),
     (SMALL_GQA, 2e-2, 5e-3, 4e-3),
+    (SMALL_ROWS, 2e-2, 5e-3, 4e-3),
     (SMALL_W2A8, 2e-2, 1e-2, 4e-3),
     (JOINT_F32, 1e-3, 1e-3, 1e-4),
     (SMALL_JOINT, 2e-2, 5e-3, 4e-3),
