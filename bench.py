@@ -35,8 +35,8 @@ PEAK_HBM_GBS = 8000.0
 # reads for a plain copy of known size (profiles/hbm_bytes_denoise_single_camera_bf16.md).  Valid for the
 # single-camera bf16 workload and the kernels as they were measured; None where no measurement stands.
 ATTN_KERNEL = "k_attn_chunk<256>"
-ATTN_TRAFFIC_BYTES_PER_LAUNCH = 16246925   # mean over all launches of a bench run (prefix, self, cross)
-DENOISE_TRAFFIC_BYTES_PER_STEP = 1903578328  # every kernel of one solver step (the denoise graph's nodes)
+ATTN_TRAFFIC_BYTES_PER_LAUNCH = None   # mean over all launches of a bench run; not yet measured for the absorbed form
+DENOISE_TRAFFIC_BYTES_PER_STEP = None  # every kernel of one solver step; not yet measured for the absorbed form
 
 
 def parse():
@@ -100,14 +100,29 @@ def expert_step_flops(c):
     return c.L_e * per_layer + 2 * M * c.d_e * (c.d_a + c.d_a)
 
 
-def expert_step_bytes(c):
-    """Algorithmic HBM bytes of one denoise step: every expert weight once (bf16) plus the cache."""
+def expert_step_bytes(c, absorbed=False):
+    """Algorithmic HBM bytes of one denoise step: every expert weight once (bf16) plus the cache.  With the
+    absorbed cross sublayer a step reads each layer's Wq_j^T K^T and V Wo_j^T (Hq_e x n_prefix x d_e each)
+    in place of the cross-attention query and output weights and the cached keys and values."""
     qe, kve = c.Hq_e * c.hd_e, c.Hkv_e * c.hd_e
     cross = 0 if c.attn == "joint" else qe * c.d_e + c.d_e * qe  # cross-attention query and output
+    if absorbed:
+        cross = 2 * c.Hq_e * c.n_prefix * c.d_e
     per_layer = (qe + 2 * kve) * c.d_e + c.d_e * qe + cross + 2 * c.F_e * c.d_e + c.d_e * c.F_e
     weights = c.L_e * per_layer + c.d_e * c.d_a * 2
-    cache = c.batch * c.L_e * 2 * kve * c.n_prefix
+    cache = 0 if absorbed else c.batch * c.L_e * 2 * kve * c.n_prefix
     return 2 * (weights + cache)
+
+
+def absorbed_form(vla, model, c):
+    """Whether this model's encode writes the absorbed cross-attention products (the cache storage then
+    exceeds the keys, values and lengths, as vla.h states)."""
+    if c.precision == "f32" or c.attn == "joint":
+        return False
+    np_ = (c.n_prefix + 31) // 32 * 32
+    core = c.batch * c.L_e * 2 * c.Hkv_e * np_ * c.hd_e * 2
+    plain = (core + 255) // 256 * 256 + (c.batch * 4 + 255) // 256 * 256
+    return vla.vla_kv_cache_bytes(model, c.batch, c.n_prefix) > plain
 
 
 SWEEP_STEPS = (1, 2, 4, 8, 16)
@@ -302,6 +317,8 @@ def dominant_kernel_roofline(vla, model, cfg, zt, xt, out, kv_storage):
     per = {}
     for name, kind, run, count in classes:
         ms, n = probe_mean_ms(vla, model, kind, run)
+        if ms is None and name == "cross":
+            continue  # the absorbed cross sublayer runs no attention over the cache
         if ms is None:
             return None
         per[name] = {"us": ms * 1e3, "bytes": b[name], "gbs": b[name] / (ms * 1e-3) / 1e9, "launches_per_step": count}
@@ -428,7 +445,8 @@ def main():
     phases = {"prefix_ms": float(np.median(pre_ms)), "denoise_ms": float(np.median(den_ms)),
               "denoise_step_ms": float(np.median(stp_ms))}
     pf = prefix_flops(cfg) * cfg.batch
-    sb = expert_step_bytes(cfg)
+    absorbed = absorbed_form(vla, model, cfg)
+    sb = expert_step_bytes(cfg, absorbed)
     prefix_peak = PEAK_INT8_TOPS if cfg.precision == "w2a8" else PEAK_BF16_TFLOPS
     phases["prefix_mfma_frac"] = pf / (phases["prefix_ms"] * 1e-3) / (prefix_peak * 1e12)
     phases["denoise_hbm_frac"] = sb / (phases["denoise_step_ms"] * 1e-3) / (PEAK_HBM_GBS * 1e9)

@@ -187,6 +187,15 @@ vla_status vla_model_destroy(vla_model* model);
  *   K block: (t, d) at ((((t/16) * (hd_e/32) + d/32) * 64 + t%16 + 16*((d/8)%4)) * 8 + d%8
  *   V block: with u = t%32, (t, d) at
  *            ((((t/32) * (hd_e/16) + d/16) * 64 + d%16 + 16*((u%16)/4)) * 8 + 4*(u/16) + u%4
+ * For one observation of a bf16 cross-attention model whose solver runs the
+ * absorbed cross sublayer (chunk of at most 64 rows, expert width a multiple
+ * of 128 up to 1024, Hq_e <= 32, Np <= 512 and Hq_e * Np <= 4096, unless the
+ * model was created with VLA_ABSORB=0 in the environment), the lengths are
+ * followed by per-layer products of the cached keys and values that the
+ * encode also writes and the denoise reads instead of them (the same
+ * attention, other rounding points): Wq_j^T K^T and V Wo_j^T for every query
+ * head j, 2 * L_e * Hq_e * Np * d_e bf16 elements, and the values once more,
+ * L_e * Hkv_e * Np * hd_e elements; their layout is internal.
  * Returns 0 for invalid arguments. */
 size_t vla_kv_cache_bytes(const vla_model* model, int32_t batch, int32_t n_prefix);
 

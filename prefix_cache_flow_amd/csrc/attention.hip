@@ -26,13 +26,6 @@
 
 namespace vla {
 
-// A workgroup-uniform int from device memory that no kernel writes while this
-// one runs, through the scalar cache: a vector load here would make the
-// compiler wait for every load issued before it (loads retire in order).
-__device__ __forceinline__ int uniform_ld(const int* p, int i) {
-  return *((const __attribute__((address_space(4))) int*)(uintptr_t)p + i);
-}
-
 template <int D>
 __global__ __launch_bounds__(256) void k_attn16(AttnArgs a) {
   constexpr int LDK = D + 8;   // K tile row stride (bf16)

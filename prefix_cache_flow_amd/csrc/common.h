@@ -30,6 +30,13 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
 }
 
+// A workgroup-uniform int from device memory that no kernel writes while this
+// one runs, through the scalar cache: a vector load here would make the
+// compiler wait for every load issued before it (loads retire in order).
+__device__ __forceinline__ int uniform_ld(const int* p, int i) {
+  return *((const __attribute__((address_space(4))) int*)(uintptr_t)p + i);
+}
+
 // 2^x on the hardware exponential unit (one instruction; results below the
 // normal range flush to zero, 2^-inf = 0).  Used for softmax weights in (0, 1].
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -28,6 +28,17 @@ __device__ __forceinline__ void cache_index(const Epilogue& e, int m, int n, lon
   idx = blk + (!e.out_frag ? (long)t * e.hd + d : kv ? vfrag_idx(t, d, e.hd) : frag_idx(t, d, e.hd));
 }
 
+// EPI_CACHE with vcopy (bf16, one observation): a value also goes to the copy
+// in frag_idx order, the operand order for products that contract over hd
+__device__ __forceinline__ void cache_vcopy(const Epilogue& e, int m, int n, float v) {
+  const int per_kv = e.hkv * e.hd, per_l = 2 * per_kv;
+  const int l = n / per_l;
+  int r = n - l * per_l - per_kv;
+  if (r < 0) return;  // a key
+  const int h = r / e.hd, d = r - h * e.hd;
+  ((bf16_t*)e.vcopy)[(long)(l * e.hkv + h) * e.npad * e.hd + frag_idx(m, d, e.hd)] = f2bf(v);
+}
+
 // EPI_QKV: query columns to rows, keys and values in their blocks (bf16: MFMA orders)
 __device__ __forceinline__ void qkv_store(const Epilogue& e, int m, int n, float v) {
   if (n < e.nq) {
@@ -61,6 +72,7 @@ __device__ __forceinline__ void epi_store_t(const Epilogue& e, int m, int n, flo
     long i;
     cache_index(e, m, n, i);
     if (e.out_f32) ((float*)e.out)[i] = v; else ((bf16_t*)e.out)[i] = f2bf(v);
+    if (e.vcopy) cache_vcopy(e, m, n, v);
   } else if (KIND == EPI_QKV) {
     qkv_store(e, m, n, v);
   }
@@ -819,6 +831,8 @@ __global__ __launch_bounds__(256) void k_chunk(ChunkP p) {
       }
     }
   }
+  // visible keys (scores), requested with the operands
+  const int nkey = KIND == EPI_SCORES ? (p.epi.klen ? min(uniform_ld(p.epi.klen, 0), p.epi.npre) : p.epi.npre) : 0;
   // column group, K chunk (or, split by rows, the workgroup's row block)
   const int bx = blockIdx.x, by = p.rsplit ? 0 : blockIdx.y, rb0 = p.rsplit ? blockIdx.y : 0;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -882,6 +896,46 @@ __global__ __launch_bounds__(256) void k_chunk(ChunkP p) {
       const int idx = (rb * NB + nb) * 4 + e;
       v[nb][e] = red[0][idx][lane] + red[1][idx][lane] + red[2][idx][lane] + red[3][idx][lane];
     }
+  if (KIND == EPI_SCORES) {
+    // the workgroup's 32 columns are keys t0 .. t0 + 31 of one head: keys past
+    // the visible count are masked, then per row the block max r (16-lane DPP
+    // reductions, every lane of a row ends with the same bits) and the weights
+    // 2^(s - r) with their sum
+    const int c0 = bx * 32, t0 = c0 % p.epi.npad, nblk = p.N >> 5;
+    const bool vis0 = t0 + col < nkey, vis1 = t0 + 16 + col < nkey;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = row0 + grp * 4 + e;
+      float a = v[0][e], b = v[NB - 1][e];
+      if (RS) {
+        const float r = 1.0f / sqrtf(((rsp[0][m] + rsp[1][m]) + (rsp[2][m] + rsp[3][m])) / (float)p.epi.rdim + p.epi.reps);
+        a *= r;
+        b *= r;
+      }
+      a = vis0 ? a : -INFINITY;
+      b = vis1 ? b : -INFINITY;
+      float mx = fmaxf(a, b);
+      mx = fmaxf(mx, dpp_mov<0xB1>(mx));
+      mx = fmaxf(mx, dpp_mov<0x4E>(mx));
+      mx = fmaxf(mx, dpp_mov<0x141>(mx));
+      mx = fmaxf(mx, dpp_mov<0x140>(mx));
+      const float ref = mx == -INFINITY ? 0.f : mx;  // a fully masked block: weights 0, max -inf
+      a = fast_exp2(a - ref);
+      b = fast_exp2(b - ref);
+      float l = a + b;
+      l += dpp_mov<0xB1>(l);
+      l += dpp_mov<0x4E>(l);
+      l += dpp_mov<0x141>(l);
+      l += dpp_mov<0x140>(l);
+      if (m < p.M) {
+        bf16_t* o = (bf16_t*)p.epi.out;
+        o[frag_idx(m, c0 + col, p.epi.ldo)] = f2bf(a);
+        o[frag_idx(m, c0 + 16 + col, p.epi.ldo)] = f2bf(b);
+        if (col == 0) *(float2*)(p.epi.stats + 2 * ((long)m * nblk + bx)) = make_float2(mx, l);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int m = row0 + grp * 4 + e;
@@ -921,6 +975,10 @@ static hipError_t launch_chunk_spw(const ChunkP& p, int kind, dim3 grid, hipStre
       else hipLaunchKernelGGL((k_chunk<1, MB, EPI_QKV, SPW, false>), grid, dim3(256), 0, s, p);
       break;
     case EPI_CACHE: hipLaunchKernelGGL((k_chunk<1, MB, EPI_CACHE, SPW, false>), grid, dim3(256), 0, s, p); break;
+    case EPI_SCORES:
+      if (rs) hipLaunchKernelGGL((k_chunk<2, MB, EPI_SCORES, SPW, true>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((k_chunk<2, MB, EPI_SCORES, SPW, false>), grid, dim3(256), 0, s, p);
+      break;
     case EPI_PARTIAL: hipLaunchKernelGGL((k_chunk<1, MB, EPI_PARTIAL, SPW, false>), grid, dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
@@ -944,11 +1002,16 @@ hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int 
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
   if (M > 64 || K % 32 || N % 32) return hipErrorInvalidValue;
   if (epi.kind != EPI_STORE && epi.kind != EPI_PARTIAL && epi.kind != EPI_GEGLU && epi.kind != EPI_QKV &&
-      epi.kind != EPI_CACHE)
+      epi.kind != EPI_CACHE && epi.kind != EPI_SCORES)
     return hipErrorInvalidValue;
   int used, per;
   chunk_plan(K, splits, &used, &per);
   if (used > 1 && !ws) return hipErrorInvalidValue;
+  // scores: whole 32-key blocks of whole heads, one K chunk, bf16 fragment-layout weights out
+  if (epi.kind == EPI_SCORES &&
+      (used > 1 || !epi.out || !epi.stats || epi.ldo != N || epi.npad <= 0 || epi.npad % 32 || N % epi.npad ||
+       epi.npre <= 0 || epi.npre > epi.npad || ((uintptr_t)epi.stats & 7)))
+    return hipErrorInvalidValue;
   // row scales apply to one K chunk's finished sums (no partials), at most 64 partials a row
   if (epi.rss && (used > 1 || epi.kind == EPI_PARTIAL || epi.kind == EPI_CACHE ||
                   (epi.nss != 8 && epi.nss != 16 && epi.nss != 32 && epi.nss != 64) || epi.rdim <= 0 ||
@@ -957,7 +1020,7 @@ hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int 
   const Prefetch pf = prefetch ? *prefetch : Prefetch{};
   if (pf.blocks < 0 || pf.blocks > 1024 || (pf.blocks && !pf.sink)) return hipErrorInvalidValue;
   const bool reduce = used > 1 && epi.kind != EPI_PARTIAL;
-  const int nb = epi.kind == EPI_GEGLU && !reduce ? 2 : 1;
+  const int nb = (epi.kind == EPI_GEGLU || epi.kind == EPI_SCORES) && !reduce ? 2 : 1;
   const int kind = reduce ? EPI_PARTIAL : epi.kind;
   const int mb = (M + 15) / 16;
   // One 16-column block per workgroup (plain and QKV stores): with all rows
@@ -966,7 +1029,7 @@ hipError_t gemm_chunk(const uint16_t* Af, const uint16_t* Wf, int M, int N, int 
   // slice read once per row block, from L2) moves far fewer bytes per CU:
   // cross query 5.7 -> about 4.8 us at 50 rows.  Two-column GeGLU workgroups
   // already fill the chip and would read their weights four times over.
-  const int rsplit = used == 1 && mb > 1 && (kind == EPI_STORE || kind == EPI_QKV) ? 1 : 0;
+  const int rsplit = used == 1 && mb > 1 && (kind == EPI_STORE || kind == EPI_QKV || kind == EPI_SCORES) ? 1 : 0;
   ChunkP p{Af, Wf, M, N, K, per * 32, epi, ws, pf, rsplit};
   const int gy = rsplit ? mb : used;
   const dim3 grid(N / (16 * nb), gy, prefetch_depth(N / (16 * nb) * gy, pf.blocks));
@@ -1110,11 +1173,114 @@ hipError_t gemm_chunk_resnorm(const uint16_t* Af, const uint16_t* Wf, int M, int
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ absorbed cross attention: residual update
+// k_chunk_probres: k_chunk_res with A = the scores kernel's block weights
+// 2^(s - r) (K = heads x padded keys, one k-step per 32-key block).  Each
+// k-step's product goes to its own accumulator; thread (row, head) < 16 x heads
+// combines the head's block statistics into the scale 2^(r - R) / L of each
+// block (R the head's max, L its weight sum), and a wave adds its k-steps'
+// products scaled by their blocks' factors, so each head's weights are
+// normalised before the heads are summed.  The statistics are requested first,
+// so the scales are formed while the operands are still in flight.
+constexpr int kProbMaxKS = 128, kProbMaxBph = 16;
+
+template <int SPW>
+__global__ __launch_bounds__(512) void k_chunk_probres(ResP p, const float* stats, int bph) {
+  __shared__ float red[8][4][64];
+  __shared__ __attribute__((aligned(16))) float cs[kProbMaxKS][16];  // [k-step][row] scale
+  if (prefetch_layer(p.pf)) return;
+  const int bx = kResXcdMajor && !(gridDim.x & 7) ? (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  const int rb = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int KS = p.K >> 5, sb = w * SPW;
+  const int nsteps = max(0, min(SPW, KS - sb));
+  const int n = bx * 16 + col;
+  // this thread's (row, head): the head's block statistics
+  const int heads = KS / bph;
+  const int sr = threadIdx.x & 15, sh = min((int)threadIdx.x >> 4, heads - 1);
+  const float2* sp = (const float2*)stats + (long)(rb * 16 + sr) * KS + sh * bph;
+  float2 st[kProbMaxBph];
+#pragma unroll
+  for (int i = 0; i < kProbMaxBph; ++i) st[i] = sp[min(i, bph - 1)];
+  const u32x4_t* Wv = (const u32x4_t*)p.W + lane;
+  const u32x4_t* Av = (const u32x4_t*)p.A + lane;
+  u32x4_t wv[SPW], av[SPW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const int ks = min(sb + s, KS - 1);  // clamped; steps past the range are masked below
+    wv[s] = Wv[((long)bx * KS + ks) * 64];
+    av[s] = Av[((long)rb * KS + ks) * 64];
+  }
+  float hold[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) hold[e] = p.h[(long)min(rb * 16 + grp * 4 + e, p.M - 1) * p.ldh + n];
+  const float g1 = p.gain ? 1.0f + p.gain[n] : 0.f;
+  __builtin_amdgcn_sched_barrier(0);
+  if ((int)threadIdx.x < 16 * heads) {
+    float R = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kProbMaxBph; ++i)
+      if (i < bph) R = fmaxf(R, st[i].x);
+    float L = 0.f;
+#pragma unroll
+    for (int i = 0; i < kProbMaxBph; ++i)
+      if (i < bph) L += st[i].y * fast_exp2(st[i].x - R);
+    const float inv = L > 0.f ? 1.0f / L : 0.f;  // rows past M: zero statistics, zero scales
+#pragma unroll
+    for (int i = 0; i < kProbMaxBph; ++i)
+      if (i < bph) cs[sh * bph + i][sr] = fast_exp2(st[i].x - R) * inv;
+  }
+  f32x4_t pr[SPW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const u32x4_t a4 = s < nsteps ? av[s] : u32x4_t{0, 0, 0, 0};
+    pr[s] = mfma16x16x32(as_bf16x8(a4), as_bf16x8(wv[s]), f32x4_t{0.f, 0.f, 0.f, 0.f});
+  }
+  __syncthreads();
+  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    if (s < nsteps) {
+      const f32x4_t c = *(const f32x4_t*)&cs[sb + s][grp * 4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[s & 1][e] = fmaf(c[e], pr[s][e], acc[s & 1][e]);
+    }
+  }
+  res_finish(p, acc, hold, g1, red, w, lane, n, rb);
+}
+
+hipError_t gemm_chunk_probres(const uint16_t* pw, const float* stats, int bph, const uint16_t* Wf, int M, int N,
+                              int K, float* h, int ldh, const float* gain, uint16_t* xb, float* ss, hipStream_t s,
+                              const Prefetch* prefetch) {
+  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  const int KS = K / 32;
+  if (M > 64 || N % 128 || N > 1024 || K % 32 || KS > kProbMaxKS || !h || !stats || (gain && (!xb || !ss)) ||
+      bph <= 0 || bph > kProbMaxBph || KS % bph || KS / bph > 32 || ((uintptr_t)stats & 7))
+    return hipErrorInvalidValue;
+  const Prefetch pf = prefetch ? *prefetch : Prefetch{};
+  if (pf.blocks < 0 || pf.blocks > 1024 || (pf.blocks && !pf.sink)) return hipErrorInvalidValue;
+  ResP p{pw, Wf, M, N, K, h, ldh, gain, xb, ss, pf};
+  const int rbs = (M + 15) / 16, wgs = N / 16 * rbs;
+  const dim3 grid(N / 16, rbs, prefetch_depth(wgs, pf.blocks));
+  // k-steps per wave: the fewest of these that cover an eighth of K
+  const int spw = (KS + 7) / 8;
+  if (spw <= 1) hipLaunchKernelGGL(k_chunk_probres<1>, grid, dim3(512), 0, s, p, stats, bph);
+  else if (spw <= 2) hipLaunchKernelGGL(k_chunk_probres<2>, grid, dim3(512), 0, s, p, stats, bph);
+  else if (spw <= 4) hipLaunchKernelGGL(k_chunk_probres<4>, grid, dim3(512), 0, s, p, stats, bph);
+  else if (spw <= 8) hipLaunchKernelGGL(k_chunk_probres<8>, grid, dim3(512), 0, s, p, stats, bph);
+  else if (spw <= 9) hipLaunchKernelGGL(k_chunk_probres<9>, grid, dim3(512), 0, s, p, stats, bph);
+  else if (spw <= 10) hipLaunchKernelGGL(k_chunk_probres<10>, grid, dim3(512), 0, s, p, stats, bph);
+  else if (spw <= 12) hipLaunchKernelGGL(k_chunk_probres<12>, grid, dim3(512), 0, s, p, stats, bph);
+  else hipLaunchKernelGGL(k_chunk_probres<16>, grid, dim3(512), 0, s, p, stats, bph);
+  return hipGetLastError();
+}
+
 size_t gemm_chunk_group_bytes(int M, int N, int K, int kind, int splits) {
   if (M > 64 || K % 32 || N % 32) return 0;
   int used, per;
   chunk_plan(K, splits, &used, &per);
-  const int nb = kind == EPI_GEGLU && used == 1 ? 2 : 1;
+  const int nb = (kind == EPI_GEGLU || kind == EPI_SCORES) && used == 1 ? 2 : 1;
   const int gx = N / (16 * nb);
   return gx % 8 ? 0 : (size_t)nb * 16 * K * 2;
 }
@@ -1126,6 +1292,29 @@ __global__ void k_frag_pack(const u32x4_t* src, int N, int K, uint16_t* dst) {
     const int n = (int)(v / (K / 8)), k = (int)(v % (K / 8)) * 8;
     *(u32x4_t*)(dst + frag_idx(n, k, K)) = src[v];
   }
+}
+
+// row-major [R][C] -> fragment layout of the transpose [C][R]: a thread gathers
+// the 8 source rows of one output vector (a one-time weight transform)
+__global__ void k_frag_pack_t(const uint16_t* src, int R, int C, uint16_t* dst) {
+  const long vecs = (long)C * (R / 8);
+  for (long v = blockIdx.x * (long)blockDim.x + threadIdx.x; v < vecs; v += (long)gridDim.x * blockDim.x) {
+    const int n = (int)(v % C), k = (int)(v / C) * 8;  // consecutive threads: consecutive source columns
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)src[(long)(k + 2 * i) * C + n] | ((uint32_t)src[(long)(k + 2 * i + 1) * C + n] << 16);
+    *(u32x4_t*)(dst + frag_idx(n, k, R)) = u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+}
+
+hipError_t frag_pack_t(const uint16_t* src, int R, int C, uint16_t* dst, hipStream_t s) {
+  if (R <= 0 || C <= 0) return hipSuccess;
+  if (C % 16 || R % 32) return hipErrorInvalidValue;
+  const long vecs = (long)C * (R / 8);
+  const int blocks = (int)std::min<long>((vecs + 255) / 256, 8192);
+  hipLaunchKernelGGL(k_frag_pack_t, dim3(blocks), dim3(256), 0, s, src, R, C, dst);
+  return hipGetLastError();
 }
 
 hipError_t frag_pack(const uint16_t* src, int N, int K, uint16_t* dst, hipStream_t s) {

@@ -42,12 +42,19 @@ enum EpiKind {
                   // (t, d) row-major (out_frag == 0) or, with out_frag, K in
                   // frag_idx and V in vfrag_idx order (common.h)
   EPI_PARTIAL = 4,// raw fp32 partial sums to ws[split][m][n], left for a row kernel
-  EPI_QKV = 5     // fused self-attention projection, row m = (b, t) with b = m / npre:
+  EPI_QKV = 5,    // fused self-attention projection, row m = (b, t) with b = m / npre:
                   // columns n < nq go to out[m * ldo + n] (rows), the next hkv * hd
                   // to kout and the last hkv * hd to vout, in blocks of npad * hd
                   // elements, block h of batch b at (b * kv_bs / (npad * hd) + h)
                   // (kv_bs = 0: hkv * npad * hd); bf16 K / V in frag_idx /
                   // vfrag_idx order, fp32 (out_f32) as rows t * hd + d
+  EPI_SCORES = 6  // cross-attention scores in log2 units, one observation: column
+                  // n = j * npad + t is key t of query head j (npad keys per head, a
+                  // multiple of 32); keys t >= klen[0] (or npre when klen is null)
+                  // are masked.  Per row m and 32-column block c (one head's keys):
+                  // r = the block's max (0 when every key is masked), out (bf16,
+                  // frag_idx with K = ldo) = 2^(s - r), stats[m * ldo / 32 + c] =
+                  // {r, sum of those weights in fp32} (gemm_chunk only, one K chunk)
 };
 
 struct Epilogue {
@@ -68,6 +75,13 @@ struct Epilogue {
   const float* beta = nullptr;
   int32_t* acc_out = nullptr;  // optional raw int32 accumulators [M][N]
   int out_frag = 0;  // bf16 output in fragment layout (frag_idx with K = ldo) instead of rows
+  // EPI_CACHE, bf16, one observation: the values also go to vcopy in frag_idx
+  // order, block (l, h) of npad * hd elements at (l * hkv + h) * npad * hd (the
+  // operand order the absorbed cross-attention products contract over hd in)
+  void* vcopy = nullptr;
+  // EPI_SCORES: per-row block maxima and sums, visible keys
+  float* stats = nullptr;
+  const int* klen = nullptr;
   // RMSNorm folded into a product (gemm_chunk, one K chunk): when rss is set,
   // output row m is first scaled by 1 / sqrt(S_m / rdim + reps), S_m the sum
   // of row m's nss partial sums of squares in rss as gemm_chunk_resnorm lays
@@ -124,12 +138,41 @@ hipError_t gemm_chunk_resnorm(const uint16_t* Af, const uint16_t* Wf, int M, int
                               const float* gain, uint16_t* xb, float* ss, hipStream_t s, const Prefetch* prefetch);
 // The Prefetch `group` for the weights of gemm_chunk_resnorm (0: ungrouped).
 size_t gemm_chunk_resnorm_group_bytes(int N, int K);
+// The residual update of an absorbed cross-attention sublayer, as
+// gemm_chunk_resnorm with A = the softmax weights of gemm_chunk's EPI_SCORES
+// output (pw: 2^(s - r) per 32-key block, stats: {r, block sum} per row and
+// block, K = Hq * npad columns, bph = npad / 32 blocks per head): each block's
+// products are scaled by 2^(r - R) / L, R and L the max and weight sum over its
+// head's blocks, before they are summed, so h += softmax(S) Wvo^T head by head.
+// K % 32 == 0, K <= 4096, bph <= 16, K / 32 / bph <= 32 heads.
+hipError_t gemm_chunk_probres(const uint16_t* pw, const float* stats, int bph, const uint16_t* Wf, int M, int N,
+                              int K, float* h, int ldh, const float* gain, uint16_t* xb, float* ss, hipStream_t s,
+                              const Prefetch* prefetch);
+// Products of the absorbed cross attention for one observation and every
+// expert layer (bf16, fragment layouts; Np keys per head block, a multiple of
+// 32; qe = Hq * hd; layer l's blocks at l * the per-layer stride):
+//   wqk[l] [Hq Np][d_e]: row j Np + t = sl2 * sum_d K_l,g(j)[t][d] Wq_l[j hd + d][:]
+//     (k: cache keys, frag_idx order; wqT: Wq_l transposed, [d_e][qe]);
+//   wvo[l] [d_e][Hq Np]: column j Np + t = sum_d Wo_l[:][j hd + d] V_l,g(j)[t][d]
+//     (v: cache values in frag_idx order; wo: [d_e][qe]).
+// g(j) = j * Hkv / Hq.  k_ls / v_ls: elements between layers of k / v; wq_ls /
+// wo_ls: between layers of wqT / wo; out_ls: between layers of wqk and wvo.
+struct AbsorbP {
+  const uint16_t *k, *v, *wqT, *wo;
+  uint16_t *wqk, *wvo;
+  long k_ls, v_ls, wq_ls, wo_ls, out_ls;
+  int L, Hq, Hkv, hd, Np, d_e;
+  float sl2;
+};
+hipError_t absorb_products(const AbsorbP& p, hipStream_t s);
 // Bytes of fragment-layout weight that one column group of gemm_chunk reads
 // (the workgroup grid's x index), or 0 when the groups do not map to XCDs
 // round robin (grid width not a multiple of 8): the `group` of a Prefetch.
 size_t gemm_chunk_group_bytes(int M, int N, int K, int kind, int splits);
 // row-major bf16 [N][K] -> fragment layout (N % 16 == 0, K % 32 == 0)
 hipError_t frag_pack(const uint16_t* src, int N, int K, uint16_t* dst, hipStream_t s);
+// row-major bf16 [R][C] -> fragment layout of its transpose [C][R] (C % 16 == 0, R % 32 == 0)
+hipError_t frag_pack_t(const uint16_t* src, int R, int C, uint16_t* dst, hipStream_t s);
 
 // Same contraction in fp32 on the vector ALU (fp32 workloads); K % 16 == 0.
 hipError_t gemm_f32(const float* A, int lda, const float* W, int ldw, int M, int N, int K,

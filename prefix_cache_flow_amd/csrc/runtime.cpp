@@ -288,6 +288,12 @@ struct vla_model {
   // model was created with VLA_FOLD=0 in the environment (then it runs them as
   // row kernels, in the persistent step's summation order)
   bool fold = true;
+  // Absorbed cross attention (batch-1 encodes): the encode also forms each
+  // layer's Wq^T K^T and V Wo^T, and the solver runs each cross sublayer as two
+  // products; off with VLA_ABSORB=0 in the environment at creation.  wqT holds
+  // every layer's cross-query weights transposed, [L_e][d_e][Hq_e hd_e].
+  bool absorb = false;
+  uint16_t* wqT = nullptr;
   float* egains = nullptr;
   unsigned* fbar = nullptr;
   unsigned* ferr = nullptr;
@@ -305,6 +311,11 @@ struct vla_kv_cache {
   int B = 0, N = 0;
   void* storage = nullptr;
   int* lens = nullptr;  // per-observation prefix lengths, in the storage's tail
+  // absorbed cross-attention products after the lengths (null: none), layer l
+  // at + l * ab_ls elements: Wqk [Hq_e Np][d_e] and Wvo [d_e][Hq_e Np]
+  uint16_t* wqk = nullptr;
+  uint16_t* wvo = nullptr;
+  long ab_ls = 0;
 };
 
 static std::mutex g_mu;
@@ -617,6 +628,14 @@ static vla_status build_weights(vla_model* m, const vla_weights* w, hipStream_t 
       TRY(put_gain(m, &E.a2, src.t[src.i++], c.d_e, s));
       const void* wqc = src.t[src.i++];
       TRY(expert_weight(&E.wqc, qe, c.d_e, [&](void* d) { return put_rows(m, d, 0, wqc, qe, c.d_e, s); }));
+      if (m->absorb) {
+        // the staging buffer still holds the row-major cross-query weights
+        if (!m->wqT) TRY(dev_alloc(m, (void**)&m->wqT, (size_t)c.L_e * c.d_e * qe * 2));
+        TRY([&]() -> vla_status {
+          HIP_TRY(frag_pack_t((const uint16_t*)stage, (int)qe, c.d_e, m->wqT + (size_t)e * c.d_e * qe, s));
+          return VLA_OK;
+        }());
+      }
       const void* woc = src.t[src.i++];
       TRY(expert_weight(&E.woc, c.d_e, qe, [&](void* d) { return put_rows(m, d, 0, woc, c.d_e, qe, s); }));
     }
@@ -684,6 +703,20 @@ static vla_status setup_fused(vla_model* m, hipStream_t s) {
   return VLA_OK;
 }
 
+// Whether the model's batch-1 solver can run the absorbed cross sublayer: bf16
+// cross attention with the chunk chain's folded norms (the same shape limits),
+// at most 32 query heads, unless VLA_ABSORB=0 is set at creation.
+static bool absorb_capable(const vla_model* m) {
+  const vla_model_config& c = m->cfg;
+  const char* env = getenv("VLA_ABSORB");
+  if ((env && env[0] == '0') || m->f32 || m->joint || !m->fold || c.H > 64 || c.Hq_e > 32) return false;
+  int used = 0, kc = 0;
+  gemm_chunk_plan(c.d_e, 1, &used, &kc);
+  const int d8 = c.d_e / 128, qe = c.Hq_e * c.hd_e;
+  return used == 1 && c.d_e % 128 == 0 && (d8 == 1 || d8 == 2 || d8 == 4 || d8 == 8) && qe % 32 == 0 &&
+         qe <= 4096 && c.F_e % 32 == 0 && c.F_e <= 4096 && (c.hd_e == 64 || c.hd_e == 128 || c.hd_e == 256);
+}
+
 extern "C" vla_status vla_model_create(const vla_model_config* cfg, const vla_weights* weights, void* stream,
                                        vla_model** out) {
   if (!out) return fail(VLA_ERR_INVALID_ARGUMENT, "out is NULL");
@@ -713,10 +746,12 @@ extern "C" vla_status vla_model_create(const vla_model_config* cfg, const vla_we
   }
   m->w2a8 = cfg->precision == VLA_W2A8_BF16;
   m->joint = cfg->attn_mode == VLA_ATTN_JOINT;
+  m->absorb = absorb_capable(m);
   (void)hipGetDevice(&m->device);
   hipStream_t s = (hipStream_t)stream;
   st = build_weights(m, weights, s);
   if (st == VLA_OK) st = setup_fused(m, s);
+  if (m->fused) m->absorb = false;  // the persistent step reads the cached keys and values
   if (st == VLA_OK && (hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking) != hipSuccess ||
                        hipEventCreate(&m->ev0) != hipSuccess || hipEventCreate(&m->ev1) != hipSuccess))
     st = fail(VLA_ERR_DEVICE, "stream/event creation failed");
@@ -752,6 +787,22 @@ extern "C" vla_status vla_model_destroy(vla_model* m) {
 // operand orders (padding rows zero), fp32 blocks are plain rows.
 static int64_t key_rows(const vla_model* m, int64_t n) { return m->f32 ? n : (n + 31) / 32 * 32; }
 
+// Padded keys per head of the absorbed products an encode of B observations of
+// N tokens forms (0: none): one observation, at most 16 key tiles per head and
+// 4096 score columns in all.
+static int64_t absorb_np(const vla_model* m, int64_t B, int64_t N) {
+  if (!m->absorb || B != 1) return 0;
+  const int64_t np = key_rows(m, N);
+  return np / 32 <= 16 && m->cfg.Hq_e * np <= 4096 ? np : 0;
+}
+// Bytes of those products: per layer Wqk and Wvo (bf16), then every layer's
+// values in frag_idx order (the operand the Wvo product reads)
+static size_t absorb_bytes(const vla_model* m, int64_t B, int64_t N) {
+  const int64_t np = absorb_np(m, B, N);
+  const vla_model_config& c = m->cfg;
+  return np ? (size_t)c.L_e * (2 * (size_t)c.Hq_e * np * c.d_e + (size_t)c.Hkv_e * np * c.hd_e) * 2 : 0;
+}
+
 // ============================================================== workspace
 // Byte layout of the model workspace for `rows` prefix tokens and `erows` chunk rows.
 struct WS {
@@ -778,6 +829,8 @@ struct WS {
   void* emlp;       // [erows][F_e]
   float* epart;     // split-K partials of the expert
   float* ess;       // folded norms: partial sums of squares of the residual [d_e / 16][64]
+  void* esc;        // absorbed cross attention: score weights, bf16 fragment layout [64][<= 4096]
+  float* est;       // absorbed cross attention: {max, sum} per row and 32-key block [64][<= 128][2]
   unsigned* sink;   // 64 words for the prefetch kernel
   size_t total;
   // byte sizes of the chunk buffers (bounds of the persistent step's accesses)
@@ -889,6 +942,11 @@ static WS plan(const vla_model* m, int64_t rows, int64_t erows, int64_t kvrows, 
   w.n_epart = (size_t)expert_part_floats(c, erows) * 4;
   w.epart = (float*)take(w.n_epart);
   w.ess = (float*)take((size_t)std::max(1, c.d_e / 16) * 64 * 4);
+  if (m->absorb) {
+    // rows past the chunk are never written: zero weights and statistics
+    w.esc = take((size_t)64 * 4096 * 2);
+    w.est = (float*)take((size_t)64 * 128 * 2 * 4);
+  }
   w.sink = (unsigned*)take(256);
   w.total = off;
   return w;
@@ -1011,7 +1069,7 @@ static Epilogue epi_store(void* out, int ldo, int out_f32) {
 // fills all N positions).  Rows past an observation's length are zeroed on the
 // way in, and their keys are masked in the prefix attention.
 static vla_status run_prefix(vla_model* m, const void* x, int x_bf16, int B, int N, const int* lens, void* kv,
-                             const WS& w, hipStream_t s) {
+                             const WS& w, hipStream_t s, uint16_t* ab = nullptr) {
   const vla_model_config& c = m->cfg;
   const int M = B * N;
   const int qw = c.Hq * c.hd, qkvw = (c.Hq + 2 * c.Hkv) * c.hd;
@@ -1188,15 +1246,42 @@ static vla_status run_prefix(vla_model* m, const void* x, int x_bf16, int B, int
   ce.npad = (int)key_rows(m, N);
   ce.out_frag = m->f32 ? 0 : 1;
   const int ncache = c.L_e * 2 * c.Hkv_e * c.hd_e;
+  // absorbed products (one observation): the values are also written in frag_idx order for them
+  const int64_t anp = ab ? absorb_np(m, B, N) : 0;
+  uint16_t* vcopy = anp ? ab + (size_t)c.L_e * 2 * c.Hq_e * anp * c.d_e : nullptr;
+  ce.vcopy = vcopy;
   // padding key rows of the last tile must hold finite values (zero weight times value)
-  if (ce.npad > N)
+  if (ce.npad > N) {
     K_TRY(zero_tails(kv, (long)B * c.L_e * 2 * c.Hkv_e, (long)ce.npad * c.hd_e, 32 * c.hd_e, s), "cache padding");
-  ProbeScope ps(m, VLA_PROBE_CACHE, s);
-  for (int rep = 0; rep < ps.reps(); ++rep) {
-    if (m->f32)
-      K_TRY(gemm_f32((const float*)w.u, c.d_p, (const float*)m->wcache, c.d_p, M, ncache, c.d_p, ce, s), "cache");
-    else
-      K_TRY(mm_frag(w.u, m->wcache, M, ncache, c.d_p, ce, w.part, s), "cache");
+    if (vcopy) K_TRY(zero_tails(vcopy, (long)c.L_e * c.Hkv_e, (long)ce.npad * c.hd_e, 32 * c.hd_e, s), "value padding");
+  }
+  {
+    ProbeScope ps(m, VLA_PROBE_CACHE, s);
+    for (int rep = 0; rep < ps.reps(); ++rep) {
+      if (m->f32)
+        K_TRY(gemm_f32((const float*)w.u, c.d_p, (const float*)m->wcache, c.d_p, M, ncache, c.d_p, ce, s), "cache");
+      else
+        K_TRY(mm_frag(w.u, m->wcache, M, ncache, c.d_p, ce, w.part, s), "cache");
+    }
+  }
+  if (anp) {
+    // each layer's Wq^T K^T (scaled to log2 units) and V Wo^T from the cache just written
+    AbsorbP ap{};
+    const int qe = c.Hq_e * c.hd_e;
+    ap.k = (const uint16_t*)kv;
+    ap.v = vcopy;
+    ap.wqT = m->wqT;
+    ap.wo = (const uint16_t*)m->el[0].woc;
+    ap.wqk = ab;
+    ap.wvo = ab + (size_t)c.Hq_e * anp * c.d_e;
+    ap.k_ls = 2L * c.Hkv_e * anp * c.hd_e;
+    ap.v_ls = (long)c.Hkv_e * anp * c.hd_e;
+    ap.wq_ls = (long)c.d_e * qe;
+    ap.wo_ls = c.L_e > 1 ? (long)(((const char*)m->el[1].woc - (const char*)m->el[0].woc) / 2) : 0;
+    ap.out_ls = 2L * c.Hq_e * anp * c.d_e;
+    ap.L = c.L_e; ap.Hq = c.Hq_e; ap.Hkv = c.Hkv_e; ap.hd = c.hd_e; ap.Np = (int)anp; ap.d_e = c.d_e;
+    ap.sl2 = 1.4426950408889634f / sqrtf((float)c.hd_e);
+    K_TRY(absorb_products(ap, s), "absorbed products");
   }
   return VLA_OK;
 }
@@ -1209,7 +1294,8 @@ static size_t kv_core_bytes(const vla_model* m, int32_t batch, int32_t n_prefix)
 
 extern "C" size_t vla_kv_cache_bytes(const vla_model* m, int32_t batch, int32_t n_prefix) {
   if (!live_model(m) || batch <= 0 || n_prefix <= 0) return 0;
-  return (kv_core_bytes(m, batch, n_prefix) + 255) / 256 * 256 + ((size_t)batch * 4 + 255) / 256 * 256;
+  return (kv_core_bytes(m, batch, n_prefix) + 255) / 256 * 256 + ((size_t)batch * 4 + 255) / 256 * 256 +
+         absorb_bytes(m, batch, n_prefix);
 }
 
 extern "C" vla_status vla_prefix_encode_ex(vla_model* m, const void* x, int32_t x_dtype, int32_t batch,
@@ -1235,9 +1321,11 @@ extern "C" vla_status vla_prefix_encode_ex(vla_model* m, const void* x, int32_t 
   vla_status st = get_ws(m, (int64_t)batch * n_prefix, 0, &w, (int64_t)batch * key_rows(m, n_prefix));
   if (st != VLA_OK) return st;
   int* lens = (int*)((char*)kv_storage + (kv_core_bytes(m, batch, n_prefix) + 255) / 256 * 256);
+  uint16_t* ab = absorb_bytes(m, batch, n_prefix) ? (uint16_t*)((char*)lens + ((size_t)batch * 4 + 255) / 256 * 256)
+                                                   : nullptr;
   if (timing) K_TRY(hipEventRecord(m->ev0, s), "event");
   if (lengths) K_TRY(set_lengths(lens, lengths, batch, n_prefix, s), "prefix lengths");
-  st = run_prefix(m, x, x_dtype == VLA_IN_BF16, batch, n_prefix, lengths ? lens : nullptr, kv_storage, w, s);
+  st = run_prefix(m, x, x_dtype == VLA_IN_BF16, batch, n_prefix, lengths ? lens : nullptr, kv_storage, w, s, ab);
   if (st != VLA_OK) return st;
   if (timing) {
     K_TRY(hipEventRecord(m->ev1, s), "event");
@@ -1255,6 +1343,12 @@ extern "C" vla_status vla_prefix_encode_ex(vla_model* m, const void* x, int32_t 
   k->N = n_prefix;
   k->storage = kv_storage;
   k->lens = lengths ? lens : nullptr;
+  if (ab) {
+    const int64_t np = absorb_np(m, batch, n_prefix);
+    k->ab_ls = 2L * m->cfg.Hq_e * np * m->cfg.d_e;
+    k->wqk = ab;
+    k->wvo = ab + (size_t)m->cfg.Hq_e * np * m->cfg.d_e;
+  }
   {
     std::lock_guard<std::mutex> g(g_mu);
     m->caches.insert(k);
@@ -1441,6 +1535,15 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
                     res_k(qe) && res_k(c.F_e);
   const size_t g_o = fold ? gemm_chunk_resnorm_group_bytes(c.d_e, qe) : g_o0;
   const size_t g_d = fold ? gemm_chunk_resnorm_group_bytes(c.d_e, c.F_e) : g_d0;
+  // absorbed cross sublayer (the encode formed the products): score columns, their weights and statistics
+  const bool absorbed = kv->wqk && fold && B == 1;
+  const int np_ab = absorbed ? (int)(kv->ab_ls / (2L * c.Hq_e * c.d_e)) : 0, ns_ab = c.Hq_e * np_ab;
+  const size_t b_ab = (size_t)ns_ab * c.d_e * es;
+  const size_t g_sc = absorbed ? gemm_chunk_group_bytes(M, ns_ab, c.d_e, EPI_SCORES, 1) : 0;
+  const size_t g_vo = absorbed ? gemm_chunk_resnorm_group_bytes(c.d_e, ns_ab) : 0;
+  Epilogue sc_e;
+  sc_e.kind = EPI_SCORES; sc_e.out = w.esc; sc_e.ldo = ns_ab; sc_e.stats = w.est;
+  sc_e.npad = np_ab; sc_e.npre = N; sc_e.klen = kv->lens;
   auto scaled = [&](Epilogue ep) {
     ep.rss = w.ess; ep.nss = c.d_e / 16; ep.rdim = c.d_e; ep.reps = eps;
     return ep;
@@ -1534,37 +1637,51 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
             K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
           }
         } else {
-          sa.pf = pfr(L.wos, b_o, g_o, L.wqc, b_q, g_q, 192);
+          sa.pf = absorbed ? pfr(L.wos, b_o, g_o, kv->wqk + (size_t)e * kv->ab_ls, b_ab, g_sc, 192)
+                           : pfr(L.wos, b_o, g_o, L.wqc, b_q, g_q, 192);
           {
             ProbeScope ps(m, VLA_PROBE_EXPERT_SELF_ATTN, s);
             for (int rep = 0; rep < ps.reps(); ++rep)
               K_TRY(attention_chunk(sa, s), "self attn");
           }
-          const Prefetch pf_kv = pfr(B == 1 ? ca.k : nullptr, B == 1 ? layer_kv : 0, 0, nullptr, 0, 0, 64);
-          if (fold) {
-            // the cache block goes with the cross query below: workgroups of this product hold too many
-            // registers for a prefetch workgroup to share their CU, so one would run after them
+          if (absorbed) {
+            // cross sublayer as two products: the scores from the normalised rows (with each
+            // 32-key block's max and weight sum), then the weights times Wvo into the residual
+            const uint16_t* wqk = kv->wqk + (size_t)e * kv->ab_ls;
+            const uint16_t* wvo = kv->wvo + (size_t)e * kv->ab_ls;
             K_TRY(gemm_chunk_resnorm((const uint16_t*)w.eattn, (const uint16_t*)L.wos, M, c.d_e, qe, w.E, c.d_e, L.a2,
                                      (uint16_t*)w.eu, w.ess, s, nullptr), "o_s");
+            const Prefetch pf_sc = pfr(wvo, b_ab, g_vo, L.wgu, b_gu, g_gu, 192);
+            K_TRY(mm(u, c.d_e, wqk, ns_ab, c.d_e, scaled(sc_e), 1, &pf_sc), "scores");
+            K_TRY(gemm_chunk_probres((const uint16_t*)w.esc, w.est, np_ab / 32, wvo, M, c.d_e, ns_ab, w.E, c.d_e, L.a3,
+                                     (uint16_t*)w.eu, w.ess, s, nullptr), "cross out");
           } else {
-            K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
-            K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr,
-                             &pf_kv), "norm");
-          }
-          const Epilogue qc_e = epi_store(w.eq, qe, 0);
-          K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, fold ? scaled(qc_e) : qc_e, 1, fold ? &pf_kv : nullptr), "q_c");
-          ca.pf = pfr(L.woc, b_o, g_o, L.wgu, b_gu, g_gu, 192);
-          {
-            ProbeScope ps(m, VLA_PROBE_EXPERT_CROSS_ATTN, s);
-            for (int rep = 0; rep < ps.reps(); ++rep)
-              K_TRY(attention_chunk(ca, s), "cross attn");
-          }
-          if (fold) {
-            K_TRY(gemm_chunk_resnorm((const uint16_t*)w.eattn, (const uint16_t*)L.woc, M, c.d_e, qe, w.E, c.d_e, L.a3,
-                                     (uint16_t*)w.eu, w.ess, s, nullptr), "o_c");
-          } else {
-            K_TRY(mm(w.eattn, qe, L.woc, c.d_e, qe, pe, S_o), "o_c");
-            K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
+            const Prefetch pf_kv = pfr(B == 1 ? ca.k : nullptr, B == 1 ? layer_kv : 0, 0, nullptr, 0, 0, 64);
+            if (fold) {
+              // the cache block goes with the cross query below: workgroups of this product hold too many
+              // registers for a prefetch workgroup to share their CU, so one would run after them
+              K_TRY(gemm_chunk_resnorm((const uint16_t*)w.eattn, (const uint16_t*)L.wos, M, c.d_e, qe, w.E, c.d_e, L.a2,
+                                       (uint16_t*)w.eu, w.ess, s, nullptr), "o_s");
+            } else {
+              K_TRY(mm(w.eattn, qe, L.wos, c.d_e, qe, pe, S_o), "o_s");
+              K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a2, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr,
+                               &pf_kv), "norm");
+            }
+            const Epilogue qc_e = epi_store(w.eq, qe, 0);
+            K_TRY(mm(u, c.d_e, L.wqc, qe, c.d_e, fold ? scaled(qc_e) : qc_e, 1, fold ? &pf_kv : nullptr), "q_c");
+            ca.pf = pfr(L.woc, b_o, g_o, L.wgu, b_gu, g_gu, 192);
+            {
+              ProbeScope ps(m, VLA_PROBE_EXPERT_CROSS_ATTN, s);
+              for (int rep = 0; rep < ps.reps(); ++rep)
+                K_TRY(attention_chunk(ca, s), "cross attn");
+            }
+            if (fold) {
+              K_TRY(gemm_chunk_resnorm((const uint16_t*)w.eattn, (const uint16_t*)L.woc, M, c.d_e, qe, w.E, c.d_e, L.a3,
+                                       (uint16_t*)w.eu, w.ess, s, nullptr), "o_c");
+            } else {
+              K_TRY(mm(w.eattn, qe, L.woc, c.d_e, qe, pe, S_o), "o_c");
+              K_TRY(resid_norm(w.E, c.d_e, w.epart, S_o, M, c.d_e, L.a3, eps, w.eu, 0, c.d_e, nullptr, nullptr, s, fr), "norm");
+            }
           }
         }
         Epilogue g = epi_store(w.emlp, c.F_e, 0);

@@ -32,7 +32,9 @@ SMALL_HD128_B2 = synth.config(1, name="small_hd128_b2", batch=2, n_prefix=40, d_
 
 
 def _model(cfg, w, b, fused, fold=False):
-    return build_model(cfg, w, b, env={"VLA_FUSED": "1" if fused else "0", "VLA_FOLD": "1" if fold else "0"})
+    # the folded chain with its cross sublayer as three kernels (the absorbed form has its own tests)
+    return build_model(cfg, w, b, env={"VLA_FUSED": "1" if fused else "0", "VLA_FOLD": "1" if fold else "0",
+                                       "VLA_ABSORB": "0"})
 
 
 def _run(cfg, model, z0, x0, timing=False):
