@@ -33,10 +33,13 @@ PEAK_HBM_GBS = 8000.0
 
 # HBM-side bytes from rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter
 # reads for a plain copy of known size (profiles/hbm_bytes_denoise_single_camera_bf16.md).  Valid for the
-# single-camera bf16 workload and the kernels as they were measured; None where no measurement stands.
+# single-camera bf16 workload with the absorbed cross sublayer and the kernels as they were measured; None where no
+# measurement stands.
 ATTN_KERNEL = "k_attn_chunk<256>"
-ATTN_TRAFFIC_BYTES_PER_LAUNCH = None   # mean over all launches of a bench run; not yet measured for the absorbed form
-DENOISE_TRAFFIC_BYTES_PER_STEP = None  # every kernel of one solver step; not yet measured for the absorbed form
+SCORES_KERNEL = "k_chunk<2, 1, 6, 8, true>"
+SCORES_TRAFFIC_BYTES_PER_LAUNCH = 27928594  # the absorbed score product, per launch
+ATTN_TRAFFIC_BYTES_PER_LAUNCH = 9596980   # mean over all launches of a bench run (prefix and expert self attention)
+DENOISE_TRAFFIC_BYTES_PER_STEP = 1893654122  # every kernel of one solver step (the denoise graph's nodes)
 
 
 def parse():
@@ -269,7 +272,15 @@ def probe_mean_ms(vla, model, kind, run):
     return (ms / n if n else None), n
 
 
-def dominant_kernel_roofline(vla, model, cfg, zt, xt, out, kv_storage):
+def scores_launch_bytes(c):
+    """Algorithmic bytes of one launch of the absorbed score product: its weights Wq_j^T K^T (Hq_e x n_prefix
+    rows of d_e, bf16) and the normalised chunk rows read once, the bf16 block weights and the fp32 block
+    statistics (max, sum per row and 32-key block) written once."""
+    M, S = c.batch * c.H, c.Hq_e * c.n_prefix
+    return 2 * S * c.d_e + 2 * M * c.d_e + 2 * M * S + 8 * M * (S // 32)
+
+
+def dominant_kernel_roofline(vla, model, cfg, zt, xt, out, kv_storage, absorbed=False):
     """Roofline of the kernel with the largest share of GPU time in the committed traces: the chunk
     attention kernel for the bf16 workloads (prefix attention in the encode, self and cross attention in
     every solver step), the int8 ternary GEMM for the ternary one.  Achieved = algorithmic bytes (or
@@ -308,6 +319,27 @@ def dominant_kernel_roofline(vla, model, cfg, zt, xt, out, kv_storage):
                 "per_shape": per, "timing": f"HIP events around {PROBE_REPEAT} back-to-back repeats of each launch, separate probe pass after the timed region, graphs off"}
     if cfg.precision != "bf16":
         return None
+    attention = attention_roofline(vla, model, cfg, encode, denoise, absorbed)
+    if not absorbed:
+        return attention
+    # the absorbed cross sublayer's score product is the largest share of the trace
+    ms, n = probe_mean_ms(vla, model, vla.PROBE_EXPERT_SCORES, denoise)
+    if ms is None:
+        return None
+    nb = scores_launch_bytes(cfg)
+    gbs = nb / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+            "traffic": SCORES_TRAFFIC_BYTES_PER_LAUNCH if (cfg.name == "single_camera_bf16") else None,
+            "kernel": SCORES_KERNEL + " (absorbed cross sublayer: score product with block max and sums)",
+            "avg_launch_us": ms * 1e3, "bytes_per_launch": nb, "launches_per_step": T * L_e,
+            "timing": f"HIP events around {PROBE_REPEAT} back-to-back repeats of each launch, separate probe pass after the timed region, graphs off",
+            "attention": attention}
+
+
+def attention_roofline(vla, model, cfg, encode, denoise, absorbed):
+    """The chunk attention kernel over one policy step's launches (prefix, expert self, and expert cross
+    unless the cross sublayer is absorbed)."""
+    L_p, T, L_e = cfg.L_p, cfg.steps, cfg.L_e
     b = attn_launch_bytes(cfg)
     classes = [("prefix", vla.PROBE_PREFIX_ATTN, encode, L_p), ("self", vla.PROBE_EXPERT_SELF_ATTN, denoise, T * L_e)]
     if cfg.attn == "cross":
@@ -327,8 +359,8 @@ def dominant_kernel_roofline(vla, model, cfg, zt, xt, out, kv_storage):
         launches += count
     gbs = tot_b / (tot_t * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-            "traffic": ATTN_TRAFFIC_BYTES_PER_LAUNCH if (cfg.name == "single_camera_bf16") else None,
-            "kernel": ATTN_KERNEL + " (chunk attention: prefix, expert self and cross)",
+            "traffic": ATTN_TRAFFIC_BYTES_PER_LAUNCH if (cfg.name == "single_camera_bf16" and absorbed) else None,
+            "kernel": ATTN_KERNEL + " (chunk attention: " + ", ".join(per) + ")",
             "avg_launch_us": tot_t * 1e3 / launches, "bytes_per_launch": tot_b / launches,
             "launches_per_step": launches, "per_class": per,
             "timing": f"HIP events around {PROBE_REPEAT} back-to-back repeats of each launch, separate probe pass after the timed region, graphs off"}
@@ -453,7 +485,8 @@ def main():
     phases["denoise_mfma_frac"] = expert_step_flops(cfg) / (phases["denoise_step_ms"] * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
 
     # ---- roofline of the kernel with the largest share of GPU time, and one entry per phase
-    roofline = None if args.no_roofline else dominant_kernel_roofline(vla, model, cfg, zt, xt, out, kv_storage)
+    roofline = None if args.no_roofline else dominant_kernel_roofline(vla, model, cfg, zt, xt, out, kv_storage,
+                                                                       absorbed)
     d_gbs = sb / (phases["denoise_step_ms"] * 1e-3) / 1e9
     p_rate = pf / (phases["prefix_ms"] * 1e-3) / 1e12
     roofline_phases = {
@@ -462,7 +495,8 @@ def main():
                    "work_per_pass": pf, "ms": phases["prefix_ms"]},
         "denoise": {"bound": "hbm", "achieved": d_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": d_gbs / PEAK_HBM_GBS,
                     "bytes_per_step": sb, "step_ms": phases["denoise_step_ms"],
-                    "traffic": DENOISE_TRAFFIC_BYTES_PER_STEP if (args.config == 1 and args.attn == "cross") else None},
+                    "traffic": DENOISE_TRAFFIC_BYTES_PER_STEP if (args.config == 1 and args.attn == "cross" and absorbed)
+                    else None},
     }
 
     # ---- solver-step sweep (Eq. 3) and the two-stream pipelined rate: context, not the metric

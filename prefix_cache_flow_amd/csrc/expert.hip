@@ -298,103 +298,80 @@ hipError_t zero_tails(void* base, long nblk, long blk, int tail, hipStream_t s) 
 // step then needs two products per cross sublayer (scores, and weights times
 // Wvo into the residual) instead of query, attention and output kernels.
 //
-// k_absorb_qk: workgroup = 256 input features x 128 keys of one head and
-// layer; wave w owns 64 input features (4 row blocks) x the 8 key blocks:
-// D[k][t] = sum_d WqT[k][j hd + d] K[t][d] on the 16x16x32 MFMA (both operands
-// straight from their fragment layouts, 12 fragment loads per 32 MFMAs), so a
-// lane's four results are four consecutive k of output row j Np + t: one
-// 8-byte store, scaled by sl2 = log2(e) / sqrt(hd).
-template <int HD>
-__global__ __launch_bounds__(256) void k_absorb_qk(AbsorbP p) {
-  constexpr int DS = HD / 32;
+// k_absorb<HD, QK>: one layer, one query head j, 144 keys (9 key blocks) and
+// 256 output features (four waves of 4 row blocks).  The keys' (QK) or values'
+// fragments of every d-step are staged once in LDS and shared by the four
+// waves; each wave requests all its rows of WqT (QK) or Wo (the other operand,
+// columns j hd .. j hd + hd - 1) up front, so a workgroup waits on memory once.
+//   QK: D[k][t] = sum_d WqT[k][j hd + d] K[t][d]: a lane's four results are four
+//       consecutive k of output row j Np + t of wqk (one 8-byte store, scaled by
+//       sl2 = log2(e) / sqrt(hd)).
+//   VO: D[t][n] = sum_d V[t][d] Wo[n][j hd + d]: four consecutive keys of row n,
+//       column j Np + t of wvo (padding keys have zero values: zero columns).
+constexpr int kAbsXB = 9, kAbsYB = 4;
+
+template <int HD, bool QK>
+__global__ __launch_bounds__(256) void k_absorb(AbsorbP p) {
+  constexpr int DS = HD / 32, XB = kAbsXB, YB = kAbsYB, NX = DS * XB * 64;
+  __shared__ u32x4_t xs[DS * XB][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int tbs = p.Np / 16, tcs = (tbs + 7) / 8, kbs = p.d_e / 16;
+  const int tbs = p.Np / 16, tcs = (tbs + XB - 1) / XB, ybs = p.d_e / 16;
   const int j = blockIdx.y / tcs, tc = blockIdx.y % tcs, l = blockIdx.z;
   const int g = j * p.Hkv / p.Hq, qe = p.Hq * HD;
-  const int kb0 = (blockIdx.x * 4 + w) * 4;
-  if (kb0 >= kbs) return;
-  const u32x4_t* A = (const u32x4_t*)(p.wqT + l * p.wq_ls) + (long)j * DS * 64 + lane;
-  const u32x4_t* Bk = (const u32x4_t*)(p.k + l * p.k_ls + (long)g * p.Np * HD) + lane;
-  f32x4_t acc[4][8];
+  const int tb0 = tc * XB, yb0 = (blockIdx.x * 4 + w) * YB;
+  const u32x4_t* X = (const u32x4_t*)((QK ? p.k + l * p.k_ls : p.v + l * p.v_ls) + (long)g * p.Np * HD);
+  const u32x4_t* Y = (const u32x4_t*)(QK ? p.wqT + l * p.wq_ls : p.wo + l * p.wo_ls) + (long)j * DS * 64 + lane;
+  // every d-step of this wave's rows requested first, then the shared blocks
+  u32x4_t y[DS][YB];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[a][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int ds = 0; ds < DS; ++ds) {
-    u32x4_t af[4], b[8];
+    for (int a = 0; a < YB; ++a) y[ds][a] = Y[((long)min(yb0 + a, ybs - 1) * (qe / 32) + ds) * 64];
+  // shared operand: blocks tb0 .. tb0 + XB - 1 (clamped), every d-step
 #pragma unroll
-    for (int a = 0; a < 4; ++a) af[a] = A[((long)min(kb0 + a, kbs - 1) * (qe / 32) + ds) * 64];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) b[i] = Bk[((long)min(tc * 8 + i, tbs - 1) * DS + ds) * 64];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[a][i] = mfma16x16x32(as_bf16x8(af[a]), as_bf16x8(b[i]), acc[a][i]);
-  }
-  uint16_t* out = p.wqk + l * p.out_ls;
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    if (kb0 + a >= kbs) break;
-    const int k = (kb0 + a) * 16 + grp * 4;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int tb = tc * 8 + i;
-      if (tb >= tbs) break;
-      const u32x2_t pk = {pack_bf2(acc[a][i][0] * p.sl2, acc[a][i][1] * p.sl2),
-                          pack_bf2(acc[a][i][2] * p.sl2, acc[a][i][3] * p.sl2)};
-      *(u32x2_t*)(out + frag_idx(j * p.Np + tb * 16 + col, k, p.d_e)) = pk;
+  for (int r = 0; r < (NX + 255) / 256; ++r) {
+    const int i = r * 256 + (int)threadIdx.x;
+    if (NX % 256 == 0 || i < NX) {
+      const int f = i >> 6, ln = i & 63, xb = f / DS, ds = f - xb * DS;
+      xs[ds * XB + xb][ln] = X[((long)min(tb0 + xb, tbs - 1) * DS + ds) * 64 + ln];
     }
   }
-}
-
-// k_absorb_vo: workgroup = 64 keys x 512 output features of one head and
-// layer; wave w owns the 4 key blocks x 128 output features (8 column
-// blocks): D[t][n] = sum_d V[t][d] Wo[n][j hd + d], a lane's four results four
-// consecutive keys of output row n, column j Np + t (one 8-byte store).
-// Padding keys have zero values, so their columns are zero.
-template <int HD>
-__global__ __launch_bounds__(256) void k_absorb_vo(AbsorbP p) {
-  constexpr int DS = HD / 32;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  const int tbs = p.Np / 16, nbs = p.d_e / 16, ngs = (nbs + 31) / 32;
-  const int j = blockIdx.y / ngs, ng = blockIdx.y % ngs, l = blockIdx.z;
-  const int g = j * p.Hkv / p.Hq, qe = p.Hq * HD;
-  const int tb0 = blockIdx.x * 4, nb0 = ng * 32 + w * 8;
-  if (nb0 >= nbs) return;
-  const u32x4_t* A = (const u32x4_t*)(p.v + l * p.v_ls + (long)g * p.Np * HD) + lane;
-  const u32x4_t* Bw = (const u32x4_t*)(p.wo + l * p.wo_ls) + (long)j * DS * 64 + lane;
-  f32x4_t acc[4][8];
+  __syncthreads();
+  if (yb0 >= ybs) return;
+  f32x4_t acc[YB][XB];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < YB; ++a)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[a][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int ds = 0; ds < DS; ++ds) {
-    u32x4_t af[4], b[8];
+    for (int i = 0; i < XB; ++i) acc[a][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int a = 0; a < 4; ++a) af[a] = A[((long)min(tb0 + a, tbs - 1) * DS + ds) * 64];
+  for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) b[i] = Bw[((long)min(nb0 + i, nbs - 1) * (qe / 32) + ds) * 64];
+    for (int i = 0; i < XB; ++i) {
+      const u32x4_t x = xs[ds * XB + i][lane];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[a][i] = mfma16x16x32(as_bf16x8(af[a]), as_bf16x8(b[i]), acc[a][i]);
-  }
-  uint16_t* out = p.wvo + l * p.out_ls;
+      for (int a = 0; a < YB; ++a)
+        acc[a][i] = QK ? mfma16x16x32(as_bf16x8(y[ds][a]), as_bf16x8(x), acc[a][i])
+                       : mfma16x16x32(as_bf16x8(x), as_bf16x8(y[ds][a]), acc[a][i]);
+    }
   const int ns = p.Hq * p.Np;
+  uint16_t* out = (QK ? p.wqk : p.wvo) + l * p.out_ls;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    if (tb0 + a >= tbs) break;
-    const int t = (tb0 + a) * 16 + grp * 4;
+  for (int a = 0; a < YB; ++a) {
+    if (yb0 + a >= ybs) break;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (nb0 + i >= nbs) break;
-      const int n = (nb0 + i) * 16 + col;
-      const u32x2_t pk = {pack_bf2(acc[a][i][0], acc[a][i][1]), pack_bf2(acc[a][i][2], acc[a][i][3])};
-      *(u32x2_t*)(out + frag_idx(n, j * p.Np + t, ns)) = pk;
+    for (int i = 0; i < XB; ++i) {
+      if (tb0 + i >= tbs) break;
+      if (QK) {
+        const int k = (yb0 + a) * 16 + grp * 4, t = (tb0 + i) * 16 + col;
+        const u32x2_t pk = {pack_bf2(acc[a][i][0] * p.sl2, acc[a][i][1] * p.sl2),
+                            pack_bf2(acc[a][i][2] * p.sl2, acc[a][i][3] * p.sl2)};
+        *(u32x2_t*)(out + frag_idx(j * p.Np + t, k, p.d_e)) = pk;
+      } else {
+        const int t = (tb0 + i) * 16 + grp * 4, n = (yb0 + a) * 16 + col;
+        const u32x2_t pk = {pack_bf2(acc[a][i][0], acc[a][i][1]), pack_bf2(acc[a][i][2], acc[a][i][3])};
+        *(u32x2_t*)(out + frag_idx(n, j * p.Np + t, ns)) = pk;
+      }
     }
   }
 }
@@ -404,20 +381,20 @@ hipError_t absorb_products(const AbsorbP& p, hipStream_t s) {
   if (!p.k || !p.v || !p.wqT || !p.wo || !p.wqk || !p.wvo || p.Hq <= 0 || p.Hkv <= 0 || p.Hq % p.Hkv ||
       p.Np <= 0 || p.Np % 32 || p.d_e <= 0 || p.d_e % 128)
     return hipErrorInvalidValue;
-  const int tbs = p.Np / 16, nbs = p.d_e / 16;
-  const dim3 gq((nbs + 15) / 16, p.Hq * ((tbs + 7) / 8), p.L), gv((tbs + 3) / 4, p.Hq * ((nbs + 31) / 32), p.L);
+  const int tbs = p.Np / 16, ybs = p.d_e / 16;
+  const dim3 grid((ybs + 4 * kAbsYB - 1) / (4 * kAbsYB), p.Hq * ((tbs + kAbsXB - 1) / kAbsXB), p.L);
   switch (p.hd) {
     case 64:
-      hipLaunchKernelGGL(k_absorb_qk<64>, gq, dim3(256), 0, s, p);
-      hipLaunchKernelGGL(k_absorb_vo<64>, gv, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((k_absorb<64, true>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((k_absorb<64, false>), grid, dim3(256), 0, s, p);
       break;
     case 128:
-      hipLaunchKernelGGL(k_absorb_qk<128>, gq, dim3(256), 0, s, p);
-      hipLaunchKernelGGL(k_absorb_vo<128>, gv, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((k_absorb<128, true>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((k_absorb<128, false>), grid, dim3(256), 0, s, p);
       break;
     case 256:
-      hipLaunchKernelGGL(k_absorb_qk<256>, gq, dim3(256), 0, s, p);
-      hipLaunchKernelGGL(k_absorb_vo<256>, gv, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((k_absorb<256, true>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((k_absorb<256, false>), grid, dim3(256), 0, s, p);
       break;
     default: return hipErrorInvalidValue;
   }

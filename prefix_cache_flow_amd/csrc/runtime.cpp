@@ -1026,7 +1026,7 @@ extern "C" vla_status vla_probe_arm(vla_model* m, int32_t kind, int32_t max_laun
 
 extern "C" vla_status vla_probe_arm_ex(vla_model* m, int32_t kind, int32_t max_launches, int32_t repeat) {
   if (!live_model(m)) return fail(VLA_ERR_INVALID_HANDLE, "unknown model");
-  if (kind < VLA_PROBE_NONE || kind > VLA_PROBE_EXPERT_CROSS_ATTN) return fail(VLA_ERR_INVALID_ARGUMENT, "bad probe kind");
+  if (kind < VLA_PROBE_NONE || kind > VLA_PROBE_EXPERT_SCORES) return fail(VLA_ERR_INVALID_ARGUMENT, "bad probe kind");
   if (max_launches < 0 || max_launches > 100000) return fail(VLA_ERR_INVALID_ARGUMENT, "bad max_launches");
   if (repeat < 1 || repeat > 1000) return fail(VLA_ERR_INVALID_ARGUMENT, "repeat must be in 1..1000");
   m->probe_repeat = repeat;
@@ -1652,7 +1652,11 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
             K_TRY(gemm_chunk_resnorm((const uint16_t*)w.eattn, (const uint16_t*)L.wos, M, c.d_e, qe, w.E, c.d_e, L.a2,
                                      (uint16_t*)w.eu, w.ess, s, nullptr), "o_s");
             const Prefetch pf_sc = pfr(wvo, b_ab, g_vo, L.wgu, b_gu, g_gu, 192);
-            K_TRY(mm(u, c.d_e, wqk, ns_ab, c.d_e, scaled(sc_e), 1, &pf_sc), "scores");
+            {
+              ProbeScope ps(m, VLA_PROBE_EXPERT_SCORES, s);
+              for (int rep = 0; rep < ps.reps(); ++rep)
+                K_TRY(mm(u, c.d_e, wqk, ns_ab, c.d_e, scaled(sc_e), 1, &pf_sc), "scores");
+            }
             K_TRY(gemm_chunk_probres((const uint16_t*)w.esc, w.est, np_ab / 32, wvo, M, c.d_e, ns_ab, w.E, c.d_e, L.a3,
                                      (uint16_t*)w.eu, w.ess, s, nullptr), "cross out");
           } else {
