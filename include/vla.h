@@ -188,7 +188,7 @@ vla_status vla_model_destroy(vla_model* model);
  *   V block: with u = t%32, (t, d) at
  *            ((((t/32) * (hd_e/16) + d/16) * 64 + d%16 + 16*((u%16)/4)) * 8 + 4*(u/16) + u%4
  * For one observation of a bf16 cross-attention model whose solver runs the
- * absorbed cross sublayer (chunk of at most 64 rows, expert width a multiple
+ * absorbed cross sublayer (chunk of 17 to 64 rows, expert width a multiple
  * of 128 up to 1024, Hq_e <= 32, Np <= 512 and Hq_e * Np <= 4096, unless the
  * model was created with VLA_ABSORB=0 in the environment), the lengths are
  * followed by per-layer products of the cached keys and values that the

@@ -789,9 +789,11 @@ static int64_t key_rows(const vla_model* m, int64_t n) { return m->f32 ? n : (n 
 
 // Padded keys per head of the absorbed products an encode of B observations of
 // N tokens forms (0: none): one observation, at most 16 key tiles per head and
-// 4096 score columns in all.
+// 4096 score columns in all, and a chunk of more than one 16-row block (with
+// one block the two products take about as long as the three kernels they
+// replace, so the encode's extra work would not pay).
 static int64_t absorb_np(const vla_model* m, int64_t B, int64_t N) {
-  if (!m->absorb || B != 1) return 0;
+  if (!m->absorb || B != 1 || m->cfg.H <= 16) return 0;
   const int64_t np = key_rows(m, N);
   return np / 32 <= 16 && m->cfg.Hq_e * np <= 4096 ? np : 0;
 }

@@ -29,6 +29,9 @@ from prefix_cache_flow_amd import vla  # noqa: E402
 # grouped heads (two query heads per key/value head) and a prefix that is not whole 32-key tiles
 SMALL_GQA_ABS = synth.config(1, name="small_gqa_absorbed", n_prefix=90, d_p=256, L_p=2, Hq=4, Hkv=2, hd=64, F_p=512,
                              d_e=128, L_e=2, Hq_e=4, Hkv_e=2, hd_e=64, F_e=256, H=40, d_a=16, steps=2)
+# the ternary prefix with a chunk of two row blocks (one block keeps the three-kernel form)
+SMALL_W2A8_H20 = synth.config(4, name="small_w2a8_h20", n_prefix=100, d_p=256, L_p=2, Hq=2, Hkv=2, hd=128, F_p=384,
+                              d_e=128, L_e=2, Hq_e=2, Hkv_e=1, hd_e=64, F_e=256, H=20, d_a=7, steps=3)
 # head width 256 with 16 key tiles per head (the most the absorbed products take) and a 50-row chunk
 SMALL_HD256_ABS = synth.config(1, name="small_hd256_absorbed", n_prefix=500, d_p=256, L_p=2, Hq=4, Hkv=1, hd=64,
                                F_p=512, d_e=256, L_e=3, Hq_e=4, Hkv_e=1, hd_e=256, F_e=512, H=50, d_a=32, steps=3)
@@ -45,7 +48,7 @@ def _run(cfg, model, z0, x0, lengths=None):
     return res
 
 
-CASES = [(SMALL_BF16, None), (SMALL_GQA_ABS, None), (SMALL_HD256_ABS, None), (SMALL_W2A8, None),
+CASES = [(SMALL_BF16, None), (SMALL_GQA_ABS, None), (SMALL_HD256_ABS, None), (SMALL_W2A8_H20, None),
          (SMALL_BF16, [37]), (SMALL_HD256_ABS, [300])]
 
 
@@ -103,3 +106,13 @@ def test_absorbed_repeats_and_graph_replays_are_bitwise():
     finally:
         del os.environ["VLA_NO_GRAPH"]
     np.testing.assert_array_equal(eager.view(np.int64), first.view(np.int64))
+
+
+def test_one_row_block_keeps_the_three_kernel_form():
+    """A chunk of at most 16 rows gets no absorbed products: the cache is only keys, values and lengths."""
+    cfg = SMALL_W2A8
+    w, b, z0, x0 = host_inputs(cfg, 0)
+    a = build_model(cfg, w, b)
+    p = build_model(cfg, w, b, env={"VLA_ABSORB": "0"})
+    assert vla.vla_kv_cache_bytes(a, 1, cfg.n_prefix) == vla.vla_kv_cache_bytes(p, 1, cfg.n_prefix)
+    np.testing.assert_array_equal(_run(cfg, a, z0, x0).view(np.int64), _run(cfg, p, z0, x0).view(np.int64))
