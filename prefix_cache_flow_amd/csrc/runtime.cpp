@@ -1512,8 +1512,10 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
   // weights.  The gate/up GEMM reads the down weights, and the norms the
   // layer's cache block and the next layer's QKV weights; with the norms folded
   // into the products, the cross query reads the cache block and the gate/up
-  // GEMM the next layer's QKV weights too.  Only for the
-  // fragment path (batch-1 sized chunks).
+  // GEMM the next layer's QKV weights too.  With the absorbed cross sublayer
+  // the self attention reads the O weights and both absorbed products, and the
+  // gate/up weights are not read ahead.  Only for the fragment path (batch-1
+  // sized chunks).
   const size_t b_qkv = (size_t)qkve * c.d_e * es, b_o = (size_t)c.d_e * qe * es, b_q = (size_t)qe * c.d_e * es;
   const size_t b_gu = (size_t)2 * c.F_e * c.d_e * es, b_d = (size_t)c.d_e * c.F_e * es;
   const size_t layer_kv = (size_t)layer_stride * es;
@@ -1641,6 +1643,13 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
         } else {
           sa.pf = absorbed ? pfr(L.wos, b_o, g_o, kv->wqk + (size_t)e * kv->ab_ls, b_ab, g_sc, 192)
                            : pfr(L.wos, b_o, g_o, L.wqc, b_q, g_q, 192);
+          if (absorbed) {
+            // absorbed: the self attention also reads Wvo; the score product carries no prefetch (the
+            // gate/up weights read by its extra workgroups cost the product more than gate/up saved)
+            sa.pf.p3 = kv->wvo + (size_t)e * kv->ab_ls;
+            sa.pf.bytes3 = b_ab;
+            sa.pf.group3 = g_vo;
+          }
           {
             ProbeScope ps(m, VLA_PROBE_EXPERT_SELF_ATTN, s);
             for (int rep = 0; rep < ps.reps(); ++rep)
@@ -1653,11 +1662,10 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
             const uint16_t* wvo = kv->wvo + (size_t)e * kv->ab_ls;
             K_TRY(gemm_chunk_resnorm((const uint16_t*)w.eattn, (const uint16_t*)L.wos, M, c.d_e, qe, w.E, c.d_e, L.a2,
                                      (uint16_t*)w.eu, w.ess, s, nullptr), "o_s");
-            const Prefetch pf_sc = pfr(wvo, b_ab, g_vo, L.wgu, b_gu, g_gu, 192);
             {
               ProbeScope ps(m, VLA_PROBE_EXPERT_SCORES, s);
               for (int rep = 0; rep < ps.reps(); ++rep)
-                K_TRY(mm(u, c.d_e, wqk, ns_ab, c.d_e, scaled(sc_e), 1, &pf_sc), "scores");
+                K_TRY(mm(u, c.d_e, wqk, ns_ab, c.d_e, scaled(sc_e), 1, nullptr), "scores");
             }
             K_TRY(gemm_chunk_probres((const uint16_t*)w.esc, w.est, np_ab / 32, wvo, M, c.d_e, ns_ab, w.E, c.d_e, L.a3,
                                      (uint16_t*)w.eu, w.ess, s, nullptr), "cross out");
