@@ -37,9 +37,11 @@ PEAK_HBM_GBS = 8000.0
 # measurement stands.
 ATTN_KERNEL = "k_attn_chunk<256>"
 SCORES_KERNEL = "k_chunk<2, 1, 6, 8, true>"
-SCORES_TRAFFIC_BYTES_PER_LAUNCH = 27928594  # the absorbed score product, per launch
-ATTN_TRAFFIC_BYTES_PER_LAUNCH = 9596980   # mean over all launches of a bench run (prefix and expert self attention)
-DENOISE_TRAFFIC_BYTES_PER_STEP = 1893654122  # every kernel of one solver step (the denoise graph's nodes)
+SCORES_TRAFFIC_BYTES_PER_LAUNCH = 6356989  # the absorbed score product, per launch
+GATEUP_KERNEL = "k_chunk<2, 4, 2, 8, true>"
+GATEUP_TRAFFIC_BYTES_PER_LAUNCH = 31905253  # the expert gate/up product, per launch
+ATTN_TRAFFIC_BYTES_PER_LAUNCH = 13895459   # mean over all launches of a bench run (prefix and expert self attention)
+DENOISE_TRAFFIC_BYTES_PER_STEP = 1590477858  # every kernel of one solver step (the denoise graph's nodes)
 
 
 def parse():
@@ -280,6 +282,13 @@ def scores_launch_bytes(c):
     return 2 * S * c.d_e + 2 * M * c.d_e + 2 * M * S + 8 * M * (S // 32)
 
 
+def gateup_launch_bytes(c):
+    """Algorithmic bytes of one launch of the expert's gate/up product: its 2 F_e x d_e bf16 weights and the
+    chunk rows read once, the GeGLU output (F_e per row, bf16) written once."""
+    M = c.batch * c.H
+    return 2 * (2 * c.F_e * c.d_e) + 2 * M * c.d_e + 2 * M * c.F_e
+
+
 def dominant_kernel_roofline(vla, model, cfg, zt, xt, out, kv_storage, absorbed=False):
     """Roofline of the kernel with the largest share of GPU time in the committed traces: the chunk
     attention kernel for the bf16 workloads (prefix attention in the encode, self and cross attention in
@@ -322,18 +331,29 @@ def dominant_kernel_roofline(vla, model, cfg, zt, xt, out, kv_storage, absorbed=
     attention = attention_roofline(vla, model, cfg, encode, denoise, absorbed)
     if not absorbed:
         return attention
-    # the absorbed cross sublayer's score product is the largest share of the trace
-    ms, n = probe_mean_ms(vla, model, vla.PROBE_EXPERT_SCORES, denoise)
-    if ms is None:
+    timing = (f"HIP events around {PROBE_REPEAT} back-to-back repeats of each launch, separate probe pass after "
+              "the timed region, graphs off")
+    measured = cfg.name == "single_camera_bf16"
+
+    def entry(kind, nb, kernel, traffic):
+        ms, n = probe_mean_ms(vla, model, kind, denoise)
+        if ms is None:
+            return None
+        gbs = nb / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                "traffic": traffic if measured else None, "kernel": kernel, "avg_launch_us": ms * 1e3,
+                "bytes_per_launch": nb, "launches_per_step": T * L_e, "timing": timing}
+
+    # with the absorbed cross sublayer the expert's gate/up product is the largest share of the trace
+    top = entry(vla.PROBE_EXPERT_GATEUP, gateup_launch_bytes(cfg),
+                GATEUP_KERNEL + " (action-expert gate/up product with the GeGLU epilogue)", GATEUP_TRAFFIC_BYTES_PER_LAUNCH)
+    if top is None:
         return None
-    nb = scores_launch_bytes(cfg)
-    gbs = nb / (ms * 1e-3) / 1e9
-    return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-            "traffic": SCORES_TRAFFIC_BYTES_PER_LAUNCH if (cfg.name == "single_camera_bf16") else None,
-            "kernel": SCORES_KERNEL + " (absorbed cross sublayer: score product with block max and sums)",
-            "avg_launch_us": ms * 1e3, "bytes_per_launch": nb, "launches_per_step": T * L_e,
-            "timing": f"HIP events around {PROBE_REPEAT} back-to-back repeats of each launch, separate probe pass after the timed region, graphs off",
-            "attention": attention}
+    top["scores"] = entry(vla.PROBE_EXPERT_SCORES, scores_launch_bytes(cfg),
+                          SCORES_KERNEL + " (absorbed cross sublayer: score product with block max and sums)",
+                          SCORES_TRAFFIC_BYTES_PER_LAUNCH)
+    top["attention"] = attention
+    return top
 
 
 def attention_roofline(vla, model, cfg, encode, denoise, absorbed):

@@ -31,7 +31,8 @@ typedef enum {
   VLA_PROBE_CACHE = 6,         /* cache-writing projection                          */
   VLA_PROBE_EXPERT_SELF_ATTN = 7,  /* action-expert self (or joint) attention          */
   VLA_PROBE_EXPERT_CROSS_ATTN = 8, /* action-expert cross-attention into the cache     */
-  VLA_PROBE_EXPERT_SCORES = 9      /* absorbed cross sublayer: the score product        */
+  VLA_PROBE_EXPERT_SCORES = 9,     /* absorbed cross sublayer: the score product        */
+  VLA_PROBE_EXPERT_GATEUP = 10     /* action-expert gate/up projection with the GeGLU   */
 } vla_probe_kind;
 vla_status vla_probe_arm(vla_model* model, int32_t kind, int32_t max_launches);
 /* The same with each bracketed launch issued `repeat` (1..1000) times back to

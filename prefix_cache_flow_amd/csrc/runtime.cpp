@@ -1028,7 +1028,7 @@ extern "C" vla_status vla_probe_arm(vla_model* m, int32_t kind, int32_t max_laun
 
 extern "C" vla_status vla_probe_arm_ex(vla_model* m, int32_t kind, int32_t max_launches, int32_t repeat) {
   if (!live_model(m)) return fail(VLA_ERR_INVALID_HANDLE, "unknown model");
-  if (kind < VLA_PROBE_NONE || kind > VLA_PROBE_EXPERT_SCORES) return fail(VLA_ERR_INVALID_ARGUMENT, "bad probe kind");
+  if (kind < VLA_PROBE_NONE || kind > VLA_PROBE_EXPERT_GATEUP) return fail(VLA_ERR_INVALID_ARGUMENT, "bad probe kind");
   if (max_launches < 0 || max_launches > 100000) return fail(VLA_ERR_INVALID_ARGUMENT, "bad max_launches");
   if (repeat < 1 || repeat > 1000) return fail(VLA_ERR_INVALID_ARGUMENT, "repeat must be in 1..1000");
   m->probe_repeat = repeat;
@@ -1711,7 +1711,11 @@ static vla_status run_steps(vla_model* m, const vla_kv_cache* kv, int steps, con
           pf_d.p2 = pf_next.p; pf_d.bytes2 = pf_next.bytes; pf_d.group2 = pf_next.group;
           pf_d.p3 = pf_next.p2; pf_d.bytes3 = pf_next.bytes2; pf_d.group3 = pf_next.group2;
         }
-        K_TRY(mm(u, c.d_e, L.wgu, 2 * c.F_e, c.d_e, fold ? scaled(g) : g, 1, &pf_d), "gate/up");
+        {
+          ProbeScope ps(m, VLA_PROBE_EXPERT_GATEUP, s);
+          for (int rep = 0; rep < ps.reps(); ++rep)
+            K_TRY(mm(u, c.d_e, L.wgu, 2 * c.F_e, c.d_e, fold ? scaled(g) : g, 1, &pf_d), "gate/up");
+        }
         if (fold) {
           // after the last layer only the residual: the step kernel applies the final norm
           K_TRY(gemm_chunk_resnorm((const uint16_t*)w.emlp, (const uint16_t*)L.wd, M, c.d_e, c.F_e, w.E, c.d_e,

@@ -36,7 +36,7 @@ EXPORTS = (
 )
 W2A8_MFMA, W2A8_DOT4 = 0, 1
 PROBE_PREFIX_GATEUP, PROBE_PREFIX_DOWN, PROBE_PREFIX_QKV, PROBE_PREFIX_ATTN, PROBE_PREFIX_O, PROBE_CACHE = range(1, 7)
-PROBE_EXPERT_SELF_ATTN, PROBE_EXPERT_CROSS_ATTN, PROBE_EXPERT_SCORES = 7, 8, 9
+PROBE_EXPERT_SELF_ATTN, PROBE_EXPERT_CROSS_ATTN, PROBE_EXPERT_SCORES, PROBE_EXPERT_GATEUP = 7, 8, 9, 10
 
 
 class VlaError(RuntimeError):
