@@ -298,20 +298,21 @@ hipError_t zero_tails(void* base, long nblk, long blk, int tail, hipStream_t s) 
 // step then needs two products per cross sublayer (scores, and weights times
 // Wvo into the residual) instead of query, attention and output kernels.
 //
-// k_absorb<HD, QK>: one layer, one query head j, 144 keys (9 key blocks) and
-// 256 output features (four waves of 4 row blocks).  The keys' (QK) or values'
-// fragments of every d-step are staged once in LDS and shared by the four
-// waves; each wave requests all its rows of WqT (QK) or Wo (the other operand,
-// columns j hd .. j hd + hd - 1) up front, so a workgroup waits on memory once.
+// k_absorb<HD, QK>: one layer, one query head j, 288 keys (18 key blocks) and
+// 256 output features (eight waves of 2 row blocks, two per SIMD).  The keys'
+// (QK) or values' fragments of every d-step are staged once in LDS and shared
+// by the eight waves; each wave requests all its rows of WqT (QK) or Wo (the
+// other operand, columns j hd .. j hd + hd - 1) up front, so a workgroup waits
+// on memory once.
 //   QK: D[k][t] = sum_d WqT[k][j hd + d] K[t][d]: a lane's four results are four
 //       consecutive k of output row j Np + t of wqk (one 8-byte store, scaled by
 //       sl2 = log2(e) / sqrt(hd)).
 //   VO: D[t][n] = sum_d V[t][d] Wo[n][j hd + d]: four consecutive keys of row n,
 //       column j Np + t of wvo (padding keys have zero values: zero columns).
-constexpr int kAbsXB = 9, kAbsYB = 4;
+constexpr int kAbsXB = 18, kAbsYB = 2;
 
 template <int HD, bool QK>
-__global__ __launch_bounds__(256) void k_absorb(AbsorbP p) {
+__global__ __launch_bounds__(512) void k_absorb(AbsorbP p) {
   constexpr int DS = HD / 32, XB = kAbsXB, YB = kAbsYB, NX = DS * XB * 64;
   __shared__ u32x4_t xs[DS * XB][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(256) void k_absorb(AbsorbP p) {
   const int tbs = p.Np / 16, tcs = (tbs + XB - 1) / XB, ybs = p.d_e / 16;
   const int j = blockIdx.y / tcs, tc = blockIdx.y % tcs, l = blockIdx.z;
   const int g = j * p.Hkv / p.Hq, qe = p.Hq * HD;
-  const int tb0 = tc * XB, yb0 = (blockIdx.x * 4 + w) * YB;
+  const int tb0 = tc * XB, yb0 = (blockIdx.x * 8 + w) * YB;
   const u32x4_t* X = (const u32x4_t*)((QK ? p.k + l * p.k_ls : p.v + l * p.v_ls) + (long)g * p.Np * HD);
   const u32x4_t* Y = (const u32x4_t*)(QK ? p.wqT + l * p.wq_ls : p.wo + l * p.wo_ls) + (long)j * DS * 64 + lane;
   // every d-step of this wave's rows requested first, then the shared blocks
@@ -330,9 +331,9 @@ __global__ __launch_bounds__(256) void k_absorb(AbsorbP p) {
     for (int a = 0; a < YB; ++a) y[ds][a] = Y[((long)min(yb0 + a, ybs - 1) * (qe / 32) + ds) * 64];
   // shared operand: blocks tb0 .. tb0 + XB - 1 (clamped), every d-step
 #pragma unroll
-  for (int r = 0; r < (NX + 255) / 256; ++r) {
-    const int i = r * 256 + (int)threadIdx.x;
-    if (NX % 256 == 0 || i < NX) {
+  for (int r = 0; r < (NX + 511) / 512; ++r) {
+    const int i = r * 512 + (int)threadIdx.x;
+    if (NX % 512 == 0 || i < NX) {
       const int f = i >> 6, ln = i & 63, xb = f / DS, ds = f - xb * DS;
       xs[ds * XB + xb][ln] = X[((long)min(tb0 + xb, tbs - 1) * DS + ds) * 64 + ln];
     }
@@ -382,19 +383,19 @@ hipError_t absorb_products(const AbsorbP& p, hipStream_t s) {
       p.Np <= 0 || p.Np % 32 || p.d_e <= 0 || p.d_e % 128)
     return hipErrorInvalidValue;
   const int tbs = p.Np / 16, ybs = p.d_e / 16;
-  const dim3 grid((ybs + 4 * kAbsYB - 1) / (4 * kAbsYB), p.Hq * ((tbs + kAbsXB - 1) / kAbsXB), p.L);
+  const dim3 grid((ybs + 8 * kAbsYB - 1) / (8 * kAbsYB), p.Hq * ((tbs + kAbsXB - 1) / kAbsXB), p.L);
   switch (p.hd) {
     case 64:
-      hipLaunchKernelGGL((k_absorb<64, true>), grid, dim3(256), 0, s, p);
-      hipLaunchKernelGGL((k_absorb<64, false>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((k_absorb<64, true>), grid, dim3(512), 0, s, p);
+      hipLaunchKernelGGL((k_absorb<64, false>), grid, dim3(512), 0, s, p);
       break;
     case 128:
-      hipLaunchKernelGGL((k_absorb<128, true>), grid, dim3(256), 0, s, p);
-      hipLaunchKernelGGL((k_absorb<128, false>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((k_absorb<128, true>), grid, dim3(512), 0, s, p);
+      hipLaunchKernelGGL((k_absorb<128, false>), grid, dim3(512), 0, s, p);
       break;
     case 256:
-      hipLaunchKernelGGL((k_absorb<256, true>), grid, dim3(256), 0, s, p);
-      hipLaunchKernelGGL((k_absorb<256, false>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((k_absorb<256, true>), grid, dim3(512), 0, s, p);
+      hipLaunchKernelGGL((k_absorb<256, false>), grid, dim3(512), 0, s, p);
       break;
     default: return hipErrorInvalidValue;
   }
